@@ -1,0 +1,288 @@
+/*
+ * pagedkv.h -- C ABI of the paged KV-cache hot path for AMD MI355X (gfx950).
+ *
+ * Attention that reads keys and values through a page table out of one
+ * shared, preallocated, paged KV pool: the pool geometry, the KV append
+ * (scatter of new tokens' K/V into their slots), index building (token table
+ * -> page-granular CSR or padded block table), paged decode attention
+ * (split-K over pages with a log-sum-exp merge), paged extend/prefill over a
+ * paged prefix, and the ragged gather.
+ *
+ * Sources, cited by short name:
+ *   [XPU]     "Enabling Encoder-Decoder Models on Intel XPU in SGLang: A KV-Cache Story"
+ *   [OMNI]    "Scheduler-Managed Paged KV Cache" (vLLM-Omni design documents)
+ *   [MINI]    "The KV pool, the page table and the token pool" (mini-sglang from Scratch)
+ *   [BACKEND] "AttentionBackend" (SGLang FlashInfer-MLA / FlashMLA backend notes)
+ *
+ * Conventions for every call:
+ *   - Ownership: the library allocates no device memory and frees none.  The
+ *     caller owns the pool buffers, tables, outputs and workspace, and keeps
+ *     them alive until the work queued on `stream` has finished.  The only
+ *     object the library owns is the immutable host-side pool handle.
+ *   - Execution: every call that launches work is asynchronous on `stream`
+ *     (a hipStream_t; NULL = the default stream) and never synchronises the
+ *     host.  Host-known maxima (max_kv_len, max_q_len, capacities) are passed
+ *     in by the caller.
+ *   - Pointers named "device" must point to device (or managed) memory;
+ *     "host" pointers are read before the call returns.
+ *   - Errors: each call returns 0 (PKV_OK) or a negative status; no C++
+ *     exception crosses this boundary; nothing falls back silently.  The
+ *     message of the last failing call on the calling thread is
+ *     pkv_last_error().
+ *   - Index contents (slots, page ids, lengths) live in device memory and are
+ *     not validated on the hot path; every kernel range-checks what it reads
+ *     and treats an out-of-range entry as the padding slot, so a corrupt
+ *     table gives an unspecified result but no out-of-bounds access.
+ *     kv_validate() checks contents (off the hot path, synchronising).
+ */
+#ifndef PAGEDKV_H_
+#define PAGEDKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_ABI_VERSION 1
+
+/* status codes */
+#define PKV_OK 0
+#define PKV_EINVAL (-1)       /* null/negative argument, or dims inconsistent with the pool */
+#define PKV_EUNSUPPORTED (-2) /* page_size, head_dim, dtype or head grouping not instantiated */
+#define PKV_EALIGN (-3)       /* base pointer not 16-byte aligned; kv_start not page aligned */
+#define PKV_ECAPACITY (-4)    /* output capacity or workspace too small */
+#define PKV_EDEVICE (-5)      /* HIP launch/runtime error (details in pkv_last_error) */
+
+/* element types */
+#define PKV_DTYPE_F32 0
+#define PKV_DTYPE_BF16 1
+
+/* pool kinds */
+#define PKV_KIND_SPLIT_KV 0 /* separate K and V buffers */
+#define PKV_KIND_LATENT 1   /* one buffer; V is the first head_dim_v values of each K row (MLA) */
+
+/* KV map formats */
+#define PKV_MAP_TOKEN_TABLE 0 /* token-granular req_to_token rows ([XPU] "two pools"; [MINI] page table) */
+#define PKV_MAP_CSR 1         /* kv_indptr / kv_indices page ids ([BACKEND] "kv_indptr 和 kv_indices") */
+#define PKV_MAP_BLOCK_TABLE 2 /* [bs, block_stride] page ids padded with -1 ([BACKEND] init_forward_metadata) */
+#define PKV_MAP_CONTIGUOUS 3  /* gathered K/V addressed by cu_seqlens_k ([XPU] "Approach 2") */
+
+/*
+ * Pool geometry ([MINI] "The KV pool: one preallocated block of memory";
+ * [XPU] "two pools and a page size").  Each buffer is laid out
+ *   [num_layers][num_pages + 1][page_size][num_kv_heads][head_dim]
+ * (row-major, token-major inside a page), so that one layer's buffer viewed
+ * per token is [(num_pages + 1) * page_size][num_kv_heads][head_dim] and
+ * slot s lives at page s / page_size, offset s % page_size.  Page num_pages
+ * is the padding page: dummy requests of a padded batch read and write it,
+ * real requests never do ([MINI] "Why the extra page?").
+ *   page_size: a power of two, 1..128.
+ *   head_dim_qk / head_dim_v: K row and V row lengths.  SPLIT_KV requires
+ *     head_dim_qk == head_dim_v; LATENT requires head_dim_v <= head_dim_qk.
+ */
+typedef struct pkv_pool_desc {
+  int32_t num_layers;
+  int32_t num_pages; /* real pages */
+  int32_t page_size;
+  int32_t num_kv_heads;
+  int32_t head_dim_qk;
+  int32_t head_dim_v;
+  int32_t dtype; /* PKV_DTYPE_* */
+  int32_t kind;  /* PKV_KIND_* */
+} pkv_pool_desc;
+
+typedef struct pkv_pool pkv_pool; /* opaque, immutable host-side handle */
+
+/*
+ * Where each request's keys live (one attention call's view).
+ *   bs          requests in the batch.
+ *   kv_lens     device int32[bs]: keys request i attends over, including the
+ *               tokens appended this step.
+ *   max_kv_len  host bound >= every kv_lens[i] (sizes the launch).
+ * TOKEN_TABLE: req_to_token device int32[table_rows][table_width] (row
+ *   stride = table_width) holding slots; req_pool_indices device int32[bs]
+ *   picks each request's row; kv_start device int32[bs] (NULL = all 0) is the
+ *   first column of the region (e.g. the decoder region of an
+ *   encoder-decoder row, [XPU] "two KV regions in one row").  Works for
+ *   every page size: slot(t) = row[kv_start + t].
+ * CSR: kv_indptr device int32[bs+1], kv_indices device int32[kv_indices_len]
+ *   of page ids; slot(t) = kv_indices[kv_indptr[i] + t/ps]*ps + t%ps.
+ * BLOCK_TABLE: block_table device int32[bs][block_stride] of page ids,
+ *   -1 past each request's last page.
+ * CONTIGUOUS: k, v device buffers [total_k][num_kv_heads][head_dim]
+ *   (v ignored for a LATENT pool) and cu_seqlens_k device int32[bs+1];
+ *   request i's keys are rows cu_seqlens_k[i] .. + kv_lens[i].
+ */
+typedef struct pkv_kv_map {
+  int32_t fmt;
+  int32_t bs;
+  const int32_t* kv_lens;
+  int32_t max_kv_len;
+  const int32_t* req_to_token;
+  int64_t table_rows;
+  int64_t table_width;
+  const int32_t* req_pool_indices;
+  const int32_t* kv_start;
+  const int32_t* kv_indptr;
+  const int32_t* kv_indices;
+  int64_t kv_indices_len;
+  const int32_t* block_table;
+  int64_t block_stride;
+  const void* k;
+  const void* v;
+  const int32_t* cu_seqlens_k;
+  int64_t total_k;
+} pkv_kv_map;
+
+/* ---- library ----------------------------------------------------------- */
+
+/* PKV_ABI_VERSION of the built library. */
+int pkv_abi_version(void);
+/* Static description of a status code. */
+const char* pkv_status_string(int status);
+/* Message of the last failing call on this thread ("" if none). */
+const char* pkv_last_error(void);
+/* Device and gfx architecture the library was built for, e.g. "gfx950". */
+const char* pkv_build_arch(void);
+
+/* ---- pool (a1) ---------------------------------------------------------- */
+
+/* Bytes of the K and V buffers for `desc` (v_bytes = 0 for LATENT). */
+int kv_pool_bytes(const pkv_pool_desc* desc, size_t* k_bytes, size_t* v_bytes);
+
+/* Describe a caller-allocated pool.  k_base (and v_base for SPLIT_KV) are
+ * device pointers to kv_pool_bytes() bytes, 16-byte aligned; v_base must be
+ * NULL for LATENT.  *out receives a handle the caller releases with
+ * kv_pool_destroy(); the buffers stay the caller's. */
+int kv_pool_create(const pkv_pool_desc* desc, void* k_base, void* v_base, pkv_pool** out);
+int kv_pool_destroy(pkv_pool* pool);
+/* Index of the padding page (== num_pages), or a negative status. */
+int32_t kv_pool_padding_page(const pkv_pool* pool);
+/* Bytes of one token's K+V in one layer (the [MINI] per-token figure / layers). */
+int64_t kv_pool_token_bytes(const pkv_pool* pool);
+
+/* ---- KV append (a2) ----------------------------------------------------- */
+
+/* pool[layer][out_loc[j]] = k[j] (and v[j]) for j < n: a bit-exact scatter
+ * of whole token rows ([MINI] store_kv; [OMNI] "Attention execution": the
+ * current K/V span is written once per layer before any attention).
+ *   k, v: device [n][num_kv_heads][head_dim] contiguous, pool dtype, 16-byte
+ *     aligned (v NULL for LATENT).
+ *   out_loc: device int32[n], slots in [0, (num_pages+1)*page_size); an
+ *     out-of-range slot is skipped.  Duplicate slots race (only meaningful
+ *     for dummy writes to the padding page). */
+int kv_store(const pkv_pool* pool, int32_t layer, const void* k, const void* v, const int32_t* out_loc,
+             int64_t n, void* stream);
+
+/* ---- index building (a3) ------------------------------------------------ */
+
+/* Turn token-table rows into page-granular indices ([XPU] "From slots to a
+ * page table": every page_size-th column divided by page_size; [BACKEND]
+ * "kv_indptr 和 kv_indices" and init_forward_metadata).
+ *   out_fmt: PKV_MAP_CSR or PKV_MAP_BLOCK_TABLE.
+ *   req_to_token, req_pool_indices, kv_start (nullable), kv_lens: as in
+ *     pkv_kv_map (device).  kv_start[i] must be a multiple of page_size
+ *     (the [XPU] page-alignment seam; kv_validate reports PKV_EALIGN).
+ *   max_kv_len: host bound >= every kv_lens[i].
+ *   CSR: kv_indptr device int32[bs+1] receives the prefix sum of
+ *     ceil(kv_lens/page_size); out = kv_indices device int32[capacity].
+ *     capacity must be >= bs * ceil(max_kv_len / page_size) (PKV_ECAPACITY).
+ *   BLOCK_TABLE: out = device int32[bs][capacity] (capacity = row stride),
+ *     capacity >= ceil(max_kv_len / page_size); entries past each request's
+ *     last page are -1.  kv_indptr is ignored (may be NULL).
+ *   kv_last_page_len: nullable device int32[bs]; receives
+ *     kv_lens - (ceil(kv_lens/page_size) - 1) * page_size (0 if empty). */
+int build_kv_indices(int32_t out_fmt, const int32_t* req_to_token, int64_t table_rows, int64_t table_width,
+                     const int32_t* req_pool_indices, const int32_t* kv_start, const int32_t* kv_lens, int32_t bs,
+                     int32_t page_size, int32_t max_kv_len, int32_t* kv_indptr, int32_t* out, int64_t capacity,
+                     int32_t* kv_last_page_len, void* stream);
+
+/* ---- paged decode (a4, a5, a6) ------------------------------------------ */
+
+/* Workspace bytes paged_decode_attn needs for this batch shape. */
+int paged_decode_workspace_bytes(const pkv_pool* pool, int32_t bs, int32_t num_q_heads, int32_t max_kv_len,
+                                 size_t* bytes);
+
+/* One query token per request attends over its kv_lens[i] keys read through
+ * `map` ([XPU] "From slots to a page table"; [BACKEND] init_forward_metadata
+ * with its split plan).  Query head h reads KV head h / (num_q_heads /
+ * num_kv_heads).  The keys are split into chunks of logical positions; each
+ * chunk's partial result is merged by log-sum-exp, so the output does not
+ * depend on where pages live.
+ *   q: device [bs][num_q_heads][head_dim_qk], pool dtype.
+ *   out: device [bs][num_q_heads][head_dim_v], pool dtype (round to nearest
+ *     even for bf16).
+ *   lse: nullable device float[bs][num_q_heads], natural-log log-sum-exp of
+ *     the scaled scores; kv_lens[i] == 0 gives out = 0 and lse = -inf.
+ *   workspace: device, >= paged_decode_workspace_bytes(), 256-byte aligned.
+ *   map->fmt: TOKEN_TABLE, CSR or BLOCK_TABLE.
+ * Supported: SPLIT_KV f32 or bf16 with head_dim 64 or 128 and
+ * num_q_heads/num_kv_heads <= 16; LATENT bf16 with head_dim_qk 576,
+ * head_dim_v 512, one KV head and num_q_heads a multiple of 32. */
+int paged_decode_attn(const pkv_pool* pool, int32_t layer, const void* q, int32_t num_q_heads,
+                      const pkv_kv_map* map, float sm_scale, void* out, float* lse, void* workspace,
+                      size_t ws_bytes, void* stream);
+
+/* ---- paged extend / prefill (a7, a8, a9) -------------------------------- */
+
+/* Each request's qo_indptr[i+1] - qo_indptr[i] new query tokens attend over
+ * its kv_lens[i] keys ([BACKEND] "例子": qo_indptr / kv_indptr; [OMNI]
+ * "Attention execution": causal and full segments).  causal != 0 aligns the
+ * queries bottom-right: the j-th of n new queries sees keys 0 .. L - n + j;
+ * causal == 0 lets every query see every key (encoder cross-attention).
+ *   q: device [total_q][num_q_heads][head_dim_qk] (total_q = qo_indptr[bs]).
+ *   qo_indptr: device int32[bs+1].
+ *   max_q_len: host bound >= every new-token count.
+ *   out: device [total_q][num_q_heads][head_dim_v]; lse nullable float
+ *     [total_q][num_q_heads].  An empty key set gives out = 0, lse = -inf
+ *     ([XPU] "Approach 2" empty-KV guard).
+ *   map->fmt: any; CONTIGUOUS is the ragged (varlen) variant.
+ * Supported: SPLIT_KV bf16, head_dim 64 or 128. */
+int paged_extend_attn(const pkv_pool* pool, int32_t layer, const void* q, const int32_t* qo_indptr,
+                      int32_t num_q_heads, int32_t max_q_len, const pkv_kv_map* map, int32_t causal,
+                      float sm_scale, void* out, float* lse, void* stream);
+
+/* ---- ragged gather (a9) ------------------------------------------------- */
+
+/* Copy each request's first kv_lens[i] K (and V) rows, in logical order,
+ * to rows cu_seqlens_k[i] .. of k_out / v_out ([XPU] "Approach 2": the
+ * index_select gather feeding the varlen kernel).  Bit exact.
+ *   map->fmt: TOKEN_TABLE, CSR or BLOCK_TABLE.
+ *   cu_seqlens_k: device int32[bs+1]; out_rows: capacity of k_out / v_out
+ *     in rows (rows past it are not written).
+ *   k_out, v_out: device [out_rows][num_kv_heads][head_dim] (v_out NULL for
+ *     LATENT), 16-byte aligned. */
+int kv_gather(const pkv_pool* pool, int32_t layer, const pkv_kv_map* map, const int32_t* cu_seqlens_k,
+              void* k_out, void* v_out, int64_t out_rows, void* stream);
+
+/* ---- debug / measurement (off the hot path) ------------------------------ */
+
+/* Check a map's contents on the device and SYNCHRONISE `stream`: slots and
+ * page ids in range, -1 only after a request's last page, no real request on
+ * the padding page, kv_start page aligned for page-granular use, tokens
+ * contiguous inside each page.
+ *   is_dummy: nullable device int32[bs], nonzero marks padded-batch dummies.
+ *   scratch: device int64[bs * 8] the kernel writes per-request counts to
+ *     (the library allocates nothing).
+ *   counts: host int64[8] receives the totals of each kind: [0] slot/page
+ *     out of range, [1] padding page used by a real request, [2] -1 inside a
+ *     length or a real id after it, [3] misaligned kv_start, [4] in-page
+ *     contiguity broken, [5] length beyond the table or a bad indptr.
+ * Returns PKV_OK when every count is zero, PKV_EALIGN when only kv_start
+ * alignment fails, else PKV_EINVAL. */
+int kv_validate(const pkv_pool* pool, const pkv_kv_map* map, const int32_t* is_dummy, int64_t* scratch,
+                int64_t counts[8], void* stream);
+
+/* Record hipEvent_t `start` before and `stop` after the main attention
+ * kernel of the next paged_decode_attn / paged_extend_attn call made on
+ * this thread (the split-K partial kernel for decode), then forget them.
+ * Pass NULLs to clear.  For measuring one kernel inside a call. */
+int pkv_set_kernel_timer(void* start_event, void* stop_event);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H_ */

@@ -1,0 +1,276 @@
+"""Paged KV-cache hot path for AMD MI355X (gfx950).
+
+A thin binding over the C ABI of ``libpagedkv.so`` (``include/pagedkv.h``):
+the functions below carry the same names as the C entry points and only
+marshal arguments (torch tensors -> device pointers, the caller's current
+HIP stream).  Every step of the hot path runs in the library's HIP kernels;
+torch provides device memory and streams.  If the library is missing, the
+first call raises -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib as L
+from ._lib import (  # noqa: F401
+    PKV_DTYPE_BF16,
+    PKV_DTYPE_F32,
+    PKV_KIND_LATENT,
+    PKV_KIND_SPLIT_KV,
+    PKV_MAP_BLOCK_TABLE,
+    PKV_MAP_CONTIGUOUS,
+    PKV_MAP_CSR,
+    PKV_MAP_TOKEN_TABLE,
+    PagedKVError,
+)
+
+__all__ = [
+    "Pool", "KVMap", "kv_pool_bytes", "kv_pool_create", "kv_pool_destroy", "kv_pool_padding_page",
+    "kv_pool_token_bytes", "kv_store", "build_kv_indices", "make_kv_map", "paged_decode_workspace_bytes",
+    "paged_decode_attn", "paged_extend_attn", "kv_gather", "kv_validate", "pkv_set_kernel_timer", "library",
+]
+
+_DTYPES = {torch.float32: PKV_DTYPE_F32, torch.bfloat16: PKV_DTYPE_BF16}
+
+
+def library() -> C.CDLL:
+    return L.load()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dev(t: Optional[torch.Tensor], name: str, dtype=None) -> Optional[int]:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+# ---------------------------------------------------------------------------
+# pool
+# ---------------------------------------------------------------------------
+
+def _desc(num_layers, num_pages, page_size, num_kv_heads, head_dim_qk, head_dim_v, dtype, latent) -> L.PoolDesc:
+    return L.PoolDesc(num_layers, num_pages, page_size, num_kv_heads, head_dim_qk,
+                      head_dim_qk if head_dim_v is None else head_dim_v,
+                      _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype),
+                      PKV_KIND_LATENT if latent else PKV_KIND_SPLIT_KV)
+
+
+def kv_pool_bytes(num_layers: int, num_pages: int, page_size: int, num_kv_heads: int, head_dim_qk: int,
+                  head_dim_v: Optional[int] = None, dtype=torch.bfloat16, latent: bool = False) -> Tuple[int, int]:
+    d = _desc(num_layers, num_pages, page_size, num_kv_heads, head_dim_qk, head_dim_v, dtype, latent)
+    kb, vb = C.c_size_t(), C.c_size_t()
+    L.check(L.load().kv_pool_bytes(C.byref(d), C.byref(kb), C.byref(vb)), "kv_pool_bytes")
+    return kb.value, vb.value
+
+
+@dataclass
+class Pool:
+    """Host handle of a pool whose buffers the caller allocated (kept
+    referenced here so they outlive the handle)."""
+    handle: int
+    k: torch.Tensor
+    v: Optional[torch.Tensor]
+    num_layers: int
+    num_pages: int
+    page_size: int
+    num_kv_heads: int
+    head_dim_qk: int
+    head_dim_v: int
+    latent: bool
+
+    @property
+    def dtype(self) -> torch.dtype:
+        return self.k.dtype
+
+    def flat(self, which: str, layer: int) -> torch.Tensor:
+        """One layer's buffer viewed per token ``[(num_pages+1)*page_size, heads, dim]``."""
+        buf = self.k if which == "k" else self.v
+        dim = self.head_dim_qk if which == "k" else self.head_dim_v
+        return buf.view(self.num_layers, (self.num_pages + 1) * self.page_size, self.num_kv_heads, dim)[layer]
+
+
+def kv_pool_create(k: torch.Tensor, v: Optional[torch.Tensor], *, num_layers: int, num_pages: int, page_size: int,
+                   num_kv_heads: int, head_dim_qk: int, head_dim_v: Optional[int] = None,
+                   latent: bool = False) -> Pool:
+    if k.dtype not in _DTYPES:
+        raise TypeError(f"pool dtype {k.dtype} not supported")
+    d = _desc(num_layers, num_pages, page_size, num_kv_heads, head_dim_qk, head_dim_v, k.dtype, latent)
+    kb, vb = kv_pool_bytes(num_layers, num_pages, page_size, num_kv_heads, head_dim_qk, head_dim_v, k.dtype, latent)
+    if k.numel() * k.element_size() < kb or (v is not None and v.numel() * v.element_size() < vb):
+        raise ValueError("pool buffers are smaller than kv_pool_bytes")
+    h = C.c_void_p()
+    L.check(L.load().kv_pool_create(C.byref(d), _dev(k, "k"), _dev(v, "v"), C.byref(h)), "kv_pool_create")
+    return Pool(h.value, k, v, num_layers, num_pages, page_size, num_kv_heads, head_dim_qk,
+                head_dim_qk if head_dim_v is None else head_dim_v, latent)
+
+
+def kv_pool_destroy(pool: Pool) -> None:
+    if pool.handle:
+        L.check(L.load().kv_pool_destroy(pool.handle), "kv_pool_destroy")
+        pool.handle = 0
+
+
+def kv_pool_padding_page(pool: Pool) -> int:
+    r = L.load().kv_pool_padding_page(pool.handle)
+    L.check(min(r, 0), "kv_pool_padding_page")
+    return r
+
+
+def kv_pool_token_bytes(pool: Pool) -> int:
+    r = L.load().kv_pool_token_bytes(pool.handle)
+    L.check(int(min(r, 0)), "kv_pool_token_bytes")
+    return r
+
+
+# ---------------------------------------------------------------------------
+# store / indices / gather
+# ---------------------------------------------------------------------------
+
+def kv_store(pool: Pool, layer: int, k: torch.Tensor, v: Optional[torch.Tensor], out_loc: torch.Tensor,
+             stream=None) -> None:
+    L.check(L.load().kv_store(pool.handle, layer, _dev(k, "k", pool.dtype), _dev(v, "v", pool.dtype),
+                              _dev(out_loc, "out_loc", torch.int32), out_loc.numel(), _stream(stream)), "kv_store")
+
+
+def build_kv_indices(out_fmt: int, req_to_token: torch.Tensor, req_pool_indices: torch.Tensor,
+                     kv_start: Optional[torch.Tensor], kv_lens: torch.Tensor, page_size: int, max_kv_len: int,
+                     kv_indptr: Optional[torch.Tensor], out: torch.Tensor,
+                     kv_last_page_len: Optional[torch.Tensor] = None, stream=None) -> None:
+    """CSR: ``out`` is kv_indices (capacity = ``out.numel()``).  BLOCK_TABLE:
+    ``out`` is ``[bs, stride]`` (capacity = stride)."""
+    i32 = torch.int32
+    rows, width = req_to_token.shape
+    cap = out.numel() if out_fmt == PKV_MAP_CSR else out.shape[-1]
+    L.check(L.load().build_kv_indices(
+        out_fmt, _dev(req_to_token, "req_to_token", i32), rows, width, _dev(req_pool_indices, "req_pool_indices", i32),
+        _dev(kv_start, "kv_start", i32), _dev(kv_lens, "kv_lens", i32), kv_lens.numel(), page_size, max_kv_len,
+        _dev(kv_indptr, "kv_indptr", i32), _dev(out, "out", i32), cap,
+        _dev(kv_last_page_len, "kv_last_page_len", i32), _stream(stream)), "build_kv_indices")
+
+
+@dataclass
+class KVMap:
+    """A pkv_kv_map plus the tensors it points at (kept alive here)."""
+    struct: L.KVMapStruct
+    refs: tuple
+
+    @property
+    def bs(self) -> int:
+        return self.struct.bs
+
+    @property
+    def max_kv_len(self) -> int:
+        return self.struct.max_kv_len
+
+
+def make_kv_map(fmt: int, kv_lens: torch.Tensor, max_kv_len: int, *, req_to_token=None, req_pool_indices=None,
+                kv_start=None, kv_indptr=None, kv_indices=None, block_table=None, k=None, v=None,
+                cu_seqlens_k=None) -> KVMap:
+    i32 = torch.int32
+    s = L.KVMapStruct()
+    s.fmt = fmt
+    s.bs = kv_lens.numel()
+    s.kv_lens = _dev(kv_lens, "kv_lens", i32)
+    s.max_kv_len = int(max_kv_len)
+    if req_to_token is not None:
+        s.req_to_token = _dev(req_to_token, "req_to_token", i32)
+        s.table_rows, s.table_width = req_to_token.shape
+    s.req_pool_indices = _dev(req_pool_indices, "req_pool_indices", i32)
+    s.kv_start = _dev(kv_start, "kv_start", i32)
+    s.kv_indptr = _dev(kv_indptr, "kv_indptr", i32)
+    if kv_indices is not None:
+        s.kv_indices = _dev(kv_indices, "kv_indices", i32)
+        s.kv_indices_len = kv_indices.numel()
+    if block_table is not None:
+        s.block_table = _dev(block_table, "block_table", i32)
+        s.block_stride = block_table.shape[-1]
+    s.k = _dev(k, "k")
+    s.v = _dev(v, "v")
+    s.cu_seqlens_k = _dev(cu_seqlens_k, "cu_seqlens_k", i32)
+    if k is not None:
+        s.total_k = k.shape[0]
+    return KVMap(s, (kv_lens, req_to_token, req_pool_indices, kv_start, kv_indptr, kv_indices, block_table, k, v,
+                     cu_seqlens_k))
+
+
+def kv_gather(pool: Pool, layer: int, kv_map: KVMap, cu_seqlens_k: torch.Tensor, k_out: torch.Tensor,
+              v_out: Optional[torch.Tensor], stream=None) -> None:
+    L.check(L.load().kv_gather(pool.handle, layer, C.byref(kv_map.struct), _dev(cu_seqlens_k, "cu_seqlens_k",
+                                                                             torch.int32),
+                               _dev(k_out, "k_out", pool.dtype), _dev(v_out, "v_out", pool.dtype), k_out.shape[0],
+                               _stream(stream)), "kv_gather")
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+
+def paged_decode_workspace_bytes(pool: Pool, bs: int, num_q_heads: int, max_kv_len: int) -> int:
+    n = C.c_size_t()
+    L.check(L.load().paged_decode_workspace_bytes(pool.handle, bs, num_q_heads, max_kv_len, C.byref(n)),
+            "paged_decode_workspace_bytes")
+    return n.value
+
+
+def paged_decode_attn(pool: Pool, layer: int, q: torch.Tensor, kv_map: KVMap, sm_scale: float, out: torch.Tensor,
+                      lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                      stream=None) -> None:
+    """q ``[bs, Hq, Dqk]`` -> out ``[bs, Hq, Dv]`` (pool dtype); workspace a
+    uint8 device tensor of at least paged_decode_workspace_bytes() bytes."""
+    ws_ptr = _dev(workspace, "workspace")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    L.check(L.load().paged_decode_attn(pool.handle, layer, _dev(q, "q", pool.dtype), q.shape[1],
+                                       C.byref(kv_map.struct), float(sm_scale), _dev(out, "out", pool.dtype),
+                                       _dev(lse, "lse", torch.float32), ws_ptr, ws_bytes, _stream(stream)),
+            "paged_decode_attn")
+
+
+def paged_extend_attn(pool: Pool, layer: int, q: torch.Tensor, qo_indptr: torch.Tensor, max_q_len: int,
+                      kv_map: KVMap, causal: bool, sm_scale: float, out: torch.Tensor,
+                      lse: Optional[torch.Tensor] = None, stream=None) -> None:
+    L.check(L.load().paged_extend_attn(pool.handle, layer, _dev(q, "q", pool.dtype),
+                                       _dev(qo_indptr, "qo_indptr", torch.int32), q.shape[1], int(max_q_len),
+                                       C.byref(kv_map.struct), 1 if causal else 0, float(sm_scale),
+                                       _dev(out, "out", pool.dtype), _dev(lse, "lse", torch.float32),
+                                       _stream(stream)), "paged_extend_attn")
+
+
+# ---------------------------------------------------------------------------
+# debug / measurement
+# ---------------------------------------------------------------------------
+
+def kv_validate(pool: Pool, kv_map: KVMap, is_dummy: Optional[torch.Tensor] = None,
+                scratch: Optional[torch.Tensor] = None, stream=None) -> Tuple[int, list]:
+    """Returns (status, counts[8]); synchronises the stream."""
+    if scratch is None:
+        scratch = torch.empty(max(kv_map.bs, 1) * 8, dtype=torch.int64, device=kv_map.refs[0].device)
+    counts = (C.c_int64 * 8)()
+    st = L.load().kv_validate(pool.handle, C.byref(kv_map.struct), _dev(is_dummy, "is_dummy", torch.int32),
+                              _dev(scratch, "scratch", torch.int64), counts, _stream(stream))
+    if st not in (L.PKV_OK, L.PKV_EINVAL, L.PKV_EALIGN):
+        L.check(st, "kv_validate")
+    return st, list(counts)
+
+
+def pkv_set_kernel_timer(start_event: Optional[int], stop_event: Optional[int]) -> None:
+    """Raw hipEvent_t handles (ints) or None."""
+    L.check(L.load().pkv_set_kernel_timer(start_event, stop_event), "pkv_set_kernel_timer")

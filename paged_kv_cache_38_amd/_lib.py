@@ -1,0 +1,126 @@
+"""ctypes view of ``libpagedkv.so`` (include/pagedkv.h).
+
+Loading fails loudly when the library has not been built: there is no
+fallback path of any kind.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
+
+PKV_OK = 0
+PKV_EINVAL = -1
+PKV_EUNSUPPORTED = -2
+PKV_EALIGN = -3
+PKV_ECAPACITY = -4
+PKV_EDEVICE = -5
+
+PKV_DTYPE_F32 = 0
+PKV_DTYPE_BF16 = 1
+PKV_KIND_SPLIT_KV = 0
+PKV_KIND_LATENT = 1
+PKV_MAP_TOKEN_TABLE = 0
+PKV_MAP_CSR = 1
+PKV_MAP_BLOCK_TABLE = 2
+PKV_MAP_CONTIGUOUS = 3
+
+
+class PoolDesc(C.Structure):
+    _fields_ = [
+        ("num_layers", C.c_int32),
+        ("num_pages", C.c_int32),
+        ("page_size", C.c_int32),
+        ("num_kv_heads", C.c_int32),
+        ("head_dim_qk", C.c_int32),
+        ("head_dim_v", C.c_int32),
+        ("dtype", C.c_int32),
+        ("kind", C.c_int32),
+    ]
+
+
+class KVMapStruct(C.Structure):
+    _fields_ = [
+        ("fmt", C.c_int32),
+        ("bs", C.c_int32),
+        ("kv_lens", C.c_void_p),
+        ("max_kv_len", C.c_int32),
+        ("req_to_token", C.c_void_p),
+        ("table_rows", C.c_int64),
+        ("table_width", C.c_int64),
+        ("req_pool_indices", C.c_void_p),
+        ("kv_start", C.c_void_p),
+        ("kv_indptr", C.c_void_p),
+        ("kv_indices", C.c_void_p),
+        ("kv_indices_len", C.c_int64),
+        ("block_table", C.c_void_p),
+        ("block_stride", C.c_int64),
+        ("k", C.c_void_p),
+        ("v", C.c_void_p),
+        ("cu_seqlens_k", C.c_void_p),
+        ("total_k", C.c_int64),
+    ]
+
+
+# name -> (restype, argtypes): every entry point include/pagedkv.h declares
+SIGNATURES = {
+    "pkv_abi_version": (C.c_int, []),
+    "pkv_status_string": (C.c_char_p, [C.c_int]),
+    "pkv_last_error": (C.c_char_p, []),
+    "pkv_build_arch": (C.c_char_p, []),
+    "kv_pool_bytes": (C.c_int, [C.POINTER(PoolDesc), C.POINTER(C.c_size_t), C.POINTER(C.c_size_t)]),
+    "kv_pool_create": (C.c_int, [C.POINTER(PoolDesc), C.c_void_p, C.c_void_p, C.POINTER(C.c_void_p)]),
+    "kv_pool_destroy": (C.c_int, [C.c_void_p]),
+    "kv_pool_padding_page": (C.c_int32, [C.c_void_p]),
+    "kv_pool_token_bytes": (C.c_int64, [C.c_void_p]),
+    "kv_store": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p]),
+    "build_kv_indices": (C.c_int, [C.c_int32, C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p,
+                                   C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p,
+                                   C.c_void_p]),
+    "paged_decode_workspace_bytes": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32,
+                                               C.POINTER(C.c_size_t)]),
+    "paged_decode_attn": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.POINTER(KVMapStruct), C.c_float,
+                                    C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "paged_extend_attn": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
+                                    C.POINTER(KVMapStruct), C.c_int32, C.c_float, C.c_void_p, C.c_void_p,
+                                    C.c_void_p]),
+    "kv_gather": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(KVMapStruct), C.c_void_p, C.c_void_p, C.c_void_p,
+                            C.c_int64, C.c_void_p]),
+    "kv_validate": (C.c_int, [C.c_void_p, C.POINTER(KVMapStruct), C.c_void_p, C.c_void_p,
+                              C.POINTER(C.c_int64), C.c_void_p]),
+    "pkv_set_kernel_timer": (C.c_int, [C.c_void_p, C.c_void_p]),
+}
+
+_lib = None
+
+
+def load() -> C.CDLL:
+    """Load ``libpagedkv.so`` once; raise if it is missing or incomplete."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build the HIP library first (python -m paged_kv_cache_38_amd.build). "
+            "There is no fallback path.")
+    lib = C.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)  # AttributeError if the symbol is not exported
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        lib = load()
+        msg = lib.pkv_last_error().decode() or lib.pkv_status_string(status).decode()
+        super().__init__(f"{call} failed with status {status} ({lib.pkv_status_string(status).decode()}): {msg}")
+        self.status = status
+
+
+def check(status: int, call: str) -> None:
+    if status != PKV_OK:
+        raise PagedKVError(status, call)

@@ -1,0 +1,400 @@
+// The C ABI (include/pagedkv.h): argument validation, descriptor checks and
+// dispatch to the kernel launchers.  No device allocation, no host sync
+// (except kv_validate, which is documented as synchronising).
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+#include <string>
+
+#include "../../include/pagedkv.h"
+#include "pkv_launch.h"
+
+struct pkv_pool {
+  pkv_pool_desc desc;
+  pkv::PoolInfo info;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+thread_local hipEvent_t g_timer_start = nullptr;
+thread_local hipEvent_t g_timer_stop = nullptr;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() { return PKV_OK; }
+
+int device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return PKV_OK;
+  return fail(PKV_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
+int32_t ilog2(int32_t x) {
+  int32_t s = 0;
+  while ((1 << s) < x) ++s;
+  return s;
+}
+
+int check_desc(const pkv_pool_desc* d) {
+  if (!d) return fail(PKV_EINVAL, "null pool descriptor");
+  if (d->num_layers <= 0 || d->num_pages < 0 || d->num_kv_heads <= 0 || d->head_dim_qk <= 0 || d->head_dim_v <= 0)
+    return fail(PKV_EINVAL, "pool dims must be positive (layers %d, pages %d, kv_heads %d, dims %d/%d)",
+                d->num_layers, d->num_pages, d->num_kv_heads, d->head_dim_qk, d->head_dim_v);
+  if (!pow2(d->page_size) || d->page_size > 128)
+    return fail(PKV_EUNSUPPORTED, "page_size %d: must be a power of two in [1, 128]", d->page_size);
+  if (d->dtype != PKV_DTYPE_F32 && d->dtype != PKV_DTYPE_BF16) return fail(PKV_EUNSUPPORTED, "dtype %d", d->dtype);
+  if (d->kind == PKV_KIND_SPLIT_KV) {
+    if (d->head_dim_qk != d->head_dim_v)
+      return fail(PKV_EINVAL, "split K/V pool needs head_dim_qk == head_dim_v (%d vs %d)", d->head_dim_qk,
+                  d->head_dim_v);
+  } else if (d->kind == PKV_KIND_LATENT) {
+    if (d->head_dim_v > d->head_dim_qk) return fail(PKV_EINVAL, "latent pool needs head_dim_v <= head_dim_qk");
+  } else {
+    return fail(PKV_EUNSUPPORTED, "pool kind %d", d->kind);
+  }
+  const int eb = d->dtype == PKV_DTYPE_F32 ? 4 : 2;
+  if (((int64_t)d->num_kv_heads * d->head_dim_qk * eb) % 16 != 0 ||
+      ((int64_t)d->num_kv_heads * d->head_dim_v * eb) % 16 != 0)
+    return fail(PKV_EUNSUPPORTED, "token rows must be a multiple of 16 bytes");
+  return PKV_OK;
+}
+
+void fill_info(const pkv_pool_desc* d, void* k, void* v, pkv::PoolInfo* p) {
+  p->num_layers = d->num_layers;
+  p->num_pages = d->num_pages;
+  p->page_size = d->page_size;
+  p->page_shift = ilog2(d->page_size);
+  p->num_kv_heads = d->num_kv_heads;
+  p->head_dim_qk = d->head_dim_qk;
+  p->head_dim_v = d->head_dim_v;
+  p->dtype = d->dtype;
+  p->kind = d->kind;
+  p->elem_bytes = d->dtype == PKV_DTYPE_F32 ? 4 : 2;
+  p->k_base = static_cast<char*>(k);
+  p->v_base = static_cast<char*>(v);
+  p->num_slots = ((int64_t)d->num_pages + 1) * d->page_size;
+  p->pad_slot = (int64_t)d->num_pages * d->page_size;
+  p->k_row_bytes = (int64_t)d->num_kv_heads * d->head_dim_qk * p->elem_bytes;
+  p->v_row_bytes = d->kind == PKV_KIND_LATENT ? 0 : (int64_t)d->num_kv_heads * d->head_dim_v * p->elem_bytes;
+  p->k_layer_bytes = p->num_slots * p->k_row_bytes;
+  p->v_layer_bytes = p->num_slots * p->v_row_bytes;
+}
+
+int check_pool(const pkv_pool* pool) {
+  if (!pool) return fail(PKV_EINVAL, "null pool handle");
+  return PKV_OK;
+}
+
+int check_layer(const pkv_pool* pool, int32_t layer) {
+  if (layer < 0 || layer >= pool->desc.num_layers)
+    return fail(PKV_EINVAL, "layer %d outside [0, %d)", layer, pool->desc.num_layers);
+  return PKV_OK;
+}
+
+// Validate a kv map's host-visible fields and turn it into the device view.
+int make_devmap(const pkv_pool* pool, const pkv_kv_map* m, bool allow_contiguous, pkv::DevMap* out) {
+  if (!m) return fail(PKV_EINVAL, "null kv map");
+  if (m->bs < 0 || m->max_kv_len < 0) return fail(PKV_EINVAL, "negative bs or max_kv_len");
+  if (m->bs > 0 && !m->kv_lens) return fail(PKV_EINVAL, "null kv_lens");
+  memset(out, 0, sizeof(*out));
+  out->fmt = m->fmt;
+  out->page_shift = pool->info.page_shift;
+  out->kv_lens = m->kv_lens;
+  out->num_slots = pool->info.num_slots;
+  out->pad_slot = pool->info.pad_slot;
+  switch (m->fmt) {
+    case PKV_MAP_TOKEN_TABLE:
+      if (m->bs > 0 && (!m->req_to_token || !m->req_pool_indices))
+        return fail(PKV_EINVAL, "token table map needs req_to_token and req_pool_indices");
+      if (m->table_rows <= 0 || m->table_width <= 0) return fail(PKV_EINVAL, "token table dims must be positive");
+      out->req_to_token = m->req_to_token;
+      out->table_rows = m->table_rows;
+      out->table_width = m->table_width;
+      out->req_pool_indices = m->req_pool_indices;
+      out->kv_start = m->kv_start;
+      break;
+    case PKV_MAP_CSR:
+      if (m->bs > 0 && (!m->kv_indptr || !m->kv_indices)) return fail(PKV_EINVAL, "CSR map needs kv_indptr, kv_indices");
+      if (m->kv_indices_len < 0) return fail(PKV_EINVAL, "negative kv_indices_len");
+      out->kv_indptr = m->kv_indptr;
+      out->kv_indices = m->kv_indices;
+      out->kv_indices_len = m->kv_indices_len;
+      break;
+    case PKV_MAP_BLOCK_TABLE: {
+      if (m->bs > 0 && !m->block_table) return fail(PKV_EINVAL, "block table map needs block_table");
+      const int64_t need = ((int64_t)m->max_kv_len + pool->desc.page_size - 1) / pool->desc.page_size;
+      if (m->block_stride < need)
+        return fail(PKV_ECAPACITY, "block_stride %lld < ceil(max_kv_len / page_size) = %lld",
+                    (long long)m->block_stride, (long long)need);
+      out->block_table = m->block_table;
+      out->block_stride = m->block_stride;
+      break;
+    }
+    case PKV_MAP_CONTIGUOUS:
+      if (!allow_contiguous) return fail(PKV_EUNSUPPORTED, "contiguous map not accepted by this call");
+      if (m->bs > 0 && (!m->k || !m->cu_seqlens_k)) return fail(PKV_EINVAL, "contiguous map needs k and cu_seqlens_k");
+      if (pool->desc.kind == PKV_KIND_SPLIT_KV && m->bs > 0 && !m->v) return fail(PKV_EINVAL, "contiguous map needs v");
+      if (m->total_k < 0) return fail(PKV_EINVAL, "negative total_k");
+      if (!aligned16(m->k) || !aligned16(m->v)) return fail(PKV_EALIGN, "contiguous k/v not 16-byte aligned");
+      out->cu_seqlens_k = m->cu_seqlens_k;
+      out->total_k = m->total_k;
+      out->num_slots = m->total_k;
+      out->pad_slot = 0;
+      break;
+    default:
+      return fail(PKV_EINVAL, "unknown map format %d", m->fmt);
+  }
+  return PKV_OK;
+}
+
+}  // namespace
+
+namespace pkv {
+void timer_before(hipStream_t s) {
+  if (g_timer_start) (void)hipEventRecord(g_timer_start, s);
+}
+void timer_after(hipStream_t s) {
+  if (g_timer_stop) (void)hipEventRecord(g_timer_stop, s);
+  g_timer_start = nullptr;
+  g_timer_stop = nullptr;
+}
+}  // namespace pkv
+
+extern "C" {
+
+int pkv_abi_version(void) { return PKV_ABI_VERSION; }
+
+const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_EINVAL: return "invalid argument";
+    case PKV_EUNSUPPORTED: return "unsupported configuration";
+    case PKV_EALIGN: return "misaligned pointer or kv_start";
+    case PKV_ECAPACITY: return "capacity or workspace too small";
+    case PKV_EDEVICE: return "device error";
+    default: return "unknown status";
+  }
+}
+
+const char* pkv_last_error(void) { return g_last_error.c_str(); }
+
+const char* pkv_build_arch(void) { return "gfx950"; }
+
+int kv_pool_bytes(const pkv_pool_desc* desc, size_t* k_bytes, size_t* v_bytes) {
+  int st = check_desc(desc);
+  if (st) return st;
+  if (!k_bytes || !v_bytes) return fail(PKV_EINVAL, "null output pointer");
+  pkv::PoolInfo p;
+  fill_info(desc, nullptr, nullptr, &p);
+  *k_bytes = (size_t)p.k_layer_bytes * desc->num_layers;
+  *v_bytes = (size_t)p.v_layer_bytes * desc->num_layers;
+  return ok();
+}
+
+int kv_pool_create(const pkv_pool_desc* desc, void* k_base, void* v_base, pkv_pool** out) {
+  int st = check_desc(desc);
+  if (st) return st;
+  if (!out) return fail(PKV_EINVAL, "null output handle");
+  if (!k_base) return fail(PKV_EINVAL, "null k_base");
+  if (desc->kind == PKV_KIND_SPLIT_KV && !v_base) return fail(PKV_EINVAL, "null v_base for a split K/V pool");
+  if (desc->kind == PKV_KIND_LATENT && v_base) return fail(PKV_EINVAL, "latent pool takes no v_base");
+  if (!aligned16(k_base) || !aligned16(v_base)) return fail(PKV_EALIGN, "pool buffers must be 16-byte aligned");
+  pkv_pool* p = new (std::nothrow) pkv_pool;
+  if (!p) return fail(PKV_EINVAL, "out of host memory");
+  p->desc = *desc;
+  fill_info(desc, k_base, v_base, &p->info);
+  *out = p;
+  return ok();
+}
+
+int kv_pool_destroy(pkv_pool* pool) {
+  delete pool;
+  return ok();
+}
+
+int32_t kv_pool_padding_page(const pkv_pool* pool) {
+  if (int st = check_pool(pool)) return st;
+  return pool->desc.num_pages;
+}
+
+int64_t kv_pool_token_bytes(const pkv_pool* pool) {
+  if (int st = check_pool(pool)) return st;
+  return pool->info.k_row_bytes + pool->info.v_row_bytes;
+}
+
+int kv_store(const pkv_pool* pool, int32_t layer, const void* k, const void* v, const int32_t* out_loc, int64_t n,
+             void* stream) {
+  if (int st = check_pool(pool)) return st;
+  if (int st = check_layer(pool, layer)) return st;
+  if (n < 0) return fail(PKV_EINVAL, "negative n");
+  if (n == 0) return ok();
+  if (!k || !out_loc) return fail(PKV_EINVAL, "null k or out_loc");
+  if (pool->desc.kind == PKV_KIND_SPLIT_KV && !v) return fail(PKV_EINVAL, "null v for a split K/V pool");
+  if (pool->desc.kind == PKV_KIND_LATENT) v = nullptr;
+  if (!aligned16(k) || !aligned16(v)) return fail(PKV_EALIGN, "k/v must be 16-byte aligned");
+  return device_status(pkv::launch_store(pool->info, layer, k, v, out_loc, n, (hipStream_t)stream), "kv_store");
+}
+
+int build_kv_indices(int32_t out_fmt, const int32_t* req_to_token, int64_t table_rows, int64_t table_width,
+                     const int32_t* req_pool_indices, const int32_t* kv_start, const int32_t* kv_lens, int32_t bs,
+                     int32_t page_size, int32_t max_kv_len, int32_t* kv_indptr, int32_t* out, int64_t capacity,
+                     int32_t* kv_last_page_len, void* stream) {
+  if (out_fmt != PKV_MAP_CSR && out_fmt != PKV_MAP_BLOCK_TABLE)
+    return fail(PKV_EINVAL, "out_fmt must be CSR or BLOCK_TABLE");
+  if (bs < 0 || max_kv_len < 0 || capacity < 0) return fail(PKV_EINVAL, "negative bs, max_kv_len or capacity");
+  if (!pow2(page_size) || page_size > 128) return fail(PKV_EUNSUPPORTED, "page_size %d", page_size);
+  if (out_fmt == PKV_MAP_CSR && !kv_indptr) return fail(PKV_EINVAL, "CSR output needs kv_indptr");
+  if (bs > 0 && (!req_to_token || !req_pool_indices || !kv_lens || !out))
+    return fail(PKV_EINVAL, "null table, indices, lengths or output");
+  if (table_rows <= 0 || table_width <= 0) return fail(PKV_EINVAL, "token table dims must be positive");
+  const int64_t per_req = ((int64_t)max_kv_len + page_size - 1) / page_size;
+  if (out_fmt == PKV_MAP_CSR && capacity < per_req * bs)
+    return fail(PKV_ECAPACITY, "kv_indices capacity %lld < bs * ceil(max_kv_len / page_size) = %lld",
+                (long long)capacity, (long long)(per_req * bs));
+  if (out_fmt == PKV_MAP_BLOCK_TABLE && capacity < per_req)
+    return fail(PKV_ECAPACITY, "block table stride %lld < ceil(max_kv_len / page_size) = %lld", (long long)capacity,
+                (long long)per_req);
+  return device_status(pkv::launch_build_indices(out_fmt, req_to_token, table_rows, table_width, req_pool_indices,
+                                                  kv_start, kv_lens, bs, ilog2(page_size), kv_indptr, out, capacity,
+                                                  kv_last_page_len, (hipStream_t)stream),
+                       "build_kv_indices");
+}
+
+int paged_decode_workspace_bytes(const pkv_pool* pool, int32_t bs, int32_t num_q_heads, int32_t max_kv_len,
+                                 size_t* bytes) {
+  if (int st = check_pool(pool)) return st;
+  if (!bytes || bs < 0 || max_kv_len < 0 || num_q_heads <= 0) return fail(PKV_EINVAL, "bad workspace query");
+  if (!pkv::decode_supported(pool->info, num_q_heads))
+    return fail(PKV_EUNSUPPORTED, "no decode kernel for this pool (dtype %d, dims %d/%d, %d q heads over %d kv heads)",
+                pool->desc.dtype, pool->desc.head_dim_qk, pool->desc.head_dim_v, num_q_heads,
+                pool->desc.num_kv_heads);
+  const pkv::DecodePlan plan = pkv::plan_decode(pool->info, bs, num_q_heads, max_kv_len);
+  *bytes = pkv::decode_workspace_bytes(pool->info, plan, bs, num_q_heads);
+  return ok();
+}
+
+int paged_decode_attn(const pkv_pool* pool, int32_t layer, const void* q, int32_t num_q_heads, const pkv_kv_map* map,
+                      float sm_scale, void* out, float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  if (int st = check_pool(pool)) return st;
+  if (int st = check_layer(pool, layer)) return st;
+  pkv::DevMap dm;
+  if (int st = make_devmap(pool, map, false, &dm)) return st;
+  if (num_q_heads <= 0 || num_q_heads % pool->desc.num_kv_heads != 0)
+    return fail(PKV_EINVAL, "num_q_heads %d not a positive multiple of num_kv_heads %d", num_q_heads,
+                pool->desc.num_kv_heads);
+  if (!pkv::decode_supported(pool->info, num_q_heads))
+    return fail(PKV_EUNSUPPORTED, "no decode kernel for this pool (dtype %d, dims %d/%d, %d q heads over %d kv heads)",
+                pool->desc.dtype, pool->desc.head_dim_qk, pool->desc.head_dim_v, num_q_heads,
+                pool->desc.num_kv_heads);
+  if (map->bs == 0) return ok();
+  if (!q || !out) return fail(PKV_EINVAL, "null q or out");
+  if (!aligned16(q)) return fail(PKV_EALIGN, "q must be 16-byte aligned");
+  const pkv::DecodePlan plan = pkv::plan_decode(pool->info, map->bs, num_q_heads, map->max_kv_len);
+  const size_t need = pkv::decode_workspace_bytes(pool->info, plan, map->bs, num_q_heads);
+  if (ws_bytes < need) return fail(PKV_ECAPACITY, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  if (need > 0 && (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)))
+    return fail(PKV_EALIGN, "workspace must be non-null and 256-byte aligned");
+  return device_status(pkv::launch_decode(pool->info, layer, q, num_q_heads, dm, map->bs, plan, sm_scale, out, lse,
+                                          workspace, (hipStream_t)stream),
+                       "paged_decode_attn");
+}
+
+int paged_extend_attn(const pkv_pool* pool, int32_t layer, const void* q, const int32_t* qo_indptr,
+                      int32_t num_q_heads, int32_t max_q_len, const pkv_kv_map* map, int32_t causal, float sm_scale,
+                      void* out, float* lse, void* stream) {
+  if (int st = check_pool(pool)) return st;
+  if (int st = check_layer(pool, layer)) return st;
+  pkv::DevMap dm;
+  if (int st = make_devmap(pool, map, true, &dm)) return st;
+  if (num_q_heads <= 0 || num_q_heads % pool->desc.num_kv_heads != 0)
+    return fail(PKV_EINVAL, "num_q_heads %d not a positive multiple of num_kv_heads %d", num_q_heads,
+                pool->desc.num_kv_heads);
+  if (max_q_len < 0) return fail(PKV_EINVAL, "negative max_q_len");
+  if (!pkv::extend_supported(pool->info, num_q_heads))
+    return fail(PKV_EUNSUPPORTED, "no extend kernel for this pool (dtype %d, dims %d/%d)", pool->desc.dtype,
+                pool->desc.head_dim_qk, pool->desc.head_dim_v);
+  if (map->bs == 0 || max_q_len == 0) return ok();
+  if (!q || !out || !qo_indptr) return fail(PKV_EINVAL, "null q, out or qo_indptr");
+  if (!aligned16(q)) return fail(PKV_EALIGN, "q must be 16-byte aligned");
+  return device_status(pkv::launch_extend(pool->info, layer, q, qo_indptr, num_q_heads, max_q_len, dm, map->bs,
+                                          map->max_kv_len, causal, sm_scale, out, lse, (hipStream_t)stream),
+                       "paged_extend_attn");
+}
+
+int kv_gather(const pkv_pool* pool, int32_t layer, const pkv_kv_map* map, const int32_t* cu_seqlens_k, void* k_out,
+              void* v_out, int64_t out_rows, void* stream) {
+  if (int st = check_pool(pool)) return st;
+  if (int st = check_layer(pool, layer)) return st;
+  pkv::DevMap dm;
+  if (int st = make_devmap(pool, map, false, &dm)) return st;
+  if (out_rows < 0) return fail(PKV_EINVAL, "negative out_rows");
+  if (map->bs == 0) return ok();
+  if (!cu_seqlens_k || !k_out) return fail(PKV_EINVAL, "null cu_seqlens_k or k_out");
+  if (pool->desc.kind == PKV_KIND_SPLIT_KV && !v_out) return fail(PKV_EINVAL, "null v_out for a split K/V pool");
+  if (pool->desc.kind == PKV_KIND_LATENT) v_out = nullptr;
+  if (!aligned16(k_out) || !aligned16(v_out)) return fail(PKV_EALIGN, "k_out/v_out must be 16-byte aligned");
+  return device_status(pkv::launch_gather(pool->info, layer, dm, map->bs, map->max_kv_len, cu_seqlens_k, k_out, v_out,
+                                          out_rows, (hipStream_t)stream),
+                       "kv_gather");
+}
+
+int kv_validate(const pkv_pool* pool, const pkv_kv_map* map, const int32_t* is_dummy, int64_t* scratch,
+                int64_t counts[8], void* stream) {
+  if (int st = check_pool(pool)) return st;
+  pkv::DevMap dm;
+  if (int st = make_devmap(pool, map, false, &dm)) return st;
+  if (!counts) return fail(PKV_EINVAL, "null counts");
+  for (int k = 0; k < 8; ++k) counts[k] = 0;
+  if (map->bs == 0) return ok();
+  if (!scratch) return fail(PKV_EINVAL, "null scratch");
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = pkv::launch_validate(pool->info, dm, map->bs, map->max_kv_len, is_dummy,
+                                      reinterpret_cast<long long*>(scratch), s);
+  if (e != hipSuccess) return device_status(e, "kv_validate launch");
+  const size_t n = (size_t)map->bs * 8;
+  long long* host = new (std::nothrow) long long[n];
+  if (!host) return fail(PKV_EINVAL, "out of host memory");
+  e = hipMemcpyAsync(host, scratch, n * sizeof(long long), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    delete[] host;
+    return device_status(e, "kv_validate copy");
+  }
+  for (size_t r = 0; r < (size_t)map->bs; ++r)
+    for (int k = 0; k < 8; ++k) counts[k] += host[r * 8 + k];
+  delete[] host;
+  bool any = false, only_align = true;
+  for (int k = 0; k < 8; ++k) {
+    if (counts[k]) {
+      any = true;
+      if (k != 3) only_align = false;
+    }
+  }
+  if (!any) return ok();
+  if (only_align) return fail(PKV_EALIGN, "kv_start not a multiple of page_size for %lld requests", (long long)counts[3]);
+  return fail(PKV_EINVAL, "map violations: range %lld, padding %lld, neg %lld, align %lld, contig %lld, len %lld",
+              (long long)counts[0], (long long)counts[1], (long long)counts[2], (long long)counts[3],
+              (long long)counts[4], (long long)counts[5]);
+}
+
+int pkv_set_kernel_timer(void* start_event, void* stop_event) {
+  if ((start_event == nullptr) != (stop_event == nullptr)) return fail(PKV_EINVAL, "pass both events or neither");
+  g_timer_start = static_cast<hipEvent_t>(start_event);
+  g_timer_stop = static_cast<hipEvent_t>(stop_event);
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,143 @@
+// Device-side building blocks shared by the paged KV-cache kernels (gfx950).
+//
+// Sources, cited by short name:
+//   [XPU]     "Enabling Encoder-Decoder Models on Intel XPU in SGLang: A KV-Cache Story"
+//   [OMNI]    "Scheduler-Managed Paged KV Cache" (vLLM-Omni design documents)
+//   [MINI]    "The KV pool, the page table and the token pool" (mini-sglang from Scratch)
+//   [BACKEND] "AttentionBackend" (SGLang FlashInfer-MLA / FlashMLA backend notes)
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+enum MapFmt : int32_t { MAP_TOKEN_TABLE = 0, MAP_CSR = 1, MAP_BLOCK_TABLE = 2, MAP_CONTIGUOUS = 3 };
+
+// How a request's logical token t reaches its slot in the per-token pool view
+// (the [XPU] "From slots to a page table" formula for page-granular tables,
+// a direct read of the token-granular req_to_token row otherwise).
+struct DevMap {
+  int32_t fmt;
+  int32_t page_shift;  // log2(page_size)
+  const int32_t* kv_lens;
+  // token table
+  const int32_t* req_to_token;
+  int64_t table_width;  // columns == row stride (row-major)
+  int64_t table_rows;
+  const int32_t* req_pool_indices;
+  const int32_t* kv_start;  // may be null (all zero)
+  // CSR
+  const int32_t* kv_indptr;
+  const int32_t* kv_indices;
+  int64_t kv_indices_len;
+  // padded block table
+  const int32_t* block_table;
+  int64_t block_stride;
+  // contiguous (gathered) K/V
+  const int32_t* cu_seqlens_k;
+  int64_t total_k;
+  // pool bounds: any resolved slot outside [0, num_slots) reads pad_slot
+  int64_t num_slots;
+  int64_t pad_slot;
+};
+
+// Per-request resolver, built once per workgroup and kept in registers.
+// Every index read from a table is range-checked: an out-of-range entry is
+// read as the padding slot (memory-safe; the result for that request is
+// then unspecified).
+struct Resolver {
+  const int32_t* base;  // token-table row (+kv_start) or page list
+  int64_t limit;        // readable entries at base
+  int64_t off;          // contiguous: first row of this request
+  int64_t num_slots, pad_slot;
+  int32_t fmt, shift, mask;
+
+  __device__ __forceinline__ int64_t slot(int32_t t) const {
+    int64_t s;
+    if (fmt == MAP_CONTIGUOUS) {
+      s = off + t;
+    } else if (fmt == MAP_TOKEN_TABLE) {
+      s = (t < limit) ? (int64_t)base[t] : pad_slot;
+    } else {
+      int32_t pi = t >> shift;
+      int64_t page = (pi < limit) ? (int64_t)base[pi] : -1;
+      s = (page < 0) ? pad_slot : ((page << shift) + (t & mask));
+    }
+    return ((uint64_t)s < (uint64_t)num_slots) ? s : pad_slot;
+  }
+};
+
+__device__ __forceinline__ Resolver make_resolver(const DevMap& m, int32_t i) {
+  Resolver r;
+  r.fmt = m.fmt;
+  r.shift = m.page_shift;
+  r.mask = (1 << m.page_shift) - 1;
+  r.num_slots = m.num_slots;
+  r.pad_slot = m.pad_slot;
+  r.off = 0;
+  r.base = nullptr;
+  r.limit = 0;
+  if (m.fmt == MAP_TOKEN_TABLE) {
+    int64_t row = m.req_pool_indices[i];
+    int64_t start = m.kv_start ? (int64_t)m.kv_start[i] : 0;
+    if (row >= 0 && row < m.table_rows && start >= 0 && start <= m.table_width) {
+      r.base = m.req_to_token + row * m.table_width + start;
+      r.limit = m.table_width - start;
+    }
+  } else if (m.fmt == MAP_CSR) {
+    int64_t a = m.kv_indptr[i], b = m.kv_indptr[i + 1];
+    if (a >= 0 && b >= a && b <= m.kv_indices_len) {
+      r.base = m.kv_indices + a;
+      r.limit = b - a;
+    }
+  } else if (m.fmt == MAP_BLOCK_TABLE) {
+    r.base = m.block_table + (int64_t)i * m.block_stride;
+    r.limit = m.block_stride;
+  } else {
+    r.off = m.cu_seqlens_k[i];
+    r.num_slots = m.total_k;
+    r.pad_slot = 0;
+  }
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// small numeric helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// xor-shuffle across the wavefront (ds_bpermute)
+__device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+__device__ __forceinline__ float shfl(float v, int src) { return __shfl(v, src, 64); }
+
+__device__ __forceinline__ int32_t wave_lane() { return (int32_t)__lane_id(); }
+
+// MFMA 16x16x32 bf16 -> f32 (gfx950).  Lane l supplies A[l%16][8*(l/16) .. +8]
+// and B[8*(l/16) .. +8][l%16]; it receives D[4*(l/16) + r][l%16], r = 0..3.
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ u32x4 as_u32x4(bf16x8 v) { return __builtin_bit_cast(u32x4, v); }
+
+}  // namespace pkv

@@ -1,0 +1,73 @@
+// Host-side launch interface between the C ABI (pkv_api.hip) and the kernel
+// translation units.  Internal to the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "pkv_device.h"
+
+namespace pkv {
+
+// Everything a launcher needs to know about the pool, resolved once by
+// kv_pool_create.
+struct PoolInfo {
+  int32_t num_layers, num_pages, page_size, page_shift;
+  int32_t num_kv_heads, head_dim_qk, head_dim_v;
+  int32_t dtype;  // 0 f32, 1 bf16
+  int32_t kind;   // 0 split K/V, 1 latent
+  int32_t elem_bytes;
+  char* k_base;
+  char* v_base;  // null for latent
+  int64_t num_slots;   // (num_pages + 1) * page_size
+  int64_t pad_slot;    // num_pages * page_size
+  int64_t k_row_bytes;  // one token, all KV heads
+  int64_t v_row_bytes;
+  int64_t k_layer_bytes;
+  int64_t v_layer_bytes;
+
+  const char* k_layer(int32_t layer) const { return k_base + (int64_t)layer * k_layer_bytes; }
+  const char* v_layer(int32_t layer) const { return v_base ? v_base + (int64_t)layer * v_layer_bytes : nullptr; }
+};
+
+// Kernel timer hook (pkv_set_kernel_timer): launchers call these around the
+// main attention kernel.
+void timer_before(hipStream_t s);
+void timer_after(hipStream_t s);
+
+hipError_t launch_store(const PoolInfo& p, int32_t layer, const void* k, const void* v, const int32_t* out_loc,
+                        int64_t n, hipStream_t s);
+
+hipError_t launch_gather(const PoolInfo& p, int32_t layer, const DevMap& m, int32_t bs, int32_t max_kv_len,
+                         const int32_t* cu_seqlens_k, void* k_out, void* v_out, int64_t out_rows, hipStream_t s);
+
+hipError_t launch_build_indices(int32_t out_fmt, const int32_t* req_to_token, int64_t table_rows,
+                                int64_t table_width, const int32_t* req_pool_indices, const int32_t* kv_start,
+                                const int32_t* kv_lens, int32_t bs, int32_t page_shift, int32_t* kv_indptr,
+                                int32_t* out, int64_t capacity, int32_t* kv_last_page_len, hipStream_t s);
+
+// Split plan for decode: chunk of logical tokens per split and the number
+// of split slots reserved per request in the workspace.
+struct DecodePlan {
+  int32_t chunk;
+  int32_t max_splits;
+  int32_t kind;  // which kernel family
+};
+DecodePlan plan_decode(const PoolInfo& p, int32_t bs, int32_t num_q_heads, int32_t max_kv_len);
+size_t decode_workspace_bytes(const PoolInfo& p, const DecodePlan& plan, int32_t bs, int32_t num_q_heads);
+bool decode_supported(const PoolInfo& p, int32_t num_q_heads);
+
+hipError_t launch_decode(const PoolInfo& p, int32_t layer, const void* q, int32_t num_q_heads, const DevMap& m,
+                         int32_t bs, const DecodePlan& plan, float sm_scale, void* out, float* lse, void* ws,
+                         hipStream_t s);
+
+bool extend_supported(const PoolInfo& p, int32_t num_q_heads);
+hipError_t launch_extend(const PoolInfo& p, int32_t layer, const void* q, const int32_t* qo_indptr,
+                         int32_t num_q_heads, int32_t max_q_len, const DevMap& m, int32_t bs, int32_t max_kv_len,
+                         int32_t causal, float sm_scale, void* out, float* lse, hipStream_t s);
+
+hipError_t launch_validate(const PoolInfo& p, const DevMap& m, int32_t bs, int32_t max_kv_len,
+                           const int32_t* is_dummy, long long* counts_dev, hipStream_t s);
+
+}  // namespace pkv
