@@ -8,7 +8,7 @@
 #include <new>
 #include <string>
 
-#include "../../include/pagedkv.h"
+#include "pagedkv.h"
 #include "pkv_launch.h"
 
 struct pkv_pool {

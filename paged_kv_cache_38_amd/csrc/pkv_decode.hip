@@ -1,5 +1,5 @@
-// Paged decode attention for grouped-query heads: split-K partial kernels and
-// the log-sum-exp merge.
+// Paged decode attention for grouped-query heads: the split plan, the
+// split-K partial kernels and the log-sum-exp merge.
 //
 // What is computed ([XPU] "From slots to a page table"; [BACKEND]
 // init_forward_metadata with its per-request split count): one new query per
@@ -10,76 +10,281 @@
 // boundaries depend only on logical positions, never on where pages live, so
 // moving pages around cannot change a single bit of the output.
 //
-// Layout on gfx950 (pool: [slots][Hkv][D], token-major):
-//   block   = WAVES wavefronts of one (split, request); wave w owns KV head
-//             g = blockIdx.z * WAVES + w and its G = Hq / Hkv query heads.
-//   bf16:   S^T[16 tokens x 16 heads] = K_tile[16 x D] * Q^T[D x 16] with
-//           v_mfma_f32_16x16x32_bf16 (tokens as M so that K loads straight
-//           from HBM into the A operand: lane (t = l%16, j = l/16) reads D/4
-//           contiguous elements of token t's head slice); the softmax runs on
-//           the MFMA output registers; P (16 heads x 32 tokens) is already in
-//           the A-operand layout of the PV product; V goes through LDS so each
-//           lane can pick the 8 tokens of one d column the B operand needs.
-//   f32 (and bf16 without MFMA): VALU dot products, 16 lanes per token.
+// Work distribution on gfx950: a one-block planner kernel lists the live
+// (request, split) items in request order; block b of the split kernel takes
+// item b / hg and KV-head group b % hg.  The hardware hands consecutive
+// blocks to the 8 XCDs round robin, so every XCD gets an equal share of live
+// items (empty splits of short requests never occupy a slot), and the head
+// groups of one item run side by side, reading whole token rows.
+//
+// Split kernel, bf16 (pool [slots][Hkv][D], token-major):
+//   block   = WAVES wavefronts of one item; wave w owns KV head
+//             g = (b % hg) * WAVES + w and its G = Hq / Hkv query heads.
+//   S^T[16 tokens x 16 heads] = K_tile[16 x D] * Q^T[D x 16] on
+//   v_mfma_f32_16x16x32_bf16 (tokens as M, so K rows load from HBM straight
+//   into A-operand registers); softmax on the MFMA output registers; P
+//   (16 heads x 32 tokens) is already the A operand of the PV product; V
+//   goes through LDS and comes back transposed with ds_read_b64_tr_b16, four
+//   tokens of one d column per lane per read.
+// Split kernel, f32: VALU dot products, 16 lanes per token.
 #include <math.h>
 
 #include "pkv_launch.h"
 
 namespace pkv {
 
-constexpr int kTile = 32;  // tokens per inner iteration of the MFMA kernel
+constexpr int kTile = 32;          // tokens per inner iteration of the MFMA kernel
+constexpr int kMaxSplits = 1024;   // per request; item = request * kMaxSplits + split
+constexpr int kItemShift = 10;
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Transposed LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane j supplies the address of 4 consecutive 16-bit values (call
+// them M[j][0..3]); lane i receives M[i/4 + 4r][i%4] for r = 0..3.
+__device__ __forceinline__ i16x4 lds_read_tr16(const bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
+// ---------------------------------------------------------------------------
+// split plan: live items in request order; an empty request still gets one
+// item, which writes its zero output and -inf lse.  Each item carries what a
+// split needs to start streaming at once (its request's table view and key
+// range), so the split kernel's first dependent loads are the table entries.
+// ---------------------------------------------------------------------------
+struct __attribute__((aligned(16))) WorkItem {
+  int32_t i;      // request
+  int32_t s;      // split
+  int32_t ns;     // splits of request i (0: empty request)
+  int32_t t_end;  // exclusive end of the split's keys (it starts at s * chunk)
+  int32_t limit;  // readable table entries (0: malformed row, read as padding)
+  int32_t off_lo, off_hi;  // element offset of the request's table row / page list
+  int32_t pad;
+};
+
+__global__ void __launch_bounds__(1024) decode_plan_kernel(DevMap m, int32_t bs, int32_t chunk, int32_t max_splits,
+                                                           WorkItem* __restrict__ items, int32_t* __restrict__ count) {
+  __shared__ int32_t wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int32_t carry = 0;
+  for (int32_t base = 0; base < bs; base += 1024) {
+    const int32_t i = base + tid;
+    int32_t n = 0, L = 0;
+    if (i < bs) {
+      L = m.kv_lens[i];
+      n = L > 0 ? min((L + chunk - 1) / chunk, max_splits) : 1;
+    }
+    int32_t x = n;  // inclusive wave scan
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int32_t y = __shfl_up(x, d, 64);
+      if (lane >= d) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    if (wave == 0) {
+      int32_t w = lane < 16 ? wsum[lane] : 0;
+#pragma unroll
+      for (int d = 1; d < 16; d <<= 1) {
+        const int32_t y = __shfl_up(w, d, 64);
+        if (lane >= d) w += y;
+      }
+      if (lane < 16) wsum[lane] = w;  // inclusive over waves
+    }
+    __syncthreads();
+    const int32_t off = carry + (wave > 0 ? wsum[wave - 1] : 0) + x - n;
+    if (n > 0) {
+      const ReqView v = request_view(m, i);
+      const int32_t ns = L > 0 ? n : 0;
+      for (int32_t s = 0; s < n; ++s) {
+        WorkItem w;
+        w.i = i;
+        w.s = s;
+        w.ns = ns;
+        w.t_end = min((s + 1) * chunk, L);
+        w.limit = v.limit;
+        w.off_lo = (int32_t)(v.off & 0xffffffff);
+        w.off_hi = (int32_t)(v.off >> 32);
+        w.pad = 0;
+        items[off + s] = w;
+      }
+    }
+    carry += wsum[15];
+    __syncthreads();
+  }
+  if (tid == 0) *count = carry;
+}
+
+__device__ __forceinline__ ReqView item_view(const WorkItem& w) {
+  ReqView v;
+  v.off = ((int64_t)w.off_hi << 32) | (uint32_t)w.off_lo;
+  v.limit = w.limit;
+  return v;
+}
 
 // ---------------------------------------------------------------------------
 // bf16 MFMA split kernel
+//
+// Per wavefront and 32-token tile: one coalesced load of the tile's 32 slots
+// (lane l -> token t0 + l%32), handed to the lanes that need them by
+// ds_bpermute; K rows go straight into MFMA A-operand registers, V rows into
+// registers.  The slots of tile i+2 and the K/V rows of tile i+1 are in
+// flight while tile i is computed (two register sets, unrolled by hand).
 // ---------------------------------------------------------------------------
-template <int D, int WAVES>
-__global__ void __launch_bounds__(64 * WAVES) decode_mfma_kernel(
-    DevMap m, const bf16* __restrict__ k_pool, const bf16* __restrict__ v_pool, const bf16* __restrict__ q,
-    int32_t Hq, int32_t Hkv, int32_t G, int32_t chunk, int32_t max_splits, float scale_log2,
-    bf16* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws_o, float* __restrict__ ws_lse) {
-  constexpr int NK = D / 32;         // MFMAs along d for S
-  constexpr int DJ = D / 4;          // contiguous K elements per lane group
-  constexpr int NT = D / 16;         // 16-wide d tiles of the PV product
-  constexpr int CPT = D / 8;         // 16-byte chunks per V head slice
-  constexpr int TPI = 64 / CPT;      // tokens per V load instruction
-  constexpr int VIT = kTile / TPI;   // V load instructions per tile
-  constexpr int LDS = D + 8;         // LDS row stride in elements (+16 B pad)
-  __shared__ bf16 vsm[WAVES][kTile * LDS];
+template <int D>
+struct DecodeTile {
+  static constexpr int NK = D / 32;        // MFMAs along d for S
+  static constexpr int CPT = D / 8;        // 16-byte chunks per head slice
+  static constexpr int TPI = 64 / CPT;     // tokens per V load instruction
+  static constexpr int VIT = kTile / TPI;  // V load instructions per tile
+  bf16x8 k[2][NK];
+  u32x4 v[VIT];
+};
 
+template <int D>
+__device__ __forceinline__ void decode_issue(DecodeTile<D>& T, int32_t tile_slot, int lane, const bf16* kb,
+                                             const bf16* vb, int64_t row_elems) {
+  constexpr int NK = DecodeTile<D>::NK, CPT = DecodeTile<D>::CPT, TPI = DecodeTile<D>::TPI;
+  constexpr int VIT = DecodeTile<D>::VIT;
+  const int col = lane & 15, grp = lane >> 4;
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int64_t slot = shfl_i(tile_slot, a * 16 + col);
+    // MFMA kk takes d = kk*32 + grp*8 .. +8: the 4 lanes of a token read 64
+    // contiguous bytes per instruction
+    const bf16* kp = kb + slot * row_elems + grp * 8;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) T.k[a][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(kp + kk * 32));
+  }
+#pragma unroll
+  for (int it = 0; it < VIT; ++it) {
+    const int64_t slot = shfl_i(tile_slot, it * TPI + lane / CPT);
+    T.v[it] = *reinterpret_cast<const u32x4*>(vb + slot * row_elems + (lane % CPT) * 8);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void decode_compute(const DecodeTile<D>& T, int t0, int t_end, int lane, const bf16x8* qb,
+                                               float scale_log2, bf16* vt, f32x4* acc, float& m_run, float& l_run) {
+  constexpr int NK = DecodeTile<D>::NK, CPT = DecodeTile<D>::CPT, TPI = DecodeTile<D>::TPI;
+  constexpr int VIT = DecodeTile<D>::VIT;
+  constexpr int NT = D / 16;
+  constexpr int LDS = D + 8;
+  const int col = lane & 15, grp = lane >> 4;
+  // ---- S^T = K Q^T  (rows: tokens a*16 + 4*grp + rr; column: head col)
+  f32x4 sacc[2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    sacc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) sacc[a] = mfma16x16x32(T.k[a][kk], qb[kk], sacc[a]);
+  }
+  // ---- V tile to LDS; keys past the end hold 0 (P * NaN would poison the sum)
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int it = 0; it < VIT; ++it) {
+    const int row = it * TPI + lane / CPT;
+    const bool ok = t0 + row < t_end;
+    u32x4 w = T.v[it];
+    if (!ok) w = u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(vt + row * LDS + (lane % CPT) * 8) = w;
+  }
+  // ---- online softmax (log2 domain)
+  float sv[2][4];
+  float mt = -INFINITY;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int t = t0 + a * 16 + grp * 4 + rr;
+      const float x = (t < t_end) ? sacc[a][rr] * scale_log2 : -INFINITY;
+      sv[a][rr] = x;
+      mt = fmaxf(mt, x);
+    }
+  mt = fmaxf(mt, shfl_xor(mt, 16));
+  mt = fmaxf(mt, shfl_xor(mt, 32));
+  const float m_new = fmaxf(m_run, mt);
+  const float alpha = fast_exp2(m_run - m_new);  // 0 on the first tile
+  float psum = 0.f;
+  bf16x8 pa;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const float p = fast_exp2(sv[a][rr] - m_new);
+      psum += p;
+      pa[a * 4 + rr] = (bf16)p;
+    }
+  l_run = l_run * alpha + psum;
+  m_run = m_new;
+  // rows of acc are heads 4*grp + rr; their alpha lives in lane 4*grp + rr
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const float ar = shfl(alpha, grp * 4 + rr);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[nt][rr] *= ar;
+  }
+  __builtin_amdgcn_wave_barrier();
+  // ---- O += P V.  B operand of lane (col, grp) = V[a*16 + 4*grp + rr][nt*16 + col]
+  // for a = 0, 1 and rr = 0..3: one transposed read per a, lane j of the group
+  // pointing at token a*16 + 4*grp + j/4, columns nt*16 + 4*(j%4) .. +4.
+  const int j = lane & 15;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const bf16* base = vt + (grp * 4 + (j >> 2)) * LDS + nt * 16 + 4 * (j & 3);
+    const i16x4 lo = lds_read_tr16(base);
+    const i16x4 hi = lds_read_tr16(base + 16 * LDS);
+    const bf16x4 blo = __builtin_bit_cast(bf16x4, lo), bhi = __builtin_bit_cast(bf16x4, hi);
+    const bf16x8 vbop = {blo[0], blo[1], blo[2], blo[3], bhi[0], bhi[1], bhi[2], bhi[3]};
+    acc[nt] = mfma16x16x32(pa, vbop, acc[nt]);
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <int D, int WAVES, int FMT>
+__global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) decode_mfma_kernel(
+    DevMap m, const bf16* k_pool, const bf16* v_pool, const bf16* __restrict__ q,
+    int32_t Hq, int32_t Hkv, int32_t G, int32_t hg, int32_t chunk, int32_t max_splits,
+    const WorkItem* __restrict__ items, const int32_t* __restrict__ item_count, float scale_log2,
+    bf16* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws_o, float* __restrict__ ws_lse) {
+  constexpr int NK = D / 32;
+  constexpr int NT = D / 16;
+  constexpr int LDS = D + 8;  // LDS row stride in elements (+16 B pad)
+  __shared__ __attribute__((aligned(16))) bf16 vsm[WAVES][kTile * LDS];
+
+  const int w_item = blockIdx.x / hg;
+  if (w_item >= *item_count) return;
+  const WorkItem item = items[w_item];
+  const int i = item.i;
+  const int s = item.s;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int s = blockIdx.x;
-  const int i = blockIdx.y;
-  const int g = blockIdx.z * WAVES + wave;
+  const int g = (blockIdx.x % hg) * WAVES + wave;
   const int col = lane & 15;  // head column of S / d column of PV
   const int grp = lane >> 4;  // lane group 0..3
-  const int L = m.kv_lens[i];
+  const int ns = item.ns;
 
-  if (L <= 0) {  // empty key set: zero output, lse = -inf ([XPU] "Approach 2" guard)
-    if (s == 0) {
-      for (int n = 0; n < G; ++n) {
-        const int64_t h = (int64_t)i * Hq + g * G + n;
-        for (int d = lane; d < D; d += 64) out[h * D + d] = (bf16)0.0f;
-        if (lse && lane == 0) lse[h] = -INFINITY;
-      }
+  if (ns == 0) {  // empty key set: zero output, lse = -inf ([XPU] "Approach 2" guard)
+    for (int n = 0; n < G; ++n) {
+      const int64_t h = (int64_t)i * Hq + g * G + n;
+      for (int d = lane; d < D; d += 64) out[h * D + d] = (bf16)0.0f;
+      if (lse && lane == 0) lse[h] = -INFINITY;
     }
     return;
   }
-  // keys past max_splits * chunk (a length above the caller's max_kv_len) are ignored
-  const int ns = min((L + chunk - 1) / chunk, max_splits);
-  if (s >= ns) return;
   const int t_begin = s * chunk;
-  const int t_end = min(t_begin + chunk, L);
-  const Resolver r = make_resolver(m, i);
+  const int t_end = item.t_end;
+  const SlotMap<FMT> sm = slotmap_from_view<FMT>(m, item_view(item));
 
-  // Q^T operand: lane (n = col, j = grp) holds q[head n][j*DJ + kk*8 .. +8]
+  // Q^T operand: lane (n = col, j = grp) holds q[head n][kk*32 + j*8 .. +8]
   bf16x8 qb[NK];
   {
     const bool ok = col < G;
-    const bf16* qp = q + ((int64_t)i * Hq + g * G + (ok ? col : 0)) * D + grp * DJ;
+    const bf16* qp = q + ((int64_t)i * Hq + g * G + (ok ? col : 0)) * D + grp * 8;
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
-      u32x4 w = *reinterpret_cast<const u32x4*>(qp + kk * 8);
+      u32x4 w = *reinterpret_cast<const u32x4*>(qp + kk * 32);
       if (!ok) w = u32x4{0u, 0u, 0u, 0u};
       qb[kk] = as_bf16x8(w);
     }
@@ -94,91 +299,47 @@ __global__ void __launch_bounds__(64 * WAVES) decode_mfma_kernel(
   const bf16* kb = k_pool + (int64_t)g * D;
   const bf16* vb = v_pool + (int64_t)g * D;
   bf16* vt = vsm[wave];
+  // Lane l looks up token t0 + l%32 of a tile (past the end -> padding slot).
+  // Order of memory instructions per iteration: the table load for tile
+  // i+2, then the K/V rows of tile i+1 (which need tile i+1's table load),
+  // then tile i is computed.  Loads retire in issue order, so each wait only
+  // covers loads issued before the ones meant to stay in flight.  The
+  // prefetch is unconditional (past the end it reads the padding row, which
+  // stays in cache): a conditional one would make the compiler wait for it.
+  const int tl = lane & 31;
+  auto slot_of = [&](int32_t raw, int t0) {
+    const int t = t0 + tl;
+    return sm.finish(raw, t, t < t_end);
+  };
 
-  for (int t0 = t_begin; t0 < t_end; t0 += kTile) {
-    // ---- global loads: K straight into A-operand registers, V into registers
-    bf16x8 ka[2][NK];
-#pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const int t = t0 + a * 16 + col;
-      const int64_t slot = (t < t_end) ? r.slot(t) : r.pad_slot;
-      const bf16* kp = kb + slot * row_elems + grp * DJ;
-#pragma unroll
-      for (int kk = 0; kk < NK; ++kk) ka[a][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(kp + kk * 8));
+  DecodeTile<D> A, B;
+  int32_t raw_next = sm.raw(t_begin + kTile + tl);
+  decode_issue<D>(A, slot_of(sm.raw(t_begin + tl), t_begin), lane, kb, vb, row_elems);
+  for (int t0 = t_begin;;) {
+    {
+      const int32_t raw_new = sm.raw(t0 + 2 * kTile + tl);
+      __builtin_amdgcn_sched_barrier(0);  // table load first: later waits on it must not cover K/V
+      decode_issue<D>(B, slot_of(raw_next, t0 + kTile), lane, kb, vb, row_elems);
+      raw_next = raw_new;
     }
-    u32x4 vr[VIT];
-#pragma unroll
-    for (int it = 0; it < VIT; ++it) {
-      const int t = t0 + it * TPI + lane / CPT;
-      if (t < t_end) {
-        const int64_t slot = r.slot(t);
-        vr[it] = *reinterpret_cast<const u32x4*>(vb + slot * row_elems + (lane % CPT) * 8);
-      } else {
-        vr[it] = u32x4{0u, 0u, 0u, 0u};  // masked keys must hold 0 (P * NaN would poison the sum)
-      }
+    // keep the prefetch ahead of the compute: the empty asm pins the loads
+    // in the IR, the scheduling barrier in the machine schedule
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    decode_compute<D>(A, t0, t_end, lane, qb, scale_log2, vt, acc, m_run, l_run);
+    t0 += kTile;
+    if (t0 >= t_end) break;
+    {
+      const int32_t raw_new = sm.raw(t0 + 2 * kTile + tl);
+      __builtin_amdgcn_sched_barrier(0);
+      decode_issue<D>(A, slot_of(raw_next, t0 + kTile), lane, kb, vb, row_elems);
+      raw_next = raw_new;
     }
-    // ---- S^T = K Q^T
-    f32x4 sacc[2];
-#pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      sacc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < NK; ++kk) sacc[a] = mfma16x16x32(ka[a][kk], qb[kk], sacc[a]);
-    }
-    // ---- V tile to LDS (row-major [token][d])
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int it = 0; it < VIT; ++it) {
-      const int row = it * TPI + lane / CPT;
-      *reinterpret_cast<u32x4*>(vt + row * LDS + (lane % CPT) * 8) = vr[it];
-    }
-    // ---- online softmax; lane holds tokens a*16 + 4*grp + rr of head col
-    float sv[2][4];
-    float mt = -INFINITY;
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int t = t0 + a * 16 + grp * 4 + rr;
-        const float x = (t < t_end) ? sacc[a][rr] * scale_log2 : -INFINITY;
-        sv[a][rr] = x;
-        mt = fmaxf(mt, x);
-      }
-    mt = fmaxf(mt, shfl_xor(mt, 16));
-    mt = fmaxf(mt, shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = fast_exp2(m_run - m_new);  // 0 on the first tile
-    float psum = 0.f;
-    bf16x8 pa;
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const float p = fast_exp2(sv[a][rr] - m_new);
-        psum += p;
-        pa[a * 4 + rr] = (bf16)p;
-      }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    // rows of acc are heads 4*grp + rr; their alpha lives in lane 4*grp + rr
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const float ar = shfl(alpha, grp * 4 + rr);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[nt][rr] *= ar;
-    }
-    __builtin_amdgcn_wave_barrier();
-    // ---- O += P V: B operand = 8 tokens (a*16 + 4*grp + rr) of d column nt*16 + col
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      bf16x8 vbop;
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) vbop[a * 4 + rr] = vt[(a * 16 + grp * 4 + rr) * LDS + nt * 16 + col];
-      acc[nt] = mfma16x16x32(pa, vbop, acc[nt]);
-    }
-    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    decode_compute<D>(B, t0, t_end, lane, qb, scale_log2, vt, acc, m_run, l_run);
+    t0 += kTile;
+    if (t0 >= t_end) break;
   }
 
   // ---- finalise: per-head sums over the four lane groups
@@ -208,9 +369,9 @@ __global__ void __launch_bounds__(64 * WAVES) decode_mfma_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// VALU split kernel (f32 pools; also serves bf16 when asked for explicitly).
-// 16 lanes per token, 4 tokens in flight per wave; each lane group keeps its
-// own online-softmax state, merged across groups at the end.
+// VALU split kernel (f32 pools).  16 lanes per token, 4 tokens in flight per
+// wave; each lane group keeps its own online-softmax state, merged across
+// groups at the end.
 // ---------------------------------------------------------------------------
 template <typename T> __device__ __forceinline__ void load_vals(const T* p, float* v, int n);
 template <> __device__ __forceinline__ void load_vals<float>(const float* p, float* v, int n) {
@@ -226,36 +387,35 @@ template <> __device__ __forceinline__ void load_vals<bf16>(const bf16* p, float
   }
 }
 
-template <typename T, int D, int GM, int WAVES>
+template <typename T, int D, int GM, int WAVES, int FMT>
 __global__ void __launch_bounds__(64 * WAVES) decode_valu_kernel(
     DevMap m, const T* __restrict__ k_pool, const T* __restrict__ v_pool, const T* __restrict__ q, int32_t Hq,
-    int32_t Hkv, int32_t G, int32_t chunk, int32_t max_splits, float scale_log2, T* __restrict__ out,
-    float* __restrict__ lse, float* __restrict__ ws_o, float* __restrict__ ws_lse) {
+    int32_t Hkv, int32_t G, int32_t hg, int32_t chunk, int32_t max_splits, const WorkItem* __restrict__ items,
+    const int32_t* __restrict__ item_count, float scale_log2, T* __restrict__ out, float* __restrict__ lse,
+    float* __restrict__ ws_o, float* __restrict__ ws_lse) {
   constexpr int E = D / 16;
+  const int w_item = blockIdx.x / hg;
+  if (w_item >= *item_count) return;
+  const WorkItem item = items[w_item];
+  const int i = item.i;
+  const int s = item.s;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int s = blockIdx.x;
-  const int i = blockIdx.y;
-  const int g = blockIdx.z * WAVES + wave;
+  const int g = (blockIdx.x % hg) * WAVES + wave;
   const int c = lane & 15;
   const int grp = lane >> 4;
-  const int L = m.kv_lens[i];
-  if (L <= 0) {
-    if (s == 0) {
-      for (int n = 0; n < G; ++n) {
-        const int64_t h = (int64_t)i * Hq + g * G + n;
-        for (int d = lane; d < D; d += 64) out[h * D + d] = from_f32<T>(0.0f);
-        if (lse && lane == 0) lse[h] = -INFINITY;
-      }
+  const int ns = item.ns;
+  if (ns == 0) {
+    for (int n = 0; n < G; ++n) {
+      const int64_t h = (int64_t)i * Hq + g * G + n;
+      for (int d = lane; d < D; d += 64) out[h * D + d] = from_f32<T>(0.0f);
+      if (lse && lane == 0) lse[h] = -INFINITY;
     }
     return;
   }
-  // keys past max_splits * chunk (a length above the caller's max_kv_len) are ignored
-  const int ns = min((L + chunk - 1) / chunk, max_splits);
-  if (s >= ns) return;
   const int t_begin = s * chunk;
-  const int t_end = min(t_begin + chunk, L);
-  const Resolver r = make_resolver(m, i);
+  const int t_end = item.t_end;
+  const SlotMap<FMT> sm = slotmap_from_view<FMT>(m, item_view(item));
 
   float qv[GM][E];
 #pragma unroll
@@ -277,7 +437,7 @@ __global__ void __launch_bounds__(64 * WAVES) decode_valu_kernel(
   }
   const int64_t row_elems = (int64_t)Hkv * D;
   for (int t = t_begin + grp; t < t_end; t += 4) {
-    const int64_t slot = r.slot(t);
+    const int64_t slot = sm(t, true);
     float kv[E], vv[E];
     load_vals<T>(k_pool + slot * row_elems + (int64_t)g * D + c * E, kv, E);
     load_vals<T>(v_pool + slot * row_elems + (int64_t)g * D + c * E, vv, E);
@@ -343,8 +503,6 @@ __global__ void __launch_bounds__(64 * WAVES) decode_valu_kernel(
 // o = sum_s exp(lse_s - lse) o_s.  One wavefront per (request, head);
 // requests that used a single split were finished by the split kernel.
 // ---------------------------------------------------------------------------
-constexpr int kMaxSplits = 1024;
-
 template <typename T>
 __global__ void __launch_bounds__(256) decode_merge_kernel(const int32_t* __restrict__ kv_lens, int32_t bs,
                                                            int32_t Hq, int32_t Dv, int32_t chunk,
@@ -374,9 +532,17 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(const int32_t* __rest
   __builtin_amdgcn_wave_barrier();
   const float inv = 1.0f / tot;
   const float* po = ws_o + idx * max_splits * Dv;
+  // 8 partial rows in flight per lane before any is used
   for (int d = lane; d < Dv; d += 64) {
     float a = 0.f;
-    for (int s = 0; s < ns; ++s) a = fmaf(wsh[wave][s], po[(int64_t)s * Dv + d], a);
+    for (int s0 = 0; s0 < ns; s0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = (s0 + k < ns) ? po[(int64_t)(s0 + k) * Dv + d] : 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (s0 + k < ns) a = fmaf(wsh[wave][s0 + k], v[k], a);
+    }
     out[idx * Dv + d] = from_f32<T>(a * inv);
   }
   if (lse && lane == 0) lse[idx] = mx + __logf(tot);
@@ -392,6 +558,7 @@ hipError_t launch_mla_decode(const PoolInfo& p, int32_t layer, const void* q, in
                              int32_t bs, const DecodePlan& plan, float sm_scale, void* out, float* lse, void* ws,
                              hipStream_t s);
 DecodePlan plan_mla_decode(const PoolInfo& p, int32_t bs, int32_t num_q_heads, int32_t max_kv_len);
+size_t mla_workspace_bytes(const PoolInfo& p, const DecodePlan& plan, int32_t bs, int32_t num_q_heads);
 
 static int decode_kind(const PoolInfo& p, int32_t Hq) {
   if (p.kind == 1) return mla_decode_supported(p, Hq) ? DK_MLA : DK_NONE;
@@ -410,13 +577,16 @@ DecodePlan plan_decode(const PoolInfo& p, int32_t bs, int32_t Hq, int32_t max_kv
   plan.kind = decode_kind(p, Hq);
   if (plan.kind == DK_MLA) return plan_mla_decode(p, bs, Hq, max_kv_len);
   // Chunk of logical tokens per split: the largest power of two in
-  // [64, 2048] that still leaves ~16 wavefronts per CU on average (the mean
-  // length is taken as max_kv_len / 2), so long requests spread over the
-  // 256 CUs while the merge traffic stays a small fraction of the KV bytes.
-  const double waves_per_token = (double)bs * p.num_kv_heads * 0.5 * (double)max_kv_len;
+  // [64, 1024] that still leaves ~16 wavefronts per CU on average (the mean
+  // length is taken as max_kv_len / 2), so long requests spread over the 256
+  // CUs while the merge traffic stays a small fraction of the KV bytes.
+  const double wave_tokens = (double)bs * p.num_kv_heads * 0.5 * (double)max_kv_len;
   int chunk = 64;
-  for (int c = 2048; c >= 64; c >>= 1) {
-    if (waves_per_token / c >= 4096.0) { chunk = c; break; }
+  for (int c = 1024; c >= 64; c >>= 1) {
+    if (wave_tokens / c >= 4096.0) {
+      chunk = c;
+      break;
+    }
   }
   int splits = max_kv_len > 0 ? (max_kv_len + chunk - 1) / chunk : 1;
   while (splits > kMaxSplits) {
@@ -428,31 +598,72 @@ DecodePlan plan_decode(const PoolInfo& p, int32_t bs, int32_t Hq, int32_t max_kv
   return plan;
 }
 
+// workspace: [item count | items[bs * max_splits] | partial o | partial lse]
+struct DecodeWs {
+  int32_t* count;
+  WorkItem* items;
+  float* o;
+  float* lse;
+};
+
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+static size_t decode_ws_layout(const PoolInfo& p, const DecodePlan& plan, int32_t bs, int32_t Hq, void* base,
+                               DecodeWs* w) {
+  size_t off = 0;
+  char* b = static_cast<char*>(base);
+  if (w) w->count = reinterpret_cast<int32_t*>(b + off);
+  off += 256;
+  if (w) w->items = reinterpret_cast<WorkItem*>(b + off);
+  off += align256((size_t)bs * plan.max_splits * sizeof(WorkItem));
+  if (plan.max_splits > 1) {
+    const size_t rows = (size_t)bs * Hq * plan.max_splits;
+    if (w) w->o = reinterpret_cast<float*>(b + off);
+    off += align256(rows * p.head_dim_v * sizeof(float));
+    if (w) w->lse = reinterpret_cast<float*>(b + off);
+    off += align256(rows * sizeof(float));
+  } else if (w) {
+    w->o = nullptr;
+    w->lse = nullptr;
+  }
+  return off;
+}
+
 size_t decode_workspace_bytes(const PoolInfo& p, const DecodePlan& plan, int32_t bs, int32_t Hq) {
-  if (plan.max_splits <= 1) return 0;
-  const size_t rows = (size_t)bs * Hq * plan.max_splits;
-  const size_t o_bytes = (rows * p.head_dim_v * sizeof(float) + 255) / 256 * 256;
-  return o_bytes + rows * sizeof(float);
+  if (plan.kind == DK_MLA) return mla_workspace_bytes(p, plan, bs, Hq);
+  return decode_ws_layout(p, plan, bs, Hq, nullptr, nullptr);
+}
+
+template <int D, int W, int FMT>
+static void launch_mfma(unsigned blocks, hipStream_t s, const DevMap& m, const PoolInfo& p, int32_t layer,
+                        const void* q, int32_t Hq, int32_t G, int32_t hg, const DecodePlan& plan, const DecodeWs& w,
+                        float sl2, void* out, float* lse) {
+  hipLaunchKernelGGL((decode_mfma_kernel<D, W, FMT>), dim3(blocks), dim3(64 * W), 0, s, m,
+                     reinterpret_cast<const bf16*>(p.k_layer(layer)), reinterpret_cast<const bf16*>(p.v_layer(layer)),
+                     static_cast<const bf16*>(q), Hq, p.num_kv_heads, G, hg, plan.chunk, plan.max_splits, w.items,
+                     w.count, sl2, static_cast<bf16*>(out), lse, w.o, w.lse);
 }
 
 template <int D, int W>
-static void launch_mfma(dim3 grid, hipStream_t s, const DevMap& m, const PoolInfo& p, int32_t layer, const void* q,
-                        int32_t Hq, int32_t G, const DecodePlan& plan, float sl2, void* out, float* lse, float* wo,
-                        float* wl) {
-  hipLaunchKernelGGL((decode_mfma_kernel<D, W>), grid, dim3(64 * W), 0, s, m,
-                     reinterpret_cast<const bf16*>(p.k_layer(layer)), reinterpret_cast<const bf16*>(p.v_layer(layer)),
-                     static_cast<const bf16*>(q), Hq, p.num_kv_heads, G, plan.chunk, plan.max_splits, sl2,
-                     static_cast<bf16*>(out), lse, wo, wl);
+static void launch_mfma_fmt(unsigned blocks, hipStream_t s, const DevMap& m, const PoolInfo& p, int32_t layer,
+                            const void* q, int32_t Hq, int32_t G, int32_t hg, const DecodePlan& plan,
+                            const DecodeWs& w, float sl2, void* out, float* lse) {
+  if (m.fmt == MAP_TOKEN_TABLE)
+    launch_mfma<D, W, SLOT_TABLE>(blocks, s, m, p, layer, q, Hq, G, hg, plan, w, sl2, out, lse);
+  else
+    launch_mfma<D, W, SLOT_PAGES>(blocks, s, m, p, layer, q, Hq, G, hg, plan, w, sl2, out, lse);
 }
 
-template <typename T, int D, int W>
-static void launch_valu(dim3 grid, hipStream_t s, const DevMap& m, const PoolInfo& p, int32_t layer, const void* q,
-                        int32_t Hq, int32_t G, const DecodePlan& plan, float sl2, void* out, float* lse, float* wo,
-                        float* wl) {
-  hipLaunchKernelGGL((decode_valu_kernel<T, D, 8, W>), grid, dim3(64 * W), 0, s, m,
-                     reinterpret_cast<const T*>(p.k_layer(layer)), reinterpret_cast<const T*>(p.v_layer(layer)),
-                     static_cast<const T*>(q), Hq, p.num_kv_heads, G, plan.chunk, plan.max_splits, sl2,
-                     static_cast<T*>(out), lse, wo, wl);
+template <int D, int W>
+static void launch_valu(unsigned blocks, hipStream_t s, const DevMap& m, const PoolInfo& p, int32_t layer,
+                        const void* q, int32_t Hq, int32_t G, int32_t hg, const DecodePlan& plan, const DecodeWs& w,
+                        float sl2, void* out, float* lse) {
+  auto kern = (m.fmt == MAP_TOKEN_TABLE) ? decode_valu_kernel<float, D, 8, W, SLOT_TABLE>
+                                         : decode_valu_kernel<float, D, 8, W, SLOT_PAGES>;
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * W), 0, s, m, reinterpret_cast<const float*>(p.k_layer(layer)),
+                     reinterpret_cast<const float*>(p.v_layer(layer)), static_cast<const float*>(q), Hq,
+                     p.num_kv_heads, G, hg, plan.chunk, plan.max_splits, w.items, w.count, sl2,
+                     static_cast<float*>(out), lse, w.o, w.lse);
 }
 
 hipError_t launch_decode(const PoolInfo& p, int32_t layer, const void* q, int32_t Hq, const DevMap& m, int32_t bs,
@@ -462,48 +673,48 @@ hipError_t launch_decode(const PoolInfo& p, int32_t layer, const void* q, int32_
   const int Hkv = p.num_kv_heads;
   const int G = Hq / Hkv;
   const int W = (Hkv % 4 == 0) ? 4 : (Hkv % 2 == 0 ? 2 : 1);
-  const dim3 grid((unsigned)plan.max_splits, (unsigned)bs, (unsigned)(Hkv / W));
+  const int hg = Hkv / W;
+  DecodeWs w;
+  decode_ws_layout(p, plan, bs, Hq, ws, &w);
+  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, s, m, bs, plan.chunk, plan.max_splits, w.items,
+                     w.count);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned blocks = (unsigned)((int64_t)bs * plan.max_splits * hg);
   const float sl2 = sm_scale * kLog2e;
-  float* wo = nullptr;
-  float* wl = nullptr;
-  if (plan.max_splits > 1) {
-    const size_t rows = (size_t)bs * Hq * plan.max_splits;
-    wo = static_cast<float*>(ws);
-    wl = reinterpret_cast<float*>(static_cast<char*>(ws) + (rows * p.head_dim_v * sizeof(float) + 255) / 256 * 256);
-  }
   const int D = p.head_dim_qk;
   timer_before(s);
   if (plan.kind == DK_MFMA) {
     if (D == 128) {
-      if (W == 4) launch_mfma<128, 4>(grid, s, m, p, layer, q, Hq, G, plan, sl2, out, lse, wo, wl);
-      else if (W == 2) launch_mfma<128, 2>(grid, s, m, p, layer, q, Hq, G, plan, sl2, out, lse, wo, wl);
-      else launch_mfma<128, 1>(grid, s, m, p, layer, q, Hq, G, plan, sl2, out, lse, wo, wl);
+      if (W == 4) launch_mfma_fmt<128, 4>(blocks, s, m, p, layer, q, Hq, G, hg, plan, w, sl2, out, lse);
+      else if (W == 2) launch_mfma_fmt<128, 2>(blocks, s, m, p, layer, q, Hq, G, hg, plan, w, sl2, out, lse);
+      else launch_mfma_fmt<128, 1>(blocks, s, m, p, layer, q, Hq, G, hg, plan, w, sl2, out, lse);
     } else {
-      if (W == 4) launch_mfma<64, 4>(grid, s, m, p, layer, q, Hq, G, plan, sl2, out, lse, wo, wl);
-      else if (W == 2) launch_mfma<64, 2>(grid, s, m, p, layer, q, Hq, G, plan, sl2, out, lse, wo, wl);
-      else launch_mfma<64, 1>(grid, s, m, p, layer, q, Hq, G, plan, sl2, out, lse, wo, wl);
+      if (W == 4) launch_mfma_fmt<64, 4>(blocks, s, m, p, layer, q, Hq, G, hg, plan, w, sl2, out, lse);
+      else if (W == 2) launch_mfma_fmt<64, 2>(blocks, s, m, p, layer, q, Hq, G, hg, plan, w, sl2, out, lse);
+      else launch_mfma_fmt<64, 1>(blocks, s, m, p, layer, q, Hq, G, hg, plan, w, sl2, out, lse);
     }
   } else {
     if (D == 128) {
-      if (W == 4) launch_valu<float, 128, 4>(grid, s, m, p, layer, q, Hq, G, plan, sl2, out, lse, wo, wl);
-      else if (W == 2) launch_valu<float, 128, 2>(grid, s, m, p, layer, q, Hq, G, plan, sl2, out, lse, wo, wl);
-      else launch_valu<float, 128, 1>(grid, s, m, p, layer, q, Hq, G, plan, sl2, out, lse, wo, wl);
+      if (W == 4) launch_valu<128, 4>(blocks, s, m, p, layer, q, Hq, G, hg, plan, w, sl2, out, lse);
+      else if (W == 2) launch_valu<128, 2>(blocks, s, m, p, layer, q, Hq, G, hg, plan, w, sl2, out, lse);
+      else launch_valu<128, 1>(blocks, s, m, p, layer, q, Hq, G, hg, plan, w, sl2, out, lse);
     } else {
-      if (W == 4) launch_valu<float, 64, 4>(grid, s, m, p, layer, q, Hq, G, plan, sl2, out, lse, wo, wl);
-      else if (W == 2) launch_valu<float, 64, 2>(grid, s, m, p, layer, q, Hq, G, plan, sl2, out, lse, wo, wl);
-      else launch_valu<float, 64, 1>(grid, s, m, p, layer, q, Hq, G, plan, sl2, out, lse, wo, wl);
+      if (W == 4) launch_valu<64, 4>(blocks, s, m, p, layer, q, Hq, G, hg, plan, w, sl2, out, lse);
+      else if (W == 2) launch_valu<64, 2>(blocks, s, m, p, layer, q, Hq, G, hg, plan, w, sl2, out, lse);
+      else launch_valu<64, 1>(blocks, s, m, p, layer, q, Hq, G, hg, plan, w, sl2, out, lse);
     }
   }
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   timer_after(s);
   if (e != hipSuccess || plan.max_splits <= 1) return e;
   const unsigned mblocks = (unsigned)(((int64_t)bs * Hq + 3) / 4);
   if (p.dtype == 1)
     hipLaunchKernelGGL(decode_merge_kernel<bf16>, dim3(mblocks), dim3(256), 0, s, m.kv_lens, bs, Hq, p.head_dim_v,
-                       plan.chunk, plan.max_splits, wo, wl, static_cast<bf16*>(out), lse);
+                       plan.chunk, plan.max_splits, w.o, w.lse, static_cast<bf16*>(out), lse);
   else
     hipLaunchKernelGGL(decode_merge_kernel<float>, dim3(mblocks), dim3(256), 0, s, m.kv_lens, bs, Hq, p.head_dim_v,
-                       plan.chunk, plan.max_splits, wo, wl, static_cast<float*>(out), lse);
+                       plan.chunk, plan.max_splits, w.o, w.lse, static_cast<float*>(out), lse);
   return hipGetLastError();
 }
 

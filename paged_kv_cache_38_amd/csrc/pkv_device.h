@@ -112,6 +112,115 @@ __device__ __forceinline__ Resolver make_resolver(const DevMap& m, int32_t i) {
   return r;
 }
 
+// Branch-free per-request slot lookup, specialised on the table family so the
+// hot loops carry no format switch and every lookup is one unconditional
+// load (out-of-range indices are clamped to a readable address and the
+// result replaced by the padding slot).  Slots fit in 32 bits (the host
+// rejects pools of 2^31 slots or more).
+enum SlotFmt : int { SLOT_TABLE = 0, SLOT_PAGES = 1, SLOT_CONTIG = 2 };
+
+template <int FMT>
+struct SlotMap {
+  const int32_t* base;  // never null: points at readable memory even when limit == 0
+  int32_t limit;        // readable entries at base (tokens or pages)
+  int32_t shift, mask;
+  int32_t num_slots, pad;
+  int32_t off;          // contiguous: first row of the request
+
+  // slot of logical token t; `valid` false gives the padding slot
+  __device__ __forceinline__ int32_t operator()(int32_t t, bool valid) const { return finish(raw(t), t, valid); }
+
+  // Two halves of a lookup, so a loop can issue the table load early and
+  // use it a tile later: raw() is the bare load (index clamped to a
+  // readable entry), finish() the checks, with no memory access.
+  __device__ __forceinline__ int32_t raw(int32_t t) const {
+    if constexpr (FMT == SLOT_CONTIG) {
+      return 0;
+    } else if constexpr (FMT == SLOT_TABLE) {
+      return base[min(max(t, 0), max(limit - 1, 0))];
+    } else {
+      return base[min(max(t >> shift, 0), max(limit - 1, 0))];
+    }
+  }
+  __device__ __forceinline__ int32_t finish(int32_t r, int32_t t, bool valid) const {
+    if constexpr (FMT == SLOT_CONTIG) {
+      const int32_t s = off + t;
+      return (valid && (uint32_t)s < (uint32_t)num_slots) ? s : pad;
+    } else if constexpr (FMT == SLOT_TABLE) {
+      const bool ok = valid && t < limit;
+      const int32_t s = ok ? r : pad;
+      return ((uint32_t)s < (uint32_t)num_slots) ? s : pad;
+    } else {
+      const bool ok = valid && (t >> shift) < limit && r >= 0;
+      const int32_t s = ok ? ((r << shift) | (t & mask)) : pad;
+      return ((uint32_t)s < (uint32_t)num_slots) ? s : pad;
+    }
+  }
+};
+
+// Where request i's table entries start (element offset into req_to_token,
+// kv_indices or block_table) and how many are readable; limit 0 marks a
+// malformed row/pointer, read as all padding.  Contiguous maps: the first
+// gathered row.
+struct ReqView {
+  int64_t off;
+  int32_t limit;
+};
+
+__device__ __forceinline__ ReqView request_view(const DevMap& m, int32_t i) {
+  ReqView v{0, 0};
+  if (m.fmt == MAP_TOKEN_TABLE) {
+    const int64_t row = m.req_pool_indices[i];
+    const int64_t start = m.kv_start ? (int64_t)m.kv_start[i] : 0;
+    if (row >= 0 && row < m.table_rows && start >= 0 && start < m.table_width) {
+      v.off = row * m.table_width + start;
+      v.limit = (int32_t)(m.table_width - start);
+    }
+  } else if (m.fmt == MAP_CSR) {
+    const int64_t a = m.kv_indptr[i], b = m.kv_indptr[i + 1];
+    if (a >= 0 && b > a && b <= m.kv_indices_len) {
+      v.off = a;
+      v.limit = (int32_t)(b - a);
+    }
+  } else if (m.fmt == MAP_BLOCK_TABLE) {
+    if (m.block_stride > 0) {
+      v.off = (int64_t)i * m.block_stride;
+      v.limit = (int32_t)m.block_stride;
+    }
+  } else {
+    v.off = m.cu_seqlens_k[i];
+    v.limit = 1;
+  }
+  return v;
+}
+
+template <int FMT>
+__device__ __forceinline__ SlotMap<FMT> slotmap_from_view(const DevMap& m, ReqView v) {
+  SlotMap<FMT> r;
+  r.shift = m.page_shift;
+  r.mask = (1 << m.page_shift) - 1;
+  r.num_slots = (int32_t)m.num_slots;
+  r.pad = (int32_t)m.pad_slot;
+  r.off = 0;
+  r.base = m.kv_lens;  // readable fallback
+  r.limit = 0;
+  if constexpr (FMT == SLOT_CONTIG) {
+    r.off = (int32_t)v.off;
+    r.num_slots = (int32_t)m.total_k;
+    r.pad = 0;
+  } else if (v.limit > 0) {
+    const int32_t* tab = (FMT == SLOT_TABLE) ? m.req_to_token : (m.fmt == MAP_CSR ? m.kv_indices : m.block_table);
+    r.base = tab + v.off;
+    r.limit = v.limit;
+  }
+  return r;
+}
+
+template <int FMT>
+__device__ __forceinline__ SlotMap<FMT> make_slotmap(const DevMap& m, int32_t i) {
+  return slotmap_from_view<FMT>(m, request_view(m, i));
+}
+
 // ---------------------------------------------------------------------------
 // small numeric helpers
 // ---------------------------------------------------------------------------
@@ -128,6 +237,8 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // xor-shuffle across the wavefront (ds_bpermute)
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 __device__ __forceinline__ float shfl(float v, int src) { return __shfl(v, src, 64); }
+// integer lane gather (ds_bpermute): value of lane `src` (0..63)
+__device__ __forceinline__ int32_t shfl_i(int32_t v, int src) { return __builtin_amdgcn_ds_bpermute(src << 2, v); }
 
 __device__ __forceinline__ int32_t wave_lane() { return (int32_t)__lane_id(); }
 

@@ -14,6 +14,8 @@ DecodePlan plan_mla_decode(const PoolInfo&, int32_t, int32_t, int32_t) {
   return p;
 }
 
+size_t mla_workspace_bytes(const PoolInfo&, const DecodePlan&, int32_t, int32_t) { return 0; }
+
 hipError_t launch_mla_decode(const PoolInfo&, int32_t, const void*, int32_t, const DevMap&, int32_t,
                              const DecodePlan&, float, void*, float*, void*, hipStream_t) {
   return hipErrorInvalidValue;
