@@ -232,7 +232,8 @@ int paged_decode_attn(const pkv_pool* pool, int32_t layer, const void* q, int32_
  * "Attention execution": causal and full segments).  causal != 0 aligns the
  * queries bottom-right: the j-th of n new queries sees keys 0 .. L - n + j;
  * causal == 0 lets every query see every key (encoder cross-attention).
- *   q: device [total_q][num_q_heads][head_dim_qk] (total_q = qo_indptr[bs]).
+ *   q: device [total_q][num_q_heads][head_dim_qk]; total_q (host) is the row
+ *     count of q and out, >= qo_indptr[bs] (rows past it are never touched).
  *   qo_indptr: device int32[bs+1].
  *   max_q_len: host bound >= every new-token count.
  *   out: device [total_q][num_q_heads][head_dim_v]; lse nullable float
@@ -240,7 +241,7 @@ int paged_decode_attn(const pkv_pool* pool, int32_t layer, const void* q, int32_
  *     ([XPU] "Approach 2" empty-KV guard).
  *   map->fmt: any; CONTIGUOUS is the ragged (varlen) variant.
  * Supported: SPLIT_KV bf16, head_dim 64 or 128. */
-int paged_extend_attn(const pkv_pool* pool, int32_t layer, const void* q, const int32_t* qo_indptr,
+int paged_extend_attn(const pkv_pool* pool, int32_t layer, const void* q, int64_t total_q, const int32_t* qo_indptr,
                       int32_t num_q_heads, int32_t max_q_len, const pkv_kv_map* map, int32_t causal,
                       float sm_scale, void* out, float* lse, void* stream);
 

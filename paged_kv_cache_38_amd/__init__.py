@@ -247,7 +247,9 @@ def paged_decode_attn(pool: Pool, layer: int, q: torch.Tensor, kv_map: KVMap, sm
 def paged_extend_attn(pool: Pool, layer: int, q: torch.Tensor, qo_indptr: torch.Tensor, max_q_len: int,
                       kv_map: KVMap, causal: bool, sm_scale: float, out: torch.Tensor,
                       lse: Optional[torch.Tensor] = None, stream=None) -> None:
-    L.check(L.load().paged_extend_attn(pool.handle, layer, _dev(q, "q", pool.dtype),
+    if out.shape[0] != q.shape[0]:
+        raise ValueError("out and q must have the same number of rows")
+    L.check(L.load().paged_extend_attn(pool.handle, layer, _dev(q, "q", pool.dtype), q.shape[0],
                                        _dev(qo_indptr, "qo_indptr", torch.int32), q.shape[1], int(max_q_len),
                                        C.byref(kv_map.struct), 1 if causal else 0, float(sm_scale),
                                        _dev(out, "out", pool.dtype), _dev(lse, "lse", torch.float32),

@@ -145,12 +145,15 @@ int make_devmap(const pkv_pool* pool, const pkv_kv_map* m, bool allow_contiguous
     }
     case PKV_MAP_CONTIGUOUS:
       if (!allow_contiguous) return fail(PKV_EUNSUPPORTED, "contiguous map not accepted by this call");
-      if (m->bs > 0 && (!m->k || !m->cu_seqlens_k)) return fail(PKV_EINVAL, "contiguous map needs k and cu_seqlens_k");
-      if (pool->desc.kind == PKV_KIND_SPLIT_KV && m->bs > 0 && !m->v) return fail(PKV_EINVAL, "contiguous map needs v");
+      if (m->bs > 0 && !m->cu_seqlens_k) return fail(PKV_EINVAL, "contiguous map needs cu_seqlens_k");
+      if (m->total_k > 0 && (!m->k || (pool->desc.kind == PKV_KIND_SPLIT_KV && !m->v)))
+        return fail(PKV_EINVAL, "contiguous map with rows needs k (and v for a split K/V pool)");
       if (m->total_k < 0) return fail(PKV_EINVAL, "negative total_k");
       if (!aligned16(m->k) || !aligned16(m->v)) return fail(PKV_EALIGN, "contiguous k/v not 16-byte aligned");
       out->cu_seqlens_k = m->cu_seqlens_k;
       out->total_k = m->total_k;
+      out->contig_k = m->k;
+      out->contig_v = pool->desc.kind == PKV_KIND_LATENT ? m->k : m->v;
       out->num_slots = m->total_k;
       out->pad_slot = 0;
       break;
@@ -312,7 +315,7 @@ int paged_decode_attn(const pkv_pool* pool, int32_t layer, const void* q, int32_
                        "paged_decode_attn");
 }
 
-int paged_extend_attn(const pkv_pool* pool, int32_t layer, const void* q, const int32_t* qo_indptr,
+int paged_extend_attn(const pkv_pool* pool, int32_t layer, const void* q, int64_t total_q, const int32_t* qo_indptr,
                       int32_t num_q_heads, int32_t max_q_len, const pkv_kv_map* map, int32_t causal, float sm_scale,
                       void* out, float* lse, void* stream) {
   if (int st = check_pool(pool)) return st;
@@ -322,14 +325,14 @@ int paged_extend_attn(const pkv_pool* pool, int32_t layer, const void* q, const 
   if (num_q_heads <= 0 || num_q_heads % pool->desc.num_kv_heads != 0)
     return fail(PKV_EINVAL, "num_q_heads %d not a positive multiple of num_kv_heads %d", num_q_heads,
                 pool->desc.num_kv_heads);
-  if (max_q_len < 0) return fail(PKV_EINVAL, "negative max_q_len");
+  if (max_q_len < 0 || total_q < 0) return fail(PKV_EINVAL, "negative max_q_len or total_q");
   if (!pkv::extend_supported(pool->info, num_q_heads))
     return fail(PKV_EUNSUPPORTED, "no extend kernel for this pool (dtype %d, dims %d/%d)", pool->desc.dtype,
                 pool->desc.head_dim_qk, pool->desc.head_dim_v);
-  if (map->bs == 0 || max_q_len == 0) return ok();
+  if (map->bs == 0 || max_q_len == 0 || total_q == 0) return ok();
   if (!q || !out || !qo_indptr) return fail(PKV_EINVAL, "null q, out or qo_indptr");
   if (!aligned16(q)) return fail(PKV_EALIGN, "q must be 16-byte aligned");
-  return device_status(pkv::launch_extend(pool->info, layer, q, qo_indptr, num_q_heads, max_q_len, dm, map->bs,
+  return device_status(pkv::launch_extend(pool->info, layer, q, total_q, qo_indptr, num_q_heads, max_q_len, dm, map->bs,
                                           map->max_kv_len, causal, sm_scale, out, lse, (hipStream_t)stream),
                        "paged_extend_attn");
 }

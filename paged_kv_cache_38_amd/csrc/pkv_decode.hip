@@ -37,15 +37,6 @@ constexpr int kTile = 32;          // tokens per inner iteration of the MFMA ker
 constexpr int kMaxSplits = 1024;   // per request; item = request * kMaxSplits + split
 constexpr int kItemShift = 10;
 
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-// Transposed LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
-// lanes, lane j supplies the address of 4 consecutive 16-bit values (call
-// them M[j][0..3]); lane i receives M[i/4 + 4r][i%4] for r = 0..3.
-__device__ __forceinline__ i16x4 lds_read_tr16(const bf16* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
-}
 
 // ---------------------------------------------------------------------------
 // split plan: live items in request order; an empty request still gets one
@@ -227,18 +218,9 @@ __device__ __forceinline__ void decode_compute(const DecodeTile<D>& T, int t0, i
   }
   __builtin_amdgcn_wave_barrier();
   // ---- O += P V.  B operand of lane (col, grp) = V[a*16 + 4*grp + rr][nt*16 + col]
-  // for a = 0, 1 and rr = 0..3: one transposed read per a, lane j of the group
-  // pointing at token a*16 + 4*grp + j/4, columns nt*16 + 4*(j%4) .. +4.
-  const int j = lane & 15;
+  // for a = 0, 1 and rr = 0..3: two transposed LDS reads
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const bf16* base = vt + (grp * 4 + (j >> 2)) * LDS + nt * 16 + 4 * (j & 3);
-    const i16x4 lo = lds_read_tr16(base);
-    const i16x4 hi = lds_read_tr16(base + 16 * LDS);
-    const bf16x4 blo = __builtin_bit_cast(bf16x4, lo), bhi = __builtin_bit_cast(bf16x4, hi);
-    const bf16x8 vbop = {blo[0], blo[1], blo[2], blo[3], bhi[0], bhi[1], bhi[2], bhi[3]};
-    acc[nt] = mfma16x16x32(pa, vbop, acc[nt]);
-  }
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma16x16x32(pa, lds_v_operand(vt, LDS, 0, nt * 16, lane), acc[nt]);
   __builtin_amdgcn_wave_barrier();
 }
 

@@ -47,6 +47,8 @@ struct DevMap {
   // contiguous (gathered) K/V
   const int32_t* cu_seqlens_k;
   int64_t total_k;
+  const void* contig_k;
+  const void* contig_v;
   // pool bounds: any resolved slot outside [0, num_slots) reads pad_slot
   int64_t num_slots;
   int64_t pad_slot;
@@ -246,6 +248,30 @@ __device__ __forceinline__ int32_t wave_lane() { return (int32_t)__lane_id(); }
 // and B[8*(l/16) .. +8][l%16]; it receives D[4*(l/16) + r][l%16], r = 0..3.
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Transposed LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane j supplies the address of 4 consecutive 16-bit values (call
+// them M[j][0..3]); lane i receives M[i/4 + 4r][i%4] for r = 0..3.
+__device__ __forceinline__ i16x4 lds_read_tr16(const bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
+// B operand of P*V for a 16x16x32 MFMA from a row-major [token][d] LDS tile
+// (row stride `lds` elements): lane (n = l%16, j = l/16) receives
+// V[r0 + 4j + r][c0 + n] for r = 0..3 (low half) and V[r0 + 16 + 4j + r][c0 + n]
+// (high half); lane x of each 16-lane group points at row r0 + 4j + x/4,
+// columns c0 + 4*(x%4) .. +4.
+__device__ __forceinline__ bf16x8 lds_v_operand(const bf16* tile, int lds, int r0, int c0, int lane) {
+  const int x = lane & 15, j = lane >> 4;
+  const bf16* base = tile + (r0 + j * 4 + (x >> 2)) * lds + c0 + 4 * (x & 3);
+  const i16x4 lo = lds_read_tr16(base);
+  const i16x4 hi = lds_read_tr16(base + 16 * lds);
+  const bf16x4 blo = __builtin_bit_cast(bf16x4, lo), bhi = __builtin_bit_cast(bf16x4, hi);
+  return bf16x8{blo[0], blo[1], blo[2], blo[3], bhi[0], bhi[1], bhi[2], bhi[3]};
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }

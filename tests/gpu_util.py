@@ -144,3 +144,31 @@ def oracle_region(case: Case, vals: dict, name: str, pk=None, pv=None, requests=
     g = case.geom
     return oracle.paged_attention(to_numpy_bits(vals["q"][name]), case.q_lens, pk, pv, g.dtype, slots,
                                   case.sm_scale, r.causal, head_dim_v=g.head_dim_v, requests=requests)
+
+
+def run_extend(dc: "DeviceCase", name: str, fmt: int, contiguous: bool = False):
+    """Extend attention of one region through the C ABI; with `contiguous`,
+    the region is first gathered by kv_gather and read back through a
+    CONTIGUOUS map (the ragged variant)."""
+    c = dc.case
+    g = c.geom
+    reg = c.regions[name]
+    qo = i32(oracle.token_indptr(c.q_lens), dc.device)
+    max_q = int(c.q_lens.max())
+    total_q = int(c.q_lens.sum())
+    out = torch.full((total_q, g.num_q_heads, g.head_dim_v), float("nan"), dtype=dc.dtype, device=dc.device)
+    lse = torch.full((total_q, g.num_q_heads), float("nan"), dtype=torch.float32, device=dc.device)
+    m = dc.kv_map(name, fmt)
+    if contiguous:
+        cu = oracle.token_indptr(reg.kv_lens)
+        tot = int(cu[-1])
+        ko = torch.empty((max(tot, 1), g.num_kv_heads, g.head_dim_qk), dtype=dc.dtype, device=dc.device)
+        vo = torch.empty_like(ko)
+        cu_d = i32(cu, dc.device)
+        P.kv_gather(dc.pool, dc.layer, m, cu_d, ko, vo)
+        _, kv_lens, maxl = dc.region_tensors(name)
+        m = P.make_kv_map(P.PKV_MAP_CONTIGUOUS, kv_lens, maxl, k=ko[:tot] if tot else ko[:0], v=vo[:tot] if tot else vo[:0],
+                          cu_seqlens_k=cu_d)
+    P.paged_extend_attn(dc.pool, dc.layer, dc.q[name], qo, max_q, m, reg.causal, c.sm_scale, out, lse)
+    torch.cuda.synchronize()
+    return out, lse
