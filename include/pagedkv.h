@@ -220,7 +220,7 @@ int paged_decode_workspace_bytes(const pkv_pool* pool, int32_t bs, int32_t num_q
  *   map->fmt: TOKEN_TABLE, CSR or BLOCK_TABLE.
  * Supported: SPLIT_KV f32 or bf16 with head_dim 64 or 128 and
  * num_q_heads/num_kv_heads <= 16; LATENT bf16 with head_dim_qk 576,
- * head_dim_v 512, one KV head and num_q_heads a multiple of 32. */
+ * head_dim_v 512, one KV head and num_q_heads a multiple of 16. */
 int paged_decode_attn(const pkv_pool* pool, int32_t layer, const void* q, int32_t num_q_heads,
                       const pkv_kv_map* map, float sm_scale, void* out, float* lse, void* workspace,
                       size_t ws_bytes, void* stream);

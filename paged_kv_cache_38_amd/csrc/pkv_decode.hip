@@ -34,8 +34,6 @@
 namespace pkv {
 
 constexpr int kTile = 32;          // tokens per inner iteration of the MFMA kernel
-constexpr int kMaxSplits = 1024;   // per request; item = request * kMaxSplits + split
-constexpr int kItemShift = 10;
 
 
 // ---------------------------------------------------------------------------
@@ -44,16 +42,6 @@ constexpr int kItemShift = 10;
 // split needs to start streaming at once (its request's table view and key
 // range), so the split kernel's first dependent loads are the table entries.
 // ---------------------------------------------------------------------------
-struct __attribute__((aligned(16))) WorkItem {
-  int32_t i;      // request
-  int32_t s;      // split
-  int32_t ns;     // splits of request i (0: empty request)
-  int32_t t_end;  // exclusive end of the split's keys (it starts at s * chunk)
-  int32_t limit;  // readable table entries (0: malformed row, read as padding)
-  int32_t off_lo, off_hi;  // element offset of the request's table row / page list
-  int32_t pad;
-};
-
 __global__ void __launch_bounds__(1024) decode_plan_kernel(DevMap m, int32_t bs, int32_t chunk, int32_t max_splits,
                                                            WorkItem* __restrict__ items, int32_t* __restrict__ count) {
   __shared__ int32_t wsum[16];
@@ -105,13 +93,6 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DevMap m, int32_t bs,
     __syncthreads();
   }
   if (tid == 0) *count = carry;
-}
-
-__device__ __forceinline__ ReqView item_view(const WorkItem& w) {
-  ReqView v;
-  v.off = ((int64_t)w.off_hi << 32) | (uint32_t)w.off_lo;
-  v.limit = w.limit;
-  return v;
 }
 
 // ---------------------------------------------------------------------------
@@ -535,12 +516,6 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(const int32_t* __rest
 // ---------------------------------------------------------------------------
 enum DecodeKind : int32_t { DK_NONE = 0, DK_MFMA = 1, DK_VALU = 2, DK_MLA = 3 };
 
-bool mla_decode_supported(const PoolInfo& p, int32_t num_q_heads);
-hipError_t launch_mla_decode(const PoolInfo& p, int32_t layer, const void* q, int32_t num_q_heads, const DevMap& m,
-                             int32_t bs, const DecodePlan& plan, float sm_scale, void* out, float* lse, void* ws,
-                             hipStream_t s);
-DecodePlan plan_mla_decode(const PoolInfo& p, int32_t bs, int32_t num_q_heads, int32_t max_kv_len);
-size_t mla_workspace_bytes(const PoolInfo& p, const DecodePlan& plan, int32_t bs, int32_t num_q_heads);
 
 static int decode_kind(const PoolInfo& p, int32_t Hq) {
   if (p.kind == 1) return mla_decode_supported(p, Hq) ? DK_MLA : DK_NONE;
@@ -581,17 +556,11 @@ DecodePlan plan_decode(const PoolInfo& p, int32_t bs, int32_t Hq, int32_t max_kv
 }
 
 // workspace: [item count | items[bs * max_splits] | partial o | partial lse]
-struct DecodeWs {
-  int32_t* count;
-  WorkItem* items;
-  float* o;
-  float* lse;
-};
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-static size_t decode_ws_layout(const PoolInfo& p, const DecodePlan& plan, int32_t bs, int32_t Hq, void* base,
-                               DecodeWs* w) {
+size_t decode_ws_layout(const PoolInfo& p, const DecodePlan& plan, int32_t bs, int32_t Hq, void* base,
+                        DecodeWs* w) {
   size_t off = 0;
   char* b = static_cast<char*>(base);
   if (w) w->count = reinterpret_cast<int32_t*>(b + off);
@@ -612,7 +581,6 @@ static size_t decode_ws_layout(const PoolInfo& p, const DecodePlan& plan, int32_
 }
 
 size_t decode_workspace_bytes(const PoolInfo& p, const DecodePlan& plan, int32_t bs, int32_t Hq) {
-  if (plan.kind == DK_MLA) return mla_workspace_bytes(p, plan, bs, Hq);
   return decode_ws_layout(p, plan, bs, Hq, nullptr, nullptr);
 }
 
@@ -651,7 +619,6 @@ static void launch_valu(unsigned blocks, hipStream_t s, const DevMap& m, const P
 hipError_t launch_decode(const PoolInfo& p, int32_t layer, const void* q, int32_t Hq, const DevMap& m, int32_t bs,
                          const DecodePlan& plan, float sm_scale, void* out, float* lse, void* ws, hipStream_t s) {
   if (bs == 0) return hipSuccess;
-  if (plan.kind == DK_MLA) return launch_mla_decode(p, layer, q, Hq, m, bs, plan, sm_scale, out, lse, ws, s);
   const int Hkv = p.num_kv_heads;
   const int G = Hq / Hkv;
   const int W = (Hkv % 4 == 0) ? 4 : (Hkv % 2 == 0 ? 2 : 1);
@@ -666,7 +633,9 @@ hipError_t launch_decode(const PoolInfo& p, int32_t layer, const void* q, int32_
   const float sl2 = sm_scale * kLog2e;
   const int D = p.head_dim_qk;
   timer_before(s);
-  if (plan.kind == DK_MFMA) {
+  if (plan.kind == DK_MLA) {
+    launch_mla_split(p, layer, q, Hq, m, bs, plan, w, sl2, out, lse, s);
+  } else if (plan.kind == DK_MFMA) {
     if (D == 128) {
       if (W == 4) launch_mfma_fmt<128, 4>(blocks, s, m, p, layer, q, Hq, G, hg, plan, w, sl2, out, lse);
       else if (W == 2) launch_mfma_fmt<128, 2>(blocks, s, m, p, layer, q, Hq, G, hg, plan, w, sl2, out, lse);

@@ -54,6 +54,42 @@ struct DecodePlan {
   int32_t max_splits;
   int32_t kind;  // which kernel family
 };
+
+constexpr int kMaxSplits = 1024;  // per request
+
+// One live (request, split) of a decode launch, written by the planner
+// kernel: what a split needs to start streaming at once.
+struct __attribute__((aligned(16))) WorkItem {
+  int32_t i;      // request
+  int32_t s;      // split
+  int32_t ns;     // splits of request i (0: empty request)
+  int32_t t_end;  // exclusive end of the split's keys (it starts at s * chunk)
+  int32_t limit;  // readable table entries (0: malformed row, read as padding)
+  int32_t off_lo, off_hi;  // element offset of the request's table row / page list
+  int32_t pad;
+};
+
+__device__ __forceinline__ ReqView item_view(const WorkItem& w) {
+  ReqView v;
+  v.off = ((int64_t)w.off_hi << 32) | (uint32_t)w.off_lo;
+  v.limit = w.limit;
+  return v;
+}
+
+// decode workspace: [item count | items[bs * max_splits] | partial o | partial lse]
+struct DecodeWs {
+  int32_t* count;
+  WorkItem* items;
+  float* o;
+  float* lse;
+};
+size_t decode_ws_layout(const PoolInfo& p, const DecodePlan& plan, int32_t bs, int32_t Hq, void* base, DecodeWs* w);
+
+bool mla_decode_supported(const PoolInfo& p, int32_t num_q_heads);
+DecodePlan plan_mla_decode(const PoolInfo& p, int32_t bs, int32_t num_q_heads, int32_t max_kv_len);
+void launch_mla_split(const PoolInfo& p, int32_t layer, const void* q, int32_t num_q_heads, const DevMap& m,
+                      int32_t bs, const DecodePlan& plan, const DecodeWs& w, float scale_log2, void* out, float* lse,
+                      hipStream_t s);
 DecodePlan plan_decode(const PoolInfo& p, int32_t bs, int32_t num_q_heads, int32_t max_kv_len);
 size_t decode_workspace_bytes(const PoolInfo& p, const DecodePlan& plan, int32_t bs, int32_t num_q_heads);
 bool decode_supported(const PoolInfo& p, int32_t num_q_heads);
