@@ -1,18 +1,24 @@
 #!/usr/bin/env python3
 """Benchmark of the paged KV-cache hot path on one MI355X.
 
-Default workload: Qwen3-0.6B-shaped single-layer decode, bf16 (batch 64, 16
-query heads over 8 KV heads, head_dim 128, page_size 1 through a
-token-granular req_to_token table of width 8192, KV lengths uniform in
-[512, 4096], slots a seeded shuffle of a 400k-token pool).  One step is one
+Default workload (the headline line): Qwen3-0.6B-shaped single-layer decode,
+bf16 -- batch 64, 16 query heads over 8 KV heads, head_dim 128, page_size 1
+through a token-granular req_to_token table of width 8192, KV lengths uniform
+in [512, 4096], slots a seeded shuffle of a 400k-token pool.  One step is one
 pass of the hot path over the batch: the KV append of the 64 new tokens
-(kv_store) followed by paged decode attention (split-K partial kernel plus
-the log-sum-exp merge).  Inputs are resident in HBM before timing starts.
+(kv_store) then paged decode attention (planner, split-K partial kernel,
+log-sum-exp merge).  Inputs are resident in HBM before timing starts.
 
-Prints one JSON line with the whole-step throughput (algorithmic HBM bytes
-per second), decode tokens/s, the roofline of the dominant kernel (the
-split-K decode kernel, timed with HIP events on the launch stream) and the
-oracle's CPU throughput on a bounded sample of the same workload.
+Other workloads (--workload): gqa_prefix_share_ps16 / _ps64 (batch-256 GQA
+decode with shared 2048-token prefixes), mla_decode (latent 576/512, 128
+heads, page_size 64), encdec_extend (Whisper-shaped causal + cross extend
+over a paged prefix), encdec_extend_ragged (the same through kv_gather and
+contiguous K/V), tiny_decode (fp32 correctness shape).
+
+Prints one JSON line: whole-step throughput (algorithmic HBM bytes per
+second), tokens per second, the roofline of the dominant kernel (timed with
+HIP events on the launch stream) and the oracle's CPU throughput on a
+bounded sample of the same workload.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 """
@@ -28,7 +34,7 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
-BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA, published
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 
 
 # ---------------------------------------------------------------------------
@@ -58,17 +64,45 @@ class HipEvents:
         self.hip.hipEventDestroy(C.c_void_p(e))
 
 
-def i32(a, dev):
+def i32(a, dev="cuda"):
     import torch
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
 
 
+def _blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"]
+        return int(max(n)) if n else 1
+    except Exception:
+        return 1
+
+
+def _row_bytes(g) -> int:
+    """One token's K and V rows over all KV heads (a latent row once)."""
+    return g.num_kv_heads * (g.head_dim_qk + (0 if g.latent else g.head_dim_v)) * g.elem_bytes
+
+
+def _make_pool(case, vals):
+    """Pool built over the generated values (one layer)."""
+    import paged_kv_cache_38_amd as P
+    g = case.geom
+    return P.kv_pool_create(vals["pool_k"].reshape(-1), None if g.latent else vals["pool_v"].reshape(-1),
+                            num_layers=1, num_pages=g.num_pages, page_size=g.page_size, num_kv_heads=g.num_kv_heads,
+                            head_dim_qk=g.head_dim_qk, head_dim_v=g.head_dim_v, latent=g.latent)
+
+
 # ---------------------------------------------------------------------------
-# workloads
+# decode workloads
 # ---------------------------------------------------------------------------
 class DecodeBench:
-    """Decode step: optional kv_store of this step's tokens, optional
-    build_kv_indices, then paged decode attention."""
+    """Decode step: kv_store of this step's tokens (if any), build_kv_indices
+    (page-granular formats), then paged decode attention."""
+
+    bound = "hbm"
+    kernel_name = "paged decode split-K partial kernel"
+    attn_calls = 1
+    tokens_label = "decode_tokens_per_s"
 
     def __init__(self, case, fmt: str, dev="cuda"):
         import torch
@@ -79,22 +113,14 @@ class DecodeBench:
         g = case.geom
         dt = torch.float32 if g.dtype == "f32" else torch.bfloat16
         self.vals = W.make_values(case, device=dev)
-        kb, vb = P.kv_pool_bytes(1, g.num_pages, g.page_size, g.num_kv_heads, g.head_dim_qk,
-                                 g.head_dim_v, dt, g.latent)
-        self.k_buf = self.vals["pool_k"].reshape(-1)
-        self.v_buf = None if g.latent else self.vals["pool_v"].reshape(-1)
-        assert self.k_buf.numel() * dt.itemsize == kb
-        self.pool = P.kv_pool_create(self.k_buf, self.v_buf, num_layers=1, num_pages=g.num_pages,
-                                     page_size=g.page_size, num_kv_heads=g.num_kv_heads, head_dim_qk=g.head_dim_qk,
-                                     head_dim_v=g.head_dim_v, latent=g.latent)
+        self.pool = _make_pool(case, self.vals)
         r = case.regions["self"]
         self.kv_lens = i32(r.kv_lens, dev)
         self.kv_start = i32(r.kv_start, dev)
         self.rpi = i32(case.req_pool_indices, dev)
         self.table = i32(case.req_to_token, dev)
         self.out_loc = i32(case.out_loc, dev)
-        self.k_new = self.vals["k_new"]
-        self.v_new = self.vals["v_new"]
+        self.k_new, self.v_new = self.vals["k_new"], self.vals["v_new"]
         self.q = self.vals["q"]["self"]
         self.max_len = int(r.kv_lens.max())
         self.fmt = fmt
@@ -116,7 +142,7 @@ class DecodeBench:
         nb = P.paged_decode_workspace_bytes(self.pool, case.bs, g.num_q_heads, self.max_len)
         self.ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
 
-    def step(self):
+    def step(self, timers=None):
         P, c = self.P, self.case
         if c.n_new:
             P.kv_store(self.pool, 0, self.k_new, self.v_new, self.out_loc)
@@ -127,35 +153,32 @@ class DecodeBench:
         elif self.fmt == "block_table":
             P.build_kv_indices(P.PKV_MAP_BLOCK_TABLE, self.table, self.rpi, self.kv_start, self.kv_lens, ps,
                                self.max_len, None, self.bt)
+        if timers:
+            P.pkv_set_kernel_timer(*timers[0])
         P.paged_decode_attn(self.pool, 0, self.q, self.map, c.sm_scale, self.out, self.lse, self.ws)
 
-    # algorithmic bytes ----------------------------------------------------
     def kernel_bytes(self) -> int:
-        """Decode split kernel: each live token's K and V rows (all KV
-        heads) once, its slot/page index, and the queries."""
+        """Decode split kernel: each live token's K/V rows once, its slot (or
+        page id share), and the queries."""
         c, g = self.case, self.case.geom
         tok = int(c.regions["self"].kv_lens.sum())
-        row = g.num_kv_heads * (g.head_dim_qk + (0 if g.latent else g.head_dim_v)) * g.elem_bytes
         idx = 4 if g.page_size == 1 or self.fmt == "token_table" else 4.0 / g.page_size
-        return int(tok * (row + idx) + c.bs * g.num_q_heads * g.head_dim_qk * g.elem_bytes)
+        return int(tok * (_row_bytes(g) + idx) + c.bs * g.num_q_heads * g.head_dim_qk * g.elem_bytes)
 
     def step_bytes(self) -> int:
         c, g = self.case, self.case.geom
         out_b = c.bs * g.num_q_heads * g.head_dim_v * g.elem_bytes
-        row = g.num_kv_heads * (g.head_dim_qk + (0 if g.latent else g.head_dim_v)) * g.elem_bytes
-        store_b = c.n_new * (2 * row + 4)
-        return self.kernel_bytes() + out_b + store_b
+        return self.kernel_bytes() + out_b + c.n_new * (2 * _row_bytes(g) + 4)
 
     def kernel_flops(self) -> int:
         c, g = self.case, self.case.geom
         tok = int(c.regions["self"].kv_lens.sum())
         return 2 * tok * g.num_q_heads * (g.head_dim_qk + g.head_dim_v)
 
-    def decode_tokens(self) -> int:
+    def tokens_per_step(self) -> int:
         return self.case.bs
 
-    # CPU baseline: the oracle on a bounded sample --------------------------
-    def cpu_baseline(self, budget_s: float = 15.0):
+    def cpu_baseline(self, budget_s: float):
         import oracle
         from workloads.cases import to_numpy_bits
 
@@ -170,7 +193,7 @@ class DecodeBench:
         # whole passes over the batch (request by request) until the budget is
         # spent, so the rate is measured over ~budget_s of oracle work
         reqs, toks, t0 = 0, 0, time.perf_counter()
-        while True:
+        while time.perf_counter() - t0 <= budget_s:
             for i in range(c.bs):
                 oracle.paged_attention(q, c.q_lens, pk, pv, g.dtype, slots, c.sm_scale, True,
                                        head_dim_v=g.head_dim_v, requests=[i])
@@ -178,11 +201,8 @@ class DecodeBench:
                 toks += int(r.kv_lens[i])
                 if time.perf_counter() - t0 > budget_s:
                     break
-            if time.perf_counter() - t0 > budget_s:
-                break
         dt = time.perf_counter() - t0
-        row = g.num_kv_heads * (g.head_dim_qk + (0 if g.latent else g.head_dim_v)) * g.elem_bytes
-        gbs = toks * (row + 4) / dt / 1e9
+        gbs = toks * (_row_bytes(g) + 4) / dt / 1e9
         return {"value": round(gbs, 4), "unit": "GB/s", "cores": _blas_threads(), "kind": "oracle",
                 "decode_tokens_per_s": round(reqs / dt, 3),
                 "sample": f"{reqs} request decodes ({reqs / c.bs:.2f} passes over the {c.bs}-request batch, "
@@ -190,30 +210,160 @@ class DecodeBench:
                           f"{dt:.1f} s"}
 
 
-def _blas_threads() -> int:
-    try:
-        from threadpoolctl import threadpool_info
-        n = [d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"]
-        return int(max(n)) if n else 1
-    except Exception:
-        return 1
+# ---------------------------------------------------------------------------
+# extend workload (encoder-decoder)
+# ---------------------------------------------------------------------------
+class ExtendBench:
+    """Extend step: kv_store of the new decoder tokens, CSR build for the
+    decoder and encoder regions, causal extend over the decoder region and
+    non-causal extend over the encoder region (ragged: kv_gather of both
+    regions, then extend over the contiguous copies)."""
+
+    bound = "mfma"
+    attn_calls = 2
+    tokens_label = "extend_tokens_per_s"
+
+    def __init__(self, case, ragged: bool, dev="cuda"):
+        import torch
+        import paged_kv_cache_38_amd as P
+        import workloads as W
+
+        self.case, self.P, self.torch, self.ragged = case, P, torch, ragged
+        self.kernel_name = "paged extend attention kernel" + (" (contiguous K/V after kv_gather)" if ragged else "")
+        g = case.geom
+        self.vals = W.make_values(case, device=dev)
+        self.pool = _make_pool(case, self.vals)
+        self.rpi = i32(case.req_pool_indices, dev)
+        self.table = i32(case.req_to_token, dev)
+        self.out_loc = i32(case.out_loc, dev)
+        self.qo = i32(np.concatenate([[0], np.cumsum(case.q_lens)]), dev)
+        self.max_q = int(case.q_lens.max())
+        self.total_q = int(case.q_lens.sum())
+        self.regions = {}
+        for name, r in case.regions.items():
+            maxl = int(r.kv_lens.max())
+            per = max(-(-maxl // g.page_size), 1)
+            d = {"kv_start": i32(r.kv_start, dev), "kv_lens": i32(r.kv_lens, dev), "max": maxl,
+                 "indptr": torch.empty(case.bs + 1, dtype=torch.int32, device=dev),
+                 "indices": torch.empty(case.bs * per, dtype=torch.int32, device=dev),
+                 "q": self.vals["q"][name], "causal": r.causal,
+                 "out": torch.empty((self.total_q, g.num_q_heads, g.head_dim_v), dtype=torch.bfloat16, device=dev),
+                 "lse": torch.empty((self.total_q, g.num_q_heads), dtype=torch.float32, device=dev)}
+            d["map"] = P.make_kv_map(P.PKV_MAP_CSR, d["kv_lens"], maxl, kv_indptr=d["indptr"],
+                                     kv_indices=d["indices"])
+            if ragged:
+                cu = np.concatenate([[0], np.cumsum(r.kv_lens)]).astype(np.int64)
+                tot = int(cu[-1])
+                d["cu"] = i32(cu, dev)
+                d["k"] = torch.empty((max(tot, 1), g.num_kv_heads, g.head_dim_qk), dtype=torch.bfloat16, device=dev)
+                d["v"] = torch.empty_like(d["k"])
+                d["cmap"] = P.make_kv_map(P.PKV_MAP_CONTIGUOUS, d["kv_lens"], maxl, k=d["k"][:tot], v=d["v"][:tot],
+                                          cu_seqlens_k=d["cu"])
+            self.regions[name] = d
+
+    def step(self, timers=None):
+        P, c = self.P, self.case
+        P.kv_store(self.pool, 0, self.vals["k_new"], self.vals["v_new"], self.out_loc)
+        for k, (name, d) in enumerate(self.regions.items()):
+            P.build_kv_indices(P.PKV_MAP_CSR, self.table, self.rpi, d["kv_start"], d["kv_lens"], c.geom.page_size,
+                               d["max"], d["indptr"], d["indices"])
+            m = d["map"]
+            if self.ragged:
+                P.kv_gather(self.pool, 0, m, d["cu"], d["k"], d["v"])
+                m = d["cmap"]
+            if timers:
+                P.pkv_set_kernel_timer(*timers[k])
+            P.paged_extend_attn(self.pool, 0, d["q"], self.qo, self.max_q, m, d["causal"], c.sm_scale, d["out"],
+                                d["lse"])
+
+    def _pairs(self, name) -> int:
+        """Unmasked (query, key) pairs of one region."""
+        c = self.case
+        r = c.regions[name]
+        n = c.q_lens.astype(np.int64)
+        L = r.kv_lens.astype(np.int64)
+        if r.causal:  # query j sees L - n + j + 1 keys
+            return int(np.sum(n * (L - n) + n * (n + 1) // 2))
+        return int(np.sum(n * L))
+
+    def kernel_flops(self) -> int:
+        g = self.case.geom
+        return sum(self._pairs(nm) for nm in self.case.regions) * g.num_q_heads * 2 * (g.head_dim_qk + g.head_dim_v)
+
+    def kernel_bytes(self) -> int:
+        """Both extend calls: every key row of both regions once, the queries
+        and the outputs of both calls."""
+        c, g = self.case, self.case.geom
+        rows = sum(int(r.kv_lens.sum()) for r in c.regions.values())
+        qo = 2 * self.total_q * g.num_q_heads * g.head_dim_qk * g.elem_bytes
+        return rows * _row_bytes(g) + 2 * qo
+
+    def step_bytes(self) -> int:
+        c, g = self.case, self.case.geom
+        b = self.kernel_bytes() + c.n_new * (2 * _row_bytes(g) + 4)
+        if self.ragged:
+            rows = sum(int(r.kv_lens.sum()) for r in c.regions.values())
+            b += 2 * rows * _row_bytes(g)  # gather reads and writes every row once more
+        return b
+
+    def tokens_per_step(self) -> int:
+        return self.total_q
+
+    def cpu_baseline(self, budget_s: float):
+        import oracle
+        from workloads.cases import to_numpy_bits
+
+        c, g = self.case, self.case.geom
+        self.torch.cuda.synchronize()
+        pk, pv = to_numpy_bits(self.pool.flat("k", 0)), to_numpy_bits(self.pool.flat("v", 0))
+        qs = {nm: to_numpy_bits(self.vals["q"][nm]) for nm in c.regions}
+        reqs, toks, t0 = 0, 0, time.perf_counter()
+        while time.perf_counter() - t0 <= budget_s:
+            for i in range(c.bs):
+                for nm, r in c.regions.items():
+                    slots = [oracle.slots_from_token_table(c.req_to_token, c.req_pool_indices[i], r.kv_start[i],
+                                                           r.kv_lens[i]) if j == i else np.zeros(0, np.int64)
+                             for j in range(c.bs)]
+                    oracle.paged_attention(qs[nm], c.q_lens, pk, pv, g.dtype, slots, c.sm_scale, r.causal,
+                                           requests=[i])
+                reqs += 1
+                toks += int(c.q_lens[i])
+                if time.perf_counter() - t0 > budget_s:
+                    break
+        dt = time.perf_counter() - t0
+        return {"value": round(toks / dt, 2), "unit": "extend tokens/s", "cores": _blas_threads(), "kind": "oracle",
+                "sample": f"{reqs} request extends (self + cross; {reqs / c.bs:.2f} passes over the {c.bs}-request "
+                          f"batch, {toks} new tokens) by the numpy fp64 oracle, {dt:.1f} s"}
 
 
 def build_workload(name: str):
     import workloads as W
     if name == "qwen3_decode":
-        return W.qwen3_decode(seed=0), "token_table", {
+        return DecodeBench(W.qwen3_decode(seed=0), "token_table"), {
             "workload": "qwen3_0.6b_decode_bf16", "batch": 64, "num_q_heads": 16, "num_kv_heads": 8,
             "head_dim": 128, "page_size": 1, "kv_len": "U[512,4096]", "pool_tokens": 400000,
             "table": "req_to_token [65, 8192]", "step": "kv_store + paged_decode_attn"}
     if name.startswith("gqa_prefix_share_ps"):
         ps = int(name[len("gqa_prefix_share_ps"):])
-        return W.gqa_prefix_share(ps, seed=0), "csr", {
+        return DecodeBench(W.gqa_prefix_share(ps, seed=0), "csr"), {
             "workload": f"gqa_prefix_share_decode_bf16_ps{ps}", "batch": 256, "num_q_heads": 32,
             "num_kv_heads": 8, "head_dim": 128, "page_size": ps, "kv_len": "lognormal(2048, 1) clip [64, 32768]",
             "prefix_share": "groups of 8 share 2048 tokens", "step": "build_kv_indices(CSR) + paged_decode_attn"}
+    if name == "mla_decode":
+        return DecodeBench(W.mla_decode(seed=0), "block_table"), {
+            "workload": "mla_decode_bf16", "batch": 128, "num_q_heads": 128, "head_dim_qk": 576, "head_dim_v": 512,
+            "page_size": 64, "kv_len": "U[4096,16384]",
+            "step": "kv_store + build_kv_indices(BLOCK_TABLE) + paged_decode_attn"}
+    if name in ("encdec_extend", "encdec_extend_ragged"):
+        ragged = name.endswith("ragged")
+        return ExtendBench(W.encdec_extend(seed=0), ragged), {
+            "workload": "whisper_encdec_extend_bf16" + ("_ragged" if ragged else ""), "batch": 32, "num_heads": 20,
+            "head_dim": 64, "page_size": 16, "encoder_len": 1500, "decoder_prefix": "U{0..448}",
+            "new_tokens": "U{1..512}",
+            "step": "kv_store + build_kv_indices(CSR) x2 + " + ("kv_gather x2 + " if ragged else "")
+                    + "paged_extend_attn (causal self + cross)"}
     if name == "tiny_decode":
-        return W.tiny_decode(seed=0), "csr", {"workload": "tiny_decode_f32", "batch": 4, "page_size": 16}
+        return DecodeBench(W.tiny_decode(seed=0), "csr"), {"workload": "tiny_decode_f32", "batch": 4, "page_size": 16}
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -237,31 +387,38 @@ def main():
     import torch
 
     torch.cuda.init()
-    case, fmt, cfg = build_workload(args.workload)
-    b = DecodeBench(case, fmt)
+    b, cfg = build_workload(args.workload)
     ev = HipEvents()
-    import paged_kv_cache_38_amd as P
-
     for _ in range(args.warmup):
         b.step()
     torch.cuda.synchronize()
-    pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    pairs = [[(ev.create(), ev.create()) for _ in range(b.attn_calls)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        P.pkv_set_kernel_timer(*pairs[k])
-        b.step()
+        b.step(pairs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kern_ms = [ev.elapsed_ms(a, z) for a, z in pairs]
-    for a, z in pairs:
-        ev.destroy(a)
-        ev.destroy(z)
+    kern_ms = [sum(ev.elapsed_ms(a, z) for a, z in step) for step in pairs]
+    for step in pairs:
+        for a, z in step:
+            ev.destroy(a)
+            ev.destroy(z)
 
     ms_step = wall * 1e3 / args.steps
     k_ms = float(np.mean(kern_ms))
     step_gbs = b.step_bytes() / (ms_step * 1e-3) / 1e9
     kern_gbs = b.kernel_bytes() / (k_ms * 1e-3) / 1e9
+    kern_tf = b.kernel_flops() / (k_ms * 1e-3) / 1e12
+    if b.bound == "hbm":
+        roof = {"bound": "hbm", "achieved": round(kern_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(kern_gbs / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(kern_tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(kern_tf / BF16_PEAK_TFLOPS, 4)}
+    roof.update({"traffic": None, "kernel": b.kernel_name, "kernel_ms": round(k_ms, 5),
+                 "kernel_bytes": b.kernel_bytes(), "kernel_gbs": round(kern_gbs, 2),
+                 "kernel_hbm_frac": round(kern_gbs / HBM_PEAK_GBS, 4), "kernel_tflops": round(kern_tf, 3)})
     res = {
         "metric": "paged decode attn: achieved HBM GB/s (% of peak) + decode tokens/s, 1 GPU",
         "value": round(step_gbs, 2),
@@ -273,23 +430,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": case.geom.dtype,
+        "dtype": b.case.geom.dtype,
         "data": "synthetic (seeded; N(0,1) values)",
         "config": cfg,
         "hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
-        "decode_tokens_per_s": round(b.decode_tokens() / (ms_step * 1e-3), 1),
-        "roofline": {
-            "kernel": "decode split-K partial (paged_decode_attn)",
-            "bound": "hbm",
-            "achieved": round(kern_gbs, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "kernel_ms": round(k_ms, 5),
-            "kernel_bytes": b.kernel_bytes(),
-            "kernel_tflops": round(b.kernel_flops() / (k_ms * 1e-3) / 1e12, 3),
-        },
+        b.tokens_label: round(b.tokens_per_step() / (ms_step * 1e-3), 1),
+        "roofline": roof,
     }
     if args.calibrate_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
