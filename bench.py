@@ -35,6 +35,37 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the workload's dominant kernel, from the
+    FETCH_SIZE / WRITE_SIZE counter passes summarised under profiles/ (each
+    scaled by what the counter reads for a plain copy of known size). None
+    when no record exists or when the kernel's sources changed since the
+    counters were taken (the record carries their sha256)."""
+    import glob
+    import hashlib
+
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        with open(path) as fh:
+            for line in fh:
+                if not line.startswith("traffic_record: "):
+                    continue
+                rec = json.loads(line[len("traffic_record: "):])
+                if rec.get("workload") != workload:
+                    continue
+                h = hashlib.sha256()
+                try:
+                    for src in rec["sources"]:
+                        with open(os.path.join(ROOT, src), "rb") as sf:
+                            h.update(sf.read())
+                except OSError:
+                    return None
+                if h.hexdigest() != rec["sources_sha256"]:
+                    return None
+                return int(rec["traffic_bytes"])
+    return None
 
 
 # ---------------------------------------------------------------------------
@@ -416,7 +447,7 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(kern_tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(kern_tf / BF16_PEAK_TFLOPS, 4)}
-    roof.update({"traffic": None, "kernel": b.kernel_name, "kernel_ms": round(k_ms, 5),
+    roof.update({"traffic": measured_traffic(args.workload), "kernel": b.kernel_name, "kernel_ms": round(k_ms, 5),
                  "kernel_bytes": b.kernel_bytes(), "kernel_gbs": round(kern_gbs, 2),
                  "kernel_hbm_frac": round(kern_gbs / HBM_PEAK_GBS, 4), "kernel_tflops": round(kern_tf, 3)})
     res = {
