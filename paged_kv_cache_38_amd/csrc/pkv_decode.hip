@@ -581,6 +581,7 @@ size_t decode_ws_layout(const PoolInfo& p, const DecodePlan& plan, int32_t bs, i
 }
 
 size_t decode_workspace_bytes(const PoolInfo& p, const DecodePlan& plan, int32_t bs, int32_t Hq) {
+  if (plan.kind == DK_MLA) return mla_ws_layout(plan, bs, Hq, nullptr, nullptr);
   return decode_ws_layout(p, plan, bs, Hq, nullptr, nullptr);
 }
 
@@ -619,6 +620,7 @@ static void launch_valu(unsigned blocks, hipStream_t s, const DevMap& m, const P
 hipError_t launch_decode(const PoolInfo& p, int32_t layer, const void* q, int32_t Hq, const DevMap& m, int32_t bs,
                          const DecodePlan& plan, float sm_scale, void* out, float* lse, void* ws, hipStream_t s) {
   if (bs == 0) return hipSuccess;
+  if (plan.kind == DK_MLA) return launch_mla_decode(p, layer, q, Hq, m, bs, plan, sm_scale * kLog2e, out, lse, ws, s);
   const int Hkv = p.num_kv_heads;
   const int G = Hq / Hkv;
   const int W = (Hkv % 4 == 0) ? 4 : (Hkv % 2 == 0 ? 2 : 1);
@@ -633,9 +635,7 @@ hipError_t launch_decode(const PoolInfo& p, int32_t layer, const void* q, int32_
   const float sl2 = sm_scale * kLog2e;
   const int D = p.head_dim_qk;
   timer_before(s);
-  if (plan.kind == DK_MLA) {
-    launch_mla_split(p, layer, q, Hq, m, bs, plan, w, sl2, out, lse, s);
-  } else if (plan.kind == DK_MFMA) {
+  if (plan.kind == DK_MFMA) {
     if (D == 128) {
       if (W == 4) launch_mfma_fmt<128, 4>(blocks, s, m, p, layer, q, Hq, G, hg, plan, w, sl2, out, lse);
       else if (W == 2) launch_mfma_fmt<128, 2>(blocks, s, m, p, layer, q, Hq, G, hg, plan, w, sl2, out, lse);

@@ -86,10 +86,22 @@ struct DecodeWs {
 size_t decode_ws_layout(const PoolInfo& p, const DecodePlan& plan, int32_t bs, int32_t Hq, void* base, DecodeWs* w);
 
 bool mla_decode_supported(const PoolInfo& p, int32_t num_q_heads);
+// MLA plan: chunk = tiles (32 tokens) per request at most, max_splits = main
+// grid (one workgroup per CU)
 DecodePlan plan_mla_decode(const PoolInfo& p, int32_t bs, int32_t num_q_heads, int32_t max_kv_len);
-void launch_mla_split(const PoolInfo& p, int32_t layer, const void* q, int32_t num_q_heads, const DevMap& m,
-                      int32_t bs, const DecodePlan& plan, const DecodeWs& w, float scale_log2, void* out, float* lse,
-                      hipStream_t s);
+// MLA workspace: [header | tile prefix | tiles | per-tile slot ids + info | pieces o | pieces lse]
+struct MlaWs {
+  int32_t* header;  // run length (tiles per workgroup), total tiles
+  int32_t* prefix;
+  int32_t* ntiles;
+  int32_t* meta;
+  float* o;
+  float* lse;
+};
+size_t mla_ws_layout(const DecodePlan& plan, int32_t bs, int32_t num_q_heads, void* base, MlaWs* w);
+hipError_t launch_mla_decode(const PoolInfo& p, int32_t layer, const void* q, int32_t num_q_heads, const DevMap& m,
+                             int32_t bs, const DecodePlan& plan, float scale_log2, void* out, float* lse, void* ws,
+                             hipStream_t s);
 DecodePlan plan_decode(const PoolInfo& p, int32_t bs, int32_t num_q_heads, int32_t max_kv_len);
 size_t decode_workspace_bytes(const PoolInfo& p, const DecodePlan& plan, int32_t bs, int32_t num_q_heads);
 bool decode_supported(const PoolInfo& p, int32_t num_q_heads);

@@ -1,22 +1,40 @@
-// MLA (latent) paged decode: the split-K partial kernel.
+// MLA (latent) paged decode.
 //
 // What is computed: the decode of [XPU] "From slots to a page table" and
 // [BACKEND] init_forward_metadata over a latent pool -- one cached row per
 // token of head_dim_qk = 576 values (512 latent + 64 rope, [BACKEND] "页表构建":
 // kv_lora_rank / qk_rope_head_dim), shared by every query head.  Keys are the
-// whole row; values are its first 512 entries.  Splitting, planning and the
-// log-sum-exp merge are those of the grouped-query decode (pkv_decode.hip).
+// whole row; values are its first 512 entries.  The result is softmax
+// attention over each request's keys in logical order; splitting is an
+// implementation detail merged back exactly with log-sum-exp weights.
 //
-// Layout on gfx950: one block per (item, group of up to 64 query heads);
-// each wavefront owns 16 heads.  A 32-token tile of latent rows (36 KiB) is
-// gathered into LDS once per block (double buffered) and shared by all
-// wavefronts:
-//   S^T[16 tokens x 16 heads] = K_tile[16 x 576] * Q^T[576 x 16]   (18 MFMAs per 16 tokens)
-//   O[16 heads x 512]        += P[16 x 32] * V_tile[32 x 512]     (32 MFMAs, B from ds_read_b64_tr_b16)
-// The latent rows are read from HBM exactly once per block; every head
-// reuses them from LDS (the 128-head reuse is what makes this a dense
-// contraction rather than a streaming dot product).
+// Design for gfx950 (one workgroup per CU, all query heads of a request in
+// one workgroup, so every latent row leaves HBM exactly once):
+//
+//  * Work split.  The requests' 32-token tiles are laid end to end and the
+//    grid (one workgroup per CU) takes equal contiguous runs of them, so every
+//    CU streams the same number of bytes whatever the length mix.  A run may
+//    end inside a request and the next run continue it: such pieces are
+//    partial results, merged afterwards.  A planner kernel resolves every tile
+//    to its 32 slot ids (through any table format) before the main kernel
+//    starts, so the main kernel never touches a table.
+//  * Streaming.  Tiles move HBM -> LDS with global_load_lds_dwordx4 (no
+//    staging registers), three tiles deep: while tile r is computed, tiles
+//    r+1 and r+2 are in flight.  The tile layout in LDS is row-major with a
+//    16-byte-chunk XOR swizzle (chunk c of token t sits at c ^ (t & 7)), so
+//    both the K-operand reads and the transposed V-operand reads are free of
+//    bank conflicts.  These loads are issued from inline assembly and waited
+//    on explicitly, because the compiler would otherwise drain the whole
+//    queue before every LDS read.
+//  * Math.  Wave w computes S^T = K Q^T for its 32 heads (queries held in
+//    registers) and the softmax for them; P goes through LDS; then every wave
+//    computes O += P V for all heads over its own slice of the 512 value
+//    columns (accumulators in AGPRs).  Rescaling is lazy: the running maximum
+//    is only moved when a score exceeds it by more than 2^8, which keeps P
+//    below 256 and skips almost every accumulator rescale.
 #include <math.h>
+
+#include <algorithm>
 
 #include "pkv_launch.h"
 
@@ -24,174 +42,431 @@ namespace pkv {
 
 constexpr int kMlaQK = 576;
 constexpr int kMlaV = 512;
-constexpr int kMlaTile = 32;
-constexpr int kMlaLds = kMlaQK + 8;                 // LDS row stride (elements)
-constexpr int kMlaChunks = kMlaTile * kMlaQK / 8;   // 16-byte chunks per tile
-constexpr int kMlaCpt = kMlaQK / 8;                 // chunks per token row
+constexpr int kMlaT = 32;                         // tokens per tile
+constexpr int kMlaRowChunks = kMlaQK / 8;         // 72 sixteen-byte chunks per row
+constexpr int kMlaRowBytes = kMlaQK * 2;          // 1152
+constexpr int kMlaTileBytes = kMlaT * kMlaRowBytes;  // 36864
+constexpr int kMlaMetaWords = 40;                 // per tile: 32 slot ids + 8 info words
+constexpr float kMlaSlack = 8.0f;                 // log2 headroom before the running max moves
 
-template <int W>
-struct MlaRegs {
-  static constexpr int IT = (kMlaChunks + 64 * W - 1) / (64 * W);
-  u32x4 v[IT];
+// Launch shape per workgroup of HPB heads (16, 32 or 64): W waves; wave w
+// computes scores for HB blocks of 16 heads and output columns
+// [w * CW, (w + 1) * CW) of all HPB heads.  A wave then holds 72 VGPRs of
+// queries and 128 accumulators.  More than 64 heads take sibling workgroups
+// (one per 64 heads) that stream the same tiles on the same XCD, the second
+// read served by its L2.
+template <int HPB>
+struct MlaCfg {
+  static constexpr int W = HPB / 16;
+  static constexpr int HB = 1;
+  static constexpr int NHB = HPB / 16;
+  static constexpr int CW = kMlaV / W;
+  static constexpr int NCB = CW / 16;
+  static constexpr int NI = (kMlaTileBytes / 1024) / W;  // tile DMA instructions per wave
 };
 
-template <int W, int FMT>
-__device__ __forceinline__ void mla_load(MlaRegs<W>& R, const SlotMap<FMT>& sm, int t0, int t_end, const bf16* kp) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int it = 0; it < MlaRegs<W>::IT; ++it) {
-    const int c = min(it * 64 * W + tid, kMlaChunks - 1);
-    const int tok = c / kMlaCpt, cc = c % kMlaCpt;
-    const int t = t0 + tok;
-    const int64_t slot = sm(t, t < t_end);
-    R.v[it] = *reinterpret_cast<const u32x4*>(kp + slot * kMlaQK + cc * 8);
-  }
+__device__ __forceinline__ uint32_t lds_off(const void* p) {
+  // the LDS aperture is 4 GiB aligned: the low 32 bits of a flat LDS address
+  // are the LDS byte offset
+  return (uint32_t)(uintptr_t)p;
 }
 
-template <int W>
-__device__ __forceinline__ void mla_store(const MlaRegs<W>& R, int t0, int t_end, bf16* ks) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int it = 0; it < MlaRegs<W>::IT; ++it) {
-    const int c = it * 64 * W + tid;
-    if (c < kMlaChunks) {
-      const int tok = c / kMlaCpt, cc = c % kMlaCpt;
-      u32x4 w = R.v[it];
-      if (t0 + tok >= t_end) w = u32x4{0u, 0u, 0u, 0u};  // masked keys hold 0
-      *reinterpret_cast<u32x4*>(ks + tok * kMlaLds + cc * 8) = w;
-    }
-  }
+// one 16-byte chunk per lane, global -> LDS at m0 + 16 * lane
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+// one dword per lane, global -> LDS at m0 + 4 * lane
+__device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
+  asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int W, int FMT>
-__global__ void __launch_bounds__(64 * W, 1) mla_decode_kernel(
-    DevMap m, const bf16* k_pool, const bf16* __restrict__ q, int32_t Hq, int32_t hg, int32_t chunk,
-    int32_t max_splits, const WorkItem* __restrict__ items, const int32_t* __restrict__ item_count, float scale_log2,
-    bf16* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws_o, float* __restrict__ ws_lse) {
-  constexpr int NK = kMlaQK / 32;  // 18
-  constexpr int NT = kMlaV / 16;   // 32
-  __shared__ __attribute__((aligned(16))) bf16 ksm[2][kMlaTile * kMlaLds];
+// byte offset of chunk c of token t inside a swizzled tile
+__device__ __forceinline__ int mla_chunk_off(int t, int c) { return (t * kMlaRowChunks + (c ^ (t & 7))) * 16; }
 
-  const int w_item = blockIdx.x / hg;
-  if (w_item >= *item_count) return;
-  const WorkItem item = items[w_item];
-  const int i = item.i, s = item.s, ns = item.ns;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int col = lane & 15, grp = lane >> 4;
-  const int h0 = ((blockIdx.x % hg) * W + wave) * 16;  // this wave's 16 heads
+// B operand of P*V (16x16x32 MFMA) from a swizzled tile: lane (n = l%16,
+// j = l/16) receives V[4j + r][c0 + n] (r = 0..3) and V[16 + 4j + r][c0 + n].
+__device__ __forceinline__ bf16x8 mla_v_operand(const char* tile, int c0, int lane) {
+  const int x = lane & 15, j = lane >> 4;
+  const int t = 4 * j + (x >> 2);
+  const int c = c0 + 4 * (x & 3);
+  const char* lo = tile + mla_chunk_off(t, c >> 3) + (c & 7) * 2;
+  const i16x4 a = lds_read_tr16(reinterpret_cast<const bf16*>(lo));
+  const i16x4 b = lds_read_tr16(reinterpret_cast<const bf16*>(lo + 16 * kMlaRowBytes));
+  const bf16x4 ba = __builtin_bit_cast(bf16x4, a), bb = __builtin_bit_cast(bf16x4, b);
+  return bf16x8{ba[0], ba[1], ba[2], ba[3], bb[0], bb[1], bb[2], bb[3]};
+}
 
-  if (ns == 0) {  // empty key set: zero output, lse = -inf
-    for (int n = 0; n < 16; ++n) {
-      const int64_t h = (int64_t)i * Hq + h0 + n;
-      for (int d = lane; d < kMlaV; d += 64) out[h * kMlaV + d] = (bf16)0.0f;
-      if (lse && lane == 0) lse[h] = -INFINITY;
-    }
-    return;
+// ---------------------------------------------------------------------------
+// Planner: one workgroup per request.  Writes the tile prefix, the run
+// length Bt of the main grid, and per tile its 32 slot ids (tokens past the
+// request's end repeat its last key, whose weight is then exactly 0) and
+// info words {request, tile, tiles of request, tile prefix, valid keys}.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int32_t mla_tiles(int32_t L) { return L > 0 ? (L + kMlaT - 1) / kMlaT : 0; }
+
+template <int FMT>
+__global__ void __launch_bounds__(256) mla_plan_kernel(DevMap m, int32_t bs, int32_t max_tiles, int32_t runs,
+                                                       int32_t* __restrict__ header,
+                                                       int32_t* __restrict__ prefix, int32_t* __restrict__ ntiles,
+                                                       int32_t* __restrict__ meta) {
+  __shared__ int32_t red[2][4];
+  const int i = blockIdx.x;
+  const int tid = threadIdx.x;
+  int32_t tot = 0, pre = 0;
+  for (int k = tid; k < bs; k += 256) {
+    const int32_t T = min(mla_tiles(m.kv_lens[k]), max_tiles);
+    tot += T;
+    if (k < i) pre += T;
   }
-  const int t_begin = s * chunk;
-  const int t_end = item.t_end;
-  const SlotMap<FMT> sm = slotmap_from_view<FMT>(m, item_view(item));
-
-  // Q^T operand: lane (head col, group grp) holds q[h0 + col][kk*32 + grp*8 .. +8]
-  bf16x8 qb[NK];
-  {
-    const bf16* qp = q + ((int64_t)i * Hq + h0 + col) * kMlaQK + grp * 8;
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk) qb[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + kk * 32));
+  for (int o = 32; o > 0; o >>= 1) {
+    tot += __shfl_xor(tot, o, 64);
+    pre += __shfl_xor(pre, o, 64);
   }
-  f32x4 acc[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
-
-  const int ntiles = (t_end - t_begin + kMlaTile - 1) / kMlaTile;
-  MlaRegs<W> R;
-  mla_load<W, FMT>(R, sm, t_begin, t_end, k_pool);
-  mla_store<W>(R, t_begin, t_end, ksm[0]);
+  if ((tid & 63) == 0) {
+    red[0][tid >> 6] = tot;
+    red[1][tid >> 6] = pre;
+  }
   __syncthreads();
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int t0 = t_begin + kt * kMlaTile;
-    // next tile in flight during this tile's math (unconditional: past the
-    // end it reads the padding row, which stays in cache)
-    mla_load<W, FMT>(R, sm, t0 + kMlaTile, t_end, k_pool);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    const bf16* ks = ksm[kt & 1];
-    // ---- S^T = K Q^T
-    f32x4 sacc[2];
+  tot = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+  pre = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+  // keys past max_kv_len (a caller error) are not read: the workspace holds
+  // max_tiles tiles per request
+  const int32_t T = min(mla_tiles(m.kv_lens[i]), max_tiles);
+  const int32_t L = min(max(m.kv_lens[i], 0), T * kMlaT);
+  if (tid == 0) {
+    prefix[i] = pre;
+    ntiles[i] = T;
+    if (i == 0) {
+      header[0] = max(1, (tot + runs - 1) / runs);
+      header[1] = tot;
+    }
+  }
+  if (T == 0) return;
+  const SlotMap<FMT> sm = make_slotmap<FMT>(m, i);
+  for (int e = tid; e < T * kMlaT; e += 256) {
+    const int32_t t = min(e, L - 1);
+    meta[(int64_t)(pre + (e >> 5)) * kMlaMetaWords + (e & 31)] = sm(t, true);
+  }
+  for (int e = tid; e < T * 8; e += 256) {
+    const int32_t j = e >> 3, f = e & 7;
+    int32_t v = 0;
+    if (f == 0) v = i;
+    else if (f == 1) v = j;
+    else if (f == 2) v = T;
+    else if (f == 3) v = pre;
+    else if (f == 4) v = min(kMlaT, L - j * kMlaT);
+    meta[(int64_t)(pre + j) * kMlaMetaWords + 32 + f] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Main kernel.
+// ---------------------------------------------------------------------------
+template <int HPB>
+__global__ void __launch_bounds__(64 * MlaCfg<HPB>::W, 1) mla_decode_kernel(
+    const char* kpool, const bf16* __restrict__ q, int32_t HQ, int32_t sibs, const int32_t* __restrict__ header,
+    const int32_t* __restrict__ meta, float scale_log2, bf16* __restrict__ out, float* __restrict__ lse,
+    float* __restrict__ ws_o, float* __restrict__ ws_lse) {
+  using C = MlaCfg<HPB>;
+  constexpr int W = C::W, HB = C::HB, NHB = C::NHB, CW = C::CW, NCB = C::NCB, NI = C::NI;
+  constexpr int NK = kMlaQK / 32;  // 18 k-steps of the score product
+
+  __shared__ __attribute__((aligned(1024))) char tiles[3][kMlaTileBytes];
+  __shared__ __attribute__((aligned(16))) bf16x8 p_lds[NHB * 64];
+  __shared__ __attribute__((aligned(256))) int32_t meta_lds[W][4][64];
+  __shared__ __attribute__((aligned(16))) float alpha_lds[HPB];
+  __shared__ __attribute__((aligned(16))) float l_lds[HPB];
+  __shared__ __attribute__((aligned(16))) float m_lds[HPB];
+  __shared__ int32_t flag_lds[W];
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  // run and sibling: siblings sit 8 workgroups apart, on the same XCD
+  const int run = sibs == 1 ? (int)blockIdx.x : (int)(blockIdx.x / 16 * 8 + blockIdx.x % 8);
+  const int h0 = sibs == 1 ? 0 : (int)(blockIdx.x / 8 % 2) * HPB;
+  const int Bt = header[0], total = header[1];
+  const int G0 = run * Bt;
+  if (G0 >= total) return;
+  const int n = min(Bt, total - G0);
+
+  // ---- loaders (every wave issues the same number of each, in the same order)
+  auto meta_dma = [&](int r) {
+    const int g = G0 + min(r, n - 1);
+    dma4(meta + (int64_t)g * kMlaMetaWords + min(lane, kMlaMetaWords - 1), lds_off(&meta_lds[w][r & 3][0]));
+  };
+  auto tile_dma = [&](int r) {
+    const int32_t* ms = &meta_lds[w][r & 3][0];
+    char* buf = tiles[r % 3];
+    int ln = lane;
+    asm volatile("" : "+v"(ln));  // recompute the per-lane positions every tile instead of holding them
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      sacc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NI; ++j) {
+      const int pos = (w * NI + j) * 64 + ln;  // 16-byte chunk position in the tile
+      const int t = pos / kMlaRowChunks;
+      const int c = (pos - t * kMlaRowChunks) ^ (t & 7);
+      const int64_t slot = ms[t];
+      dma16(kpool + slot * kMlaRowBytes + c * 16, lds_off(buf + (w * NI + j) * 1024));
+    }
+  };
+
+  f32x4 acc[NHB][NCB];
+#pragma unroll
+  for (int a = 0; a < NHB; ++a)
+#pragma unroll
+    for (int b = 0; b < NCB; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bf16x8 qf[HB][NK];
+  float m_ref[HB], l_part[HB];
+
+  // prologue: queue = tile(0), meta(2), tile(1)
+  meta_dma(0);
+  meta_dma(1);
+  wait_vm<0>();
+  tile_dma(0);
+  meta_dma(2);
+  tile_dma(1);
+
+  for (int r = 0; r < n; ++r) {
+    meta_dma(r + 3);
+    wait_vm<NI + 1>();  // meta(r + 2) and tile(r) have landed
+    __syncthreads();    // tile r visible to all waves; every wave is past P*V of tile r - 1
+    tile_dma(r + 2);
+
+    const int32_t* info = &meta_lds[w][r & 3][32];
+    const int i = __builtin_amdgcn_readfirstlane(info[0]);
+    const int jt = __builtin_amdgcn_readfirstlane(info[1]);
+    const int T = __builtin_amdgcn_readfirstlane(info[2]);
+    const int P = __builtin_amdgcn_readfirstlane(info[3]);
+    const int valid = __builtin_amdgcn_readfirstlane(info[4]);
+    const bool seg_begin = (r == 0) || (jt == 0);
+    const bool seg_end = (r == n - 1) || (jt == T - 1);
+    const char* tile = tiles[r % 3];
+
+    if (seg_begin) {
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        const int h = h0 + (w * HB + hb) * 16 + col;
+        const bf16* qp = q + ((int64_t)i * HQ + h) * kMlaQK + grp * 8;
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) qf[hb][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + kk * 32));
+        m_ref[hb] = -INFINITY;
+        l_part[hb] = 0.f;
+      }
+    }
+
+    // ---- S^T = K Q^T for this wave's heads.  Chunk 4kk + grp of token t
+    // sits at 8 (kk / 2) + ((4 (kk & 1) + grp) ^ (t & 7)): two per-lane bases
+    // (even / odd kk) plus compile-time offsets.
+    f32x4 sacc[2][HB];
+    {
+      const int t = col;  // token 16a + col; (t & 7) is the same for a = 0, 1
+      const char* kb_even = tile + (t * kMlaRowChunks + (grp ^ (t & 7))) * 16;
+      const char* kb_odd = tile + (t * kMlaRowChunks + ((4 + grp) ^ (t & 7))) * 16;
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) sacc[a][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
-        const bf16x8 ka =
-            as_bf16x8(*reinterpret_cast<const u32x4*>(ks + (a * 16 + col) * kMlaLds + kk * 32 + grp * 8));
-        sacc[a] = mfma16x16x32(ka, qb[kk], sacc[a]);
+        const char* kb = (kk & 1) ? kb_odd : kb_even;
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+          const bf16x8 kf =
+              as_bf16x8(*reinterpret_cast<const u32x4*>(kb + a * 16 * kMlaRowBytes + (kk >> 1) * 128));
+#pragma unroll
+          for (int hb = 0; hb < HB; ++hb) sacc[a][hb] = mfma16x16x32(kf, qf[hb][kk], sacc[a][hb]);
+        }
       }
     }
-    // ---- online softmax (log2 domain); lane holds tokens a*16 + 4*grp + rr of head col
-    float sv[2][4];
-    float mt = -INFINITY;
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int t = t0 + a * 16 + grp * 4 + rr;
-        const float x = (t < t_end) ? sacc[a][rr] * scale_log2 : -INFINITY;
-        sv[a][rr] = x;
-        mt = fmaxf(mt, x);
-      }
-    mt = fmaxf(mt, shfl_xor(mt, 16));
-    mt = fmaxf(mt, shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = fast_exp2(m_run - m_new);
-    float psum = 0.f;
-    bf16x8 pa;
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const float p = fast_exp2(sv[a][rr] - m_new);
-        psum += p;
-        pa[a * 4 + rr] = (bf16)p;
-      }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const float ar = shfl(alpha, grp * 4 + rr);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[nt][rr] *= ar;
-    }
-    // ---- O += P V, V = the first 512 columns of the latent rows
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma16x16x32(pa, lds_v_operand(ks, kMlaLds, 0, nt * 16, lane), acc[nt]);
-    if (kt + 1 < ntiles) mla_store<W>(R, t0 + kMlaTile, t_end, ksm[(kt + 1) & 1]);
-    __syncthreads();
-  }
 
-  // ---- finalise: heads h0 + 4*grp + rr
-  float l_tot = l_run + shfl_xor(l_run, 16);
-  l_tot += shfl_xor(l_tot, 32);
+    // ---- softmax (log2 domain) for head 16 * (w * HB + hb) + col; this lane
+    // holds tokens 16a + 4 grp + rr
+    bool moved = false;
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    const int hr = grp * 4 + rr;
-    const float lt = shfl(l_tot, hr);
-    const float mr = shfl(m_run, hr);
-    const int64_t h = (int64_t)i * Hq + h0 + hr;
-    const float inv = 1.0f / lt;
-    const float lse_nat = (mr + __log2f(lt)) * kLn2;
-    if (ns == 1) {
+    for (int hb = 0; hb < HB; ++hb) {
+      float x[2][4];
+      float mt = -INFINITY;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) out[h * kMlaV + nt * 16 + col] = (bf16)(acc[nt][rr] * inv);
-      if (lse && col == 0) lse[h] = lse_nat;
-    } else {
-      float* po = ws_o + (h * max_splits + s) * kMlaV;
+      for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) po[nt * 16 + col] = acc[nt][rr] * inv;
-      if (col == 0) ws_lse[h * max_splits + s] = lse_nat;
+        for (int rr = 0; rr < 4; ++rr) {
+          const int t = 16 * a + 4 * grp + rr;
+          x[a][rr] = t < valid ? sacc[a][hb][rr] * scale_log2 : -INFINITY;
+          mt = fmaxf(mt, x[a][rr]);
+        }
+      mt = fmaxf(mt, shfl_xor(mt, 16));
+      mt = fmaxf(mt, shfl_xor(mt, 32));
+      float alpha = 1.0f;
+      if (mt > m_ref[hb] + kMlaSlack) {
+        alpha = fast_exp2(m_ref[hb] - mt);
+        m_ref[hb] = mt;
+        l_part[hb] *= alpha;
+        moved = true;
+      }
+      bf16x8 pa;
+      float ps = 0.f;
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const float p = fast_exp2(x[a][rr] - m_ref[hb]);
+          ps += p;
+          pa[a * 4 + rr] = (bf16)p;
+        }
+      l_part[hb] += ps;
+      const int hbg = w * HB + hb;
+      p_lds[hbg * 64 + lane] = pa;
+      if (grp == 0) alpha_lds[hbg * 16 + col] = alpha;
+    }
+    const bool any_moved = __builtin_amdgcn_ballot_w64(moved) != 0;
+    if (lane == 0) flag_lds[w] = any_moved ? 1 : 0;
+    __syncthreads();  // P, alphas and flags of every wave are in LDS
+
+    int rescale = 0;
+#pragma unroll
+    for (int v = 0; v < W; ++v) rescale |= flag_lds[v];
+    if (rescale) {
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb) {
+        const f32x4 al = *reinterpret_cast<const f32x4*>(&alpha_lds[hb * 16 + 4 * grp]);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) acc[hb][cb] *= al;
+      }
+    }
+
+    // ---- O += P V over this wave's columns, all heads; four column blocks
+    // of V at a time (held in registers), P fragments re-read per group.
+    // Column block cb = 4 m + u of the whole row: the transposed read of
+    // lane (x, j) starts at token t = 4 j + x / 4, chunk 8 (cb / 4) +
+    // ((2 u + (x & 3) / 2) ^ (t & 7)): four per-lane bases (u) plus offsets.
+    {
+      const int x = lane & 15, jg = lane >> 4;
+      const int t = 4 * jg + (x >> 2);
+      const char* vb[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        vb[u] = tile + (t * kMlaRowChunks + ((2 * u + ((x & 3) >> 1)) ^ (t & 7))) * 16 + (x & 1) * 8 +
+                (w * NCB / 4) * 128;
+#pragma unroll
+      for (int cg = 0; cg < NCB; cg += 4) {
+        bf16x8 vf[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const char* lo = vb[u] + (cg / 4) * 128;
+          const i16x4 va = lds_read_tr16(reinterpret_cast<const bf16*>(lo));
+          const i16x4 vc = lds_read_tr16(reinterpret_cast<const bf16*>(lo + 16 * kMlaRowBytes));
+          const bf16x4 ba = __builtin_bit_cast(bf16x4, va), bc = __builtin_bit_cast(bf16x4, vc);
+          vf[u] = bf16x8{ba[0], ba[1], ba[2], ba[3], bc[0], bc[1], bc[2], bc[3]};
+        }
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) {
+          const bf16x8 pf = p_lds[hb * 64 + lane];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) acc[hb][cg + u] = mfma16x16x32(pf, vf[u], acc[hb][cg + u]);
+        }
+      }
+    }
+
+    if (seg_end) {
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        float lt = l_part[hb] + shfl_xor(l_part[hb], 16);
+        lt += shfl_xor(lt, 32);
+        if (grp == 0) {
+          l_lds[(w * HB + hb) * 16 + col] = lt;
+          m_lds[(w * HB + hb) * 16 + col] = m_ref[hb];
+        }
+      }
+      __syncthreads();
+      const int b0 = P / Bt, b1 = (P + T - 1) / Bt;
+      const bool direct = b0 == b1;
+      // per-lane bases computed here (not hoisted out of the tile loop), then
+      // compile-time offsets: head 16 hb + 4 grp + rr, column w CW + 16 cb + col
+      int g4 = 4 * grp;
+      asm volatile("" : "+v"(g4));
+      const int64_t row0 = (direct ? (int64_t)i * HQ : ((int64_t)run + i) * HQ) + h0 + g4;
+      bf16* ob = out + row0 * kMlaV + w * CW + col;
+      float* wb = ws_o + row0 * kMlaV + w * CW + col;
+      float* lb = (direct ? lse : ws_lse) + (lse || !direct ? row0 : 0);
+      const bool write_lse = (lse || !direct) && w == 0 && col == 0;
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb) {
+        const f32x4 lv = *reinterpret_cast<const f32x4*>(&l_lds[hb * 16 + g4]);
+        const f32x4 mv = *reinterpret_cast<const f32x4*>(&m_lds[hb * 16 + g4]);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int hoff = hb * 16 + rr;
+          const float inv = 1.0f / lv[rr];
+          if (direct) {
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) ob[hoff * kMlaV + cb * 16] = (bf16)(acc[hb][cb][rr] * inv);
+          } else {
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) wb[hoff * kMlaV + cb * 16] = acc[hb][cb][rr] * inv;
+          }
+          if (write_lse) lb[hoff] = (mv[rr] + __log2f(lv[rr])) * kLn2;
+        }
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) acc[hb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
     }
   }
+  wait_vm<0>();  // no load may still target this workgroup's LDS when it ends
+}
+
+// ---------------------------------------------------------------------------
+// Merge: one wavefront per (request, head).  Requests finished inside one run
+// were written directly; empty requests get zeros and lse = -inf; the rest
+// combine their pieces (ids run + request) with log-sum-exp weights.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) mla_merge_kernel(int32_t bs, int32_t Hq,
+                                                        const int32_t* __restrict__ header,
+                                                        const int32_t* __restrict__ prefix,
+                                                        const int32_t* __restrict__ ntiles,
+                                                        const float* __restrict__ ws_o,
+                                                        const float* __restrict__ ws_lse, bf16* __restrict__ out,
+                                                        float* __restrict__ lse) {
+  const int lane = threadIdx.x & 63;
+  const int64_t idx = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (idx >= (int64_t)bs * Hq) return;
+  const int i = (int)(idx / Hq), h = (int)(idx % Hq);
+  bf16* op = out + idx * kMlaV + lane * 8;
+  const int T = ntiles[i];
+  if (T == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) op[e] = (bf16)0.0f;
+    if (lse && lane == 0) lse[idx] = -INFINITY;
+    return;
+  }
+  const int Bt = header[0];
+  const int P = prefix[i];
+  const int b0 = P / Bt, b1 = (P + T - 1) / Bt;
+  if (b0 == b1) return;
+  float mx = -INFINITY;
+  for (int b = b0; b <= b1; ++b) mx = fmaxf(mx, ws_lse[((int64_t)b + i) * Hq + h]);
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float sum = 0.f;
+  for (int b = b0; b <= b1; ++b) {
+    const int64_t row = ((int64_t)b + i) * Hq + h;
+    const float wgt = __expf(ws_lse[row] - mx);
+    const f32x4* src = reinterpret_cast<const f32x4*>(ws_o + row * kMlaV + lane * 8);
+    const f32x4 x0 = src[0], x1 = src[1];
+    sum += wgt;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      o[e] += wgt * x0[e];
+      o[4 + e] += wgt * x1[e];
+    }
+  }
+  const float inv = 1.0f / sum;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) op[e] = (bf16)(o[e] * inv);
+  if (lse && lane == 0) lse[idx] = mx + __logf(sum);
 }
 
 // ---------------------------------------------------------------------------
@@ -199,71 +474,97 @@ __global__ void __launch_bounds__(64 * W, 1) mla_decode_kernel(
 // ---------------------------------------------------------------------------
 bool mla_decode_supported(const PoolInfo& p, int32_t Hq) {
   return p.kind == 1 && p.dtype == 1 && p.num_kv_heads == 1 && p.head_dim_qk == kMlaQK && p.head_dim_v == kMlaV &&
-         Hq > 0 && Hq % 16 == 0;
+         (Hq == 16 || Hq == 32 || Hq == 64 || Hq == 128);
 }
 
-// Wavefronts per block: 4 (64 heads).  A wave holds its 16 heads' queries
-// (72 VGPRs) and 16 x 512 fp32 accumulators (128), which only fits at one
-// wave per SIMD, so a block of 4 fills a CU; larger head counts take
-// several blocks per item.
-static int mla_waves(int32_t Hq) {
-  const int groups = Hq / 16;
-  return groups % 4 == 0 ? 4 : (groups % 2 == 0 ? 2 : 1);
+// One workgroup per CU of the current device.
+static int32_t mla_grid() {
+  static int32_t cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 DecodePlan plan_mla_decode(const PoolInfo& p, int32_t bs, int32_t Hq, int32_t max_kv_len) {
   (void)p;
+  (void)bs;
   DecodePlan plan;
   plan.kind = 3;
-  // Each split re-reads nothing but writes a 2 KiB partial row per head, so
-  // splits are long: the largest power of two in [256, 4096] that still
-  // gives ~2 blocks per CU on average (mean length taken as max_kv_len / 2).
-  const int hg = (Hq / 16) / mla_waves(Hq);
-  const double tokens = (double)bs * hg * 0.5 * (double)max_kv_len;
-  int chunk = 256;
-  for (int c = 4096; c >= 256; c >>= 1) {
-    if (tokens / c >= 512.0) {
-      chunk = c;
-      break;
-    }
-  }
-  int splits = max_kv_len > 0 ? (max_kv_len + chunk - 1) / chunk : 1;
-  while (splits > kMaxSplits) {
-    chunk *= 2;
-    splits = (max_kv_len + chunk - 1) / chunk;
-  }
-  plan.chunk = chunk;
-  plan.max_splits = splits < 1 ? 1 : splits;
+  plan.chunk = max_kv_len > 0 ? (max_kv_len + kMlaT - 1) / kMlaT : 0;  // tiles per request, at most
+  // runs of tiles: one workgroup per CU, two sibling workgroups per run
+  // above 64 heads (an even split of the CUs)
+  plan.max_splits = Hq > 64 ? std::max(8, mla_grid() / 2 / 8 * 8) : mla_grid();
   return plan;
 }
 
-template <int W, int FMT>
-static void launch_mla(unsigned blocks, hipStream_t s, const DevMap& m, const bf16* kp, const void* q, int32_t Hq,
-                       int32_t hg, const DecodePlan& plan, const DecodeWs& w, float sl2, void* out, float* lse) {
-  hipLaunchKernelGGL((mla_decode_kernel<W, FMT>), dim3(blocks), dim3(64 * W), 0, s, m, kp,
-                     static_cast<const bf16*>(q), Hq, hg, plan.chunk, plan.max_splits, w.items, w.count, sl2,
-                     static_cast<bf16*>(out), lse, w.o, w.lse);
+static size_t al256(size_t x) { return (x + 255) / 256 * 256; }
+
+// [header | tile prefix[bs] | tiles[bs] | meta[bs * max tiles][40] | pieces o | pieces lse]
+size_t mla_ws_layout(const DecodePlan& plan, int32_t bs, int32_t Hq, void* base, MlaWs* w) {
+  char* b = static_cast<char*>(base);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* at = b ? b + off : nullptr;
+    off += al256(bytes);
+    return at;
+  };
+  char* hdr = take(256);
+  char* pre = take((size_t)bs * 4);
+  char* nt = take((size_t)bs * 4);
+  char* meta = take((size_t)bs * plan.chunk * kMlaMetaWords * 4);
+  const size_t pieces = (size_t)plan.max_splits + bs;
+  char* o = take(pieces * Hq * kMlaV * 4);
+  char* l = take(pieces * Hq * 4);
+  if (w) {
+    w->header = reinterpret_cast<int32_t*>(hdr);
+    w->prefix = reinterpret_cast<int32_t*>(pre);
+    w->ntiles = reinterpret_cast<int32_t*>(nt);
+    w->meta = reinterpret_cast<int32_t*>(meta);
+    w->o = reinterpret_cast<float*>(o);
+    w->lse = reinterpret_cast<float*>(l);
+  }
+  return off;
 }
 
-template <int W>
-static void launch_mla_fmt(unsigned blocks, hipStream_t s, const DevMap& m, const bf16* kp, const void* q,
-                           int32_t Hq, int32_t hg, const DecodePlan& plan, const DecodeWs& w, float sl2, void* out,
-                           float* lse) {
+template <int HPB>
+static void launch_mla_main(int32_t runs, int32_t Hq, hipStream_t s, const char* kp, const void* q, const MlaWs& w,
+                            float sl2, void* out, float* lse) {
+  const int sibs = Hq / HPB;
+  hipLaunchKernelGGL((mla_decode_kernel<HPB>), dim3(runs * sibs), dim3(64 * MlaCfg<HPB>::W), 0, s, kp,
+                     static_cast<const bf16*>(q), Hq, sibs, w.header, w.meta, sl2, static_cast<bf16*>(out), lse,
+                     w.o, w.lse);
+}
+
+hipError_t launch_mla_decode(const PoolInfo& p, int32_t layer, const void* q, int32_t Hq, const DevMap& m, int32_t bs,
+                             const DecodePlan& plan, float sl2, void* out, float* lse, void* ws, hipStream_t s) {
+  MlaWs w;
+  mla_ws_layout(plan, bs, Hq, ws, &w);
+  const int32_t runs = plan.max_splits;
   if (m.fmt == MAP_TOKEN_TABLE)
-    launch_mla<W, SLOT_TABLE>(blocks, s, m, kp, q, Hq, hg, plan, w, sl2, out, lse);
+    hipLaunchKernelGGL(mla_plan_kernel<SLOT_TABLE>, dim3(bs), dim3(256), 0, s, m, bs, plan.chunk, runs, w.header, w.prefix,
+                       w.ntiles, w.meta);
   else
-    launch_mla<W, SLOT_PAGES>(blocks, s, m, kp, q, Hq, hg, plan, w, sl2, out, lse);
-}
-
-void launch_mla_split(const PoolInfo& p, int32_t layer, const void* q, int32_t Hq, const DevMap& m, int32_t bs,
-                      const DecodePlan& plan, const DecodeWs& w, float sl2, void* out, float* lse, hipStream_t s) {
-  const int W = mla_waves(Hq);
-  const int hg = (Hq / 16) / W;
-  const unsigned blocks = (unsigned)((int64_t)bs * plan.max_splits * hg);
-  const bf16* kp = reinterpret_cast<const bf16*>(p.k_layer(layer));
-  if (W == 4) launch_mla_fmt<4>(blocks, s, m, kp, q, Hq, hg, plan, w, sl2, out, lse);
-  else if (W == 2) launch_mla_fmt<2>(blocks, s, m, kp, q, Hq, hg, plan, w, sl2, out, lse);
-  else launch_mla_fmt<1>(blocks, s, m, kp, q, Hq, hg, plan, w, sl2, out, lse);
+    hipLaunchKernelGGL(mla_plan_kernel<SLOT_PAGES>, dim3(bs), dim3(256), 0, s, m, bs, plan.chunk, runs, w.header, w.prefix,
+                       w.ntiles, w.meta);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const char* kp = p.k_layer(layer);
+  timer_before(s);
+  if (Hq >= 64) launch_mla_main<64>(runs, Hq, s, kp, q, w, sl2, out, lse);
+  else if (Hq == 32) launch_mla_main<32>(runs, Hq, s, kp, q, w, sl2, out, lse);
+  else launch_mla_main<16>(runs, Hq, s, kp, q, w, sl2, out, lse);
+  e = hipGetLastError();
+  timer_after(s);
+  if (e != hipSuccess) return e;
+  const unsigned mblocks = (unsigned)(((int64_t)bs * Hq + 3) / 4);
+  hipLaunchKernelGGL(mla_merge_kernel, dim3(mblocks), dim3(256), 0, s, bs, Hq, w.header, w.prefix,
+                     w.ntiles, w.o, w.lse, static_cast<bf16*>(out), lse);
+  return hipGetLastError();
 }
 
 }  // namespace pkv

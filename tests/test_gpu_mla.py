@@ -62,3 +62,33 @@ def test_mla_planted_key_and_empty_request():
     # the planted key dominates: every head returns (nearly) its V part
     np.testing.assert_allclose(out[i].float().cpu().numpy(),
                                np.repeat(key[:512].float().cpu().numpy()[None], case.geom.num_q_heads, 0), atol=0.05)
+
+
+@pytest.mark.parametrize("heads", [32, 128])
+def test_mla_many_short_requests(heads):
+    """Many short requests (and empty ones) so that every run of tiles holds
+    several requests and many requests are split across runs."""
+    case = W.mla_decode(seed=4, bs=48, len_range=(1, 90), num_q_heads=heads)
+    for i in (3, 17, 18, 40):
+        case.regions["self"].kv_lens[i] = 0
+    vals = W.make_values(case, canary=True)
+    dc = DeviceCase(case, vals)
+    dc.store()
+    out, lse = dc.decode(P.PKV_MAP_BLOCK_TABLE)
+    live = [i for i in range(case.bs) if case.regions["self"].kv_lens[i] > 0]
+    ref_o, ref_l = oracle_region(case, vals, "self", requests=live)
+    assert_attn_close(out, ref_o, "bf16", f"mla short {heads}", rows=live)
+    assert_lse_close(lse, ref_l, "bf16", f"mla short {heads}", rows=live)
+    for i in (3, 17, 18, 40):
+        assert (out[i].float() == 0).all() and torch.isneginf(lse[i]).all()
+
+
+def test_mla_formats_agree_bitwise_and_repeat():
+    case = W.mla_decode(seed=6, bs=9, len_range=(1, 3000))
+    vals = W.make_values(case, canary=True)
+    dc = DeviceCase(case, vals)
+    dc.store()
+    outs = [dc.decode(f) for f in FMTS] + [dc.decode(P.PKV_MAP_BLOCK_TABLE)]
+    for o, l in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0][0].view(torch.int16))
+        assert torch.equal(l, outs[0][1])
