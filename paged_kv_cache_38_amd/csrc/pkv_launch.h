@@ -89,11 +89,12 @@ bool mla_decode_supported(const PoolInfo& p, int32_t num_q_heads);
 // MLA plan: chunk = tiles (32 tokens) per request at most, max_splits = main
 // grid (one workgroup per CU)
 DecodePlan plan_mla_decode(const PoolInfo& p, int32_t bs, int32_t num_q_heads, int32_t max_kv_len);
-// MLA workspace: [header | tile prefix | tiles | per-tile slot ids + info | pieces o | pieces lse]
+// MLA workspace: [header | tile prefix | tiles | fallback flags | per-tile slot ids + info | pieces o | pieces lse]
 struct MlaWs {
   int32_t* header;  // run length (tiles per workgroup), total tiles
   int32_t* prefix;
   int32_t* ntiles;
+  int32_t* fallback;  // requests to recompute exactly (set by the main kernel)
   int32_t* meta;
   float* o;
   float* lse;

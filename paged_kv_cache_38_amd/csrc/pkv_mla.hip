@@ -19,8 +19,8 @@
 //    to its 32 slot ids (through any table format) before the main kernel
 //    starts, so the main kernel never touches a table.
 //  * Streaming.  Tiles move HBM -> LDS with global_load_lds_dwordx4 (no
-//    staging registers), three tiles deep: while tile r is computed, tiles
-//    r+1 and r+2 are in flight.  The tile layout in LDS is row-major with a
+//    staging registers), four tiles deep: while tile r is computed, tiles
+//    r+1 .. r+3 are in flight (about 100 KiB per CU).  The tile layout in LDS is row-major with a
 //    16-byte-chunk XOR swizzle (chunk c of token t sits at c ^ (t & 7)), so
 //    both the K-operand reads and the transposed V-operand reads are free of
 //    bank conflicts.  These loads are issued from inline assembly and waited
@@ -29,9 +29,11 @@
 //  * Math.  Wave w computes S^T = K Q^T for its 32 heads (queries held in
 //    registers) and the softmax for them; P goes through LDS; then every wave
 //    computes O += P V for all heads over its own slice of the 512 value
-//    columns (accumulators in AGPRs).  Rescaling is lazy: the running maximum
-//    is only moved when a score exceeds it by more than 2^8, which keeps P
-//    below 256 and skips almost every accumulator rescale.
+//    columns (accumulators in AGPRs).  The softmax reference is the maximum
+//    of a piece's first tile and then stays fixed, so the accumulators are
+//    never rescaled (any reference gives the same normalised result); should
+//    a later score exceed it by more than 2^64 (P could overflow), the
+//    request is recomputed exactly by a fallback in the merge pass.
 #include <math.h>
 
 #include <algorithm>
@@ -47,7 +49,9 @@ constexpr int kMlaRowChunks = kMlaQK / 8;         // 72 sixteen-byte chunks per 
 constexpr int kMlaRowBytes = kMlaQK * 2;          // 1152
 constexpr int kMlaTileBytes = kMlaT * kMlaRowBytes;  // 36864
 constexpr int kMlaMetaWords = 40;                 // per tile: 32 slot ids + 8 info words
-constexpr float kMlaSlack = 8.0f;                 // log2 headroom before the running max moves
+constexpr int kMlaBufs = 4;                       // LDS tile buffers: three tiles in flight during compute
+constexpr int kMlaMetaRing = 8;                   // per-wave ring of per-tile slot ids / info
+constexpr float kMlaHeadroom = 64.0f;             // log2 units a score may exceed the reference by
 
 // Launch shape per workgroup of HPB heads (16, 32 or 64): W waves; wave w
 // computes scores for HB blocks of 16 heads and output columns
@@ -86,6 +90,15 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// The P*V accumulators live in AGPRs for the whole kernel: outside the MFMAs
+// they are only read (through this), never redefined in a branch, which would
+// make the compiler copy all of them on every tile.
+__device__ __forceinline__ float acc_get(float a) {
+  float v;
+  asm("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+  return v;
+}
+
 // byte offset of chunk c of token t inside a swizzled tile
 __device__ __forceinline__ int mla_chunk_off(int t, int c) { return (t * kMlaRowChunks + (c ^ (t & 7))) * 16; }
 
@@ -114,7 +127,7 @@ template <int FMT>
 __global__ void __launch_bounds__(256) mla_plan_kernel(DevMap m, int32_t bs, int32_t max_tiles, int32_t runs,
                                                        int32_t* __restrict__ header,
                                                        int32_t* __restrict__ prefix, int32_t* __restrict__ ntiles,
-                                                       int32_t* __restrict__ meta) {
+                                                       int32_t* __restrict__ fallback, int32_t* __restrict__ meta) {
   __shared__ int32_t red[2][4];
   const int i = blockIdx.x;
   const int tid = threadIdx.x;
@@ -142,6 +155,7 @@ __global__ void __launch_bounds__(256) mla_plan_kernel(DevMap m, int32_t bs, int
   if (tid == 0) {
     prefix[i] = pre;
     ntiles[i] = T;
+    fallback[i] = 0;
     if (i == 0) {
       header[0] = max(1, (tot + runs - 1) / runs);
       header[1] = tot;
@@ -165,6 +179,44 @@ __global__ void __launch_bounds__(256) mla_plan_kernel(DevMap m, int32_t bs, int
   }
 }
 
+// O += P V for one tile over a wave's NCB column blocks and NHB head
+// blocks; P fragments of all heads and four column blocks of V at a time
+// in registers.  Column block cb = 4 m + u of the whole row: the
+// transposed read of lane (x, j) starts at token t = 4 j + x / 4, chunk
+// 8 (cb / 4) + ((2 u + (x & 3) / 2) ^ (t & 7)): four per-lane bases (u) plus
+// compile-time offsets.  ZERO starts the accumulators from zero.
+template <int NHB, int NCB, bool ZERO>
+__device__ __forceinline__ void mla_pv(f32x4 (&acc)[NHB][NCB], const char* tile, const bf16x8* p_lds, int w,
+                                       int lane) {
+  const int x = lane & 15, jg = lane >> 4;
+  const int t = 4 * jg + (x >> 2);
+  const char* vb[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    vb[u] = tile + (t * kMlaRowChunks + ((2 * u + ((x & 3) >> 1)) ^ (t & 7))) * 16 + (x & 1) * 8 +
+            (w * NCB / 4) * 128;
+  bf16x8 pf[NHB];
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb) pf[hb] = p_lds[hb * 64 + lane];
+#pragma unroll
+  for (int cg = 0; cg < NCB; cg += 4) {
+    bf16x8 vf[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const char* lo = vb[u] + (cg / 4) * 128;
+      const i16x4 va = lds_read_tr16(reinterpret_cast<const bf16*>(lo));
+      const i16x4 vc = lds_read_tr16(reinterpret_cast<const bf16*>(lo + 16 * kMlaRowBytes));
+      const bf16x4 ba = __builtin_bit_cast(bf16x4, va), bc = __builtin_bit_cast(bf16x4, vc);
+      vf[u] = bf16x8{ba[0], ba[1], ba[2], ba[3], bc[0], bc[1], bc[2], bc[3]};
+    }
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        acc[hb][cg + u] = mfma16x16x32(pf[hb], vf[u], ZERO ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[hb][cg + u]);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Main kernel.
 // ---------------------------------------------------------------------------
@@ -172,18 +224,16 @@ template <int HPB>
 __global__ void __launch_bounds__(64 * MlaCfg<HPB>::W, 1) mla_decode_kernel(
     const char* kpool, const bf16* __restrict__ q, int32_t HQ, int32_t sibs, const int32_t* __restrict__ header,
     const int32_t* __restrict__ meta, float scale_log2, bf16* __restrict__ out, float* __restrict__ lse,
-    float* __restrict__ ws_o, float* __restrict__ ws_lse) {
+    float* __restrict__ ws_o, float* __restrict__ ws_lse, int32_t* __restrict__ fallback) {
   using C = MlaCfg<HPB>;
   constexpr int W = C::W, HB = C::HB, NHB = C::NHB, CW = C::CW, NCB = C::NCB, NI = C::NI;
   constexpr int NK = kMlaQK / 32;  // 18 k-steps of the score product
 
-  __shared__ __attribute__((aligned(1024))) char tiles[3][kMlaTileBytes];
+  __shared__ __attribute__((aligned(1024))) char tiles[kMlaBufs][kMlaTileBytes];
   __shared__ __attribute__((aligned(16))) bf16x8 p_lds[NHB * 64];
-  __shared__ __attribute__((aligned(256))) int32_t meta_lds[W][4][64];
-  __shared__ __attribute__((aligned(16))) float alpha_lds[HPB];
+  __shared__ __attribute__((aligned(256))) int32_t meta_lds[W][kMlaMetaRing][64];
   __shared__ __attribute__((aligned(16))) float l_lds[HPB];
   __shared__ __attribute__((aligned(16))) float m_lds[HPB];
-  __shared__ int32_t flag_lds[W];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
@@ -198,11 +248,11 @@ __global__ void __launch_bounds__(64 * MlaCfg<HPB>::W, 1) mla_decode_kernel(
   // ---- loaders (every wave issues the same number of each, in the same order)
   auto meta_dma = [&](int r) {
     const int g = G0 + min(r, n - 1);
-    dma4(meta + (int64_t)g * kMlaMetaWords + min(lane, kMlaMetaWords - 1), lds_off(&meta_lds[w][r & 3][0]));
+    dma4(meta + (int64_t)g * kMlaMetaWords + min(lane, kMlaMetaWords - 1), lds_off(&meta_lds[w][r & (kMlaMetaRing - 1)][0]));
   };
   auto tile_dma = [&](int r) {
-    const int32_t* ms = &meta_lds[w][r & 3][0];
-    char* buf = tiles[r % 3];
+    const int32_t* ms = &meta_lds[w][r & (kMlaMetaRing - 1)][0];
+    char* buf = tiles[r % kMlaBufs];
     int ln = lane;
     asm volatile("" : "+v"(ln));  // recompute the per-lane positions every tile instead of holding them
 #pragma unroll
@@ -223,21 +273,28 @@ __global__ void __launch_bounds__(64 * MlaCfg<HPB>::W, 1) mla_decode_kernel(
   bf16x8 qf[HB][NK];
   float m_ref[HB], l_part[HB];
 
-  // prologue: queue = tile(0), meta(2), tile(1)
+  // Per iteration r a wave issues meta(r + 6) then tile(r + 3); tile(r) is
+  // then followed in the queue by meta(r + 4), tile(r + 1), meta(r + 5),
+  // tile(r + 2), meta(r + 6): 2 NI + 3 operations.  The prologue builds that
+  // state for r = 0.
+  constexpr int kWait = 2 * NI + 3 < 63 ? 2 * NI + 3 : 63;
   meta_dma(0);
   meta_dma(1);
-  wait_vm<0>();
-  tile_dma(0);
   meta_dma(2);
-  tile_dma(1);
+  wait_vm<0>();
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    meta_dma(k + 3);
+    tile_dma(k);
+  }
 
   for (int r = 0; r < n; ++r) {
-    meta_dma(r + 3);
-    wait_vm<NI + 1>();  // meta(r + 2) and tile(r) have landed
+    meta_dma(r + 6);
+    wait_vm<kWait>();   // tile(r) (and every meta before it) has landed
     __syncthreads();    // tile r visible to all waves; every wave is past P*V of tile r - 1
-    tile_dma(r + 2);
+    tile_dma(r + 3);    // into the buffer tile r - 1 used
 
-    const int32_t* info = &meta_lds[w][r & 3][32];
+    const int32_t* info = &meta_lds[w][r & (kMlaMetaRing - 1)][32];
     const int i = __builtin_amdgcn_readfirstlane(info[0]);
     const int jt = __builtin_amdgcn_readfirstlane(info[1]);
     const int T = __builtin_amdgcn_readfirstlane(info[2]);
@@ -245,7 +302,7 @@ __global__ void __launch_bounds__(64 * MlaCfg<HPB>::W, 1) mla_decode_kernel(
     const int valid = __builtin_amdgcn_readfirstlane(info[4]);
     const bool seg_begin = (r == 0) || (jt == 0);
     const bool seg_end = (r == n - 1) || (jt == T - 1);
-    const char* tile = tiles[r % 3];
+    const char* tile = tiles[r % kMlaBufs];
 
     if (seg_begin) {
 #pragma unroll
@@ -254,7 +311,6 @@ __global__ void __launch_bounds__(64 * MlaCfg<HPB>::W, 1) mla_decode_kernel(
         const bf16* qp = q + ((int64_t)i * HQ + h) * kMlaQK + grp * 8;
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) qf[hb][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + kk * 32));
-        m_ref[hb] = -INFINITY;
         l_part[hb] = 0.f;
       }
     }
@@ -271,42 +327,55 @@ __global__ void __launch_bounds__(64 * MlaCfg<HPB>::W, 1) mla_decode_kernel(
       for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb) sacc[a][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < NK; ++kk) {
+      // K fragments stream through a window of KD k-steps (2 fragments each);
+      // a sched barrier per step keeps the compiler from hoisting all 36
+      // reads (which would need 144 more VGPRs)
+      constexpr int KD = 5;
+      bf16x8 kf[KD][2];
+      auto kload = [&](int kk, bf16x8* dst) {
         const char* kb = (kk & 1) ? kb_odd : kb_even;
 #pragma unroll
-        for (int a = 0; a < 2; ++a) {
-          const bf16x8 kf =
-              as_bf16x8(*reinterpret_cast<const u32x4*>(kb + a * 16 * kMlaRowBytes + (kk >> 1) * 128));
+        for (int a = 0; a < 2; ++a)
+          dst[a] = as_bf16x8(*reinterpret_cast<const u32x4*>(kb + a * 16 * kMlaRowBytes + (kk >> 1) * 128));
+      };
 #pragma unroll
-          for (int hb = 0; hb < HB; ++hb) sacc[a][hb] = mfma16x16x32(kf, qf[hb][kk], sacc[a][hb]);
-        }
+      for (int kk = 0; kk < KD - 1; ++kk) kload(kk, kf[kk]);
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        if (kk + KD - 1 < NK) kload(kk + KD - 1, kf[(kk + KD - 1) % KD]);
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int hb = 0; hb < HB; ++hb) sacc[a][hb] = mfma16x16x32(kf[kk % KD][a], qf[hb][kk], sacc[a][hb]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
 
     // ---- softmax (log2 domain) for head 16 * (w * HB + hb) + col; this lane
-    // holds tokens 16a + 4 grp + rr
-    bool moved = false;
+    // holds tokens 16a + 4 grp + rr.  The reference maximum is the first
+    // tile's maximum and stays fixed for the piece, so the accumulators are
+    // never rescaled; a later score more than kMlaHeadroom above it (P could
+    // overflow) sends the request to the exact fallback in the merge pass.
+    bool over = false;
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
       float x[2][4];
-      float mt = -INFINITY;
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int t = 16 * a + 4 * grp + rr;
           x[a][rr] = t < valid ? sacc[a][hb][rr] * scale_log2 : -INFINITY;
-          mt = fmaxf(mt, x[a][rr]);
         }
-      mt = fmaxf(mt, shfl_xor(mt, 16));
-      mt = fmaxf(mt, shfl_xor(mt, 32));
-      float alpha = 1.0f;
-      if (mt > m_ref[hb] + kMlaSlack) {
-        alpha = fast_exp2(m_ref[hb] - mt);
+      if (seg_begin) {
+        float mt = -INFINITY;
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) mt = fmaxf(mt, x[a][rr]);
+        mt = fmaxf(mt, shfl_xor(mt, 16));
+        mt = fmaxf(mt, shfl_xor(mt, 32));
         m_ref[hb] = mt;
-        l_part[hb] *= alpha;
-        moved = true;
       }
       bf16x8 pa;
       float ps = 0.f;
@@ -314,63 +383,23 @@ __global__ void __launch_bounds__(64 * MlaCfg<HPB>::W, 1) mla_decode_kernel(
       for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
+          over |= x[a][rr] > m_ref[hb] + kMlaHeadroom;
           const float p = fast_exp2(x[a][rr] - m_ref[hb]);
           ps += p;
           pa[a * 4 + rr] = (bf16)p;
         }
       l_part[hb] += ps;
-      const int hbg = w * HB + hb;
-      p_lds[hbg * 64 + lane] = pa;
-      if (grp == 0) alpha_lds[hbg * 16 + col] = alpha;
+      p_lds[(w * HB + hb) * 64 + lane] = pa;
     }
-    const bool any_moved = __builtin_amdgcn_ballot_w64(moved) != 0;
-    if (lane == 0) flag_lds[w] = any_moved ? 1 : 0;
-    __syncthreads();  // P, alphas and flags of every wave are in LDS
+    if (__builtin_amdgcn_ballot_w64(over) != 0 && lane == 0) fallback[i] = 1;
+    __syncthreads();  // P of every wave is in LDS
 
-    int rescale = 0;
-#pragma unroll
-    for (int v = 0; v < W; ++v) rescale |= flag_lds[v];
-    if (rescale) {
-#pragma unroll
-      for (int hb = 0; hb < NHB; ++hb) {
-        const f32x4 al = *reinterpret_cast<const f32x4*>(&alpha_lds[hb * 16 + 4 * grp]);
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) acc[hb][cb] *= al;
-      }
-    }
-
-    // ---- O += P V over this wave's columns, all heads; four column blocks
-    // of V at a time (held in registers), P fragments re-read per group.
-    // Column block cb = 4 m + u of the whole row: the transposed read of
-    // lane (x, j) starts at token t = 4 j + x / 4, chunk 8 (cb / 4) +
-    // ((2 u + (x & 3) / 2) ^ (t & 7)): four per-lane bases (u) plus offsets.
-    {
-      const int x = lane & 15, jg = lane >> 4;
-      const int t = 4 * jg + (x >> 2);
-      const char* vb[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        vb[u] = tile + (t * kMlaRowChunks + ((2 * u + ((x & 3) >> 1)) ^ (t & 7))) * 16 + (x & 1) * 8 +
-                (w * NCB / 4) * 128;
-#pragma unroll
-      for (int cg = 0; cg < NCB; cg += 4) {
-        bf16x8 vf[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const char* lo = vb[u] + (cg / 4) * 128;
-          const i16x4 va = lds_read_tr16(reinterpret_cast<const bf16*>(lo));
-          const i16x4 vc = lds_read_tr16(reinterpret_cast<const bf16*>(lo + 16 * kMlaRowBytes));
-          const bf16x4 ba = __builtin_bit_cast(bf16x4, va), bc = __builtin_bit_cast(bf16x4, vc);
-          vf[u] = bf16x8{ba[0], ba[1], ba[2], ba[3], bc[0], bc[1], bc[2], bc[3]};
-        }
-#pragma unroll
-        for (int hb = 0; hb < NHB; ++hb) {
-          const bf16x8 pf = p_lds[hb * 64 + lane];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) acc[hb][cg + u] = mfma16x16x32(pf, vf[u], acc[hb][cg + u]);
-        }
-      }
-    }
+    // ---- O += P V over this wave's columns, all heads (the first tile of a
+    // piece starts the accumulators from zero inside the MFMA)
+    if (seg_begin)
+      mla_pv<NHB, NCB, true>(acc, tile, p_lds, w, lane);
+    else
+      mla_pv<NHB, NCB, false>(acc, tile, p_lds, w, lane);
 
     if (seg_end) {
 #pragma unroll
@@ -404,33 +433,70 @@ __global__ void __launch_bounds__(64 * MlaCfg<HPB>::W, 1) mla_decode_kernel(
           const float inv = 1.0f / lv[rr];
           if (direct) {
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) ob[hoff * kMlaV + cb * 16] = (bf16)(acc[hb][cb][rr] * inv);
+            for (int cb = 0; cb < NCB; ++cb) ob[hoff * kMlaV + cb * 16] = (bf16)(acc_get(acc[hb][cb][rr]) * inv);
           } else {
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) wb[hoff * kMlaV + cb * 16] = acc[hb][cb][rr] * inv;
+            for (int cb = 0; cb < NCB; ++cb) wb[hoff * kMlaV + cb * 16] = acc_get(acc[hb][cb][rr]) * inv;
           }
           if (write_lse) lb[hoff] = (mv[rr] + __log2f(lv[rr])) * kLn2;
         }
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) acc[hb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
+      // no zeroing here: the next segment's first tile rescales every head
+      // by exp2(-inf) = 0 (the accumulators are finite), and redefining the
+      // accumulators in this branch would cost a full copy per tile
     }
   }
   wait_vm<0>();  // no load may still target this workgroup's LDS when it ends
 }
 
 // ---------------------------------------------------------------------------
-// Merge: one wavefront per (request, head).  Requests finished inside one run
-// were written directly; empty requests get zeros and lse = -inf; the rest
-// combine their pieces (ids run + request) with log-sum-exp weights.
+// Exact fallback for one (request, head): plain online softmax over the
+// request's keys, one key at a time (lane l holds query values 9l .. 9l+8 and
+// value columns 8l .. 8l+7).  Only requests whose scores outran the fixed
+// softmax reference by more than the headroom come here.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) mla_merge_kernel(int32_t bs, int32_t Hq,
-                                                        const int32_t* __restrict__ header,
+__device__ void mla_exact_one(const char* kpool, const bf16* q_row, const int32_t* meta, int P, int L, float scale_log2,
+                              int lane, bf16* op, float* lse_out) {
+  float qv[9];
+#pragma unroll
+  for (int e = 0; e < 9; ++e) qv[e] = (float)q_row[lane * 9 + e];
+  float m = -INFINITY, l = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < L; ++t) {
+    const int64_t slot = meta[(int64_t)(P + t / kMlaT) * kMlaMetaWords + t % kMlaT];
+    const bf16* row = reinterpret_cast<const bf16*>(kpool + slot * kMlaRowBytes);
+    float d = 0.f;
+#pragma unroll
+    for (int e = 0; e < 9; ++e) d += qv[e] * (float)row[lane * 9 + e];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) d += shfl_xor(d, off);
+    const float sc = d * scale_log2;
+    const float mn = fmaxf(m, sc);
+    const float corr = fast_exp2(m - mn), p = fast_exp2(sc - mn);
+    l = l * corr + p;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = o[e] * corr + p * (float)row[lane * 8 + e];
+    m = mn;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) op[e] = (bf16)(o[e] / l);
+  if (lse_out && lane == 0) *lse_out = (m + __log2f(l)) * kLn2;
+}
+
+// ---------------------------------------------------------------------------
+// Merge: one wavefront per (request, head).  Requests finished inside one run
+// were written directly; empty requests get zeros and lse = -inf; flagged
+// requests are recomputed exactly; the rest combine their pieces (ids
+// run + request) with log-sum-exp weights.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) mla_merge_kernel(int32_t bs, int32_t Hq, const int32_t* __restrict__ header,
                                                         const int32_t* __restrict__ prefix,
                                                         const int32_t* __restrict__ ntiles,
+                                                        const int32_t* __restrict__ fallback,
                                                         const float* __restrict__ ws_o,
-                                                        const float* __restrict__ ws_lse, bf16* __restrict__ out,
-                                                        float* __restrict__ lse) {
+                                                        const float* __restrict__ ws_lse, const char* kpool,
+                                                        const bf16* __restrict__ q, const int32_t* __restrict__ meta,
+                                                        const int32_t* __restrict__ kv_lens, float scale_log2,
+                                                        bf16* __restrict__ out, float* __restrict__ lse) {
   const int lane = threadIdx.x & 63;
   const int64_t idx = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (idx >= (int64_t)bs * Hq) return;
@@ -443,8 +509,13 @@ __global__ void __launch_bounds__(256) mla_merge_kernel(int32_t bs, int32_t Hq,
     if (lse && lane == 0) lse[idx] = -INFINITY;
     return;
   }
-  const int Bt = header[0];
   const int P = prefix[i];
+  if (fallback[i]) {
+    const int L = min(kv_lens[i], T * kMlaT);
+    mla_exact_one(kpool, q + idx * kMlaQK, meta, P, L, scale_log2, lane, op, lse ? lse + idx : nullptr);
+    return;
+  }
+  const int Bt = header[0];
   const int b0 = P / Bt, b1 = (P + T - 1) / Bt;
   if (b0 == b1) return;
   float mx = -INFINITY;
@@ -504,7 +575,7 @@ DecodePlan plan_mla_decode(const PoolInfo& p, int32_t bs, int32_t Hq, int32_t ma
 
 static size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 
-// [header | tile prefix[bs] | tiles[bs] | meta[bs * max tiles][40] | pieces o | pieces lse]
+// [header | tile prefix[bs] | tiles[bs] | fallback flags[bs] | meta[bs * max tiles][40] | pieces o | pieces lse]
 size_t mla_ws_layout(const DecodePlan& plan, int32_t bs, int32_t Hq, void* base, MlaWs* w) {
   char* b = static_cast<char*>(base);
   size_t off = 0;
@@ -516,6 +587,7 @@ size_t mla_ws_layout(const DecodePlan& plan, int32_t bs, int32_t Hq, void* base,
   char* hdr = take(256);
   char* pre = take((size_t)bs * 4);
   char* nt = take((size_t)bs * 4);
+  char* fb = take((size_t)bs * 4);
   char* meta = take((size_t)bs * plan.chunk * kMlaMetaWords * 4);
   const size_t pieces = (size_t)plan.max_splits + bs;
   char* o = take(pieces * Hq * kMlaV * 4);
@@ -524,6 +596,7 @@ size_t mla_ws_layout(const DecodePlan& plan, int32_t bs, int32_t Hq, void* base,
     w->header = reinterpret_cast<int32_t*>(hdr);
     w->prefix = reinterpret_cast<int32_t*>(pre);
     w->ntiles = reinterpret_cast<int32_t*>(nt);
+    w->fallback = reinterpret_cast<int32_t*>(fb);
     w->meta = reinterpret_cast<int32_t*>(meta);
     w->o = reinterpret_cast<float*>(o);
     w->lse = reinterpret_cast<float*>(l);
@@ -537,7 +610,7 @@ static void launch_mla_main(int32_t runs, int32_t Hq, hipStream_t s, const char*
   const int sibs = Hq / HPB;
   hipLaunchKernelGGL((mla_decode_kernel<HPB>), dim3(runs * sibs), dim3(64 * MlaCfg<HPB>::W), 0, s, kp,
                      static_cast<const bf16*>(q), Hq, sibs, w.header, w.meta, sl2, static_cast<bf16*>(out), lse,
-                     w.o, w.lse);
+                     w.o, w.lse, w.fallback);
 }
 
 hipError_t launch_mla_decode(const PoolInfo& p, int32_t layer, const void* q, int32_t Hq, const DevMap& m, int32_t bs,
@@ -546,11 +619,11 @@ hipError_t launch_mla_decode(const PoolInfo& p, int32_t layer, const void* q, in
   mla_ws_layout(plan, bs, Hq, ws, &w);
   const int32_t runs = plan.max_splits;
   if (m.fmt == MAP_TOKEN_TABLE)
-    hipLaunchKernelGGL(mla_plan_kernel<SLOT_TABLE>, dim3(bs), dim3(256), 0, s, m, bs, plan.chunk, runs, w.header, w.prefix,
-                       w.ntiles, w.meta);
+    hipLaunchKernelGGL(mla_plan_kernel<SLOT_TABLE>, dim3(bs), dim3(256), 0, s, m, bs, plan.chunk, runs,
+                       w.header, w.prefix, w.ntiles, w.fallback, w.meta);
   else
-    hipLaunchKernelGGL(mla_plan_kernel<SLOT_PAGES>, dim3(bs), dim3(256), 0, s, m, bs, plan.chunk, runs, w.header, w.prefix,
-                       w.ntiles, w.meta);
+    hipLaunchKernelGGL(mla_plan_kernel<SLOT_PAGES>, dim3(bs), dim3(256), 0, s, m, bs, plan.chunk, runs,
+                       w.header, w.prefix, w.ntiles, w.fallback, w.meta);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const char* kp = p.k_layer(layer);
@@ -562,8 +635,9 @@ hipError_t launch_mla_decode(const PoolInfo& p, int32_t layer, const void* q, in
   timer_after(s);
   if (e != hipSuccess) return e;
   const unsigned mblocks = (unsigned)(((int64_t)bs * Hq + 3) / 4);
-  hipLaunchKernelGGL(mla_merge_kernel, dim3(mblocks), dim3(256), 0, s, bs, Hq, w.header, w.prefix,
-                     w.ntiles, w.o, w.lse, static_cast<bf16*>(out), lse);
+  hipLaunchKernelGGL(mla_merge_kernel, dim3(mblocks), dim3(256), 0, s, bs, Hq, w.header, w.prefix, w.ntiles,
+                     w.fallback, w.o, w.lse, kp, static_cast<const bf16*>(q), w.meta, m.kv_lens, sl2,
+                     static_cast<bf16*>(out), lse);
   return hipGetLastError();
 }
 

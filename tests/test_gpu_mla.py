@@ -39,7 +39,11 @@ def test_mla_decode_fewer_heads(heads):
     assert_lse_close(lse, ref_l, "bf16", f"mla {heads} heads")
 
 
-def test_mla_planted_key_and_empty_request():
+@pytest.mark.parametrize("key_scale", [80.0, 200.0])
+def test_mla_planted_key_and_empty_request(key_scale):
+    """One key far along the query direction.  At 200 its score sits ~100
+    log2 units above the first tile's: the kernel's fixed softmax reference
+    would overflow there, so the request goes through the exact fallback."""
     case = W.mla_decode(seed=3, bs=4, len_range=(200, 900))
     case.regions["self"].kv_lens[2] = 0
     vals = W.make_values(case)
@@ -49,7 +53,7 @@ def test_mla_planted_key_and_empty_request():
     u = torch.randn(576, generator=torch.Generator().manual_seed(5))
     u = u / u.norm()
     vals["q"]["self"][i] = (u * 8.0).to(torch.bfloat16)[None, :].expand(case.geom.num_q_heads, 576)
-    key = (u * 80.0).to(torch.bfloat16)
+    key = (u * key_scale).to(torch.bfloat16)
     t = L // 2
     slot = int(case.req_to_token[case.req_pool_indices[i], t])
     vals["pool_k"][slot, 0] = key
