@@ -430,7 +430,8 @@ def main():
         b.step(pairs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kern_ms = [sum(ev.elapsed_ms(a, z) for a, z in step) for step in pairs]
+    call_ms = [[ev.elapsed_ms(a, z) for a, z in step] for step in pairs]
+    kern_ms = [sum(c) for c in call_ms]
     for step in pairs:
         for a, z in step:
             ev.destroy(a)
@@ -450,6 +451,8 @@ def main():
     roof.update({"traffic": measured_traffic(args.workload), "kernel": b.kernel_name, "kernel_ms": round(k_ms, 5),
                  "kernel_bytes": b.kernel_bytes(), "kernel_gbs": round(kern_gbs, 2),
                  "kernel_hbm_frac": round(kern_gbs / HBM_PEAK_GBS, 4), "kernel_tflops": round(kern_tf, 3)})
+    if b.attn_calls > 1:
+        roof["call_ms"] = [round(float(np.mean([c[k] for c in call_ms])), 5) for k in range(b.attn_calls)]
     res = {
         "metric": "paged decode attn: achieved HBM GB/s (% of peak) + decode tokens/s, 1 GPU",
         "value": round(step_gbs, 2),

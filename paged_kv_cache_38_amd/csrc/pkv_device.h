@@ -135,6 +135,16 @@ struct SlotMap {
   // Two halves of a lookup, so a loop can issue the table load early and
   // use it a tile later: raw() is the bare load (index clamped to a
   // readable entry), finish() the checks, with no memory access.
+  // address raw(t) reads (any readable word for a contiguous map)
+  __device__ __forceinline__ const int32_t* raw_ptr(int32_t t) const {
+    if constexpr (FMT == SLOT_CONTIG) {
+      return base;
+    } else if constexpr (FMT == SLOT_TABLE) {
+      return base + min(max(t, 0), max(limit - 1, 0));
+    } else {
+      return base + min(max(t >> shift, 0), max(limit - 1, 0));
+    }
+  }
   __device__ __forceinline__ int32_t raw(int32_t t) const {
     if constexpr (FMT == SLOT_CONTIG) {
       return 0;
@@ -239,6 +249,14 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // xor-shuffle across the wavefront (ds_bpermute)
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 __device__ __forceinline__ float shfl(float v, int src) { return __shfl(v, src, 64); }
+// max over lanes l, l ^ 16, l ^ 32, l ^ 48 with the gfx950 lane-swap
+// instructions (VALU, no LDS traffic)
+__device__ __forceinline__ float max_xor16_32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
 // integer lane gather (ds_bpermute): value of lane `src` (0..63)
 __device__ __forceinline__ int32_t shfl_i(int32_t v, int src) { return __builtin_amdgcn_ds_bpermute(src << 2, v); }
 
@@ -272,6 +290,33 @@ __device__ __forceinline__ bf16x8 lds_v_operand(const bf16* tile, int lds, int r
   const i16x4 hi = lds_read_tr16(base + 16 * lds);
   const bf16x4 blo = __builtin_bit_cast(bf16x4, lo), bhi = __builtin_bit_cast(bf16x4, hi);
   return bf16x8{blo[0], blo[1], blo[2], blo[3], bhi[0], bhi[1], bhi[2], bhi[3]};
+}
+
+// ---------------------------------------------------------------------------
+// HBM -> LDS loads (global_load_lds_*) issued from inline assembly.  The
+// compiler does not see them, so it never drains the whole memory queue for
+// them; every user waits on them explicitly with wait_vm<N>() (N = memory
+// operations issued after the one needed, counting every vector memory
+// operation of the wave).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t lds_off(const void* p) {
+  // the LDS aperture is 4 GiB aligned: the low 32 bits of a flat LDS address
+  // are the LDS byte offset
+  return (uint32_t)(uintptr_t)p;
+}
+// one 16-byte chunk per lane, global -> LDS at m0 + 16 * lane
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+// one dword per lane, global -> LDS at m0 + 4 * lane
+__device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
+  asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }

@@ -11,7 +11,7 @@
 //
 // Layout on gfx950: one block per (64-query tile, query head, request); four
 // wavefronts of 16 query rows each.  Key tiles of 64 tokens are gathered
-// through the table into LDS (token-major, 16-byte padded rows), double
+// through the table into LDS (token-major rows, 16-byte chunks XOR-swizzled), double
 // buffered so the next tile's HBM reads overlap this tile's MFMA work:
 //   S^T[16 keys x 16 rows] = K_tile[16 x D] * Q^T[D x 16]   (v_mfma_f32_16x16x32_bf16)
 // leaves each lane one query row (lane % 16) and 16 keys, so the row softmax
@@ -20,209 +20,298 @@
 // whose B operand comes from LDS with ds_read_b64_tr_b16.
 #include <math.h>
 
+#include <type_traits>
+
 #include "pkv_launch.h"
 
 namespace pkv {
 
-constexpr int kBM = 64;  // query rows per block
-constexpr int kBN = 64;  // keys per tile
+constexpr int kBM = 128;  // query rows per block (32 per wave, two 16-row blocks)
+constexpr int kBN = 64;   // keys per tile
+constexpr float kExtSlack = 8.0f;  // log2 headroom before a row's running max moves
 
 template <int D>
 struct ExtendCfg {
-  static constexpr int LDS = D + 8;          // LDS row stride (elements)
-  static constexpr int NK = D / 32;          // MFMAs along d for S
+  static constexpr int NK = D / 32;          // k-steps of the score product
   static constexpr int NT = D / 16;          // 16-wide d tiles of O
   static constexpr int CPK = D / 8;          // 16-byte chunks per key row (one head)
-  static constexpr int KPI = 256 / CPK;      // keys per block-wide load instruction
-  static constexpr int LIT = kBN / KPI;      // load instructions per tile per tensor
+  static constexpr int TILE = kBN * D * 2;   // bytes of one K (or V) tile
+  static constexpr int NI = 2 * TILE / 1024 / 4;  // K+V DMA instructions per wave per tile
+  static constexpr int S = D == 64 ? 3 : 2;  // LDS stages (tiles resident)
+  static constexpr int WAIT = S == 2 ? 1 : NI + 1;
 };
 
+// Byte offset of 16-byte chunk c of key row t in an LDS tile: rows are
+// D * 2 bytes apart and chunk c sits at c ^ (t & 7), so the eight rows a
+// K-operand read touches at once, and the four rows of a transposed V read,
+// fall in different banks.
 template <int D>
-struct ExtendRegs {
-  u32x4 k[ExtendCfg<D>::LIT];
-  u32x4 v[ExtendCfg<D>::LIT];
-};
-
-// global -> registers for key tile starting at k0 (keys past kv_end read the
-// padding row and are zeroed when written to LDS)
-template <int D, int FMT>
-__device__ __forceinline__ void extend_load(ExtendRegs<D>& R, const SlotMap<FMT>& sm, int k0, int kv_end,
-                                            const bf16* kb, const bf16* vb, int64_t row_elems) {
-  using C = ExtendCfg<D>;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int it = 0; it < C::LIT; ++it) {
-    const int t = k0 + it * C::KPI + tid / C::CPK;
-    const int64_t slot = sm(t, t < kv_end);
-    const int64_t off = slot * row_elems + (tid % C::CPK) * 8;
-    R.k[it] = *reinterpret_cast<const u32x4*>(kb + off);
-    R.v[it] = *reinterpret_cast<const u32x4*>(vb + off);
-  }
+__device__ __forceinline__ int ext_off(int t, int c) {
+  return (t * (D / 8) + (c ^ (t & 7))) * 16;
 }
 
+// B operand of P*V from a swizzled tile: lane (n = l%16, j = l/16) receives
+// V[r0 + 4j + r][c0 + n] (low half) and V[r0 + 16 + 4j + r][c0 + n] (high half).
 template <int D>
-__device__ __forceinline__ void extend_store_lds(const ExtendRegs<D>& R, int k0, int kv_end, bf16* ks, bf16* vs) {
-  using C = ExtendCfg<D>;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int it = 0; it < C::LIT; ++it) {
-    const int row = it * C::KPI + tid / C::CPK;
-    const bool ok = k0 + row < kv_end;
-    u32x4 kw = R.k[it], vw = R.v[it];
-    if (!ok) {
-      kw = u32x4{0u, 0u, 0u, 0u};
-      vw = u32x4{0u, 0u, 0u, 0u};  // masked keys must hold 0 (P * NaN would poison the sum)
-    }
-    const int o = row * C::LDS + (tid % C::CPK) * 8;
-    *reinterpret_cast<u32x4*>(ks + o) = kw;
-    *reinterpret_cast<u32x4*>(vs + o) = vw;
-  }
+__device__ __forceinline__ bf16x8 ext_v_operand(const char* tile, int r0, int c0, int lane) {
+  const int x = lane & 15, j = lane >> 4;
+  const int t = r0 + 4 * j + (x >> 2);
+  const int c = c0 + 4 * (x & 3);
+  const char* lo = tile + ext_off<D>(t, c >> 3) + (c & 7) * 2;
+  const i16x4 a = lds_read_tr16(reinterpret_cast<const bf16*>(lo));
+  const i16x4 b = lds_read_tr16(reinterpret_cast<const bf16*>(lo + 16 * D * 2));
+  const bf16x4 ba = __builtin_bit_cast(bf16x4, a), bb = __builtin_bit_cast(bf16x4, b);
+  return bf16x8{ba[0], ba[1], ba[2], ba[3], bb[0], bb[1], bb[2], bb[3]};
 }
 
 template <int D, int FMT>
-__global__ void __launch_bounds__(256, 2) extend_kernel(DevMap m, const bf16* k_pool, const bf16* v_pool,
-                                                        int64_t row_elems, const bf16* __restrict__ q,
-                                                        int64_t total_q, const int32_t* __restrict__ qo_indptr,
-                                                        int32_t Hq,
-                                                        int32_t G, int32_t causal, float scale_log2,
-                                                        bf16* __restrict__ out, float* __restrict__ lse) {
+__global__ void __launch_bounds__(256, D == 64 ? 3 : 2) extend_kernel(DevMap m, const char* k_pool, const char* v_pool,
+                                                     int64_t row_bytes, const bf16* __restrict__ q, int64_t total_q,
+                                                     const int32_t* __restrict__ qo_indptr, int32_t Hq, int32_t n_req,
+                                                     int32_t n_qtiles, int32_t G, int32_t causal, float scale_log2,
+                                                     bf16* __restrict__ out, float* __restrict__ lse) {
   using C = ExtendCfg<D>;
-  constexpr int LDS = C::LDS, NK = C::NK, NT = C::NT;
-  __shared__ __attribute__((aligned(16))) bf16 ksm[2][kBN * LDS];
-  __shared__ __attribute__((aligned(16))) bf16 vsm[2][kBN * LDS];
+  constexpr int NK = C::NK, NT = C::NT, CPK = C::CPK, NI = C::NI, S = C::S;
+  __shared__ __attribute__((aligned(1024))) char kv_lds[S][2][C::TILE];
+  __shared__ __attribute__((aligned(256))) int32_t tab_lds[4][S + 1][64];
 
-  const int qt = blockIdx.x, h = blockIdx.y, i = blockIdx.z;
+  // blocks are dealt to the 8 XCDs round robin (block b on XCD b % 8).  The
+  // (request, head) pairs are spread over the XCDs round robin too (pair p
+  // on XCD p % 8), so every request's work is split evenly across them,
+  // and all query tiles of one pair run back to back on one XCD, sharing
+  // its L2: each key/value tile leaves HBM once.
+  const int x = (int)(blockIdx.x & 7), k = (int)(blockIdx.x >> 3);
+  const int pair = x + 8 * (k / n_qtiles);
+  const int qt = k % n_qtiles;
+  const int h = pair % Hq;
+  const int i = pair / Hq;
+  if (i >= n_req) return;
   const int q0 = qo_indptr[i];
   // rows past total_q (a qo_indptr beyond the buffers) are never touched
   const int n = (q0 < 0 || q0 >= total_q) ? 0 : (int)min((int64_t)(qo_indptr[i + 1] - q0), total_q - q0);
   if (qt * kBM >= n) return;
   int L = m.kv_lens[i];
   if (FMT == SLOT_CONTIG && m.total_k <= 0) L = 0;  // nothing gathered: no row is readable
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (L < 0) L = 0;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int g = h / G;
-  const int r0 = qt * kBM + wave * 16;  // first query row (within the request) of this wave
+  const int rw = qt * kBM + w * 32;  // first query row (within the request) of this wave
 
-  // keys any row of this tile may see
+  // keys any row of this block may see
   int kv_end = L;
   if (causal) kv_end = min(L, L - n + min(qt * kBM + kBM, n));
   if (kv_end < 0) kv_end = 0;
+  const int ntiles = (kv_end + kBN - 1) / kBN;
+  // keys this wave's rows may see, and where the causal mask starts to bite
+  const int w_end = causal ? max(0, min(L, L - n + min(rw + 32, n))) : L;
+  const int w_free = causal ? max(0, L - n + rw + 1) : L;  // keys visible to every row of the wave
 
-  // Q^T operand: lane (row col, group grp) holds q[row][kk*32 + grp*8 .. +8]
-  bf16x8 qb[NK];
-  {
-    const int row = r0 + col;
+  // Q^T operands: lane (row col of row block rb, group grp) holds
+  // q[row][kk*32 + grp*8 .. +8]
+  bf16x8 qb[2][NK];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int row = rw + rb * 16 + col;
     const bool ok = row < n;
     const bf16* qp = q + ((int64_t)(q0 + (ok ? row : 0)) * Hq + h) * D + grp * 8;
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
-      u32x4 w = *reinterpret_cast<const u32x4*>(qp + kk * 32);
-      if (!ok) w = u32x4{0u, 0u, 0u, 0u};
-      qb[kk] = as_bf16x8(w);
+      u32x4 v = *reinterpret_cast<const u32x4*>(qp + kk * 32);
+      if (!ok) v = u32x4{0u, 0u, 0u, 0u};
+      qb[rb][kk] = as_bf16x8(v);
     }
   }
-  // last key (exclusive) this lane's row may see
-  const int my_row = r0 + col;
-  const int row_end = causal ? min(L, L - n + my_row + 1) : L;
-
-  f32x4 acc[NT];
+  int row_end[2];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int rb = 0; rb < 2; ++rb) {
+    const int row = rw + rb * 16 + col;
+    row_end[rb] = causal ? min(L, L - n + row + 1) : L;
+  }
 
-  const int ntiles = (kv_end + kBN - 1) / kBN;
+  f32x4 acc[2][NT];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[rb][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 acc_l[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};  // row sums (any column)
+  float m_run[2] = {-INFINITY, -INFINITY};
+
   if (ntiles > 0) {
     const SlotMap<FMT> sm = make_slotmap<FMT>(m, i);
-    const bf16* kb = k_pool + (int64_t)g * D;
-    const bf16* vb = v_pool + (int64_t)g * D;
-    ExtendRegs<D> R;
-    extend_load<D, FMT>(R, sm, 0, kv_end, kb, vb, row_elems);
-    extend_store_lds<D>(R, 0, kv_end, ksm[0], vsm[0]);
-    __syncthreads();
-    for (int kt = 0; kt < ntiles; ++kt) {
-      const int k0 = kt * kBN;
-      // next tile's rows in flight during this tile's math (unconditional:
-      // past the last tile it reads the padding row, which stays in cache)
-      extend_load<D, FMT>(R, sm, k0 + kBN, kv_end, kb, vb, row_elems);
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_sched_barrier(0);
-      const bf16* ks = ksm[kt & 1];
-      const bf16* vs = vsm[kt & 1];
-      // ---- S^T: 4 subtiles of 16 keys
-      f32x4 sacc[4];
+    const char* kb = k_pool + (int64_t)g * D * 2;
+    const char* vb = v_pool + (int64_t)g * D * 2;
+    // table entries of a tile's 64 keys (keys past kv_end repeat the last
+    // visible key, so every row read is a real, finite one)
+    auto tab_dma = [&](int kt) {
+      const int t = min(min(kt, ntiles - 1) * kBN + lane, kv_end - 1);
+      dma4(sm.raw_ptr(t), lds_off(&tab_lds[w][kt % (S + 1)][0]));
+    };
+    // K and V rows of a tile; wave w moves chunk positions
+    // [w * NI/2 * 64, (w + 1) * NI/2 * 64) of each
+    auto kv_dma = [&](int kt) {
+      const int32_t* tr = &tab_lds[w][kt % (S + 1)][0];
+      const int k0 = min(kt, ntiles - 1) * kBN;
+      char* kt_lds = kv_lds[kt % S][0];
+      char* vt_lds = kv_lds[kt % S][1];
+      int ln = lane;
+      asm volatile("" : "+v"(ln));  // recompute per tile instead of holding NI addresses
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        sacc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < NK; ++kk) {
-          const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(ks + (a * 16 + col) * LDS + kk * 32 + grp * 8));
-          sacc[a] = mfma16x16x32(ka, qb[kk], sacc[a]);
-        }
+      for (int j = 0; j < NI / 2; ++j) {
+        const int pos = (w * (NI / 2) + j) * 64 + ln;
+        const int t = pos / CPK;
+        const int c = (pos % CPK) ^ (t & 7);
+        const int tt = min(k0 + t, kv_end - 1);
+        const int64_t slot = sm.finish(tr[t], tt, true);
+        const int64_t off = slot * row_bytes + c * 16;
+        dma16(kb + off, lds_off(kt_lds + (w * (NI / 2) + j) * 1024));
+        dma16(vb + off, lds_off(vt_lds + (w * (NI / 2) + j) * 1024));
       }
-      // ---- online softmax for row my_row over keys k0 + a*16 + 4*grp + rr
-      float sv[4][4];
-      float mt = -INFINITY;
+    };
+    // prologue: queue = [tables 0 .. S-1 landed] tile 0 .. tile S-2, table S-1 ..
+    for (int k = 0; k < S; ++k) tab_dma(k);
+    wait_vm<0>();
+    for (int k = 0; k < S - 1; ++k) kv_dma(k);
+
+    // per-lane parts of the LDS addresses; the tile loop is unrolled by the
+    // stage count so stage bases and subtile steps become immediates.
+    // K operand (token a*16 + col, chunk kk*4 + grp): chunk bits above the
+    // swizzle are kk / 2, so two bases (kk even / odd) cover every read.
+    const int sk = col & 7;
+    const int kbase0 = (col * CPK + (grp ^ sk)) * 16;
+    const int kbase1 = (col * CPK + ((4 + grp) ^ sk)) * 16;
+    // V operand (token b*32 + 4j + x/4, chunk 2 nt + (x&3)/2): four bases by
+    // nt & 3, the rest immediates
+    int vbase[4];
+    {
+      const int x = lane & 15, j = lane >> 4;
+      const int t = 4 * j + (x >> 2);
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int t = k0 + a * 16 + grp * 4 + rr;
-          const float x = (t < row_end) ? sacc[a][rr] * scale_log2 : -INFINITY;
-          sv[a][rr] = x;
-          mt = fmaxf(mt, x);
-        }
-      mt = fmaxf(mt, shfl_xor(mt, 16));
-      mt = fmaxf(mt, shfl_xor(mt, 32));
-      const float m_new = fmaxf(m_run, mt);
-      // a row that has seen no key yet keeps m = -inf; its p and alpha are 0
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      float psum = 0.f;
-      bf16x8 pa[2];
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const float p = fast_exp2(sv[a][rr] - m_use);
-          psum += p;
-          pa[a >> 1][(a & 1) * 4 + rr] = (bf16)p;
-        }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const float ar = shfl(alpha, grp * 4 + rr);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[nt][rr] *= ar;
-      }
-      // ---- O += P V over two 32-key halves
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-          acc[nt] = mfma16x16x32(pa[b], lds_v_operand(vs, LDS, b * 32, nt * 16, lane), acc[nt]);
-      // ---- next tile into the other buffer
-      if (kt + 1 < ntiles) extend_store_lds<D>(R, k0 + kBN, kv_end, ksm[(kt + 1) & 1], vsm[(kt + 1) & 1]);
-      __syncthreads();
+      for (int u = 0; u < 4; ++u) vbase[u] = (t * CPK + ((2 * u + ((x & 3) >> 1)) ^ (t & 7))) * 16 + (x & 1) * 8;
     }
+    const char* lds0 = &kv_lds[0][0][0];
+    const bf16x8 ones = bf16x8{(bf16)1.f, (bf16)1.f, (bf16)1.f, (bf16)1.f, (bf16)1.f, (bf16)1.f, (bf16)1.f, (bf16)1.f};
+
+    auto tile_step = [&](int kt, auto stage_c, auto mask_c) {
+      constexpr int st = decltype(stage_c)::value;
+      constexpr bool MASK = decltype(mask_c)::value;
+      const char* ks = lds0 + (st * 2 + 0) * C::TILE;
+      const char* vs = lds0 + (st * 2 + 1) * C::TILE;
+      const int k0 = kt * kBN;
+
+      // ---- S^T = K Q^T: four 16-key subtiles x two 16-row blocks
+      f32x4 sacc[4][2];
+#pragma unroll
+      for (int a2 = 0; a2 < 4; ++a2) {
+        sacc[a2][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        sacc[a2][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        const char* kb = ks + ((kk & 1) ? kbase1 : kbase0) + (kk >> 1) * 128;
+#pragma unroll
+        for (int a2 = 0; a2 < 4; ++a2) {
+          const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(kb + a2 * 16 * CPK * 16));
+          sacc[a2][0] = mfma16x16x32(ka, qb[0][kk], sacc[a2][0]);
+          sacc[a2][1] = mfma16x16x32(ka, qb[1][kk], sacc[a2][1]);
+        }
+      }
+
+      // ---- online softmax (log2 domain); lane holds keys k0 + 16a + 4grp + rr
+      // of row rb*16 + col.  The max is taken on raw scores (the scale is
+      // positive), so each probability is one fma and one exp2.  O is kept
+      // transposed (lane col = row, like the scores), so the per-row rescale
+      // is a plain multiply in every lane: no cross-lane traffic.
+      bf16x8 pa[2][2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        float x[4][4];
+        float mr = -INFINITY;
+#pragma unroll
+        for (int a2 = 0; a2 < 4; ++a2)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            x[a2][rr] = sacc[a2][rb][rr];
+            if (MASK && k0 + a2 * 16 + grp * 4 + rr >= row_end[rb]) x[a2][rr] = -INFINITY;
+            mr = fmaxf(mr, x[a2][rr]);
+          }
+        const float m_new = fmaxf(m_run[rb], max_xor16_32(mr) * scale_log2);
+        // a row that has seen no key yet keeps m = -inf: use 0 so p = 0
+        const float mu = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run[rb] - mu);
+        m_run[rb] = m_new;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[rb][nt] *= alpha;
+        acc_l[rb] *= alpha;
+#pragma unroll
+        for (int a2 = 0; a2 < 4; ++a2)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            pa[rb][a2 >> 1][(a2 & 1) * 4 + rr] = (bf16)fast_exp2(fmaf(x[a2][rr], scale_log2, -mu));
+      }
+
+      // ---- O^T += V^T P^T over two 32-key halves (each V fragment serves
+      // both row blocks); the row sums ride along as a row of ones in V^T
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const char* lo = vs + vbase[nt & 3] + (nt >> 2) * 128 + b2 * 32 * CPK * 16;
+          const i16x4 va = lds_read_tr16(reinterpret_cast<const bf16*>(lo));
+          const i16x4 vc = lds_read_tr16(reinterpret_cast<const bf16*>(lo + 16 * CPK * 16));
+          const bf16x4 ba = __builtin_bit_cast(bf16x4, va), bc = __builtin_bit_cast(bf16x4, vc);
+          const bf16x8 vf = bf16x8{ba[0], ba[1], ba[2], ba[3], bc[0], bc[1], bc[2], bc[3]};
+          acc[0][nt] = mfma16x16x32(vf, pa[0][b2], acc[0][nt]);
+          acc[1][nt] = mfma16x16x32(vf, pa[1][b2], acc[1][nt]);
+        }
+        acc_l[0] = mfma16x16x32(ones, pa[0][b2], acc_l[0]);
+        acc_l[1] = mfma16x16x32(ones, pa[1][b2], acc_l[1]);
+      }
+    };
+
+    auto step = [&](int kt, auto stage_c) {
+      tab_dma(kt + S);
+      wait_vm<C::WAIT>();  // tile kt and table kt + S - 1 have landed
+      __syncthreads();     // tile kt visible to all waves; every wave is past tile kt - 1
+      kv_dma(kt + S - 1);  // into the stage tile kt - 1 used
+      // a wave whose rows are all past n, or whose rows see none of this
+      // tile's keys, only helps move the tiles; keys past what every row of
+      // the wave sees need the per-element mask
+      if (rw < n && kt * kBN < w_end) {
+        if (kt * kBN + kBN <= w_free)
+          tile_step(kt, stage_c, std::false_type{});
+        else
+          tile_step(kt, stage_c, std::true_type{});
+      }
+    };
+    for (int kt = 0; kt < ntiles; kt += S) {
+      step(kt, std::integral_constant<int, 0>{});
+      if (kt + 1 < ntiles) step(kt + 1, std::integral_constant<int, 1>{});
+      if constexpr (S > 2) {
+        if (kt + 2 < ntiles) step(kt + 2, std::integral_constant<int, 2 % S>{});
+      }
+    }
+    wait_vm<0>();  // no load may still target this block's LDS when it ends
   }
 
-  // ---- finalise rows 4*grp + rr of this wave
-  float l_tot = l_run + shfl_xor(l_run, 16);
-  l_tot += shfl_xor(l_tot, 32);
+  // ---- finalise: lane (row col of block rb, group grp) holds
+  // O[row][16 nt + 4 grp + rr] and the row's sum in acc_l
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    const int rl = grp * 4 + rr;
-    const float lt = shfl(l_tot, rl);
-    const float mr = shfl(m_run, rl);
-    const int row = r0 + rl;
+  for (int rb = 0; rb < 2; ++rb) {
+    const int row = rw + rb * 16 + col;
     if (row < n) {
       const int64_t o = ((int64_t)(q0 + row) * Hq + h);
+      const float lt = acc_l[rb][0];
       const bool any = lt > 0.f;
       const float inv = any ? 1.0f / lt : 0.f;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) out[o * D + nt * 16 + col] = (bf16)(acc[nt][rr] * inv);
-      if (lse && col == 0) lse[o] = any ? (mr + __log2f(lt)) * kLn2 : -INFINITY;
+      for (int nt = 0; nt < NT; ++nt) {
+        bf16x4 v;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) v[rr] = (bf16)(acc[rb][nt][rr] * inv);
+        *reinterpret_cast<bf16x4*>(out + o * D + nt * 16 + grp * 4) = v;
+      }
+      if (lse && grp == 0) lse[o] = any ? (m_run[rb] + __log2f(lt)) * kLn2 : -INFINITY;
     }
   }
 }
@@ -236,23 +325,28 @@ bool extend_supported(const PoolInfo& p, int32_t num_q_heads) {
 }
 
 template <int D, int FMT>
-static void launch_ext(dim3 grid, hipStream_t s, const DevMap& m, const bf16* kp, const bf16* vp, int64_t row_elems,
+static void launch_ext(dim3 grid, hipStream_t s, const DevMap& m, const char* kp, const char* vp, int64_t row_bytes,
                        const void* q, int64_t tq, const int32_t* qo, int32_t Hq, int32_t G, int32_t causal, float sl2,
                        void* out, float* lse) {
-  hipLaunchKernelGGL((extend_kernel<D, FMT>), grid, dim3(256), 0, s, m, kp, vp, row_elems,
-                     static_cast<const bf16*>(q), tq, qo, Hq, G, causal, sl2, static_cast<bf16*>(out), lse);
+  const int32_t qtiles = (int32_t)grid.y;
+  const int32_t nreq = (int32_t)grid.z;
+  const int64_t pairs = (int64_t)nreq * Hq;
+  const dim3 g1((unsigned)(8 * ((pairs + 7) / 8) * qtiles));
+  hipLaunchKernelGGL((extend_kernel<D, FMT>), g1, dim3(256), 0, s, m, kp, vp, row_bytes,
+                     static_cast<const bf16*>(q), tq, qo, Hq, nreq, qtiles, G, causal, sl2, static_cast<bf16*>(out),
+                     lse);
 }
 
 template <int D>
-static void launch_ext_fmt(dim3 grid, hipStream_t s, const DevMap& m, const bf16* kp, const bf16* vp,
-                           int64_t row_elems, const void* q, int64_t tq, const int32_t* qo, int32_t Hq, int32_t G,
+static void launch_ext_fmt(dim3 grid, hipStream_t s, const DevMap& m, const char* kp, const char* vp,
+                           int64_t row_bytes, const void* q, int64_t tq, const int32_t* qo, int32_t Hq, int32_t G,
                            int32_t causal, float sl2, void* out, float* lse) {
   if (m.fmt == MAP_TOKEN_TABLE)
-    launch_ext<D, SLOT_TABLE>(grid, s, m, kp, vp, row_elems, q, tq, qo, Hq, G, causal, sl2, out, lse);
+    launch_ext<D, SLOT_TABLE>(grid, s, m, kp, vp, row_bytes, q, tq, qo, Hq, G, causal, sl2, out, lse);
   else if (m.fmt == MAP_CONTIGUOUS)
-    launch_ext<D, SLOT_CONTIG>(grid, s, m, kp, vp, row_elems, q, tq, qo, Hq, G, causal, sl2, out, lse);
+    launch_ext<D, SLOT_CONTIG>(grid, s, m, kp, vp, row_bytes, q, tq, qo, Hq, G, causal, sl2, out, lse);
   else
-    launch_ext<D, SLOT_PAGES>(grid, s, m, kp, vp, row_elems, q, tq, qo, Hq, G, causal, sl2, out, lse);
+    launch_ext<D, SLOT_PAGES>(grid, s, m, kp, vp, row_bytes, q, tq, qo, Hq, G, causal, sl2, out, lse);
 }
 
 hipError_t launch_extend(const PoolInfo& p, int32_t layer, const void* q, int64_t total_q, const int32_t* qo_indptr,
@@ -262,17 +356,18 @@ hipError_t launch_extend(const PoolInfo& p, int32_t layer, const void* q, int64_
   (void)max_kv_len;
   if (bs == 0 || max_q_len == 0) return hipSuccess;
   // contiguous (ragged) maps read the caller's gathered K/V, paged maps the pool
-  const bf16* kp = reinterpret_cast<const bf16*>(m.fmt == MAP_CONTIGUOUS ? m.contig_k : p.k_layer(layer));
-  const bf16* vp = reinterpret_cast<const bf16*>(m.fmt == MAP_CONTIGUOUS ? m.contig_v : p.v_layer(layer));
+  const char* kp = reinterpret_cast<const char*>(m.fmt == MAP_CONTIGUOUS ? m.contig_k : p.k_layer(layer));
+  const char* vp = reinterpret_cast<const char*>(m.fmt == MAP_CONTIGUOUS ? m.contig_v : p.v_layer(layer));
   const int G = Hq / p.num_kv_heads;
-  const dim3 grid((unsigned)((max_q_len + kBM - 1) / kBM), (unsigned)Hq, (unsigned)bs);
-  const int64_t row_elems = (int64_t)p.num_kv_heads * p.head_dim_qk;
+  // (query tiles, -, requests); the launcher flattens it XCD-aware
+  const dim3 grid(1, (unsigned)((max_q_len + kBM - 1) / kBM), (unsigned)bs);
+  const int64_t row_bytes = (int64_t)p.num_kv_heads * p.head_dim_qk * 2;  // one token row, all KV heads
   const float sl2 = sm_scale * kLog2e;
   timer_before(s);
   if (p.head_dim_qk == 128)
-    launch_ext_fmt<128>(grid, s, m, kp, vp, row_elems, q, total_q, qo_indptr, Hq, G, causal, sl2, out, lse);
+    launch_ext_fmt<128>(grid, s, m, kp, vp, row_bytes, q, total_q, qo_indptr, Hq, G, causal, sl2, out, lse);
   else
-    launch_ext_fmt<64>(grid, s, m, kp, vp, row_elems, q, total_q, qo_indptr, Hq, G, causal, sl2, out, lse);
+    launch_ext_fmt<64>(grid, s, m, kp, vp, row_bytes, q, total_q, qo_indptr, Hq, G, causal, sl2, out, lse);
   hipError_t e = hipGetLastError();
   timer_after(s);
   return e;

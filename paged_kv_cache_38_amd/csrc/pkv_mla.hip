@@ -69,27 +69,6 @@ struct MlaCfg {
   static constexpr int NI = (kMlaTileBytes / 1024) / W;  // tile DMA instructions per wave
 };
 
-__device__ __forceinline__ uint32_t lds_off(const void* p) {
-  // the LDS aperture is 4 GiB aligned: the low 32 bits of a flat LDS address
-  // are the LDS byte offset
-  return (uint32_t)(uintptr_t)p;
-}
-
-// one 16-byte chunk per lane, global -> LDS at m0 + 16 * lane
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
-               : "memory");
-}
-// one dword per lane, global -> LDS at m0 + 4 * lane
-__device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
-  asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
-}
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
 // The P*V accumulators live in AGPRs for the whole kernel: outside the MFMAs
 // they are only read (through this), never redefined in a branch, which would
 // make the compiler copy all of them on every tile.
