@@ -1,46 +1,46 @@
-// Paged decode attention for grouped-query heads: the split plan, the
-// split-K partial kernels and the log-sum-exp merge.
+// Paged decode attention for grouped-query heads: the split plans, the
+// split-K partial kernels and the log-sum-exp merges.
 //
 // What is computed ([XPU] "From slots to a page table"; [BACKEND]
 // init_forward_metadata with its per-request split count): one new query per
 // request attends over its L keys; key t of request i lives at the slot the
-// request's table resolves t to.  The keys are cut into chunks of `chunk`
-// *logical* positions; each chunk (split) produces a normalised partial
-// output and its log-sum-exp, and the merge combines them exactly.  Split
-// boundaries depend only on logical positions, never on where pages live, so
-// moving pages around cannot change a single bit of the output.
+// request's table resolves t to.  The keys are cut into pieces at *logical*
+// positions; each piece produces a normalised partial output and its
+// log-sum-exp, and the merge combines them exactly.  Piece boundaries depend
+// only on logical positions (the request lengths), never on where pages
+// live, so moving pages around cannot change a single bit of the output.
 //
-// Work distribution on gfx950: a one-block planner kernel lists the live
-// (request, split) items in request order; block b of the split kernel takes
-// item b / hg and KV-head group b % hg.  The hardware hands consecutive
-// blocks to the 8 XCDs round robin, so every XCD gets an equal share of live
-// items (empty splits of short requests never occupy a slot), and the head
-// groups of one item run side by side, reading whole token rows.
-//
-// Split kernel, bf16 (pool [slots][Hkv][D], token-major):
-//   block   = WAVES wavefronts of one item; wave w owns KV head
-//             g = (b % hg) * WAVES + w and its G = Hq / Hkv query heads.
+// bf16 pools (pool [slots][Hkv][D], token-major): stream split.  The stream
+// planner (pkv_stream.hip) lays all requests' 32-key tiles end to end and
+// cuts the sequence into equal runs; each run is streamed by hg workgroups
+// (one per group of WAVES KV heads) on one XCD.  Wave w owns KV head g and
+// its G = Hq / Hkv query heads:
 //   S^T[16 tokens x 16 heads] = K_tile[16 x D] * Q^T[D x 16] on
 //   v_mfma_f32_16x16x32_bf16 (tokens as M, so K rows load from HBM straight
 //   into A-operand registers); softmax on the MFMA output registers; P
 //   (16 heads x 32 tokens) is already the A operand of the PV product; V
 //   goes through LDS and comes back transposed with ds_read_b64_tr_b16, four
 //   tokens of one d column per lane per read.
-// Split kernel, f32: VALU dot products, 16 lanes per token.
+// f32 pools: per-request splits of `chunk` logical positions listed by a
+// one-block planner (live (request, split) items in request order; block b
+// takes item b / hg and KV-head group b % hg), VALU dot products with 16
+// lanes per token.
 #include <math.h>
+
+#include <algorithm>
 
 #include "pkv_launch.h"
 
 namespace pkv {
 
-constexpr int kTile = 32;          // tokens per inner iteration of the MFMA kernel
-
+constexpr int kTile = 32;  // tokens per tile of the bf16 kernel
 
 // ---------------------------------------------------------------------------
-// split plan: live items in request order; an empty request still gets one
-// item, which writes its zero output and -inf lse.  Each item carries what a
-// split needs to start streaming at once (its request's table view and key
-// range), so the split kernel's first dependent loads are the table entries.
+// split plan of the f32 path: live items in request order; an empty request
+// still gets one item, which writes its zero output and -inf lse.  Each item
+// carries what a split needs to start streaming at once (its request's table
+// view and key range), so the split kernel's first dependent loads are the
+// table entries.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(1024) decode_plan_kernel(DevMap m, int32_t bs, int32_t chunk, int32_t max_splits,
                                                            WorkItem* __restrict__ items, int32_t* __restrict__ count) {
@@ -96,13 +96,10 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DevMap m, int32_t bs,
 }
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA split kernel
-//
-// Per wavefront and 32-token tile: one coalesced load of the tile's 32 slots
-// (lane l -> token t0 + l%32), handed to the lanes that need them by
-// ds_bpermute; K rows go straight into MFMA A-operand registers, V rows into
-// registers.  The slots of tile i+2 and the K/V rows of tile i+1 are in
-// flight while tile i is computed (two register sets, unrolled by hand).
+// bf16 tile helpers.  Per wavefront and 32-token tile: the tile's 32 slot
+// ids sit in lanes 0..31 of one register and reach the lanes that need them
+// by ds_bpermute; K rows go straight into MFMA A-operand registers, V rows
+// into registers (decode_issue); decode_compute does the tile's math.
 // ---------------------------------------------------------------------------
 template <int D>
 struct DecodeTile {
@@ -205,130 +202,183 @@ __device__ __forceinline__ void decode_compute(const DecodeTile<D>& T, int t0, i
   __builtin_amdgcn_wave_barrier();
 }
 
-template <int D, int WAVES, int FMT>
-__global__ void __launch_bounds__(64 * WAVES, 8 / WAVES) decode_mfma_kernel(
-    DevMap m, const bf16* k_pool, const bf16* v_pool, const bf16* __restrict__ q,
-    int32_t Hq, int32_t Hkv, int32_t G, int32_t hg, int32_t chunk, int32_t max_splits,
-    const WorkItem* __restrict__ items, const int32_t* __restrict__ item_count, float scale_log2,
+// ---------------------------------------------------------------------------
+// bf16 MFMA stream-split kernel.  The hg workgroups of a run are 8 blocks
+// apart (block b: run (b / 8hg) * 8 + b % 8, KV-head group (b / 8) % hg);
+// wave w owns KV head group * WAVES + w.  A wave streams its run
+// tile after tile across request boundaries with NS register tile sets (NS - 1
+// tiles in flight during a tile's math), so no split restarts its pipeline and
+// every CU streams the same number of bytes.  Per tile the wave loads the
+// planner's 40 words (slot ids in lanes 0..31, info in lanes 32..36), the K
+// and V rows and the queries of the tile's request (the queries ride along
+// with every tile so that no load is conditional).  A request finished inside
+// the run is written directly; one cut by a run boundary leaves a piece
+// (id run + request) for the merge.
+// ---------------------------------------------------------------------------
+template <int D>
+struct StreamSet {
+  DecodeTile<D> t;
+  bf16x8 q[D / 32];
+  int32_t mv;  // planner word of lane l
+};
+
+template <int D, int WAVES, int NS>
+__global__ void __launch_bounds__(64 * WAVES, NS <= 2 ? 8 / WAVES : 4 / WAVES) decode_stream_kernel(
+    const bf16* k_pool, const bf16* v_pool, const bf16* __restrict__ q, int32_t Hq, int32_t Hkv, int32_t G,
+    int32_t hg, const int32_t* __restrict__ header, const int32_t* __restrict__ meta, float scale_log2,
     bf16* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws_o, float* __restrict__ ws_lse) {
   constexpr int NK = D / 32;
   constexpr int NT = D / 16;
-  constexpr int LDS = D + 8;  // LDS row stride in elements (+16 B pad)
+  constexpr int LDS = D + 8;
   __shared__ __attribute__((aligned(16))) bf16 vsm[WAVES][kTile * LDS];
 
-  const int w_item = blockIdx.x / hg;
-  if (w_item >= *item_count) return;
-  const WorkItem item = items[w_item];
-  const int i = item.i;
-  const int s = item.s;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int g = (blockIdx.x % hg) * WAVES + wave;
-  const int col = lane & 15;  // head column of S / d column of PV
-  const int grp = lane >> 4;  // lane group 0..3
-  const int ns = item.ns;
+  // the hg workgroups of a run sit on one XCD (dispatch goes round robin
+  // over the 8 XCDs), so the halves of a slot's row meet in one L2
+  const int run = (blockIdx.x / (8 * hg)) * 8 + blockIdx.x % 8;
+  const int Bt = header[0], total = header[1];
+  const int G0 = run * Bt;
+  if (G0 >= total) return;
+  const int n = min(Bt, total - G0);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int g = ((blockIdx.x / 8) % hg) * WAVES + wave;
+  const int64_t row_elems = (int64_t)Hkv * D;
+  const bf16* kb = k_pool + (int64_t)g * D;
+  const bf16* vb = v_pool + (int64_t)g * D;
+  bf16* vt = vsm[wave];
+  const bool qok = col < G;
 
-  if (ns == 0) {  // empty key set: zero output, lse = -inf ([XPU] "Approach 2" guard)
-    for (int n = 0; n < G; ++n) {
-      const int64_t h = (int64_t)i * Hq + g * G + n;
-      for (int d = lane; d < D; d += 64) out[h * D + d] = (bf16)0.0f;
-      if (lse && lane == 0) lse[h] = -INFINITY;
-    }
-    return;
-  }
-  const int t_begin = s * chunk;
-  const int t_end = item.t_end;
-  const SlotMap<FMT> sm = slotmap_from_view<FMT>(m, item_view(item));
-
-  // Q^T operand: lane (n = col, j = grp) holds q[head n][kk*32 + j*8 .. +8]
-  bf16x8 qb[NK];
-  {
-    const bool ok = col < G;
-    const bf16* qp = q + ((int64_t)i * Hq + g * G + (ok ? col : 0)) * D + grp * 8;
+  auto meta_word = [&](int r) -> int32_t {
+    return meta[(int64_t)(G0 + min(r, n - 1)) * kStreamMetaWords + min(lane, kStreamMetaWords - 1)];
+  };
+  auto issue = [&](StreamSet<D>& S, int32_t mv) {
+    S.mv = mv;
+    decode_issue<D>(S.t, mv, lane, kb, vb, row_elems);
+    const int i = __builtin_amdgcn_readlane(mv, 32);
+    const bf16* qp = q + ((int64_t)i * Hq + g * G + (qok ? col : 0)) * D + grp * 8;
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
       u32x4 w = *reinterpret_cast<const u32x4*>(qp + kk * 32);
-      if (!ok) w = u32x4{0u, 0u, 0u, 0u};
-      qb[kk] = as_bf16x8(w);
+      if (!qok) w = u32x4{0u, 0u, 0u, 0u};
+      S.q[kk] = as_bf16x8(w);
     }
-  }
+  };
 
   f32x4 acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  const int64_t row_elems = (int64_t)Hkv * D;
-  const bf16* kb = k_pool + (int64_t)g * D;
-  const bf16* vb = v_pool + (int64_t)g * D;
-  bf16* vt = vsm[wave];
-  // Lane l looks up token t0 + l%32 of a tile (past the end -> padding slot).
-  // Order of memory instructions per iteration: the table load for tile
-  // i+2, then the K/V rows of tile i+1 (which need tile i+1's table load),
-  // then tile i is computed.  Loads retire in issue order, so each wait only
-  // covers loads issued before the ones meant to stay in flight.  The
-  // prefetch is unconditional (past the end it reads the padding row, which
-  // stays in cache): a conditional one would make the compiler wait for it.
-  const int tl = lane & 31;
-  auto slot_of = [&](int32_t raw, int t0) {
-    const int t = t0 + tl;
-    return sm.finish(raw, t, t < t_end);
+  auto finish = [&](int i, int P, int T) {
+    const int b0 = P / Bt, b1 = (P + T - 1) / Bt;
+    const bool direct = b0 == b1;
+    float l_tot = l_run + shfl_xor(l_run, 16);
+    l_tot += shfl_xor(l_tot, 32);
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int hr = grp * 4 + rr;
+      const float lt = shfl(l_tot, hr);
+      const float mr = shfl(m_run, hr);
+      if (hr < G) {
+        const int h = g * G + hr;
+        const float inv = 1.0f / lt;
+        const float lse_nat = (mr + __log2f(lt)) * kLn2;
+        if (direct) {
+          const int64_t o = (int64_t)i * Hq + h;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) out[o * D + nt * 16 + col] = (bf16)(acc[nt][rr] * inv);
+          if (lse && col == 0) lse[o] = lse_nat;
+        } else {
+          const int64_t o = ((int64_t)run + i) * Hq + h;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) ws_o[o * D + nt * 16 + col] = acc[nt][rr] * inv;
+          if (col == 0) ws_lse[o] = lse_nat;
+        }
+      }
+    }
   };
 
-  DecodeTile<D> A, B;
-  int32_t raw_next = sm.raw(t_begin + kTile + tl);
-  decode_issue<D>(A, slot_of(sm.raw(t_begin + tl), t_begin), lane, kb, vb, row_elems);
-  for (int t0 = t_begin;;) {
-    {
-      const int32_t raw_new = sm.raw(t0 + 2 * kTile + tl);
-      __builtin_amdgcn_sched_barrier(0);  // table load first: later waits on it must not cover K/V
-      decode_issue<D>(B, slot_of(raw_next, t0 + kTile), lane, kb, vb, row_elems);
-      raw_next = raw_new;
-    }
-    // keep the prefetch ahead of the compute: the empty asm pins the loads
-    // in the IR, the scheduling barrier in the machine schedule
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    decode_compute<D>(A, t0, t_end, lane, qb, scale_log2, vt, acc, m_run, l_run);
-    t0 += kTile;
-    if (t0 >= t_end) break;
-    {
-      const int32_t raw_new = sm.raw(t0 + 2 * kTile + tl);
-      __builtin_amdgcn_sched_barrier(0);
-      decode_issue<D>(A, slot_of(raw_next, t0 + kTile), lane, kb, vb, row_elems);
-      raw_next = raw_new;
-    }
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    decode_compute<D>(B, t0, t_end, lane, qb, scale_log2, vt, acc, m_run, l_run);
-    t0 += kTile;
-    if (t0 >= t_end) break;
-  }
-
-  // ---- finalise: per-head sums over the four lane groups
-  float l_tot = l_run + shfl_xor(l_run, 16);
-  l_tot += shfl_xor(l_tot, 32);
+  StreamSet<D> S[NS];
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    const int hr = grp * 4 + rr;
-    const float lt = shfl(l_tot, hr);
-    const float mr = shfl(m_run, hr);
-    if (hr < G) {
-      const int64_t h = (int64_t)i * Hq + g * G + hr;
-      const float inv = 1.0f / lt;
-      const float lse_nat = (mr + __log2f(lt)) * kLn2;
-      if (ns == 1) {
+  for (int k = 0; k < NS - 1; ++k) issue(S[k], meta_word(k));
+  int32_t mv_next = meta_word(NS - 1);
+  bool done = false;
+  for (int r = 0; !done;) {
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) out[h * D + nt * 16 + col] = (bf16)(acc[nt][rr] * inv);
-        if (lse && col == 0) lse[h] = lse_nat;
-      } else {
-        float* po = ws_o + (h * max_splits + s) * D;
+    for (int j = 0; j < NS; ++j) {
+      if (!done) {
+        const int32_t mv_new = meta_word(r + NS);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(S[(j + NS - 1) % NS], mv_next);
+        mv_next = mv_new;
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        const int32_t mv = S[j].mv;
+        const int i = __builtin_amdgcn_readlane(mv, 32);
+        const int jt = __builtin_amdgcn_readlane(mv, 33);
+        const int T = __builtin_amdgcn_readlane(mv, 34);
+        const int P = __builtin_amdgcn_readlane(mv, 35);
+        const int valid = __builtin_amdgcn_readlane(mv, 36);
+        if (r == 0 || jt == 0) {
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) po[nt * 16 + col] = acc[nt][rr] * inv;
-        if (col == 0) ws_lse[h * max_splits + s] = lse_nat;
+          for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          m_run = -INFINITY;
+          l_run = 0.f;
+        }
+        decode_compute<D>(S[j].t, 0, valid, lane, S[j].q, scale_log2, vt, acc, m_run, l_run);
+        if (r == n - 1 || jt == T - 1) finish(i, P, T);
+        ++r;
+        if (r >= n) done = true;
       }
     }
   }
+}
+
+// Merge of the stream pieces: one wavefront per (request, head).  Requests
+// finished inside one run were written directly; empty requests get zeros
+// and lse = -inf; the rest combine their pieces (ids run + request).
+template <int D>
+__global__ void __launch_bounds__(256) decode_stream_merge_kernel(int32_t bs, int32_t Hq,
+                                                                  const int32_t* __restrict__ header,
+                                                                  const int32_t* __restrict__ prefix,
+                                                                  const int32_t* __restrict__ ntiles,
+                                                                  const float* __restrict__ ws_o,
+                                                                  const float* __restrict__ ws_lse,
+                                                                  bf16* __restrict__ out, float* __restrict__ lse) {
+  constexpr int E = D / 64;  // elements per lane
+  const int lane = threadIdx.x & 63;
+  const int64_t idx = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (idx >= (int64_t)bs * Hq) return;
+  const int i = (int)(idx / Hq), h = (int)(idx % Hq);
+  bf16* op = out + idx * D + lane * E;
+  const int T = ntiles[i];
+  if (T == 0) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) op[e] = (bf16)0.0f;
+    if (lse && lane == 0) lse[idx] = -INFINITY;
+    return;
+  }
+  const int Bt = header[0];
+  const int P = prefix[i];
+  const int b0 = P / Bt, b1 = (P + T - 1) / Bt;
+  if (b0 == b1) return;
+  float mx = -INFINITY;
+  for (int b = b0; b <= b1; ++b) mx = fmaxf(mx, ws_lse[((int64_t)b + i) * Hq + h]);
+  float o[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) o[e] = 0.f;
+  float sum = 0.f;
+  for (int b = b0; b <= b1; ++b) {
+    const int64_t row = ((int64_t)b + i) * Hq + h;
+    const float wgt = __expf(ws_lse[row] - mx);
+    sum += wgt;
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] = fmaf(wgt, ws_o[row * D + lane * E + e], o[e]);
+  }
+  const float inv = 1.0f / sum;
+#pragma unroll
+  for (int e = 0; e < E; ++e) op[e] = (bf16)(o[e] * inv);
+  if (lse && lane == 0) lse[idx] = mx + __logf(sum);
 }
 
 // ---------------------------------------------------------------------------
@@ -514,15 +564,15 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(const int32_t* __rest
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-enum DecodeKind : int32_t { DK_NONE = 0, DK_MFMA = 1, DK_VALU = 2, DK_MLA = 3 };
-
+enum DecodeKind : int32_t { DK_NONE = 0, DK_STREAM = 1, DK_VALU = 2, DK_MLA = 3 };
+constexpr int kStreamSets = 3;  // register tile sets of the stream kernel
 
 static int decode_kind(const PoolInfo& p, int32_t Hq) {
   if (p.kind == 1) return mla_decode_supported(p, Hq) ? DK_MLA : DK_NONE;
   if (p.head_dim_qk != p.head_dim_v || (p.head_dim_qk != 64 && p.head_dim_qk != 128)) return DK_NONE;
   if (Hq <= 0 || Hq % p.num_kv_heads != 0) return DK_NONE;
   const int G = Hq / p.num_kv_heads;
-  if (p.dtype == 1 && G <= 16) return DK_MFMA;
+  if (p.dtype == 1 && G <= 16) return DK_STREAM;
   if (p.dtype == 0 && G <= 8) return DK_VALU;
   return DK_NONE;
 }
@@ -533,6 +583,15 @@ DecodePlan plan_decode(const PoolInfo& p, int32_t bs, int32_t Hq, int32_t max_kv
   DecodePlan plan;
   plan.kind = decode_kind(p, Hq);
   if (plan.kind == DK_MLA) return plan_mla_decode(p, bs, Hq, max_kv_len);
+  if (plan.kind == DK_STREAM) {
+    // runs: workgroups that fit on the device at once, over the KV-head groups
+    const int Hkv = p.num_kv_heads;
+    const int W = (Hkv % 4 == 0) ? 4 : (Hkv % 2 == 0 ? 2 : 1);
+    const int per_cu = (kStreamSets <= 2 ? 8 : 4) / W;
+    plan.chunk = max_kv_len > 0 ? (max_kv_len + kStreamT - 1) / kStreamT : 0;  // tiles per request, at most
+    plan.max_splits = std::max(8, device_cu_count() * per_cu / (Hkv / W) / 8 * 8);  // a multiple of 8
+    return plan;
+  }
   // Chunk of logical tokens per split: the largest power of two in
   // [64, 1024] that still leaves ~16 wavefronts per CU on average (the mean
   // length is taken as max_kv_len / 2), so long requests spread over the 256
@@ -581,28 +640,9 @@ size_t decode_ws_layout(const PoolInfo& p, const DecodePlan& plan, int32_t bs, i
 }
 
 size_t decode_workspace_bytes(const PoolInfo& p, const DecodePlan& plan, int32_t bs, int32_t Hq) {
-  if (plan.kind == DK_MLA) return mla_ws_layout(plan, bs, Hq, nullptr, nullptr);
+  if (plan.kind == DK_MLA || plan.kind == DK_STREAM)
+    return stream_ws_layout(bs, plan.chunk, plan.max_splits, Hq, p.head_dim_v, nullptr, nullptr);
   return decode_ws_layout(p, plan, bs, Hq, nullptr, nullptr);
-}
-
-template <int D, int W, int FMT>
-static void launch_mfma(unsigned blocks, hipStream_t s, const DevMap& m, const PoolInfo& p, int32_t layer,
-                        const void* q, int32_t Hq, int32_t G, int32_t hg, const DecodePlan& plan, const DecodeWs& w,
-                        float sl2, void* out, float* lse) {
-  hipLaunchKernelGGL((decode_mfma_kernel<D, W, FMT>), dim3(blocks), dim3(64 * W), 0, s, m,
-                     reinterpret_cast<const bf16*>(p.k_layer(layer)), reinterpret_cast<const bf16*>(p.v_layer(layer)),
-                     static_cast<const bf16*>(q), Hq, p.num_kv_heads, G, hg, plan.chunk, plan.max_splits, w.items,
-                     w.count, sl2, static_cast<bf16*>(out), lse, w.o, w.lse);
-}
-
-template <int D, int W>
-static void launch_mfma_fmt(unsigned blocks, hipStream_t s, const DevMap& m, const PoolInfo& p, int32_t layer,
-                            const void* q, int32_t Hq, int32_t G, int32_t hg, const DecodePlan& plan,
-                            const DecodeWs& w, float sl2, void* out, float* lse) {
-  if (m.fmt == MAP_TOKEN_TABLE)
-    launch_mfma<D, W, SLOT_TABLE>(blocks, s, m, p, layer, q, Hq, G, hg, plan, w, sl2, out, lse);
-  else
-    launch_mfma<D, W, SLOT_PAGES>(blocks, s, m, p, layer, q, Hq, G, hg, plan, w, sl2, out, lse);
 }
 
 template <int D, int W>
@@ -617,10 +657,58 @@ static void launch_valu(unsigned blocks, hipStream_t s, const DevMap& m, const P
                      static_cast<float*>(out), lse, w.o, w.lse);
 }
 
+template <int D, int W>
+static void launch_stream_main(int32_t runs, int32_t hg, hipStream_t s, const PoolInfo& p, int32_t layer,
+                               const void* q, int32_t Hq, int32_t G, const StreamWs& w, float sl2, void* out,
+                               float* lse) {
+  hipLaunchKernelGGL((decode_stream_kernel<D, W, kStreamSets>), dim3((unsigned)(runs * hg)), dim3(64 * W), 0, s,
+                     reinterpret_cast<const bf16*>(p.k_layer(layer)), reinterpret_cast<const bf16*>(p.v_layer(layer)),
+                     static_cast<const bf16*>(q), Hq, p.num_kv_heads, G, hg, w.header, w.meta, sl2,
+                     static_cast<bf16*>(out), lse, w.o, w.lse);
+}
+
+static hipError_t launch_stream_decode(const PoolInfo& p, int32_t layer, const void* q, int32_t Hq, const DevMap& m,
+                                       int32_t bs, const DecodePlan& plan, float sl2, void* out, float* lse, void* ws,
+                                       hipStream_t s) {
+  const int Hkv = p.num_kv_heads;
+  const int G = Hq / Hkv;
+  const int W = (Hkv % 4 == 0) ? 4 : (Hkv % 2 == 0 ? 2 : 1);
+  const int hg = Hkv / W;
+  const int32_t runs = plan.max_splits;
+  if (runs % 8 != 0) return hipErrorInvalidValue;  // the block -> (run, head group) map needs whole XCD rounds
+  StreamWs w;
+  stream_ws_layout(bs, plan.chunk, runs, Hq, p.head_dim_v, ws, &w);
+  hipError_t e = launch_stream_plan(m, bs, plan.chunk, runs, w, s);
+  if (e != hipSuccess) return e;
+  const int D = p.head_dim_qk;
+  timer_before(s);
+  if (D == 128) {
+    if (W == 4) launch_stream_main<128, 4>(runs, hg, s, p, layer, q, Hq, G, w, sl2, out, lse);
+    else if (W == 2) launch_stream_main<128, 2>(runs, hg, s, p, layer, q, Hq, G, w, sl2, out, lse);
+    else launch_stream_main<128, 1>(runs, hg, s, p, layer, q, Hq, G, w, sl2, out, lse);
+  } else {
+    if (W == 4) launch_stream_main<64, 4>(runs, hg, s, p, layer, q, Hq, G, w, sl2, out, lse);
+    else if (W == 2) launch_stream_main<64, 2>(runs, hg, s, p, layer, q, Hq, G, w, sl2, out, lse);
+    else launch_stream_main<64, 1>(runs, hg, s, p, layer, q, Hq, G, w, sl2, out, lse);
+  }
+  e = hipGetLastError();
+  timer_after(s);
+  if (e != hipSuccess) return e;
+  const unsigned mblocks = (unsigned)(((int64_t)bs * Hq + 3) / 4);
+  if (D == 128)
+    hipLaunchKernelGGL(decode_stream_merge_kernel<128>, dim3(mblocks), dim3(256), 0, s, bs, Hq, w.header, w.prefix,
+                       w.ntiles, w.o, w.lse, static_cast<bf16*>(out), lse);
+  else
+    hipLaunchKernelGGL(decode_stream_merge_kernel<64>, dim3(mblocks), dim3(256), 0, s, bs, Hq, w.header, w.prefix,
+                       w.ntiles, w.o, w.lse, static_cast<bf16*>(out), lse);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(const PoolInfo& p, int32_t layer, const void* q, int32_t Hq, const DevMap& m, int32_t bs,
                          const DecodePlan& plan, float sm_scale, void* out, float* lse, void* ws, hipStream_t s) {
   if (bs == 0) return hipSuccess;
   if (plan.kind == DK_MLA) return launch_mla_decode(p, layer, q, Hq, m, bs, plan, sm_scale * kLog2e, out, lse, ws, s);
+  if (plan.kind == DK_STREAM) return launch_stream_decode(p, layer, q, Hq, m, bs, plan, sm_scale * kLog2e, out, lse, ws, s);
   const int Hkv = p.num_kv_heads;
   const int G = Hq / Hkv;
   const int W = (Hkv % 4 == 0) ? 4 : (Hkv % 2 == 0 ? 2 : 1);
@@ -635,26 +723,14 @@ hipError_t launch_decode(const PoolInfo& p, int32_t layer, const void* q, int32_
   const float sl2 = sm_scale * kLog2e;
   const int D = p.head_dim_qk;
   timer_before(s);
-  if (plan.kind == DK_MFMA) {
-    if (D == 128) {
-      if (W == 4) launch_mfma_fmt<128, 4>(blocks, s, m, p, layer, q, Hq, G, hg, plan, w, sl2, out, lse);
-      else if (W == 2) launch_mfma_fmt<128, 2>(blocks, s, m, p, layer, q, Hq, G, hg, plan, w, sl2, out, lse);
-      else launch_mfma_fmt<128, 1>(blocks, s, m, p, layer, q, Hq, G, hg, plan, w, sl2, out, lse);
-    } else {
-      if (W == 4) launch_mfma_fmt<64, 4>(blocks, s, m, p, layer, q, Hq, G, hg, plan, w, sl2, out, lse);
-      else if (W == 2) launch_mfma_fmt<64, 2>(blocks, s, m, p, layer, q, Hq, G, hg, plan, w, sl2, out, lse);
-      else launch_mfma_fmt<64, 1>(blocks, s, m, p, layer, q, Hq, G, hg, plan, w, sl2, out, lse);
-    }
+  if (D == 128) {
+    if (W == 4) launch_valu<128, 4>(blocks, s, m, p, layer, q, Hq, G, hg, plan, w, sl2, out, lse);
+    else if (W == 2) launch_valu<128, 2>(blocks, s, m, p, layer, q, Hq, G, hg, plan, w, sl2, out, lse);
+    else launch_valu<128, 1>(blocks, s, m, p, layer, q, Hq, G, hg, plan, w, sl2, out, lse);
   } else {
-    if (D == 128) {
-      if (W == 4) launch_valu<128, 4>(blocks, s, m, p, layer, q, Hq, G, hg, plan, w, sl2, out, lse);
-      else if (W == 2) launch_valu<128, 2>(blocks, s, m, p, layer, q, Hq, G, hg, plan, w, sl2, out, lse);
-      else launch_valu<128, 1>(blocks, s, m, p, layer, q, Hq, G, hg, plan, w, sl2, out, lse);
-    } else {
-      if (W == 4) launch_valu<64, 4>(blocks, s, m, p, layer, q, Hq, G, hg, plan, w, sl2, out, lse);
-      else if (W == 2) launch_valu<64, 2>(blocks, s, m, p, layer, q, Hq, G, hg, plan, w, sl2, out, lse);
-      else launch_valu<64, 1>(blocks, s, m, p, layer, q, Hq, G, hg, plan, w, sl2, out, lse);
-    }
+    if (W == 4) launch_valu<64, 4>(blocks, s, m, p, layer, q, Hq, G, hg, plan, w, sl2, out, lse);
+    else if (W == 2) launch_valu<64, 2>(blocks, s, m, p, layer, q, Hq, G, hg, plan, w, sl2, out, lse);
+    else launch_valu<64, 1>(blocks, s, m, p, layer, q, Hq, G, hg, plan, w, sl2, out, lse);
   }
   e = hipGetLastError();
   timer_after(s);

@@ -89,17 +89,26 @@ bool mla_decode_supported(const PoolInfo& p, int32_t num_q_heads);
 // MLA plan: chunk = tiles (32 tokens) per request at most, max_splits = main
 // grid (one workgroup per CU)
 DecodePlan plan_mla_decode(const PoolInfo& p, int32_t bs, int32_t num_q_heads, int32_t max_kv_len);
-// MLA workspace: [header | tile prefix | tiles | fallback flags | per-tile slot ids + info | pieces o | pieces lse]
-struct MlaWs {
-  int32_t* header;  // run length (tiles per workgroup), total tiles
-  int32_t* prefix;
-  int32_t* ntiles;
-  int32_t* fallback;  // requests to recompute exactly (set by the main kernel)
+// Stream-split decode (pkv_stream.hip): tiles of kStreamT logical positions
+// laid end to end and cut into equal runs; per tile the planner writes
+// kStreamMetaWords words: 32 slot ids + {request, tile, tiles of request,
+// tile prefix, valid keys, 0, 0, 0}.
+constexpr int kStreamT = 32;
+constexpr int kStreamMetaWords = 40;
+struct StreamWs {
+  int32_t* header;    // run length (tiles per run), total tiles
+  int32_t* prefix;    // per request: first tile
+  int32_t* ntiles;    // per request: tiles
+  int32_t* fallback;  // requests to recompute exactly (set by a main kernel)
   int32_t* meta;
-  float* o;
+  float* o;           // pieces: [(runs + bs)][Hq][Dv], id run + request
   float* lse;
 };
-size_t mla_ws_layout(const DecodePlan& plan, int32_t bs, int32_t num_q_heads, void* base, MlaWs* w);
+size_t stream_ws_layout(int32_t bs, int32_t max_tiles, int32_t runs, int32_t Hq, int32_t Dv, void* base,
+                        StreamWs* w);
+hipError_t launch_stream_plan(const DevMap& m, int32_t bs, int32_t max_tiles, int32_t runs, const StreamWs& w,
+                              hipStream_t s);
+int32_t device_cu_count();
 hipError_t launch_mla_decode(const PoolInfo& p, int32_t layer, const void* q, int32_t num_q_heads, const DevMap& m,
                              int32_t bs, const DecodePlan& plan, float scale_log2, void* out, float* lse, void* ws,
                              hipStream_t s);

@@ -44,11 +44,11 @@ namespace pkv {
 
 constexpr int kMlaQK = 576;
 constexpr int kMlaV = 512;
-constexpr int kMlaT = 32;                         // tokens per tile
+constexpr int kMlaT = kStreamT;                   // tokens per tile
 constexpr int kMlaRowChunks = kMlaQK / 8;         // 72 sixteen-byte chunks per row
 constexpr int kMlaRowBytes = kMlaQK * 2;          // 1152
 constexpr int kMlaTileBytes = kMlaT * kMlaRowBytes;  // 36864
-constexpr int kMlaMetaWords = 40;                 // per tile: 32 slot ids + 8 info words
+constexpr int kMlaMetaWords = kStreamMetaWords;   // per tile: 32 slot ids + 8 info words
 constexpr int kMlaBufs = 4;                       // LDS tile buffers: three tiles in flight during compute
 constexpr int kMlaMetaRing = 8;                   // per-wave ring of per-tile slot ids / info
 constexpr float kMlaHeadroom = 64.0f;             // log2 units a score may exceed the reference by
@@ -92,70 +92,6 @@ __device__ __forceinline__ bf16x8 mla_v_operand(const char* tile, int c0, int la
   const i16x4 b = lds_read_tr16(reinterpret_cast<const bf16*>(lo + 16 * kMlaRowBytes));
   const bf16x4 ba = __builtin_bit_cast(bf16x4, a), bb = __builtin_bit_cast(bf16x4, b);
   return bf16x8{ba[0], ba[1], ba[2], ba[3], bb[0], bb[1], bb[2], bb[3]};
-}
-
-// ---------------------------------------------------------------------------
-// Planner: one workgroup per request.  Writes the tile prefix, the run
-// length Bt of the main grid, and per tile its 32 slot ids (tokens past the
-// request's end repeat its last key, whose weight is then exactly 0) and
-// info words {request, tile, tiles of request, tile prefix, valid keys}.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ int32_t mla_tiles(int32_t L) { return L > 0 ? (L + kMlaT - 1) / kMlaT : 0; }
-
-template <int FMT>
-__global__ void __launch_bounds__(256) mla_plan_kernel(DevMap m, int32_t bs, int32_t max_tiles, int32_t runs,
-                                                       int32_t* __restrict__ header,
-                                                       int32_t* __restrict__ prefix, int32_t* __restrict__ ntiles,
-                                                       int32_t* __restrict__ fallback, int32_t* __restrict__ meta) {
-  __shared__ int32_t red[2][4];
-  const int i = blockIdx.x;
-  const int tid = threadIdx.x;
-  int32_t tot = 0, pre = 0;
-  for (int k = tid; k < bs; k += 256) {
-    const int32_t T = min(mla_tiles(m.kv_lens[k]), max_tiles);
-    tot += T;
-    if (k < i) pre += T;
-  }
-  for (int o = 32; o > 0; o >>= 1) {
-    tot += __shfl_xor(tot, o, 64);
-    pre += __shfl_xor(pre, o, 64);
-  }
-  if ((tid & 63) == 0) {
-    red[0][tid >> 6] = tot;
-    red[1][tid >> 6] = pre;
-  }
-  __syncthreads();
-  tot = red[0][0] + red[0][1] + red[0][2] + red[0][3];
-  pre = red[1][0] + red[1][1] + red[1][2] + red[1][3];
-  // keys past max_kv_len (a caller error) are not read: the workspace holds
-  // max_tiles tiles per request
-  const int32_t T = min(mla_tiles(m.kv_lens[i]), max_tiles);
-  const int32_t L = min(max(m.kv_lens[i], 0), T * kMlaT);
-  if (tid == 0) {
-    prefix[i] = pre;
-    ntiles[i] = T;
-    fallback[i] = 0;
-    if (i == 0) {
-      header[0] = max(1, (tot + runs - 1) / runs);
-      header[1] = tot;
-    }
-  }
-  if (T == 0) return;
-  const SlotMap<FMT> sm = make_slotmap<FMT>(m, i);
-  for (int e = tid; e < T * kMlaT; e += 256) {
-    const int32_t t = min(e, L - 1);
-    meta[(int64_t)(pre + (e >> 5)) * kMlaMetaWords + (e & 31)] = sm(t, true);
-  }
-  for (int e = tid; e < T * 8; e += 256) {
-    const int32_t j = e >> 3, f = e & 7;
-    int32_t v = 0;
-    if (f == 0) v = i;
-    else if (f == 1) v = j;
-    else if (f == 2) v = T;
-    else if (f == 3) v = pre;
-    else if (f == 4) v = min(kMlaT, L - j * kMlaT);
-    meta[(int64_t)(pre + j) * kMlaMetaWords + 32 + f] = v;
-  }
 }
 
 // O += P V for one tile over a wave's NCB column blocks and NHB head
@@ -527,19 +463,6 @@ bool mla_decode_supported(const PoolInfo& p, int32_t Hq) {
          (Hq == 16 || Hq == 32 || Hq == 64 || Hq == 128);
 }
 
-// One workgroup per CU of the current device.
-static int32_t mla_grid() {
-  static int32_t cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
-
 DecodePlan plan_mla_decode(const PoolInfo& p, int32_t bs, int32_t Hq, int32_t max_kv_len) {
   (void)p;
   (void)bs;
@@ -548,43 +471,12 @@ DecodePlan plan_mla_decode(const PoolInfo& p, int32_t bs, int32_t Hq, int32_t ma
   plan.chunk = max_kv_len > 0 ? (max_kv_len + kMlaT - 1) / kMlaT : 0;  // tiles per request, at most
   // runs of tiles: one workgroup per CU, two sibling workgroups per run
   // above 64 heads (an even split of the CUs)
-  plan.max_splits = Hq > 64 ? std::max(8, mla_grid() / 2 / 8 * 8) : mla_grid();
+  plan.max_splits = Hq > 64 ? std::max(8, device_cu_count() / 2 / 8 * 8) : device_cu_count();
   return plan;
 }
 
-static size_t al256(size_t x) { return (x + 255) / 256 * 256; }
-
-// [header | tile prefix[bs] | tiles[bs] | fallback flags[bs] | meta[bs * max tiles][40] | pieces o | pieces lse]
-size_t mla_ws_layout(const DecodePlan& plan, int32_t bs, int32_t Hq, void* base, MlaWs* w) {
-  char* b = static_cast<char*>(base);
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    char* at = b ? b + off : nullptr;
-    off += al256(bytes);
-    return at;
-  };
-  char* hdr = take(256);
-  char* pre = take((size_t)bs * 4);
-  char* nt = take((size_t)bs * 4);
-  char* fb = take((size_t)bs * 4);
-  char* meta = take((size_t)bs * plan.chunk * kMlaMetaWords * 4);
-  const size_t pieces = (size_t)plan.max_splits + bs;
-  char* o = take(pieces * Hq * kMlaV * 4);
-  char* l = take(pieces * Hq * 4);
-  if (w) {
-    w->header = reinterpret_cast<int32_t*>(hdr);
-    w->prefix = reinterpret_cast<int32_t*>(pre);
-    w->ntiles = reinterpret_cast<int32_t*>(nt);
-    w->fallback = reinterpret_cast<int32_t*>(fb);
-    w->meta = reinterpret_cast<int32_t*>(meta);
-    w->o = reinterpret_cast<float*>(o);
-    w->lse = reinterpret_cast<float*>(l);
-  }
-  return off;
-}
-
 template <int HPB>
-static void launch_mla_main(int32_t runs, int32_t Hq, hipStream_t s, const char* kp, const void* q, const MlaWs& w,
+static void launch_mla_main(int32_t runs, int32_t Hq, hipStream_t s, const char* kp, const void* q, const StreamWs& w,
                             float sl2, void* out, float* lse) {
   const int sibs = Hq / HPB;
   hipLaunchKernelGGL((mla_decode_kernel<HPB>), dim3(runs * sibs), dim3(64 * MlaCfg<HPB>::W), 0, s, kp,
@@ -594,16 +486,10 @@ static void launch_mla_main(int32_t runs, int32_t Hq, hipStream_t s, const char*
 
 hipError_t launch_mla_decode(const PoolInfo& p, int32_t layer, const void* q, int32_t Hq, const DevMap& m, int32_t bs,
                              const DecodePlan& plan, float sl2, void* out, float* lse, void* ws, hipStream_t s) {
-  MlaWs w;
-  mla_ws_layout(plan, bs, Hq, ws, &w);
+  StreamWs w;
+  stream_ws_layout(bs, plan.chunk, plan.max_splits, Hq, kMlaV, ws, &w);
   const int32_t runs = plan.max_splits;
-  if (m.fmt == MAP_TOKEN_TABLE)
-    hipLaunchKernelGGL(mla_plan_kernel<SLOT_TABLE>, dim3(bs), dim3(256), 0, s, m, bs, plan.chunk, runs,
-                       w.header, w.prefix, w.ntiles, w.fallback, w.meta);
-  else
-    hipLaunchKernelGGL(mla_plan_kernel<SLOT_PAGES>, dim3(bs), dim3(256), 0, s, m, bs, plan.chunk, runs,
-                       w.header, w.prefix, w.ntiles, w.fallback, w.meta);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_stream_plan(m, bs, plan.chunk, runs, w, s);
   if (e != hipSuccess) return e;
   const char* kp = p.k_layer(layer);
   timer_before(s);

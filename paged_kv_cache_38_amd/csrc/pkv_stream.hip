@@ -1,0 +1,150 @@
+// Stream split for decode: the pieces shared by the MLA and the grouped-query
+// decode kernels.
+//
+// What is computed: nothing of the attention itself -- this file lays the
+// requests' key tiles (32 logical positions each) end to end, cuts the
+// sequence into equal runs, one per workgroup (or group of workgroups), and
+// resolves every tile to its slot ids through the request's table ([XPU]
+// "From slots to a page table"; [BACKEND] init_forward_metadata).  A run
+// may end inside a request; the pieces a request is cut into are merged
+// exactly with log-sum-exp weights (the split/merge identity of the decode
+// split-K, here with splits placed by the run boundaries).  Piece (run r,
+// request i) has workspace id r + i: runs and requests are both in order,
+// so (r, i) -> r + i is one-to-one over the pieces that exist.
+#include <math.h>
+
+#include <algorithm>
+
+#include "pkv_launch.h"
+
+namespace pkv {
+
+// ---------------------------------------------------------------------------
+// Planner: workgroup (i, c) resolves tiles 8c .. 8c+7 of request i, one
+// thread per key position, and writes their info words {request, tile,
+// tiles of request, tile prefix, valid keys}; tokens past the request's end
+// repeat its last key, whose weight is then exactly 0.  Every workgroup sums
+// the tile counts itself (bs loads), so the planner is one launch with no
+// serial pass; workgroup (i, 0) also writes the request's prefix, tile count
+// and fallback flag, and (0, 0) the run length Bt and the tile total.
+// ---------------------------------------------------------------------------
+constexpr int kPlanTiles = 8;  // tiles per planner workgroup (256 threads)
+
+__device__ __forceinline__ int32_t stream_tiles(int32_t L) { return L > 0 ? (L + kStreamT - 1) / kStreamT : 0; }
+
+template <int FMT>
+__global__ void __launch_bounds__(256) stream_plan_kernel(DevMap m, int32_t bs, int32_t max_tiles, int32_t runs,
+                                                       int32_t* __restrict__ header,
+                                                       int32_t* __restrict__ prefix, int32_t* __restrict__ ntiles,
+                                                       int32_t* __restrict__ fallback, int32_t* __restrict__ meta) {
+  __shared__ int32_t red[2][4];
+  const int i = blockIdx.x, c = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int32_t T = min(stream_tiles(m.kv_lens[i]), max_tiles);
+  const bool lead = c == 0;
+  if (!lead && c * kPlanTiles >= T) return;  // uniform per workgroup
+  int32_t tot = 0, pre = 0;
+  for (int k = tid; k < bs; k += 256) {
+    const int32_t Tk = min(stream_tiles(m.kv_lens[k]), max_tiles);
+    tot += Tk;
+    if (k < i) pre += Tk;
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    tot += __shfl_xor(tot, o, 64);
+    pre += __shfl_xor(pre, o, 64);
+  }
+  if ((tid & 63) == 0) {
+    red[0][tid >> 6] = tot;
+    red[1][tid >> 6] = pre;
+  }
+  __syncthreads();
+  tot = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+  pre = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+  // keys past max_kv_len (a caller error) are not read: the workspace holds
+  // max_tiles tiles per request
+  const int32_t L = min(max(m.kv_lens[i], 0), T * kStreamT);
+  if (lead && tid == 0) {
+    prefix[i] = pre;
+    ntiles[i] = T;
+    fallback[i] = 0;
+    if (i == 0) {
+      header[0] = max(1, (tot + runs - 1) / runs);
+      header[1] = tot;
+    }
+  }
+  const int j = c * kPlanTiles + (tid >> 5);
+  if (j >= T) return;
+  const SlotMap<FMT> sm = make_slotmap<FMT>(m, i);
+  int32_t* tile = meta + (int64_t)(pre + j) * kStreamMetaWords;
+  tile[tid & 31] = sm(min(j * kStreamT + (tid & 31), L - 1), true);
+  const int f = tid & 31;
+  if (f < 8) {
+    int32_t v = 0;
+    if (f == 0) v = i;
+    else if (f == 1) v = j;
+    else if (f == 2) v = T;
+    else if (f == 3) v = pre;
+    else if (f == 4) v = min(kStreamT, L - j * kStreamT);
+    tile[32 + f] = v;
+  }
+}
+
+static size_t al256(size_t x) { return (x + 255) / 256 * 256; }
+
+// [header | tile prefix[bs] | tiles[bs] | fallback flags[bs] | meta[bs * max tiles][40] |
+//  pieces o[(runs + bs) * Hq * Dv] | pieces lse[(runs + bs) * Hq]]
+size_t stream_ws_layout(int32_t bs, int32_t max_tiles, int32_t runs, int32_t Hq, int32_t Dv, void* base,
+                        StreamWs* w) {
+  char* b = static_cast<char*>(base);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* at = b ? b + off : nullptr;
+    off += al256(bytes);
+    return at;
+  };
+  char* hdr = take(256);
+  char* pre = take((size_t)bs * 4);
+  char* nt = take((size_t)bs * 4);
+  char* fb = take((size_t)bs * 4);
+  char* meta = take((size_t)bs * max_tiles * kStreamMetaWords * 4);
+  const size_t pieces = (size_t)runs + bs;
+  char* o = take(pieces * Hq * Dv * 4);
+  char* l = take(pieces * Hq * 4);
+  if (w) {
+    w->header = reinterpret_cast<int32_t*>(hdr);
+    w->prefix = reinterpret_cast<int32_t*>(pre);
+    w->ntiles = reinterpret_cast<int32_t*>(nt);
+    w->fallback = reinterpret_cast<int32_t*>(fb);
+    w->meta = reinterpret_cast<int32_t*>(meta);
+    w->o = reinterpret_cast<float*>(o);
+    w->lse = reinterpret_cast<float*>(l);
+  }
+  return off;
+}
+
+hipError_t launch_stream_plan(const DevMap& m, int32_t bs, int32_t max_tiles, int32_t runs, const StreamWs& w,
+                              hipStream_t s) {
+  const dim3 grid((unsigned)bs, (unsigned)std::max(1, (max_tiles + kPlanTiles - 1) / kPlanTiles));
+  if (m.fmt == MAP_TOKEN_TABLE)
+    hipLaunchKernelGGL(stream_plan_kernel<SLOT_TABLE>, grid, dim3(256), 0, s, m, bs, max_tiles, runs, w.header,
+                       w.prefix, w.ntiles, w.fallback, w.meta);
+  else
+    hipLaunchKernelGGL(stream_plan_kernel<SLOT_PAGES>, grid, dim3(256), 0, s, m, bs, max_tiles, runs, w.header,
+                       w.prefix, w.ntiles, w.fallback, w.meta);
+  return hipGetLastError();
+}
+
+// One workgroup per CU of the current device.
+int32_t device_cu_count() {
+  static int32_t cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+}  // namespace pkv
