@@ -131,7 +131,7 @@ class DecodeBench:
     (page-granular formats), then paged decode attention."""
 
     bound = "hbm"
-    kernel_name = "paged decode split-K partial kernel"
+    kernel_name = "paged decode split-K kernel (stream split)"
     attn_calls = 1
     tokens_label = "decode_tokens_per_s"
 
