@@ -235,14 +235,23 @@ __global__ void __launch_bounds__(256, D == 64 ? 3 : 2) extend_kernel(DevMap m, 
             if (MASK && k0 + a2 * 16 + grp * 4 + rr >= row_end[rb]) x[a2][rr] = -INFINITY;
             mr = fmaxf(mr, x[a2][rr]);
           }
-        const float m_new = fmaxf(m_run[rb], max_xor16_32(mr) * scale_log2);
-        // a row that has seen no key yet keeps m = -inf: use 0 so p = 0
-        const float mu = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run[rb] - mu);
-        m_run[rb] = m_new;
+        // The row's reference m_run moves only when a score passes it by
+        // more than kExtSlack (log2 units), so probabilities stay below
+        // 2^kExtSlack and the accumulators are rescaled only on the (rare)
+        // tiles where some row of the wave moves; any reference gives the same
+        // normalised result.  A row's first visible key always moves it
+        // (-inf + slack = -inf).
+        const float m_tile = max_xor16_32(mr) * scale_log2;
+        const bool bump = m_tile > m_run[rb] + kExtSlack;
+        if (__builtin_amdgcn_ballot_w64(bump) != 0) {
+          const float alpha = bump ? fast_exp2(m_run[rb] - m_tile) : 1.0f;
+          m_run[rb] = bump ? m_tile : m_run[rb];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[rb][nt] *= alpha;
-        acc_l[rb] *= alpha;
+          for (int nt = 0; nt < NT; ++nt) acc[rb][nt] *= alpha;
+          acc_l[rb] *= alpha;
+        }
+        // a row that has seen no key yet keeps m = -inf: use 0 so p = 0
+        const float mu = m_run[rb] == -INFINITY ? 0.f : m_run[rb];
 #pragma unroll
         for (int a2 = 0; a2 < 4; ++a2)
 #pragma unroll
