@@ -130,7 +130,6 @@ class DecodeBench:
     """Decode step: kv_store of this step's tokens (if any), build_kv_indices
     (page-granular formats), then paged decode attention."""
 
-    bound = "hbm"
     kernel_name = "paged decode split-K kernel (stream split)"
     attn_calls = 1
     tokens_label = "decode_tokens_per_s"
@@ -250,7 +249,6 @@ class ExtendBench:
     non-causal extend over the encoder region (ragged: kv_gather of both
     regions, then extend over the contiguous copies)."""
 
-    bound = "mfma"
     attn_calls = 2
     tokens_label = "extend_tokens_per_s"
 
@@ -442,7 +440,11 @@ def main():
     step_gbs = b.step_bytes() / (ms_step * 1e-3) / 1e9
     kern_gbs = b.kernel_bytes() / (k_ms * 1e-3) / 1e9
     kern_tf = b.kernel_flops() / (k_ms * 1e-3) / 1e12
-    if b.bound == "hbm":
+    # the roof that bounds the kernel at its arithmetic intensity: HBM below
+    # the ridge point (peak flop/s / peak bytes/s = 312.5 flop/B), MFMA above
+    intensity = b.kernel_flops() / max(b.kernel_bytes(), 1)
+    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if intensity < ridge:
         roof = {"bound": "hbm", "achieved": round(kern_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(kern_gbs / HBM_PEAK_GBS, 4)}
     else:
@@ -450,7 +452,9 @@ def main():
                 "frac": round(kern_tf / BF16_PEAK_TFLOPS, 4)}
     roof.update({"traffic": measured_traffic(args.workload), "kernel": b.kernel_name, "kernel_ms": round(k_ms, 5),
                  "kernel_bytes": b.kernel_bytes(), "kernel_gbs": round(kern_gbs, 2),
-                 "kernel_hbm_frac": round(kern_gbs / HBM_PEAK_GBS, 4), "kernel_tflops": round(kern_tf, 3)})
+                 "kernel_hbm_frac": round(kern_gbs / HBM_PEAK_GBS, 4), "kernel_tflops": round(kern_tf, 3),
+                 "kernel_mfma_frac": round(kern_tf / BF16_PEAK_TFLOPS, 4),
+                 "flop_per_byte": round(intensity, 2)})
     if b.attn_calls > 1:
         roof["call_ms"] = [round(float(np.mean([c[k] for c in call_ms])), 5) for k in range(b.attn_calls)]
     res = {
