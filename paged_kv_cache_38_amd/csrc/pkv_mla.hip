@@ -8,8 +8,8 @@
 // attention over each request's keys in logical order; splitting is an
 // implementation detail merged back exactly with log-sum-exp weights.
 //
-// Design for gfx950 (one workgroup per CU, all query heads of a request in
-// one workgroup, so every latent row leaves HBM exactly once):
+// Design for gfx950 (one workgroup per CU holding every query head of the
+// request, so every latent row leaves HBM exactly once):
 //
 //  * Work split.  The requests' 32-token tiles are laid end to end and the
 //    grid (one workgroup per CU) takes equal contiguous runs of them, so every
@@ -26,14 +26,17 @@
 //    bank conflicts.  These loads are issued from inline assembly and waited
 //    on explicitly, because the compiler would otherwise drain the whole
 //    queue before every LDS read.
-//  * Math.  Wave w computes S^T = K Q^T for its 32 heads (queries held in
-//    registers) and the softmax for them; P goes through LDS; then every wave
-//    computes O += P V for all heads over its own slice of the 512 value
-//    columns (accumulators in AGPRs).  The softmax reference is the maximum
-//    of a piece's first tile and then stays fixed, so the accumulators are
-//    never rescaled (any reference gives the same normalised result); should
-//    a later score exceed it by more than 2^64 (P could overflow), the
-//    request is recomputed exactly by a fallback in the merge pass.
+//  * Math.  Each wave owns 32 query heads (16 when there are fewer than 128)
+//    end to end: S^T = K Q^T with the queries in registers, the softmax, and
+//    O += P V over all 512 value columns with the accumulators in AGPRs, P
+//    going straight from the score registers into the MFMA A operand.  Every
+//    K and V fragment read from LDS feeds two MFMAs (two 16-head blocks),
+//    and one barrier per tile is the only synchronisation.  The softmax
+//    reference is the maximum of a piece's first tile and then stays fixed,
+//    so the accumulators are never rescaled (any reference gives the same
+//    normalised result); should a later score exceed it by more than 2^64 (P
+//    could overflow), the request is recomputed exactly by a fallback in the
+//    merge pass.
 #include <math.h>
 
 #include <algorithm>
@@ -53,19 +56,13 @@ constexpr int kMlaBufs = 4;                       // LDS tile buffers: three til
 constexpr int kMlaMetaRing = 8;                   // per-wave ring of per-tile slot ids / info
 constexpr float kMlaHeadroom = 64.0f;             // log2 units a score may exceed the reference by
 
-// Launch shape per workgroup of HPB heads (16, 32 or 64): W waves; wave w
-// computes scores for HB blocks of 16 heads and output columns
-// [w * CW, (w + 1) * CW) of all HPB heads.  A wave then holds 72 VGPRs of
-// queries and 128 accumulators.  More than 64 heads take sibling workgroups
-// (one per 64 heads) that stream the same tiles on the same XCD, the second
-// read served by its L2.
-template <int HPB>
-struct MlaCfg {
-  static constexpr int W = HPB / 16;
-  static constexpr int HB = 1;
-  static constexpr int NHB = HPB / 16;
-  static constexpr int CW = kMlaV / W;
-  static constexpr int NCB = CW / 16;
+// Launch shape: W waves per workgroup, HB blocks of 16 query heads per wave
+// (Hq = 16 HB W).  A wave owns its heads end to end: queries in registers
+// (72 VGPRs per 16 heads), scores, softmax and the P*V accumulators of all
+// 512 value columns (128 AGPRs per 16 heads), so P never leaves the wave.
+// With HB = 2 every K and V fragment read from LDS feeds two MFMAs.
+template <int HB, int W>
+struct MlaShape {
   static constexpr int NI = (kMlaTileBytes / 1024) / W;  // tile DMA instructions per wave
 };
 
@@ -81,84 +78,72 @@ __device__ __forceinline__ float acc_get(float a) {
 // byte offset of chunk c of token t inside a swizzled tile
 __device__ __forceinline__ int mla_chunk_off(int t, int c) { return (t * kMlaRowChunks + (c ^ (t & 7))) * 16; }
 
-// B operand of P*V (16x16x32 MFMA) from a swizzled tile: lane (n = l%16,
-// j = l/16) receives V[4j + r][c0 + n] (r = 0..3) and V[16 + 4j + r][c0 + n].
-__device__ __forceinline__ bf16x8 mla_v_operand(const char* tile, int c0, int lane) {
-  const int x = lane & 15, j = lane >> 4;
-  const int t = 4 * j + (x >> 2);
-  const int c = c0 + 4 * (x & 3);
-  const char* lo = tile + mla_chunk_off(t, c >> 3) + (c & 7) * 2;
-  const i16x4 a = lds_read_tr16(reinterpret_cast<const bf16*>(lo));
-  const i16x4 b = lds_read_tr16(reinterpret_cast<const bf16*>(lo + 16 * kMlaRowBytes));
-  const bf16x4 ba = __builtin_bit_cast(bf16x4, a), bb = __builtin_bit_cast(bf16x4, b);
-  return bf16x8{ba[0], ba[1], ba[2], ba[3], bb[0], bb[1], bb[2], bb[3]};
-}
-
-// O += P V for one tile over a wave's NCB column blocks and NHB head
-// blocks; P fragments of all heads and four column blocks of V at a time
-// in registers.  Column block cb = 4 m + u of the whole row: the
-// transposed read of lane (x, j) starts at token t = 4 j + x / 4, chunk
-// 8 (cb / 4) + ((2 u + (x & 3) / 2) ^ (t & 7)): four per-lane bases (u) plus
-// compile-time offsets.  ZERO starts the accumulators from zero.
-template <int NHB, int NCB, bool ZERO>
-__device__ __forceinline__ void mla_pv(f32x4 (&acc)[NHB][NCB], const char* tile, const bf16x8* p_lds, int w,
+// O += P V for one tile over all 32 column blocks of the wave's HB head
+// blocks.  The B operand of column block cb = 4 m + u comes from two
+// transposed reads: lane (x, j) starts at token t = 4 j + x / 4, chunk
+// 8 m + ((2 u + (x & 3) / 2) ^ (t & 7)), so four per-lane bases (u) plus
+// compile-time offsets cover every read; lane (x, j) then holds
+// V[4j + r][16 cb + x] and V[16 + 4j + r][16 cb + x] (r = 0..3), the token
+// order of the P fragment the score layout leaves in the lane.  ZERO starts
+// the accumulators from zero inside the MFMA.
+template <int HB, bool ZERO>
+__device__ __forceinline__ void mla_pv(f32x4 (&acc)[HB][kMlaV / 16], const char* tile, const bf16x8 (&pa)[HB],
                                        int lane) {
   const int x = lane & 15, jg = lane >> 4;
   const int t = 4 * jg + (x >> 2);
   const char* vb[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u)
-    vb[u] = tile + (t * kMlaRowChunks + ((2 * u + ((x & 3) >> 1)) ^ (t & 7))) * 16 + (x & 1) * 8 +
-            (w * NCB / 4) * 128;
-  bf16x8 pf[NHB];
-#pragma unroll
-  for (int hb = 0; hb < NHB; ++hb) pf[hb] = p_lds[hb * 64 + lane];
-#pragma unroll
-  for (int cg = 0; cg < NCB; cg += 4) {
-    bf16x8 vf[4];
+    vb[u] = tile + (t * kMlaRowChunks + ((2 * u + ((x & 3) >> 1)) ^ (t & 7))) * 16 + (x & 1) * 8;
+  auto vload = [&](int m, bf16x8* vf) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const char* lo = vb[u] + (cg / 4) * 128;
+      const char* lo = vb[u] + m * 128;
       const i16x4 va = lds_read_tr16(reinterpret_cast<const bf16*>(lo));
       const i16x4 vc = lds_read_tr16(reinterpret_cast<const bf16*>(lo + 16 * kMlaRowBytes));
       const bf16x4 ba = __builtin_bit_cast(bf16x4, va), bc = __builtin_bit_cast(bf16x4, vc);
       vf[u] = bf16x8{ba[0], ba[1], ba[2], ba[3], bc[0], bc[1], bc[2], bc[3]};
     }
+  };
+  // groups of four column blocks, the next group's reads in flight while
+  // this group's MFMAs run
+  bf16x8 vf[2][4];
+  vload(0, vf[0]);
 #pragma unroll
-    for (int hb = 0; hb < NHB; ++hb)
+  for (int m = 0; m < kMlaV / 64; ++m) {
+    if (m + 1 < kMlaV / 64) vload(m + 1, vf[(m + 1) & 1]);
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        acc[hb][cg + u] = mfma16x16x32(pf[hb], vf[u], ZERO ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[hb][cg + u]);
+        acc[hb][4 * m + u] = mfma16x16x32(pa[hb], vf[m & 1][u], ZERO ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[hb][4 * m + u]);
+    __builtin_amdgcn_sched_barrier(0);  // keep later groups' reads from being hoisted (VGPRs)
   }
 }
 
 // ---------------------------------------------------------------------------
-// Main kernel.
+// Main kernel: one workgroup per run (one per CU).
 // ---------------------------------------------------------------------------
-template <int HPB>
-__global__ void __launch_bounds__(64 * MlaCfg<HPB>::W, 1) mla_decode_kernel(
-    const char* kpool, const bf16* __restrict__ q, int32_t HQ, int32_t sibs, const int32_t* __restrict__ header,
+template <int HB, int W>
+__global__ void __launch_bounds__(64 * W, 1) mla_decode_kernel(
+    const char* kpool, const bf16* __restrict__ q, int32_t HQ, const int32_t* __restrict__ header,
     const int32_t* __restrict__ meta, float scale_log2, bf16* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ ws_o, float* __restrict__ ws_lse, int32_t* __restrict__ fallback) {
-  using C = MlaCfg<HPB>;
-  constexpr int W = C::W, HB = C::HB, NHB = C::NHB, CW = C::CW, NCB = C::NCB, NI = C::NI;
+  constexpr int NI = MlaShape<HB, W>::NI;
   constexpr int NK = kMlaQK / 32;  // 18 k-steps of the score product
+  constexpr int NC = kMlaV / 16;   // 32 column blocks of the output
 
   __shared__ __attribute__((aligned(1024))) char tiles[kMlaBufs][kMlaTileBytes];
-  __shared__ __attribute__((aligned(16))) bf16x8 p_lds[NHB * 64];
   __shared__ __attribute__((aligned(256))) int32_t meta_lds[W][kMlaMetaRing][64];
-  __shared__ __attribute__((aligned(16))) float l_lds[HPB];
-  __shared__ __attribute__((aligned(16))) float m_lds[HPB];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
-  // run and sibling: siblings sit 8 workgroups apart, on the same XCD
-  const int run = sibs == 1 ? (int)blockIdx.x : (int)(blockIdx.x / 16 * 8 + blockIdx.x % 8);
-  const int h0 = sibs == 1 ? 0 : (int)(blockIdx.x / 8 % 2) * HPB;
+  const int run = (int)blockIdx.x;
   const int Bt = header[0], total = header[1];
   const int G0 = run * Bt;
   if (G0 >= total) return;
   const int n = min(Bt, total - G0);
+  const int hw = w * HB * 16;  // first head of this wave
 
   // ---- loaders (every wave issues the same number of each, in the same order)
   auto meta_dma = [&](int r) {
@@ -180,18 +165,18 @@ __global__ void __launch_bounds__(64 * MlaCfg<HPB>::W, 1) mla_decode_kernel(
     }
   };
 
-  f32x4 acc[NHB][NCB];
+  f32x4 acc[HB][NC];
 #pragma unroll
-  for (int a = 0; a < NHB; ++a)
+  for (int a = 0; a < HB; ++a)
 #pragma unroll
-    for (int b = 0; b < NCB; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < NC; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
   bf16x8 qf[HB][NK];
   float m_ref[HB], l_part[HB];
 
   // Per iteration r a wave issues meta(r + 6) then tile(r + 3); tile(r) is
   // then followed in the queue by meta(r + 4), tile(r + 1), meta(r + 5),
   // tile(r + 2), meta(r + 6): 2 NI + 3 operations.  The prologue builds that
-  // state for r = 0.
+  // state for r = 0.  (Above 63 the counter's maximum waits for more.)
   constexpr int kWait = 2 * NI + 3 < 63 ? 2 * NI + 3 : 63;
   meta_dma(0);
   meta_dma(1);
@@ -206,7 +191,7 @@ __global__ void __launch_bounds__(64 * MlaCfg<HPB>::W, 1) mla_decode_kernel(
   for (int r = 0; r < n; ++r) {
     meta_dma(r + 6);
     wait_vm<kWait>();   // tile(r) (and every meta before it) has landed
-    __syncthreads();    // tile r visible to all waves; every wave is past P*V of tile r - 1
+    __syncthreads();    // tile r visible to all waves; every wave is past tile r - 1
     tile_dma(r + 3);    // into the buffer tile r - 1 used
 
     const int32_t* info = &meta_lds[w][r & (kMlaMetaRing - 1)][32];
@@ -222,7 +207,7 @@ __global__ void __launch_bounds__(64 * MlaCfg<HPB>::W, 1) mla_decode_kernel(
     if (seg_begin) {
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
-        const int h = h0 + (w * HB + hb) * 16 + col;
+        const int h = hw + hb * 16 + col;
         const bf16* qp = q + ((int64_t)i * HQ + h) * kMlaQK + grp * 8;
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) qf[hb][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + kk * 32));
@@ -244,8 +229,8 @@ __global__ void __launch_bounds__(64 * MlaCfg<HPB>::W, 1) mla_decode_kernel(
         for (int hb = 0; hb < HB; ++hb) sacc[a][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
       // K fragments stream through a window of KD k-steps (2 fragments each);
       // a sched barrier per step keeps the compiler from hoisting all 36
-      // reads (which would need 144 more VGPRs)
-      constexpr int KD = 5;
+      // reads
+      constexpr int KD = 3;
       bf16x8 kf[KD][2];
       auto kload = [&](int kk, bf16x8* dst) {
         const char* kb = (kk & 1) ? kb_odd : kb_even;
@@ -266,12 +251,14 @@ __global__ void __launch_bounds__(64 * MlaCfg<HPB>::W, 1) mla_decode_kernel(
       }
     }
 
-    // ---- softmax (log2 domain) for head 16 * (w * HB + hb) + col; this lane
-    // holds tokens 16a + 4 grp + rr.  The reference maximum is the first
-    // tile's maximum and stays fixed for the piece, so the accumulators are
-    // never rescaled; a later score more than kMlaHeadroom above it (P could
+    // ---- softmax (log2 domain) for head hw + 16 hb + col; this lane holds
+    // tokens 16a + 4 grp + rr, which is also the token order of P as the A
+    // operand of P*V.  The reference maximum is the first tile's maximum
+    // and stays fixed for the piece, so the accumulators are never
+    // rescaled; a later score more than kMlaHeadroom above it (P could
     // overflow) sends the request to the exact fallback in the merge pass.
     bool over = false;
+    bf16x8 pa[HB];
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
       float x[2][4];
@@ -288,11 +275,8 @@ __global__ void __launch_bounds__(64 * MlaCfg<HPB>::W, 1) mla_decode_kernel(
         for (int a = 0; a < 2; ++a)
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) mt = fmaxf(mt, x[a][rr]);
-        mt = fmaxf(mt, shfl_xor(mt, 16));
-        mt = fmaxf(mt, shfl_xor(mt, 32));
-        m_ref[hb] = mt;
+        m_ref[hb] = max_xor16_32(mt);
       }
-      bf16x8 pa;
       float ps = 0.f;
 #pragma unroll
       for (int a = 0; a < 2; ++a)
@@ -301,64 +285,50 @@ __global__ void __launch_bounds__(64 * MlaCfg<HPB>::W, 1) mla_decode_kernel(
           over |= x[a][rr] > m_ref[hb] + kMlaHeadroom;
           const float p = fast_exp2(x[a][rr] - m_ref[hb]);
           ps += p;
-          pa[a * 4 + rr] = (bf16)p;
+          pa[hb][a * 4 + rr] = (bf16)p;
         }
       l_part[hb] += ps;
-      p_lds[(w * HB + hb) * 64 + lane] = pa;
     }
     if (__builtin_amdgcn_ballot_w64(over) != 0 && lane == 0) fallback[i] = 1;
-    __syncthreads();  // P of every wave is in LDS
 
-    // ---- O += P V over this wave's columns, all heads (the first tile of a
-    // piece starts the accumulators from zero inside the MFMA)
+    // ---- O += P V over all columns of this wave's heads (the first tile of
+    // a piece starts the accumulators from zero inside the MFMA)
     if (seg_begin)
-      mla_pv<NHB, NCB, true>(acc, tile, p_lds, w, lane);
+      mla_pv<HB, true>(acc, tile, pa, lane);
     else
-      mla_pv<NHB, NCB, false>(acc, tile, p_lds, w, lane);
+      mla_pv<HB, false>(acc, tile, pa, lane);
 
     if (seg_end) {
+      const int b0 = P / Bt, b1 = (P + T - 1) / Bt;
+      const bool direct = b0 == b1;
+      const int64_t row0 = (direct ? (int64_t)i * HQ : ((int64_t)run + i) * HQ) + hw;
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
         float lt = l_part[hb] + shfl_xor(l_part[hb], 16);
-        lt += shfl_xor(lt, 32);
-        if (grp == 0) {
-          l_lds[(w * HB + hb) * 16 + col] = lt;
-          m_lds[(w * HB + hb) * 16 + col] = m_ref[hb];
-        }
-      }
-      __syncthreads();
-      const int b0 = P / Bt, b1 = (P + T - 1) / Bt;
-      const bool direct = b0 == b1;
-      // per-lane bases computed here (not hoisted out of the tile loop), then
-      // compile-time offsets: head 16 hb + 4 grp + rr, column w CW + 16 cb + col
-      int g4 = 4 * grp;
-      asm volatile("" : "+v"(g4));
-      const int64_t row0 = (direct ? (int64_t)i * HQ : ((int64_t)run + i) * HQ) + h0 + g4;
-      bf16* ob = out + row0 * kMlaV + w * CW + col;
-      float* wb = ws_o + row0 * kMlaV + w * CW + col;
-      float* lb = (direct ? lse : ws_lse) + (lse || !direct ? row0 : 0);
-      const bool write_lse = (lse || !direct) && w == 0 && col == 0;
-#pragma unroll
-      for (int hb = 0; hb < NHB; ++hb) {
-        const f32x4 lv = *reinterpret_cast<const f32x4*>(&l_lds[hb * 16 + g4]);
-        const f32x4 mv = *reinterpret_cast<const f32x4*>(&m_lds[hb * 16 + g4]);
+        lt += shfl_xor(lt, 32);  // row sum of head hw + 16 hb + col, in every lane of that column
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          const int hoff = hb * 16 + rr;
-          const float inv = 1.0f / lv[rr];
+          // output rows of the accumulators are heads 16 hb + 4 grp + rr
+          const int hr = 4 * grp + rr;
+          const float lr = shfl(lt, hr);
+          const float mr = shfl(m_ref[hb], hr);
+          const float inv = 1.0f / lr;
+          const int64_t row = row0 + hb * 16 + hr;
           if (direct) {
+            bf16* ob = out + row * kMlaV + col;
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) ob[hoff * kMlaV + cb * 16] = (bf16)(acc_get(acc[hb][cb][rr]) * inv);
+            for (int cb = 0; cb < NC; ++cb) ob[cb * 16] = (bf16)(acc_get(acc[hb][cb][rr]) * inv);
+            if (lse && col == 0) lse[row] = (mr + __log2f(lr)) * kLn2;
           } else {
+            float* wb = ws_o + row * kMlaV + col;
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) wb[hoff * kMlaV + cb * 16] = acc_get(acc[hb][cb][rr]) * inv;
+            for (int cb = 0; cb < NC; ++cb) wb[cb * 16] = acc_get(acc[hb][cb][rr]) * inv;
+            if (col == 0) ws_lse[row] = (mr + __log2f(lr)) * kLn2;
           }
-          if (write_lse) lb[hoff] = (mv[rr] + __log2f(lv[rr])) * kLn2;
         }
       }
-      // no zeroing here: the next segment's first tile rescales every head
-      // by exp2(-inf) = 0 (the accumulators are finite), and redefining the
-      // accumulators in this branch would cost a full copy per tile
+      // no zeroing here: the next piece's first tile starts the
+      // accumulators from zero inside the MFMA
     }
   }
   wait_vm<0>();  // no load may still target this workgroup's LDS when it ends
@@ -466,22 +436,19 @@ bool mla_decode_supported(const PoolInfo& p, int32_t Hq) {
 DecodePlan plan_mla_decode(const PoolInfo& p, int32_t bs, int32_t Hq, int32_t max_kv_len) {
   (void)p;
   (void)bs;
+  (void)Hq;
   DecodePlan plan;
   plan.kind = 3;
   plan.chunk = max_kv_len > 0 ? (max_kv_len + kMlaT - 1) / kMlaT : 0;  // tiles per request, at most
-  // runs of tiles: one workgroup per CU, two sibling workgroups per run
-  // above 64 heads (an even split of the CUs)
-  plan.max_splits = Hq > 64 ? std::max(8, device_cu_count() / 2 / 8 * 8) : device_cu_count();
+  plan.max_splits = device_cu_count();  // runs of tiles: one workgroup per CU, all heads in it
   return plan;
 }
 
-template <int HPB>
+template <int HB, int W>
 static void launch_mla_main(int32_t runs, int32_t Hq, hipStream_t s, const char* kp, const void* q, const StreamWs& w,
                             float sl2, void* out, float* lse) {
-  const int sibs = Hq / HPB;
-  hipLaunchKernelGGL((mla_decode_kernel<HPB>), dim3(runs * sibs), dim3(64 * MlaCfg<HPB>::W), 0, s, kp,
-                     static_cast<const bf16*>(q), Hq, sibs, w.header, w.meta, sl2, static_cast<bf16*>(out), lse,
-                     w.o, w.lse, w.fallback);
+  hipLaunchKernelGGL((mla_decode_kernel<HB, W>), dim3(runs), dim3(64 * W), 0, s, kp, static_cast<const bf16*>(q), Hq,
+                     w.header, w.meta, sl2, static_cast<bf16*>(out), lse, w.o, w.lse, w.fallback);
 }
 
 hipError_t launch_mla_decode(const PoolInfo& p, int32_t layer, const void* q, int32_t Hq, const DevMap& m, int32_t bs,
@@ -493,9 +460,10 @@ hipError_t launch_mla_decode(const PoolInfo& p, int32_t layer, const void* q, in
   if (e != hipSuccess) return e;
   const char* kp = p.k_layer(layer);
   timer_before(s);
-  if (Hq >= 64) launch_mla_main<64>(runs, Hq, s, kp, q, w, sl2, out, lse);
-  else if (Hq == 32) launch_mla_main<32>(runs, Hq, s, kp, q, w, sl2, out, lse);
-  else launch_mla_main<16>(runs, Hq, s, kp, q, w, sl2, out, lse);
+  if (Hq == 128) launch_mla_main<2, 4>(runs, Hq, s, kp, q, w, sl2, out, lse);
+  else if (Hq == 64) launch_mla_main<1, 4>(runs, Hq, s, kp, q, w, sl2, out, lse);
+  else if (Hq == 32) launch_mla_main<1, 2>(runs, Hq, s, kp, q, w, sl2, out, lse);
+  else launch_mla_main<1, 1>(runs, Hq, s, kp, q, w, sl2, out, lse);
   e = hipGetLastError();
   timer_after(s);
   if (e != hipSuccess) return e;
