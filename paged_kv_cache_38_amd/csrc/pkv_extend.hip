@@ -9,15 +9,17 @@
 // zero output and lse = -inf ([XPU] "Approach 2" guard).  With a CONTIGUOUS
 // map this is the ragged (varlen) variant over gathered K/V.
 //
-// Layout on gfx950: one block per (64-query tile, query head, request); four
-// wavefronts of 16 query rows each.  Key tiles of 64 tokens are gathered
-// through the table into LDS (token-major rows, 16-byte chunks XOR-swizzled), double
-// buffered so the next tile's HBM reads overlap this tile's MFMA work:
+// Layout on gfx950: one workgroup per (query tile, query head, request); four
+// wavefronts of 16 RB query rows each (RB 16-row blocks: 3 at D = 64, 2 at
+// D = 128).  Key tiles of 64 tokens move HBM -> LDS through the table by
+// global_load_lds (token-major rows, 16-byte chunks XOR-swizzled), S stages
+// deep, so the next tiles' reads overlap this tile's MFMA work:
 //   S^T[16 keys x 16 rows] = K_tile[16 x D] * Q^T[D x 16]   (v_mfma_f32_16x16x32_bf16)
 // leaves each lane one query row (lane % 16) and 16 keys, so the row softmax
-// needs only two cross-lane steps, and P is already the A operand of
-//   O[16 rows x D] += P[16 x 32 keys] * V[32 keys x D]
-// whose B operand comes from LDS with ds_read_b64_tr_b16.
+// needs only two cross-lane steps, and P is already the B operand of
+//   O^T[D x 16 rows] += V^T[D x 32 keys] * P^T[32 keys x 16 rows]
+// whose A operand comes from LDS with ds_read_b64_tr_b16.  Every K and V
+// fragment read from LDS feeds the RB row blocks of the wave.
 #include <math.h>
 
 #include <type_traits>
@@ -26,12 +28,18 @@
 
 namespace pkv {
 
-constexpr int kBM = 128;  // query rows per block (32 per wave, two 16-row blocks)
 constexpr int kBN = 64;   // keys per tile
 constexpr float kExtSlack = 8.0f;  // log2 headroom before a row's running max moves
 
+// Rows: D = 64 takes three 16-row blocks per wave (192 query rows per
+// workgroup, 216 VGPRs, two workgroups per CU), so every K and V fragment
+// read from LDS feeds three MFMAs and a (request, head) pair re-streams its
+// keys once per 192 queries; D = 128 takes two (128 rows, two per CU).
 template <int D>
 struct ExtendCfg {
+  static constexpr int RB = D == 64 ? 3 : 2;  // 16-row blocks per wave
+  static constexpr int WR = 16 * RB;          // query rows per wave
+  static constexpr int BM = 4 * WR;           // query rows per workgroup (four waves)
   static constexpr int NK = D / 32;          // k-steps of the score product
   static constexpr int NT = D / 16;          // 16-wide d tiles of O
   static constexpr int CPK = D / 8;          // 16-byte chunks per key row (one head)
@@ -65,13 +73,14 @@ __device__ __forceinline__ bf16x8 ext_v_operand(const char* tile, int r0, int c0
 }
 
 template <int D, int FMT>
-__global__ void __launch_bounds__(256, D == 64 ? 3 : 2) extend_kernel(DevMap m, const char* k_pool, const char* v_pool,
+__global__ void __launch_bounds__(256, 2) extend_kernel(DevMap m, const char* k_pool, const char* v_pool,
                                                      int64_t row_bytes, const bf16* __restrict__ q, int64_t total_q,
                                                      const int32_t* __restrict__ qo_indptr, int32_t Hq, int32_t n_req,
                                                      int32_t n_qtiles, int32_t G, int32_t causal, float scale_log2,
                                                      bf16* __restrict__ out, float* __restrict__ lse) {
   using C = ExtendCfg<D>;
   constexpr int NK = C::NK, NT = C::NT, CPK = C::CPK, NI = C::NI, S = C::S;
+  constexpr int kRB = C::RB, kWR = C::WR, kBM = C::BM;
   __shared__ __attribute__((aligned(1024))) char kv_lds[S][2][C::TILE];
   __shared__ __attribute__((aligned(256))) int32_t tab_lds[4][S + 1][64];
 
@@ -96,7 +105,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 3 : 2) extend_kernel(DevMap m, 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int g = h / G;
-  const int rw = qt * kBM + w * 32;  // first query row (within the request) of this wave
+  const int rw = qt * kBM + w * kWR;  // first query row (within the request) of this wave
 
   // keys any row of this block may see
   int kv_end = L;
@@ -104,14 +113,14 @@ __global__ void __launch_bounds__(256, D == 64 ? 3 : 2) extend_kernel(DevMap m, 
   if (kv_end < 0) kv_end = 0;
   const int ntiles = (kv_end + kBN - 1) / kBN;
   // keys this wave's rows may see, and where the causal mask starts to bite
-  const int w_end = causal ? max(0, min(L, L - n + min(rw + 32, n))) : L;
+  const int w_end = causal ? max(0, min(L, L - n + min(rw + kWR, n))) : L;
   const int w_free = causal ? max(0, L - n + rw + 1) : L;  // keys visible to every row of the wave
 
   // Q^T operands: lane (row col of row block rb, group grp) holds
   // q[row][kk*32 + grp*8 .. +8]
-  bf16x8 qb[2][NK];
+  bf16x8 qb[kRB][NK];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < kRB; ++rb) {
     const int row = rw + rb * 16 + col;
     const bool ok = row < n;
     const bf16* qp = q + ((int64_t)(q0 + (ok ? row : 0)) * Hq + h) * D + grp * 8;
@@ -122,20 +131,25 @@ __global__ void __launch_bounds__(256, D == 64 ? 3 : 2) extend_kernel(DevMap m, 
       qb[rb][kk] = as_bf16x8(v);
     }
   }
-  int row_end[2];
+  int row_end[kRB];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < kRB; ++rb) {
     const int row = rw + rb * 16 + col;
     row_end[rb] = causal ? min(L, L - n + row + 1) : L;
   }
 
-  f32x4 acc[2][NT];
+  f32x4 acc[kRB][NT];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+  for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[rb][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  f32x4 acc_l[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};  // row sums (any column)
-  float m_run[2] = {-INFINITY, -INFINITY};
+  f32x4 acc_l[kRB];  // row sums (any column)
+  float m_run[kRB];
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) {
+    acc_l[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[rb] = -INFINITY;
+  }
 
   if (ntiles > 0) {
     const SlotMap<FMT> sm = make_slotmap<FMT>(m, i);
@@ -200,20 +214,19 @@ __global__ void __launch_bounds__(256, D == 64 ? 3 : 2) extend_kernel(DevMap m, 
       const int k0 = kt * kBN;
 
       // ---- S^T = K Q^T: four 16-key subtiles x two 16-row blocks
-      f32x4 sacc[4][2];
+      f32x4 sacc[4][kRB];
 #pragma unroll
-      for (int a2 = 0; a2 < 4; ++a2) {
-        sacc[a2][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-        sacc[a2][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+      for (int a2 = 0; a2 < 4; ++a2)
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) sacc[a2][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
         const char* kb = ks + ((kk & 1) ? kbase1 : kbase0) + (kk >> 1) * 128;
 #pragma unroll
         for (int a2 = 0; a2 < 4; ++a2) {
           const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(kb + a2 * 16 * CPK * 16));
-          sacc[a2][0] = mfma16x16x32(ka, qb[0][kk], sacc[a2][0]);
-          sacc[a2][1] = mfma16x16x32(ka, qb[1][kk], sacc[a2][1]);
+#pragma unroll
+          for (int rb = 0; rb < kRB; ++rb) sacc[a2][rb] = mfma16x16x32(ka, qb[rb][kk], sacc[a2][rb]);
         }
       }
 
@@ -222,9 +235,9 @@ __global__ void __launch_bounds__(256, D == 64 ? 3 : 2) extend_kernel(DevMap m, 
       // positive), so each probability is one fma and one exp2.  O is kept
       // transposed (lane col = row, like the scores), so the per-row rescale
       // is a plain multiply in every lane: no cross-lane traffic.
-      bf16x8 pa[2][2];
+      bf16x8 pa[kRB][2];
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
+      for (int rb = 0; rb < kRB; ++rb) {
         float x[4][4];
         float mr = -INFINITY;
 #pragma unroll
@@ -270,11 +283,11 @@ __global__ void __launch_bounds__(256, D == 64 ? 3 : 2) extend_kernel(DevMap m, 
           const i16x4 vc = lds_read_tr16(reinterpret_cast<const bf16*>(lo + 16 * CPK * 16));
           const bf16x4 ba = __builtin_bit_cast(bf16x4, va), bc = __builtin_bit_cast(bf16x4, vc);
           const bf16x8 vf = bf16x8{ba[0], ba[1], ba[2], ba[3], bc[0], bc[1], bc[2], bc[3]};
-          acc[0][nt] = mfma16x16x32(vf, pa[0][b2], acc[0][nt]);
-          acc[1][nt] = mfma16x16x32(vf, pa[1][b2], acc[1][nt]);
+#pragma unroll
+          for (int rb = 0; rb < kRB; ++rb) acc[rb][nt] = mfma16x16x32(vf, pa[rb][b2], acc[rb][nt]);
         }
-        acc_l[0] = mfma16x16x32(ones, pa[0][b2], acc_l[0]);
-        acc_l[1] = mfma16x16x32(ones, pa[1][b2], acc_l[1]);
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) acc_l[rb] = mfma16x16x32(ones, pa[rb][b2], acc_l[rb]);
       }
     };
 
@@ -299,6 +312,10 @@ __global__ void __launch_bounds__(256, D == 64 ? 3 : 2) extend_kernel(DevMap m, 
       if constexpr (S > 2) {
         if (kt + 2 < ntiles) step(kt + 2, std::integral_constant<int, 2 % S>{});
       }
+      if constexpr (S > 3) {
+        if (kt + 3 < ntiles) step(kt + 3, std::integral_constant<int, 3 % S>{});
+      }
+      static_assert(S <= 4, "the tile loop is unrolled for at most four stages");
     }
     wait_vm<0>();  // no load may still target this block's LDS when it ends
   }
@@ -306,7 +323,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 3 : 2) extend_kernel(DevMap m, 
   // ---- finalise: lane (row col of block rb, group grp) holds
   // O[row][16 nt + 4 grp + rr] and the row's sum in acc_l
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < kRB; ++rb) {
     const int row = rw + rb * 16 + col;
     if (row < n) {
       const int64_t o = ((int64_t)(q0 + row) * Hq + h);
@@ -369,7 +386,8 @@ hipError_t launch_extend(const PoolInfo& p, int32_t layer, const void* q, int64_
   const char* vp = reinterpret_cast<const char*>(m.fmt == MAP_CONTIGUOUS ? m.contig_v : p.v_layer(layer));
   const int G = Hq / p.num_kv_heads;
   // (query tiles, -, requests); the launcher flattens it XCD-aware
-  const dim3 grid(1, (unsigned)((max_q_len + kBM - 1) / kBM), (unsigned)bs);
+  const int bm = p.head_dim_qk == 128 ? ExtendCfg<128>::BM : ExtendCfg<64>::BM;
+  const dim3 grid(1, (unsigned)((max_q_len + bm - 1) / bm), (unsigned)bs);
   const int64_t row_bytes = (int64_t)p.num_kv_heads * p.head_dim_qk * 2;  // one token row, all KV heads
   const float sl2 = sm_scale * kLog2e;
   timer_before(s);
