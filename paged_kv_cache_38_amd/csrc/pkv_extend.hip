@@ -235,41 +235,62 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(DevMap m, const char* k_
       // positive), so each probability is one fma and one exp2.  O is kept
       // transposed (lane col = row, like the scores), so the per-row rescale
       // is a plain multiply in every lane: no cross-lane traffic.
-      bf16x8 pa[kRB][2];
+      // Keys past a row's visible range get -inf in place (boundary tiles
+      // only).  The row's reference m_run moves only when a score passes it
+      // by more than kExtSlack (log2 units), so probabilities stay below
+      // 2^kExtSlack and the accumulators are rescaled only on the (rare)
+      // tiles where some row of the wave moves; any reference gives the same
+      // normalised result.  A row's first visible key always moves it
+      // (-inf + slack = -inf).  One branch covers all row blocks, so the
+      // softmax of the row blocks stays one basic block.
+      if (MASK) {
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) {
+          const int lim = row_end[rb] - k0 - grp * 4;  // key a2*16 + rr of this lane is visible below lim
+#pragma unroll
+          for (int a2 = 0; a2 < 4; ++a2)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+              if (a2 * 16 + rr >= lim) sacc[a2][rb][rr] = -INFINITY;
+        }
+      }
+      // Common case first: each lane compares its own maximum with the
+      // row's reference, and only when some lane of the wave passes it does
+      // the wave take the cross-lane row maxima and rescale.
+      float lane_max[kRB];
+      bool lane_bump = false;
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb) {
-        float x[4][4];
         float mr = -INFINITY;
 #pragma unroll
         for (int a2 = 0; a2 < 4; ++a2)
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            x[a2][rr] = sacc[a2][rb][rr];
-            if (MASK && k0 + a2 * 16 + grp * 4 + rr >= row_end[rb]) x[a2][rr] = -INFINITY;
-            mr = fmaxf(mr, x[a2][rr]);
-          }
-        // The row's reference m_run moves only when a score passes it by
-        // more than kExtSlack (log2 units), so probabilities stay below
-        // 2^kExtSlack and the accumulators are rescaled only on the (rare)
-        // tiles where some row of the wave moves; any reference gives the same
-        // normalised result.  A row's first visible key always moves it
-        // (-inf + slack = -inf).
-        const float m_tile = max_xor16_32(mr) * scale_log2;
-        const bool bump = m_tile > m_run[rb] + kExtSlack;
-        if (__builtin_amdgcn_ballot_w64(bump) != 0) {
+          for (int rr = 0; rr < 4; ++rr) mr = fmaxf(mr, sacc[a2][rb][rr]);
+        lane_max[rb] = mr;
+        lane_bump |= mr * scale_log2 > m_run[rb] + kExtSlack;
+      }
+      if (__builtin_amdgcn_ballot_w64(lane_bump) != 0) {
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) {
+          const float m_tile = max_xor16_32(lane_max[rb]) * scale_log2;
+          const bool bump = m_tile > m_run[rb] + kExtSlack;  // the same in the row's four lanes
           const float alpha = bump ? fast_exp2(m_run[rb] - m_tile) : 1.0f;
           m_run[rb] = bump ? m_tile : m_run[rb];
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) acc[rb][nt] *= alpha;
           acc_l[rb] *= alpha;
         }
+      }
+      bf16x8 pa[kRB][2];
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) {
         // a row that has seen no key yet keeps m = -inf: use 0 so p = 0
         const float mu = m_run[rb] == -INFINITY ? 0.f : m_run[rb];
 #pragma unroll
         for (int a2 = 0; a2 < 4; ++a2)
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr)
-            pa[rb][a2 >> 1][(a2 & 1) * 4 + rr] = (bf16)fast_exp2(fmaf(x[a2][rr], scale_log2, -mu));
+            pa[rb][a2 >> 1][(a2 & 1) * 4 + rr] = (bf16)fast_exp2(fmaf(sacc[a2][rb][rr], scale_log2, -mu));
       }
 
       // ---- O^T += V^T P^T over two 32-key halves (each V fragment serves
