@@ -165,6 +165,36 @@ def test_decode_matches_oracle(name, fmt, seed):
     assert_lse_close(lse, ref_l, case.geom.dtype, f"{name} fmt {fmt}", rows=real)
 
 
+STREAM_SHAPES = {
+    # runs each cover many whole requests (most written directly, a few cut)
+    "many_short": lambda s: W.qwen3_decode(seed=s, bs=1500, len_range=(1, 70), pool_tokens=60000, max_context=128),
+    # one request cut into a piece per run (the merge sees 100+ pieces)
+    "one_long": lambda s: W.qwen3_decode(seed=s, bs=1, len_range=(60000, 60000), pool_tokens=61000,
+                                         max_context=60032),
+    # long and short requests side by side, page-granular map
+    "mixed_ps64": lambda s: W.gqa_prefix_share(64, seed=s, bs=40, prefix=64, median=200, sigma=2.0,
+                                               clip=(1, 30000)),
+}
+
+
+@pytest.mark.parametrize("name", list(STREAM_SHAPES))
+def test_decode_stream_split_shapes(name):
+    """The bf16 decode cuts the concatenated key tiles of all requests into
+    equal runs; these shapes put many requests in one run, one request over
+    every run, and both at once."""
+    case = STREAM_SHAPES[name](7)
+    print(f"stream shape {name}: bs {case.bs}, sum L {int(case.regions['self'].kv_lens.sum())}", flush=True)
+    vals = W.make_values(case)
+    dc = DeviceCase(case, vals)
+    if case.n_new:
+        dc.store()
+    fmt = P.PKV_MAP_TOKEN_TABLE if case.geom.page_size == 1 else P.PKV_MAP_CSR
+    out, lse = dc.decode(fmt)
+    ref_o, ref_l = oracle_region(case, vals, "self")
+    assert_attn_close(out, ref_o, case.geom.dtype, name)
+    assert_lse_close(lse, ref_l, case.geom.dtype, name)
+
+
 def test_decode_formats_agree_bitwise_and_repeat():
     """The three table formats resolve to the same slots, and split
     boundaries are logical: all give identical bits, run after run."""
