@@ -208,8 +208,10 @@ int paged_decode_workspace_bytes(const pkv_pool* pool, int32_t bs, int32_t num_q
 /* One query token per request attends over its kv_lens[i] keys read through
  * `map` ([XPU] "From slots to a page table"; [BACKEND] init_forward_metadata
  * with its split plan).  Query head h reads KV head h / (num_q_heads /
- * num_kv_heads).  The keys are split into chunks of logical positions; each
- * chunk's partial result is merged by log-sum-exp, so the output does not
+ * num_kv_heads).  The keys are split at logical positions that depend only
+ * on kv_lens (bf16: the requests' 32-key tiles laid end to end and cut into
+ * equal runs, one per workgroup; f32: fixed-size chunks per request); each
+ * piece's partial result is merged by log-sum-exp, so the output does not
  * depend on where pages live.
  *   q: device [bs][num_q_heads][head_dim_qk], pool dtype.
  *   out: device [bs][num_q_heads][head_dim_v], pool dtype (round to nearest
@@ -278,7 +280,7 @@ int kv_validate(const pkv_pool* pool, const pkv_kv_map* map, const int32_t* is_d
 
 /* Record hipEvent_t `start` before and `stop` after the main attention
  * kernel of the next paged_decode_attn / paged_extend_attn call made on
- * this thread (the split-K partial kernel for decode), then forget them.
+ * this thread (the split-K kernel for decode), then forget them.
  * Pass NULLs to clear.  For measuring one kernel inside a call. */
 int pkv_set_kernel_timer(void* start_event, void* stop_event);
 
