@@ -218,6 +218,7 @@ int paged_decode_workspace_bytes(const pkv_pool* pool, int32_t bs, int32_t num_q
  *     even for bf16).
  *   lse: nullable device float[bs][num_q_heads], natural-log log-sum-exp of
  *     the scaled scores; kv_lens[i] == 0 gives out = 0 and lse = -inf.
+ *   sm_scale: the score scale, positive and finite (else PKV_EINVAL).
  *   workspace: device, >= paged_decode_workspace_bytes(), 256-byte aligned.
  *   map->fmt: TOKEN_TABLE, CSR or BLOCK_TABLE.
  * Supported: SPLIT_KV f32 or bf16 with head_dim 64 or 128 and
@@ -241,6 +242,7 @@ int paged_decode_attn(const pkv_pool* pool, int32_t layer, const void* q, int32_
  *   out: device [total_q][num_q_heads][head_dim_v]; lse nullable float
  *     [total_q][num_q_heads].  An empty key set gives out = 0, lse = -inf
  *     ([XPU] "Approach 2" empty-KV guard).
+ *   sm_scale: the score scale, positive and finite (else PKV_EINVAL).
  *   map->fmt: any; CONTIGUOUS is the ragged (varlen) variant.
  * Supported: SPLIT_KV bf16, head_dim 64 or 128. */
 int paged_extend_attn(const pkv_pool* pool, int32_t layer, const void* q, int64_t total_q, const int32_t* qo_indptr,

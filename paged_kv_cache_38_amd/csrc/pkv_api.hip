@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <cmath>
 #include <new>
 #include <string>
 
@@ -302,6 +303,7 @@ int paged_decode_attn(const pkv_pool* pool, int32_t layer, const void* q, int32_
     return fail(PKV_EUNSUPPORTED, "no decode kernel for this pool (dtype %d, dims %d/%d, %d q heads over %d kv heads)",
                 pool->desc.dtype, pool->desc.head_dim_qk, pool->desc.head_dim_v, num_q_heads,
                 pool->desc.num_kv_heads);
+  if (!(sm_scale > 0.0f) || std::isinf(sm_scale)) return fail(PKV_EINVAL, "sm_scale must be positive and finite");
   if (map->bs == 0) return ok();
   if (!q || !out) return fail(PKV_EINVAL, "null q or out");
   if (!aligned16(q)) return fail(PKV_EALIGN, "q must be 16-byte aligned");
@@ -326,6 +328,7 @@ int paged_extend_attn(const pkv_pool* pool, int32_t layer, const void* q, int64_
     return fail(PKV_EINVAL, "num_q_heads %d not a positive multiple of num_kv_heads %d", num_q_heads,
                 pool->desc.num_kv_heads);
   if (max_q_len < 0 || total_q < 0) return fail(PKV_EINVAL, "negative max_q_len or total_q");
+  if (!(sm_scale > 0.0f) || std::isinf(sm_scale)) return fail(PKV_EINVAL, "sm_scale must be positive and finite");
   if (!pkv::extend_supported(pool->info, num_q_heads))
     return fail(PKV_EUNSUPPORTED, "no extend kernel for this pool (dtype %d, dims %d/%d)", pool->desc.dtype,
                 pool->desc.head_dim_qk, pool->desc.head_dim_v);

@@ -309,6 +309,12 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
                : "memory");
 }
+// one 16-byte chunk per lane from base + off (base uniform, in SGPRs),
+// global -> LDS at m0 + 16 * lane
+__device__ __forceinline__ void dma16_s(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
 // one dword per lane, global -> LDS at m0 + 4 * lane
 __device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
   asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(__builtin_amdgcn_readfirstlane(lds)) : "memory");

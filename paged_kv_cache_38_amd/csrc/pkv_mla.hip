@@ -40,6 +40,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "pkv_launch.h"
 
@@ -63,7 +64,9 @@ constexpr float kMlaHeadroom = 64.0f;             // log2 units a score may exce
 // With HB = 2 every K and V fragment read from LDS feeds two MFMAs.
 template <int HB, int W>
 struct MlaShape {
-  static constexpr int NI = (kMlaTileBytes / 1024) / W;  // tile DMA instructions per wave
+  static constexpr int RPW = kMlaT / W;  // tile rows moved per wave
+  static constexpr int NI = 2 * RPW;     // tile DMA instructions per wave (two per row)
+  static_assert(RPW * W == kMlaT, "rows split evenly over the waves");
 };
 
 // The P*V accumulators live in AGPRs for the whole kernel: outside the MFMAs
@@ -129,7 +132,7 @@ __global__ void __launch_bounds__(64 * W, 1) mla_decode_kernel(
     const char* kpool, const bf16* __restrict__ q, int32_t HQ, const int32_t* __restrict__ header,
     const int32_t* __restrict__ meta, float scale_log2, bf16* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ ws_o, float* __restrict__ ws_lse, int32_t* __restrict__ fallback) {
-  constexpr int NI = MlaShape<HB, W>::NI;
+  constexpr int NI = MlaShape<HB, W>::NI, RPW = MlaShape<HB, W>::RPW;
   constexpr int NK = kMlaQK / 32;  // 18 k-steps of the score product
   constexpr int NC = kMlaV / 16;   // 32 column blocks of the output
 
@@ -146,22 +149,33 @@ __global__ void __launch_bounds__(64 * W, 1) mla_decode_kernel(
   const int hw = w * HB * 16;  // first head of this wave
 
   // ---- loaders (every wave issues the same number of each, in the same order)
+  auto tile_slots = [&](int r) -> int32_t {  // lane l: slot of row l % 32 of tile r
+    return meta_lds[w][r & (kMlaMetaRing - 1)][lane & 31];
+  };
   auto meta_dma = [&](int r) {
     const int g = G0 + min(r, n - 1);
     dma4(meta + (int64_t)g * kMlaMetaWords + min(lane, kMlaMetaWords - 1), lds_off(&meta_lds[w][r & (kMlaMetaRing - 1)][0]));
   };
-  auto tile_dma = [&](int r) {
-    const int32_t* ms = &meta_lds[w][r & (kMlaMetaRing - 1)][0];
+  // Each of the tile's 32 rows (72 chunks, 1152 B) moves as one 64-lane
+  // DMA (LDS positions 0..63) plus one 8-lane DMA (64..71); wave w moves
+  // rows w, w + W, ...  The row's address is uniform (SGPRs, from the slot
+  // list through v_readlane) and lane l fetches global chunk p ^ (row & 7)
+  // for LDS position p: the tile's swizzle costs one XOR per row.  Part p of
+  // 3 issues rows [p RPW / 3, (p + 1) RPW / 3) of the wave: the main loop
+  // spreads a tile's DMAs over its phases.
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  auto tile_dma = [&](int r, int32_t vslot, auto part_c) {
+    constexpr int p = decltype(part_c)::value;
     char* buf = tiles[r % kMlaBufs];
-    int ln = lane;
-    asm volatile("" : "+v"(ln));  // recompute the per-lane positions every tile instead of holding them
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int pos = (w * NI + j) * 64 + ln;  // 16-byte chunk position in the tile
-      const int t = pos / kMlaRowChunks;
-      const int c = (pos - t * kMlaRowChunks) ^ (t & 7);
-      const int64_t slot = ms[t];
-      dma16(kpool + slot * kMlaRowBytes + c * 16, lds_off(buf + (w * NI + j) * 1024));
+    for (int k = p * RPW / 3; k < (p + 1) * RPW / 3; ++k) {
+      const int t = k * W + wu;
+      const int32_t slot = __builtin_amdgcn_readlane(vslot, t);
+      const char* row = kpool + (int64_t)slot * kMlaRowBytes;
+      const uint32_t sw = (uint32_t)(t & 7) << 4;
+      char* dst = buf + t * kMlaRowBytes;
+      dma16_s(row, ((uint32_t)lane << 4) ^ sw, lds_off(dst));
+      if (lane < 8) dma16_s(row, (((uint32_t)lane + 64) << 4) ^ sw, lds_off(dst + 1024));
     }
   };
 
@@ -172,6 +186,7 @@ __global__ void __launch_bounds__(64 * W, 1) mla_decode_kernel(
     for (int b = 0; b < NC; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
   bf16x8 qf[HB][NK];
   float m_ref[HB], l_part[HB];
+  float s_over[HB];  // raw score above which P could overflow (kMlaHeadroom past the reference)
 
   // Per iteration r a wave issues meta(r + 6) then tile(r + 3); tile(r) is
   // then followed in the queue by meta(r + 4), tile(r + 1), meta(r + 5),
@@ -185,14 +200,19 @@ __global__ void __launch_bounds__(64 * W, 1) mla_decode_kernel(
 #pragma unroll
   for (int k = 0; k < 3; ++k) {
     meta_dma(k + 3);
-    tile_dma(k);
+    const int32_t vs = tile_slots(k);
+    tile_dma(k, vs, std::integral_constant<int, 0>{});
+    tile_dma(k, vs, std::integral_constant<int, 1>{});
+    tile_dma(k, vs, std::integral_constant<int, 2>{});
   }
 
   for (int r = 0; r < n; ++r) {
     meta_dma(r + 6);
     wait_vm<kWait>();   // tile(r) (and every meta before it) has landed
     __syncthreads();    // tile r visible to all waves; every wave is past tile r - 1
-    tile_dma(r + 3);    // into the buffer tile r - 1 used
+    // tile r + 3 goes into the buffer tile r - 1 used, in three parts
+    const int32_t vs_next = tile_slots(r + 3);
+    tile_dma(r + 3, vs_next, std::integral_constant<int, 0>{});
 
     const int32_t* info = &meta_lds[w][r & (kMlaMetaRing - 1)][32];
     const int i = __builtin_amdgcn_readfirstlane(info[0]);
@@ -213,6 +233,11 @@ __global__ void __launch_bounds__(64 * W, 1) mla_decode_kernel(
         for (int kk = 0; kk < NK; ++kk) qf[hb][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + kk * 32));
         l_part[hb] = 0.f;
       }
+      // Wait for the queries here, once per piece.  Left pending across the
+      // branch, they would make the compiler wait on the memory counter in
+      // the score loop of every tile, where the tile DMAs (invisible to it)
+      // also count: that drains the whole tile ring each tile.
+      __builtin_amdgcn_s_waitcnt(0);
     }
 
     // ---- S^T = K Q^T for this wave's heads.  Chunk 4kk + grp of token t
@@ -251,45 +276,55 @@ __global__ void __launch_bounds__(64 * W, 1) mla_decode_kernel(
       }
     }
 
+    tile_dma(r + 3, vs_next, std::integral_constant<int, 1>{});
+
     // ---- softmax (log2 domain) for head hw + 16 hb + col; this lane holds
     // tokens 16a + 4 grp + rr, which is also the token order of P as the A
     // operand of P*V.  The reference maximum is the first tile's maximum
     // and stays fixed for the piece, so the accumulators are never
     // rescaled; a later score more than kMlaHeadroom above it (P could
     // overflow) sends the request to the exact fallback in the merge pass.
+    // keys past the request's end (its last tile only) get -inf in place
+    if (valid < kMlaT) {
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            if (16 * a + 4 * grp + rr >= valid) sacc[a][hb][rr] = -INFINITY;
+    }
+    // the scale is positive (checked at the boundary): maxima and the
+    // overflow test work on raw scores, each probability is one fma + exp2
     bool over = false;
     bf16x8 pa[HB];
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
-      float x[2][4];
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int t = 16 * a + 4 * grp + rr;
-          x[a][rr] = t < valid ? sacc[a][hb][rr] * scale_log2 : -INFINITY;
-        }
       if (seg_begin) {
         float mt = -INFINITY;
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) mt = fmaxf(mt, x[a][rr]);
-        m_ref[hb] = max_xor16_32(mt);
+          for (int rr = 0; rr < 4; ++rr) mt = fmaxf(mt, sacc[a][hb][rr]);
+        m_ref[hb] = max_xor16_32(mt) * scale_log2;
+        s_over[hb] = (m_ref[hb] + kMlaHeadroom) / scale_log2;
       }
       float ps = 0.f;
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          over |= x[a][rr] > m_ref[hb] + kMlaHeadroom;
-          const float p = fast_exp2(x[a][rr] - m_ref[hb]);
+          const float sv = sacc[a][hb][rr];
+          over |= sv > s_over[hb];
+          const float p = fast_exp2(fmaf(sv, scale_log2, -m_ref[hb]));
           ps += p;
           pa[hb][a * 4 + rr] = (bf16)p;
         }
       l_part[hb] += ps;
     }
     if (__builtin_amdgcn_ballot_w64(over) != 0 && lane == 0) fallback[i] = 1;
+
+    tile_dma(r + 3, vs_next, std::integral_constant<int, 2>{});
 
     // ---- O += P V over all columns of this wave's heads (the first tile of
     // a piece starts the accumulators from zero inside the MFMA)

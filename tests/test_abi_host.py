@@ -153,6 +153,9 @@ def test_call_argument_checks_before_launch(lib):
         assert lib.paged_decode_attn(h, 0, 0x4000, 4, C.byref(m), 0.125, 0x5000, None, None, 0, None) \
             == L.PKV_ECAPACITY
         m.fmt = L.PKV_MAP_TOKEN_TABLE
+        for bad in (0.0, -0.125, float("inf"), float("nan")):  # the kernels take the row max on raw scores
+            assert lib.paged_decode_attn(h, 0, 0x4000, 4, C.byref(m), bad, 0x5000, None, None, 0, None) \
+                == L.PKV_EINVAL
         m.bs = 0
         assert lib.paged_decode_attn(h, 0, 0x4000, 4, C.byref(m), 0.125, 0x5000, None, None, 0, None) == 0
         assert lib.pkv_set_kernel_timer(0x1, None) == L.PKV_EINVAL
