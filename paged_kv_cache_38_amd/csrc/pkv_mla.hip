@@ -49,9 +49,15 @@ namespace pkv {
 constexpr int kMlaQK = 576;
 constexpr int kMlaV = 512;
 constexpr int kMlaT = kStreamT;                   // tokens per tile
-constexpr int kMlaRowChunks = kMlaQK / 8;         // 72 sixteen-byte chunks per row
 constexpr int kMlaRowBytes = kMlaQK * 2;          // 1152
 constexpr int kMlaTileBytes = kMlaT * kMlaRowBytes;  // 36864
+// LDS tile layout: the main part holds chunks 0..63 of every row (1024 B
+// per row, values 0..511: all of V and most of K), the tail part chunks
+// 64..71 (the 64 rope values) of every row, 128 B per row, in the order the
+// waves move them.  In both, chunk c of row t sits at position c ^ (t & 7)
+// of its row (c counted from the part's first chunk).
+constexpr int kMlaMainBytes = 1024;
+constexpr int kMlaTailOff = kMlaT * kMlaMainBytes;  // 32768
 constexpr int kMlaMetaWords = kStreamMetaWords;   // per tile: 32 slot ids + 8 info words
 constexpr int kMlaBufs = 4;                       // LDS tile buffers: three tiles in flight during compute
 constexpr int kMlaMetaRing = 8;                   // per-wave ring of per-tile slot ids / info
@@ -64,9 +70,9 @@ constexpr float kMlaHeadroom = 64.0f;             // log2 units a score may exce
 // With HB = 2 every K and V fragment read from LDS feeds two MFMAs.
 template <int HB, int W>
 struct MlaShape {
-  static constexpr int RPW = kMlaT / W;  // tile rows moved per wave
-  static constexpr int NI = 2 * RPW;     // tile DMA instructions per wave (two per row)
-  static_assert(RPW * W == kMlaT, "rows split evenly over the waves");
+  static constexpr int RPW = kMlaT / W;      // tile rows moved per wave
+  static constexpr int NI = RPW + RPW / 8;   // tile DMA instructions per wave (a row each, a tail per 8 rows)
+  static_assert(RPW * W == kMlaT && RPW % 8 == 0, "rows split evenly over the waves, tails in groups of eight");
 };
 
 // The P*V accumulators live in AGPRs for the whole kernel: outside the MFMAs
@@ -77,9 +83,6 @@ __device__ __forceinline__ float acc_get(float a) {
   asm("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
   return v;
 }
-
-// byte offset of chunk c of token t inside a swizzled tile
-__device__ __forceinline__ int mla_chunk_off(int t, int c) { return (t * kMlaRowChunks + (c ^ (t & 7))) * 16; }
 
 // O += P V for one tile over all 32 column blocks of the wave's HB head
 // blocks.  The B operand of column block cb = 4 m + u comes from two
@@ -97,13 +100,13 @@ __device__ __forceinline__ void mla_pv(f32x4 (&acc)[HB][kMlaV / 16], const char*
   const char* vb[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u)
-    vb[u] = tile + (t * kMlaRowChunks + ((2 * u + ((x & 3) >> 1)) ^ (t & 7))) * 16 + (x & 1) * 8;
+    vb[u] = tile + t * kMlaMainBytes + ((2 * u + ((x & 3) >> 1)) ^ (t & 7)) * 16 + (x & 1) * 8;
   auto vload = [&](int m, bf16x8* vf) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const char* lo = vb[u] + m * 128;
       const i16x4 va = lds_read_tr16(reinterpret_cast<const bf16*>(lo));
-      const i16x4 vc = lds_read_tr16(reinterpret_cast<const bf16*>(lo + 16 * kMlaRowBytes));
+      const i16x4 vc = lds_read_tr16(reinterpret_cast<const bf16*>(lo + 16 * kMlaMainBytes));
       const bf16x4 ba = __builtin_bit_cast(bf16x4, va), bc = __builtin_bit_cast(bf16x4, vc);
       vf[u] = bf16x8{ba[0], ba[1], ba[2], ba[3], bc[0], bc[1], bc[2], bc[3]};
     }
@@ -156,13 +159,13 @@ __global__ void __launch_bounds__(64 * W, 1) mla_decode_kernel(
     const int g = G0 + min(r, n - 1);
     dma4(meta + (int64_t)g * kMlaMetaWords + min(lane, kMlaMetaWords - 1), lds_off(&meta_lds[w][r & (kMlaMetaRing - 1)][0]));
   };
-  // Each of the tile's 32 rows (72 chunks, 1152 B) moves as one 64-lane
-  // DMA (LDS positions 0..63) plus one 8-lane DMA (64..71); wave w moves
-  // rows w, w + W, ...  The row's address is uniform (SGPRs, from the slot
-  // list through v_readlane) and lane l fetches global chunk p ^ (row & 7)
-  // for LDS position p: the tile's swizzle costs one XOR per row.  Part p of
-  // 3 issues rows [p RPW / 3, (p + 1) RPW / 3) of the wave: the main loop
-  // spreads a tile's DMAs over its phases.
+  // Wave w moves rows w, w + W, ... of a tile: per row one 64-lane DMA of
+  // chunks 0..63 into the main part, from the row's address in SGPRs (slot
+  // id via v_readlane), lane l fetching chunk l ^ (row & 7); and per eight
+  // rows one 64-lane DMA of their chunks 64..71 into the tail part (lane l:
+  // row l / 8 of the group, slot via ds_bpermute).  Part p of 3 issues rows
+  // [p RPW / 3, (p + 1) RPW / 3) of the wave and, with the last part, the
+  // tail DMAs: the main loop spreads a tile's DMAs over its phases.
   const int wu = __builtin_amdgcn_readfirstlane(w);
   auto tile_dma = [&](int r, int32_t vslot, auto part_c) {
     constexpr int p = decltype(part_c)::value;
@@ -172,10 +175,17 @@ __global__ void __launch_bounds__(64 * W, 1) mla_decode_kernel(
       const int t = k * W + wu;
       const int32_t slot = __builtin_amdgcn_readlane(vslot, t);
       const char* row = kpool + (int64_t)slot * kMlaRowBytes;
-      const uint32_t sw = (uint32_t)(t & 7) << 4;
-      char* dst = buf + t * kMlaRowBytes;
-      dma16_s(row, ((uint32_t)lane << 4) ^ sw, lds_off(dst));
-      if (lane < 8) dma16_s(row, (((uint32_t)lane + 64) << 4) ^ sw, lds_off(dst + 1024));
+      dma16_s(row, ((uint32_t)lane ^ (uint32_t)(t & 7)) << 4, lds_off(buf + t * kMlaMainBytes));
+    }
+    if constexpr (p == 2) {
+#pragma unroll
+      for (int g8 = 0; g8 < RPW / 8; ++g8) {
+        const int k = g8 * 8 + (lane >> 3);
+        const int t = k * W + wu;
+        const int64_t slot = __shfl(vslot, t, 64);
+        const char* src = kpool + slot * kMlaRowBytes + (64 + ((lane & 7) ^ (t & 7))) * 16;
+        dma16(src, lds_off(buf + kMlaTailOff + (wu * RPW + g8 * 8) * 128));
+      }
     }
   };
 
@@ -240,14 +250,16 @@ __global__ void __launch_bounds__(64 * W, 1) mla_decode_kernel(
       __builtin_amdgcn_s_waitcnt(0);
     }
 
-    // ---- S^T = K Q^T for this wave's heads.  Chunk 4kk + grp of token t
-    // sits at 8 (kk / 2) + ((4 (kk & 1) + grp) ^ (t & 7)): two per-lane bases
-    // (even / odd kk) plus compile-time offsets.
+    // ---- S^T = K Q^T for this wave's heads.  Chunk 4kk + grp (kk < 16) of
+    // token t sits at 8 (kk / 2) + ((4 (kk & 1) + grp) ^ (t & 7)) of its main
+    // row: two per-lane bases (even / odd kk) plus compile-time offsets.
+    // kk = 16, 17 read the tail part, whose row of token 16a + col is
+    // ((16a + col) % W) RPW + (16a + col) / W.
     f32x4 sacc[2][HB];
     {
       const int t = col;  // token 16a + col; (t & 7) is the same for a = 0, 1
-      const char* kb_even = tile + (t * kMlaRowChunks + (grp ^ (t & 7))) * 16;
-      const char* kb_odd = tile + (t * kMlaRowChunks + ((4 + grp) ^ (t & 7))) * 16;
+      const char* kb_even = tile + t * kMlaMainBytes + (grp ^ (t & 7)) * 16;
+      const char* kb_odd = tile + t * kMlaMainBytes + ((4 + grp) ^ (t & 7)) * 16;
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -258,10 +270,20 @@ __global__ void __launch_bounds__(64 * W, 1) mla_decode_kernel(
       constexpr int KD = 3;
       bf16x8 kf[KD][2];
       auto kload = [&](int kk, bf16x8* dst) {
-        const char* kb = (kk & 1) ? kb_odd : kb_even;
+        if (kk < 16) {
+          const char* kb = (kk & 1) ? kb_odd : kb_even;
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
-          dst[a] = as_bf16x8(*reinterpret_cast<const u32x4*>(kb + a * 16 * kMlaRowBytes + (kk >> 1) * 128));
+          for (int a = 0; a < 2; ++a)
+            dst[a] = as_bf16x8(*reinterpret_cast<const u32x4*>(kb + a * 16 * kMlaMainBytes + (kk >> 1) * 128));
+        } else {
+#pragma unroll
+          for (int a = 0; a < 2; ++a) {
+            const int ta = 16 * a + col;
+            const char* tb = tile + kMlaTailOff + ((ta % W) * RPW + ta / W) * 128 +
+                             ((4 * (kk & 1) + grp) ^ (ta & 7)) * 16;
+            dst[a] = as_bf16x8(*reinterpret_cast<const u32x4*>(tb));
+          }
+        }
       };
 #pragma unroll
       for (int kk = 0; kk < KD - 1; ++kk) kload(kk, kf[kk]);
