@@ -171,6 +171,12 @@ class DecodeBench:
         self.lse = torch.empty((case.bs, g.num_q_heads), dtype=torch.float32, device=dev)
         nb = P.paged_decode_workspace_bytes(self.pool, case.bs, g.num_q_heads, self.max_len)
         self.ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+        # requests that share prefix pages read the same K/V rows: HBM has to
+        # deliver each distinct row once (the rest can come from cache)
+        self.logical_tokens = int(r.kv_lens.sum())
+        slots = [np.repeat(np.asarray(pl, np.int64) * ps, ps)[:L] + np.tile(np.arange(ps), len(pl))[:L]
+                 for pl, L in zip(r.page_lists, r.kv_lens.tolist())]
+        self.unique_tokens = int(np.unique(np.concatenate(slots)).size) if slots else 0
 
     def step(self, timers=None):
         P, c = self.P, self.case
@@ -187,13 +193,15 @@ class DecodeBench:
             P.pkv_set_kernel_timer(*timers[0])
         P.paged_decode_attn(self.pool, 0, self.q, self.map, c.sm_scale, self.out, self.lse, self.ws)
 
-    def kernel_bytes(self) -> int:
-        """Decode split kernel: each live token's K/V rows once, its slot (or
-        page id share), and the queries."""
+    def kernel_bytes(self, logical: bool = False) -> int:
+        """Decode kernel: the K/V rows of every distinct live slot once
+        (every live token's, when logical), a slot id (or page id share) per
+        token, and the queries."""
         c, g = self.case, self.case.geom
-        tok = int(c.regions["self"].kv_lens.sum())
         idx = 4 if g.page_size == 1 or self.fmt == "token_table" else 4.0 / g.page_size
-        return int(tok * (_row_bytes(g) + idx) + c.bs * g.num_q_heads * g.head_dim_qk * g.elem_bytes)
+        rows = self.logical_tokens if logical else self.unique_tokens
+        return int(rows * _row_bytes(g) + self.logical_tokens * idx +
+                   c.bs * g.num_q_heads * g.head_dim_qk * g.elem_bytes)
 
     def step_bytes(self) -> int:
         c, g = self.case, self.case.geom
@@ -319,9 +327,10 @@ class ExtendBench:
         g = self.case.geom
         return sum(self._pairs(nm) for nm in self.case.regions) * g.num_q_heads * 2 * (g.head_dim_qk + g.head_dim_v)
 
-    def kernel_bytes(self) -> int:
+    def kernel_bytes(self, logical: bool = False) -> int:
         """Both extend calls: every key row of both regions once, the queries
-        and the outputs of both calls."""
+        and the outputs of both calls (no row is shared between requests, so
+        logical and distinct bytes are the same)."""
         c, g = self.case, self.case.geom
         rows = sum(int(r.kv_lens.sum()) for r in c.regions.values())
         qo = 2 * self.total_q * g.num_q_heads * g.head_dim_qk * g.elem_bytes
@@ -404,6 +413,9 @@ def main():
     ap.add_argument("--workload", default="qwen3_decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--cold-steps", type=int, default=10,
+                    help="after the timed steps, time the kernel this many more times with the caches "
+                         "cleared (a 1 GiB read) before each step; reported as roofline.kernel_ms_cold")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run a plain 256 MiB device copy three times (a known-size reference "
                          "for HBM byte counters)")
@@ -457,6 +469,31 @@ def main():
                  "flop_per_byte": round(intensity, 2)})
     if b.attn_calls > 1:
         roof["call_ms"] = [round(float(np.mean([c[k] for c in call_ms])), 5) for k in range(b.attn_calls)]
+    if b.kernel_bytes(logical=True) != b.kernel_bytes():
+        # shared prefix pages: the kernel reads more rows than there are
+        # distinct ones; the roofline counts each distinct row once
+        lb = b.kernel_bytes(logical=True)
+        roof.update({"kernel_logical_bytes": lb, "kernel_logical_gbs": round(lb / (k_ms * 1e-3) / 1e9, 2)})
+    if args.cold_steps > 0:
+        # the same kernel with the caches cleared first: a 1 GiB buffer is
+        # read before each step (MALL and L2 are smaller; reading leaves no
+        # dirty lines to write back during the kernel), outside the events
+        # that time the kernel
+        flush = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
+        cold = [[(ev.create(), ev.create()) for _ in range(b.attn_calls)] for _ in range(args.cold_steps)]
+        for k in range(args.cold_steps):
+            flush.sum()
+            b.step(cold[k])
+        torch.cuda.synchronize()
+        cold_ms = float(np.mean([sum(ev.elapsed_ms(a, z) for a, z in st) for st in cold]))
+        for st in cold:
+            for a, z in st:
+                ev.destroy(a)
+                ev.destroy(z)
+        del flush
+        cold_gbs = b.kernel_bytes() / (cold_ms * 1e-3) / 1e9
+        roof.update({"kernel_ms_cold": round(cold_ms, 5), "kernel_gbs_cold": round(cold_gbs, 2),
+                     "kernel_hbm_frac_cold": round(cold_gbs / HBM_PEAK_GBS, 4)})
     res = {
         "metric": "paged decode attn: achieved HBM GB/s (% of peak) + decode tokens/s, 1 GPU",
         "value": round(step_gbs, 2),
