@@ -52,3 +52,13 @@ from .indices import (  # noqa: F401
     in_page_contiguous,
 )
 from .attention import attend, paged_attention, merge_partials, gather  # noqa: F401
+from .alloc import (  # noqa: F401
+    FreeRing,
+    new_pages_needed,
+    alloc,
+    alloc_extend,
+    alloc_decode,
+    free_pages,
+    pages_of_slots,
+    write_req_to_token,
+)
