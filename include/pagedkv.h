@@ -6,7 +6,8 @@
  * (scatter of new tokens' K/V into their slots), index building (token table
  * -> page-granular CSR or padded block table), paged decode attention
  * (split-K over pages with a log-sum-exp merge), paged extend/prefill over a
- * paged prefix, and the ragged gather.
+ * paged prefix, and the ragged gather; plus the device-side slot
+ * allocator (a free list of pages) and the writing of request rows.
  *
  * Sources, cited by short name:
  *   [XPU]     "Enabling Encoder-Decoder Models on Intel XPU in SGLang: A KV-Cache Story"
@@ -261,6 +262,96 @@ int paged_extend_attn(const pkv_pool* pool, int32_t layer, const void* q, int64_
  *     LATENT), 16-byte aligned. */
 int kv_gather(const pkv_pool* pool, int32_t layer, const pkv_kv_map* map, const int32_t* cu_seqlens_k,
               void* k_out, void* v_out, int64_t out_rows, void* stream);
+
+/* ---- slot allocation and row writing ------------------------------------ */
+
+/* Device free list of pages ([XPU] "How SGLang stores the KV cache: two
+ * pools and a page size": the token allocator's free list of slots and the
+ * paged allocator's free list of page ids; at page_size 1 a page is a slot).
+ * It is a ring the caller owns:
+ *   free_pages: device int32[capacity] of page ids.
+ *   free_state: device int32[2] = {head, size}; the free entries, front
+ *     first, are free_pages[(head + k) % capacity] for k < size.
+ *   status: device int32, written by every call below (PKV_ALLOC_*).  A call
+ *     that is not granted changes neither the ring nor its outputs.
+ * Allocation takes entries from the front in order; freeing appends at the
+ * back.  Calls on one ring must be ordered on one stream (overlapping calls
+ * race).  Each call is a fixed sequence of kernel launches with no host
+ * synchronisation and no memset, so it may be captured in a graph; the
+ * caller reads `status` when it next synchronises. */
+#define PKV_ALLOC_OK 0
+#define PKV_ALLOC_NO_SPACE 1     /* fewer free pages than needed (the pages' None) */
+#define PKV_ALLOC_OUT_CAPACITY 2 /* more new tokens than out_capacity */
+#define PKV_ALLOC_BAD_LENGTHS 3  /* some prefix_len < 0 or seq_len < prefix_len */
+#define PKV_ALLOC_RING_FULL 4    /* free: the pages do not fit in the ring */
+
+/* free_pages[k] = first + k for k < count, free_state = {0, count} (the
+ * pages' clear(): at page_size 1 the free list 1 .. size skips slot 0;
+ * with this library's pool, whose padding page is the last one, first = 0
+ * and count = num_pages).  count <= capacity (PKV_ECAPACITY). */
+int kv_free_list_init(int32_t* free_pages, int32_t capacity, int32_t first, int32_t count, int32_t* free_state,
+                      void* stream);
+
+/* Page-aligned alloc ([XPU] paged allocator alloc(); [BACKEND] opening
+ * table, page-aligned allocation row): the first need / page_size free pages,
+ * page p expanded to slots p * page_size + 0 .. page_size - 1, written to
+ * out (device int32[need]).  need must be a multiple of page_size
+ * (PKV_EINVAL); page_size a power of two <= 128. */
+int kv_alloc(int32_t page_size, int64_t need, int32_t* free_pages, int32_t capacity, int32_t* free_state,
+             int32_t* out, int32_t* status, void* stream);
+
+/* Growth path ([XPU] paged allocator alloc_extend): request i grows from
+ * prefix_lens[i] to seq_lens[i] tokens.  Its new tokens first fill the rest
+ * of its partly used last page (the slots after last_loc[i], the slot of
+ * its last cached token), then take whole pages from the front of the free
+ * list, request after request, so every page holds consecutive logical
+ * positions.  out_cache_loc (device int32[out_capacity]) receives the new
+ * slots of request 0, then request 1, ...; entries past the total are not
+ * written.
+ *   prefix_lens, seq_lens: device int32[bs]; bs <= 8000 (PKV_EUNSUPPORTED).
+ *   last_loc: device int32[bs], read only for requests whose prefix ends
+ *     inside a page; may be NULL when page_size == 1.
+ * Denied (status set, nothing written) when the batch needs more pages than
+ * are free, more slots than out_capacity, or has invalid lengths. */
+int kv_alloc_extend(int32_t page_size, int32_t bs, const int32_t* prefix_lens, const int32_t* seq_lens,
+                    const int32_t* last_loc, int32_t* free_pages, int32_t capacity, int32_t* free_state,
+                    int32_t* out_cache_loc, int64_t out_capacity, int32_t* status, void* stream);
+
+/* Decode growth ([XPU] paged allocator alloc_decode): kv_alloc_extend with
+ * prefix_lens = seq_lens - 1, one slot per request into out_cache_loc
+ * (device int32[bs]).  seq_lens[i] >= 1 (else PKV_ALLOC_BAD_LENGTHS). */
+int kv_alloc_decode(int32_t page_size, int32_t bs, const int32_t* seq_lens, const int32_t* last_loc,
+                    int32_t* free_pages, int32_t capacity, int32_t* free_state, int32_t* out_cache_loc,
+                    int32_t* status, void* stream);
+
+/* Free ([XPU] paged allocator free): the distinct pages slots[0 .. n) lie on
+ * (slot / page_size), in increasing page order, are appended to the back of
+ * the free list.  Negative slots and pages >= num_pages (the padding page)
+ * are ignored.  page_bitmap: device uint32[(num_pages + 31) / 32] the call
+ * uses as scratch (its contents on entry do not matter).  Denied with
+ * PKV_ALLOC_RING_FULL when the pages do not fit in the ring. */
+int kv_free(int32_t page_size, const int32_t* slots, int64_t n, int32_t num_pages, int32_t* free_pages,
+            int32_t capacity, int32_t* free_state, uint32_t* page_bitmap, int32_t* status, void* stream);
+
+/* write_cache_indices ([XPU] "How SGLang stores the KV cache", the two
+ * writes per request and the one-program-per-request kernel): row
+ * req_pool_indices[i] of req_to_token (device int32[table_rows][table_width])
+ * gets prefix slots in columns [0, prefix_lens[i]) and its new slots in
+ * [prefix_lens[i], seq_lens[i]), the latter from out_cache_loc (device
+ * int32[n_out]) after the new tokens of requests 0 .. i-1.
+ *   prefix_ptrs: nullable device array of bs device pointers; entry i (may be
+ *     NULL) points at request i's int32[prefix_lens[i]] prefix slots.  A NULL
+ *     array or entry leaves those columns as they are (e.g. a chunked prefill
+ *     continuing its own row, or decode).
+ *   max_seq_len: host bound >= every seq_lens[i], <= table_width.
+ * A request whose lengths are invalid (prefix < 0, seq < prefix) writes
+ * nothing and counts no new tokens; one whose row is out of range or whose
+ * seq_len exceeds table_width writes nothing; reads of out_cache_loc past
+ * n_out are skipped. */
+int write_req_to_token(int32_t* req_to_token, int64_t table_rows, int64_t table_width,
+                       const int32_t* req_pool_indices, const int32_t* prefix_lens, const int32_t* seq_lens,
+                       const int32_t* out_cache_loc, int64_t n_out, const int32_t* const* prefix_ptrs, int32_t bs,
+                       int32_t max_seq_len, void* stream);
 
 /* ---- debug / measurement (off the hot path) ------------------------------ */
 

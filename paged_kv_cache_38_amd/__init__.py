@@ -25,6 +25,11 @@ from ._lib import (  # noqa: F401
     PKV_MAP_CONTIGUOUS,
     PKV_MAP_CSR,
     PKV_MAP_TOKEN_TABLE,
+    PKV_ALLOC_BAD_LENGTHS,
+    PKV_ALLOC_NO_SPACE,
+    PKV_ALLOC_OK,
+    PKV_ALLOC_OUT_CAPACITY,
+    PKV_ALLOC_RING_FULL,
     PagedKVError,
 )
 
@@ -32,6 +37,8 @@ __all__ = [
     "Pool", "KVMap", "kv_pool_bytes", "kv_pool_create", "kv_pool_destroy", "kv_pool_padding_page",
     "kv_pool_token_bytes", "kv_store", "build_kv_indices", "make_kv_map", "paged_decode_workspace_bytes",
     "paged_decode_attn", "paged_extend_attn", "kv_gather", "kv_validate", "pkv_set_kernel_timer", "library",
+    "FreeList", "kv_free_list_create", "kv_free_list_init", "kv_alloc", "kv_alloc_extend", "kv_alloc_decode",
+    "kv_free", "write_req_to_token",
 ]
 
 _DTYPES = {torch.float32: PKV_DTYPE_F32, torch.bfloat16: PKV_DTYPE_BF16}
@@ -254,6 +261,113 @@ def paged_extend_attn(pool: Pool, layer: int, q: torch.Tensor, qo_indptr: torch.
                                        C.byref(kv_map.struct), 1 if causal else 0, float(sm_scale),
                                        _dev(out, "out", pool.dtype), _dev(lse, "lse", torch.float32),
                                        _stream(stream)), "paged_extend_attn")
+
+
+# ---------------------------------------------------------------------------
+# slot allocation and row writing
+# ---------------------------------------------------------------------------
+
+@dataclass
+class FreeList:
+    """The device tensors of one free list of pages: the ring of page ids,
+    its {head, size} state, the status word every call writes, and the page
+    bitmap kv_free uses as scratch."""
+    page_size: int
+    num_pages: int
+    pages: torch.Tensor   # int32[capacity]
+    state: torch.Tensor   # int32[2]
+    status: torch.Tensor  # int32[1]
+    bitmap: torch.Tensor  # int32[(num_pages + 31) // 32], read as uint32
+
+    @property
+    def capacity(self) -> int:
+        return self.pages.numel()
+
+    def _ptrs(self):
+        i32 = torch.int32
+        return (_dev(self.pages, "free_pages", i32), self.capacity, _dev(self.state, "free_state", i32))
+
+
+def kv_free_list_create(page_size: int, num_pages: int, capacity: Optional[int] = None, first: int = 0,
+                        count: Optional[int] = None, device="cuda", stream=None) -> FreeList:
+    """Allocate the tensors of a free list (capacity defaults to num_pages)
+    and initialise it to pages first .. first + count - 1 (count defaults to
+    num_pages)."""
+    cap = num_pages if capacity is None else capacity
+    i32 = torch.int32
+    fl = FreeList(page_size, num_pages, torch.empty(cap, dtype=i32, device=device),
+                  torch.empty(2, dtype=i32, device=device), torch.zeros(1, dtype=i32, device=device),
+                  torch.empty((num_pages + 31) // 32, dtype=i32, device=device))
+    kv_free_list_init(fl, first, num_pages if count is None else count, stream)
+    return fl
+
+
+def kv_free_list_init(fl: FreeList, first: int, count: int, stream=None) -> None:
+    L.check(L.load().kv_free_list_init(_dev(fl.pages, "free_pages", torch.int32), fl.capacity, int(first),
+                                       int(count), _dev(fl.state, "free_state", torch.int32), _stream(stream)),
+            "kv_free_list_init")
+
+
+def kv_alloc(fl: FreeList, need: int, out: torch.Tensor, stream=None) -> None:
+    if out.numel() < need:
+        raise ValueError("out holds fewer than need slots")
+    L.check(L.load().kv_alloc(fl.page_size, int(need), *fl._ptrs(), _dev(out, "out", torch.int32),
+                              _dev(fl.status, "status", torch.int32), _stream(stream)), "kv_alloc")
+
+
+def kv_alloc_extend(fl: FreeList, prefix_lens: torch.Tensor, seq_lens: torch.Tensor,
+                    last_loc: Optional[torch.Tensor], out_cache_loc: torch.Tensor, stream=None) -> None:
+    i32 = torch.int32
+    bs = seq_lens.numel()
+    if prefix_lens.numel() != bs or (last_loc is not None and last_loc.numel() != bs):
+        raise ValueError("prefix_lens, seq_lens and last_loc must have bs entries")
+    L.check(L.load().kv_alloc_extend(fl.page_size, bs, _dev(prefix_lens, "prefix_lens", i32),
+                                     _dev(seq_lens, "seq_lens", i32), _dev(last_loc, "last_loc", i32), *fl._ptrs(),
+                                     _dev(out_cache_loc, "out_cache_loc", i32), out_cache_loc.numel(),
+                                     _dev(fl.status, "status", i32), _stream(stream)), "kv_alloc_extend")
+
+
+def kv_alloc_decode(fl: FreeList, seq_lens: torch.Tensor, last_loc: Optional[torch.Tensor],
+                    out_cache_loc: torch.Tensor, stream=None) -> None:
+    i32 = torch.int32
+    bs = seq_lens.numel()
+    if out_cache_loc.numel() < bs or (last_loc is not None and last_loc.numel() != bs):
+        raise ValueError("out_cache_loc and last_loc must have bs entries")
+    L.check(L.load().kv_alloc_decode(fl.page_size, bs, _dev(seq_lens, "seq_lens", i32),
+                                     _dev(last_loc, "last_loc", i32), *fl._ptrs(),
+                                     _dev(out_cache_loc, "out_cache_loc", i32), _dev(fl.status, "status", i32),
+                                     _stream(stream)), "kv_alloc_decode")
+
+
+def kv_free(fl: FreeList, slots: torch.Tensor, stream=None) -> None:
+    i32 = torch.int32
+    L.check(L.load().kv_free(fl.page_size, _dev(slots, "slots", i32), slots.numel(), fl.num_pages, *fl._ptrs(),
+                             _dev(fl.bitmap, "page_bitmap", i32), _dev(fl.status, "status", i32),
+                             _stream(stream)), "kv_free")
+
+
+def write_req_to_token(req_to_token: torch.Tensor, req_pool_indices: torch.Tensor, prefix_lens: torch.Tensor,
+                       seq_lens: torch.Tensor, out_cache_loc: torch.Tensor, max_seq_len: int,
+                       prefix_ptrs=None, stream=None) -> None:
+    """prefix_ptrs: None, a device int64 tensor of bs pointers, or a list of
+    bs int32 device tensors / None (their addresses are copied to the
+    device here; the tensors must stay alive until the work is done)."""
+    i32 = torch.int32
+    bs = req_pool_indices.numel()
+    ptrs = prefix_ptrs
+    if isinstance(prefix_ptrs, (list, tuple)):
+        if len(prefix_ptrs) != bs:
+            raise ValueError("prefix_ptrs must have bs entries")
+        addrs = [0 if t is None else _dev(t, "prefix slots", i32) for t in prefix_ptrs]
+        ptrs = torch.tensor(addrs, dtype=torch.int64).to(req_to_token.device)
+        if stream is not None:  # keep the pointer array alive for the kernel's stream
+            ptrs.record_stream(torch.cuda.ExternalStream(_stream(stream)))
+    rows, width = req_to_token.shape
+    L.check(L.load().write_req_to_token(
+        _dev(req_to_token, "req_to_token", i32), rows, width, _dev(req_pool_indices, "req_pool_indices", i32),
+        _dev(prefix_lens, "prefix_lens", i32), _dev(seq_lens, "seq_lens", i32),
+        _dev(out_cache_loc, "out_cache_loc", i32), out_cache_loc.numel(),
+        _dev(ptrs, "prefix_ptrs", torch.int64), bs, int(max_seq_len), _stream(stream)), "write_req_to_token")
 
 
 # ---------------------------------------------------------------------------

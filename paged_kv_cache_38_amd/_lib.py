@@ -26,6 +26,12 @@ PKV_MAP_CSR = 1
 PKV_MAP_BLOCK_TABLE = 2
 PKV_MAP_CONTIGUOUS = 3
 
+PKV_ALLOC_OK = 0
+PKV_ALLOC_NO_SPACE = 1
+PKV_ALLOC_OUT_CAPACITY = 2
+PKV_ALLOC_BAD_LENGTHS = 3
+PKV_ALLOC_RING_FULL = 4
+
 
 class PoolDesc(C.Structure):
     _fields_ = [
@@ -90,6 +96,17 @@ SIGNATURES = {
     "kv_validate": (C.c_int, [C.c_void_p, C.POINTER(KVMapStruct), C.c_void_p, C.c_void_p,
                               C.POINTER(C.c_int64), C.c_void_p]),
     "pkv_set_kernel_timer": (C.c_int, [C.c_void_p, C.c_void_p]),
+    "kv_free_list_init": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]),
+    "kv_alloc": (C.c_int, [C.c_int32, C.c_int64, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
+                           C.c_void_p]),
+    "kv_alloc_extend": (C.c_int, [C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
+                                  C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p]),
+    "kv_alloc_decode": (C.c_int, [C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p,
+                                  C.c_void_p, C.c_void_p, C.c_void_p]),
+    "kv_free": (C.c_int, [C.c_int32, C.c_void_p, C.c_int64, C.c_int32, C.c_void_p, C.c_int32, C.c_void_p,
+                          C.c_void_p, C.c_void_p, C.c_void_p]),
+    "write_req_to_token": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p,
+                                     C.c_void_p, C.c_int64, C.c_void_p, C.c_int32, C.c_int32, C.c_void_p]),
 }
 
 _lib = None

@@ -357,6 +357,99 @@ int kv_gather(const pkv_pool* pool, int32_t layer, const pkv_kv_map* map, const 
                        "kv_gather");
 }
 
+int kv_free_list_init(int32_t* free_pages, int32_t capacity, int32_t first, int32_t count, int32_t* free_state,
+                      void* stream) {
+  if (!free_pages || !free_state) return fail(PKV_EINVAL, "null free list or state");
+  if (capacity <= 0 || count < 0 || first < 0) return fail(PKV_EINVAL, "capacity must be positive, count and first >= 0");
+  if (count > capacity) return fail(PKV_ECAPACITY, "count %d > capacity %d", count, capacity);
+  if ((int64_t)first + count > INT32_MAX) return fail(PKV_EINVAL, "page ids past INT32_MAX");
+  return device_status(pkv::launch_free_list_init(free_pages, first, count, free_state, (hipStream_t)stream),
+                       "kv_free_list_init");
+}
+
+namespace {
+int check_ring(int32_t page_size, const int32_t* free_pages, int32_t capacity, const int32_t* free_state,
+               const int32_t* status) {
+  if (!pow2(page_size) || page_size > 128) return fail(PKV_EUNSUPPORTED, "page_size %d", page_size);
+  if (!free_pages || !free_state || !status) return fail(PKV_EINVAL, "null free list, state or status");
+  if (capacity <= 0) return fail(PKV_EINVAL, "free list capacity must be positive");
+  return ok();
+}
+}  // namespace
+
+int kv_alloc(int32_t page_size, int64_t need, int32_t* free_pages, int32_t capacity, int32_t* free_state,
+             int32_t* out, int32_t* status, void* stream) {
+  if (int st = check_ring(page_size, free_pages, capacity, free_state, status)) return st;
+  if (need < 0 || need % page_size != 0)
+    return fail(PKV_EINVAL, "need %lld is not a non-negative multiple of page_size %d", (long long)need, page_size);
+  if (need > INT32_MAX) return fail(PKV_EINVAL, "need %lld past INT32_MAX", (long long)need);
+  if (need > 0 && !out) return fail(PKV_EINVAL, "null out");
+  return device_status(pkv::launch_alloc_pages(ilog2(page_size), need / page_size, free_pages, capacity, free_state,
+                                               out, status, (hipStream_t)stream),
+                       "kv_alloc");
+}
+
+namespace {
+int alloc_growth(const char* call, int32_t page_size, int32_t bs, const int32_t* prefix_lens, const int32_t* seq_lens,
+                 const int32_t* last_loc, int32_t* free_pages, int32_t capacity, int32_t* free_state,
+                 int32_t* out_cache_loc, int64_t out_capacity, int32_t* status, void* stream) {
+  if (int st = check_ring(page_size, free_pages, capacity, free_state, status)) return st;
+  if (bs < 0 || out_capacity < 0) return fail(PKV_EINVAL, "negative bs or out_capacity");
+  if (bs > pkv::kMaxAllocBatch) return fail(PKV_EUNSUPPORTED, "bs %d > %d", bs, pkv::kMaxAllocBatch);
+  if (out_capacity > INT32_MAX) return fail(PKV_EINVAL, "out_capacity past INT32_MAX");
+  if (bs > 0 && (!seq_lens || !out_cache_loc)) return fail(PKV_EINVAL, "null seq_lens or out_cache_loc");
+  if (bs > 0 && page_size > 1 && !last_loc) return fail(PKV_EINVAL, "page_size > 1 needs last_loc");
+  return device_status(pkv::launch_alloc_extend(ilog2(page_size), bs, prefix_lens, seq_lens, last_loc, free_pages,
+                                                capacity, free_state, out_cache_loc, out_capacity, status,
+                                                (hipStream_t)stream),
+                       call);
+}
+}  // namespace
+
+int kv_alloc_extend(int32_t page_size, int32_t bs, const int32_t* prefix_lens, const int32_t* seq_lens,
+                    const int32_t* last_loc, int32_t* free_pages, int32_t capacity, int32_t* free_state,
+                    int32_t* out_cache_loc, int64_t out_capacity, int32_t* status, void* stream) {
+  if (bs > 0 && !prefix_lens) return fail(PKV_EINVAL, "null prefix_lens");
+  return alloc_growth("kv_alloc_extend", page_size, bs, prefix_lens, seq_lens, last_loc, free_pages, capacity,
+                      free_state, out_cache_loc, out_capacity, status, stream);
+}
+
+int kv_alloc_decode(int32_t page_size, int32_t bs, const int32_t* seq_lens, const int32_t* last_loc,
+                    int32_t* free_pages, int32_t capacity, int32_t* free_state, int32_t* out_cache_loc,
+                    int32_t* status, void* stream) {
+  return alloc_growth("kv_alloc_decode", page_size, bs, nullptr, seq_lens, last_loc, free_pages, capacity, free_state,
+                      out_cache_loc, bs, status, stream);
+}
+
+int kv_free(int32_t page_size, const int32_t* slots, int64_t n, int32_t num_pages, int32_t* free_pages,
+            int32_t capacity, int32_t* free_state, uint32_t* page_bitmap, int32_t* status, void* stream) {
+  if (int st = check_ring(page_size, free_pages, capacity, free_state, status)) return st;
+  if (n < 0 || num_pages <= 0) return fail(PKV_EINVAL, "negative n or non-positive num_pages");
+  if (n > 0 && !slots) return fail(PKV_EINVAL, "null slots");
+  if (!page_bitmap) return fail(PKV_EINVAL, "null page_bitmap");
+  return device_status(pkv::launch_free(ilog2(page_size), slots, n, num_pages, free_pages, capacity, free_state,
+                                        page_bitmap, status, (hipStream_t)stream),
+                       "kv_free");
+}
+
+int write_req_to_token(int32_t* req_to_token, int64_t table_rows, int64_t table_width,
+                       const int32_t* req_pool_indices, const int32_t* prefix_lens, const int32_t* seq_lens,
+                       const int32_t* out_cache_loc, int64_t n_out, const int32_t* const* prefix_ptrs, int32_t bs,
+                       int32_t max_seq_len, void* stream) {
+  if (bs < 0 || max_seq_len < 0 || n_out < 0) return fail(PKV_EINVAL, "negative bs, max_seq_len or n_out");
+  if (table_rows <= 0 || table_width <= 0) return fail(PKV_EINVAL, "token table dims must be positive");
+  if (bs > 0 && (!req_to_token || !req_pool_indices || !prefix_lens || !seq_lens))
+    return fail(PKV_EINVAL, "null table, indices or lengths");
+  if (n_out > 0 && !out_cache_loc) return fail(PKV_EINVAL, "null out_cache_loc");
+  if (max_seq_len > table_width) return fail(PKV_EINVAL, "max_seq_len %d > table_width %lld", max_seq_len,
+                                             (long long)table_width);
+  if (((int64_t)max_seq_len + 1023) / 1024 > 65535) return fail(PKV_EUNSUPPORTED, "max_seq_len %d", max_seq_len);
+  return device_status(pkv::launch_write_rows(req_to_token, table_rows, table_width, req_pool_indices, prefix_lens,
+                                              seq_lens, out_cache_loc, n_out, prefix_ptrs, bs, max_seq_len,
+                                              (hipStream_t)stream),
+                       "write_req_to_token");
+}
+
 int kv_validate(const pkv_pool* pool, const pkv_kv_map* map, const int32_t* is_dummy, int64_t* scratch,
                 int64_t counts[8], void* stream) {
   if (int st = check_pool(pool)) return st;

@@ -172,3 +172,42 @@ def test_unsupported_decode_shapes_are_rejected(lib):
         assert lib.paged_decode_workspace_bytes(h, 4, 4, 100, C.byref(ws)) == L.PKV_EUNSUPPORTED
     finally:
         lib.kv_pool_destroy(h)
+
+
+def test_allocator_argument_checks_before_launch(lib):
+    ring, state, status, out = 0x1000, 0x2000, 0x3000, 0x4000
+    assert lib.kv_free_list_init(None, 8, 0, 8, state, None) == L.PKV_EINVAL
+    assert lib.kv_free_list_init(ring, 8, 0, 9, state, None) == L.PKV_ECAPACITY
+    assert lib.kv_free_list_init(ring, 0, 0, 0, state, None) == L.PKV_EINVAL
+    assert lib.kv_free_list_init(ring, 8, -1, 8, state, None) == L.PKV_EINVAL
+    assert lib.kv_free_list_init(ring, 8, 2**31 - 4, 8, state, None) == L.PKV_EINVAL
+    # page-aligned alloc: need a multiple of page_size, page_size a power of two
+    assert lib.kv_alloc(16, 17, ring, 8, state, out, status, None) == L.PKV_EINVAL
+    assert lib.kv_alloc(16, -16, ring, 8, state, out, status, None) == L.PKV_EINVAL
+    assert lib.kv_alloc(12, 24, ring, 8, state, out, status, None) == L.PKV_EUNSUPPORTED
+    assert lib.kv_alloc(256, 256, ring, 8, state, out, status, None) == L.PKV_EUNSUPPORTED
+    assert lib.kv_alloc(16, 32, ring, 8, state, out, None, None) == L.PKV_EINVAL
+    assert lib.kv_alloc(16, 32, ring, 8, state, None, status, None) == L.PKV_EINVAL
+    # growth paths
+    lens = 0x5000
+    assert lib.kv_alloc_extend(16, 4, None, lens, lens, ring, 8, state, out, 64, status, None) == L.PKV_EINVAL
+    assert lib.kv_alloc_extend(16, 4, lens, lens, None, ring, 8, state, out, 64, status, None) == L.PKV_EINVAL
+    assert lib.kv_alloc_extend(16, 4, lens, lens, lens, ring, 8, state, out, -1, status, None) == L.PKV_EINVAL
+    assert lib.kv_alloc_extend(16, 4, lens, lens, lens, ring, 8, state, out, 2**31, status, None) == L.PKV_EINVAL
+    assert lib.kv_alloc_extend(16, 8001, lens, lens, lens, ring, 8, state, out, 64, status, None) \
+        == L.PKV_EUNSUPPORTED
+    assert lib.kv_alloc_extend(16, 4, lens, lens, lens, ring, 0, state, out, 64, status, None) == L.PKV_EINVAL
+    assert lib.kv_alloc_decode(16, 4, lens, None, ring, 8, state, out, status, None) == L.PKV_EINVAL
+    assert lib.kv_alloc_decode(16, -1, lens, lens, ring, 8, state, out, status, None) == L.PKV_EINVAL
+    # free
+    assert lib.kv_free(16, 0x6000, 4, 64, ring, 8, state, None, status, None) == L.PKV_EINVAL
+    assert lib.kv_free(16, None, 4, 64, ring, 8, state, 0x7000, status, None) == L.PKV_EINVAL
+    assert lib.kv_free(16, 0x6000, 4, 0, ring, 8, state, 0x7000, status, None) == L.PKV_EINVAL
+    # row writing
+    t = 0x8000
+    assert lib.write_req_to_token(t, 4, 64, lens, lens, lens, out, 10, None, 2, 65, None) == L.PKV_EINVAL
+    assert lib.write_req_to_token(t, 4, 64, None, lens, lens, out, 10, None, 2, 64, None) == L.PKV_EINVAL
+    assert lib.write_req_to_token(t, 0, 64, lens, lens, lens, out, 10, None, 2, 64, None) == L.PKV_EINVAL
+    assert lib.write_req_to_token(t, 4, 64, lens, lens, lens, None, 10, None, 2, 64, None) == L.PKV_EINVAL
+    assert lib.write_req_to_token(t, 4, 2**27, lens, lens, lens, out, 10, None, 2, 2**26 + 1, None) \
+        == L.PKV_EUNSUPPORTED
