@@ -13,7 +13,9 @@ Other workloads (--workload): gqa_prefix_share_ps16 / _ps64 (batch-256 GQA
 decode with shared 2048-token prefixes), mla_decode (latent 576/512, 128
 heads, page_size 64), encdec_extend (Whisper-shaped causal + cross extend
 over a paged prefix), encdec_extend_ragged (the same through kv_gather and
-contiguous K/V), tiny_decode (fp32 correctness shape).
+contiguous K/V), tiny_decode (fp32 correctness shape), serving_alloc_decode /
+serving_alloc_extend (one step of the device slot allocator: alloc, row
+write and free; integer work bound by launch latency).
 
 Prints one JSON line: whole-step throughput (algorithmic HBM bytes per
 second), tokens per second, the roofline of the dominant kernel (timed with
@@ -374,6 +376,105 @@ class ExtendBench:
                           f"batch, {toks} new tokens) by the numpy fp64 oracle, {dt:.1f} s"}
 
 
+# ---------------------------------------------------------------------------
+# slot allocation workload
+# ---------------------------------------------------------------------------
+class AllocBench:
+    """Slot allocation step: kv_alloc_decode (or kv_alloc_extend) of the
+    batch, write_req_to_token of the new slots into the requests' rows, then
+    kv_free of the same slots, which returns exactly the pages just taken
+    (every prefix is page aligned), so every step does the same work."""
+
+    attn_calls = 1
+    tokens_label = "new_slots_per_s"
+    metric = "slot allocation step (alloc + row write + free): new slots per second, 1 GPU"
+    unit = "slots/s"
+
+    def __init__(self, decode: bool, dev="cuda"):
+        import torch
+        import paged_kv_cache_38_amd as P
+        from workloads.alloc import serving_alloc
+
+        self.P, self.torch, self.decode = P, torch, decode
+        self.kernel_name = ("allocation step: " + ("kv_alloc_decode" if decode else "kv_alloc_extend") +
+                            " + write_req_to_token + kv_free (6 launches)")
+        self.w = w = serving_alloc(decode)
+        self.case = None
+        self.bs = len(w.seq_lens)
+        self.new = int((w.seq_lens - w.prefix_lens).sum())
+        self.pages = int(sum(-(-int(s) // w.page_size) - int(p) // w.page_size
+                             for p, s in zip(w.prefix_lens, w.seq_lens)))
+        self.fl = P.kv_free_list_create(w.page_size, w.num_pages, device=dev)
+        self.prefix, self.seq, self.rpi = i32(w.prefix_lens, dev), i32(w.seq_lens, dev), i32(w.req_pool_indices, dev)
+        self.last = i32(np.full(self.bs, -1), dev)
+        self.out = torch.empty(self.new, dtype=torch.int32, device=dev)
+        self.table = torch.zeros((self.bs + 1, w.table_width), dtype=torch.int32, device=dev)
+        self.max_seq = int(w.seq_lens.max())
+        self.stream = torch.cuda.current_stream().cuda_stream
+        self.hip = HipEvents().hip
+        self.hip.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
+
+    def step(self, timers=None):
+        P = self.P
+        if timers:
+            assert self.hip.hipEventRecord(C.c_void_p(timers[0][0]), C.c_void_p(self.stream)) == 0
+        if self.decode:
+            P.kv_alloc_decode(self.fl, self.seq, self.last, self.out)
+        else:
+            P.kv_alloc_extend(self.fl, self.prefix, self.seq, self.last, self.out)
+        P.write_req_to_token(self.table, self.rpi, self.prefix, self.seq, self.out, self.max_seq)
+        P.kv_free(self.fl, self.out)
+        if timers:
+            assert self.hip.hipEventRecord(C.c_void_p(timers[0][1]), C.c_void_p(self.stream)) == 0
+
+    def check(self):
+        """Every step must be granted: the free list is back at full size."""
+        self.torch.cuda.synchronize()
+        st = int(self.fl.status.item())
+        size = int(self.fl.state[1].item())
+        if st != 0 or size != self.w.num_pages:
+            raise SystemExit(f"allocation step left status {st}, free size {size} (expected 0, {self.w.num_pages})")
+
+    def kernel_bytes(self, logical: bool = False) -> int:
+        """Lengths read by the allocator and the row writer, the ring entries
+        taken and given back, the new slots written, read back by the row
+        writer and by the free, the table cells written, and the free's page
+        bitmap cleared, marked and read."""
+        words = (self.w.num_pages + 31) // 32
+        lens = self.bs * (4 if self.decode else 8) + self.bs * 12
+        return lens + 2 * self.pages * 4 + 4 * self.new * 4 + 3 * words * 4
+
+    def step_bytes(self) -> int:
+        return self.kernel_bytes()
+
+    def kernel_flops(self) -> int:
+        return 0
+
+    def tokens_per_step(self) -> int:
+        return self.new
+
+    def value(self, ms_step: float) -> float:
+        return self.new / (ms_step * 1e-3)
+
+    def cpu_baseline(self, budget_s: float):
+        import oracle
+
+        w = self.w
+        ring = oracle.FreeRing(list(range(w.num_pages)), w.num_pages)
+        table = np.zeros((self.bs + 1, w.table_width), np.int64)
+        last = [-1] * self.bs
+        steps, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 <= budget_s:
+            slots = oracle.alloc_extend(ring, w.page_size, w.prefix_lens, w.seq_lens, last)
+            table = oracle.write_req_to_token(table, w.req_pool_indices, w.prefix_lens, w.seq_lens, slots)
+            oracle.free_pages(ring, oracle.pages_of_slots(slots, w.page_size))
+            steps += 1
+        dt = time.perf_counter() - t0
+        return {"value": round(steps * self.new / dt, 1), "unit": "slots/s", "cores": 1, "kind": "oracle",
+                "sample": f"{steps} whole allocation steps ({steps * self.new} slots) by the Python oracle, "
+                          f"{dt:.1f} s"}
+
+
 def build_workload(name: str):
     import workloads as W
     if name == "qwen3_decode":
@@ -400,6 +501,13 @@ def build_workload(name: str):
             "new_tokens": "U{1..512}",
             "step": "kv_store + build_kv_indices(CSR) x2 + " + ("kv_gather x2 + " if ragged else "")
                     + "paged_extend_attn (causal self + cross)"}
+    if name in ("serving_alloc_decode", "serving_alloc_extend"):
+        dec = name.endswith("decode")
+        return AllocBench(dec), {
+            "workload": name, "batch": 4096 if dec else 64, "page_size": 16, "pool_pages": 65536,
+            "prefix": "page aligned, " + ("U[512,4096)" if dec else "U[0,4096)"),
+            "new_tokens": "1 (every request opens a page)" if dec else "U[1,2048]",
+            "step": ("kv_alloc_decode" if dec else "kv_alloc_extend") + " + write_req_to_token + kv_free"}
     if name == "tiny_decode":
         return DecodeBench(W.tiny_decode(seed=0), "csr"), {"workload": "tiny_decode_f32", "batch": 4, "page_size": 16}
     raise SystemExit(f"unknown workload {name}")
@@ -495,9 +603,9 @@ def main():
         roof.update({"kernel_ms_cold": round(cold_ms, 5), "kernel_gbs_cold": round(cold_gbs, 2),
                      "kernel_hbm_frac_cold": round(cold_gbs / HBM_PEAK_GBS, 4)})
     res = {
-        "metric": "paged decode attn: achieved HBM GB/s (% of peak) + decode tokens/s, 1 GPU",
-        "value": round(step_gbs, 2),
-        "unit": "GB/s",
+        "metric": getattr(b, "metric", "paged decode attn: achieved HBM GB/s (% of peak) + decode tokens/s, 1 GPU"),
+        "value": round(b.value(ms_step), 1) if hasattr(b, "value") else round(step_gbs, 2),
+        "unit": getattr(b, "unit", "GB/s"),
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -505,7 +613,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": b.case.geom.dtype,
+        "dtype": b.case.geom.dtype if b.case is not None else "int32",
         "data": "synthetic (seeded; N(0,1) values)",
         "config": cfg,
         "hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
@@ -519,6 +627,8 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         res["calibration_copy_bytes"] = src.numel()
+    if hasattr(b, "check"):
+        b.check()
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = b.cpu_baseline(args.cpu_budget)
     print(json.dumps(res), flush=True)

@@ -59,3 +59,32 @@ def growth_batch(seed: int, bs: int, page_size: int, max_prefix: int, max_new: i
     head = cap - min(3, cap)
     return GrowthBatch(page_size, num_pages, cap, head, free.astype(np.int32), prefix.astype(np.int32),
                        seq.astype(np.int32), last.astype(np.int32))
+
+
+@dataclass
+class ServingAlloc:
+    """One serving step's allocation work: bs requests holding page-aligned
+    prefixes grow by new_lens tokens (one each for decode)."""
+    page_size: int
+    num_pages: int
+    prefix_lens: np.ndarray
+    seq_lens: np.ndarray
+    req_pool_indices: np.ndarray
+    table_width: int
+
+
+def serving_alloc(decode: bool, seed: int = 0) -> ServingAlloc:
+    """Decode: 4096 requests, page_size 16, prefixes page aligned in
+    [512, 4096), so every request opens a new page (the allocator's busiest
+    decode step).  Extend: 64 requests, page_size 16, page-aligned prefixes
+    in [0, 4096) growing by U[1, 2048] tokens.  A 65536-page (1M-slot) pool;
+    rows are a seeded shuffle of a 4097- or 65-row table of width 8192."""
+    rng = np.random.default_rng(seed)
+    ps = 16
+    bs = 4096 if decode else 64
+    lo = 512 if decode else 0
+    prefix = rng.integers(lo // ps, 4096 // ps, bs) * ps
+    new = np.ones(bs, np.int64) if decode else rng.integers(1, 2049, bs)
+    rpi = rng.permutation(bs + 1)[:bs]
+    return ServingAlloc(ps, 65536, prefix.astype(np.int32), (prefix + new).astype(np.int32), rpi.astype(np.int32),
+                        8192)
