@@ -14,7 +14,7 @@
 // each call is a fixed number of launches (no host synchronisation, no
 // memset, so it may be captured in a graph), and the batch-wide prefix sums
 // are block scans in LDS rather than a separate scan pass.
-#include "pkv_launch.h"
+#include "pkv_alloc.h"
 
 namespace pkv {
 

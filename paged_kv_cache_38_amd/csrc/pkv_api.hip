@@ -10,6 +10,7 @@
 #include <string>
 
 #include "pagedkv.h"
+#include "pkv_alloc.h"
 #include "pkv_launch.h"
 
 struct pkv_pool {

@@ -47,21 +47,6 @@ hipError_t launch_build_indices(int32_t out_fmt, const int32_t* req_to_token, in
                                 const int32_t* kv_lens, int32_t bs, int32_t page_shift, int32_t* kv_indptr,
                                 int32_t* out, int64_t capacity, int32_t* kv_last_page_len, hipStream_t s);
 
-// Slot allocation and row writing (pkv_alloc.hip).
-constexpr int32_t kMaxAllocBatch = 8000;  // requests per alloc_extend call (LDS offsets)
-
-hipError_t launch_free_list_init(int32_t* ring, int32_t first, int32_t count, int32_t* state, hipStream_t s);
-hipError_t launch_alloc_pages(int32_t shift, int64_t n_pages, int32_t* ring, int32_t cap, int32_t* state,
-                              int32_t* out, int32_t* status, hipStream_t s);
-hipError_t launch_alloc_extend(int32_t shift, int32_t bs, const int32_t* prefix, const int32_t* seq,
-                               const int32_t* last_loc, int32_t* ring, int32_t cap, int32_t* state, int32_t* out,
-                               int64_t out_cap, int32_t* status, hipStream_t s);
-hipError_t launch_free(int32_t shift, const int32_t* slots, int64_t n, int32_t num_pages, int32_t* ring,
-                       int32_t cap, int32_t* state, uint32_t* bits, int32_t* status, hipStream_t s);
-hipError_t launch_write_rows(int32_t* table, int64_t rows, int64_t width, const int32_t* rpi, const int32_t* prefix,
-                             const int32_t* seq, const int32_t* out_loc, int64_t n_out,
-                             const int32_t* const* prefix_ptrs, int32_t bs, int32_t max_seq_len, hipStream_t s);
-
 // Split plan for decode: chunk of logical tokens per split and the number
 // of split slots reserved per request in the workspace.
 struct DecodePlan {
