@@ -51,7 +51,7 @@ from .indices import (  # noqa: F401
     token_indptr,
     in_page_contiguous,
 )
-from .attention import attend, paged_attention, merge_partials, gather  # noqa: F401
+from .attention import attend, paged_attention, merge_partials, gather, span_segments  # noqa: F401
 from .alloc import (  # noqa: F401
     FreeRing,
     new_pages_needed,

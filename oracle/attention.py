@@ -19,6 +19,16 @@ encoder-decoder post, "Approach 2": an empty KV returns a zero context).
 Keys and values are the exact stored values, gathered by slot: paged and
 dense attention describe the same result ([OMNI] "Dense and paged
 representation").
+
+Softcap (the SGLang encoder-decoder post, "Approach 2": the ragged call passes
+``softcap``; the pages do not define it, so the plainest reading is taken):
+with ``softcap > 0`` every scaled score becomes ``softcap * tanh(s /
+softcap)`` before the softmax; ``0`` leaves the scores as they are.
+
+Mixed spans ([OMNI] "Attention execution"): a row's tokens fall into causal
+and full spans; a causal span ``[s, e)`` is the segment ``Q[s:e]`` over
+``K[:e]`` with the causal flag, a full span ``[a, b)`` is ``Q[a:b]`` over
+``K[:b]`` without it.  Each segment is then an ordinary request.
 """
 from typing import List, Optional, Sequence, Tuple
 
@@ -27,7 +37,8 @@ import numpy as np
 from .numerics import to_f64
 
 
-def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float, causal: bool) -> Tuple[np.ndarray, np.ndarray]:
+def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float, causal: bool,
+           softcap: float = 0.0) -> Tuple[np.ndarray, np.ndarray]:
     """One request.  q ``[n, Hq, Dqk]``, K ``[L, Hkv, Dqk]``, V ``[L, Hkv, Dv]``
     (float64).  Returns out ``[n, Hq, Dv]`` and lse ``[n, Hq]`` (natural log)."""
     q = np.asarray(q, np.float64)
@@ -47,6 +58,8 @@ def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float, causal: bo
     for g in range(Hkv):
         qg = q[:, g * G:(g + 1) * G, :].reshape(n * G, -1)  # rows (j, h)
         s = scale * (qg @ K[:, g, :].T)  # [n*G, L]
+        if softcap > 0:
+            s = softcap * np.tanh(s / softcap)
         s = s.reshape(n, G, L)
         s = np.where(visible[:, None, :], s, -np.inf)
         m = s.max(axis=2, keepdims=True)
@@ -65,8 +78,8 @@ def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float, causal: bo
 
 def paged_attention(q_raw: np.ndarray, q_lens: Sequence[int], pool_k_raw: np.ndarray,
                     pool_v_raw: Optional[np.ndarray], dtype: str, slot_lists: List[np.ndarray],
-                    scale: float, causal: bool, head_dim_v: Optional[int] = None,
-                    requests: Optional[Sequence[int]] = None):
+                    scale: float, causal, head_dim_v: Optional[int] = None,
+                    requests: Optional[Sequence[int]] = None, softcap: float = 0.0):
     """Batch of requests reading K/V through slot lists.
 
     ``q_raw`` ``[sum(q_lens), Hq, Dqk]`` and the per-token pool views
@@ -75,7 +88,8 @@ def paged_attention(q_raw: np.ndarray, q_lens: Sequence[int], pool_k_raw: np.nda
     tokens ``0..L_i-1`` (from any of the table formats).  A latent pool
     passes ``pool_v_raw=None`` and ``head_dim_v``: V is the first
     ``head_dim_v`` values of each K row.  ``requests`` limits the work to a
-    subset; other rows of the result stay NaN.
+    subset; other rows of the result stay NaN.  ``causal`` is one flag for
+    every request or a per-request sequence (mixed causal/full segments).
 
     Returns out ``[sum(q_lens), Hq, Dv]`` and lse ``[sum(q_lens), Hq]``, fp64."""
     q_lens = np.asarray(q_lens, np.int64)
@@ -90,7 +104,8 @@ def paged_attention(q_raw: np.ndarray, q_lens: Sequence[int], pool_k_raw: np.nda
         slots = np.asarray(slot_lists[i], np.int64)
         K = to_f64(pool_k_raw[slots], dtype)
         V = K[..., :Dv] if pool_v_raw is None else to_f64(pool_v_raw[slots], dtype)
-        o, l = attend(to_f64(q_raw[a:b], dtype), K, V, scale, causal)
+        c = bool(causal[i]) if isinstance(causal, (list, tuple, np.ndarray)) else bool(causal)
+        o, l = attend(to_f64(q_raw[a:b], dtype), K, V, scale, c, softcap)
         out[a:b] = o
         lse[a:b] = l
     return out, lse
@@ -122,3 +137,10 @@ def gather(pool_raw: np.ndarray, slot_lists: List[np.ndarray]) -> np.ndarray:
         return pool_raw[:0].copy()
     idx = np.concatenate([np.asarray(s, np.int64) for s in slot_lists])
     return pool_raw[idx].copy()
+
+
+def span_segments(spans: Sequence[Tuple[int, int, bool]]) -> List[Tuple[int, int, int, bool]]:
+    """A row's spans ``(start, end, causal)`` as native segments ``(q_start,
+    q_end, kv_len, causal)``: both kinds read the row's keys up to the span's
+    end ([OMNI] "Attention execution", the segment table)."""
+    return [(int(a), int(b), int(b), bool(c)) for a, b, c in spans]

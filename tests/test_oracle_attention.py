@@ -353,3 +353,110 @@ def test_workload_tables_are_in_page_contiguous_and_match_page_lists():
                                                        reg.kv_lens[i], c.geom.page_size)
                 assert np.array_equal(ids, reg.page_lists[i])
                 assert not (ids == c.geom.padding_page).any()
+
+
+# --------------------------------------------------------------------------
+# softcap (the encoder-decoder post's ragged call passes it; reading: every
+# scaled score s becomes cap * tanh(s / cap))
+# --------------------------------------------------------------------------
+
+def test_softcap_closed_form_two_keys():
+    """Raw scores cap * atanh(+-1/2) are capped to +-cap/2, so the first key's
+    weight is 1 / (1 + e^-cap) and lse = log(2 cosh(cap / 2))."""
+    for cap in (0.5, 4.0, 30.0):
+        x = cap * math.atanh(0.5)
+        q = np.array([[[1.0]]])
+        K = np.array([[[x]], [[-x]]])
+        V = np.array([[[1.0]], [[0.0]]])
+        o, l = oracle.attend(q, K, V, 1.0, False, softcap=cap)
+        assert abs(o[0, 0, 0] - 1.0 / (1.0 + math.exp(-cap))) < 1e-14
+        assert abs(l[0, 0] - math.log(2.0 * math.cosh(cap / 2.0))) < 1e-12
+
+
+def test_softcap_vanishes_for_a_huge_cap_and_bounds_the_weights():
+    rng = np.random.default_rng(21)
+    q = rng.normal(size=(3, 4, 8))
+    K = rng.normal(size=(11, 2, 8))
+    V = rng.normal(size=(11, 2, 5))
+    o0, l0 = oracle.attend(q, K, V, 0.7, True)
+    o1, l1 = oracle.attend(q, K, V, 0.7, True, softcap=1e9)
+    np.testing.assert_allclose(o1, o0, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l1, l0, rtol=0, atol=1e-12)
+    # scores of +-1e4 capped at 2: every weight within e^(2 * 2) of every other
+    cap = 2.0
+    Kb = np.array([[[1e4]], [[-1e4]], [[0.0]]])
+    Vb = np.eye(3)[:, None, :]
+    ob, _ = oracle.attend(np.array([[[1.0]]]), Kb, Vb, 1.0, False, softcap=cap)
+    w = ob[0, 0]
+    assert np.isfinite(w).all() and abs(w.sum() - 1) < 1e-12
+    assert w.max() / w.min() <= math.exp(2 * cap) * (1 + 1e-12)
+
+
+def test_softcap_matches_brute_force():
+    rng = np.random.default_rng(22)
+    q = rng.normal(size=(2, 2, 3)) * 3
+    K = rng.normal(size=(5, 1, 3)) * 3
+    V = rng.normal(size=(5, 1, 2))
+    cap = 1.5
+    o, l = oracle.attend(q, K, V, 0.9, True, softcap=cap)
+    for j in range(2):
+        for h in range(2):
+            keys = [t for t in range(5) if t <= 5 - 2 + j]
+            s = [cap * math.tanh(0.9 * math.fsum(q[j, h, d] * K[t, 0, d] for d in range(3)) / cap) for t in keys]
+            m = max(s)
+            e = [math.exp(x - m) for x in s]
+            tot = math.fsum(e)
+            for d in range(2):
+                assert abs(o[j, h, d] - math.fsum(e[a] * V[t, 0, d] for a, t in enumerate(keys)) / tot) < 1e-12
+            assert abs(l[j, h] - (m + math.log(tot))) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# mixed causal/full spans (vLLM-Omni notes, "Attention execution")
+# --------------------------------------------------------------------------
+
+def test_span_segments_equal_one_dense_masked_row():
+    """A row of causal and full spans, run as native segments, equals dense
+    attention over the whole row with the mask the spans describe: a
+    position in a causal span sees keys up to itself, a position in a full
+    span [a, b) sees keys up to b."""
+    rng = np.random.default_rng(23)
+    spans = [(0, 5, True), (5, 12, False), (12, 15, True), (15, 19, False)]
+    T, Hq, Hkv, D = 19, 4, 2, 6
+    q = rng.normal(size=(T, Hq, D))
+    K = rng.normal(size=(T, Hkv, D))
+    V = rng.normal(size=(T, Hkv, D))
+    seg_o = np.zeros((T, Hq, D))
+    seg_l = np.zeros((T, Hq))
+    segs = oracle.span_segments(spans)
+    assert [(a, b, kv) for a, b, kv, _ in segs] == [(0, 5, 5), (5, 12, 12), (12, 15, 15), (15, 19, 19)]
+    for a, b, kv, causal in segs:
+        o, l = oracle.attend(q[a:b], K[:kv], V[:kv], 0.4, causal)
+        seg_o[a:b], seg_l[a:b] = o, l
+    # dense row: torch SDPA in float64 with the span mask, KV heads repeated
+    mask = np.zeros((T, T), bool)
+    for a, b, causal in spans:
+        for p in range(a, b):
+            mask[p, :(p + 1 if causal else b)] = True
+    G = Hq // Hkv
+    tq = torch.from_numpy(q).permute(1, 0, 2)
+    tk = torch.from_numpy(K).permute(1, 0, 2).repeat_interleave(G, dim=0)
+    tv = torch.from_numpy(V).permute(1, 0, 2).repeat_interleave(G, dim=0)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.from_numpy(mask), scale=0.4)
+    np.testing.assert_allclose(seg_o, ref.permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+    # lse of the dense row, by hand
+    s = np.einsum("phd,thd->pht", q, np.repeat(K, G, axis=1)) * 0.4
+    s = np.where(mask[:, None, :], s, -np.inf)
+    m = s.max(axis=2)
+    np.testing.assert_allclose(seg_l, m + np.log(np.exp(s - m[..., None]).sum(axis=2)), rtol=0, atol=1e-12)
+
+
+def test_paged_attention_takes_per_request_causal_flags():
+    rng = np.random.default_rng(24)
+    pool = rng.normal(size=(40, 2, 4)).astype(np.float32)
+    q = rng.normal(size=(7, 2, 4)).astype(np.float32)
+    slots = [np.arange(0, 9), np.arange(10, 25)]
+    o, l = oracle.paged_attention(q, [3, 4], pool, pool, "f32", slots, 0.5, [True, False])
+    o0, _ = oracle.paged_attention(q, [3, 4], pool, pool, "f32", slots, 0.5, True, requests=[0])
+    o1, _ = oracle.paged_attention(q, [3, 4], pool, pool, "f32", slots, 0.5, False, requests=[1])
+    assert np.array_equal(o[:3], o0[:3]) and np.array_equal(o[3:], o1[3:])
