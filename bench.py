@@ -13,7 +13,9 @@ Other workloads (--workload): gqa_prefix_share_ps16 / _ps64 (batch-256 GQA
 decode with shared 2048-token prefixes), mla_decode (latent 576/512, 128
 heads, page_size 64), encdec_extend (Whisper-shaped causal + cross extend
 over a paged prefix), encdec_extend_ragged (the same through kv_gather and
-contiguous K/V), tiny_decode (fp32 correctness shape), serving_alloc_decode /
+contiguous K/V), mixed_spans_extend / _softcap (rows of a causal text span
+and a full image span run as per-segment-flagged requests, without and with
+softcap 30), tiny_decode (fp32 correctness shape), serving_alloc_decode /
 serving_alloc_extend (one step of the device slot allocator: alloc, row
 write and free; integer work bound by launch latency).
 
@@ -262,13 +264,15 @@ class ExtendBench:
     attn_calls = 2
     tokens_label = "extend_tokens_per_s"
 
-    def __init__(self, case, ragged: bool, dev="cuda"):
+    def __init__(self, case, ragged: bool, softcap: float = 0.0, dev="cuda"):
         import torch
         import paged_kv_cache_38_amd as P
         import workloads as W
 
-        self.case, self.P, self.torch, self.ragged = case, P, torch, ragged
+        self.case, self.P, self.torch, self.ragged, self.softcap = case, P, torch, ragged, softcap
         self.kernel_name = "paged extend attention kernel" + (" (contiguous K/V after kv_gather)" if ragged else "")
+        if softcap:
+            self.kernel_name += f" (softcap {softcap:g})"
         g = case.geom
         self.vals = W.make_values(case, device=dev)
         self.pool = _make_pool(case, self.vals)
@@ -283,6 +287,7 @@ class ExtendBench:
             maxl = int(r.kv_lens.max())
             per = max(-(-maxl // g.page_size), 1)
             d = {"kv_start": i32(r.kv_start, dev), "kv_lens": i32(r.kv_lens, dev), "max": maxl,
+                 "flags": None if r.causal_flags is None else i32(r.causal_flags, dev),
                  "indptr": torch.empty(case.bs + 1, dtype=torch.int32, device=dev),
                  "indices": torch.empty(case.bs * per, dtype=torch.int32, device=dev),
                  "q": self.vals["q"][name], "causal": r.causal,
@@ -312,8 +317,12 @@ class ExtendBench:
                 m = d["cmap"]
             if timers:
                 P.pkv_set_kernel_timer(*timers[k])
-            P.paged_extend_attn(self.pool, 0, d["q"], self.qo, self.max_q, m, d["causal"], c.sm_scale, d["out"],
-                                d["lse"])
+            if d["flags"] is None and not self.softcap:
+                P.paged_extend_attn(self.pool, 0, d["q"], self.qo, self.max_q, m, d["causal"], c.sm_scale,
+                                    d["out"], d["lse"])
+            else:
+                P.paged_extend_attn_ex(self.pool, 0, d["q"], self.qo, self.max_q, m, c.sm_scale, d["out"],
+                                       d["lse"], causal=d["causal"], causal_flags=d["flags"], softcap=self.softcap)
 
     def _pairs(self, name) -> int:
         """Unmasked (query, key) pairs of one region."""
@@ -321,9 +330,9 @@ class ExtendBench:
         r = c.regions[name]
         n = c.q_lens.astype(np.int64)
         L = r.kv_lens.astype(np.int64)
-        if r.causal:  # query j sees L - n + j + 1 keys
-            return int(np.sum(n * (L - n) + n * (n + 1) // 2))
-        return int(np.sum(n * L))
+        causal = np.full(len(n), bool(r.causal)) if r.causal_flags is None else r.causal_flags != 0
+        # a causal request's query j sees L - n + j + 1 keys, a full one sees L
+        return int(np.sum(np.where(causal, n * (L - n) + n * (n + 1) // 2, n * L)))
 
     def kernel_flops(self) -> int:
         g = self.case.geom
@@ -364,16 +373,17 @@ class ExtendBench:
                     slots = [oracle.slots_from_token_table(c.req_to_token, c.req_pool_indices[i], r.kv_start[i],
                                                            r.kv_lens[i]) if j == i else np.zeros(0, np.int64)
                              for j in range(c.bs)]
-                    oracle.paged_attention(qs[nm], c.q_lens, pk, pv, g.dtype, slots, c.sm_scale, r.causal,
-                                           requests=[i])
+                    causal = r.causal if r.causal_flags is None else [bool(f) for f in r.causal_flags]
+                    oracle.paged_attention(qs[nm], c.q_lens, pk, pv, g.dtype, slots, c.sm_scale, causal,
+                                           requests=[i], softcap=self.softcap)
                 reqs += 1
                 toks += int(c.q_lens[i])
                 if time.perf_counter() - t0 > budget_s:
                     break
         dt = time.perf_counter() - t0
         return {"value": round(toks / dt, 2), "unit": "extend tokens/s", "cores": _blas_threads(), "kind": "oracle",
-                "sample": f"{reqs} request extends (self + cross; {reqs / c.bs:.2f} passes over the {c.bs}-request "
-                          f"batch, {toks} new tokens) by the numpy fp64 oracle, {dt:.1f} s"}
+                "sample": f"{reqs} request extends ({' + '.join(c.regions)}; {reqs / c.bs:.2f} passes over the "
+                          f"{c.bs}-request batch, {toks} new tokens) by the numpy fp64 oracle, {dt:.1f} s"}
 
 
 # ---------------------------------------------------------------------------
@@ -508,6 +518,15 @@ def build_workload(name: str):
             "prefix": "page aligned, " + ("U[512,4096)" if dec else "U[0,4096)"),
             "new_tokens": "1 (every request opens a page)" if dec else "U[1,2048]",
             "step": ("kv_alloc_decode" if dec else "kv_alloc_extend") + " + write_req_to_token + kv_free"}
+    if name in ("mixed_spans_extend", "mixed_spans_extend_softcap"):
+        cap = 30.0 if name.endswith("softcap") else 0.0
+        b = ExtendBench(W.mixed_spans(seed=0), False, softcap=cap)
+        b.attn_calls = 1
+        return b, {
+            "workload": name, "rows": 4, "spans": "causal text 128 + full image 2048 per row, one segment each",
+            "num_q_heads": 32, "num_kv_heads": 8, "head_dim": 128, "page_size": 16, "softcap": cap,
+            "step": "kv_store of every row token + build_kv_indices(CSR) + paged_extend_attn_ex "
+                    "(per-segment causal flags)"}
     if name == "tiny_decode":
         return DecodeBench(W.tiny_decode(seed=0), "csr"), {"workload": "tiny_decode_f32", "batch": 4, "page_size": 16}
     raise SystemExit(f"unknown workload {name}")

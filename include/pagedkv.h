@@ -250,6 +250,31 @@ int paged_extend_attn(const pkv_pool* pool, int32_t layer, const void* q, int64_
                       int32_t num_q_heads, int32_t max_q_len, const pkv_kv_map* map, int32_t causal,
                       float sm_scale, void* out, float* lse, void* stream);
 
+/* Options of paged_extend_attn_ex.
+ *   causal: the mask of every request when causal_flags is NULL (as in
+ *     paged_extend_attn).
+ *   causal_flags: nullable device int32[bs], one flag per request: nonzero
+ *     = causal (bottom-right), 0 = full.  A row of mixed causal and full spans
+ *     ([OMNI] "Attention execution": causal [s, e) is Q[s:e] over K[:e] with
+ *     the causal flag, full [a, b) is Q[a:b] over K[:b] without it) runs as
+ *     one call whose requests are its segments: several requests may read
+ *     the same table row, each with its own kv_lens and query rows.
+ *   softcap: 0 = off; > 0 (finite) replaces every scaled score s by
+ *     softcap * tanh(s / softcap) before the softmax ([XPU] "Approach 2":
+ *     the ragged call passes softcap). */
+typedef struct pkv_extend_opts {
+  int32_t causal;
+  const int32_t* causal_flags;
+  float softcap;
+} pkv_extend_opts;
+
+/* paged_extend_attn with per-request causal flags and softcap (opts, host,
+ * required).  Everything else as paged_extend_attn; negative or infinite
+ * softcap gives PKV_EINVAL. */
+int paged_extend_attn_ex(const pkv_pool* pool, int32_t layer, const void* q, int64_t total_q,
+                         const int32_t* qo_indptr, int32_t num_q_heads, int32_t max_q_len, const pkv_kv_map* map,
+                         const pkv_extend_opts* opts, float sm_scale, void* out, float* lse, void* stream);
+
 /* ---- ragged gather (a9) ------------------------------------------------- */
 
 /* Copy each request's first kv_lens[i] K (and V) rows, in logical order,

@@ -36,7 +36,8 @@ from ._lib import (  # noqa: F401
 __all__ = [
     "Pool", "KVMap", "kv_pool_bytes", "kv_pool_create", "kv_pool_destroy", "kv_pool_padding_page",
     "kv_pool_token_bytes", "kv_store", "build_kv_indices", "make_kv_map", "paged_decode_workspace_bytes",
-    "paged_decode_attn", "paged_extend_attn", "kv_gather", "kv_validate", "pkv_set_kernel_timer", "library",
+    "paged_decode_attn", "paged_extend_attn", "paged_extend_attn_ex", "kv_gather", "kv_validate",
+    "pkv_set_kernel_timer", "library",
     "FreeList", "kv_free_list_create", "kv_free_list_init", "kv_alloc", "kv_alloc_extend", "kv_alloc_decode",
     "kv_free", "write_req_to_token",
 ]
@@ -261,6 +262,24 @@ def paged_extend_attn(pool: Pool, layer: int, q: torch.Tensor, qo_indptr: torch.
                                        C.byref(kv_map.struct), 1 if causal else 0, float(sm_scale),
                                        _dev(out, "out", pool.dtype), _dev(lse, "lse", torch.float32),
                                        _stream(stream)), "paged_extend_attn")
+
+
+def paged_extend_attn_ex(pool: Pool, layer: int, q: torch.Tensor, qo_indptr: torch.Tensor, max_q_len: int,
+                         kv_map: KVMap, sm_scale: float, out: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                         causal: bool = True, causal_flags: Optional[torch.Tensor] = None, softcap: float = 0.0,
+                         stream=None) -> None:
+    """paged_extend_attn with per-request causal flags (device int32[bs],
+    nonzero = causal) and softcap (0 = off)."""
+    if out.shape[0] != q.shape[0]:
+        raise ValueError("out and q must have the same number of rows")
+    if causal_flags is not None and causal_flags.numel() != kv_map.bs:
+        raise ValueError("causal_flags must have one entry per request")
+    opts = L.ExtendOpts(1 if causal else 0, _dev(causal_flags, "causal_flags", torch.int32), float(softcap))
+    L.check(L.load().paged_extend_attn_ex(pool.handle, layer, _dev(q, "q", pool.dtype), q.shape[0],
+                                          _dev(qo_indptr, "qo_indptr", torch.int32), q.shape[1], int(max_q_len),
+                                          C.byref(kv_map.struct), C.byref(opts), float(sm_scale),
+                                          _dev(out, "out", pool.dtype), _dev(lse, "lse", torch.float32),
+                                          _stream(stream)), "paged_extend_attn_ex")
 
 
 # ---------------------------------------------------------------------------

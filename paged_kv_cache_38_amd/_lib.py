@@ -69,6 +69,14 @@ class KVMapStruct(C.Structure):
     ]
 
 
+class ExtendOpts(C.Structure):
+    _fields_ = [
+        ("causal", C.c_int32),
+        ("causal_flags", C.c_void_p),
+        ("softcap", C.c_float),
+    ]
+
+
 # name -> (restype, argtypes): every entry point include/pagedkv.h declares
 SIGNATURES = {
     "pkv_abi_version": (C.c_int, []),
@@ -91,6 +99,9 @@ SIGNATURES = {
     "paged_extend_attn": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_int64, C.c_void_p, C.c_int32, C.c_int32,
                                     C.POINTER(KVMapStruct), C.c_int32, C.c_float, C.c_void_p, C.c_void_p,
                                     C.c_void_p]),
+    "paged_extend_attn_ex": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_int64, C.c_void_p, C.c_int32,
+                                       C.c_int32, C.POINTER(KVMapStruct), C.POINTER(ExtendOpts), C.c_float,
+                                       C.c_void_p, C.c_void_p, C.c_void_p]),
     "kv_gather": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(KVMapStruct), C.c_void_p, C.c_void_p, C.c_void_p,
                             C.c_int64, C.c_void_p]),
     "kv_validate": (C.c_int, [C.c_void_p, C.POINTER(KVMapStruct), C.c_void_p, C.c_void_p,

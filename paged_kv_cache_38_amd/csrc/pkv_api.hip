@@ -318,9 +318,11 @@ int paged_decode_attn(const pkv_pool* pool, int32_t layer, const void* q, int32_
                        "paged_decode_attn");
 }
 
-int paged_extend_attn(const pkv_pool* pool, int32_t layer, const void* q, int64_t total_q, const int32_t* qo_indptr,
-                      int32_t num_q_heads, int32_t max_q_len, const pkv_kv_map* map, int32_t causal, float sm_scale,
-                      void* out, float* lse, void* stream) {
+namespace {
+int extend_call(const char* call, const pkv_pool* pool, int32_t layer, const void* q, int64_t total_q,
+                const int32_t* qo_indptr, int32_t num_q_heads, int32_t max_q_len, const pkv_kv_map* map,
+                int32_t causal, const int32_t* causal_flags, float softcap, float sm_scale, void* out, float* lse,
+                void* stream) {
   if (int st = check_pool(pool)) return st;
   if (int st = check_layer(pool, layer)) return st;
   pkv::DevMap dm;
@@ -330,6 +332,8 @@ int paged_extend_attn(const pkv_pool* pool, int32_t layer, const void* q, int64_
                 pool->desc.num_kv_heads);
   if (max_q_len < 0 || total_q < 0) return fail(PKV_EINVAL, "negative max_q_len or total_q");
   if (!(sm_scale > 0.0f) || std::isinf(sm_scale)) return fail(PKV_EINVAL, "sm_scale must be positive and finite");
+  if (!(softcap >= 0.0f) || std::isinf(softcap))
+    return fail(PKV_EINVAL, "softcap must be 0 (off) or positive and finite");
   if (!pkv::extend_supported(pool->info, num_q_heads))
     return fail(PKV_EUNSUPPORTED, "no extend kernel for this pool (dtype %d, dims %d/%d)", pool->desc.dtype,
                 pool->desc.head_dim_qk, pool->desc.head_dim_v);
@@ -337,8 +341,25 @@ int paged_extend_attn(const pkv_pool* pool, int32_t layer, const void* q, int64_
   if (!q || !out || !qo_indptr) return fail(PKV_EINVAL, "null q, out or qo_indptr");
   if (!aligned16(q)) return fail(PKV_EALIGN, "q must be 16-byte aligned");
   return device_status(pkv::launch_extend(pool->info, layer, q, total_q, qo_indptr, num_q_heads, max_q_len, dm, map->bs,
-                                          map->max_kv_len, causal, sm_scale, out, lse, (hipStream_t)stream),
-                       "paged_extend_attn");
+                                          map->max_kv_len, causal, causal_flags, softcap, sm_scale, out, lse,
+                                          (hipStream_t)stream),
+                       call);
+}
+}  // namespace
+
+int paged_extend_attn(const pkv_pool* pool, int32_t layer, const void* q, int64_t total_q, const int32_t* qo_indptr,
+                      int32_t num_q_heads, int32_t max_q_len, const pkv_kv_map* map, int32_t causal, float sm_scale,
+                      void* out, float* lse, void* stream) {
+  return extend_call("paged_extend_attn", pool, layer, q, total_q, qo_indptr, num_q_heads, max_q_len, map, causal,
+                     nullptr, 0.0f, sm_scale, out, lse, stream);
+}
+
+int paged_extend_attn_ex(const pkv_pool* pool, int32_t layer, const void* q, int64_t total_q,
+                         const int32_t* qo_indptr, int32_t num_q_heads, int32_t max_q_len, const pkv_kv_map* map,
+                         const pkv_extend_opts* opts, float sm_scale, void* out, float* lse, void* stream) {
+  if (!opts) return fail(PKV_EINVAL, "null extend options");
+  return extend_call("paged_extend_attn_ex", pool, layer, q, total_q, qo_indptr, num_q_heads, max_q_len, map,
+                     opts->causal, opts->causal_flags, opts->softcap, sm_scale, out, lse, stream);
 }
 
 int kv_gather(const pkv_pool* pool, int32_t layer, const pkv_kv_map* map, const int32_t* cu_seqlens_k, void* k_out,

@@ -72,12 +72,27 @@ __device__ __forceinline__ bf16x8 ext_v_operand(const char* tile, int r0, int c0
   return bf16x8{ba[0], ba[1], ba[2], ba[3], bb[0], bb[1], bb[2], bb[3]};
 }
 
-template <int D, int FMT>
+// Softcap ([XPU] "Approach 2": the ragged call passes softcap; a score s
+// becomes cap tanh(s / cap)).  Scores stay in the kernel's raw domain (the
+// scale is applied inside exp2), so a raw score x turns into
+// (cap / scale) tanh(x scale / cap) = b - 2 b / (exp2(a x) + 1) with
+// a = 2 log2(e) scale / cap and b = cap / scale: one exp2 and one
+// reciprocal per score, saturating to +-b at the extremes.
+struct SoftCap {
+  float a, b;
+  __device__ __forceinline__ float operator()(float x) const {
+    return b - 2.0f * b * __builtin_amdgcn_rcpf(fast_exp2(a * x) + 1.0f);
+  }
+};
+
+template <int D, int FMT, bool SC>
 __global__ void __launch_bounds__(256, 2) extend_kernel(DevMap m, const char* k_pool, const char* v_pool,
                                                      int64_t row_bytes, const bf16* __restrict__ q, int64_t total_q,
                                                      const int32_t* __restrict__ qo_indptr, int32_t Hq, int32_t n_req,
-                                                     int32_t n_qtiles, int32_t G, int32_t causal, float scale_log2,
-                                                     bf16* __restrict__ out, float* __restrict__ lse) {
+                                                     int32_t n_qtiles, int32_t G, int32_t causal_all,
+                                                     const int32_t* __restrict__ causal_flags, SoftCap cap,
+                                                     float scale_log2, bf16* __restrict__ out,
+                                                     float* __restrict__ lse) {
   using C = ExtendCfg<D>;
   constexpr int NK = C::NK, NT = C::NT, CPK = C::CPK, NI = C::NI, S = C::S;
   constexpr int kRB = C::RB, kWR = C::WR, kBM = C::BM;
@@ -95,6 +110,9 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(DevMap m, const char* k_
   const int h = pair % Hq;
   const int i = pair / Hq;
   if (i >= n_req) return;
+  // mixed causal/full segments ([OMNI] "Attention execution") carry one
+  // flag per request
+  const int causal = causal_flags ? (causal_flags[i] != 0) : causal_all;
   const int q0 = qo_indptr[i];
   // rows past total_q (a qo_indptr beyond the buffers) are never touched
   const int n = (q0 < 0 || q0 >= total_q) ? 0 : (int)min((int64_t)(qo_indptr[i + 1] - q0), total_q - q0);
@@ -228,6 +246,14 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(DevMap m, const char* k_
 #pragma unroll
           for (int rb = 0; rb < kRB; ++rb) sacc[a2][rb] = mfma16x16x32(ka, qb[rb][kk], sacc[a2][rb]);
         }
+      }
+      if constexpr (SC) {
+#pragma unroll
+        for (int a2 = 0; a2 < 4; ++a2)
+#pragma unroll
+          for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) sacc[a2][rb][rr] = cap(sacc[a2][rb][rr]);
       }
 
       // ---- online softmax (log2 domain); lane holds keys k0 + 16a + 4grp + rr
@@ -373,33 +399,45 @@ bool extend_supported(const PoolInfo& p, int32_t num_q_heads) {
 
 template <int D, int FMT>
 static void launch_ext(dim3 grid, hipStream_t s, const DevMap& m, const char* kp, const char* vp, int64_t row_bytes,
-                       const void* q, int64_t tq, const int32_t* qo, int32_t Hq, int32_t G, int32_t causal, float sl2,
-                       void* out, float* lse) {
+                       const void* q, int64_t tq, const int32_t* qo, int32_t Hq, int32_t G, int32_t causal,
+                       const int32_t* flags, float softcap, float sm_scale, void* out, float* lse) {
   const int32_t qtiles = (int32_t)grid.y;
   const int32_t nreq = (int32_t)grid.z;
   const int64_t pairs = (int64_t)nreq * Hq;
   const dim3 g1((unsigned)(8 * ((pairs + 7) / 8) * qtiles));
-  hipLaunchKernelGGL((extend_kernel<D, FMT>), g1, dim3(256), 0, s, m, kp, vp, row_bytes,
-                     static_cast<const bf16*>(q), tq, qo, Hq, nreq, qtiles, G, causal, sl2, static_cast<bf16*>(out),
-                     lse);
+  const float sl2 = sm_scale * kLog2e;
+  if (softcap > 0.0f) {
+    const SoftCap cap{2.0f * kLog2e * sm_scale / softcap, softcap / sm_scale};
+    hipLaunchKernelGGL((extend_kernel<D, FMT, true>), g1, dim3(256), 0, s, m, kp, vp, row_bytes,
+                       static_cast<const bf16*>(q), tq, qo, Hq, nreq, qtiles, G, causal, flags, cap, sl2,
+                       static_cast<bf16*>(out), lse);
+  } else {
+    hipLaunchKernelGGL((extend_kernel<D, FMT, false>), g1, dim3(256), 0, s, m, kp, vp, row_bytes,
+                       static_cast<const bf16*>(q), tq, qo, Hq, nreq, qtiles, G, causal, flags, SoftCap{0.f, 0.f},
+                       sl2, static_cast<bf16*>(out), lse);
+  }
 }
 
 template <int D>
 static void launch_ext_fmt(dim3 grid, hipStream_t s, const DevMap& m, const char* kp, const char* vp,
                            int64_t row_bytes, const void* q, int64_t tq, const int32_t* qo, int32_t Hq, int32_t G,
-                           int32_t causal, float sl2, void* out, float* lse) {
+                           int32_t causal, const int32_t* flags, float softcap, float sm_scale, void* out,
+                           float* lse) {
   if (m.fmt == MAP_TOKEN_TABLE)
-    launch_ext<D, SLOT_TABLE>(grid, s, m, kp, vp, row_bytes, q, tq, qo, Hq, G, causal, sl2, out, lse);
+    launch_ext<D, SLOT_TABLE>(grid, s, m, kp, vp, row_bytes, q, tq, qo, Hq, G, causal, flags, softcap, sm_scale, out,
+                              lse);
   else if (m.fmt == MAP_CONTIGUOUS)
-    launch_ext<D, SLOT_CONTIG>(grid, s, m, kp, vp, row_bytes, q, tq, qo, Hq, G, causal, sl2, out, lse);
+    launch_ext<D, SLOT_CONTIG>(grid, s, m, kp, vp, row_bytes, q, tq, qo, Hq, G, causal, flags, softcap, sm_scale, out,
+                               lse);
   else
-    launch_ext<D, SLOT_PAGES>(grid, s, m, kp, vp, row_bytes, q, tq, qo, Hq, G, causal, sl2, out, lse);
+    launch_ext<D, SLOT_PAGES>(grid, s, m, kp, vp, row_bytes, q, tq, qo, Hq, G, causal, flags, softcap, sm_scale, out,
+                              lse);
 }
 
 hipError_t launch_extend(const PoolInfo& p, int32_t layer, const void* q, int64_t total_q, const int32_t* qo_indptr,
-                         int32_t Hq,
-                         int32_t max_q_len, const DevMap& m, int32_t bs, int32_t max_kv_len, int32_t causal,
-                         float sm_scale, void* out, float* lse, hipStream_t s) {
+                         int32_t Hq, int32_t max_q_len, const DevMap& m, int32_t bs, int32_t max_kv_len,
+                         int32_t causal, const int32_t* causal_flags, float softcap, float sm_scale, void* out,
+                         float* lse, hipStream_t s) {
   (void)max_kv_len;
   if (bs == 0 || max_q_len == 0) return hipSuccess;
   // contiguous (ragged) maps read the caller's gathered K/V, paged maps the pool
@@ -410,12 +448,13 @@ hipError_t launch_extend(const PoolInfo& p, int32_t layer, const void* q, int64_
   const int bm = p.head_dim_qk == 128 ? ExtendCfg<128>::BM : ExtendCfg<64>::BM;
   const dim3 grid(1, (unsigned)((max_q_len + bm - 1) / bm), (unsigned)bs);
   const int64_t row_bytes = (int64_t)p.num_kv_heads * p.head_dim_qk * 2;  // one token row, all KV heads
-  const float sl2 = sm_scale * kLog2e;
   timer_before(s);
   if (p.head_dim_qk == 128)
-    launch_ext_fmt<128>(grid, s, m, kp, vp, row_bytes, q, total_q, qo_indptr, Hq, G, causal, sl2, out, lse);
+    launch_ext_fmt<128>(grid, s, m, kp, vp, row_bytes, q, total_q, qo_indptr, Hq, G, causal, causal_flags, softcap,
+                        sm_scale, out, lse);
   else
-    launch_ext_fmt<64>(grid, s, m, kp, vp, row_bytes, q, total_q, qo_indptr, Hq, G, causal, sl2, out, lse);
+    launch_ext_fmt<64>(grid, s, m, kp, vp, row_bytes, q, total_q, qo_indptr, Hq, G, causal, causal_flags, softcap,
+                       sm_scale, out, lse);
   hipError_t e = hipGetLastError();
   timer_after(s);
   return e;

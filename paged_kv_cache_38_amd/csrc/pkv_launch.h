@@ -123,7 +123,8 @@ hipError_t launch_decode(const PoolInfo& p, int32_t layer, const void* q, int32_
 bool extend_supported(const PoolInfo& p, int32_t num_q_heads);
 hipError_t launch_extend(const PoolInfo& p, int32_t layer, const void* q, int64_t total_q, const int32_t* qo_indptr,
                          int32_t num_q_heads, int32_t max_q_len, const DevMap& m, int32_t bs, int32_t max_kv_len,
-                         int32_t causal, float sm_scale, void* out, float* lse, hipStream_t s);
+                         int32_t causal, const int32_t* causal_flags, float softcap, float sm_scale, void* out,
+                         float* lse, hipStream_t s);
 
 hipError_t launch_validate(const PoolInfo& p, const DevMap& m, int32_t bs, int32_t max_kv_len,
                            const int32_t* is_dummy, long long* counts_dev, hipStream_t s);

@@ -135,21 +135,24 @@ def oracle_after_store(case: Case, vals: dict):
     return pk, pv
 
 
-def oracle_region(case: Case, vals: dict, name: str, pk=None, pv=None, requests=None):
+def oracle_region(case: Case, vals: dict, name: str, pk=None, pv=None, requests=None, softcap: float = 0.0):
     if pk is None:
         pk, pv = oracle_after_store(case, vals)
     r = case.regions[name]
     slots = [oracle.slots_from_token_table(case.req_to_token, case.req_pool_indices[i], r.kv_start[i], r.kv_lens[i])
              for i in range(case.bs)]
     g = case.geom
+    causal = r.causal if r.causal_flags is None else [bool(f) for f in r.causal_flags]
     return oracle.paged_attention(to_numpy_bits(vals["q"][name]), case.q_lens, pk, pv, g.dtype, slots,
-                                  case.sm_scale, r.causal, head_dim_v=g.head_dim_v, requests=requests)
+                                  case.sm_scale, causal, head_dim_v=g.head_dim_v, requests=requests,
+                                  softcap=softcap)
 
 
-def run_extend(dc: "DeviceCase", name: str, fmt: int, contiguous: bool = False):
+def run_extend(dc: "DeviceCase", name: str, fmt: int, contiguous: bool = False, softcap: float = 0.0):
     """Extend attention of one region through the C ABI; with `contiguous`,
     the region is first gathered by kv_gather and read back through a
-    CONTIGUOUS map (the ragged variant)."""
+    CONTIGUOUS map (the ragged variant).  Regions with per-request causal
+    flags, and any softcap, go through paged_extend_attn_ex."""
     c = dc.case
     g = c.geom
     reg = c.regions[name]
@@ -169,6 +172,11 @@ def run_extend(dc: "DeviceCase", name: str, fmt: int, contiguous: bool = False):
         _, kv_lens, maxl = dc.region_tensors(name)
         m = P.make_kv_map(P.PKV_MAP_CONTIGUOUS, kv_lens, maxl, k=ko[:tot] if tot else ko[:0], v=vo[:tot] if tot else vo[:0],
                           cu_seqlens_k=cu_d)
-    P.paged_extend_attn(dc.pool, dc.layer, dc.q[name], qo, max_q, m, reg.causal, c.sm_scale, out, lse)
+    if reg.causal_flags is None and softcap == 0.0:
+        P.paged_extend_attn(dc.pool, dc.layer, dc.q[name], qo, max_q, m, reg.causal, c.sm_scale, out, lse)
+    else:
+        flags = None if reg.causal_flags is None else i32(reg.causal_flags, dc.device)
+        P.paged_extend_attn_ex(dc.pool, dc.layer, dc.q[name], qo, max_q, m, c.sm_scale, out, lse, causal=reg.causal,
+                               causal_flags=flags, softcap=softcap)
     torch.cuda.synchronize()
     return out, lse

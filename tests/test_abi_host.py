@@ -211,3 +211,24 @@ def test_allocator_argument_checks_before_launch(lib):
     assert lib.write_req_to_token(t, 4, 64, lens, lens, lens, None, 10, None, 2, 64, None) == L.PKV_EINVAL
     assert lib.write_req_to_token(t, 4, 2**27, lens, lens, lens, out, 10, None, 2, 2**26 + 1, None) \
         == L.PKV_EUNSUPPORTED
+
+
+def test_extend_options_checked_before_launch(lib):
+    st, h = make_pool(lib, desc(dtype=1))
+    assert st == 0
+    try:
+        m = L.KVMapStruct()
+        m.fmt, m.bs, m.kv_lens, m.max_kv_len = L.PKV_MAP_TOKEN_TABLE, 4, 0x1000, 100
+        m.req_to_token, m.table_rows, m.table_width, m.req_pool_indices = 0x2000, 5, 128, 0x3000
+        args = [h, 0, 0x4000, 40, 0x5000, 4, 10, C.byref(m)]
+        assert lib.paged_extend_attn_ex(*args, None, 0.125, 0x6000, None, None) == L.PKV_EINVAL
+        for bad in (-1.0, float("inf"), float("nan")):
+            opts = L.ExtendOpts(1, None, bad)
+            assert lib.paged_extend_attn_ex(*args, C.byref(opts), 0.125, 0x6000, None, None) == L.PKV_EINVAL
+        opts = L.ExtendOpts(1, None, 0.0)
+        assert lib.paged_extend_attn_ex(*args, C.byref(opts), -1.0, 0x6000, None, None) == L.PKV_EINVAL
+        m.bs = 0  # nothing to do, options accepted
+        opts = L.ExtendOpts(0, 0x7000, 30.0)
+        assert lib.paged_extend_attn_ex(*args, C.byref(opts), 0.125, 0x6000, None, None) == 0
+    finally:
+        lib.kv_pool_destroy(h)

@@ -104,3 +104,66 @@ def test_extend_repeatable_bitwise():
     a = run_extend(dc, "cross", P.PKV_MAP_BLOCK_TABLE)
     b = run_extend(dc, "cross", P.PKV_MAP_BLOCK_TABLE)
     assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16)) and torch.equal(a[1], b[1])
+
+
+# --------------------------------------------------------------------------
+# mixed causal/full spans and softcap (extend options)
+# --------------------------------------------------------------------------
+
+SPANS = ((5, True), (40, False), (17, True), (70, False), (1, True))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_mixed_span_segments_match_oracle(fmt):
+    """Rows of causal and full spans (several not aligned to a tile or a page)
+    run as one call whose requests are the segments, each with its flag."""
+    case = W.mixed_spans(seed=1, rows=3, spans=SPANS, num_q_heads=8, num_kv_heads=2, head_dim=128)
+    print(f"mixed spans fmt {fmt}: {case.bs} segments", flush=True)
+    vals = W.make_values(case, canary=True)
+    dc = DeviceCase(case, vals)
+    dc.store()
+    out, lse = run_extend(dc, "self", fmt)
+    ref_o, ref_l = oracle_region(case, vals, "self")
+    assert_attn_close(out, ref_o, "bf16", f"mixed spans fmt {fmt}")
+    assert_lse_close(lse, ref_l, "bf16", f"mixed spans fmt {fmt}")
+
+
+def test_mixed_spans_flags_equal_separate_calls_bitwise():
+    """Per-request flags give the same bits as running the causal and the
+    full segments in two calls with one flag each."""
+    case = W.mixed_spans(seed=2, rows=2, spans=SPANS, num_q_heads=4, num_kv_heads=4, head_dim=64)
+    vals = W.make_values(case)
+    dc = DeviceCase(case, vals)
+    dc.store()
+    out, lse = run_extend(dc, "self", P.PKV_MAP_CSR)
+    reg = case.regions["self"]
+    flags = reg.causal_flags.copy()
+    for value in (0, 1):
+        reg.causal_flags = None
+        reg.causal = bool(value)
+        o1, l1 = run_extend(dc, "self", P.PKV_MAP_CSR)
+        qo = np.concatenate([[0], np.cumsum(case.q_lens)])
+        for i in np.nonzero(flags == value)[0]:
+            a, b = int(qo[i]), int(qo[i + 1])
+            assert torch.equal(out[a:b].view(torch.int16), o1[a:b].view(torch.int16))
+            assert torch.equal(lse[a:b], l1[a:b])
+    reg.causal_flags = flags
+
+
+@pytest.mark.parametrize("softcap", [0.5, 5.0, 30.0])
+@pytest.mark.parametrize("head_dim", [64, 128])
+def test_softcap_matches_oracle(softcap, head_dim):
+    case = encdec(7, num_heads=4, head_dim=head_dim, bs=4, enc_len=260, new_range=(1, 140))
+    vals = W.make_values(case, canary=True)
+    # larger scores so the cap bites
+    vals["q"] = {k: (v.float() * 4).to(v.dtype) for k, v in vals["q"].items()}
+    dc = DeviceCase(case, vals)
+    dc.store()
+    for region in ("self", "cross"):
+        out, lse = run_extend(dc, region, P.PKV_MAP_CSR, softcap=softcap)
+        ref_o, ref_l = oracle_region(case, vals, region, softcap=softcap)
+        assert_attn_close(out, ref_o, "bf16", f"softcap {softcap} {region}")
+        assert_lse_close(lse, ref_l, "bf16", f"softcap {softcap} {region}")
+        # the ragged variant takes the same options
+        out2, _ = run_extend(dc, region, P.PKV_MAP_TOKEN_TABLE, contiguous=True, softcap=softcap)
+        assert torch.equal(out.view(torch.int16), out2.view(torch.int16))

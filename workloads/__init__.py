@@ -12,6 +12,7 @@ from .cases import (  # noqa: F401
     gqa_prefix_share,
     mla_decode,
     encdec_extend,
+    mixed_spans,
     make_values,
     to_numpy_bits,
     CONFIG_BUILDERS,

@@ -78,6 +78,7 @@ class Region:
     kv_lens: np.ndarray  # int32 [bs]
     page_lists: List[np.ndarray]  # physical pages in logical order, per request
     causal: bool
+    causal_flags: Optional[np.ndarray] = None  # int32 [bs], per-request mask (mixed causal/full segments)
 
 
 @dataclass
@@ -366,12 +367,63 @@ def encdec_extend(seed: int = 0, bs: int = 32, enc_len: int = 1500, prefix_range
     )
 
 
+def mixed_spans(seed: int = 0, rows: int = 4, spans=((128, True), (2048, False)), num_q_heads: int = 32,
+                num_kv_heads: int = 8, head_dim: int = 128, page_size: int = 16) -> Case:
+    """Rows of mixed causal and full spans, bf16, written once and attended
+    as native segments (the vLLM-Omni notes, "Attention execution": a causal
+    span [s, e) is Q[s:e] over K[:e] with the causal flag, a full span
+    [a, b) is Q[a:b] over K[:b] without it; the first denoising step writes
+    the complete sequence once).  Default: 4 rows (two requests, one
+    conditional and one unconditional branch each) of a 128-token causal
+    text span followed by a 2048-token full image span; GQA 32 / 8 query /
+    KV heads, head_dim 128, page_size 16.  The sizes are synthetic choices:
+    the notes give none.  Each segment is one request of the batch, every
+    segment of a row reading the same table row."""
+    rs, rp, vseed, qseed = _streams(6, seed, (rows, len(spans)))
+    ps = page_size
+    row_len = int(sum(n for n, _ in spans))
+    pages_per_row = _cdiv(row_len, ps)
+    num_pages = _cdiv(rows * pages_per_row * 12, 10)
+    geom = Geometry("bf16", ps, num_pages, num_kv_heads, head_dim, head_dim, False, num_q_heads)
+    perm = rp.permutation(num_pages)
+    table = _new_table(rows + 1, _round32(row_len), geom)
+    row_ids = rs.permutation(rows).astype(np.int32)
+    bs = rows * len(spans)
+    rpi, q_lens, kv_lens, flags, lists, out_loc = [], [], [], [], [], []
+    for r in range(rows):
+        pages = perm[r * pages_per_row:(r + 1) * pages_per_row].astype(np.int64)
+        tr = row_ids[r]
+        table[tr, :row_len] = _expand(pages, ps, row_len)
+        out_loc.append(table[tr, :row_len])
+        start = 0
+        for n, causal in spans:
+            end = start + int(n)
+            rpi.append(tr)
+            q_lens.append(int(n))
+            kv_lens.append(end)
+            flags.append(1 if causal else 0)
+            lists.append(pages[:_cdiv(end, ps)])
+            start = end
+    tails = _tail_slots([perm[r * pages_per_row:(r + 1) * pages_per_row] for r in range(rows)],
+                        np.full(rows, row_len, np.int32), ps)
+    region = Region(np.zeros(bs, np.int32), np.asarray(kv_lens, np.int32), lists, causal=True,
+                    causal_flags=np.asarray(flags, np.int32))
+    return Case(
+        name=f"mixed_spans_r{rows}", geom=geom, bs=bs, req_to_token=table, req_pool_indices=np.asarray(rpi, np.int32),
+        q_lens=np.asarray(q_lens, np.int32), regions={"self": region},
+        out_loc=np.concatenate(out_loc).astype(np.int32), sm_scale=1.0 / np.sqrt(float(head_dim)), value_scale=1.0,
+        value_seed=vseed, query_seed=qseed, free_pages=perm[rows * pages_per_row:].astype(np.int64),
+        tail_slots=np.concatenate(tails) if tails else np.zeros(0, np.int64),
+    )
+
+
 CONFIG_BUILDERS = {
     1: tiny_decode,
     2: qwen3_decode,
     3: gqa_prefix_share,
     4: mla_decode,
     5: encdec_extend,
+    6: mixed_spans,
 }
 
 
