@@ -11,7 +11,8 @@ log-sum-exp merge).  Inputs are resident in HBM before timing starts.
 
 Other workloads (--workload): gqa_prefix_share_ps16 / _ps64 (batch-256 GQA
 decode with shared 2048-token prefixes), mla_decode (latent 576/512, 128
-heads, page_size 64), encdec_extend (Whisper-shaped causal + cross extend
+heads, page_size 64), mla_verify (the same pool, 32 heads x 4 draft tokens
+verified per request), encdec_extend (Whisper-shaped causal + cross extend
 over a paged prefix), encdec_extend_ragged (the same through kv_gather and
 contiguous K/V), mixed_spans_extend / _softcap (rows of a causal text span
 and a full image span run as per-segment-flagged requests, without and with
@@ -250,6 +251,83 @@ class DecodeBench:
                 "sample": f"{reqs} request decodes ({reqs / c.bs:.2f} passes over the {c.bs}-request batch, "
                           f"{toks} KV tokens) by the numpy fp64 oracle (gather + BLAS matmul per request), "
                           f"{dt:.1f} s"}
+
+
+class VerifyBench(DecodeBench):
+    """Target-verification step over the MLA pool: kv_store of the drafts,
+    build_kv_indices (block table), then paged_verify_attn (drafts folded
+    into heads, bottom-right causal among them)."""
+
+    kernel_name = "MLA decode kernel, target verification (drafts folded into heads)"
+    tokens_label = "verified_tokens_per_s"
+
+    def __init__(self, case, n_draft: int, dev="cuda"):
+        super().__init__(case, "block_table", dev)
+        g = case.geom
+        self.n = n_draft
+        self.qv = self.q.view(case.bs, n_draft, g.num_q_heads, g.head_dim_qk)
+        self.out = self.torch.empty((case.bs, n_draft, g.num_q_heads, g.head_dim_v), dtype=self.torch.bfloat16,
+                                    device=dev)
+        self.lse = self.torch.empty((case.bs, n_draft, g.num_q_heads), dtype=self.torch.float32, device=dev)
+        nb = self.P.paged_decode_workspace_bytes(self.pool, case.bs, n_draft * g.num_q_heads, self.max_len)
+        self.ws = self.torch.empty(max(nb, 256), dtype=self.torch.uint8, device=dev)
+
+    def step(self, timers=None):
+        P, c = self.P, self.case
+        P.kv_store(self.pool, 0, self.k_new, self.v_new, self.out_loc)
+        P.build_kv_indices(P.PKV_MAP_BLOCK_TABLE, self.table, self.rpi, self.kv_start, self.kv_lens,
+                           c.geom.page_size, self.max_len, None, self.bt)
+        if timers:
+            P.pkv_set_kernel_timer(*timers[0])
+        P.paged_verify_attn(self.pool, 0, self.qv, self.map, c.sm_scale, self.out, self.lse, self.ws)
+
+    def kernel_bytes(self, logical: bool = False) -> int:
+        """Every distinct latent row once, a page id share per token, and the
+        queries of every draft."""
+        c, g = self.case, self.case.geom
+        return int(self.unique_tokens * _row_bytes(g) + self.logical_tokens * 4.0 / g.page_size +
+                   c.bs * self.n * g.num_q_heads * g.head_dim_qk * g.elem_bytes)
+
+    def step_bytes(self) -> int:
+        c, g = self.case, self.case.geom
+        out_b = c.bs * self.n * g.num_q_heads * g.head_dim_v * g.elem_bytes
+        return self.kernel_bytes() + out_b + c.n_new * (2 * _row_bytes(g) + 4)
+
+    def kernel_flops(self) -> int:
+        """Draft j of a request sees L - n + j + 1 keys."""
+        c, g = self.case, self.case.geom
+        L = c.regions["self"].kv_lens.astype(np.int64)
+        pairs = int(np.sum(self.n * L - self.n * (self.n - 1) // 2))
+        return 2 * pairs * g.num_q_heads * (g.head_dim_qk + g.head_dim_v)
+
+    def tokens_per_step(self) -> int:
+        return self.case.bs * self.n
+
+    def cpu_baseline(self, budget_s: float):
+        import oracle
+        from workloads.cases import to_numpy_bits
+
+        c, g = self.case, self.case.geom
+        r = c.regions["self"]
+        self.torch.cuda.synchronize()
+        pk = to_numpy_bits(self.pool.flat("k", 0))
+        q = to_numpy_bits(self.q)
+        slots = [oracle.slots_from_token_table(c.req_to_token, c.req_pool_indices[i], r.kv_start[i], r.kv_lens[i])
+                 for i in range(c.bs)]
+        reqs, toks, t0 = 0, 0, time.perf_counter()
+        while time.perf_counter() - t0 <= budget_s:
+            for i in range(c.bs):
+                oracle.paged_attention(q, c.q_lens, pk, None, g.dtype, slots, c.sm_scale, True,
+                                       head_dim_v=g.head_dim_v, requests=[i])
+                reqs += 1
+                toks += int(r.kv_lens[i])
+                if time.perf_counter() - t0 > budget_s:
+                    break
+        dt = time.perf_counter() - t0
+        return {"value": round(toks * _row_bytes(g) / dt / 1e9, 4), "unit": "GB/s", "cores": _blas_threads(),
+                "kind": "oracle", "verified_tokens_per_s": round(reqs * self.n / dt, 3),
+                "sample": f"{reqs} request verifications of {self.n} drafts ({toks} KV tokens) by the numpy fp64 "
+                          f"oracle, {dt:.1f} s"}
 
 
 # ---------------------------------------------------------------------------
@@ -503,6 +581,12 @@ def build_workload(name: str):
             "workload": "mla_decode_bf16", "batch": 128, "num_q_heads": 128, "head_dim_qk": 576, "head_dim_v": 512,
             "page_size": 64, "kv_len": "U[4096,16384]",
             "step": "kv_store + build_kv_indices(BLOCK_TABLE) + paged_decode_attn"}
+    if name == "mla_verify":
+        return VerifyBench(W.mla_decode(seed=0, num_q_heads=32, num_draft=4), 4), {
+            "workload": "mla_target_verify_bf16", "batch": 128, "num_q_heads": 32, "num_draft": 4,
+            "rows_per_request": 128, "head_dim_qk": 576, "head_dim_v": 512, "page_size": 64,
+            "kv_len": "U[4096,16384] including the drafts",
+            "step": "kv_store (drafts) + build_kv_indices(BLOCK_TABLE) + paged_verify_attn"}
     if name in ("encdec_extend", "encdec_extend_ragged"):
         ragged = name.endswith("ragged")
         return ExtendBench(W.encdec_extend(seed=0), ragged), {

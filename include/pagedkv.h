@@ -229,6 +229,26 @@ int paged_decode_attn(const pkv_pool* pool, int32_t layer, const void* q, int32_
                       const pkv_kv_map* map, float sm_scale, void* out, float* lse, void* workspace,
                       size_t ws_bytes, void* stream);
 
+/* Target verification over a latent (MLA) pool ([BACKEND]
+ * init_forward_metadata, the target-verify branch: the sequence lengths
+ * include the draft tokens and the drafts multiply the head count).  Each
+ * request's num_draft draft tokens are checked in one pass: map->kv_lens
+ * counts the keys including the drafts (stored by kv_store first), and the
+ * drafts' heads are folded into the head dimension of the decode kernel.
+ * Draft j of request i sits at position kv_lens[i] - num_draft + j and sees
+ * keys 0 .. that position (bottom-right, as paged_extend_attn's causal mode).
+ *   q: device [bs][num_draft][num_q_heads][576] bf16.
+ *   out: device [bs][num_draft][num_q_heads][512] bf16; lse nullable float
+ *     [bs][num_draft][num_q_heads].  A draft that sees no key
+ *     (kv_lens[i] < num_draft) gets out = 0 and lse = -inf.
+ *   workspace: device, >= paged_decode_workspace_bytes(pool, bs,
+ *     num_draft * num_q_heads, max_kv_len), 256-byte aligned.
+ * Supported: LATENT bf16 576/512 pools with num_draft * num_q_heads in
+ * {16, 32, 64, 128} (else PKV_EUNSUPPORTED); sm_scale positive and finite. */
+int paged_verify_attn(const pkv_pool* pool, int32_t layer, const void* q, int32_t num_q_heads, int32_t num_draft,
+                      const pkv_kv_map* map, float sm_scale, void* out, float* lse, void* workspace, size_t ws_bytes,
+                      void* stream);
+
 /* ---- paged extend / prefill (a7, a8, a9) -------------------------------- */
 
 /* Each request's qo_indptr[i+1] - qo_indptr[i] new query tokens attend over

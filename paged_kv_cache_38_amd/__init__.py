@@ -36,7 +36,8 @@ from ._lib import (  # noqa: F401
 __all__ = [
     "Pool", "KVMap", "kv_pool_bytes", "kv_pool_create", "kv_pool_destroy", "kv_pool_padding_page",
     "kv_pool_token_bytes", "kv_store", "build_kv_indices", "make_kv_map", "paged_decode_workspace_bytes",
-    "paged_decode_attn", "paged_extend_attn", "paged_extend_attn_ex", "kv_gather", "kv_validate",
+    "paged_decode_attn", "paged_verify_attn", "paged_extend_attn", "paged_extend_attn_ex", "kv_gather",
+    "kv_validate",
     "pkv_set_kernel_timer", "library",
     "FreeList", "kv_free_list_create", "kv_free_list_init", "kv_alloc", "kv_alloc_extend", "kv_alloc_decode",
     "kv_free", "write_req_to_token",
@@ -250,6 +251,22 @@ def paged_decode_attn(pool: Pool, layer: int, q: torch.Tensor, kv_map: KVMap, sm
                                        C.byref(kv_map.struct), float(sm_scale), _dev(out, "out", pool.dtype),
                                        _dev(lse, "lse", torch.float32), ws_ptr, ws_bytes, _stream(stream)),
             "paged_decode_attn")
+
+
+def paged_verify_attn(pool: Pool, layer: int, q: torch.Tensor, kv_map: KVMap, sm_scale: float, out: torch.Tensor,
+                      lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                      stream=None) -> None:
+    """Target verification over a latent pool: q ``[bs, num_draft, Hq, 576]``
+    -> out ``[bs, num_draft, Hq, 512]``; workspace of at least
+    paged_decode_workspace_bytes(pool, bs, num_draft * Hq, max_kv_len) bytes."""
+    if q.dim() != 4 or out.shape[:3] != q.shape[:3]:
+        raise ValueError("q must be [bs, num_draft, Hq, 576] and out [bs, num_draft, Hq, 512]")
+    ws_ptr = _dev(workspace, "workspace")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    L.check(L.load().paged_verify_attn(pool.handle, layer, _dev(q, "q", pool.dtype), q.shape[2], q.shape[1],
+                                       C.byref(kv_map.struct), float(sm_scale), _dev(out, "out", pool.dtype),
+                                       _dev(lse, "lse", torch.float32), ws_ptr, ws_bytes, _stream(stream)),
+            "paged_verify_attn")
 
 
 def paged_extend_attn(pool: Pool, layer: int, q: torch.Tensor, qo_indptr: torch.Tensor, max_q_len: int,

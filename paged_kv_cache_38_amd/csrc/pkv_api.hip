@@ -318,6 +318,33 @@ int paged_decode_attn(const pkv_pool* pool, int32_t layer, const void* q, int32_
                        "paged_decode_attn");
 }
 
+int paged_verify_attn(const pkv_pool* pool, int32_t layer, const void* q, int32_t num_q_heads, int32_t num_draft,
+                      const pkv_kv_map* map, float sm_scale, void* out, float* lse, void* workspace, size_t ws_bytes,
+                      void* stream) {
+  if (int st = check_pool(pool)) return st;
+  if (int st = check_layer(pool, layer)) return st;
+  pkv::DevMap dm;
+  if (int st = make_devmap(pool, map, false, &dm)) return st;
+  if (num_q_heads <= 0 || num_draft <= 0) return fail(PKV_EINVAL, "num_q_heads and num_draft must be positive");
+  if (!(sm_scale > 0.0f) || std::isinf(sm_scale)) return fail(PKV_EINVAL, "sm_scale must be positive and finite");
+  const int64_t rows = (int64_t)num_q_heads * num_draft;
+  if (pool->desc.kind != PKV_KIND_LATENT || rows > 128 || !pkv::decode_supported(pool->info, (int32_t)rows))
+    return fail(PKV_EUNSUPPORTED,
+                "target verification needs a latent bf16 576/512 pool and num_draft * num_q_heads in {16, 32, 64, "
+                "128} (got %d x %d)", num_draft, num_q_heads);
+  if (map->bs == 0) return ok();
+  if (!q || !out) return fail(PKV_EINVAL, "null q or out");
+  if (!aligned16(q)) return fail(PKV_EALIGN, "q must be 16-byte aligned");
+  const pkv::DecodePlan plan = pkv::plan_decode(pool->info, map->bs, (int32_t)rows, map->max_kv_len);
+  const size_t need = pkv::decode_workspace_bytes(pool->info, plan, map->bs, (int32_t)rows);
+  if (ws_bytes < need) return fail(PKV_ECAPACITY, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  if (need > 0 && (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)))
+    return fail(PKV_EALIGN, "workspace must be non-null and 256-byte aligned");
+  return device_status(pkv::launch_mla_verify(pool->info, layer, q, (int32_t)rows, num_draft, dm, map->bs, plan,
+                                              sm_scale * pkv::kLog2e, out, lse, workspace, (hipStream_t)stream),
+                       "paged_verify_attn");
+}
+
 namespace {
 int extend_call(const char* call, const pkv_pool* pool, int32_t layer, const void* q, int64_t total_q,
                 const int32_t* qo_indptr, int32_t num_q_heads, int32_t max_q_len, const pkv_kv_map* map,

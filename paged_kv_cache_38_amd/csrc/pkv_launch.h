@@ -112,6 +112,11 @@ int32_t device_cu_count();
 hipError_t launch_mla_decode(const PoolInfo& p, int32_t layer, const void* q, int32_t num_q_heads, const DevMap& m,
                              int32_t bs, const DecodePlan& plan, float scale_log2, void* out, float* lse, void* ws,
                              hipStream_t s);
+// Target verification over a latent pool: n_draft query tokens per request,
+// folded into Hq = n_draft * heads rows, bottom-right causal among the drafts.
+hipError_t launch_mla_verify(const PoolInfo& p, int32_t layer, const void* q, int32_t Hq, int32_t n_draft,
+                             const DevMap& m, int32_t bs, const DecodePlan& plan, float sl2, void* out, float* lse,
+                             void* ws, hipStream_t s);
 DecodePlan plan_decode(const PoolInfo& p, int32_t bs, int32_t num_q_heads, int32_t max_kv_len);
 size_t decode_workspace_bytes(const PoolInfo& p, const DecodePlan& plan, int32_t bs, int32_t num_q_heads);
 bool decode_supported(const PoolInfo& p, int32_t num_q_heads);

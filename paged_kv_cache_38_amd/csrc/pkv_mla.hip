@@ -130,11 +130,19 @@ __device__ __forceinline__ void mla_pv(f32x4 (&acc)[HB][kMlaV / 16], const char*
 // ---------------------------------------------------------------------------
 // Main kernel: one workgroup per run (one per CU).
 // ---------------------------------------------------------------------------
-template <int HB, int W>
+// VERIFY (target verification, [BACKEND] init_forward_metadata's
+// target-verify branch): every request carries n_draft query tokens whose
+// heads are folded into the head dimension (row = draft * hq_base + head,
+// HQ = n_draft * hq_base rows), and the keys include the drafts.  Draft j
+// sits at position L - n_draft + j and sees keys 0 .. L - n_draft + j
+// (bottom-right, as in extend), so the tiles holding the last n_draft - 1
+// keys take a per-row mask.
+template <int HB, int W, bool VERIFY>
 __global__ void __launch_bounds__(64 * W, 1) mla_decode_kernel(
     const char* kpool, const bf16* __restrict__ q, int32_t HQ, const int32_t* __restrict__ header,
     const int32_t* __restrict__ meta, float scale_log2, bf16* __restrict__ out, float* __restrict__ lse,
-    float* __restrict__ ws_o, float* __restrict__ ws_lse, int32_t* __restrict__ fallback) {
+    float* __restrict__ ws_o, float* __restrict__ ws_lse, int32_t* __restrict__ fallback,
+    const int32_t* __restrict__ kv_lens, int32_t n_draft, int32_t hq_base) {
   constexpr int NI = MlaShape<HB, W>::NI, RPW = MlaShape<HB, W>::RPW;
   constexpr int NK = kMlaQK / 32;  // 18 k-steps of the score product
   constexpr int NC = kMlaV / 16;   // 32 column blocks of the output
@@ -197,6 +205,14 @@ __global__ void __launch_bounds__(64 * W, 1) mla_decode_kernel(
   bf16x8 qf[HB][NK];
   float m_ref[HB], l_part[HB];
   float s_over[HB];  // raw score above which P could overflow (kMlaHeadroom past the reference)
+  // VERIFY: each row's draft index, and the request's first key that the
+  // first draft cannot see
+  int jrow[HB];
+  int k_zone = 0;
+  if constexpr (VERIFY) {
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) jrow[hb] = (hw + hb * 16 + col) / hq_base;
+  }
 
   // Per iteration r a wave issues meta(r + 6) then tile(r + 3); tile(r) is
   // then followed in the queue by meta(r + 4), tile(r + 1), meta(r + 5),
@@ -243,6 +259,7 @@ __global__ void __launch_bounds__(64 * W, 1) mla_decode_kernel(
         for (int kk = 0; kk < NK; ++kk) qf[hb][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + kk * 32));
         l_part[hb] = 0.f;
       }
+      if constexpr (VERIFY) k_zone = kv_lens[i] - n_draft + 1;
       // Wait for the queries here, once per piece.  Left pending across the
       // branch, they would make the compiler wait on the memory counter in
       // the score loop of every tile, where the tile DMAs (invisible to it)
@@ -306,8 +323,22 @@ __global__ void __launch_bounds__(64 * W, 1) mla_decode_kernel(
     // and stays fixed for the piece, so the accumulators are never
     // rescaled; a later score more than kMlaHeadroom above it (P could
     // overflow) sends the request to the exact fallback in the merge pass.
-    // keys past the request's end (its last tile only) get -inf in place
-    if (valid < kMlaT) {
+    // keys past the request's end (its last tile only) get -inf in place;
+    // VERIFY: so do keys past each draft's position, in the tiles that
+    // reach past the first draft's
+    if constexpr (VERIFY) {
+      if (valid < kMlaT || jt * kMlaT + kMlaT > k_zone) {
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
+          const int lim = min(valid, k_zone + jrow[hb] - jt * kMlaT);
+#pragma unroll
+          for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+              if (16 * a + 4 * grp + rr >= lim) sacc[a][hb][rr] = -INFINITY;
+        }
+      }
+    } else if (valid < kMlaT) {
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
@@ -329,6 +360,9 @@ __global__ void __launch_bounds__(64 * W, 1) mla_decode_kernel(
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) mt = fmaxf(mt, sacc[a][hb][rr]);
         m_ref[hb] = max_xor16_32(mt) * scale_log2;
+        // VERIFY: a draft that sees none of the piece's first tile sees none
+        // of the piece (keys only grow): any finite reference gives P = 0
+        if constexpr (VERIFY) m_ref[hb] = m_ref[hb] == -INFINITY ? 0.f : m_ref[hb];
         s_over[hb] = (m_ref[hb] + kMlaHeadroom) / scale_log2;
       }
       float ps = 0.f;
@@ -369,18 +403,21 @@ __global__ void __launch_bounds__(64 * W, 1) mla_decode_kernel(
           const int hr = 4 * grp + rr;
           const float lr = shfl(lt, hr);
           const float mr = shfl(m_ref[hb], hr);
-          const float inv = 1.0f / lr;
+          // (VERIFY: a piece none of whose keys a draft sees gives o = 0
+          // and lse = -inf, which the merge weighs by zero)
+          const bool any = !VERIFY || lr > 0.f;
+          const float inv = any ? 1.0f / lr : 0.f;
           const int64_t row = row0 + hb * 16 + hr;
           if (direct) {
             bf16* ob = out + row * kMlaV + col;
 #pragma unroll
             for (int cb = 0; cb < NC; ++cb) ob[cb * 16] = (bf16)(acc_get(acc[hb][cb][rr]) * inv);
-            if (lse && col == 0) lse[row] = (mr + __log2f(lr)) * kLn2;
+            if (lse && col == 0) lse[row] = any ? (mr + __log2f(lr)) * kLn2 : -INFINITY;
           } else {
             float* wb = ws_o + row * kMlaV + col;
 #pragma unroll
             for (int cb = 0; cb < NC; ++cb) wb[cb * 16] = acc_get(acc[hb][cb][rr]) * inv;
-            if (col == 0) ws_lse[row] = (mr + __log2f(lr)) * kLn2;
+            if (col == 0) ws_lse[row] = any ? (mr + __log2f(lr)) * kLn2 : -INFINITY;
           }
         }
       }
@@ -438,7 +475,8 @@ __global__ void __launch_bounds__(256) mla_merge_kernel(int32_t bs, int32_t Hq, 
                                                         const float* __restrict__ ws_lse, const char* kpool,
                                                         const bf16* __restrict__ q, const int32_t* __restrict__ meta,
                                                         const int32_t* __restrict__ kv_lens, float scale_log2,
-                                                        bf16* __restrict__ out, float* __restrict__ lse) {
+                                                        bf16* __restrict__ out, float* __restrict__ lse,
+                                                        int32_t n_draft, int32_t hq_base) {
   const int lane = threadIdx.x & 63;
   const int64_t idx = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (idx >= (int64_t)bs * Hq) return;
@@ -453,7 +491,15 @@ __global__ void __launch_bounds__(256) mla_merge_kernel(int32_t bs, int32_t Hq, 
   }
   const int P = prefix[i];
   if (fallback[i]) {
-    const int L = min(kv_lens[i], T * kMlaT);
+    // keys this row sees (all of them for decode, where n_draft = 1 and
+    // h < hq_base)
+    const int L = min(min(kv_lens[i], T * kMlaT), kv_lens[i] - n_draft + 1 + h / hq_base);
+    if (L <= 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) op[e] = (bf16)0.0f;
+      if (lse && lane == 0) lse[idx] = -INFINITY;
+      return;
+    }
     mla_exact_one(kpool, q + idx * kMlaQK, meta, P, L, scale_log2, lane, op, lse ? lse + idx : nullptr);
     return;
   }
@@ -462,6 +508,12 @@ __global__ void __launch_bounds__(256) mla_merge_kernel(int32_t bs, int32_t Hq, 
   if (b0 == b1) return;
   float mx = -INFINITY;
   for (int b = b0; b <= b1; ++b) mx = fmaxf(mx, ws_lse[((int64_t)b + i) * Hq + h]);
+  if (mx == -INFINITY) {  // a draft that sees no key at all (kv_lens below n_draft)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) op[e] = (bf16)0.0f;
+    if (lse && lane == 0) lse[idx] = -INFINITY;
+    return;
+  }
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float sum = 0.f;
   for (int b = b0; b <= b1; ++b) {
@@ -503,13 +555,25 @@ DecodePlan plan_mla_decode(const PoolInfo& p, int32_t bs, int32_t Hq, int32_t ma
 
 template <int HB, int W>
 static void launch_mla_main(int32_t runs, int32_t Hq, hipStream_t s, const char* kp, const void* q, const StreamWs& w,
-                            float sl2, void* out, float* lse) {
-  hipLaunchKernelGGL((mla_decode_kernel<HB, W>), dim3(runs), dim3(64 * W), 0, s, kp, static_cast<const bf16*>(q), Hq,
-                     w.header, w.meta, sl2, static_cast<bf16*>(out), lse, w.o, w.lse, w.fallback);
+                            float sl2, void* out, float* lse, const int32_t* kv_lens, int32_t n_draft) {
+  if (n_draft > 1)
+    hipLaunchKernelGGL((mla_decode_kernel<HB, W, true>), dim3(runs), dim3(64 * W), 0, s, kp,
+                       static_cast<const bf16*>(q), Hq, w.header, w.meta, sl2, static_cast<bf16*>(out), lse, w.o,
+                       w.lse, w.fallback, kv_lens, n_draft, Hq / n_draft);
+  else
+    hipLaunchKernelGGL((mla_decode_kernel<HB, W, false>), dim3(runs), dim3(64 * W), 0, s, kp,
+                       static_cast<const bf16*>(q), Hq, w.header, w.meta, sl2, static_cast<bf16*>(out), lse, w.o,
+                       w.lse, w.fallback, kv_lens, 1, Hq);
 }
 
 hipError_t launch_mla_decode(const PoolInfo& p, int32_t layer, const void* q, int32_t Hq, const DevMap& m, int32_t bs,
                              const DecodePlan& plan, float sl2, void* out, float* lse, void* ws, hipStream_t s) {
+  return launch_mla_verify(p, layer, q, Hq, 1, m, bs, plan, sl2, out, lse, ws, s);
+}
+
+hipError_t launch_mla_verify(const PoolInfo& p, int32_t layer, const void* q, int32_t Hq, int32_t n_draft,
+                             const DevMap& m, int32_t bs, const DecodePlan& plan, float sl2, void* out, float* lse,
+                             void* ws, hipStream_t s) {
   StreamWs w;
   stream_ws_layout(bs, plan.chunk, plan.max_splits, Hq, kMlaV, ws, &w);
   const int32_t runs = plan.max_splits;
@@ -517,17 +581,17 @@ hipError_t launch_mla_decode(const PoolInfo& p, int32_t layer, const void* q, in
   if (e != hipSuccess) return e;
   const char* kp = p.k_layer(layer);
   timer_before(s);
-  if (Hq == 128) launch_mla_main<2, 4>(runs, Hq, s, kp, q, w, sl2, out, lse);
-  else if (Hq == 64) launch_mla_main<1, 4>(runs, Hq, s, kp, q, w, sl2, out, lse);
-  else if (Hq == 32) launch_mla_main<1, 2>(runs, Hq, s, kp, q, w, sl2, out, lse);
-  else launch_mla_main<1, 1>(runs, Hq, s, kp, q, w, sl2, out, lse);
+  if (Hq == 128) launch_mla_main<2, 4>(runs, Hq, s, kp, q, w, sl2, out, lse, m.kv_lens, n_draft);
+  else if (Hq == 64) launch_mla_main<1, 4>(runs, Hq, s, kp, q, w, sl2, out, lse, m.kv_lens, n_draft);
+  else if (Hq == 32) launch_mla_main<1, 2>(runs, Hq, s, kp, q, w, sl2, out, lse, m.kv_lens, n_draft);
+  else launch_mla_main<1, 1>(runs, Hq, s, kp, q, w, sl2, out, lse, m.kv_lens, n_draft);
   e = hipGetLastError();
   timer_after(s);
   if (e != hipSuccess) return e;
   const unsigned mblocks = (unsigned)(((int64_t)bs * Hq + 3) / 4);
   hipLaunchKernelGGL(mla_merge_kernel, dim3(mblocks), dim3(256), 0, s, bs, Hq, w.header, w.prefix, w.ntiles,
                      w.fallback, w.o, w.lse, kp, static_cast<const bf16*>(q), w.meta, m.kv_lens, sl2,
-                     static_cast<bf16*>(out), lse);
+                     static_cast<bf16*>(out), lse, n_draft, Hq / n_draft);
   return hipGetLastError();
 }
 

@@ -232,3 +232,28 @@ def test_extend_options_checked_before_launch(lib):
         assert lib.paged_extend_attn_ex(*args, C.byref(opts), 0.125, 0x6000, None, None) == 0
     finally:
         lib.kv_pool_destroy(h)
+
+
+def test_verify_arguments_checked_before_launch(lib):
+    st, h = make_pool(lib, desc(dtype=1, kind=1, num_kv_heads=1, head_dim_qk=576, head_dim_v=512, page_size=64),
+                      v=None)  # a latent pool takes no V buffer
+    assert st == 0
+    st2, hs = make_pool(lib, desc(dtype=1))
+    assert st2 == 0
+    try:
+        m = L.KVMapStruct()
+        m.fmt, m.bs, m.kv_lens, m.max_kv_len = L.PKV_MAP_TOKEN_TABLE, 4, 0x1000, 100
+        m.req_to_token, m.table_rows, m.table_width, m.req_pool_indices = 0x2000, 5, 128, 0x3000
+        call = lambda pool, hq, n, scale=0.04: lib.paged_verify_attn(pool, 0, 0x4000, hq, n, C.byref(m), scale,
+                                                                       0x5000, None, None, 0, None)
+        assert call(h, 16, 0) == L.PKV_EINVAL
+        assert call(h, 16, 2, scale=0.0) == L.PKV_EINVAL
+        assert call(h, 16, 9) == L.PKV_EUNSUPPORTED      # 144 rows
+        assert call(h, 24, 2) == L.PKV_EUNSUPPORTED      # 48 rows
+        assert call(hs, 16, 2) == L.PKV_EUNSUPPORTED     # not a latent pool
+        assert call(h, 16, 2) == L.PKV_ECAPACITY         # no workspace
+        m.bs = 0
+        assert call(h, 16, 2) == 0
+    finally:
+        lib.kv_pool_destroy(h)
+        lib.kv_pool_destroy(hs)

@@ -96,3 +96,75 @@ def test_mla_formats_agree_bitwise_and_repeat():
     for o, l in outs[1:]:
         assert torch.equal(o.view(torch.int16), outs[0][0].view(torch.int16))
         assert torch.equal(l, outs[0][1])
+
+
+# --------------------------------------------------------------------------
+# target verification: drafts folded into heads, bottom-right causal
+# --------------------------------------------------------------------------
+
+def run_verify(dc, fmt, n):
+    c, g = dc.case, dc.case.geom
+    m = dc.kv_map("self", fmt)
+    q = dc.q["self"].view(c.bs, n, g.num_q_heads, g.head_dim_qk)
+    out = torch.full((c.bs, n, g.num_q_heads, g.head_dim_v), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((c.bs, n, g.num_q_heads), float("nan"), dtype=torch.float32, device="cuda")
+    nb = P.paged_decode_workspace_bytes(dc.pool, c.bs, n * g.num_q_heads, m.max_kv_len)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+    P.paged_verify_attn(dc.pool, 0, q, m, c.sm_scale, out, lse, ws)
+    torch.cuda.synchronize()
+    return out.view(c.bs * n, g.num_q_heads, g.head_dim_v), lse.view(c.bs * n, g.num_q_heads)
+
+
+@pytest.mark.parametrize("heads,n", [(16, 2), (16, 8), (32, 4), (64, 2), (16, 4)])
+@pytest.mark.parametrize("fmt", FMTS)
+def test_mla_verify_matches_oracle(heads, n, fmt):
+    """Short and long requests (pieces cut across runs, drafts straddling a
+    tile boundary), one request shorter than its drafts (its first drafts see
+    no key)."""
+    # request 0 is shorter than its drafts; request 1's drafts straddle the
+    # 32-key tile boundary at 64
+    case = W.mla_decode(seed=heads + n, bs=6, len_range=(1, 1300), num_q_heads=heads, num_draft=n,
+                        fixed_lens={0: max(1, n - 1), 1: 64 + n // 2})
+    print(f"mla verify heads {heads} drafts {n} fmt {fmt}", flush=True)
+    vals = W.make_values(case, canary=True)
+    dc = DeviceCase(case, vals)
+    dc.store()
+    out, lse = run_verify(dc, fmt, n)
+    ref_o, ref_l = oracle_region(case, vals, "self")
+    assert_attn_close(out, ref_o, "bf16", f"verify {heads}x{n} fmt {fmt}")
+    assert_lse_close(lse, ref_l, "bf16", f"verify {heads}x{n} fmt {fmt}")
+
+
+def test_mla_verify_planted_key_goes_through_the_exact_fallback():
+    """A key far along the queries' direction at the last draft's own
+    position: only the last draft sees it (its score outruns the fixed
+    softmax reference, so the request is recomputed exactly), the earlier
+    drafts must not."""
+    n, heads = 4, 16
+    case = W.mla_decode(seed=9, bs=3, len_range=(300, 900), num_q_heads=heads, num_draft=n)
+    vals = W.make_values(case)
+    i = 1
+    L = int(case.regions["self"].kv_lens[i])
+    u = torch.randn(576, generator=torch.Generator().manual_seed(6))
+    u = u / u.norm()
+    qrows = vals["q"]["self"][i * n:(i + 1) * n]
+    qrows[:] = (u * 8.0).to(torch.bfloat16)[None, None, :]
+    # the last draft's K row is stored this step: plant it in k_new
+    vals["k_new"][(i + 1) * n - 1, 0] = (u * 200.0).to(torch.bfloat16)
+    dc = DeviceCase(case, vals)
+    dc.store()
+    out, lse = run_verify(dc, P.PKV_MAP_BLOCK_TABLE, n)
+    ref_o, ref_l = oracle_region(case, vals, "self")
+    assert_attn_close(out, ref_o, "bf16", "verify planted key")
+    assert_lse_close(lse, ref_l, "bf16", "verify planted key")
+    assert np.isfinite(ref_l[i * n + n - 1]).all() and ref_l[i * n + n - 1, 0] > ref_l[i * n, 0] + 50
+
+
+def test_mla_verify_with_one_draft_equals_decode_bitwise():
+    case = W.mla_decode(seed=4, bs=4, len_range=(10, 800), num_q_heads=64)
+    vals = W.make_values(case)
+    dc = DeviceCase(case, vals)
+    dc.store()
+    o1, l1 = dc.decode(P.PKV_MAP_CSR)
+    o2, l2 = run_verify(dc, P.PKV_MAP_CSR, 1)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)

@@ -279,20 +279,29 @@ def gqa_prefix_share(page_size: int, seed: int = 0, bs: int = 256, group: int = 
     )
 
 
-def mla_decode(seed: int = 0, bs: int = 128, len_range=(4096, 16384), num_q_heads: int = 128) -> Case:
+def mla_decode(seed: int = 0, bs: int = 128, len_range=(4096, 16384), num_q_heads: int = 128,
+               num_draft: int = 1, fixed_lens: Optional[Dict[int, int]] = None) -> Case:
     """MLA-shaped paged decode, bf16: page_size 64, 128 query heads over one
     latent KV row of 576 values (512 latent + 64 rope); V is the first 512;
     KV lengths uniform in [4096, 16384]; values N(0,1) x 0.1; pool =
     ceil(1.2 x needed) real pages, seeded free-list order, popped in request
-    order; one new token per request at position L-1."""
-    rs, rp, vseed, qseed = _streams(4, seed)
+    order; one new token per request at position L-1.
+
+    ``num_draft > 1`` is target verification ([BACKEND] init_forward_metadata,
+    target-verify branch): each request's last ``num_draft`` tokens are draft
+    tokens appended this step (positions L - num_draft .. L - 1, those that
+    exist), each with its own queries, attending causally (bottom-right).
+    ``fixed_lens`` sets chosen requests' lengths (edge cases in tests)."""
+    rs, rp, vseed, qseed = _streams(4, seed, (num_draft,) if num_draft > 1 else ())
     ps = 64
     lens = rs.integers(len_range[0], len_range[1] + 1, size=bs).astype(np.int32)
+    for i, n in (fixed_lens or {}).items():
+        lens[i] = n
     npg = [_cdiv(n, ps) for n in lens]
     num_pages = _cdiv(sum(npg) * 12, 10)
     geom = Geometry("bf16", ps, num_pages, 1, 576, 512, True, num_q_heads)
     perm = rp.permutation(num_pages)
-    width = _round32(int(len_range[1]))
+    width = _round32(int(max(len_range[1], lens.max())))
     table = _new_table(bs + 1, width, geom)
     rpi = rs.permutation(bs).astype(np.int32)
     pos, page_lists = 0, []
@@ -301,12 +310,13 @@ def mla_decode(seed: int = 0, bs: int = 128, len_range=(4096, 16384), num_q_head
         pos += npg[i]
         page_lists.append(pages)
         table[rpi[i], :lens[i]] = _expand(pages, ps, lens[i])
-    out_loc = np.array([table[rpi[i], lens[i] - 1] for i in range(bs)], dtype=np.int32)
+    out_loc = np.concatenate([table[rpi[i], max(0, lens[i] - num_draft):lens[i]] for i in range(bs)]).astype(np.int32)
     tails = _tail_slots(page_lists, lens, ps)
     region = Region(np.zeros(bs, np.int32), lens, page_lists, causal=True)
     return Case(
-        name="mla_decode_bf16", geom=geom, bs=bs, req_to_token=table, req_pool_indices=rpi,
-        q_lens=np.ones(bs, np.int32), regions={"self": region}, out_loc=out_loc,
+        name="mla_decode_bf16" if num_draft == 1 else f"mla_verify{num_draft}_bf16", geom=geom, bs=bs,
+        req_to_token=table, req_pool_indices=rpi, q_lens=np.full(bs, num_draft, np.int32), regions={"self": region},
+        out_loc=out_loc,
         sm_scale=1.0 / np.sqrt(576.0), value_scale=0.1, value_seed=vseed, query_seed=qseed,
         free_pages=perm[pos:].astype(np.int64),
         tail_slots=np.concatenate(tails) if tails else np.zeros(0, np.int64),
