@@ -10,7 +10,8 @@ pass of the hot path over the batch: the KV append of the 64 new tokens
 log-sum-exp merge).  Inputs are resident in HBM before timing starts.
 
 Other workloads (--workload): gqa_prefix_share_ps16 / _ps64 (batch-256 GQA
-decode with shared 2048-token prefixes), mla_decode (latent 576/512, 128
+decode with shared 2048-token prefixes; the _cascade variants pass the
+prefix groups to the cascade decode), mla_decode (latent 576/512, 128
 heads, page_size 64), mla_verify (the same pool, 32 heads x 4 draft tokens
 verified per request), encdec_extend (Whisper-shaped causal + cross extend
 over a paged prefix), encdec_extend_ragged (the same through kv_gather and
@@ -251,6 +252,33 @@ class DecodeBench:
                 "sample": f"{reqs} request decodes ({reqs / c.bs:.2f} passes over the {c.bs}-request batch, "
                           f"{toks} KV tokens) by the numpy fp64 oracle (gather + BLAS matmul per request), "
                           f"{dt:.1f} s"}
+
+
+class CascadeBench(DecodeBench):
+    """Decode step with the prefix groups known: build_kv_indices (CSR) then
+    paged_decode_attn_cascade (each group's shared prefix read once, the own
+    keys by the split-K kernel, one log-sum-exp merge)."""
+
+    kernel_name = "cascade decode: split-K kernel over own keys + shared-prefix kernel"
+
+    def __init__(self, case, dev="cuda"):
+        super().__init__(case, "csr", dev)
+        g = case.geom
+        indptr, plen = case.prefix_groups
+        self.groups = self.P.make_prefix_groups(i32(indptr, dev), i32(plen, dev), int(np.diff(indptr).max()),
+                                                int(plen.max()))
+        nb = self.P.paged_decode_cascade_workspace_bytes(self.pool, case.bs, g.num_q_heads, self.max_len,
+                                                         self.groups)
+        self.ws = self.torch.empty(max(nb, 256), dtype=self.torch.uint8, device=dev)
+
+    def step(self, timers=None):
+        P, c = self.P, self.case
+        P.build_kv_indices(P.PKV_MAP_CSR, self.table, self.rpi, self.kv_start, self.kv_lens, c.geom.page_size,
+                           self.max_len, self.indptr, self.indices)
+        if timers:
+            P.pkv_set_kernel_timer(*timers[0])
+        P.paged_decode_attn_cascade(self.pool, 0, self.q, self.map, self.groups, c.sm_scale, self.out, self.lse,
+                                    self.ws)
 
 
 class VerifyBench(DecodeBench):
@@ -570,6 +598,13 @@ def build_workload(name: str):
             "workload": "qwen3_0.6b_decode_bf16", "batch": 64, "num_q_heads": 16, "num_kv_heads": 8,
             "head_dim": 128, "page_size": 1, "kv_len": "U[512,4096]", "pool_tokens": 400000,
             "table": "req_to_token [65, 8192]", "step": "kv_store + paged_decode_attn"}
+    if name.startswith("gqa_prefix_share_ps") and name.endswith("_cascade"):
+        ps = int(name[len("gqa_prefix_share_ps"):-len("_cascade")])
+        return CascadeBench(W.gqa_prefix_share(ps, seed=0)), {
+            "workload": f"gqa_prefix_share_decode_bf16_ps{ps}_cascade", "batch": 256, "num_q_heads": 32,
+            "num_kv_heads": 8, "head_dim": 128, "page_size": ps, "kv_len": "lognormal(2048, 1) clip [64, 32768]",
+            "prefix_share": "groups of 8 share 2048 tokens, passed as prefix groups",
+            "step": "build_kv_indices(CSR) + paged_decode_attn_cascade"}
     if name.startswith("gqa_prefix_share_ps"):
         ps = int(name[len("gqa_prefix_share_ps"):])
         return DecodeBench(W.gqa_prefix_share(ps, seed=0), "csr"), {

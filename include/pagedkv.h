@@ -249,6 +249,41 @@ int paged_verify_attn(const pkv_pool* pool, int32_t layer, const void* q, int32_
                       const pkv_kv_map* map, float sm_scale, void* out, float* lse, void* workspace, size_t ws_bytes,
                       void* stream);
 
+/* Groups of requests that share a prefix ([XPU] introduction: requests
+ * sharing a prefix share its pages; [MINI]'s prefix cache).  Group g is the
+ * requests group_indptr[g] .. group_indptr[g+1] - 1 of the batch (groups
+ * increasing and disjoint; requests in no group are allowed); the first
+ * min(kv_lens[i], prefix_len[g]) keys of every member read the same slots.
+ *   num_groups, max_group_size, max_prefix_len: host; the bounds size the
+ *     launch and must hold every group's member count and prefix_len.
+ *   group_indptr: device int32[num_groups + 1]; prefix_len: device
+ *     int32[num_groups] (tokens). */
+typedef struct pkv_prefix_groups {
+  int32_t num_groups;
+  int32_t max_group_size;
+  int32_t max_prefix_len;
+  const int32_t* group_indptr;
+  const int32_t* prefix_len;
+} pkv_prefix_groups;
+
+/* Workspace bytes paged_decode_attn_cascade needs. */
+int paged_decode_cascade_workspace_bytes(const pkv_pool* pool, int32_t bs, int32_t num_q_heads, int32_t max_kv_len,
+                                         const pkv_prefix_groups* groups, size_t* bytes);
+
+/* The result of paged_decode_attn (same arguments and outputs), computed as
+ * a cascade: each group's shared prefix (prefix_len rounded down to 32 keys)
+ * is read once per KV head and scored against all members' queries, each
+ * request's remaining keys go through the split-K decode, and the parts
+ * are merged by log-sum-exp.  A caller whose groups break the sharing
+ * promise gets an unspecified result (never an out-of-range access).
+ *   groups: host struct (see pkv_prefix_groups); num_groups 0 is plain decode.
+ *   workspace: >= paged_decode_cascade_workspace_bytes(), 256-byte aligned.
+ * Supported: SPLIT_KV bf16, head_dim 64 or 128, num_q_heads / num_kv_heads
+ * <= 16; map TOKEN_TABLE, CSR or BLOCK_TABLE. */
+int paged_decode_attn_cascade(const pkv_pool* pool, int32_t layer, const void* q, int32_t num_q_heads,
+                              const pkv_kv_map* map, const pkv_prefix_groups* groups, float sm_scale, void* out,
+                              float* lse, void* workspace, size_t ws_bytes, void* stream);
+
 /* ---- paged extend / prefill (a7, a8, a9) -------------------------------- */
 
 /* Each request's qo_indptr[i+1] - qo_indptr[i] new query tokens attend over

@@ -36,7 +36,8 @@ from ._lib import (  # noqa: F401
 __all__ = [
     "Pool", "KVMap", "kv_pool_bytes", "kv_pool_create", "kv_pool_destroy", "kv_pool_padding_page",
     "kv_pool_token_bytes", "kv_store", "build_kv_indices", "make_kv_map", "paged_decode_workspace_bytes",
-    "paged_decode_attn", "paged_verify_attn", "paged_extend_attn", "paged_extend_attn_ex", "kv_gather",
+    "paged_decode_attn", "PrefixGroups", "make_prefix_groups", "paged_decode_cascade_workspace_bytes",
+    "paged_decode_attn_cascade", "paged_verify_attn", "paged_extend_attn", "paged_extend_attn_ex", "kv_gather",
     "kv_validate",
     "pkv_set_kernel_timer", "library",
     "FreeList", "kv_free_list_create", "kv_free_list_init", "kv_alloc", "kv_alloc_extend", "kv_alloc_decode",
@@ -251,6 +252,43 @@ def paged_decode_attn(pool: Pool, layer: int, q: torch.Tensor, kv_map: KVMap, sm
                                        C.byref(kv_map.struct), float(sm_scale), _dev(out, "out", pool.dtype),
                                        _dev(lse, "lse", torch.float32), ws_ptr, ws_bytes, _stream(stream)),
             "paged_decode_attn")
+
+
+@dataclass
+class PrefixGroups:
+    """A pkv_prefix_groups plus the device tensors it points at."""
+    struct: L.PrefixGroups
+    refs: tuple
+
+
+def make_prefix_groups(group_indptr: torch.Tensor, prefix_len: torch.Tensor, max_group_size: int,
+                       max_prefix_len: int) -> PrefixGroups:
+    """group_indptr device int32[G + 1] (group g = requests indptr[g] ..
+    indptr[g+1] - 1), prefix_len device int32[G]; host bounds."""
+    i32 = torch.int32
+    st = L.PrefixGroups(prefix_len.numel(), int(max_group_size), int(max_prefix_len),
+                        _dev(group_indptr, "group_indptr", i32), _dev(prefix_len, "prefix_len", i32))
+    return PrefixGroups(st, (group_indptr, prefix_len))
+
+
+def paged_decode_cascade_workspace_bytes(pool: Pool, bs: int, num_q_heads: int, max_kv_len: int,
+                                         groups: PrefixGroups) -> int:
+    n = C.c_size_t()
+    L.check(L.load().paged_decode_cascade_workspace_bytes(pool.handle, bs, num_q_heads, max_kv_len,
+                                                          C.byref(groups.struct), C.byref(n)),
+            "paged_decode_cascade_workspace_bytes")
+    return n.value
+
+
+def paged_decode_attn_cascade(pool: Pool, layer: int, q: torch.Tensor, kv_map: KVMap, groups: PrefixGroups,
+                              sm_scale: float, out: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                              workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    ws_ptr = _dev(workspace, "workspace")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    L.check(L.load().paged_decode_attn_cascade(pool.handle, layer, _dev(q, "q", pool.dtype), q.shape[1],
+                                               C.byref(kv_map.struct), C.byref(groups.struct), float(sm_scale),
+                                               _dev(out, "out", pool.dtype), _dev(lse, "lse", torch.float32), ws_ptr,
+                                               ws_bytes, _stream(stream)), "paged_decode_attn_cascade")
 
 
 def paged_verify_attn(pool: Pool, layer: int, q: torch.Tensor, kv_map: KVMap, sm_scale: float, out: torch.Tensor,

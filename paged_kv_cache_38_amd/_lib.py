@@ -77,6 +77,16 @@ class ExtendOpts(C.Structure):
     ]
 
 
+class PrefixGroups(C.Structure):
+    _fields_ = [
+        ("num_groups", C.c_int32),
+        ("max_group_size", C.c_int32),
+        ("max_prefix_len", C.c_int32),
+        ("group_indptr", C.c_void_p),
+        ("prefix_len", C.c_void_p),
+    ]
+
+
 # name -> (restype, argtypes): every entry point include/pagedkv.h declares
 SIGNATURES = {
     "pkv_abi_version": (C.c_int, []),
@@ -96,6 +106,11 @@ SIGNATURES = {
                                                C.POINTER(C.c_size_t)]),
     "paged_decode_attn": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.POINTER(KVMapStruct), C.c_float,
                                     C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "paged_decode_cascade_workspace_bytes": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32,
+                                                       C.POINTER(PrefixGroups), C.POINTER(C.c_size_t)]),
+    "paged_decode_attn_cascade": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.POINTER(KVMapStruct),
+                                            C.POINTER(PrefixGroups), C.c_float, C.c_void_p, C.c_void_p, C.c_void_p,
+                                            C.c_size_t, C.c_void_p]),
     "paged_verify_attn": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.c_int32, C.POINTER(KVMapStruct),
                                     C.c_float, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "paged_extend_attn": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_int64, C.c_void_p, C.c_int32, C.c_int32,

@@ -318,6 +318,58 @@ int paged_decode_attn(const pkv_pool* pool, int32_t layer, const void* q, int32_
                        "paged_decode_attn");
 }
 
+namespace {
+int check_groups(const pkv_pool* pool, int32_t num_q_heads, const pkv_prefix_groups* g) {
+  if (!g) return fail(PKV_EINVAL, "null prefix groups");
+  if (g->num_groups < 0 || g->max_group_size < 0 || g->max_prefix_len < 0)
+    return fail(PKV_EINVAL, "negative group count or bound");
+  if (g->num_groups > 0 && (!g->group_indptr || !g->prefix_len))
+    return fail(PKV_EINVAL, "prefix groups need group_indptr and prefix_len");
+  if (pool->desc.kind != PKV_KIND_SPLIT_KV || pool->desc.dtype != PKV_DTYPE_BF16 ||
+      !pkv::decode_supported(pool->info, num_q_heads) || num_q_heads % pool->desc.num_kv_heads != 0 ||
+      num_q_heads / pool->desc.num_kv_heads > 16)
+    return fail(PKV_EUNSUPPORTED, "cascade decode needs a bf16 split K/V pool, head_dim 64 or 128, at most 16 query "
+                                  "heads per KV head");
+  return ok();
+}
+}  // namespace
+
+int paged_decode_cascade_workspace_bytes(const pkv_pool* pool, int32_t bs, int32_t num_q_heads, int32_t max_kv_len,
+                                         const pkv_prefix_groups* groups, size_t* bytes) {
+  if (int st = check_pool(pool)) return st;
+  if (!bytes || bs < 0 || max_kv_len < 0 || num_q_heads <= 0) return fail(PKV_EINVAL, "bad workspace query");
+  if (int st = check_groups(pool, num_q_heads, groups)) return st;
+  const pkv::CascadePlan cp = pkv::plan_cascade(pool->info, bs, num_q_heads, max_kv_len, groups->num_groups,
+                                                groups->max_group_size, groups->max_prefix_len);
+  *bytes = pkv::cascade_ws_layout(pool->info, cp, bs, num_q_heads, nullptr, nullptr);
+  return ok();
+}
+
+int paged_decode_attn_cascade(const pkv_pool* pool, int32_t layer, const void* q, int32_t num_q_heads,
+                              const pkv_kv_map* map, const pkv_prefix_groups* groups, float sm_scale, void* out,
+                              float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  if (int st = check_pool(pool)) return st;
+  if (int st = check_layer(pool, layer)) return st;
+  pkv::DevMap dm;
+  if (int st = make_devmap(pool, map, false, &dm)) return st;
+  if (num_q_heads <= 0) return fail(PKV_EINVAL, "num_q_heads must be positive");
+  if (int st = check_groups(pool, num_q_heads, groups)) return st;
+  if (!(sm_scale > 0.0f) || std::isinf(sm_scale)) return fail(PKV_EINVAL, "sm_scale must be positive and finite");
+  if (map->bs == 0) return ok();
+  if (!q || !out) return fail(PKV_EINVAL, "null q or out");
+  if (!aligned16(q)) return fail(PKV_EALIGN, "q must be 16-byte aligned");
+  const pkv::CascadePlan cp = pkv::plan_cascade(pool->info, map->bs, num_q_heads, map->max_kv_len,
+                                                groups->num_groups, groups->max_group_size, groups->max_prefix_len);
+  const size_t need = pkv::cascade_ws_layout(pool->info, cp, map->bs, num_q_heads, nullptr, nullptr);
+  if (ws_bytes < need) return fail(PKV_ECAPACITY, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return fail(PKV_EALIGN, "workspace must be non-null and 256-byte aligned");
+  return device_status(pkv::launch_decode_cascade(pool->info, layer, q, num_q_heads, dm, map->bs, cp,
+                                                  groups->group_indptr, groups->prefix_len, groups->num_groups,
+                                                  sm_scale, out, lse, workspace, (hipStream_t)stream),
+                       "paged_decode_attn_cascade");
+}
+
 int paged_verify_attn(const pkv_pool* pool, int32_t layer, const void* q, int32_t num_q_heads, int32_t num_draft,
                       const pkv_kv_map* map, float sm_scale, void* out, float* lse, void* workspace, size_t ws_bytes,
                       void* stream) {

@@ -226,7 +226,8 @@ template <int D, int WAVES, int NS>
 __global__ void __launch_bounds__(64 * WAVES, NS <= 2 ? 8 / WAVES : 4 / WAVES) decode_stream_kernel(
     const bf16* k_pool, const bf16* v_pool, const bf16* __restrict__ q, int32_t Hq, int32_t Hkv, int32_t G,
     int32_t hg, const int32_t* __restrict__ header, const int32_t* __restrict__ meta, float scale_log2,
-    bf16* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws_o, float* __restrict__ ws_lse) {
+    bf16* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws_o, float* __restrict__ ws_lse,
+    int32_t pieces_only) {
   constexpr int NK = D / 32;
   constexpr int NT = D / 16;
   constexpr int LDS = D + 8;
@@ -271,7 +272,8 @@ __global__ void __launch_bounds__(64 * WAVES, NS <= 2 ? 8 / WAVES : 4 / WAVES) d
 
   auto finish = [&](int i, int P, int T) {
     const int b0 = P / Bt, b1 = (P + T - 1) / Bt;
-    const bool direct = b0 == b1;
+    // (cascade decode merges every request afterwards: all results are pieces)
+    const bool direct = b0 == b1 && !pieces_only;
     float l_tot = l_run + shfl_xor(l_run, 16);
     l_tot += shfl_xor(l_tot, 32);
 #pragma unroll
@@ -378,6 +380,297 @@ __global__ void __launch_bounds__(256) decode_stream_merge_kernel(int32_t bs, in
   const float inv = 1.0f / sum;
 #pragma unroll
   for (int e = 0; e < E; ++e) op[e] = (bf16)(o[e] * inv);
+  if (lse && lane == 0) lse[idx] = mx + __logf(sum);
+}
+
+// ---------------------------------------------------------------------------
+// Cascade decode over shared prefixes ([XPU] introduction and [MINI]: the
+// requests of a group reuse the same prefix pages; [BACKEND]: split-K with a
+// log-sum-exp merge).  Request i of group g splits its keys at S_g, the
+// group's shared prefix length rounded down to the 32-key tile: keys
+// [0, min(L_i, S_g)) are the same slots for every member, [S_g, L_i) its
+// own.  The shared part is read once per group and KV head and scored
+// against every member's queries together; the own part goes through the
+// stream kernel with the first S_g keys skipped; a final merge combines the
+// prefix chunks and the suffix pieces.  The result is the same attention as
+// paged_decode_attn, with every shared K/V row leaving HBM once per group.
+// ---------------------------------------------------------------------------
+
+// skip[i] = S_g for a member of group g (groups are increasing, disjoint
+// ranges of the batch), 0 for a request in no group.
+__global__ void __launch_bounds__(256) cascade_skip_kernel(const int32_t* __restrict__ group_indptr,
+                                                           const int32_t* __restrict__ prefix_len,
+                                                           int32_t num_groups, int32_t bs,
+                                                           int32_t* __restrict__ skip) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= bs) return;
+  int lo = 0, hi = num_groups;  // last g with group_indptr[g] <= i, in [lo, hi)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (group_indptr[mid] <= i) lo = mid;
+    else hi = mid;
+  }
+  int32_t v = 0;
+  if (num_groups > 0 && group_indptr[lo] <= i && i < group_indptr[lo + 1])
+    v = max(prefix_len[lo], 0) & ~(kTile - 1);
+  skip[i] = v;
+}
+
+// One tile of the shared prefix against NB blocks of 16 query rows.  Like
+// decode_compute, with a key limit per query row (lane column) instead of
+// one per tile, the V tile staged in LDS once for all blocks, and rows that
+// have seen no key yet kept at m = -inf without NaNs.
+template <int D, int NB>
+__device__ __forceinline__ void cascade_tile(const DecodeTile<D>& T, int t0, int v_end, const int (&lim)[NB],
+                                             int lane, const bf16x8 (&qb)[NB][D / 32], float scale_log2, bf16* vt,
+                                             f32x4 (&acc)[NB][D / 16], float (&m_run)[NB], float (&l_run)[NB]) {
+  constexpr int NK = DecodeTile<D>::NK, CPT = DecodeTile<D>::CPT, TPI = DecodeTile<D>::TPI;
+  constexpr int VIT = DecodeTile<D>::VIT;
+  constexpr int NT = D / 16;
+  constexpr int LDS = D + 8;
+  const int grp = lane >> 4;
+  f32x4 sacc[NB][2];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      sacc[b][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) sacc[b][a] = mfma16x16x32(T.k[a][kk], qb[b][kk], sacc[b][a]);
+    }
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int it = 0; it < VIT; ++it) {
+    const int row = it * TPI + lane / CPT;
+    u32x4 w = T.v[it];
+    if (t0 + row >= v_end) w = u32x4{0u, 0u, 0u, 0u};  // keys past the prefix: P = 0 there, V must not be NaN
+    *reinterpret_cast<u32x4*>(vt + row * LDS + (lane % CPT) * 8) = w;
+  }
+  bf16x8 pa[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    float sv[2][4];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const float x = (t0 + a * 16 + grp * 4 + rr < lim[b]) ? sacc[b][a][rr] * scale_log2 : -INFINITY;
+        sv[a][rr] = x;
+        mt = fmaxf(mt, x);
+      }
+    mt = fmaxf(mt, shfl_xor(mt, 16));
+    mt = fmaxf(mt, shfl_xor(mt, 32));
+    const float m_new = fmaxf(m_run[b], mt);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;  // nothing seen yet: every p and alpha is 0
+    const float alpha = fast_exp2(m_run[b] - m_use);
+    float psum = 0.f;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const float p = fast_exp2(sv[a][rr] - m_use);
+        psum += p;
+        pa[b][a * 4 + rr] = (bf16)p;
+      }
+    l_run[b] = l_run[b] * alpha + psum;
+    m_run[b] = m_new;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const float ar = shfl(alpha, grp * 4 + rr);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[b][nt][rr] *= ar;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const bf16x8 vop = lds_v_operand(vt, LDS, 0, nt * 16, lane);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b][nt] = mfma16x16x32(pa[b], vop, acc[b][nt]);
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+constexpr int kCascadeCols = 32;  // query rows (member x head) per wave: two MFMA column blocks
+
+// Shared-prefix kernel: one wave per (group, member slice, prefix chunk, KV
+// head).  A slice holds up to 32 / G members, so its rows fill two 16-row
+// MFMA column blocks; the prefix tiles are read through the table of the
+// group's longest member (every member's prefix keys are among its keys).
+// The hg workgroups of one work item are 8 blocks apart (one XCD), as in the
+// stream kernel.  Every (member, head, chunk) gets a partial result,
+// o = 0 / lse = -inf where the chunk holds none of the member's keys.
+template <int D, int W, int FMT>
+__global__ void __launch_bounds__(64 * W) cascade_prefix_kernel(
+    DevMap m, const bf16* k_pool, const bf16* v_pool, const bf16* __restrict__ q, int32_t bs, int32_t Hq,
+    int32_t Hkv, int32_t G, int32_t hg, const int32_t* __restrict__ group_indptr,
+    const int32_t* __restrict__ prefix_len, int32_t num_groups, int32_t slices, int32_t chunks, int32_t tpc,
+    int32_t ms, float scale_log2, float* __restrict__ ws_po, float* __restrict__ ws_plse) {
+  constexpr int NK = D / 32;
+  constexpr int NT = D / 16;
+  constexpr int LDS = D + 8;
+  constexpr int NB = kCascadeCols / 16;
+  __shared__ __attribute__((aligned(16))) bf16 vsm[W][kTile * LDS];
+  const int work = (blockIdx.x / (8 * hg)) * 8 + blockIdx.x % 8;
+  if (work >= num_groups * slices * chunks) return;
+  const int c = work % chunks, sl = (work / chunks) % slices, gi = work / (chunks * slices);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int h = ((blockIdx.x / 8) % hg) * W + wave;  // KV head
+  const int ga = max(group_indptr[gi], 0), gb = min(group_indptr[gi + 1], bs);
+  const int i0 = ga + sl * ms, i1 = min(gb, i0 + ms);
+  if (i0 >= i1) return;  // uniform per workgroup
+  const int S = max(prefix_len[gi], 0) & ~(kTile - 1);
+  int rd = ga, Lmax = 0;  // the longest member reads the prefix
+  for (int k = ga; k < gb; ++k) {
+    const int L = m.kv_lens[k];
+    if (L > Lmax) {
+      Lmax = L;
+      rd = k;
+    }
+  }
+  const int E = min(S, Lmax);  // prefix keys any member sees
+  const int t_begin = c * tpc, t_end = min(t_begin + tpc, (E + kTile - 1) / kTile);
+
+  // rows: column cc of block b is member i0 + cc / G, query head h G + cc % G
+  bf16x8 qb[NB][NK];
+  int lim[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int cc = b * 16 + col;
+    const int mm = i0 + cc / G;
+    const bool ok = cc < ms * G && mm < i1;
+    lim[b] = ok ? min(m.kv_lens[mm], S) : 0;
+    const bf16* qp = q + ((int64_t)(ok ? mm : i0) * Hq + h * G + cc % G) * D + grp * 8;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      u32x4 v = *reinterpret_cast<const u32x4*>(qp + kk * 32);
+      if (!ok) v = u32x4{0u, 0u, 0u, 0u};
+      qb[b][kk] = as_bf16x8(v);
+    }
+  }
+  f32x4 acc[NB][NT];
+  float m_run[NB], l_run[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[b][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[b] = -INFINITY;
+    l_run[b] = 0.f;
+  }
+
+  if (t_begin < t_end) {
+    const SlotMap<FMT> sm = make_slotmap<FMT>(m, rd);
+    const int64_t row_elems = (int64_t)Hkv * D;
+    const bf16* kb = k_pool + (int64_t)h * D;
+    const bf16* vb = v_pool + (int64_t)h * D;
+    bf16* vt = vsm[wave];
+    // lane l < 32 holds the slot of key 32 t + l (keys past E read the padding slot)
+    auto slot_word = [&](int t) -> int32_t {
+      const int key = t * kTile + (lane & 31);
+      return sm(min(key, E - 1), key < E);
+    };
+    DecodeTile<D> T[2];
+    decode_issue<D>(T[0], slot_word(t_begin), lane, kb, vb, row_elems);
+    for (int t = t_begin; t < t_end; t += 2) {
+      if (t + 1 < t_end) decode_issue<D>(T[1], slot_word(t + 1), lane, kb, vb, row_elems);
+      cascade_tile<D, NB>(T[0], t * kTile, E, lim, lane, qb, scale_log2, vt, acc, m_run, l_run);
+      if (t + 1 < t_end) {
+        if (t + 2 < t_end) decode_issue<D>(T[0], slot_word(t + 2), lane, kb, vb, row_elems);
+        cascade_tile<D, NB>(T[1], (t + 1) * kTile, E, lim, lane, qb, scale_log2, vt, acc, m_run, l_run);
+      }
+    }
+  }
+
+  // ---- partial results: lane (col, grp) holds O[row 4 grp + rr][d 16 nt + col]
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    float l_tot = l_run[b] + shfl_xor(l_run[b], 16);
+    l_tot += shfl_xor(l_tot, 32);
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int hr = grp * 4 + rr;
+      const float lt = shfl(l_tot, hr);
+      const float mr = shfl(m_run[b], hr);
+      const int cc = b * 16 + hr;
+      const int mm = i0 + cc / G;
+      if (cc < ms * G && mm < i1) {
+        const int64_t o = ((int64_t)c * bs + mm) * Hq + h * G + cc % G;
+        const bool any = lt > 0.f;
+        const float inv = any ? 1.0f / lt : 0.f;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) ws_po[o * D + nt * 16 + col] = acc[b][nt][rr] * inv;
+        if (col == 0) ws_plse[o] = any ? (mr + __log2f(lt)) * kLn2 : -INFINITY;
+      }
+    }
+  }
+}
+
+// Final merge of a cascade decode: one wavefront per (request, head) over the
+// suffix pieces (ids run + request, every one in the workspace) and, for a
+// group member, the prefix chunks.
+template <int D>
+__global__ void __launch_bounds__(256) cascade_merge_kernel(int32_t bs, int32_t Hq, int32_t chunks,
+                                                            const int32_t* __restrict__ header,
+                                                            const int32_t* __restrict__ prefix,
+                                                            const int32_t* __restrict__ ntiles,
+                                                            const int32_t* __restrict__ skip,
+                                                            const float* __restrict__ ws_o,
+                                                            const float* __restrict__ ws_lse,
+                                                            const float* __restrict__ ws_po,
+                                                            const float* __restrict__ ws_plse,
+                                                            bf16* __restrict__ out, float* __restrict__ lse) {
+  constexpr int E = D / 64;  // elements per lane
+  const int lane = threadIdx.x & 63;
+  const int64_t idx = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (idx >= (int64_t)bs * Hq) return;
+  const int i = (int)(idx / Hq), h = (int)(idx % Hq);
+  const int T = ntiles[i];
+  const int Bt = header[0];
+  const int P = prefix[i];
+  const int b0 = P / Bt, b1 = T > 0 ? (P + T - 1) / Bt : b0 - 1;
+  const int nc = skip[i] > 0 ? chunks : 0;
+  auto piece = [&](int k, const float*& o) -> float {  // k < pieces: suffix, else prefix chunk
+    const int np = b1 - b0 + 1;
+    if (k < np) {
+      const int64_t row = ((int64_t)(b0 + k) + i) * Hq + h;
+      o = ws_o + row * D;
+      return ws_lse[row];
+    }
+    const int64_t row = ((int64_t)(k - np) * bs + i) * Hq + h;
+    o = ws_po + row * D;
+    return ws_plse[row];
+  };
+  const int n = (b1 - b0 + 1) + nc;
+  float mx = -INFINITY;
+  for (int k = 0; k < n; ++k) {
+    const float* o;
+    mx = fmaxf(mx, piece(k, o));
+  }
+  bf16* op = out + idx * D + lane * E;
+  if (mx == -INFINITY) {  // no key at all
+#pragma unroll
+    for (int e = 0; e < E; ++e) op[e] = (bf16)0.0f;
+    if (lse && lane == 0) lse[idx] = -INFINITY;
+    return;
+  }
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  float sum = 0.f;
+  for (int k = 0; k < n; ++k) {
+    const float* o;
+    const float l = piece(k, o);
+    if (l == -INFINITY) continue;
+    const float wgt = __expf(l - mx);
+    sum += wgt;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = fmaf(wgt, o[lane * E + e], acc[e]);
+  }
+  const float inv = 1.0f / sum;
+#pragma unroll
+  for (int e = 0; e < E; ++e) op[e] = (bf16)(acc[e] * inv);
   if (lse && lane == 0) lse[idx] = mx + __logf(sum);
 }
 
@@ -660,11 +953,11 @@ static void launch_valu(unsigned blocks, hipStream_t s, const DevMap& m, const P
 template <int D, int W>
 static void launch_stream_main(int32_t runs, int32_t hg, hipStream_t s, const PoolInfo& p, int32_t layer,
                                const void* q, int32_t Hq, int32_t G, const StreamWs& w, float sl2, void* out,
-                               float* lse) {
+                               float* lse, int32_t pieces_only = 0) {
   hipLaunchKernelGGL((decode_stream_kernel<D, W, kStreamSets>), dim3((unsigned)(runs * hg)), dim3(64 * W), 0, s,
                      reinterpret_cast<const bf16*>(p.k_layer(layer)), reinterpret_cast<const bf16*>(p.v_layer(layer)),
                      static_cast<const bf16*>(q), Hq, p.num_kv_heads, G, hg, w.header, w.meta, sl2,
-                     static_cast<bf16*>(out), lse, w.o, w.lse);
+                     static_cast<bf16*>(out), lse, w.o, w.lse, pieces_only);
 }
 
 static hipError_t launch_stream_decode(const PoolInfo& p, int32_t layer, const void* q, int32_t Hq, const DevMap& m,
@@ -701,6 +994,114 @@ static hipError_t launch_stream_decode(const PoolInfo& p, int32_t layer, const v
   else
     hipLaunchKernelGGL(decode_stream_merge_kernel<64>, dim3(mblocks), dim3(256), 0, s, bs, Hq, w.header, w.prefix,
                        w.ntiles, w.o, w.lse, static_cast<bf16*>(out), lse);
+  return hipGetLastError();
+}
+
+// ---- cascade decode host side
+CascadePlan plan_cascade(const PoolInfo& p, int32_t bs, int32_t Hq, int32_t max_kv_len, int32_t num_groups,
+                         int32_t max_group_size, int32_t max_prefix_len) {
+  CascadePlan cp;
+  cp.dp = plan_decode(p, bs, Hq, max_kv_len);
+  const int Hkv = p.num_kv_heads;
+  const int G = Hq / Hkv;
+  cp.ms = std::max(1, kCascadeCols / G);
+  cp.slices = std::max(1, (max_group_size + cp.ms - 1) / cp.ms);
+  const int ptiles = std::max(1, (std::min(max_prefix_len, max_kv_len) + kTile - 1) / kTile);
+  const int64_t items = std::max<int64_t>(1, (int64_t)num_groups * cp.slices * Hkv);
+  // about four waves per CU over the prefix work
+  int chunks = (int)std::min<int64_t>(ptiles, std::max<int64_t>(1, (device_cu_count() * 4 + items - 1) / items));
+  cp.tpc = (ptiles + chunks - 1) / chunks;
+  cp.chunks = (ptiles + cp.tpc - 1) / cp.tpc;
+  return cp;
+}
+
+// [stream workspace | skip[bs] | prefix o[chunks][bs][Hq][D] | prefix lse[chunks][bs][Hq]]
+size_t cascade_ws_layout(const PoolInfo& p, const CascadePlan& cp, int32_t bs, int32_t Hq, void* base,
+                         CascadeWs* w) {
+  char* b = static_cast<char*>(base);
+  size_t off = stream_ws_layout(bs, cp.dp.chunk, cp.dp.max_splits, Hq, p.head_dim_v, base, w ? &w->stream : nullptr);
+  auto take = [&](size_t bytes) {
+    char* at = b ? b + off : nullptr;
+    off += align256(bytes);
+    return at;
+  };
+  char* skip = take((size_t)bs * 4);
+  char* po = take((size_t)cp.chunks * bs * Hq * p.head_dim_v * 4);
+  char* pl = take((size_t)cp.chunks * bs * Hq * 4);
+  if (w) {
+    w->skip = reinterpret_cast<int32_t*>(skip);
+    w->po = reinterpret_cast<float*>(po);
+    w->plse = reinterpret_cast<float*>(pl);
+  }
+  return off;
+}
+
+template <int D, int W>
+static void launch_cascade_prefix(const PoolInfo& p, int32_t layer, const DevMap& m, const void* q, int32_t bs,
+                                  int32_t Hq, int32_t G, int32_t hg, const int32_t* group_indptr,
+                                  const int32_t* prefix_len, int32_t num_groups, const CascadePlan& cp, float sl2,
+                                  const CascadeWs& w, hipStream_t s) {
+  const int64_t works = (int64_t)num_groups * cp.slices * cp.chunks;
+  const unsigned blocks = (unsigned)((works + 7) / 8 * 8 * hg);
+  auto kern = (m.fmt == MAP_TOKEN_TABLE) ? cascade_prefix_kernel<D, W, SLOT_TABLE> : cascade_prefix_kernel<D, W, SLOT_PAGES>;
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * W), 0, s, m, reinterpret_cast<const bf16*>(p.k_layer(layer)),
+                     reinterpret_cast<const bf16*>(p.v_layer(layer)), static_cast<const bf16*>(q), bs, Hq,
+                     p.num_kv_heads, G, hg, group_indptr, prefix_len, num_groups, cp.slices, cp.chunks, cp.tpc, cp.ms,
+                     sl2, w.po, w.plse);
+}
+
+hipError_t launch_decode_cascade(const PoolInfo& p, int32_t layer, const void* q, int32_t Hq, const DevMap& m,
+                                 int32_t bs, const CascadePlan& cp, const int32_t* group_indptr,
+                                 const int32_t* prefix_len, int32_t num_groups, float sm_scale, void* out, float* lse,
+                                 void* ws, hipStream_t s) {
+  if (bs == 0) return hipSuccess;
+  const int Hkv = p.num_kv_heads;
+  const int G = Hq / Hkv;
+  const int W = (Hkv % 4 == 0) ? 4 : (Hkv % 2 == 0 ? 2 : 1);
+  const int hg = Hkv / W;
+  const int32_t runs = cp.dp.max_splits;
+  if (cp.dp.kind != DK_STREAM || runs % 8 != 0) return hipErrorInvalidValue;
+  CascadeWs w;
+  cascade_ws_layout(p, cp, bs, Hq, ws, &w);
+  hipLaunchKernelGGL(cascade_skip_kernel, dim3((unsigned)((bs + 255) / 256)), dim3(256), 0, s, group_indptr,
+                     prefix_len, num_groups, bs, w.skip);
+  hipError_t e = launch_stream_plan(m, bs, cp.dp.chunk, runs, w.stream, s, w.skip);
+  if (e != hipSuccess) return e;
+  const float sl2 = sm_scale * kLog2e;
+  const int D = p.head_dim_qk;
+  timer_before(s);
+  if (D == 128) {
+    if (W == 4) launch_stream_main<128, 4>(runs, hg, s, p, layer, q, Hq, G, w.stream, sl2, out, lse, 1);
+    else if (W == 2) launch_stream_main<128, 2>(runs, hg, s, p, layer, q, Hq, G, w.stream, sl2, out, lse, 1);
+    else launch_stream_main<128, 1>(runs, hg, s, p, layer, q, Hq, G, w.stream, sl2, out, lse, 1);
+  } else {
+    if (W == 4) launch_stream_main<64, 4>(runs, hg, s, p, layer, q, Hq, G, w.stream, sl2, out, lse, 1);
+    else if (W == 2) launch_stream_main<64, 2>(runs, hg, s, p, layer, q, Hq, G, w.stream, sl2, out, lse, 1);
+    else launch_stream_main<64, 1>(runs, hg, s, p, layer, q, Hq, G, w.stream, sl2, out, lse, 1);
+  }
+  if (num_groups > 0) {
+    if (D == 128) {
+      if (W == 4) launch_cascade_prefix<128, 4>(p, layer, m, q, bs, Hq, G, hg, group_indptr, prefix_len, num_groups, cp, sl2, w, s);
+      else if (W == 2) launch_cascade_prefix<128, 2>(p, layer, m, q, bs, Hq, G, hg, group_indptr, prefix_len, num_groups, cp, sl2, w, s);
+      else launch_cascade_prefix<128, 1>(p, layer, m, q, bs, Hq, G, hg, group_indptr, prefix_len, num_groups, cp, sl2, w, s);
+    } else {
+      if (W == 4) launch_cascade_prefix<64, 4>(p, layer, m, q, bs, Hq, G, hg, group_indptr, prefix_len, num_groups, cp, sl2, w, s);
+      else if (W == 2) launch_cascade_prefix<64, 2>(p, layer, m, q, bs, Hq, G, hg, group_indptr, prefix_len, num_groups, cp, sl2, w, s);
+      else launch_cascade_prefix<64, 1>(p, layer, m, q, bs, Hq, G, hg, group_indptr, prefix_len, num_groups, cp, sl2, w, s);
+    }
+  }
+  e = hipGetLastError();
+  timer_after(s);
+  if (e != hipSuccess) return e;
+  const unsigned mblocks = (unsigned)(((int64_t)bs * Hq + 3) / 4);
+  if (D == 128)
+    hipLaunchKernelGGL(cascade_merge_kernel<128>, dim3(mblocks), dim3(256), 0, s, bs, Hq, cp.chunks, w.stream.header,
+                       w.stream.prefix, w.stream.ntiles, w.skip, w.stream.o, w.stream.lse, w.po, w.plse,
+                       static_cast<bf16*>(out), lse);
+  else
+    hipLaunchKernelGGL(cascade_merge_kernel<64>, dim3(mblocks), dim3(256), 0, s, bs, Hq, cp.chunks, w.stream.header,
+                       w.stream.prefix, w.stream.ntiles, w.skip, w.stream.o, w.stream.lse, w.po, w.plse,
+                       static_cast<bf16*>(out), lse);
   return hipGetLastError();
 }
 

@@ -106,8 +106,10 @@ struct StreamWs {
 };
 size_t stream_ws_layout(int32_t bs, int32_t max_tiles, int32_t runs, int32_t Hq, int32_t Dv, void* base,
                         StreamWs* w);
+// skip (nullable, device int32[bs]): keys left out at the start of each
+// request, a multiple of kStreamT (cascade decode reads them elsewhere).
 hipError_t launch_stream_plan(const DevMap& m, int32_t bs, int32_t max_tiles, int32_t runs, const StreamWs& w,
-                              hipStream_t s);
+                              hipStream_t s, const int32_t* skip = nullptr);
 int32_t device_cu_count();
 hipError_t launch_mla_decode(const PoolInfo& p, int32_t layer, const void* q, int32_t num_q_heads, const DevMap& m,
                              int32_t bs, const DecodePlan& plan, float scale_log2, void* out, float* lse, void* ws,
@@ -125,7 +127,31 @@ hipError_t launch_decode(const PoolInfo& p, int32_t layer, const void* q, int32_
                          int32_t bs, const DecodePlan& plan, float sm_scale, void* out, float* lse, void* ws,
                          hipStream_t s);
 
-bool extend_supported(const PoolInfo& p, int32_t num_q_heads);
+// Cascade decode over shared prefixes (pkv_decode.hip): the stream decode of
+// each request's own keys plus one pass per group over the shared ones.
+struct CascadePlan {
+  DecodePlan dp;   // the stream plan of the own (suffix) keys
+  int32_t ms;      // members per slice (32 query rows per wave)
+  int32_t slices;  // slices per group, at most
+  int32_t chunks;  // prefix chunks per group
+  int32_t tpc;     // tiles per chunk
+};
+struct CascadeWs {
+  StreamWs stream;
+  int32_t* skip;  // per request: keys read by the prefix pass
+  float* po;      // prefix partials [chunks][bs][Hq][Dv]
+  float* plse;    // [chunks][bs][Hq]
+};
+CascadePlan plan_cascade(const PoolInfo& p, int32_t bs, int32_t Hq, int32_t max_kv_len, int32_t num_groups,
+                         int32_t max_group_size, int32_t max_prefix_len);
+size_t cascade_ws_layout(const PoolInfo& p, const CascadePlan& cp, int32_t bs, int32_t Hq, void* base,
+                         CascadeWs* w);
+hipError_t launch_decode_cascade(const PoolInfo& p, int32_t layer, const void* q, int32_t Hq, const DevMap& m,
+                                 int32_t bs, const CascadePlan& cp, const int32_t* group_indptr,
+                                 const int32_t* prefix_len, int32_t num_groups, float sm_scale, void* out, float* lse,
+                                 void* ws, hipStream_t s);
+
+bool extend_supported(const PoolInfo& p, int32_t num_q_heads);bool extend_supported(const PoolInfo& p, int32_t num_q_heads);
 hipError_t launch_extend(const PoolInfo& p, int32_t layer, const void* q, int64_t total_q, const int32_t* qo_indptr,
                          int32_t num_q_heads, int32_t max_q_len, const DevMap& m, int32_t bs, int32_t max_kv_len,
                          int32_t causal, const int32_t* causal_flags, float softcap, float sm_scale, void* out,

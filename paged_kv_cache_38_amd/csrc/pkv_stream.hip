@@ -32,20 +32,30 @@ constexpr int kPlanTiles = 8;  // tiles per planner workgroup (256 threads)
 
 __device__ __forceinline__ int32_t stream_tiles(int32_t L) { return L > 0 ? (L + kStreamT - 1) / kStreamT : 0; }
 
+// With `skip` (cascade decode), request i's first skip[i] keys (a multiple
+// of the tile) are left out: its tiles start at key skip[i].
+__device__ __forceinline__ int32_t skip_tiles(const int32_t* skip, int32_t i, int32_t T) {
+  return skip ? min(max(skip[i], 0) / kStreamT, T) : 0;
+}
+
 template <int FMT>
 __global__ void __launch_bounds__(256) stream_plan_kernel(DevMap m, int32_t bs, int32_t max_tiles, int32_t runs,
                                                        int32_t* __restrict__ header,
                                                        int32_t* __restrict__ prefix, int32_t* __restrict__ ntiles,
-                                                       int32_t* __restrict__ fallback, int32_t* __restrict__ meta) {
+                                                       int32_t* __restrict__ fallback, int32_t* __restrict__ meta,
+                                                       const int32_t* __restrict__ skip) {
   __shared__ int32_t red[2][4];
   const int i = blockIdx.x, c = blockIdx.y;
   const int tid = threadIdx.x;
-  const int32_t T = min(stream_tiles(m.kv_lens[i]), max_tiles);
+  const int32_t T_all = min(stream_tiles(m.kv_lens[i]), max_tiles);
+  const int32_t st = skip_tiles(skip, i, T_all);  // tiles left out at the start
+  const int32_t T = T_all - st;
   const bool lead = c == 0;
   if (!lead && c * kPlanTiles >= T) return;  // uniform per workgroup
   int32_t tot = 0, pre = 0;
   for (int k = tid; k < bs; k += 256) {
-    const int32_t Tk = min(stream_tiles(m.kv_lens[k]), max_tiles);
+    const int32_t Tk_all = min(stream_tiles(m.kv_lens[k]), max_tiles);
+    const int32_t Tk = Tk_all - skip_tiles(skip, k, Tk_all);
     tot += Tk;
     if (k < i) pre += Tk;
   }
@@ -62,7 +72,7 @@ __global__ void __launch_bounds__(256) stream_plan_kernel(DevMap m, int32_t bs, 
   pre = red[1][0] + red[1][1] + red[1][2] + red[1][3];
   // keys past max_kv_len (a caller error) are not read: the workspace holds
   // max_tiles tiles per request
-  const int32_t L = min(max(m.kv_lens[i], 0), T * kStreamT);
+  const int32_t L = min(max(m.kv_lens[i], 0), T_all * kStreamT);
   if (lead && tid == 0) {
     prefix[i] = pre;
     ntiles[i] = T;
@@ -76,7 +86,8 @@ __global__ void __launch_bounds__(256) stream_plan_kernel(DevMap m, int32_t bs, 
   if (j >= T) return;
   const SlotMap<FMT> sm = make_slotmap<FMT>(m, i);
   int32_t* tile = meta + (int64_t)(pre + j) * kStreamMetaWords;
-  tile[tid & 31] = sm(min(j * kStreamT + (tid & 31), L - 1), true);
+  const int32_t jt = st + j;  // key tile
+  tile[tid & 31] = sm(min(jt * kStreamT + (tid & 31), L - 1), true);
   const int f = tid & 31;
   if (f < 8) {
     int32_t v = 0;
@@ -84,7 +95,7 @@ __global__ void __launch_bounds__(256) stream_plan_kernel(DevMap m, int32_t bs, 
     else if (f == 1) v = j;
     else if (f == 2) v = T;
     else if (f == 3) v = pre;
-    else if (f == 4) v = min(kStreamT, L - j * kStreamT);
+    else if (f == 4) v = min(kStreamT, L - jt * kStreamT);
     tile[32 + f] = v;
   }
 }
@@ -123,14 +134,14 @@ size_t stream_ws_layout(int32_t bs, int32_t max_tiles, int32_t runs, int32_t Hq,
 }
 
 hipError_t launch_stream_plan(const DevMap& m, int32_t bs, int32_t max_tiles, int32_t runs, const StreamWs& w,
-                              hipStream_t s) {
+                              hipStream_t s, const int32_t* skip) {
   const dim3 grid((unsigned)bs, (unsigned)std::max(1, (max_tiles + kPlanTiles - 1) / kPlanTiles));
   if (m.fmt == MAP_TOKEN_TABLE)
     hipLaunchKernelGGL(stream_plan_kernel<SLOT_TABLE>, grid, dim3(256), 0, s, m, bs, max_tiles, runs, w.header,
-                       w.prefix, w.ntiles, w.fallback, w.meta);
+                       w.prefix, w.ntiles, w.fallback, w.meta, skip);
   else
     hipLaunchKernelGGL(stream_plan_kernel<SLOT_PAGES>, grid, dim3(256), 0, s, m, bs, max_tiles, runs, w.header,
-                       w.prefix, w.ntiles, w.fallback, w.meta);
+                       w.prefix, w.ntiles, w.fallback, w.meta, skip);
   return hipGetLastError();
 }
 

@@ -1,0 +1,105 @@
+"""GPU parity of the cascade decode over shared prefixes (each group's
+shared prefix read once for all members, each request's own keys by the
+split-K decode, merged by log-sum-exp) against the oracle, through the C
+ABI.  The oracle knows nothing of groups: the result must be plain
+attention over each request's keys."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_38_amd as P
+import workloads as W
+
+from gpu_util import DeviceCase, assert_attn_close, assert_lse_close, i32, oracle_region
+
+pytestmark = pytest.mark.gpu
+
+FMTS = [P.PKV_MAP_TOKEN_TABLE, P.PKV_MAP_CSR, P.PKV_MAP_BLOCK_TABLE]
+
+
+def cascade(dc, fmt, indptr, prefix_len, max_group=None):
+    c, g = dc.case, dc.case.geom
+    m = dc.kv_map("self", fmt)
+    ip, pl = i32(indptr), i32(prefix_len)
+    mg = max_group if max_group is not None else int(np.diff(indptr).max(initial=0))
+    groups = P.make_prefix_groups(ip, pl, mg, int(np.max(prefix_len, initial=0)))
+    out = torch.full((c.bs, g.num_q_heads, g.head_dim_v), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((c.bs, g.num_q_heads), float("nan"), dtype=torch.float32, device="cuda")
+    nb = P.paged_decode_cascade_workspace_bytes(dc.pool, c.bs, g.num_q_heads, m.max_kv_len, groups)
+    ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda")
+    P.paged_decode_attn_cascade(dc.pool, 0, dc.q["self"], m, groups, c.sm_scale, out, lse, ws)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def small(ps, seed=0, bs=32, group=8, prefix=512, num_q_heads=32):
+    return W.gqa_prefix_share(ps, seed=seed, bs=bs, group=group, prefix=prefix, median=prefix, clip=(64, 4 * prefix),
+                              num_q_heads=num_q_heads)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("ps", [16, 64])
+def test_cascade_matches_oracle(ps, fmt):
+    case = small(ps, seed=ps)
+    print(f"cascade ps {ps} fmt {fmt}: lens {case.regions['self'].kv_lens.tolist()}", flush=True)
+    vals = W.make_values(case, canary=True)
+    dc = DeviceCase(case, vals)
+    out, lse = cascade(dc, fmt, *case.prefix_groups)
+    ref_o, ref_l = oracle_region(case, vals, "self")
+    assert_attn_close(out, ref_o, "bf16", f"cascade ps {ps} fmt {fmt}")
+    assert_lse_close(lse, ref_l, "bf16", f"cascade ps {ps} fmt {fmt}")
+
+
+@pytest.mark.parametrize("group,heads", [(16, 32), (8, 64), (4, 8)])
+def test_cascade_group_slices_and_head_counts(group, heads):
+    """Groups with more rows than one wave holds (16 members x 4 heads, 8 x 8)
+    and a group of one-head members."""
+    case = small(16, seed=group + heads, bs=32, group=group, prefix=256, num_q_heads=heads)
+    vals = W.make_values(case, canary=True)
+    dc = DeviceCase(case, vals)
+    out, lse = cascade(dc, P.PKV_MAP_CSR, *case.prefix_groups)
+    ref_o, ref_l = oracle_region(case, vals, "self")
+    assert_attn_close(out, ref_o, "bf16", f"cascade group {group} heads {heads}")
+    assert_lse_close(lse, ref_l, "bf16", f"cascade group {group} heads {heads}")
+
+
+def test_cascade_unaligned_prefix_partial_groups_and_empty_request():
+    """prefix_len 48 (not a multiple of the 32-key tile: the cascade splits
+    at 32), only the first two groups declared (the rest decode as plain
+    requests), and one empty request inside a group."""
+    case = small(16, seed=5, bs=32, group=8, prefix=48)
+    case.regions["self"].kv_lens[3] = 0
+    vals = W.make_values(case, canary=True)
+    dc = DeviceCase(case, vals)
+    indptr, pl = case.prefix_groups
+    out, lse = cascade(dc, P.PKV_MAP_TOKEN_TABLE, indptr[:3], pl[:2])
+    ref_o, ref_l = oracle_region(case, vals, "self")
+    assert_attn_close(out, ref_o, "bf16", "cascade unaligned")
+    assert_lse_close(lse, ref_l, "bf16", "cascade unaligned")
+    assert (out[3].float() == 0).all() and torch.isneginf(lse[3]).all()
+
+
+def test_cascade_without_groups_equals_decode_bitwise():
+    case = small(64, seed=7)
+    vals = W.make_values(case)
+    dc = DeviceCase(case, vals)
+    o1, l1 = dc.decode(P.PKV_MAP_CSR)
+    o2, l2 = cascade(dc, P.PKV_MAP_CSR, np.zeros(1, np.int32), np.zeros(0, np.int32), max_group=0)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+
+
+def test_cascade_full_size_prefix_share():
+    """The 256-request, 2048-token-prefix workload at page_size 16, checked on
+    a seeded sample of requests (always the shortest and the longest)."""
+    case = W.gqa_prefix_share(16, seed=0)
+    vals = W.make_values(case, device="cuda")
+    dc = DeviceCase(case, vals)
+    out, lse = cascade(dc, P.PKV_MAP_CSR, *case.prefix_groups)
+    L = case.regions["self"].kv_lens
+    rng = np.random.default_rng(3)
+    reqs = sorted(set(rng.choice(case.bs, 30, replace=False).tolist()) | {int(np.argmin(L)), int(np.argmax(L))})
+    ref_o, ref_l = oracle_region(case, vals, "self", requests=reqs)
+    rows = np.asarray(reqs)
+    assert_attn_close(out, ref_o, "bf16", "cascade full size", rows=rows)
+    assert_lse_close(lse, ref_l, "bf16", "cascade full size", rows=rows)

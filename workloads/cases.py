@@ -27,7 +27,7 @@ page placement, K/V values, queries).
 from __future__ import annotations
 
 from dataclasses import dataclass, field
-from typing import Dict, List, Optional
+from typing import Dict, List, Optional, Tuple
 
 import numpy as np
 
@@ -98,6 +98,8 @@ class Case:
     free_pages: np.ndarray  # pages no request owns
     tail_slots: np.ndarray  # slots of owned pages that no region covers
     dummy: np.ndarray = field(default_factory=lambda: np.zeros(0, bool))  # [bs] padded-batch dummies
+    # requests sharing a prefix: (group_indptr int32 [G + 1], prefix_len int32 [G]) or None
+    prefix_groups: Optional[Tuple[np.ndarray, np.ndarray]] = None
 
     @property
     def padding_row(self) -> int:
@@ -276,6 +278,7 @@ def gqa_prefix_share(page_size: int, seed: int = 0, bs: int = 256, group: int = 
         sm_scale=1.0 / np.sqrt(128.0), value_scale=1.0, value_seed=vseed, query_seed=qseed,
         free_pages=perm[pos:].astype(np.int64),
         tail_slots=np.concatenate(tails) if tails else np.zeros(0, np.int64),
+        prefix_groups=(np.arange(0, bs + 1, group, dtype=np.int32), np.full(ngroups, prefix, np.int32)),
     )
 
 
