@@ -643,7 +643,9 @@ __global__ void __launch_bounds__(256) cascade_merge_kernel(int32_t bs, int32_t 
     return ws_plse[row];
   };
   const int n = (b1 - b0 + 1) + nc;
+  // the sources' lse loads are independent: issue them together
   float mx = -INFINITY;
+#pragma unroll 8
   for (int k = 0; k < n; ++k) {
     const float* o;
     mx = fmaxf(mx, piece(k, o));
@@ -659,6 +661,7 @@ __global__ void __launch_bounds__(256) cascade_merge_kernel(int32_t bs, int32_t 
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
   float sum = 0.f;
+#pragma unroll 8
   for (int k = 0; k < n; ++k) {
     const float* o;
     const float l = piece(k, o);
