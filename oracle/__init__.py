@@ -62,3 +62,10 @@ from .alloc import (  # noqa: F401
     pages_of_slots,
     write_req_to_token,
 )
+from .enc_cache import (  # noqa: F401
+    write_blocks,
+    merge_blocks,
+    fill_counts,
+    check_filled,
+    global_to_local_positions,
+)
