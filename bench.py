@@ -493,6 +493,86 @@ class ExtendBench:
 
 
 # ---------------------------------------------------------------------------
+# encoder-embedding block cache workload
+# ---------------------------------------------------------------------------
+class EncCacheBench:
+    """Encoder cache step at the Neuron notes' Qwen3-VL geometry: the encoder's
+    8 output blocks scattered into the cache (6 items + 2 padding blocks to
+    the scratch block), then 8 blocks gathered and merged into the batch's
+    hidden rows by the position map (2865 real tokens of 40 KiB)."""
+
+    attn_calls = 1
+    dtype = "bf16"
+    tokens_label = "merged_tokens_per_s"
+    kernel_name = "encoder cache: enc_write_kernel + enc_merge_kernel"
+
+    def __init__(self, dev="cuda"):
+        import torch
+        import paged_kv_cache_38_amd as P
+        from workloads.enc_cache import enc_cache_case
+
+        self.P, self.torch, self.case = P, torch, None
+        self.w = w = enc_cache_case(seed=0)
+        g = torch.Generator(device=dev).manual_seed(w.value_seed)
+        shape = (w.block_size, w.fat_dim)
+        self.buf = torch.randn((w.num_blocks, *shape), generator=g, device=dev).to(torch.bfloat16)
+        self.src = torch.randn((len(w.write_ids), *shape), generator=g, device=dev).to(torch.bfloat16)
+        self.hidden = torch.zeros((w.num_tokens, w.fat_dim), dtype=torch.bfloat16, device=dev)
+        self.write_ids = i32(w.write_ids, dev)
+        self.gather_ids = i32(w.gather_ids, dev)
+        self.pos = torch.from_numpy(w.positions).to(dev)
+        self.row = w.fat_dim * 2
+        self.stream = torch.cuda.current_stream().cuda_stream
+        self.hip = HipEvents().hip
+        self.hip.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
+
+    def step(self, timers=None):
+        P = self.P
+        if timers:
+            assert self.hip.hipEventRecord(C.c_void_p(timers[0][0]), C.c_void_p(self.stream)) == 0
+        P.enc_cache_write(self.buf, self.src, self.write_ids)
+        P.enc_cache_merge(self.buf, self.gather_ids, self.pos, self.hidden)
+        if timers:
+            assert self.hip.hipEventRecord(C.c_void_p(timers[0][1]), C.c_void_p(self.stream)) == 0
+
+    def kernel_bytes(self, logical: bool = False) -> int:
+        """Every written block read and written once, every real gathered
+        token's row read and written once, plus the position map."""
+        w = self.w
+        return (2 * len(w.write_ids) * w.block_size * self.row + 2 * w.real_tokens * self.row +
+                w.positions.size * 8 + 4 * (len(w.write_ids) + len(w.gather_ids)))
+
+    def step_bytes(self) -> int:
+        return self.kernel_bytes()
+
+    def kernel_flops(self) -> int:
+        return 0
+
+    def tokens_per_step(self) -> int:
+        return self.w.real_tokens
+
+    def cpu_baseline(self, budget_s: float):
+        import oracle
+        from workloads.cases import to_numpy_bits
+
+        w = self.w
+        self.torch.cuda.synchronize()
+        buf = to_numpy_bits(self.buf)
+        src = to_numpy_bits(self.src)
+        hidden = to_numpy_bits(self.hidden)
+        steps, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 <= budget_s:
+            b2 = oracle.write_blocks(buf, src, w.write_ids)
+            oracle.merge_blocks(b2, w.gather_ids, w.positions, hidden, w.num_tokens)
+            steps += 1
+        dt = time.perf_counter() - t0
+        return {"value": round(steps * self.kernel_bytes() / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+                "kind": "oracle", "merged_tokens_per_s": round(steps * w.real_tokens / dt, 1),
+                "sample": f"{steps} whole write + merge steps by the numpy oracle (a full buffer copy per write), "
+                          f"{dt:.1f} s"}
+
+
+# ---------------------------------------------------------------------------
 # slot allocation workload
 # ---------------------------------------------------------------------------
 class AllocBench:
@@ -502,6 +582,7 @@ class AllocBench:
     (every prefix is page aligned), so every step does the same work."""
 
     attn_calls = 1
+    dtype = "int32"
     tokens_label = "new_slots_per_s"
     metric = "slot allocation step (alloc + row write + free): new slots per second, 1 GPU"
     unit = "slots/s"
@@ -630,6 +711,11 @@ def build_workload(name: str):
             "new_tokens": "U{1..512}",
             "step": "kv_store + build_kv_indices(CSR) x2 + " + ("kv_gather x2 + " if ragged else "")
                     + "paged_extend_attn (causal self + cross)"}
+    if name == "enc_cache_qwen3vl":
+        return EncCacheBench(), {
+            "workload": "encoder_cache_qwen3vl_bf16", "num_blocks": 33, "block_size": 512, "fat_dim": 20480,
+            "written_blocks": "8 (6 items + 2 padding to the scratch block)", "gathered_blocks": 8,
+            "real_tokens": 2865, "num_tokens": 8192, "step": "enc_cache_write + enc_cache_merge"}
     if name in ("serving_alloc_decode", "serving_alloc_extend"):
         dec = name.endswith("decode")
         return AllocBench(dec), {
@@ -751,7 +837,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": b.case.geom.dtype if b.case is not None else "int32",
+        "dtype": b.case.geom.dtype if b.case is not None else b.dtype,
         "data": "synthetic (seeded; N(0,1) values)",
         "config": cfg,
         "hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),

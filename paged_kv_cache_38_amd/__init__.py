@@ -40,6 +40,7 @@ __all__ = [
     "paged_decode_attn_cascade", "paged_verify_attn", "paged_extend_attn", "paged_extend_attn_ex", "kv_gather",
     "kv_validate",
     "pkv_set_kernel_timer", "library",
+    "enc_cache_write", "enc_cache_merge", "enc_cache_check",
     "FreeList", "kv_free_list_create", "kv_free_list_init", "kv_alloc", "kv_alloc_extend", "kv_alloc_decode",
     "kv_free", "write_req_to_token",
 ]
@@ -335,6 +336,57 @@ def paged_extend_attn_ex(pool: Pool, layer: int, q: torch.Tensor, qo_indptr: tor
                                           C.byref(kv_map.struct), C.byref(opts), float(sm_scale),
                                           _dev(out, "out", pool.dtype), _dev(lse, "lse", torch.float32),
                                           _stream(stream)), "paged_extend_attn_ex")
+
+
+# ---------------------------------------------------------------------------
+# encoder-embedding block cache
+# ---------------------------------------------------------------------------
+
+def _enc_geometry(buffer: torch.Tensor):
+    if buffer.dim() < 2:
+        raise ValueError("buffer must be [num_blocks, block_size, ...]")
+    row_bytes = buffer[0, 0].numel() * buffer.element_size()
+    return buffer.shape[0], buffer.shape[1], row_bytes
+
+
+def enc_cache_write(buffer: torch.Tensor, src: torch.Tensor, block_ids: torch.Tensor, stream=None) -> None:
+    """buffer [num_blocks, block_size, ...]; src [n, block_size, ...] of the
+    same dtype and row shape; block_ids device int32[n]."""
+    nb, bsz, rb = _enc_geometry(buffer)
+    if src.dtype != buffer.dtype or src.shape[1:] != buffer.shape[1:] or block_ids.numel() != src.shape[0]:
+        raise ValueError("src must be [n, block_size, ...] like buffer, with one block id per block")
+    L.check(L.load().enc_cache_write(_dev(buffer, "buffer"), nb, bsz, rb, _dev(src, "src"), src.shape[0],
+                                     _dev(block_ids, "block_ids", torch.int32), _stream(stream)), "enc_cache_write")
+
+
+def enc_cache_merge(buffer: torch.Tensor, block_ids: torch.Tensor, positions: torch.Tensor, hidden: torch.Tensor,
+                    fill_count: Optional[torch.Tensor] = None, stream=None) -> None:
+    """positions device int64 [max_blocks, block_size]; hidden [num_tokens,
+    ...] rows like the buffer's; fill_count optional int32[num_tokens]."""
+    nb, bsz, rb = _enc_geometry(buffer)
+    if positions.dim() != 2 or positions.shape[1] != bsz or block_ids.numel() != positions.shape[0]:
+        raise ValueError("positions must be [max_blocks, block_size] with one block id per row")
+    if hidden.dtype != buffer.dtype or hidden[0].numel() * hidden.element_size() != rb:
+        raise ValueError("hidden rows must match the buffer's rows")
+    L.check(L.load().enc_cache_merge(_dev(buffer, "buffer"), nb, bsz, rb, _dev(block_ids, "block_ids", torch.int32),
+                                     positions.shape[0], _dev(positions, "positions", torch.int64),
+                                     _dev(hidden, "hidden"), hidden.shape[0],
+                                     _dev(fill_count, "fill_count", torch.int32), _stream(stream)),
+            "enc_cache_merge")
+
+
+def enc_cache_check(fill_count: torch.Tensor, scheduled: Optional[torch.Tensor] = None,
+                    stream=None) -> Tuple[int, list]:
+    """Returns (status, [unfilled scheduled rows, rows filled twice]);
+    synchronises the stream."""
+    scratch = torch.empty(2, dtype=torch.int64, device=fill_count.device)
+    counts = (C.c_int64 * 2)()
+    st = L.load().enc_cache_check(_dev(fill_count, "fill_count", torch.int32),
+                                  _dev(scheduled, "scheduled", torch.int32), fill_count.numel(),
+                                  _dev(scratch, "scratch", torch.int64), counts, _stream(stream))
+    if st not in (L.PKV_OK, L.PKV_EINVAL):
+        L.check(st, "enc_cache_check")
+    return st, list(counts)
 
 
 # ---------------------------------------------------------------------------

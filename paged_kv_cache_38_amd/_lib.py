@@ -119,6 +119,12 @@ SIGNATURES = {
     "paged_extend_attn_ex": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_int64, C.c_void_p, C.c_int32,
                                        C.c_int32, C.POINTER(KVMapStruct), C.POINTER(ExtendOpts), C.c_float,
                                        C.c_void_p, C.c_void_p, C.c_void_p]),
+    "enc_cache_write": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int64, C.c_void_p, C.c_int32, C.c_void_p,
+                                  C.c_void_p]),
+    "enc_cache_merge": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int64, C.c_void_p, C.c_int32, C.c_void_p,
+                                  C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p]),
+    "enc_cache_check": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p, C.POINTER(C.c_int64),
+                                  C.c_void_p]),
     "kv_gather": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(KVMapStruct), C.c_void_p, C.c_void_p, C.c_void_p,
                             C.c_int64, C.c_void_p]),
     "kv_validate": (C.c_int, [C.c_void_p, C.POINTER(KVMapStruct), C.c_void_p, C.c_void_p,

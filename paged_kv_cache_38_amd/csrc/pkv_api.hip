@@ -11,6 +11,7 @@
 
 #include "pagedkv.h"
 #include "pkv_alloc.h"
+#include "pkv_enc.h"
 #include "pkv_launch.h"
 
 struct pkv_pool {
@@ -588,6 +589,64 @@ int kv_validate(const pkv_pool* pool, const pkv_kv_map* map, const int32_t* is_d
   return fail(PKV_EINVAL, "map violations: range %lld, padding %lld, neg %lld, align %lld, contig %lld, len %lld",
               (long long)counts[0], (long long)counts[1], (long long)counts[2], (long long)counts[3],
               (long long)counts[4], (long long)counts[5]);
+}
+
+namespace {
+int check_enc_geometry(int32_t num_blocks, int32_t block_size, int64_t row_bytes) {
+  if (num_blocks <= 0 || block_size <= 0) return fail(PKV_EINVAL, "num_blocks and block_size must be positive");
+  if (row_bytes <= 0 || row_bytes % 16 != 0) return fail(PKV_EALIGN, "row_bytes must be a positive multiple of 16");
+  return ok();
+}
+}  // namespace
+
+int enc_cache_write(void* buffer, int32_t num_blocks, int32_t block_size, int64_t row_bytes, const void* src,
+                    int32_t n, const int32_t* block_ids, void* stream) {
+  if (int st = check_enc_geometry(num_blocks, block_size, row_bytes)) return st;
+  if (n < 0) return fail(PKV_EINVAL, "negative n");
+  if (n == 0) return ok();
+  if (!buffer || !src || !block_ids) return fail(PKV_EINVAL, "null buffer, src or block_ids");
+  if (!aligned16(buffer) || !aligned16(src)) return fail(PKV_EALIGN, "buffer and src must be 16-byte aligned");
+  if ((int64_t)n * block_size > INT32_MAX) return fail(PKV_EUNSUPPORTED, "too many rows in one call");
+  return device_status(pkv::launch_enc_write(static_cast<char*>(buffer), num_blocks, block_size, row_bytes / 16,
+                                             static_cast<const char*>(src), n, block_ids, (hipStream_t)stream),
+                       "enc_cache_write");
+}
+
+int enc_cache_merge(const void* buffer, int32_t num_blocks, int32_t block_size, int64_t row_bytes,
+                    const int32_t* block_ids, int32_t max_blocks, const int64_t* positions, void* hidden,
+                    int64_t num_tokens, int32_t* fill_count, void* stream) {
+  if (int st = check_enc_geometry(num_blocks, block_size, row_bytes)) return st;
+  if (max_blocks < 0 || num_tokens < 0) return fail(PKV_EINVAL, "negative max_blocks or num_tokens");
+  if (max_blocks == 0) return ok();
+  if (!buffer || !block_ids || !positions || (num_tokens > 0 && !hidden))
+    return fail(PKV_EINVAL, "null buffer, block_ids, positions or hidden");
+  if (!aligned16(buffer) || !aligned16(hidden)) return fail(PKV_EALIGN, "buffer and hidden must be 16-byte aligned");
+  if ((int64_t)max_blocks * block_size > INT32_MAX) return fail(PKV_EUNSUPPORTED, "too many rows in one call");
+  return device_status(pkv::launch_enc_merge(static_cast<const char*>(buffer), num_blocks, block_size, row_bytes / 16,
+                                             block_ids, max_blocks, positions, static_cast<char*>(hidden),
+                                             num_tokens, fill_count, (hipStream_t)stream),
+                       "enc_cache_merge");
+}
+
+int enc_cache_check(const int32_t* fill_count, const int32_t* scheduled, int64_t num_tokens, int64_t* scratch,
+                    int64_t counts[2], void* stream) {
+  if (!counts) return fail(PKV_EINVAL, "null counts");
+  counts[0] = counts[1] = 0;
+  if (num_tokens < 0) return fail(PKV_EINVAL, "negative num_tokens");
+  if (num_tokens == 0) return ok();
+  if (!fill_count || !scratch) return fail(PKV_EINVAL, "null fill_count or scratch");
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = pkv::launch_enc_check(fill_count, scheduled, num_tokens, reinterpret_cast<long long*>(scratch), s);
+  if (e != hipSuccess) return device_status(e, "enc_cache_check launch");
+  long long host[2] = {0, 0};
+  e = hipMemcpyAsync(host, scratch, sizeof(host), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return device_status(e, "enc_cache_check copy");
+  counts[0] = host[0];
+  counts[1] = host[1];
+  if (host[0] == 0 && host[1] == 0) return ok();
+  return fail(PKV_EINVAL, "encoder positions: %lld scheduled rows unfilled, %lld rows filled more than once",
+              host[0], host[1]);
 }
 
 int pkv_set_kernel_timer(void* start_event, void* stop_event) {

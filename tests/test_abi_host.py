@@ -257,3 +257,21 @@ def test_verify_arguments_checked_before_launch(lib):
     finally:
         lib.kv_pool_destroy(h)
         lib.kv_pool_destroy(hs)
+
+
+def test_encoder_cache_arguments_checked_before_launch(lib):
+    buf, src, ids, pos, hid = 0x10000, 0x20000, 0x3000, 0x4000, 0x50000
+    assert lib.enc_cache_write(buf, 9, 16, 130, src, 4, ids, None) == L.PKV_EALIGN   # row not a multiple of 16
+    assert lib.enc_cache_write(buf, 0, 16, 128, src, 4, ids, None) == L.PKV_EINVAL
+    assert lib.enc_cache_write(buf, 9, 16, 128, src, -1, ids, None) == L.PKV_EINVAL
+    assert lib.enc_cache_write(buf, 9, 16, 128, None, 4, ids, None) == L.PKV_EINVAL
+    assert lib.enc_cache_write(buf + 8, 9, 16, 128, src, 4, ids, None) == L.PKV_EALIGN
+    assert lib.enc_cache_write(buf, 9, 16, 128, src, 0, ids, None) == 0
+    assert lib.enc_cache_merge(buf, 9, 16, 128, ids, 4, None, hid, 90, None, None) == L.PKV_EINVAL
+    assert lib.enc_cache_merge(buf, 9, 16, 128, ids, -1, pos, hid, 90, None, None) == L.PKV_EINVAL
+    assert lib.enc_cache_merge(buf, 9, 16, 128, ids, 4, pos, hid + 4, 90, None, None) == L.PKV_EALIGN
+    assert lib.enc_cache_merge(buf, 9, 16, 128, ids, 0, pos, hid, 90, None, None) == 0
+    counts = (C.c_int64 * 2)()
+    assert lib.enc_cache_check(None, None, 10, 0x6000, counts, None) == L.PKV_EINVAL
+    assert lib.enc_cache_check(0x7000, None, 0, 0x6000, counts, None) == 0
+    assert lib.enc_cache_check(0x7000, None, 10, 0x6000, None, None) == L.PKV_EINVAL
