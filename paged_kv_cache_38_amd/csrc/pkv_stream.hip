@@ -20,15 +20,19 @@
 namespace pkv {
 
 // ---------------------------------------------------------------------------
-// Planner: workgroup (i, c) resolves tiles 8c .. 8c+7 of request i, one
-// thread per key position, and writes their info words {request, tile,
+// Planner: workgroup (i, c) resolves tiles kPlanTiles c .. of request i,
+// one thread per key position, and writes their info words {request, tile,
 // tiles of request, tile prefix, valid keys}; tokens past the request's end
 // repeat its last key, whose weight is then exactly 0.  Every workgroup sums
 // the tile counts itself (bs loads), so the planner is one launch with no
 // serial pass; workgroup (i, 0) also writes the request's prefix, tile count
 // and fallback flag, and (0, 0) the run length Bt and the tile total.
 // ---------------------------------------------------------------------------
-constexpr int kPlanTiles = 8;  // tiles per planner workgroup (256 threads)
+// Tiles per planner workgroup (256 threads: eight tiles at a time).  A
+// workgroup's fixed cost (the O(bs) sums) and the empty workgroups past
+// short requests' ends are what the planner spends its time on, so each
+// takes several passes.
+constexpr int kPlanTiles = 64;
 
 __device__ __forceinline__ int32_t stream_tiles(int32_t L) { return L > 0 ? (L + kStreamT - 1) / kStreamT : 0; }
 
@@ -82,21 +86,22 @@ __global__ void __launch_bounds__(256) stream_plan_kernel(DevMap m, int32_t bs, 
       header[1] = tot;
     }
   }
-  const int j = c * kPlanTiles + (tid >> 5);
-  if (j >= T) return;
   const SlotMap<FMT> sm = make_slotmap<FMT>(m, i);
-  int32_t* tile = meta + (int64_t)(pre + j) * kStreamMetaWords;
-  const int32_t jt = st + j;  // key tile
-  tile[tid & 31] = sm(min(jt * kStreamT + (tid & 31), L - 1), true);
-  const int f = tid & 31;
-  if (f < 8) {
-    int32_t v = 0;
-    if (f == 0) v = i;
-    else if (f == 1) v = j;
-    else if (f == 2) v = T;
-    else if (f == 3) v = pre;
-    else if (f == 4) v = min(kStreamT, L - jt * kStreamT);
-    tile[32 + f] = v;
+  const int j_end = min(T, (c + 1) * kPlanTiles);
+  for (int j = c * kPlanTiles + (tid >> 5); j < j_end; j += 256 / 32) {
+    int32_t* tile = meta + (int64_t)(pre + j) * kStreamMetaWords;
+    const int32_t jt = st + j;  // key tile
+    tile[tid & 31] = sm(min(jt * kStreamT + (tid & 31), L - 1), true);
+    const int f = tid & 31;
+    if (f < 8) {
+      int32_t v = 0;
+      if (f == 0) v = i;
+      else if (f == 1) v = j;
+      else if (f == 2) v = T;
+      else if (f == 3) v = pre;
+      else if (f == 4) v = min(kStreamT, L - jt * kStreamT);
+      tile[32 + f] = v;
+    }
   }
 }
 
