@@ -275,3 +275,35 @@ def test_encoder_cache_arguments_checked_before_launch(lib):
     assert lib.enc_cache_check(None, None, 10, 0x6000, counts, None) == L.PKV_EINVAL
     assert lib.enc_cache_check(0x7000, None, 0, 0x6000, counts, None) == 0
     assert lib.enc_cache_check(0x7000, None, 10, 0x6000, None, None) == L.PKV_EINVAL
+
+
+def test_cascade_arguments_checked_before_launch(lib):
+    st, h = make_pool(lib, desc(dtype=1, head_dim_qk=128, head_dim_v=128, num_kv_heads=2))
+    assert st == 0
+    st2, hf = make_pool(lib, desc(dtype=0))  # f32 pool: no cascade kernel
+    assert st2 == 0
+    try:
+        m = L.KVMapStruct()
+        m.fmt, m.bs, m.kv_lens, m.max_kv_len = L.PKV_MAP_CSR, 4, 0x1000, 100
+        m.kv_indptr, m.kv_indices, m.kv_indices_len = 0x2000, 0x3000, 64
+        g = L.PrefixGroups(2, 2, 64, 0x4000, 0x5000)
+        ws = C.c_size_t()
+        assert lib.paged_decode_cascade_workspace_bytes(h, 4, 8, 100, C.byref(g), C.byref(ws)) == 0 and ws.value > 0
+        assert lib.paged_decode_cascade_workspace_bytes(hf, 4, 4, 100, C.byref(g), C.byref(ws)) == L.PKV_EUNSUPPORTED
+        assert lib.paged_decode_cascade_workspace_bytes(h, 4, 8, 100, None, C.byref(ws)) == L.PKV_EINVAL
+        bad = L.PrefixGroups(2, 2, 64, None, 0x5000)
+        assert lib.paged_decode_cascade_workspace_bytes(h, 4, 8, 100, C.byref(bad), C.byref(ws)) == L.PKV_EINVAL
+        neg = L.PrefixGroups(-1, 2, 64, 0x4000, 0x5000)
+        assert lib.paged_decode_cascade_workspace_bytes(h, 4, 8, 100, C.byref(neg), C.byref(ws)) == L.PKV_EINVAL
+        call = lambda ws_ptr, n, scale=0.1: lib.paged_decode_attn_cascade(h, 0, 0x6000, 8, C.byref(m), C.byref(g),
+                                                                         scale, 0x7000, None, ws_ptr, n, None)
+        assert call(0x8000, ws.value - 1) == L.PKV_ECAPACITY
+        assert call(0x8004, ws.value) == L.PKV_EALIGN
+        assert call(0x8000, ws.value, scale=float("nan")) == L.PKV_EINVAL
+        assert lib.paged_decode_attn_cascade(h, 0, 0x6000, 34, C.byref(m), C.byref(g), 0.1, 0x7000, None, 0x8000,
+                                             ws.value, None) == L.PKV_EUNSUPPORTED  # 17 query heads per KV head
+        m.bs = 0
+        assert call(None, 0) == 0
+    finally:
+        lib.kv_pool_destroy(h)
+        lib.kv_pool_destroy(hf)
