@@ -748,6 +748,8 @@ def main():
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="after the timed steps, time the kernel this many more times with the caches "
                          "cleared (a 1 GiB read) before each step; reported as roofline.kernel_ms_cold")
+    ap.add_argument("--no-attainable", action="store_true",
+                    help="skip the plain 1 GiB device copy that reports roofline.attainable_copy_gbs")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run a plain 256 MiB device copy three times (a known-size reference "
                          "for HBM byte counters)")
@@ -798,7 +800,8 @@ def main():
                  "kernel_bytes": b.kernel_bytes(), "kernel_gbs": round(kern_gbs, 2),
                  "kernel_hbm_frac": round(kern_gbs / HBM_PEAK_GBS, 4), "kernel_tflops": round(kern_tf, 3),
                  "kernel_mfma_frac": round(kern_tf / BF16_PEAK_TFLOPS, 4),
-                 "flop_per_byte": round(intensity, 2)})
+                 "flop_per_byte": round(intensity, 2),
+                 "kernel_ms_p10_p50_p90": [round(float(x), 5) for x in np.percentile(kern_ms, [10, 50, 90])]})
     if b.attn_calls > 1:
         roof["call_ms"] = [round(float(np.mean([c[k] for c in call_ms])), 5) for k in range(b.attn_calls)]
     if b.kernel_bytes(logical=True) != b.kernel_bytes():
@@ -844,6 +847,28 @@ def main():
         b.tokens_label: round(b.tokens_per_step() / (ms_step * 1e-3), 1),
         "roofline": roof,
     }
+    if not args.no_attainable and not args.calibrate_copy:
+        # the attainable HBM rate on this machine: a plain 1 GiB device-to-device
+        # copy (read + write bytes over its event time), beside the 8 TB/s peak
+        # (left out of counter runs, whose known-size copy must stay the largest)
+        a_src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        a_dst = torch.empty_like(a_src)
+        a_dst.copy_(a_src)
+        e0, e1 = ev.create(), ev.create()
+        hip_rec = ev.hip.hipEventRecord
+        hip_rec.argtypes = [C.c_void_p, C.c_void_p]
+        cur = torch.cuda.current_stream().cuda_stream
+        hip_rec(C.c_void_p(e0), C.c_void_p(cur))
+        for _ in range(5):
+            a_dst.copy_(a_src)
+        hip_rec(C.c_void_p(e1), C.c_void_p(cur))
+        copy_ms = ev.elapsed_ms(e0, e1) / 5
+        ev.destroy(e0)
+        ev.destroy(e1)
+        del a_src, a_dst
+        roof["attainable_copy_gbs"] = round(2 * (1 << 30) / (copy_ms * 1e-3) / 1e9, 1)
+        if roof["unit"] == "GB/s":
+            roof["frac_of_attainable_copy"] = round(kern_gbs / roof["attainable_copy_gbs"], 4)
     if args.calibrate_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
