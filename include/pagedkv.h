@@ -224,7 +224,8 @@ int paged_decode_workspace_bytes(const pkv_pool* pool, int32_t bs, int32_t num_q
  *   map->fmt: TOKEN_TABLE, CSR or BLOCK_TABLE.
  * Supported: SPLIT_KV f32 or bf16 with head_dim 64 or 128 and
  * num_q_heads/num_kv_heads <= 16; LATENT bf16 with head_dim_qk 576,
- * head_dim_v 512, one KV head and num_q_heads a multiple of 16. */
+ * head_dim_v 512, one KV head and num_q_heads in {16, 32, 64} or a multiple
+ * of 128 up to 1024 (more than 128 heads run as slices of 128). */
 int paged_decode_attn(const pkv_pool* pool, int32_t layer, const void* q, int32_t num_q_heads,
                       const pkv_kv_map* map, float sm_scale, void* out, float* lse, void* workspace,
                       size_t ws_bytes, void* stream);
@@ -244,7 +245,9 @@ int paged_decode_attn(const pkv_pool* pool, int32_t layer, const void* q, int32_
  *   workspace: device, >= paged_decode_workspace_bytes(pool, bs,
  *     num_draft * num_q_heads, max_kv_len), 256-byte aligned.
  * Supported: LATENT bf16 576/512 pools with num_draft * num_q_heads in
- * {16, 32, 64, 128} (else PKV_EUNSUPPORTED); sm_scale positive and finite. */
+ * {16, 32, 64} or a multiple of 128 up to 1024 (else PKV_EUNSUPPORTED);
+ * sm_scale positive and finite.  More than 128 rows run as slices of 128
+ * rows, one after another on the stream, sharing the workspace. */
 int paged_verify_attn(const pkv_pool* pool, int32_t layer, const void* q, int32_t num_q_heads, int32_t num_draft,
                       const pkv_kv_map* map, float sm_scale, void* out, float* lse, void* workspace, size_t ws_bytes,
                       void* stream);

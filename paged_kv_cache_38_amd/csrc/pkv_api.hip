@@ -381,10 +381,10 @@ int paged_verify_attn(const pkv_pool* pool, int32_t layer, const void* q, int32_
   if (num_q_heads <= 0 || num_draft <= 0) return fail(PKV_EINVAL, "num_q_heads and num_draft must be positive");
   if (!(sm_scale > 0.0f) || std::isinf(sm_scale)) return fail(PKV_EINVAL, "sm_scale must be positive and finite");
   const int64_t rows = (int64_t)num_q_heads * num_draft;
-  if (pool->desc.kind != PKV_KIND_LATENT || rows > 128 || !pkv::decode_supported(pool->info, (int32_t)rows))
+  if (pool->desc.kind != PKV_KIND_LATENT || rows > 1024 || !pkv::decode_supported(pool->info, (int32_t)rows))
     return fail(PKV_EUNSUPPORTED,
-                "target verification needs a latent bf16 576/512 pool and num_draft * num_q_heads in {16, 32, 64, "
-                "128} (got %d x %d)", num_draft, num_q_heads);
+                "target verification needs a latent bf16 576/512 pool and num_draft * num_q_heads in {16, 32, 64} "
+                "or a multiple of 128 up to 1024 (got %d x %d)", num_draft, num_q_heads);
   if (map->bs == 0) return ok();
   if (!q || !out) return fail(PKV_EINVAL, "null q or out");
   if (!aligned16(q)) return fail(PKV_EALIGN, "q must be 16-byte aligned");

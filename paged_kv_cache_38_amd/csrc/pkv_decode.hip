@@ -936,7 +936,9 @@ size_t decode_ws_layout(const PoolInfo& p, const DecodePlan& plan, int32_t bs, i
 }
 
 size_t decode_workspace_bytes(const PoolInfo& p, const DecodePlan& plan, int32_t bs, int32_t Hq) {
-  if (plan.kind == DK_MLA || plan.kind == DK_STREAM)
+  if (plan.kind == DK_MLA)  // slices of rows reuse one workspace
+    return stream_ws_layout(bs, plan.chunk, plan.max_splits, mla_slice_rows(Hq), p.head_dim_v, nullptr, nullptr);
+  if (plan.kind == DK_STREAM)
     return stream_ws_layout(bs, plan.chunk, plan.max_splits, Hq, p.head_dim_v, nullptr, nullptr);
   return decode_ws_layout(p, plan, bs, Hq, nullptr, nullptr);
 }

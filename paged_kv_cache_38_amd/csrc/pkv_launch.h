@@ -86,6 +86,8 @@ struct DecodeWs {
 size_t decode_ws_layout(const PoolInfo& p, const DecodePlan& plan, int32_t bs, int32_t Hq, void* base, DecodeWs* w);
 
 bool mla_decode_supported(const PoolInfo& p, int32_t num_q_heads);
+// Rows one MLA main-kernel launch covers (more run as consecutive slices).
+int32_t mla_slice_rows(int32_t num_q_heads);
 // MLA plan: chunk = tiles (32 tokens) per request at most, max_splits = main
 // grid (one workgroup per CU)
 DecodePlan plan_mla_decode(const PoolInfo& p, int32_t bs, int32_t num_q_heads, int32_t max_kv_len);

@@ -61,6 +61,8 @@ constexpr int kMlaTailOff = kMlaT * kMlaMainBytes;  // 32768
 constexpr int kMlaMetaWords = kStreamMetaWords;   // per tile: 32 slot ids + 8 info words
 constexpr int kMlaBufs = 4;                       // LDS tile buffers: three tiles in flight during compute
 constexpr int kMlaMetaRing = 8;                   // per-wave ring of per-tile slot ids / info
+constexpr int kMlaSlice = 128;                    // rows (heads x drafts) of one main-kernel launch
+constexpr int kMlaMaxRows = 1024;                 // rows of one call, in slices of kMlaSlice
 constexpr float kMlaHeadroom = 64.0f;             // log2 units a score may exceed the reference by
 
 // Launch shape: W waves per workgroup, HB blocks of 16 query heads per wave
@@ -142,7 +144,7 @@ __global__ void __launch_bounds__(64 * W, 1) mla_decode_kernel(
     const char* kpool, const bf16* __restrict__ q, int32_t HQ, const int32_t* __restrict__ header,
     const int32_t* __restrict__ meta, float scale_log2, bf16* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ ws_o, float* __restrict__ ws_lse, int32_t* __restrict__ fallback,
-    const int32_t* __restrict__ kv_lens, int32_t n_draft, int32_t hq_base) {
+    const int32_t* __restrict__ kv_lens, int32_t n_draft, int32_t hq_base, int32_t row_stride, int32_t row_off) {
   constexpr int NI = MlaShape<HB, W>::NI, RPW = MlaShape<HB, W>::RPW;
   constexpr int NK = kMlaQK / 32;  // 18 k-steps of the score product
   constexpr int NC = kMlaV / 16;   // 32 column blocks of the output
@@ -211,7 +213,7 @@ __global__ void __launch_bounds__(64 * W, 1) mla_decode_kernel(
   int k_zone = 0;
   if constexpr (VERIFY) {
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb) jrow[hb] = (hw + hb * 16 + col) / hq_base;
+    for (int hb = 0; hb < HB; ++hb) jrow[hb] = (row_off + hw + hb * 16 + col) / hq_base;
   }
 
   // Per iteration r a wave issues meta(r + 6) then tile(r + 3); tile(r) is
@@ -254,7 +256,7 @@ __global__ void __launch_bounds__(64 * W, 1) mla_decode_kernel(
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
         const int h = hw + hb * 16 + col;
-        const bf16* qp = q + ((int64_t)i * HQ + h) * kMlaQK + grp * 8;
+        const bf16* qp = q + ((int64_t)i * row_stride + row_off + h) * kMlaQK + grp * 8;
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) qf[hb][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + kk * 32));
         l_part[hb] = 0.f;
@@ -392,7 +394,8 @@ __global__ void __launch_bounds__(64 * W, 1) mla_decode_kernel(
     if (seg_end) {
       const int b0 = P / Bt, b1 = (P + T - 1) / Bt;
       const bool direct = b0 == b1;
-      const int64_t row0 = (direct ? (int64_t)i * HQ : ((int64_t)run + i) * HQ) + hw;
+      // outputs: row row_off + h of request i; pieces: this launch's HQ rows
+      const int64_t row0 = (direct ? (int64_t)i * row_stride + row_off : ((int64_t)run + i) * HQ) + hw;
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
         float lt = l_part[hb] + shfl_xor(l_part[hb], 16);
@@ -476,11 +479,13 @@ __global__ void __launch_bounds__(256) mla_merge_kernel(int32_t bs, int32_t Hq, 
                                                         const bf16* __restrict__ q, const int32_t* __restrict__ meta,
                                                         const int32_t* __restrict__ kv_lens, float scale_log2,
                                                         bf16* __restrict__ out, float* __restrict__ lse,
-                                                        int32_t n_draft, int32_t hq_base) {
+                                                        int32_t n_draft, int32_t hq_base, int32_t row_stride,
+                                                        int32_t row_off) {
   const int lane = threadIdx.x & 63;
-  const int64_t idx = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (idx >= (int64_t)bs * Hq) return;
-  const int i = (int)(idx / Hq), h = (int)(idx % Hq);
+  const int64_t pid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (request, row of this launch)
+  if (pid >= (int64_t)bs * Hq) return;
+  const int i = (int)(pid / Hq), h = (int)(pid % Hq);
+  const int64_t idx = (int64_t)i * row_stride + row_off + h;  // output row
   bf16* op = out + idx * kMlaV + lane * 8;
   const int T = ntiles[i];
   if (T == 0) {
@@ -493,7 +498,7 @@ __global__ void __launch_bounds__(256) mla_merge_kernel(int32_t bs, int32_t Hq, 
   if (fallback[i]) {
     // keys this row sees (all of them for decode, where n_draft = 1 and
     // h < hq_base)
-    const int L = min(min(kv_lens[i], T * kMlaT), kv_lens[i] - n_draft + 1 + h / hq_base);
+    const int L = min(min(kv_lens[i], T * kMlaT), kv_lens[i] - n_draft + 1 + (row_off + h) / hq_base);
     if (L <= 0) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) op[e] = (bf16)0.0f;
@@ -539,8 +544,10 @@ __global__ void __launch_bounds__(256) mla_merge_kernel(int32_t bs, int32_t Hq, 
 // ---------------------------------------------------------------------------
 bool mla_decode_supported(const PoolInfo& p, int32_t Hq) {
   return p.kind == 1 && p.dtype == 1 && p.num_kv_heads == 1 && p.head_dim_qk == kMlaQK && p.head_dim_v == kMlaV &&
-         (Hq == 16 || Hq == 32 || Hq == 64 || Hq == 128);
+         (Hq == 16 || Hq == 32 || Hq == 64 || (Hq % kMlaSlice == 0 && Hq <= kMlaMaxRows));
 }
+
+int32_t mla_slice_rows(int32_t Hq) { return Hq < kMlaSlice ? Hq : kMlaSlice; }
 
 DecodePlan plan_mla_decode(const PoolInfo& p, int32_t bs, int32_t Hq, int32_t max_kv_len) {
   (void)p;
@@ -554,16 +561,17 @@ DecodePlan plan_mla_decode(const PoolInfo& p, int32_t bs, int32_t Hq, int32_t ma
 }
 
 template <int HB, int W>
-static void launch_mla_main(int32_t runs, int32_t Hq, hipStream_t s, const char* kp, const void* q, const StreamWs& w,
-                            float sl2, void* out, float* lse, const int32_t* kv_lens, int32_t n_draft) {
+static void launch_mla_main(int32_t runs, int32_t hs, hipStream_t s, const char* kp, const void* q,
+                            const StreamWs& w, float sl2, void* out, float* lse, const int32_t* kv_lens,
+                            int32_t n_draft, int32_t hq_base, int32_t rows, int32_t off) {
   if (n_draft > 1)
     hipLaunchKernelGGL((mla_decode_kernel<HB, W, true>), dim3(runs), dim3(64 * W), 0, s, kp,
-                       static_cast<const bf16*>(q), Hq, w.header, w.meta, sl2, static_cast<bf16*>(out), lse, w.o,
-                       w.lse, w.fallback, kv_lens, n_draft, Hq / n_draft);
+                       static_cast<const bf16*>(q), hs, w.header, w.meta, sl2, static_cast<bf16*>(out), lse, w.o,
+                       w.lse, w.fallback, kv_lens, n_draft, hq_base, rows, off);
   else
     hipLaunchKernelGGL((mla_decode_kernel<HB, W, false>), dim3(runs), dim3(64 * W), 0, s, kp,
-                       static_cast<const bf16*>(q), Hq, w.header, w.meta, sl2, static_cast<bf16*>(out), lse, w.o,
-                       w.lse, w.fallback, kv_lens, 1, Hq);
+                       static_cast<const bf16*>(q), hs, w.header, w.meta, sl2, static_cast<bf16*>(out), lse, w.o,
+                       w.lse, w.fallback, kv_lens, 1, hq_base, rows, off);
 }
 
 hipError_t launch_mla_decode(const PoolInfo& p, int32_t layer, const void* q, int32_t Hq, const DevMap& m, int32_t bs,
@@ -571,28 +579,40 @@ hipError_t launch_mla_decode(const PoolInfo& p, int32_t layer, const void* q, in
   return launch_mla_verify(p, layer, q, Hq, 1, m, bs, plan, sl2, out, lse, ws, s);
 }
 
+// More than kMlaSlice rows (many heads, or heads times drafts) run as
+// consecutive slices of kMlaSlice rows: one plan, then the main kernel and the
+// merge per slice, each reading and writing its rows of the full row list and
+// reusing the one workspace in stream order.  A request that one slice sends
+// to the exact fallback keeps the flag for the later slices, which is exact
+// too.
 hipError_t launch_mla_verify(const PoolInfo& p, int32_t layer, const void* q, int32_t Hq, int32_t n_draft,
                              const DevMap& m, int32_t bs, const DecodePlan& plan, float sl2, void* out, float* lse,
                              void* ws, hipStream_t s) {
+  const int32_t hs = mla_slice_rows(Hq);
   StreamWs w;
-  stream_ws_layout(bs, plan.chunk, plan.max_splits, Hq, kMlaV, ws, &w);
+  stream_ws_layout(bs, plan.chunk, plan.max_splits, hs, kMlaV, ws, &w);
   const int32_t runs = plan.max_splits;
   hipError_t e = launch_stream_plan(m, bs, plan.chunk, runs, w, s);
   if (e != hipSuccess) return e;
   const char* kp = p.k_layer(layer);
-  timer_before(s);
-  if (Hq == 128) launch_mla_main<2, 4>(runs, Hq, s, kp, q, w, sl2, out, lse, m.kv_lens, n_draft);
-  else if (Hq == 64) launch_mla_main<1, 4>(runs, Hq, s, kp, q, w, sl2, out, lse, m.kv_lens, n_draft);
-  else if (Hq == 32) launch_mla_main<1, 2>(runs, Hq, s, kp, q, w, sl2, out, lse, m.kv_lens, n_draft);
-  else launch_mla_main<1, 1>(runs, Hq, s, kp, q, w, sl2, out, lse, m.kv_lens, n_draft);
-  e = hipGetLastError();
-  timer_after(s);
-  if (e != hipSuccess) return e;
-  const unsigned mblocks = (unsigned)(((int64_t)bs * Hq + 3) / 4);
-  hipLaunchKernelGGL(mla_merge_kernel, dim3(mblocks), dim3(256), 0, s, bs, Hq, w.header, w.prefix, w.ntiles,
-                     w.fallback, w.o, w.lse, kp, static_cast<const bf16*>(q), w.meta, m.kv_lens, sl2,
-                     static_cast<bf16*>(out), lse, n_draft, Hq / n_draft);
-  return hipGetLastError();
+  const int32_t hq_base = Hq / n_draft;
+  const unsigned mblocks = (unsigned)(((int64_t)bs * hs + 3) / 4);
+  for (int32_t off = 0; off < Hq; off += hs) {
+    timer_before(s);
+    if (hs == 128) launch_mla_main<2, 4>(runs, hs, s, kp, q, w, sl2, out, lse, m.kv_lens, n_draft, hq_base, Hq, off);
+    else if (hs == 64) launch_mla_main<1, 4>(runs, hs, s, kp, q, w, sl2, out, lse, m.kv_lens, n_draft, hq_base, Hq, off);
+    else if (hs == 32) launch_mla_main<1, 2>(runs, hs, s, kp, q, w, sl2, out, lse, m.kv_lens, n_draft, hq_base, Hq, off);
+    else launch_mla_main<1, 1>(runs, hs, s, kp, q, w, sl2, out, lse, m.kv_lens, n_draft, hq_base, Hq, off);
+    e = hipGetLastError();
+    timer_after(s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(mla_merge_kernel, dim3(mblocks), dim3(256), 0, s, bs, hs, w.header, w.prefix, w.ntiles,
+                       w.fallback, w.o, w.lse, kp, static_cast<const bf16*>(q), w.meta, m.kv_lens, sl2,
+                       static_cast<bf16*>(out), lse, n_draft, hq_base, Hq, off);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace pkv

@@ -250,6 +250,9 @@ def test_verify_arguments_checked_before_launch(lib):
         assert call(h, 16, 2, scale=0.0) == L.PKV_EINVAL
         assert call(h, 16, 9) == L.PKV_EUNSUPPORTED      # 144 rows
         assert call(h, 24, 2) == L.PKV_EUNSUPPORTED      # 48 rows
+        assert call(h, 128, 16) == L.PKV_EUNSUPPORTED    # 2048 rows
+        assert call(h, 128, 4) == L.PKV_ECAPACITY        # 512 rows (four slices) pass the shape check
+        assert call(h, 16, 8) == L.PKV_ECAPACITY         # 128 rows
         assert call(hs, 16, 2) == L.PKV_EUNSUPPORTED     # not a latent pool
         assert call(h, 16, 2) == L.PKV_ECAPACITY         # no workspace
         m.bs = 0

@@ -115,7 +115,7 @@ def run_verify(dc, fmt, n):
     return out.view(c.bs * n, g.num_q_heads, g.head_dim_v), lse.view(c.bs * n, g.num_q_heads)
 
 
-@pytest.mark.parametrize("heads,n", [(16, 2), (16, 8), (32, 4), (64, 2), (16, 4)])
+@pytest.mark.parametrize("heads,n", [(16, 2), (16, 8), (32, 4), (64, 2), (16, 4), (128, 2), (64, 4), (32, 12)])
 @pytest.mark.parametrize("fmt", FMTS)
 def test_mla_verify_matches_oracle(heads, n, fmt):
     """Short and long requests (pieces cut across runs, drafts straddling a
@@ -135,12 +135,15 @@ def test_mla_verify_matches_oracle(heads, n, fmt):
     assert_lse_close(lse, ref_l, "bf16", f"verify {heads}x{n} fmt {fmt}")
 
 
-def test_mla_verify_planted_key_goes_through_the_exact_fallback():
+@pytest.mark.parametrize("heads,n", [(16, 4), (128, 2)])
+def test_mla_verify_planted_key_goes_through_the_exact_fallback(heads, n):
     """A key far along the queries' direction at the last draft's own
     position: only the last draft sees it (its score outruns the fixed
     softmax reference, so the request is recomputed exactly), the earlier
-    drafts must not."""
-    n, heads = 4, 16
+    drafts must not.  At 128 heads x 2 drafts the last draft is the second
+    slice of 128 rows: the first slice finishes normally, the second takes
+    the fallback."""
+    print(f"mla verify planted key heads {heads} drafts {n}", flush=True)
     case = W.mla_decode(seed=9, bs=3, len_range=(300, 900), num_q_heads=heads, num_draft=n)
     vals = W.make_values(case)
     i = 1
@@ -158,6 +161,19 @@ def test_mla_verify_planted_key_goes_through_the_exact_fallback():
     assert_attn_close(out, ref_o, "bf16", "verify planted key")
     assert_lse_close(lse, ref_l, "bf16", "verify planted key")
     assert np.isfinite(ref_l[i * n + n - 1]).all() and ref_l[i * n + n - 1, 0] > ref_l[i * n, 0] + 50
+
+
+def test_mla_decode_256_heads_in_two_slices():
+    """256 query heads: two slices of 128 rows over one plan and workspace."""
+    case = W.mla_decode(seed=12, bs=5, len_range=(1, 2000), num_q_heads=256)
+    print("mla decode 256 heads", flush=True)
+    vals = W.make_values(case, canary=True)
+    dc = DeviceCase(case, vals)
+    dc.store()
+    out, lse = dc.decode(P.PKV_MAP_BLOCK_TABLE)
+    ref_o, ref_l = oracle_region(case, vals, "self")
+    assert_attn_close(out, ref_o, "bf16", "mla 256 heads")
+    assert_lse_close(lse, ref_l, "bf16", "mla 256 heads")
 
 
 def test_mla_verify_with_one_draft_equals_decode_bitwise():
