@@ -749,7 +749,8 @@ def main():
                     help="after the timed steps, time the kernel this many more times with the caches "
                          "cleared (a 1 GiB read) before each step; reported as roofline.kernel_ms_cold")
     ap.add_argument("--no-attainable", action="store_true",
-                    help="skip the plain 1 GiB device copy that reports roofline.attainable_copy_gbs")
+                    help="skip the plain 1 GiB device copy and the 8192^3 bf16 GEMM that report "
+                         "roofline.attainable_copy_gbs and roofline.attainable_gemm_tflops")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run a plain 256 MiB device copy three times (a known-size reference "
                          "for HBM byte counters)")
@@ -869,6 +870,25 @@ def main():
         roof["attainable_copy_gbs"] = round(2 * (1 << 30) / (copy_ms * 1e-3) / 1e9, 1)
         if roof["unit"] == "GB/s":
             roof["frac_of_attainable_copy"] = round(kern_gbs / roof["attainable_copy_gbs"], 4)
+        # the attainable bf16 MFMA rate: a plain 8192^3 bf16 GEMM from the
+        # vendor BLAS (contiguous 2-D operands), beside the 2.5 PFLOP/s peak
+        g_n = 8192
+        g_a = torch.randn(g_n, g_n, device="cuda").to(torch.bfloat16)
+        g_b = torch.randn(g_n, g_n, device="cuda").to(torch.bfloat16).contiguous()
+        g_c = torch.matmul(g_a, g_b)
+        for _ in range(3):
+            torch.matmul(g_a, g_b, out=g_c)
+        e0, e1 = ev.create(), ev.create()
+        hip_rec(C.c_void_p(e0), C.c_void_p(cur))
+        for _ in range(10):
+            torch.matmul(g_a, g_b, out=g_c)
+        hip_rec(C.c_void_p(e1), C.c_void_p(cur))
+        gemm_ms = ev.elapsed_ms(e0, e1) / 10
+        ev.destroy(e0)
+        ev.destroy(e1)
+        del g_a, g_b, g_c
+        roof["attainable_gemm_tflops"] = round(2 * g_n ** 3 / (gemm_ms * 1e-3) / 1e12, 1)
+        roof["frac_of_attainable_gemm"] = round(kern_tf / roof["attainable_gemm_tflops"], 4)
     if args.calibrate_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
