@@ -180,3 +180,18 @@ def run_extend(dc: "DeviceCase", name: str, fmt: int, contiguous: bool = False, 
                                causal_flags=flags, softcap=softcap)
     torch.cuda.synchronize()
     return out, lse
+
+
+def run_verify(dc: "DeviceCase", fmt: int, n: int):
+    """paged_verify_attn over the case's latent pool with n drafts per
+    request; out and lse flattened to one row per (request, draft)."""
+    c, g = dc.case, dc.case.geom
+    m = dc.kv_map("self", fmt)
+    q = dc.q["self"].view(c.bs, n, g.num_q_heads, g.head_dim_qk)
+    out = torch.full((c.bs, n, g.num_q_heads, g.head_dim_v), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((c.bs, n, g.num_q_heads), float("nan"), dtype=torch.float32, device="cuda")
+    nb = P.paged_decode_workspace_bytes(dc.pool, c.bs, n * g.num_q_heads, m.max_kv_len)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+    P.paged_verify_attn(dc.pool, 0, q, m, c.sm_scale, out, lse, ws)
+    torch.cuda.synchronize()
+    return out.view(c.bs * n, g.num_q_heads, g.head_dim_v), lse.view(c.bs * n, g.num_q_heads)

@@ -19,7 +19,7 @@ import workloads as W
 from workloads.cases import to_numpy_bits
 
 from gpu_util import DeviceCase, assert_attn_close, assert_lse_close, i32, oracle_after_store, oracle_region, \
-    run_extend
+    run_extend, run_verify
 
 pytestmark = pytest.mark.gpu
 
@@ -110,3 +110,43 @@ def test_extend_full_size(ragged):
         ref_o, ref_l = oracle_region(case, vals, name, pk, pv)
         assert_attn_close(out, ref_o, "bf16", f"extend {name}")
         assert_lse_close(lse, ref_l, "bf16", f"extend {name}")
+
+
+def test_verify_full_size():
+    """Target verification at its benchmark shape: bs 128, L ~ U{4096..16384}
+    including the drafts, 32 heads x 4 drafts folded into 128 rows, block
+    table; the oracle checks a seeded sample of requests, every draft."""
+    n = 4
+    case = W.mla_decode(seed=0, num_q_heads=32, num_draft=n)
+    print(f"full-size target verification: bs {case.bs}, sum L {int(case.regions['self'].kv_lens.sum())}",
+          flush=True)
+    vals = W.make_values(case, device="cuda")
+    dc = DeviceCase(case, vals)
+    dc.store()
+    out, lse = run_verify(dc, P.PKV_MAP_BLOCK_TABLE, n)
+    pk, pv = oracle_after_store(case, vals)
+    got = to_numpy_bits(dc.pool.flat("k", 0))[case.out_loc]  # the drafts' K rows, bit-exact
+    assert np.array_equal(got.view(np.uint8), pk[case.out_loc].view(np.uint8))
+    reqs = _sample(case, 16)
+    ref_o, ref_l = oracle_region(case, vals, "self", pk, pv, requests=reqs)
+    rows = np.asarray([i * n + j for i in reqs for j in range(n)])
+    assert_attn_close(out, ref_o, "bf16", "verify full size", rows=rows)
+    assert_lse_close(lse, ref_l, "bf16", "verify full size", rows=rows)
+
+
+@pytest.mark.parametrize("softcap", [0.0, 30.0])
+def test_mixed_spans_full_size(softcap):
+    """Mixed causal/full spans at their benchmark shape (4 rows of a
+    128-token causal span and a 2048-token full span, 32 / 8 heads, D 128,
+    CSR map, per-segment flags), every segment checked."""
+    case = W.mixed_spans(seed=0)
+    print(f"full-size mixed spans (softcap {softcap}): {case.bs} segments, sum n {int(case.q_lens.sum())}",
+          flush=True)
+    vals = W.make_values(case, device="cuda")
+    dc = DeviceCase(case, vals)
+    dc.store()
+    out, lse = run_extend(dc, "self", P.PKV_MAP_CSR, softcap=softcap)
+    pk, pv = oracle_after_store(case, vals)
+    ref_o, ref_l = oracle_region(case, vals, "self", pk, pv, softcap=softcap)
+    assert_attn_close(out, ref_o, "bf16", f"mixed spans full size, cap {softcap}")
+    assert_lse_close(lse, ref_l, "bf16", f"mixed spans full size, cap {softcap}")

@@ -7,7 +7,7 @@ import torch
 import paged_kv_cache_38_amd as P
 import workloads as W
 
-from gpu_util import DeviceCase, assert_attn_close, assert_lse_close, oracle_region
+from gpu_util import DeviceCase, assert_attn_close, assert_lse_close, oracle_region, run_verify
 
 pytestmark = pytest.mark.gpu
 
@@ -101,19 +101,6 @@ def test_mla_formats_agree_bitwise_and_repeat():
 # --------------------------------------------------------------------------
 # target verification: drafts folded into heads, bottom-right causal
 # --------------------------------------------------------------------------
-
-def run_verify(dc, fmt, n):
-    c, g = dc.case, dc.case.geom
-    m = dc.kv_map("self", fmt)
-    q = dc.q["self"].view(c.bs, n, g.num_q_heads, g.head_dim_qk)
-    out = torch.full((c.bs, n, g.num_q_heads, g.head_dim_v), float("nan"), dtype=torch.bfloat16, device="cuda")
-    lse = torch.full((c.bs, n, g.num_q_heads), float("nan"), dtype=torch.float32, device="cuda")
-    nb = P.paged_decode_workspace_bytes(dc.pool, c.bs, n * g.num_q_heads, m.max_kv_len)
-    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
-    P.paged_verify_attn(dc.pool, 0, q, m, c.sm_scale, out, lse, ws)
-    torch.cuda.synchronize()
-    return out.view(c.bs * n, g.num_q_heads, g.head_dim_v), lse.view(c.bs * n, g.num_q_heads)
-
 
 @pytest.mark.parametrize("heads,n", [(16, 2), (16, 8), (32, 4), (64, 2), (16, 4), (128, 2), (64, 4), (32, 12)])
 @pytest.mark.parametrize("fmt", FMTS)
