@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import paged_kv_cache_38_amd as P
-from workloads.alloc import growth_batch
+from workloads.alloc import growth_batch, serving_alloc
 
 pytestmark = pytest.mark.gpu
 
@@ -227,4 +227,38 @@ def test_serving_schedule_matches_oracle(page_size):
             del live[r]
         torch.cuda.synchronize()
         assert np.array_equal(dt.cpu().numpy(), table.astype(np.int32)), f"step {step}"
+        assert_ring_equal(fl, ring, f"step {step}")
+
+
+@pytest.mark.parametrize("decode", [True, False])
+def test_serving_alloc_full_size(decode):
+    """The allocator's benchmark steps at full size (decode: 4096 requests
+    each opening a page; extend: 64 requests growing by up to 2048 tokens;
+    a 65536-page pool), in bench.py's call sequence -- alloc, row write,
+    free of the same slots -- twice, so the second step starts from a ring
+    the first one advanced.  Slots, table, ring and status bit for bit."""
+    w = serving_alloc(decode)
+    bs = len(w.seq_lens)
+    print(f"full-size allocation step (decode={decode}): {bs} requests", flush=True)
+    fl = P.kv_free_list_create(w.page_size, w.num_pages, device=DEV)
+    ring = oracle.FreeRing(list(range(w.num_pages)), w.num_pages)
+    new = int((w.seq_lens - w.prefix_lens).sum())
+    out = torch.empty(new, dtype=torch.int32, device=DEV)
+    dt = torch.zeros((bs + 1, w.table_width), dtype=torch.int32, device=DEV)
+    table = np.zeros((bs + 1, w.table_width), np.int64)
+    last = np.full(bs, -1)
+    for step in range(2):
+        if decode:
+            P.kv_alloc_decode(fl, t32(w.seq_lens), t32(last), out)
+        else:
+            P.kv_alloc_extend(fl, t32(w.prefix_lens), t32(w.seq_lens), t32(last), out)
+        P.write_req_to_token(dt, t32(w.req_pool_indices), t32(w.prefix_lens), t32(w.seq_lens), out,
+                             int(w.seq_lens.max()))
+        P.kv_free(fl, out)
+        want = oracle.alloc_extend(ring, w.page_size, w.prefix_lens, w.seq_lens, last)
+        table = oracle.write_req_to_token(table, w.req_pool_indices, w.prefix_lens, w.seq_lens, want)
+        assert oracle.free_pages(ring, oracle.pages_of_slots(want, w.page_size))
+        assert status(fl) == P.PKV_ALLOC_OK, f"step {step}"
+        assert np.array_equal(out.cpu().numpy(), want.astype(np.int32)), f"step {step}: slots"
+        assert np.array_equal(dt.cpu().numpy(), table.astype(np.int32)), f"step {step}: table"
         assert_ring_equal(fl, ring, f"step {step}")
