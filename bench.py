@@ -846,6 +846,9 @@ def main():
         "config": cfg,
         "hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
         b.tokens_label: round(b.tokens_per_step() / (ms_step * 1e-3), 1),
+        # the same count over the timed kernel(s) alone (attention only for the
+        # decode and extend workloads: no append, planner or merge)
+        b.tokens_label + "_kernel_only": round(b.tokens_per_step() / (k_ms * 1e-3), 1),
         "roofline": roof,
     }
     if not args.no_attainable and not args.calibrate_copy:
