@@ -184,9 +184,14 @@ class DecodeBench:
                  for pl, L in zip(r.page_lists, r.kv_lens.tolist())]
         self.unique_tokens = int(np.unique(np.concatenate(slots)).size) if slots else 0
 
+    # the step's KV append rides in the decode call (its planner launch);
+    # --separate-append issues kv_store on its own first
+    fused_append = True
+
     def step(self, timers=None):
         P, c = self.P, self.case
-        if c.n_new:
+        fused = c.n_new and self.fused_append
+        if c.n_new and not fused:
             P.kv_store(self.pool, 0, self.k_new, self.v_new, self.out_loc)
         ps = c.geom.page_size
         if self.fmt == "csr":
@@ -197,7 +202,11 @@ class DecodeBench:
                                self.max_len, None, self.bt)
         if timers:
             P.pkv_set_kernel_timer(*timers[0])
-        P.paged_decode_attn(self.pool, 0, self.q, self.map, c.sm_scale, self.out, self.lse, self.ws)
+        if fused:
+            P.paged_decode_attn_append(self.pool, 0, self.q, self.map, self.k_new, self.v_new, self.out_loc,
+                                       c.sm_scale, self.out, self.lse, self.ws)
+        else:
+            P.paged_decode_attn(self.pool, 0, self.q, self.map, c.sm_scale, self.out, self.lse, self.ws)
 
     def kernel_bytes(self, logical: bool = False) -> int:
         """Decode kernel: the K/V rows of every distinct live slot once
@@ -748,6 +757,9 @@ def main():
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="after the timed steps, time the kernel this many more times with the caches "
                          "cleared (a 1 GiB read) before each step; reported as roofline.kernel_ms_cold")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="decode workloads: launch kv_store on its own before paged_decode_attn instead of "
+                         "passing the append to paged_decode_attn_append")
     ap.add_argument("--no-attainable", action="store_true",
                     help="skip the plain 1 GiB device copy and the 8192^3 bf16 GEMM that report "
                          "roofline.attainable_copy_gbs and roofline.attainable_gemm_tflops")
@@ -764,6 +776,11 @@ def main():
 
     torch.cuda.init()
     b, cfg = build_workload(args.workload)
+    if isinstance(b, DecodeBench) and b.case.n_new:
+        b.fused_append = not args.separate_append
+        if b.fused_append:
+            cfg["step"] = cfg["step"].replace("kv_store + ", "").replace(
+                "paged_decode_attn", "paged_decode_attn_append (the kv_store runs in its planner launch)")
     ev = HipEvents()
     for _ in range(args.warmup):
         b.step()

@@ -230,6 +230,23 @@ int paged_decode_attn(const pkv_pool* pool, int32_t layer, const void* q, int32_
                       const pkv_kv_map* map, float sm_scale, void* out, float* lse, void* workspace,
                       size_t ws_bytes, void* stream);
 
+/* paged_decode_attn with the step's KV append in the same call ([MINI]
+ * "The KV pool: one preallocated block of memory": the attention backend
+ * stores the step's new K/V by out_loc before it computes attention).  The
+ * result is that of kv_store(pool, layer, k_new, v_new, out_loc, n_new)
+ * followed by paged_decode_attn(...) on the same stream, bit for bit; the
+ * append runs inside the decode's planner launch (bf16 and latent pools),
+ * which reads only the tables, so a step launches one kernel fewer.
+ *   k_new, v_new, out_loc, n_new: as kv_store (v_new ignored for a latent
+ *     pool); n_new = 0 stores nothing.  map->kv_lens count the new tokens.
+ *   Other arguments and errors: as paged_decode_attn, and as kv_store for
+ *   the append's arguments (all checked before anything is launched).  With
+ *   map->bs = 0 only the append runs. */
+int paged_decode_attn_append(const pkv_pool* pool, int32_t layer, const void* q, int32_t num_q_heads,
+                             const pkv_kv_map* map, const void* k_new, const void* v_new, const int32_t* out_loc,
+                             int64_t n_new, float sm_scale, void* out, float* lse, void* workspace, size_t ws_bytes,
+                             void* stream);
+
 /* Target verification over a latent (MLA) pool ([BACKEND]
  * init_forward_metadata, the target-verify branch: the sequence lengths
  * include the draft tokens and the drafts multiply the head count).  Each

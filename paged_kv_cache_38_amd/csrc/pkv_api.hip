@@ -241,16 +241,30 @@ int64_t kv_pool_token_bytes(const pkv_pool* pool) {
   return pool->info.k_row_bytes + pool->info.v_row_bytes;
 }
 
+}  // extern "C"
+
+namespace {
+// Arguments of a KV append (kv_store, or the append a decode call carries);
+// a latent pool's v is dropped.
+int check_store(const pkv_pool* pool, const void* k, const void** v, const int32_t* out_loc, int64_t n) {
+  if (n < 0) return fail(PKV_EINVAL, "negative n");
+  if (n == 0) return PKV_OK;
+  if (!k || !out_loc) return fail(PKV_EINVAL, "null k or out_loc");
+  if (pool->desc.kind == PKV_KIND_SPLIT_KV && !*v) return fail(PKV_EINVAL, "null v for a split K/V pool");
+  if (pool->desc.kind == PKV_KIND_LATENT) *v = nullptr;
+  if (!aligned16(k) || !aligned16(*v)) return fail(PKV_EALIGN, "k/v must be 16-byte aligned");
+  return PKV_OK;
+}
+}  // namespace
+
+extern "C" {
+
 int kv_store(const pkv_pool* pool, int32_t layer, const void* k, const void* v, const int32_t* out_loc, int64_t n,
              void* stream) {
   if (int st = check_pool(pool)) return st;
   if (int st = check_layer(pool, layer)) return st;
-  if (n < 0) return fail(PKV_EINVAL, "negative n");
+  if (int st = check_store(pool, k, &v, out_loc, n)) return st;
   if (n == 0) return ok();
-  if (!k || !out_loc) return fail(PKV_EINVAL, "null k or out_loc");
-  if (pool->desc.kind == PKV_KIND_SPLIT_KV && !v) return fail(PKV_EINVAL, "null v for a split K/V pool");
-  if (pool->desc.kind == PKV_KIND_LATENT) v = nullptr;
-  if (!aligned16(k) || !aligned16(v)) return fail(PKV_EALIGN, "k/v must be 16-byte aligned");
   return device_status(pkv::launch_store(pool->info, layer, k, v, out_loc, n, (hipStream_t)stream), "kv_store");
 }
 
@@ -292,12 +306,16 @@ int paged_decode_workspace_bytes(const pkv_pool* pool, int32_t bs, int32_t num_q
   return ok();
 }
 
-int paged_decode_attn(const pkv_pool* pool, int32_t layer, const void* q, int32_t num_q_heads, const pkv_kv_map* map,
-                      float sm_scale, void* out, float* lse, void* workspace, size_t ws_bytes, void* stream) {
-  if (int st = check_pool(pool)) return st;
-  if (int st = check_layer(pool, layer)) return st;
+}  // extern "C"
+
+namespace {
+// paged_decode_attn with an optional KV append (st.n == 0: none), checked
+// before anything is launched.
+int decode_call(const pkv_pool* pool, int32_t layer, const void* q, int32_t num_q_heads, const pkv_kv_map* map,
+                float sm_scale, void* out, float* lse, void* workspace, size_t ws_bytes, void* stream,
+                const pkv::StoreArgs& st, const char* what) {
   pkv::DevMap dm;
-  if (int st = make_devmap(pool, map, false, &dm)) return st;
+  if (int e = make_devmap(pool, map, false, &dm)) return e;
   if (num_q_heads <= 0 || num_q_heads % pool->desc.num_kv_heads != 0)
     return fail(PKV_EINVAL, "num_q_heads %d not a positive multiple of num_kv_heads %d", num_q_heads,
                 pool->desc.num_kv_heads);
@@ -306,7 +324,10 @@ int paged_decode_attn(const pkv_pool* pool, int32_t layer, const void* q, int32_
                 pool->desc.dtype, pool->desc.head_dim_qk, pool->desc.head_dim_v, num_q_heads,
                 pool->desc.num_kv_heads);
   if (!(sm_scale > 0.0f) || std::isinf(sm_scale)) return fail(PKV_EINVAL, "sm_scale must be positive and finite");
-  if (map->bs == 0) return ok();
+  if (map->bs == 0) {
+    if (st.n == 0) return ok();
+    return device_status(pkv::launch_store_args(st, (hipStream_t)stream), what);
+  }
   if (!q || !out) return fail(PKV_EINVAL, "null q or out");
   if (!aligned16(q)) return fail(PKV_EALIGN, "q must be 16-byte aligned");
   const pkv::DecodePlan plan = pkv::plan_decode(pool->info, map->bs, num_q_heads, map->max_kv_len);
@@ -315,8 +336,32 @@ int paged_decode_attn(const pkv_pool* pool, int32_t layer, const void* q, int32_
   if (need > 0 && (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)))
     return fail(PKV_EALIGN, "workspace must be non-null and 256-byte aligned");
   return device_status(pkv::launch_decode(pool->info, layer, q, num_q_heads, dm, map->bs, plan, sm_scale, out, lse,
-                                          workspace, (hipStream_t)stream),
-                       "paged_decode_attn");
+                                          workspace, (hipStream_t)stream, st.n > 0 ? &st : nullptr),
+                       what);
+}
+}  // namespace
+
+extern "C" {
+
+int paged_decode_attn_append(const pkv_pool* pool, int32_t layer, const void* q, int32_t num_q_heads,
+                             const pkv_kv_map* map, const void* k_new, const void* v_new, const int32_t* out_loc,
+                             int64_t n_new, float sm_scale, void* out, float* lse, void* workspace, size_t ws_bytes,
+                             void* stream) {
+  if (int st = check_pool(pool)) return st;
+  if (int st = check_layer(pool, layer)) return st;
+  if (int st = check_store(pool, k_new, &v_new, out_loc, n_new)) return st;
+  const pkv::StoreArgs sa = pkv::make_store_args(pool->info, layer, k_new, v_new, out_loc, n_new);
+  return decode_call(pool, layer, q, num_q_heads, map, sm_scale, out, lse, workspace, ws_bytes, stream, sa,
+                     "paged_decode_attn_append");
+}
+
+int paged_decode_attn(const pkv_pool* pool, int32_t layer, const void* q, int32_t num_q_heads, const pkv_kv_map* map,
+                      float sm_scale, void* out, float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  if (int st = check_pool(pool)) return st;
+  if (int st = check_layer(pool, layer)) return st;
+  pkv::StoreArgs none{};
+  return decode_call(pool, layer, q, num_q_heads, map, sm_scale, out, lse, workspace, ws_bytes, stream, none,
+                     "paged_decode_attn");
 }
 
 namespace {

@@ -14,37 +14,35 @@ namespace pkv {
 // any attention reads the pool).
 // One wavefront per new token: lanes stride over the row's 16-byte units.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) store_rows_kernel(char* __restrict__ k_dst, char* __restrict__ v_dst,
-                                                         const char* __restrict__ k_src,
-                                                         const char* __restrict__ v_src,
-                                                         const int32_t* __restrict__ out_loc, int64_t n,
-                                                         int64_t num_slots, int32_t k_units, int32_t v_units) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= n) return;
-  const int64_t slot = out_loc[row];
-  if (slot < 0 || slot >= num_slots) return;  // out-of-range slot: skipped
-  {
-    const u32x4* src = reinterpret_cast<const u32x4*>(k_src) + row * k_units;
-    u32x4* dst = reinterpret_cast<u32x4*>(k_dst) + slot * k_units;
-    for (int c = lane; c < k_units; c += 64) dst[c] = src[c];
-  }
-  if (v_dst) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(v_src) + row * v_units;
-    u32x4* dst = reinterpret_cast<u32x4*>(v_dst) + slot * v_units;
-    for (int c = lane; c < v_units; c += 64) dst[c] = src[c];
-  }
+__global__ void __launch_bounds__(256) store_rows_kernel(StoreArgs a) {
+  store_one_row(a, (int64_t)blockIdx.x * kStoreRowsPerBlock + (threadIdx.x >> 6), threadIdx.x & 63);
+}
+
+StoreArgs make_store_args(const PoolInfo& p, int32_t layer, const void* k, const void* v, const int32_t* out_loc,
+                          int64_t n) {
+  StoreArgs a;
+  a.k_dst = const_cast<char*>(p.k_layer(layer));
+  a.v_dst = const_cast<char*>(p.v_layer(layer));
+  a.k_src = static_cast<const char*>(k);
+  a.v_src = static_cast<const char*>(v);
+  a.out_loc = out_loc;
+  a.n = n;
+  a.num_slots = p.num_slots;
+  a.k_units = (int32_t)(p.k_row_bytes / 16);
+  a.v_units = (int32_t)(p.v_row_bytes / 16);
+  return a;
+}
+
+hipError_t launch_store_args(const StoreArgs& a, hipStream_t s) {
+  if (a.n == 0) return hipSuccess;
+  const int64_t blocks = (a.n + kStoreRowsPerBlock - 1) / kStoreRowsPerBlock;
+  hipLaunchKernelGGL(store_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_store(const PoolInfo& p, int32_t layer, const void* k, const void* v, const int32_t* out_loc,
                         int64_t n, hipStream_t s) {
-  if (n == 0) return hipSuccess;
-  const int64_t blocks = (n + 3) / 4;
-  hipLaunchKernelGGL(store_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
-                     const_cast<char*>(p.k_layer(layer)), const_cast<char*>(p.v_layer(layer)),
-                     static_cast<const char*>(k), static_cast<const char*>(v), out_loc, n, p.num_slots,
-                     (int32_t)(p.k_row_bytes / 16), (int32_t)(p.v_row_bytes / 16));
-  return hipGetLastError();
+  return launch_store_args(make_store_args(p, layer, k, v, out_loc, n), s);
 }
 
 // ---------------------------------------------------------------------------

@@ -967,7 +967,7 @@ static void launch_stream_main(int32_t runs, int32_t hg, hipStream_t s, const Po
 
 static hipError_t launch_stream_decode(const PoolInfo& p, int32_t layer, const void* q, int32_t Hq, const DevMap& m,
                                        int32_t bs, const DecodePlan& plan, float sl2, void* out, float* lse, void* ws,
-                                       hipStream_t s) {
+                                       hipStream_t s, const StoreArgs* st) {
   const int Hkv = p.num_kv_heads;
   const int G = Hq / Hkv;
   const int W = (Hkv % 4 == 0) ? 4 : (Hkv % 2 == 0 ? 2 : 1);
@@ -976,7 +976,7 @@ static hipError_t launch_stream_decode(const PoolInfo& p, int32_t layer, const v
   if (runs % 8 != 0) return hipErrorInvalidValue;  // the block -> (run, head group) map needs whole XCD rounds
   StreamWs w;
   stream_ws_layout(bs, plan.chunk, runs, Hq, p.head_dim_v, ws, &w);
-  hipError_t e = launch_stream_plan(m, bs, plan.chunk, runs, w, s);
+  hipError_t e = launch_stream_plan(m, bs, plan.chunk, runs, w, s, nullptr, st);
   if (e != hipSuccess) return e;
   const int D = p.head_dim_qk;
   timer_before(s);
@@ -1111,10 +1111,19 @@ hipError_t launch_decode_cascade(const PoolInfo& p, int32_t layer, const void* q
 }
 
 hipError_t launch_decode(const PoolInfo& p, int32_t layer, const void* q, int32_t Hq, const DevMap& m, int32_t bs,
-                         const DecodePlan& plan, float sm_scale, void* out, float* lse, void* ws, hipStream_t s) {
-  if (bs == 0) return hipSuccess;
-  if (plan.kind == DK_MLA) return launch_mla_decode(p, layer, q, Hq, m, bs, plan, sm_scale * kLog2e, out, lse, ws, s);
-  if (plan.kind == DK_STREAM) return launch_stream_decode(p, layer, q, Hq, m, bs, plan, sm_scale * kLog2e, out, lse, ws, s);
+                         const DecodePlan& plan, float sm_scale, void* out, float* lse, void* ws, hipStream_t s,
+                         const StoreArgs* st) {
+  if (bs == 0) {  // nothing to attend: only the append, if any
+    return st && st->n > 0 ? launch_store_args(*st, s) : hipSuccess;
+  }
+  if (plan.kind == DK_MLA)
+    return launch_mla_decode(p, layer, q, Hq, m, bs, plan, sm_scale * kLog2e, out, lse, ws, s, st);
+  if (plan.kind == DK_STREAM)
+    return launch_stream_decode(p, layer, q, Hq, m, bs, plan, sm_scale * kLog2e, out, lse, ws, s, st);
+  if (st && st->n > 0) {  // the fp32 path has no planner launch to carry it
+    hipError_t e = launch_store_args(*st, s);
+    if (e != hipSuccess) return e;
+  }
   const int Hkv = p.num_kv_heads;
   const int G = Hq / Hkv;
   const int W = (Hkv % 4 == 0) ? 4 : (Hkv % 2 == 0 ? 2 : 1);

@@ -39,6 +39,42 @@ void timer_after(hipStream_t s);
 hipError_t launch_store(const PoolInfo& p, int32_t layer, const void* k, const void* v, const int32_t* out_loc,
                         int64_t n, hipStream_t s);
 
+// A KV append carried by another launch (the decode planner runs it in
+// blocks of its own: the planner reads only tables, so the two are
+// independent, and the attention kernel after them reads the stored rows).
+struct StoreArgs {
+  char* k_dst;
+  char* v_dst;  // null for a latent pool
+  const char* k_src;
+  const char* v_src;
+  const int32_t* out_loc;
+  int64_t n;  // rows; 0: nothing to store
+  int64_t num_slots;
+  int32_t k_units, v_units;  // 16-byte units per row
+};
+StoreArgs make_store_args(const PoolInfo& p, int32_t layer, const void* k, const void* v, const int32_t* out_loc,
+                          int64_t n);
+constexpr int kStoreRowsPerBlock = 4;  // one wavefront per row, 256-thread blocks
+hipError_t launch_store_args(const StoreArgs& a, hipStream_t s);  // the append on its own
+
+// Row `row` of a store, by one wavefront (lanes stride over its 16-byte
+// units); slots outside the pool are skipped.
+__device__ __forceinline__ void store_one_row(const StoreArgs& a, int64_t row, int lane) {
+  if (row >= a.n) return;
+  const int64_t slot = a.out_loc[row];
+  if (slot < 0 || slot >= a.num_slots) return;
+  {
+    const u32x4* src = reinterpret_cast<const u32x4*>(a.k_src) + row * a.k_units;
+    u32x4* dst = reinterpret_cast<u32x4*>(a.k_dst) + slot * a.k_units;
+    for (int c = lane; c < a.k_units; c += 64) dst[c] = src[c];
+  }
+  if (a.v_dst) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(a.v_src) + row * a.v_units;
+    u32x4* dst = reinterpret_cast<u32x4*>(a.v_dst) + slot * a.v_units;
+    for (int c = lane; c < a.v_units; c += 64) dst[c] = src[c];
+  }
+}
+
 hipError_t launch_gather(const PoolInfo& p, int32_t layer, const DevMap& m, int32_t bs, int32_t max_kv_len,
                          const int32_t* cu_seqlens_k, void* k_out, void* v_out, int64_t out_rows, hipStream_t s);
 
@@ -110,24 +146,27 @@ size_t stream_ws_layout(int32_t bs, int32_t max_tiles, int32_t runs, int32_t Hq,
                         StreamWs* w);
 // skip (nullable, device int32[bs]): keys left out at the start of each
 // request, a multiple of kStreamT (cascade decode reads them elsewhere).
+// st (nullable): a KV append run by extra blocks of the same launch.
 hipError_t launch_stream_plan(const DevMap& m, int32_t bs, int32_t max_tiles, int32_t runs, const StreamWs& w,
-                              hipStream_t s, const int32_t* skip = nullptr);
+                              hipStream_t s, const int32_t* skip = nullptr, const StoreArgs* st = nullptr);
 int32_t device_cu_count();
 hipError_t launch_mla_decode(const PoolInfo& p, int32_t layer, const void* q, int32_t num_q_heads, const DevMap& m,
                              int32_t bs, const DecodePlan& plan, float scale_log2, void* out, float* lse, void* ws,
-                             hipStream_t s);
+                             hipStream_t s, const StoreArgs* st = nullptr);
 // Target verification over a latent pool: n_draft query tokens per request,
 // folded into Hq = n_draft * heads rows, bottom-right causal among the drafts.
 hipError_t launch_mla_verify(const PoolInfo& p, int32_t layer, const void* q, int32_t Hq, int32_t n_draft,
                              const DevMap& m, int32_t bs, const DecodePlan& plan, float sl2, void* out, float* lse,
-                             void* ws, hipStream_t s);
+                             void* ws, hipStream_t s, const StoreArgs* st = nullptr);
 DecodePlan plan_decode(const PoolInfo& p, int32_t bs, int32_t num_q_heads, int32_t max_kv_len);
 size_t decode_workspace_bytes(const PoolInfo& p, const DecodePlan& plan, int32_t bs, int32_t num_q_heads);
 bool decode_supported(const PoolInfo& p, int32_t num_q_heads);
 
+// st (nullable): the step's KV append, stored before the attention reads
+// the pool (inside the planner launch where there is one).
 hipError_t launch_decode(const PoolInfo& p, int32_t layer, const void* q, int32_t num_q_heads, const DevMap& m,
                          int32_t bs, const DecodePlan& plan, float sm_scale, void* out, float* lse, void* ws,
-                         hipStream_t s);
+                         hipStream_t s, const StoreArgs* st = nullptr);
 
 // Cascade decode over shared prefixes (pkv_decode.hip): the stream decode of
 // each request's own keys plus one pass per group over the shared ones.

@@ -575,8 +575,9 @@ static void launch_mla_main(int32_t runs, int32_t hs, hipStream_t s, const char*
 }
 
 hipError_t launch_mla_decode(const PoolInfo& p, int32_t layer, const void* q, int32_t Hq, const DevMap& m, int32_t bs,
-                             const DecodePlan& plan, float sl2, void* out, float* lse, void* ws, hipStream_t s) {
-  return launch_mla_verify(p, layer, q, Hq, 1, m, bs, plan, sl2, out, lse, ws, s);
+                             const DecodePlan& plan, float sl2, void* out, float* lse, void* ws, hipStream_t s,
+                             const StoreArgs* st) {
+  return launch_mla_verify(p, layer, q, Hq, 1, m, bs, plan, sl2, out, lse, ws, s, st);
 }
 
 // More than kMlaSlice rows (many heads, or heads times drafts) run as
@@ -587,12 +588,12 @@ hipError_t launch_mla_decode(const PoolInfo& p, int32_t layer, const void* q, in
 // too.
 hipError_t launch_mla_verify(const PoolInfo& p, int32_t layer, const void* q, int32_t Hq, int32_t n_draft,
                              const DevMap& m, int32_t bs, const DecodePlan& plan, float sl2, void* out, float* lse,
-                             void* ws, hipStream_t s) {
+                             void* ws, hipStream_t s, const StoreArgs* st) {
   const int32_t hs = mla_slice_rows(Hq);
   StreamWs w;
   stream_ws_layout(bs, plan.chunk, plan.max_splits, hs, kMlaV, ws, &w);
   const int32_t runs = plan.max_splits;
-  hipError_t e = launch_stream_plan(m, bs, plan.chunk, runs, w, s);
+  hipError_t e = launch_stream_plan(m, bs, plan.chunk, runs, w, s, nullptr, st);
   if (e != hipSuccess) return e;
   const char* kp = p.k_layer(layer);
   const int32_t hq_base = Hq / n_draft;

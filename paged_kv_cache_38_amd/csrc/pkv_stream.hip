@@ -47,10 +47,14 @@ __global__ void __launch_bounds__(256) stream_plan_kernel(DevMap m, int32_t bs, 
                                                        int32_t* __restrict__ header,
                                                        int32_t* __restrict__ prefix, int32_t* __restrict__ ntiles,
                                                        int32_t* __restrict__ fallback, int32_t* __restrict__ meta,
-                                                       const int32_t* __restrict__ skip) {
+                                                       const int32_t* __restrict__ skip, StoreArgs app) {
   __shared__ int32_t red[2][4];
   const int i = blockIdx.x, c = blockIdx.y;
   const int tid = threadIdx.x;
+  if (i >= bs) {  // blocks past the batch carry the step's KV append
+    if (c == 0) store_one_row(app, (int64_t)(i - bs) * kStoreRowsPerBlock + (tid >> 6), tid & 63);
+    return;
+  }
   const int32_t T_all = min(stream_tiles(m.kv_lens[i]), max_tiles);
   const int32_t st = skip_tiles(skip, i, T_all);  // tiles left out at the start
   const int32_t T = T_all - st;
@@ -139,14 +143,17 @@ size_t stream_ws_layout(int32_t bs, int32_t max_tiles, int32_t runs, int32_t Hq,
 }
 
 hipError_t launch_stream_plan(const DevMap& m, int32_t bs, int32_t max_tiles, int32_t runs, const StreamWs& w,
-                              hipStream_t s, const int32_t* skip) {
-  const dim3 grid((unsigned)bs, (unsigned)std::max(1, (max_tiles + kPlanTiles - 1) / kPlanTiles));
+                              hipStream_t s, const int32_t* skip, const StoreArgs* st) {
+  StoreArgs a{};
+  if (st) a = *st;
+  const int64_t store_blocks = (a.n + kStoreRowsPerBlock - 1) / kStoreRowsPerBlock;
+  const dim3 grid((unsigned)(bs + store_blocks), (unsigned)std::max(1, (max_tiles + kPlanTiles - 1) / kPlanTiles));
   if (m.fmt == MAP_TOKEN_TABLE)
     hipLaunchKernelGGL(stream_plan_kernel<SLOT_TABLE>, grid, dim3(256), 0, s, m, bs, max_tiles, runs, w.header,
-                       w.prefix, w.ntiles, w.fallback, w.meta, skip);
+                       w.prefix, w.ntiles, w.fallback, w.meta, skip, a);
   else
     hipLaunchKernelGGL(stream_plan_kernel<SLOT_PAGES>, grid, dim3(256), 0, s, m, bs, max_tiles, runs, w.header,
-                       w.prefix, w.ntiles, w.fallback, w.meta, skip);
+                       w.prefix, w.ntiles, w.fallback, w.meta, skip, a);
   return hipGetLastError();
 }
 

@@ -234,6 +234,36 @@ def test_extend_options_checked_before_launch(lib):
         lib.kv_pool_destroy(h)
 
 
+def test_decode_append_arguments_checked_before_launch(lib):
+    st, h = make_pool(lib, desc(dtype=1))
+    assert st == 0
+    try:
+        m = L.KVMapStruct()
+        m.fmt, m.bs, m.kv_lens, m.max_kv_len = L.PKV_MAP_TOKEN_TABLE, 4, 0x1000, 100
+        m.req_to_token, m.table_rows, m.table_width, m.req_pool_indices = 0x2000, 5, 128, 0x3000
+        hq = 2 * desc(dtype=1).num_kv_heads
+
+        def call(k=0x10000, v=0x20000, loc=0x30000, n=4, scale=0.1, ws=0):
+            return lib.paged_decode_attn_append(h, 0, 0x4000, hq, C.byref(m), k, v, loc, n, scale, 0x5000, None,
+                                                0x60000 if ws else None, ws, None)
+
+        assert call(n=-1) == L.PKV_EINVAL                 # append arguments first
+        assert call(k=None) == L.PKV_EINVAL
+        assert call(loc=None) == L.PKV_EINVAL
+        assert call(v=None) == L.PKV_EINVAL               # a split pool needs v
+        assert call(k=0x10008) == L.PKV_EALIGN
+        assert call(scale=0.0) == L.PKV_EINVAL            # then the decode's
+        assert call() == L.PKV_ECAPACITY                  # no workspace: nothing launched
+        assert lib.paged_decode_attn_append(h, 0, 0x4000, 3, C.byref(m), 0x10000, 0x20000, 0x30000, 4, 0.1,
+                                            0x5000, None, None, 0, None) == L.PKV_EINVAL  # 3 heads over 2
+        assert lib.paged_decode_attn_append(h, 7, 0x4000, hq, C.byref(m), 0x10000, 0x20000, 0x30000, 4, 0.1,
+                                            0x5000, None, None, 0, None) == L.PKV_EINVAL  # no layer 7
+        m.bs = 0
+        assert call(n=0) == 0                             # nothing to store, nothing to attend
+    finally:
+        lib.kv_pool_destroy(h)
+
+
 def test_verify_arguments_checked_before_launch(lib):
     st, h = make_pool(lib, desc(dtype=1, kind=1, num_kv_heads=1, head_dim_qk=576, head_dim_v=512, page_size=64),
                       v=None)  # a latent pool takes no V buffer

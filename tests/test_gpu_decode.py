@@ -276,3 +276,73 @@ def test_decode_empty_request_gives_zero_and_minus_inf():
         ref_o, ref_l = oracle_region(case, vals, "self", requests=[0, 2, 3, 5])
         rows = [0, 2, 3, 5]
         assert_attn_close(out, ref_o, "bf16", "empty-mixed", rows=rows)
+
+
+# ---------------------------------------------------------------------------
+# decode with the step's append in the same call
+# ---------------------------------------------------------------------------
+
+APPEND_CASES = {
+    "tiny_f32": lambda: W.tiny_decode(seed=3),                      # fp32: separate store launch
+    "tiny_f32_padded": lambda: W.tiny_decode(seed=3, padded=True),  # dummy rows on the padding page
+    "qwen3_small": lambda: small_cases()["qwen3_small"](3),
+    "gqa_ps64_small": lambda: small_cases()["gqa_ps64_small"](3),
+    "many_short": lambda: STREAM_SHAPES["many_short"](3),           # 1500 rows: 375 extra planner blocks
+    "mla_small": lambda: W.mla_decode(seed=3, bs=6, len_range=(1, 900)),
+}
+
+
+def _bits(t):
+    return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("name", list(APPEND_CASES))
+def test_decode_append_equals_store_then_decode_bitwise(name, fmt):
+    """paged_decode_attn_append gives the bits of kv_store followed by
+    paged_decode_attn: outputs, lse and the whole pool."""
+    case = APPEND_CASES[name]()
+    g = case.geom
+    print(f"decode append {name} fmt {fmt}: bs {case.bs}, {len(case.out_loc)} new rows", flush=True)
+    vals = W.make_values(case, canary=True)
+    a = DeviceCase(case, vals)
+    a.store()
+    oa, la = a.decode(fmt)
+    b = DeviceCase(case, vals)
+    m = b.kv_map("self", fmt)
+    out = torch.full_like(oa, float("nan"))
+    lse = torch.full_like(la, float("nan"))
+    nb = P.paged_decode_workspace_bytes(b.pool, case.bs, g.num_q_heads, m.max_kv_len)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+    P.paged_decode_attn_append(b.pool, 0, b.q["self"], m, b.k_new, b.v_new, b.out_loc, case.sm_scale, out, lse, ws)
+    torch.cuda.synchronize()
+    # dummy requests all write the padding page, in no defined order, and
+    # read it back: compare real rows and real pages bit for bit
+    real = ~case.dummy if case.dummy.size else np.ones(case.bs, bool)
+    rt = torch.from_numpy(real).to("cuda")
+    assert torch.equal(_bits(out)[rt], _bits(oa)[rt]) and torch.equal(_bits(lse)[rt], _bits(la)[rt])
+    real_slots = g.num_pages * g.page_size
+    assert torch.equal(_bits(b.pool.flat("k", 0))[:real_slots], _bits(a.pool.flat("k", 0))[:real_slots])
+    if not g.latent:
+        assert torch.equal(_bits(b.pool.flat("v", 0))[:real_slots], _bits(a.pool.flat("v", 0))[:real_slots])
+    ref_o, ref_l = oracle_region(case, vals, "self")
+    assert_attn_close(out, ref_o, g.dtype, f"append {name}", rows=real)
+    assert_lse_close(lse, ref_l, g.dtype, f"append {name}", rows=real)
+
+
+def test_decode_append_with_empty_batch_only_stores():
+    case = small_cases()["qwen3_small"](4)
+    vals = W.make_values(case)
+    a = DeviceCase(case, vals)
+    a.store()
+    b = DeviceCase(case, vals)
+    empty = torch.empty(0, dtype=torch.int32, device="cuda")
+    m = P.make_kv_map(P.PKV_MAP_TOKEN_TABLE, empty, 0, req_to_token=b.req_to_token, req_pool_indices=empty,
+                      kv_start=empty)
+    g = case.geom
+    q = torch.empty((0, g.num_q_heads, g.head_dim_qk), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((0, g.num_q_heads, g.head_dim_v), dtype=torch.bfloat16, device="cuda")
+    P.paged_decode_attn_append(b.pool, 0, q, m, b.k_new, b.v_new, b.out_loc, case.sm_scale, out)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(b.pool.flat("k", 0)), _bits(a.pool.flat("k", 0)))
+    assert torch.equal(_bits(b.pool.flat("v", 0)), _bits(a.pool.flat("v", 0)))
