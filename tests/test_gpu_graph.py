@@ -40,8 +40,9 @@ def check_replays(g, outputs, refs, reset, eager):
         torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("append", [False, True])
 @pytest.mark.parametrize("name", ["qwen3_small", "mla_small"])
-def test_decode_step_replays_bitwise(name):
+def test_decode_step_replays_bitwise(name, append):
     case = W.qwen3_decode(seed=1, bs=16) if name == "qwen3_small" else W.mla_decode(seed=1, bs=8, len_range=(100, 900))
     vals = W.make_values(case)
     dc = DeviceCase(case, vals)
@@ -54,8 +55,12 @@ def test_decode_step_replays_bitwise(name):
     ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda")
 
     def step():
-        dc.store()
-        P.paged_decode_attn(dc.pool, 0, dc.q["self"], m, case.sm_scale, out, lse, ws)
+        if append:  # the append rides in the decode's planner launch
+            P.paged_decode_attn_append(dc.pool, 0, dc.q["self"], m, dc.k_new, dc.v_new, dc.out_loc, case.sm_scale,
+                                       out, lse, ws)
+        else:
+            dc.store()
+            P.paged_decode_attn(dc.pool, 0, dc.q["self"], m, case.sm_scale, out, lse, ws)
 
     step()
     torch.cuda.synchronize()
