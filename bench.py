@@ -778,7 +778,7 @@ def main():
     b, cfg = build_workload(args.workload)
     if isinstance(b, DecodeBench) and b.case.n_new:
         b.fused_append = not args.separate_append
-        if b.fused_append:
+        if b.fused_append and "step" in cfg:
             cfg["step"] = cfg["step"].replace("kv_store + ", "").replace(
                 "paged_decode_attn", "paged_decode_attn_append (the kv_store runs in its planner launch)")
     ev = HipEvents()
