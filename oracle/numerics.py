@@ -11,7 +11,8 @@ import numpy as np
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     """uint16 bf16 bit patterns -> float64, exactly (NaN stays NaN)."""
     bits = np.asarray(bits, dtype=np.uint16)
-    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore"):  # signalling-NaN patterns widen to NaN
+        return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
 def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:

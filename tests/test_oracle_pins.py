@@ -6,6 +6,7 @@ import os
 
 import numpy as np
 import pytest
+import torch
 
 import oracle
 
@@ -203,3 +204,41 @@ def test_in_page_contiguity_detects_violation():
 def test_block_table_rejects_negative_entry_inside_length():
     with pytest.raises(AssertionError):
         oracle.slots_from_pages([3, -1], 16, 20)
+
+
+# ---------------------------------------------------------------------------
+# element-format conversions (oracle/numerics.py)
+# ---------------------------------------------------------------------------
+
+def test_bf16_widening_matches_torch_and_closed_forms():
+    from oracle.numerics import bf16_bits_to_f64, to_f64
+    bits = np.array([0x3F80, 0xC000, 0x0000, 0x8000, 0x7F80, 0xFF80, 0x0001, 0x7F7F, 0x3F81], np.uint16)
+    want = [1.0, -2.0, 0.0, -0.0, np.inf, -np.inf, 2.0 ** -133, (2 - 2 ** -7) * 2.0 ** 127, 1 + 2 ** -7]
+    got = bf16_bits_to_f64(bits)
+    assert got.tolist() == want
+    assert np.signbit(got[3]) and not np.signbit(got[2])
+    assert np.isnan(bf16_bits_to_f64(np.array([0x7FC0], np.uint16)))[0]
+    # every finite pattern against torch's own bf16 -> fp64 widening
+    allbits = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    t = torch.from_numpy(allbits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    mine = bf16_bits_to_f64(allbits)
+    fin = np.isfinite(t)
+    assert np.array_equal(mine[fin], t[fin]) and np.array_equal(np.isnan(mine), np.isnan(t))
+    assert np.array_equal(to_f64(allbits, "bf16")[fin], t[fin])
+    f32 = np.array([1.5, -3.25e-30, 7e37], np.float32)
+    assert to_f64(f32, "f32").tolist() == [float(x) for x in f32]
+    with pytest.raises(ValueError):
+        to_f64(f32, "fp8")
+
+
+def test_bf16_rounding_is_nearest_even():
+    from oracle.numerics import f64_to_bf16_bits
+    # ties go to the even mantissa: 1 + 2^-8 -> 1.0, 1 + 3 * 2^-8 -> 1 + 2^-6
+    x = np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -8 + 2 ** -20, -2.0, np.nan], np.float64)
+    assert f64_to_bf16_bits(x).tolist() == [0x3F80, 0x3F80, 0x3F82, 0x3F81, 0xC000, 0x7FC0]
+    # random binary32 values (ties included) against torch's float32 -> bf16
+    rng = np.random.default_rng(7)
+    f = (rng.standard_normal(20000) * 10.0 ** rng.integers(-20, 20, 20000)).astype(np.float32)
+    f[:2000] = (f[:2000].view(np.uint32) & np.uint32(0xFFFF8000) | np.uint32(0x8000)).view(np.float32)  # ties
+    want = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(f64_to_bf16_bits(f.astype(np.float64)), want)
