@@ -192,6 +192,6 @@ def run_verify(dc: "DeviceCase", fmt: int, n: int):
     lse = torch.full((c.bs, n, g.num_q_heads), float("nan"), dtype=torch.float32, device="cuda")
     nb = P.paged_decode_workspace_bytes(dc.pool, c.bs, n * g.num_q_heads, m.max_kv_len)
     ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
-    P.paged_verify_attn(dc.pool, 0, q, m, c.sm_scale, out, lse, ws)
+    P.paged_verify_attn(dc.pool, dc.layer, q, m, c.sm_scale, out, lse, ws)
     torch.cuda.synchronize()
     return out.view(c.bs * n, g.num_q_heads, g.head_dim_v), lse.view(c.bs * n, g.num_q_heads)

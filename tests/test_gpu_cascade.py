@@ -27,7 +27,7 @@ def cascade(dc, fmt, indptr, prefix_len, max_group=None):
     lse = torch.full((c.bs, g.num_q_heads), float("nan"), dtype=torch.float32, device="cuda")
     nb = P.paged_decode_cascade_workspace_bytes(dc.pool, c.bs, g.num_q_heads, m.max_kv_len, groups)
     ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda")
-    P.paged_decode_attn_cascade(dc.pool, 0, dc.q["self"], m, groups, c.sm_scale, out, lse, ws)
+    P.paged_decode_attn_cascade(dc.pool, dc.layer, dc.q["self"], m, groups, c.sm_scale, out, lse, ws)
     torch.cuda.synchronize()
     return out, lse
 
