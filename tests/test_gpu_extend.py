@@ -167,3 +167,19 @@ def test_softcap_matches_oracle(softcap, head_dim):
         # the ragged variant takes the same options
         out2, _ = run_extend(dc, region, P.PKV_MAP_TOKEN_TABLE, contiguous=True, softcap=softcap)
         assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+@pytest.mark.parametrize("head_dim", [64, 128])
+def test_long_causal_prefill_matches_oracle(head_dim):
+    """One 3000-token causal prefill (16 query tiles of the diagonal, every
+    mask boundary) followed by a 1000-token full span over all 4000 keys."""
+    case = W.mixed_spans(seed=11, rows=1, spans=((3000, True), (1000, False)), num_q_heads=8, num_kv_heads=2,
+                         head_dim=head_dim)
+    print(f"long causal prefill, head_dim {head_dim}", flush=True)
+    vals = W.make_values(case, canary=True)
+    dc = DeviceCase(case, vals)
+    dc.store()
+    out, lse = run_extend(dc, "self", P.PKV_MAP_CSR)
+    ref_o, ref_l = oracle_region(case, vals, "self")
+    assert_attn_close(out, ref_o, "bf16", f"long prefill d{head_dim}")
+    assert_lse_close(lse, ref_l, "bf16", f"long prefill d{head_dim}")
