@@ -311,12 +311,17 @@ class VerifyBench(DecodeBench):
 
     def step(self, timers=None):
         P, c = self.P, self.case
-        P.kv_store(self.pool, 0, self.k_new, self.v_new, self.out_loc)
+        if not self.fused_append:
+            P.kv_store(self.pool, 0, self.k_new, self.v_new, self.out_loc)
         P.build_kv_indices(P.PKV_MAP_BLOCK_TABLE, self.table, self.rpi, self.kv_start, self.kv_lens,
                            c.geom.page_size, self.max_len, None, self.bt)
         if timers:
             P.pkv_set_kernel_timer(*timers[0])
-        P.paged_verify_attn(self.pool, 0, self.qv, self.map, c.sm_scale, self.out, self.lse, self.ws)
+        if self.fused_append:
+            P.paged_verify_attn_append(self.pool, 0, self.qv, self.map, self.k_new, self.out_loc, c.sm_scale,
+                                       self.out, self.lse, self.ws)
+        else:
+            P.paged_verify_attn(self.pool, 0, self.qv, self.map, c.sm_scale, self.out, self.lse, self.ws)
 
     def kernel_bytes(self, logical: bool = False) -> int:
         """Every distinct latent row once, a page id share per token, and the
@@ -758,8 +763,9 @@ def main():
                     help="after the timed steps, time the kernel this many more times with the caches "
                          "cleared (a 1 GiB read) before each step; reported as roofline.kernel_ms_cold")
     ap.add_argument("--separate-append", action="store_true",
-                    help="decode workloads: launch kv_store on its own before paged_decode_attn instead of "
-                         "passing the append to paged_decode_attn_append")
+                    help="decode and verification workloads: launch kv_store on its own before the attention "
+                         "call instead of passing the append to paged_decode_attn_append / "
+                         "paged_verify_attn_append")
     ap.add_argument("--no-attainable", action="store_true",
                     help="skip the plain 1 GiB device copy and the 8192^3 bf16 GEMM that report "
                          "roofline.attainable_copy_gbs and roofline.attainable_gemm_tflops")
@@ -779,8 +785,9 @@ def main():
     if isinstance(b, DecodeBench) and b.case.n_new:
         b.fused_append = not args.separate_append
         if b.fused_append and "step" in cfg:
-            cfg["step"] = cfg["step"].replace("kv_store + ", "").replace(
-                "paged_decode_attn", "paged_decode_attn_append (the kv_store runs in its planner launch)")
+            cfg["step"] = cfg["step"].replace("kv_store (drafts) + ", "").replace("kv_store + ", "").replace(
+                "paged_decode_attn", "paged_decode_attn_append (the kv_store runs in its planner launch)").replace(
+                "paged_verify_attn", "paged_verify_attn_append (the drafts' kv_store runs in its planner launch)")
     ev = HipEvents()
     for _ in range(args.warmup):
         b.step()

@@ -269,6 +269,21 @@ int paged_verify_attn(const pkv_pool* pool, int32_t layer, const void* q, int32_
                       const pkv_kv_map* map, float sm_scale, void* out, float* lse, void* workspace, size_t ws_bytes,
                       void* stream);
 
+/* paged_verify_attn with the drafts' latent rows stored in the same call
+ * ([BACKEND] target verify: the drafts' keys are written to the pool and
+ * attended in one step; [MINI] "The KV pool: one preallocated block of
+ * memory": the backend stores before it attends).  Bits equal kv_store(pool,
+ * layer, k_new, NULL, out_loc, n_new) followed by paged_verify_attn(...);
+ * the append runs inside the verification's planner launch.
+ *   k_new, out_loc, n_new: as kv_store on a latent pool.
+ *   Other arguments and errors: as paged_verify_attn, and as kv_store for
+ *   the append's arguments (all checked before anything is launched).  With
+ *   map->bs = 0 only the append runs. */
+int paged_verify_attn_append(const pkv_pool* pool, int32_t layer, const void* q, int32_t num_q_heads,
+                             int32_t num_draft, const pkv_kv_map* map, const void* k_new, const int32_t* out_loc,
+                             int64_t n_new, float sm_scale, void* out, float* lse, void* workspace, size_t ws_bytes,
+                             void* stream);
+
 /* Groups of requests that share a prefix ([XPU] introduction: requests
  * sharing a prefix share its pages; [MINI]'s prefix cache).  Group g is the
  * requests group_indptr[g] .. group_indptr[g+1] - 1 of the batch (groups

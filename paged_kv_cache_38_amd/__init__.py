@@ -37,7 +37,7 @@ __all__ = [
     "Pool", "KVMap", "kv_pool_bytes", "kv_pool_create", "kv_pool_destroy", "kv_pool_padding_page",
     "kv_pool_token_bytes", "kv_store", "build_kv_indices", "make_kv_map", "paged_decode_workspace_bytes",
     "paged_decode_attn", "PrefixGroups", "make_prefix_groups", "paged_decode_cascade_workspace_bytes",
-    "paged_decode_attn_cascade", "paged_decode_attn_append", "paged_verify_attn", "paged_extend_attn", "paged_extend_attn_ex", "kv_gather",
+    "paged_decode_attn_cascade", "paged_decode_attn_append", "paged_verify_attn", "paged_verify_attn_append", "paged_extend_attn", "paged_extend_attn_ex", "kv_gather",
     "kv_validate",
     "pkv_set_kernel_timer", "library",
     "enc_cache_write", "enc_cache_merge", "enc_cache_check",
@@ -322,6 +322,24 @@ def paged_verify_attn(pool: Pool, layer: int, q: torch.Tensor, kv_map: KVMap, sm
                                        C.byref(kv_map.struct), float(sm_scale), _dev(out, "out", pool.dtype),
                                        _dev(lse, "lse", torch.float32), ws_ptr, ws_bytes, _stream(stream)),
             "paged_verify_attn")
+
+
+def paged_verify_attn_append(pool: Pool, layer: int, q: torch.Tensor, kv_map: KVMap, k_new: torch.Tensor,
+                             out_loc: torch.Tensor, sm_scale: float, out: torch.Tensor,
+                             lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                             stream=None) -> None:
+    """kv_store(pool, layer, k_new, None, out_loc) then paged_verify_attn, as
+    one call whose append rides in the verification's planner launch."""
+    if q.dim() != 4 or out.shape[:3] != q.shape[:3]:
+        raise ValueError("q must be [bs, num_draft, Hq, 576] and out [bs, num_draft, Hq, 512]")
+    ws_ptr = _dev(workspace, "workspace")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    L.check(L.load().paged_verify_attn_append(pool.handle, layer, _dev(q, "q", pool.dtype), q.shape[2], q.shape[1],
+                                              C.byref(kv_map.struct), _dev(k_new, "k_new", pool.dtype),
+                                              _dev(out_loc, "out_loc", torch.int32), out_loc.numel(),
+                                              float(sm_scale), _dev(out, "out", pool.dtype),
+                                              _dev(lse, "lse", torch.float32), ws_ptr, ws_bytes, _stream(stream)),
+            "paged_verify_attn_append")
 
 
 def paged_extend_attn(pool: Pool, layer: int, q: torch.Tensor, qo_indptr: torch.Tensor, max_q_len: int,

@@ -116,6 +116,9 @@ SIGNATURES = {
                                             C.c_size_t, C.c_void_p]),
     "paged_verify_attn": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.c_int32, C.POINTER(KVMapStruct),
                                     C.c_float, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "paged_verify_attn_append": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.c_int32,
+                                           C.POINTER(KVMapStruct), C.c_void_p, C.c_void_p, C.c_int64, C.c_float,
+                                           C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "paged_extend_attn": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_int64, C.c_void_p, C.c_int32, C.c_int32,
                                     C.POINTER(KVMapStruct), C.c_int32, C.c_float, C.c_void_p, C.c_void_p,
                                     C.c_void_p]),

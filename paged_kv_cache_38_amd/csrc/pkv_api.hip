@@ -416,13 +416,16 @@ int paged_decode_attn_cascade(const pkv_pool* pool, int32_t layer, const void* q
                        "paged_decode_attn_cascade");
 }
 
-int paged_verify_attn(const pkv_pool* pool, int32_t layer, const void* q, int32_t num_q_heads, int32_t num_draft,
-                      const pkv_kv_map* map, float sm_scale, void* out, float* lse, void* workspace, size_t ws_bytes,
-                      void* stream) {
-  if (int st = check_pool(pool)) return st;
-  if (int st = check_layer(pool, layer)) return st;
+}  // extern "C"
+
+namespace {
+// paged_verify_attn with an optional append of the drafts' K rows (st.n ==
+// 0: none), checked before anything is launched.
+int verify_call(const pkv_pool* pool, int32_t layer, const void* q, int32_t num_q_heads, int32_t num_draft,
+                const pkv_kv_map* map, float sm_scale, void* out, float* lse, void* workspace, size_t ws_bytes,
+                void* stream, const pkv::StoreArgs& st, const char* what) {
   pkv::DevMap dm;
-  if (int st = make_devmap(pool, map, false, &dm)) return st;
+  if (int e = make_devmap(pool, map, false, &dm)) return e;
   if (num_q_heads <= 0 || num_draft <= 0) return fail(PKV_EINVAL, "num_q_heads and num_draft must be positive");
   if (!(sm_scale > 0.0f) || std::isinf(sm_scale)) return fail(PKV_EINVAL, "sm_scale must be positive and finite");
   const int64_t rows = (int64_t)num_q_heads * num_draft;
@@ -430,7 +433,10 @@ int paged_verify_attn(const pkv_pool* pool, int32_t layer, const void* q, int32_
     return fail(PKV_EUNSUPPORTED,
                 "target verification needs a latent bf16 576/512 pool and num_draft * num_q_heads in {16, 32, 64} "
                 "or a multiple of 128 up to 1024 (got %d x %d)", num_draft, num_q_heads);
-  if (map->bs == 0) return ok();
+  if (map->bs == 0) {
+    if (st.n == 0) return ok();
+    return device_status(pkv::launch_store_args(st, (hipStream_t)stream), what);
+  }
   if (!q || !out) return fail(PKV_EINVAL, "null q or out");
   if (!aligned16(q)) return fail(PKV_EALIGN, "q must be 16-byte aligned");
   const pkv::DecodePlan plan = pkv::plan_decode(pool->info, map->bs, (int32_t)rows, map->max_kv_len);
@@ -439,8 +445,37 @@ int paged_verify_attn(const pkv_pool* pool, int32_t layer, const void* q, int32_
   if (need > 0 && (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)))
     return fail(PKV_EALIGN, "workspace must be non-null and 256-byte aligned");
   return device_status(pkv::launch_mla_verify(pool->info, layer, q, (int32_t)rows, num_draft, dm, map->bs, plan,
-                                              sm_scale * pkv::kLog2e, out, lse, workspace, (hipStream_t)stream),
-                       "paged_verify_attn");
+                                              sm_scale * pkv::kLog2e, out, lse, workspace, (hipStream_t)stream,
+                                              st.n > 0 ? &st : nullptr),
+                       what);
+}
+}  // namespace
+
+extern "C" {
+
+int paged_verify_attn(const pkv_pool* pool, int32_t layer, const void* q, int32_t num_q_heads, int32_t num_draft,
+                      const pkv_kv_map* map, float sm_scale, void* out, float* lse, void* workspace, size_t ws_bytes,
+                      void* stream) {
+  if (int st = check_pool(pool)) return st;
+  if (int st = check_layer(pool, layer)) return st;
+  pkv::StoreArgs none{};
+  return verify_call(pool, layer, q, num_q_heads, num_draft, map, sm_scale, out, lse, workspace, ws_bytes, stream,
+                     none, "paged_verify_attn");
+}
+
+int paged_verify_attn_append(const pkv_pool* pool, int32_t layer, const void* q, int32_t num_q_heads,
+                             int32_t num_draft, const pkv_kv_map* map, const void* k_new, const int32_t* out_loc,
+                             int64_t n_new, float sm_scale, void* out, float* lse, void* workspace, size_t ws_bytes,
+                             void* stream) {
+  if (int st = check_pool(pool)) return st;
+  if (int st = check_layer(pool, layer)) return st;
+  const void* v_new = nullptr;  // a latent pool keeps one row per token
+  if (pool->desc.kind == PKV_KIND_LATENT)
+    if (int st = check_store(pool, k_new, &v_new, out_loc, n_new)) return st;
+  const pkv::StoreArgs sa = pkv::make_store_args(pool->info, layer, k_new, nullptr, out_loc,
+                                                 pool->desc.kind == PKV_KIND_LATENT ? n_new : 0);
+  return verify_call(pool, layer, q, num_q_heads, num_draft, map, sm_scale, out, lse, workspace, ws_bytes, stream,
+                     sa, "paged_verify_attn_append");
 }
 
 namespace {

@@ -285,8 +285,20 @@ def test_verify_arguments_checked_before_launch(lib):
         assert call(h, 16, 8) == L.PKV_ECAPACITY         # 128 rows
         assert call(hs, 16, 2) == L.PKV_EUNSUPPORTED     # not a latent pool
         assert call(h, 16, 2) == L.PKV_ECAPACITY         # no workspace
+
+        def app(pool, k=0x10000, loc=0x30000, n=8, scale=0.04):
+            return lib.paged_verify_attn_append(pool, 0, 0x4000, 16, 2, C.byref(m), k, loc, n, scale, 0x5000, None,
+                                                None, 0, None)
+        assert app(h, n=-1) == L.PKV_EINVAL               # the append's arguments first
+        assert app(h, k=None) == L.PKV_EINVAL
+        assert app(h, loc=None) == L.PKV_EINVAL
+        assert app(h, k=0x10004) == L.PKV_EALIGN
+        assert app(h, scale=0.0) == L.PKV_EINVAL
+        assert app(hs) == L.PKV_EUNSUPPORTED              # not a latent pool
+        assert app(h) == L.PKV_ECAPACITY                  # no workspace: nothing launched
         m.bs = 0
         assert call(h, 16, 2) == 0
+        assert app(h, n=0) == 0
     finally:
         lib.kv_pool_destroy(h)
         lib.kv_pool_destroy(hs)

@@ -171,3 +171,29 @@ def test_mla_verify_with_one_draft_equals_decode_bitwise():
     o1, l1 = dc.decode(P.PKV_MAP_CSR)
     o2, l2 = run_verify(dc, P.PKV_MAP_CSR, 1)
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("heads,n", [(16, 4), (128, 2)])
+def test_mla_verify_append_equals_store_then_verify_bitwise(heads, n):
+    """paged_verify_attn_append gives the bits of kv_store followed by
+    paged_verify_attn: outputs, lse and the latent pool."""
+    case = W.mla_decode(seed=20 + n, bs=5, len_range=(1, 900), num_q_heads=heads, num_draft=n,
+                        fixed_lens={0: max(1, n - 1)})
+    print(f"mla verify append heads {heads} drafts {n}", flush=True)
+    vals = W.make_values(case, canary=True)
+    a = DeviceCase(case, vals)
+    a.store()
+    oa, la = run_verify(a, P.PKV_MAP_BLOCK_TABLE, n)
+    b = DeviceCase(case, vals)
+    g = case.geom
+    m = b.kv_map("self", P.PKV_MAP_BLOCK_TABLE)
+    q = b.q["self"].view(case.bs, n, g.num_q_heads, g.head_dim_qk)
+    out = torch.full((case.bs, n, g.num_q_heads, g.head_dim_v), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((case.bs, n, g.num_q_heads), float("nan"), dtype=torch.float32, device="cuda")
+    nb = P.paged_decode_workspace_bytes(b.pool, case.bs, n * g.num_q_heads, m.max_kv_len)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+    P.paged_verify_attn_append(b.pool, 0, q, m, b.k_new, b.out_loc, case.sm_scale, out, lse, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(-1, g.num_q_heads, g.head_dim_v).view(torch.int16), oa.view(torch.int16))
+    assert torch.equal(lse.view(-1, g.num_q_heads).view(torch.int32), la.view(torch.int32))
+    assert torch.equal(b.pool.flat("k", 0).view(torch.int16), a.pool.flat("k", 0).view(torch.int16))
