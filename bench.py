@@ -1,16 +1,21 @@
 #!/usr/bin/env python3
 """Benchmark of the paged KV-cache hot path on one MI355X.
 
-Default workload (the headline line): Qwen3-0.6B-shaped single-layer decode,
-bf16 -- batch 64, 16 query heads over 8 KV heads, head_dim 128, page_size 1
-through a token-granular req_to_token table of width 8192, KV lengths uniform
-in [512, 4096], slots a seeded shuffle of a 400k-token pool.  One step is one
-pass of the hot path over the batch: the KV append of the 64 new tokens
-(kv_store) then paged decode attention (planner, split-K partial kernel,
-log-sum-exp merge).  Inputs are resident in HBM before timing starts.
+Default workload (the headline line): large-batch paged GQA decode with
+prefix sharing, bf16 -- batch 256, 32 query heads over 8 KV heads, head_dim
+128, page_size 16, KV lengths lognormal (median 2048, sigma 1, clipped to
+[64, 32768]), groups of 8 requests reading the same physical pages for a
+common 2048-token prefix, pool of 1.2x the pages needed in a seeded
+free-list order.  One step is one pass of the hot path over the batch:
+build_kv_indices (CSR) then paged_decode_attn (planner, split-K kernel,
+log-sum-exp merge).  Inputs are resident in HBM before timing starts.  This
+is the largest of the decode workloads that fit one GPU; the roofline
+counts each distinct K/V row once.
 
-Other workloads (--workload): gqa_prefix_share_ps16 / _ps64 (batch-256 GQA
-decode with shared 2048-token prefixes; the _cascade variants pass the
+Other workloads (--workload): qwen3_decode (Qwen3-0.6B-shaped decode: batch
+64, 16 / 8 heads, head_dim 128, page_size 1 through a token table of width
+8192, lengths U[512, 4096], the step's KV append in the planner launch),
+gqa_prefix_share_ps64 (page size 64; the _cascade variants pass the
 prefix groups to the cascade decode), mla_decode (latent 576/512, 128
 heads, page_size 64), mla_verify (the same pool, 32 heads x 4 draft tokens
 verified per request), encdec_extend (Whisper-shaped causal + cross extend
@@ -113,6 +118,22 @@ def _blas_threads() -> int:
         return int(max(n)) if n else 1
     except Exception:
         return 1
+
+
+_LIMITER = None
+
+
+def _cpu_cores() -> dict:
+    """The host cores this process may run on (its CPU affinity), with the
+    BLAS pool set to that many threads; both are reported."""
+    global _LIMITER
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_limits
+        _LIMITER = threadpool_limits(limits=cores, user_api="blas")
+    except Exception:
+        pass
+    return {"cores": cores, "blas_threads": _blas_threads()}
 
 
 def _row_bytes(g) -> int:
@@ -235,6 +256,7 @@ class DecodeBench:
         import oracle
         from workloads.cases import to_numpy_bits
 
+        cpu = _cpu_cores()
         c, g = self.case, self.case.geom
         r = c.regions["self"]
         self.torch.cuda.synchronize()
@@ -256,7 +278,7 @@ class DecodeBench:
                     break
         dt = time.perf_counter() - t0
         gbs = toks * (_row_bytes(g) + 4) / dt / 1e9
-        return {"value": round(gbs, 4), "unit": "GB/s", "cores": _blas_threads(), "kind": "oracle",
+        return {"value": round(gbs, 4), "unit": "GB/s", **cpu, "kind": "oracle",
                 "decode_tokens_per_s": round(reqs / dt, 3),
                 "sample": f"{reqs} request decodes ({reqs / c.bs:.2f} passes over the {c.bs}-request batch, "
                           f"{toks} KV tokens) by the numpy fp64 oracle (gather + BLAS matmul per request), "
@@ -349,6 +371,7 @@ class VerifyBench(DecodeBench):
         import oracle
         from workloads.cases import to_numpy_bits
 
+        cpu = _cpu_cores()
         c, g = self.case, self.case.geom
         r = c.regions["self"]
         self.torch.cuda.synchronize()
@@ -366,7 +389,7 @@ class VerifyBench(DecodeBench):
                 if time.perf_counter() - t0 > budget_s:
                     break
         dt = time.perf_counter() - t0
-        return {"value": round(toks * _row_bytes(g) / dt / 1e9, 4), "unit": "GB/s", "cores": _blas_threads(),
+        return {"value": round(toks * _row_bytes(g) / dt / 1e9, 4), "unit": "GB/s", **cpu,
                 "kind": "oracle", "verified_tokens_per_s": round(reqs * self.n / dt, 3),
                 "sample": f"{reqs} request verifications of {self.n} drafts ({toks} KV tokens) by the numpy fp64 "
                           f"oracle, {dt:.1f} s"}
@@ -482,6 +505,7 @@ class ExtendBench:
         import oracle
         from workloads.cases import to_numpy_bits
 
+        cpu = _cpu_cores()
         c, g = self.case, self.case.geom
         self.torch.cuda.synchronize()
         pk, pv = to_numpy_bits(self.pool.flat("k", 0)), to_numpy_bits(self.pool.flat("v", 0))
@@ -501,7 +525,7 @@ class ExtendBench:
                 if time.perf_counter() - t0 > budget_s:
                     break
         dt = time.perf_counter() - t0
-        return {"value": round(toks / dt, 2), "unit": "extend tokens/s", "cores": _blas_threads(), "kind": "oracle",
+        return {"value": round(toks / dt, 2), "unit": "extend tokens/s", **cpu, "kind": "oracle",
                 "sample": f"{reqs} request extends ({' + '.join(c.regions)}; {reqs / c.bs:.2f} passes over the "
                           f"{c.bs}-request batch, {toks} new tokens) by the numpy fp64 oracle, {dt:.1f} s"}
 
@@ -569,6 +593,7 @@ class EncCacheBench:
         import oracle
         from workloads.cases import to_numpy_bits
 
+        cpu = _cpu_cores()
         w = self.w
         self.torch.cuda.synchronize()
         buf = to_numpy_bits(self.buf)
@@ -581,6 +606,7 @@ class EncCacheBench:
             steps += 1
         dt = time.perf_counter() - t0
         return {"value": round(steps * self.kernel_bytes() / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+                "cores_available": cpu["cores"],
                 "kind": "oracle", "merged_tokens_per_s": round(steps * w.real_tokens / dt, 1),
                 "sample": f"{steps} whole write + merge steps by the numpy oracle (a full buffer copy per write), "
                           f"{dt:.1f} s"}
@@ -681,7 +707,8 @@ class AllocBench:
             oracle.free_pages(ring, oracle.pages_of_slots(slots, w.page_size))
             steps += 1
         dt = time.perf_counter() - t0
-        return {"value": round(steps * self.new / dt, 1), "unit": "slots/s", "cores": 1, "kind": "oracle",
+        return {"value": round(steps * self.new / dt, 1), "unit": "slots/s", "cores": 1,
+                "cores_available": len(os.sched_getaffinity(0)), "kind": "oracle",
                 "sample": f"{steps} whole allocation steps ({steps * self.new} slots) by the Python oracle, "
                           f"{dt:.1f} s"}
 
@@ -756,7 +783,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="qwen3_decode")
+    ap.add_argument("--workload", default="gqa_prefix_share_ps16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--cold-steps", type=int, default=10,

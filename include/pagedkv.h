@@ -515,7 +515,13 @@ int enc_cache_check(const int32_t* fill_count, const int32_t* scheduled, int64_t
 /* Check a map's contents on the device and SYNCHRONISE `stream`: slots and
  * page ids in range, -1 only after a request's last page, no real request on
  * the padding page, kv_start page aligned for page-granular use, tokens
- * contiguous inside each page.
+ * contiguous inside each page.  The invariants are the pages': the paged
+ * allocator hands out whole pages and keeps a request's tokens contiguous
+ * inside each page, so a page id is slot // page_size ([XPU] "How SGLang
+ * stores the KV cache: two pools and a page size"; the page-aligned encoder
+ * start of [XPU] "Approach 1: page-align the encoder"); the extra last page
+ * is a padding page that only dummy requests of a padded batch point at
+ * ([MINI] "Why the extra page?").  A debug call, off the hot path.
  *   is_dummy: nullable device int32[bs], nonzero marks padded-batch dummies.
  *   scratch: device int64[bs * 8] the kernel writes per-request counts to
  *     (the library allocates nothing).

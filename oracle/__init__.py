@@ -67,5 +67,4 @@ from .enc_cache import (  # noqa: F401
     merge_blocks,
     fill_counts,
     check_filled,
-    global_to_local_positions,
 )

@@ -14,9 +14,7 @@ What the AWS Neuron on-device encoder cache page describes ("Buffer Layout",
   and a position map ``[max_blocks, block_size]`` (int64) giving, for every
   token of every gathered block, its row in the batch's hidden states; the
   sentinel ``num_tokens`` marks a don't-care token, whose write lands in a
-  dummy row that is thrown away.  Under sequence parallelism, global
-  positions are remapped to the rank's local range and everything outside
-  becomes the sentinel.
+  dummy row that is thrown away.
 * Fail loud: every scheduled position must have been filled.
 
 Plain numpy and Python loops over blocks and tokens.
@@ -74,12 +72,3 @@ def check_filled(counts: np.ndarray, scheduled: np.ndarray = None) -> Tuple[int,
     counts = np.asarray(counts)
     sched = np.ones(len(counts), bool) if scheduled is None else np.asarray(scheduled, bool)
     return int(np.sum(sched & (counts == 0))), int(np.sum(counts > 1))
-
-
-def global_to_local_positions(positions: np.ndarray, rank_start: int, rank_len: int) -> np.ndarray:
-    """A rank's view of a global position map: positions inside
-    ``[rank_start, rank_start + rank_len)`` shifted to the rank's rows, all
-    others (and the global sentinel) set to the local sentinel ``rank_len``."""
-    p = np.asarray(positions, np.int64)
-    inside = (p >= rank_start) & (p < rank_start + rank_len)
-    return np.where(inside, p - rank_start, rank_len)

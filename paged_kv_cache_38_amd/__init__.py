@@ -74,6 +74,34 @@ def _dev(t: Optional[torch.Tensor], name: str, dtype=None) -> Optional[int]:
     return t.data_ptr()
 
 
+def _check_rows(pool: "Pool", t: Optional[torch.Tensor], name: str, n: int, which: str) -> None:
+    """``t`` must hold at least ``n`` token rows of the pool's K (or V) row
+    size: the kernels read ``n`` rows from it and cannot check."""
+    if n <= 0:
+        return
+    if t is None:
+        raise ValueError(f"{name} is required")
+    per = pool.num_kv_heads * (pool.head_dim_qk if which == "k" else pool.head_dim_v)
+    if t.dim() < 1 or t.shape[0] < n or t.numel() != t.shape[0] * per:
+        raise ValueError(f"{name} must be [>= {n}, {pool.num_kv_heads}, "
+                         f"{pool.head_dim_qk if which == 'k' else pool.head_dim_v}] rows, got {tuple(t.shape)}")
+
+
+def _check_attn(pool: "Pool", q: torch.Tensor, out: torch.Tensor, lse: Optional[torch.Tensor], lead: tuple,
+                what: str) -> None:
+    """q ``[*lead, Hq, head_dim_qk]``, out ``[*lead, Hq, head_dim_v]``, lse
+    ``[*lead, Hq]``: the kernels index them by these sizes and cannot check."""
+    k = len(lead)
+    if q.dim() != k + 2 or tuple(q.shape[:k]) != tuple(lead) or q.shape[-1] != pool.head_dim_qk:
+        raise ValueError(f"{what}: q must be [{', '.join(map(str, lead))}, Hq, {pool.head_dim_qk}], "
+                         f"got {tuple(q.shape)}")
+    want = (*lead, q.shape[k], pool.head_dim_v)
+    if tuple(out.shape) != want:
+        raise ValueError(f"{what}: out must be {want}, got {tuple(out.shape)}")
+    if lse is not None and lse.numel() != q.numel() // q.shape[-1]:
+        raise ValueError(f"{what}: lse must have one entry per query row and head")
+
+
 # ---------------------------------------------------------------------------
 # pool
 # ---------------------------------------------------------------------------
@@ -158,6 +186,9 @@ def kv_pool_token_bytes(pool: Pool) -> int:
 
 def kv_store(pool: Pool, layer: int, k: torch.Tensor, v: Optional[torch.Tensor], out_loc: torch.Tensor,
              stream=None) -> None:
+    _check_rows(pool, k, "k", out_loc.numel(), "k")
+    if not pool.latent:
+        _check_rows(pool, v, "v", out_loc.numel(), "v")
     L.check(L.load().kv_store(pool.handle, layer, _dev(k, "k", pool.dtype), _dev(v, "v", pool.dtype),
                               _dev(out_loc, "out_loc", torch.int32), out_loc.numel(), _stream(stream)), "kv_store")
 
@@ -247,6 +278,7 @@ def paged_decode_attn(pool: Pool, layer: int, q: torch.Tensor, kv_map: KVMap, sm
                       stream=None) -> None:
     """q ``[bs, Hq, Dqk]`` -> out ``[bs, Hq, Dv]`` (pool dtype); workspace a
     uint8 device tensor of at least paged_decode_workspace_bytes() bytes."""
+    _check_attn(pool, q, out, lse, (kv_map.bs,), "paged_decode_attn")
     ws_ptr = _dev(workspace, "workspace")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     L.check(L.load().paged_decode_attn(pool.handle, layer, _dev(q, "q", pool.dtype), q.shape[1],
@@ -261,6 +293,10 @@ def paged_decode_attn_append(pool: Pool, layer: int, q: torch.Tensor, kv_map: KV
                              workspace: Optional[torch.Tensor] = None, stream=None) -> None:
     """kv_store(pool, layer, k_new, v_new, out_loc) then paged_decode_attn,
     as one call whose append rides in the decode's planner launch."""
+    _check_attn(pool, q, out, lse, (kv_map.bs,), "paged_decode_attn_append")
+    _check_rows(pool, k_new, "k_new", out_loc.numel(), "k")
+    if not pool.latent:
+        _check_rows(pool, v_new, "v_new", out_loc.numel(), "v")
     ws_ptr = _dev(workspace, "workspace")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     L.check(L.load().paged_decode_attn_append(pool.handle, layer, _dev(q, "q", pool.dtype), q.shape[1],
@@ -300,6 +336,7 @@ def paged_decode_cascade_workspace_bytes(pool: Pool, bs: int, num_q_heads: int, 
 def paged_decode_attn_cascade(pool: Pool, layer: int, q: torch.Tensor, kv_map: KVMap, groups: PrefixGroups,
                               sm_scale: float, out: torch.Tensor, lse: Optional[torch.Tensor] = None,
                               workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    _check_attn(pool, q, out, lse, (kv_map.bs,), "paged_decode_attn_cascade")
     ws_ptr = _dev(workspace, "workspace")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     L.check(L.load().paged_decode_attn_cascade(pool.handle, layer, _dev(q, "q", pool.dtype), q.shape[1],
@@ -314,8 +351,9 @@ def paged_verify_attn(pool: Pool, layer: int, q: torch.Tensor, kv_map: KVMap, sm
     """Target verification over a latent pool: q ``[bs, num_draft, Hq, 576]``
     -> out ``[bs, num_draft, Hq, 512]``; workspace of at least
     paged_decode_workspace_bytes(pool, bs, num_draft * Hq, max_kv_len) bytes."""
-    if q.dim() != 4 or out.shape[:3] != q.shape[:3]:
+    if q.dim() != 4:
         raise ValueError("q must be [bs, num_draft, Hq, 576] and out [bs, num_draft, Hq, 512]")
+    _check_attn(pool, q, out, lse, (kv_map.bs, q.shape[1]), "paged_verify_attn")
     ws_ptr = _dev(workspace, "workspace")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     L.check(L.load().paged_verify_attn(pool.handle, layer, _dev(q, "q", pool.dtype), q.shape[2], q.shape[1],
@@ -330,8 +368,10 @@ def paged_verify_attn_append(pool: Pool, layer: int, q: torch.Tensor, kv_map: KV
                              stream=None) -> None:
     """kv_store(pool, layer, k_new, None, out_loc) then paged_verify_attn, as
     one call whose append rides in the verification's planner launch."""
-    if q.dim() != 4 or out.shape[:3] != q.shape[:3]:
+    _check_rows(pool, k_new, "k_new", out_loc.numel(), "k")
+    if q.dim() != 4:
         raise ValueError("q must be [bs, num_draft, Hq, 576] and out [bs, num_draft, Hq, 512]")
+    _check_attn(pool, q, out, lse, (kv_map.bs, q.shape[1]), "paged_verify_attn")
     ws_ptr = _dev(workspace, "workspace")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     L.check(L.load().paged_verify_attn_append(pool.handle, layer, _dev(q, "q", pool.dtype), q.shape[2], q.shape[1],
@@ -345,8 +385,9 @@ def paged_verify_attn_append(pool: Pool, layer: int, q: torch.Tensor, kv_map: KV
 def paged_extend_attn(pool: Pool, layer: int, q: torch.Tensor, qo_indptr: torch.Tensor, max_q_len: int,
                       kv_map: KVMap, causal: bool, sm_scale: float, out: torch.Tensor,
                       lse: Optional[torch.Tensor] = None, stream=None) -> None:
-    if out.shape[0] != q.shape[0]:
-        raise ValueError("out and q must have the same number of rows")
+    _check_attn(pool, q, out, lse, (q.shape[0],), "paged_extend_attn")
+    if qo_indptr.numel() != kv_map.bs + 1:
+        raise ValueError("qo_indptr must have bs + 1 entries")
     L.check(L.load().paged_extend_attn(pool.handle, layer, _dev(q, "q", pool.dtype), q.shape[0],
                                        _dev(qo_indptr, "qo_indptr", torch.int32), q.shape[1], int(max_q_len),
                                        C.byref(kv_map.struct), 1 if causal else 0, float(sm_scale),
@@ -360,8 +401,9 @@ def paged_extend_attn_ex(pool: Pool, layer: int, q: torch.Tensor, qo_indptr: tor
                          stream=None) -> None:
     """paged_extend_attn with per-request causal flags (device int32[bs],
     nonzero = causal) and softcap (0 = off)."""
-    if out.shape[0] != q.shape[0]:
-        raise ValueError("out and q must have the same number of rows")
+    _check_attn(pool, q, out, lse, (q.shape[0],), "paged_extend_attn")
+    if qo_indptr.numel() != kv_map.bs + 1:
+        raise ValueError("qo_indptr must have bs + 1 entries")
     if causal_flags is not None and causal_flags.numel() != kv_map.bs:
         raise ValueError("causal_flags must have one entry per request")
     opts = L.ExtendOpts(1 if causal else 0, _dev(causal_flags, "causal_flags", torch.int32), float(softcap))

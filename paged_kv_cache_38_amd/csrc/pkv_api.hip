@@ -68,6 +68,11 @@ int check_desc(const pkv_pool_desc* d) {
   } else {
     return fail(PKV_EUNSUPPORTED, "pool kind %d", d->kind);
   }
+  // slot ids are int32 everywhere (tables, out_loc, the kernels' slot maps):
+  // every slot of the pool, the padding page's included, must fit
+  if (((int64_t)d->num_pages + 1) * d->page_size > (int64_t)INT32_MAX)
+    return fail(PKV_EUNSUPPORTED, "pool of %lld slots: slot ids must fit in int32",
+                (long long)(((int64_t)d->num_pages + 1) * d->page_size));
   const int eb = d->dtype == PKV_DTYPE_F32 ? 4 : 2;
   if (((int64_t)d->num_kv_heads * d->head_dim_qk * eb) % 16 != 0 ||
       ((int64_t)d->num_kv_heads * d->head_dim_v * eb) % 16 != 0)

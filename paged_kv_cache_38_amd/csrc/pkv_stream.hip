@@ -14,6 +14,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "pkv_launch.h"
 
@@ -157,17 +158,21 @@ hipError_t launch_stream_plan(const DevMap& m, int32_t bs, int32_t max_tiles, in
   return hipGetLastError();
 }
 
-// One workgroup per CU of the current device.
+// One workgroup per CU of the current device.  The count is cached per
+// device in atomics: threads making their first call at once may each ask
+// the runtime, and all store the same value.
 int32_t device_cu_count() {
-  static int32_t cached[64] = {0};
+  static std::atomic<int32_t> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
+  int32_t n = cached[dev].load(std::memory_order_acquire);
+  if (n == 0) {
+    int c = 0;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
+    n = c;
+    cached[dev].store(n, std::memory_order_release);
   }
-  return cached[dev];
+  return n;
 }
 
 }  // namespace pkv

@@ -9,7 +9,7 @@ import paged_kv_cache_38_amd as P
 import workloads as W
 from workloads.cases import to_numpy_bits
 
-from gpu_util import DeviceCase, assert_attn_close, assert_lse_close, i32, oracle_after_store, oracle_region
+from gpu_util import DeviceCase, assert_attn_close, assert_lse_close, i32, offsets, oracle_after_store, oracle_region
 
 pytestmark = pytest.mark.gpu
 
@@ -132,7 +132,7 @@ def test_kv_gather_bit_exact(fmt):
     pk, pv = oracle_after_store(case, vals)
     for rname, r in case.regions.items():
         m = dc.kv_map(rname, fmt)
-        cu = oracle.token_indptr(r.kv_lens)
+        cu = offsets(r.kv_lens)
         tot = int(cu[-1])
         ko = torch.full((tot + 3, case.geom.num_kv_heads, case.geom.head_dim_qk), float("nan"), dtype=dc.dtype,
                         device="cuda")

@@ -8,8 +8,7 @@ import torch
 import paged_kv_cache_38_amd as P
 import workloads as W
 
-from gpu_util import DeviceCase, i32
-import oracle
+from gpu_util import DeviceCase, i32, offsets
 
 pytestmark = pytest.mark.gpu
 
@@ -28,7 +27,7 @@ def test_two_streams_give_the_sequential_bits():
     d_lse = torch.empty((dcase.bs, g.num_q_heads), dtype=torch.float32, device="cuda")
     ws = torch.empty(max(P.paged_decode_workspace_bytes(dd.pool, dcase.bs, g.num_q_heads, dm.max_kv_len), 256),
                      dtype=torch.uint8, device="cuda")
-    qo = i32(oracle.token_indptr(ecase.q_lens))
+    qo = i32(offsets(ecase.q_lens))
     tq = int(ecase.q_lens.sum())
     e_out = torch.empty((tq, ge.num_q_heads, ge.head_dim_v), dtype=torch.bfloat16, device="cuda")
     e_lse = torch.empty((tq, ge.num_q_heads), dtype=torch.float32, device="cuda")

@@ -3,9 +3,8 @@ encoder cache notes: "Buffer Layout", "Write Path", "Read Path", "Merge
 Inside Compiled Graph").  CPU only.
 
 merge_blocks walks blocks and tokens one by one; the pins restate the
-notes' own in-graph steps (stack, flatten, index_put with a dummy row),
-split the batch over sequence-parallel ranks, and use the printed layout
-example."""
+notes' own in-graph steps (stack, flatten, index_put with a dummy row) and
+use the printed layout example."""
 import json
 import os
 
@@ -47,18 +46,6 @@ def test_merge_equals_stack_flatten_index_put_with_dummy_row():
     padded = np.concatenate([hidden, np.zeros((1, hidden.shape[1]))])
     padded[pos.reshape(-1)] = stacked
     np.testing.assert_array_equal(got, padded[:n])
-
-
-def test_sequence_parallel_shards_reassemble_the_global_merge():
-    buf, ids, pos, hidden, n = world(1, num_tokens=60)
-    full = oracle.merge_blocks(buf, ids, pos, hidden, n)
-    parts = []
-    for r in range(3):
-        start, length = r * 20, 20
-        local = oracle.global_to_local_positions(pos, start, length)
-        assert ((local == length) | ((local >= 0) & (local < length))).all()
-        parts.append(oracle.merge_blocks(buf, ids, local, hidden[start:start + length], length))
-    np.testing.assert_array_equal(np.concatenate(parts), full)
 
 
 def test_write_path_scratch_block_absorbs_padding():
