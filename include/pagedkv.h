@@ -335,7 +335,9 @@ int paged_decode_attn_cascade(const pkv_pool* pool, int32_t layer, const void* q
  *     ([XPU] "Approach 2" empty-KV guard).
  *   sm_scale: the score scale, positive and finite (else PKV_EINVAL).
  *   map->fmt: any; CONTIGUOUS is the ragged (varlen) variant.
- * Supported: SPLIT_KV bf16, head_dim 64 or 128. */
+ * Supported: SPLIT_KV bf16 (MFMA kernel) or f32 (vector-ALU kernel, fp32
+ * throughout), head_dim 64 or 128, num_q_heads a multiple of
+ * num_kv_heads. */
 int paged_extend_attn(const pkv_pool* pool, int32_t layer, const void* q, int64_t total_q, const int32_t* qo_indptr,
                       int32_t num_q_heads, int32_t max_q_len, const pkv_kv_map* map, int32_t causal,
                       float sm_scale, void* out, float* lse, void* stream);

@@ -227,7 +227,7 @@ __global__ void __launch_bounds__(64 * WAVES, NS <= 2 ? 8 / WAVES : 4 / WAVES) d
     const bf16* k_pool, const bf16* v_pool, const bf16* __restrict__ q, int32_t Hq, int32_t Hkv, int32_t G,
     int32_t hg, const int32_t* __restrict__ header, const int32_t* __restrict__ meta, float scale_log2,
     bf16* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws_o, float* __restrict__ ws_lse,
-    int32_t pieces_only) {
+    int32_t pieces_only, const int32_t* __restrict__ prefix_skip) {
   constexpr int NK = D / 32;
   constexpr int NT = D / 16;
   constexpr int LDS = D + 8;
@@ -272,8 +272,10 @@ __global__ void __launch_bounds__(64 * WAVES, NS <= 2 ? 8 / WAVES : 4 / WAVES) d
 
   auto finish = [&](int i, int P, int T) {
     const int b0 = P / Bt, b1 = (P + T - 1) / Bt;
-    // (cascade decode merges every request afterwards: all results are pieces)
-    const bool direct = b0 == b1 && !pieces_only;
+    // (cascade decode merges every request afterwards: all results are
+    // pieces; with shared prefixes found by the decode, so is every request
+    // part of whose keys the prefix pass reads)
+    const bool direct = b0 == b1 && !pieces_only && (!prefix_skip || prefix_skip[i] == 0);
     float l_tot = l_run + shfl_xor(l_run, 16);
     l_tot += shfl_xor(l_tot, 32);
 #pragma unroll
@@ -334,53 +336,6 @@ __global__ void __launch_bounds__(64 * WAVES, NS <= 2 ? 8 / WAVES : 4 / WAVES) d
       }
     }
   }
-}
-
-// Merge of the stream pieces: one wavefront per (request, head).  Requests
-// finished inside one run were written directly; empty requests get zeros
-// and lse = -inf; the rest combine their pieces (ids run + request).
-template <int D>
-__global__ void __launch_bounds__(256) decode_stream_merge_kernel(int32_t bs, int32_t Hq,
-                                                                  const int32_t* __restrict__ header,
-                                                                  const int32_t* __restrict__ prefix,
-                                                                  const int32_t* __restrict__ ntiles,
-                                                                  const float* __restrict__ ws_o,
-                                                                  const float* __restrict__ ws_lse,
-                                                                  bf16* __restrict__ out, float* __restrict__ lse) {
-  constexpr int E = D / 64;  // elements per lane
-  const int lane = threadIdx.x & 63;
-  const int64_t idx = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (idx >= (int64_t)bs * Hq) return;
-  const int i = (int)(idx / Hq), h = (int)(idx % Hq);
-  bf16* op = out + idx * D + lane * E;
-  const int T = ntiles[i];
-  if (T == 0) {
-#pragma unroll
-    for (int e = 0; e < E; ++e) op[e] = (bf16)0.0f;
-    if (lse && lane == 0) lse[idx] = -INFINITY;
-    return;
-  }
-  const int Bt = header[0];
-  const int P = prefix[i];
-  const int b0 = P / Bt, b1 = (P + T - 1) / Bt;
-  if (b0 == b1) return;
-  float mx = -INFINITY;
-  for (int b = b0; b <= b1; ++b) mx = fmaxf(mx, ws_lse[((int64_t)b + i) * Hq + h]);
-  float o[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) o[e] = 0.f;
-  float sum = 0.f;
-  for (int b = b0; b <= b1; ++b) {
-    const int64_t row = ((int64_t)b + i) * Hq + h;
-    const float wgt = __expf(ws_lse[row] - mx);
-    sum += wgt;
-#pragma unroll
-    for (int e = 0; e < E; ++e) o[e] = fmaf(wgt, ws_o[row * D + lane * E + e], o[e]);
-  }
-  const float inv = 1.0f / sum;
-#pragma unroll
-  for (int e = 0; e < E; ++e) op[e] = (bf16)(o[e] * inv);
-  if (lse && lane == 0) lse[idx] = mx + __logf(sum);
 }
 
 // ---------------------------------------------------------------------------
@@ -494,44 +449,27 @@ __device__ __forceinline__ void cascade_tile(const DecodeTile<D>& T, int t0, int
 
 constexpr int kCascadeCols = 32;  // query rows (member x head) per wave: two MFMA column blocks
 
-// Shared-prefix kernel: one wave per (group, member slice, prefix chunk, KV
-// head).  A slice holds up to 32 / G members, so its rows fill two 16-row
-// MFMA column blocks; the prefix tiles are read through the table of the
-// group's longest member (every member's prefix keys are among its keys).
-// The hg workgroups of one work item are 8 blocks apart (one XCD), as in the
-// stream kernel.  Every (member, head, chunk) gets a partial result,
-// o = 0 / lse = -inf where the chunk holds none of the member's keys.
+// One prefix work item of the cascade: members [i0, i1) (consecutive
+// requests of one group, up to 32 / G of them so their rows fill two
+// 16-row MFMA column blocks) against tiles [t_begin, t_end) of the prefix
+// keys [0, E), read through the table of member rd (whose keys [0, E) every
+// member shares up to its own limit).  Row limits: min(kv_len, S) with one
+// S for the group, or min(kv_len, lim_arr[member]) when lim_arr is given.
+// Every (member, head) row gets a partial result in chunk slot c, o = 0 /
+// lse = -inf where the chunk holds none of the member's prefix keys.
 template <int D, int W, int FMT>
-__global__ void __launch_bounds__(64 * W) cascade_prefix_kernel(
-    DevMap m, const bf16* k_pool, const bf16* v_pool, const bf16* __restrict__ q, int32_t bs, int32_t Hq,
-    int32_t Hkv, int32_t G, int32_t hg, const int32_t* __restrict__ group_indptr,
-    const int32_t* __restrict__ prefix_len, int32_t num_groups, int32_t slices, int32_t chunks, int32_t tpc,
-    int32_t ms, float scale_log2, float* __restrict__ ws_po, float* __restrict__ ws_plse) {
+__device__ __forceinline__ void cascade_prefix_work(const DevMap& m, const bf16* k_pool, const bf16* v_pool,
+                                                    const bf16* __restrict__ q, int32_t bs, int32_t Hq,
+                                                    int32_t Hkv, int32_t G, int i0, int i1, int rd, int S,
+                                                    const int32_t* lim_arr, int E, int t_begin, int t_end, int c,
+                                                    int ms, float scale_log2, float* __restrict__ ws_po,
+                                                    float* __restrict__ ws_plse, bf16* vt) {
   constexpr int NK = D / 32;
   constexpr int NT = D / 16;
-  constexpr int LDS = D + 8;
   constexpr int NB = kCascadeCols / 16;
-  __shared__ __attribute__((aligned(16))) bf16 vsm[W][kTile * LDS];
-  const int work = (blockIdx.x / (8 * hg)) * 8 + blockIdx.x % 8;
-  if (work >= num_groups * slices * chunks) return;
-  const int c = work % chunks, sl = (work / chunks) % slices, gi = work / (chunks * slices);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
-  const int h = ((blockIdx.x / 8) % hg) * W + wave;  // KV head
-  const int ga = max(group_indptr[gi], 0), gb = min(group_indptr[gi + 1], bs);
-  const int i0 = ga + sl * ms, i1 = min(gb, i0 + ms);
-  if (i0 >= i1) return;  // uniform per workgroup
-  const int S = max(prefix_len[gi], 0) & ~(kTile - 1);
-  int rd = ga, Lmax = 0;  // the longest member reads the prefix
-  for (int k = ga; k < gb; ++k) {
-    const int L = m.kv_lens[k];
-    if (L > Lmax) {
-      Lmax = L;
-      rd = k;
-    }
-  }
-  const int E = min(S, Lmax);  // prefix keys any member sees
-  const int t_begin = c * tpc, t_end = min(t_begin + tpc, (E + kTile - 1) / kTile);
+  const int h = ((blockIdx.x / 8) % (Hkv / W)) * W + wave;  // KV head
 
   // rows: column cc of block b is member i0 + cc / G, query head h G + cc % G
   bf16x8 qb[NB][NK];
@@ -541,7 +479,8 @@ __global__ void __launch_bounds__(64 * W) cascade_prefix_kernel(
     const int cc = b * 16 + col;
     const int mm = i0 + cc / G;
     const bool ok = cc < ms * G && mm < i1;
-    lim[b] = ok ? min(m.kv_lens[mm], S) : 0;
+    const int L = ok ? m.kv_lens[mm] : 0;
+    lim[b] = ok ? min(L, lim_arr ? lim_arr[mm] : S) : 0;
     const bf16* qp = q + ((int64_t)(ok ? mm : i0) * Hq + h * G + cc % G) * D + grp * 8;
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
@@ -565,7 +504,6 @@ __global__ void __launch_bounds__(64 * W) cascade_prefix_kernel(
     const int64_t row_elems = (int64_t)Hkv * D;
     const bf16* kb = k_pool + (int64_t)h * D;
     const bf16* vb = v_pool + (int64_t)h * D;
-    bf16* vt = vsm[wave];
     // lane l < 32 holds the slot of key 32 t + l (keys past E read the padding slot)
     auto slot_word = [&](int t) -> int32_t {
       const int key = t * kTile + (lane & 31);
@@ -607,11 +545,151 @@ __global__ void __launch_bounds__(64 * W) cascade_prefix_kernel(
   }
 }
 
+// Shared-prefix kernel for caller-given groups: one wave per (group, member
+// slice, prefix chunk, KV head).  The prefix tiles are read through the
+// table of the group's longest member (every member's prefix keys are among
+// its keys).  The hg workgroups of one work item are 8 blocks apart (one
+// XCD), as in the stream kernel.
+template <int D, int W, int FMT>
+__global__ void __launch_bounds__(64 * W) cascade_prefix_kernel(
+    DevMap m, const bf16* k_pool, const bf16* v_pool, const bf16* __restrict__ q, int32_t bs, int32_t Hq,
+    int32_t Hkv, int32_t G, int32_t hg, const int32_t* __restrict__ group_indptr,
+    const int32_t* __restrict__ prefix_len, int32_t num_groups, int32_t slices, int32_t chunks, int32_t tpc,
+    int32_t ms, float scale_log2, float* __restrict__ ws_po, float* __restrict__ ws_plse) {
+  constexpr int LDS = D + 8;
+  __shared__ __attribute__((aligned(16))) bf16 vsm[W][kTile * LDS];
+  const int work = (blockIdx.x / (8 * hg)) * 8 + blockIdx.x % 8;
+  if (work >= num_groups * slices * chunks) return;
+  const int c = work % chunks, sl = (work / chunks) % slices, gi = work / (chunks * slices);
+  const int ga = max(group_indptr[gi], 0), gb = min(group_indptr[gi + 1], bs);
+  const int i0 = ga + sl * ms, i1 = min(gb, i0 + ms);
+  if (i0 >= i1) return;  // uniform per workgroup
+  const int S = max(prefix_len[gi], 0) & ~(kTile - 1);
+  int rd = ga, Lmax = 0;  // the longest member reads the prefix
+  for (int k = ga; k < gb; ++k) {
+    const int L = m.kv_lens[k];
+    if (L > Lmax) {
+      Lmax = L;
+      rd = k;
+    }
+  }
+  const int E = min(S, Lmax);  // prefix keys any member sees
+  const int t_begin = c * tpc, t_end = min(t_begin + tpc, (E + kTile - 1) / kTile);
+  cascade_prefix_work<D, W, FMT>(m, k_pool, v_pool, q, bs, Hq, Hkv, G, i0, i1, rd, S, nullptr, E, t_begin, t_end, c,
+                                 ms, scale_log2, ws_po, ws_plse, vsm[threadIdx.x >> 6]);
+}
+
+// Shared-prefix kernel for the groups paged_decode_attn finds itself: the
+// planner lists the work items (*count of them); a fixed grid strides over
+// them.
+template <int D, int W, int FMT>
+__global__ void __launch_bounds__(64 * W) share_prefix_kernel(
+    DevMap m, const bf16* k_pool, const bf16* v_pool, const bf16* __restrict__ q, int32_t bs, int32_t Hq,
+    int32_t Hkv, int32_t G, int32_t hg, const PrefixItem* __restrict__ items, const int32_t* __restrict__ count,
+    const int32_t* __restrict__ lim_arr, int32_t ms, float scale_log2, float* __restrict__ ws_po,
+    float* __restrict__ ws_plse) {
+  constexpr int LDS = D + 8;
+  __shared__ __attribute__((aligned(16))) bf16 vsm[W][kTile * LDS];
+  const int works = (int)gridDim.x / hg;  // a multiple of 8
+  const int n_items = *count;
+  for (int w = (blockIdx.x / (8 * hg)) * 8 + blockIdx.x % 8; w < n_items; w += works) {
+    const PrefixItem it = items[w];
+    cascade_prefix_work<D, W, FMT>(m, k_pool, v_pool, q, bs, Hq, Hkv, G, it.i0, it.i1, it.ref, 0, lim_arr, it.E,
+                                   it.t0, it.t1, it.c, ms, scale_log2, ws_po, ws_plse, vsm[threadIdx.x >> 6]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Shared prefixes found by paged_decode_attn itself ([MINI] prefix caching
+// and [XPU]: requests that share a prefix read the same pages; the pages
+// give no interface for it, so a plain decode looks for it).  One wave per
+// request.  Within each 64-request block of the batch, consecutive
+// requests whose keys start at the same slot form a group; the group's
+// reference is its longest member (the first on ties); every other member
+// shares the keys before the first page (token-table maps: the first slot)
+// where its table and the reference's differ.  Per request the kernel
+// writes s: the shared keys rounded down to the 32-key tile, or the whole
+// request rounded up to it when every key is shared, 0 when nothing is, -1
+// for the reference; and the group's bounds.  The planner derives each
+// request's skip from them and the prefix pass reads each shared tile once
+// for the whole group.  Grouping changes which keys a piece holds, never
+// the result beyond rounding: every key is still read exactly once per
+// request, by the prefix pass or the stream kernel.
+// ---------------------------------------------------------------------------
+template <int FMT>
+__global__ void __launch_bounds__(64) share_detect_kernel(DevMap m, int32_t bs, int32_t* __restrict__ s_out,
+                                                          int32_t* __restrict__ gs_out, int32_t* __restrict__ ge_out) {
+  const int i = blockIdx.x, lane = threadIdx.x;
+  const int base = i & ~63;
+  const int j = base + lane;
+  const bool in = j < bs;
+  const int32_t Lj = in ? max(m.kv_lens[j], 0) : 0;
+  int32_t key = -1;
+  if (in && Lj > 0) {
+    const SlotMap<FMT> smj = make_slotmap<FMT>(m, j);
+    key = smj(0, true);
+    if (key == smj.pad) key = -1;  // dummies on the padding page are never grouped
+  }
+  const int32_t prev = __shfl_up(key, 1, 64);
+  const bool opens = !in || lane == 0 || key < 0 || key != prev;
+  const uint64_t starts = __builtin_amdgcn_ballot_w64(opens);
+  const int li = i - base;
+  const uint64_t upto = (li == 63) ? ~0ull : ((2ull << li) - 1);
+  const int gs_l = 63 - __builtin_clzll(starts & upto);  // lane 0 always opens
+  const uint64_t after = starts & ~upto;
+  const int ge_l = after ? __builtin_ctzll(after) : 64;
+  const int gs = base + gs_l, ge = min(base + ge_l, bs);
+  // the reference: the longest member, the first on ties
+  int64_t pk = (in && lane >= gs_l && lane < ge_l) ? (((int64_t)Lj << 8) | (63 - lane)) : -1;
+  for (int o = 32; o > 0; o >>= 1) {
+    const int64_t y = __shfl_xor(pk, o, 64);
+    pk = y > pk ? y : pk;
+  }
+  const int ref = base + 63 - (int)(pk & 255);
+  int32_t s = 0;
+  const int32_t key_i = __shfl(key, li, 64);
+  if (ge - gs >= 2 && key_i >= 0) {
+    if (i == ref) {
+      s = -1;
+    } else {
+      const int32_t Li = __shfl(Lj, li, 64), Lr = __shfl(Lj, ref - base, 64);
+      const int32_t n = min(Li, Lr);
+      const int32_t gran = FMT == SLOT_PAGES ? (1 << m.page_shift) : 1;  // one probe per page
+      const SlotMap<FMT> smi = make_slotmap<FMT>(m, i), smr = make_slotmap<FMT>(m, ref);
+      const int32_t nk = (n + gran - 1) / gran;
+      int32_t c = n;
+      for (int32_t kb = 0; kb < nk; kb += 64) {
+        const int32_t k = kb + lane;
+        bool mis = false;
+        if (k < nk) {
+          const int32_t a = smi(k * gran, true), b = smr(k * gran, true);
+          mis = a != b || a == smi.pad;
+        }
+        const uint64_t mm = __builtin_amdgcn_ballot_w64(mis);
+        if (mm) {
+          c = min(n, (kb + (int32_t)__builtin_ctzll(mm)) * gran);
+          break;
+        }
+      }
+      s = c >= Li ? (Li + kTile - 1) / kTile * kTile : c / kTile * kTile;
+    }
+  }
+  if (lane == 0) {
+    s_out[i] = s;
+    gs_out[i] = gs;
+    ge_out[i] = ge;
+  }
+}
+
 // Final merge of a cascade decode: one wavefront per (request, head) over the
 // suffix pieces (ids run + request, every one in the workspace) and, for a
 // group member, the prefix chunks.
+// With direct_written (shared prefixes found by the decode itself), a
+// request outside the prefix pass that one run finished was written by the
+// stream kernel and is skipped here.
 template <int D>
 __global__ void __launch_bounds__(256) cascade_merge_kernel(int32_t bs, int32_t Hq, int32_t chunks,
+                                                            int32_t direct_written,
                                                             const int32_t* __restrict__ header,
                                                             const int32_t* __restrict__ prefix,
                                                             const int32_t* __restrict__ ntiles,
@@ -631,6 +709,7 @@ __global__ void __launch_bounds__(256) cascade_merge_kernel(int32_t bs, int32_t 
   const int P = prefix[i];
   const int b0 = P / Bt, b1 = T > 0 ? (P + T - 1) / Bt : b0 - 1;
   const int nc = skip[i] > 0 ? chunks : 0;
+  if (direct_written && nc == 0 && b0 == b1) return;
   auto piece = [&](int k, const float*& o) -> float {  // k < pieces: suffix, else prefix chunk
     const int np = b1 - b0 + 1;
     if (k < np) {
@@ -935,11 +1014,58 @@ size_t decode_ws_layout(const PoolInfo& p, const DecodePlan& plan, int32_t bs, i
   return off;
 }
 
+// ---- shared prefixes found by the stream decode itself
+constexpr int kShareChunks = 4;  // chunks of a group's prefix in the prefix pass
+struct ShareWs {
+  int32_t* s;
+  int32_t* gs;
+  int32_t* ge;
+  int32_t* skip;
+  int32_t* count;
+  PrefixItem* items;  // at most bs * kShareChunks (every slice holds a member)
+  float* po;          // prefix partials [kShareChunks][bs][Hq][Dv]
+  float* plse;        // [kShareChunks][bs][Hq]
+  int32_t ms;
+};
+
+// [stream workspace | s, gs, ge, skip [bs] | items [bs][ipr] | prefix o | prefix lse]
+static size_t stream_decode_ws_layout(const PoolInfo& p, const DecodePlan& plan, int32_t bs, int32_t Hq, void* base,
+                                      StreamWs* sw, ShareWs* sh) {
+  char* b = static_cast<char*>(base);
+  size_t off = stream_ws_layout(bs, plan.chunk, plan.max_splits, Hq, p.head_dim_v, base, sw);
+  auto take = [&](size_t bytes) {
+    char* at = b ? b + off : nullptr;
+    off += align256(bytes);
+    return at;
+  };
+  const int G = Hq / p.num_kv_heads;
+  const int32_t ms = std::max(1, kCascadeCols / G);
+  char* a_s = take((size_t)bs * 4);
+  char* a_gs = take((size_t)bs * 4);
+  char* a_ge = take((size_t)bs * 4);
+  char* a_skip = take((size_t)bs * 4);
+  char* a_count = take(4);
+  char* a_items = take((size_t)bs * kShareChunks * sizeof(PrefixItem));
+  char* a_po = take((size_t)kShareChunks * bs * Hq * p.head_dim_v * 4);
+  char* a_pl = take((size_t)kShareChunks * bs * Hq * 4);
+  if (sh) {
+    sh->s = reinterpret_cast<int32_t*>(a_s);
+    sh->gs = reinterpret_cast<int32_t*>(a_gs);
+    sh->ge = reinterpret_cast<int32_t*>(a_ge);
+    sh->skip = reinterpret_cast<int32_t*>(a_skip);
+    sh->count = reinterpret_cast<int32_t*>(a_count);
+    sh->items = reinterpret_cast<PrefixItem*>(a_items);
+    sh->po = reinterpret_cast<float*>(a_po);
+    sh->plse = reinterpret_cast<float*>(a_pl);
+    sh->ms = ms;
+  }
+  return off;
+}
+
 size_t decode_workspace_bytes(const PoolInfo& p, const DecodePlan& plan, int32_t bs, int32_t Hq) {
   if (plan.kind == DK_MLA)  // slices of rows reuse one workspace
     return stream_ws_layout(bs, plan.chunk, plan.max_splits, mla_slice_rows(Hq), p.head_dim_v, nullptr, nullptr);
-  if (plan.kind == DK_STREAM)
-    return stream_ws_layout(bs, plan.chunk, plan.max_splits, Hq, p.head_dim_v, nullptr, nullptr);
+  if (plan.kind == DK_STREAM) return stream_decode_ws_layout(p, plan, bs, Hq, nullptr, nullptr, nullptr);
   return decode_ws_layout(p, plan, bs, Hq, nullptr, nullptr);
 }
 
@@ -958,13 +1084,31 @@ static void launch_valu(unsigned blocks, hipStream_t s, const DevMap& m, const P
 template <int D, int W>
 static void launch_stream_main(int32_t runs, int32_t hg, hipStream_t s, const PoolInfo& p, int32_t layer,
                                const void* q, int32_t Hq, int32_t G, const StreamWs& w, float sl2, void* out,
-                               float* lse, int32_t pieces_only = 0) {
+                               float* lse, int32_t pieces_only = 0, const int32_t* prefix_skip = nullptr) {
   hipLaunchKernelGGL((decode_stream_kernel<D, W, kStreamSets>), dim3((unsigned)(runs * hg)), dim3(64 * W), 0, s,
                      reinterpret_cast<const bf16*>(p.k_layer(layer)), reinterpret_cast<const bf16*>(p.v_layer(layer)),
                      static_cast<const bf16*>(q), Hq, p.num_kv_heads, G, hg, w.header, w.meta, sl2,
-                     static_cast<bf16*>(out), lse, w.o, w.lse, pieces_only);
+                     static_cast<bf16*>(out), lse, w.o, w.lse, pieces_only, prefix_skip);
 }
 
+template <int D, int W>
+static void launch_share_prefix(const PoolInfo& p, int32_t layer, const DevMap& m, const void* q, int32_t bs,
+                                int32_t Hq, int32_t G, int32_t hg, const ShareWs& sh, float sl2, hipStream_t s) {
+  // at most bs * kShareChunks items; one work per CU covers the usual count
+  const int64_t works = (std::min<int64_t>((int64_t)bs * kShareChunks, device_cu_count()) + 7) / 8 * 8;
+  auto kern = (m.fmt == MAP_TOKEN_TABLE) ? share_prefix_kernel<D, W, SLOT_TABLE> : share_prefix_kernel<D, W, SLOT_PAGES>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(works * hg)), dim3(64 * W), 0, s, m,
+                     reinterpret_cast<const bf16*>(p.k_layer(layer)), reinterpret_cast<const bf16*>(p.v_layer(layer)),
+                     static_cast<const bf16*>(q), bs, Hq, p.num_kv_heads, G, hg, sh.items, sh.count, sh.skip, sh.ms,
+                     sl2, sh.po, sh.plse);
+}
+
+// The bf16 decode: find shared prefixes (share_detect_kernel), plan the
+// stream of every request's own tiles (the append, if any, rides in the
+// planner launch), stream them, read each group's shared prefix once
+// (share_prefix_kernel), then merge pieces and prefix chunks.  Without
+// shared prefixes the prefix pass finds no work and every request one run
+// finishes is written by the stream kernel directly.
 static hipError_t launch_stream_decode(const PoolInfo& p, int32_t layer, const void* q, int32_t Hq, const DevMap& m,
                                        int32_t bs, const DecodePlan& plan, float sl2, void* out, float* lse, void* ws,
                                        hipStream_t s, const StoreArgs* st) {
@@ -975,30 +1119,52 @@ static hipError_t launch_stream_decode(const PoolInfo& p, int32_t layer, const v
   const int32_t runs = plan.max_splits;
   if (runs % 8 != 0) return hipErrorInvalidValue;  // the block -> (run, head group) map needs whole XCD rounds
   StreamWs w;
-  stream_ws_layout(bs, plan.chunk, runs, Hq, p.head_dim_v, ws, &w);
-  hipError_t e = launch_stream_plan(m, bs, plan.chunk, runs, w, s, nullptr, st);
+  ShareWs sh;
+  stream_decode_ws_layout(p, plan, bs, Hq, ws, &w, &sh);
+  if (m.fmt == MAP_TOKEN_TABLE)
+    hipLaunchKernelGGL(share_detect_kernel<SLOT_TABLE>, dim3((unsigned)bs), dim3(64), 0, s, m, bs, sh.s, sh.gs, sh.ge);
+  else
+    hipLaunchKernelGGL(share_detect_kernel<SLOT_PAGES>, dim3((unsigned)bs), dim3(64), 0, s, m, bs, sh.s, sh.gs, sh.ge);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  ShareArgs sa;
+  sa.s = sh.s;
+  sa.gs = sh.gs;
+  sa.ge = sh.ge;
+  sa.skip = sh.skip;
+  sa.items = sh.items;
+  sa.count = sh.count;
+  sa.ms = sh.ms;
+  sa.ch = kShareChunks;
+  e = launch_stream_plan(m, bs, plan.chunk, runs, w, s, nullptr, st, &sa);
   if (e != hipSuccess) return e;
   const int D = p.head_dim_qk;
   timer_before(s);
   if (D == 128) {
-    if (W == 4) launch_stream_main<128, 4>(runs, hg, s, p, layer, q, Hq, G, w, sl2, out, lse);
-    else if (W == 2) launch_stream_main<128, 2>(runs, hg, s, p, layer, q, Hq, G, w, sl2, out, lse);
-    else launch_stream_main<128, 1>(runs, hg, s, p, layer, q, Hq, G, w, sl2, out, lse);
+    if (W == 4) launch_stream_main<128, 4>(runs, hg, s, p, layer, q, Hq, G, w, sl2, out, lse, 0, sh.skip);
+    else if (W == 2) launch_stream_main<128, 2>(runs, hg, s, p, layer, q, Hq, G, w, sl2, out, lse, 0, sh.skip);
+    else launch_stream_main<128, 1>(runs, hg, s, p, layer, q, Hq, G, w, sl2, out, lse, 0, sh.skip);
+    if (W == 4) launch_share_prefix<128, 4>(p, layer, m, q, bs, Hq, G, hg, sh, sl2, s);
+    else if (W == 2) launch_share_prefix<128, 2>(p, layer, m, q, bs, Hq, G, hg, sh, sl2, s);
+    else launch_share_prefix<128, 1>(p, layer, m, q, bs, Hq, G, hg, sh, sl2, s);
   } else {
-    if (W == 4) launch_stream_main<64, 4>(runs, hg, s, p, layer, q, Hq, G, w, sl2, out, lse);
-    else if (W == 2) launch_stream_main<64, 2>(runs, hg, s, p, layer, q, Hq, G, w, sl2, out, lse);
-    else launch_stream_main<64, 1>(runs, hg, s, p, layer, q, Hq, G, w, sl2, out, lse);
+    if (W == 4) launch_stream_main<64, 4>(runs, hg, s, p, layer, q, Hq, G, w, sl2, out, lse, 0, sh.skip);
+    else if (W == 2) launch_stream_main<64, 2>(runs, hg, s, p, layer, q, Hq, G, w, sl2, out, lse, 0, sh.skip);
+    else launch_stream_main<64, 1>(runs, hg, s, p, layer, q, Hq, G, w, sl2, out, lse, 0, sh.skip);
+    if (W == 4) launch_share_prefix<64, 4>(p, layer, m, q, bs, Hq, G, hg, sh, sl2, s);
+    else if (W == 2) launch_share_prefix<64, 2>(p, layer, m, q, bs, Hq, G, hg, sh, sl2, s);
+    else launch_share_prefix<64, 1>(p, layer, m, q, bs, Hq, G, hg, sh, sl2, s);
   }
   e = hipGetLastError();
   timer_after(s);
   if (e != hipSuccess) return e;
   const unsigned mblocks = (unsigned)(((int64_t)bs * Hq + 3) / 4);
   if (D == 128)
-    hipLaunchKernelGGL(decode_stream_merge_kernel<128>, dim3(mblocks), dim3(256), 0, s, bs, Hq, w.header, w.prefix,
-                       w.ntiles, w.o, w.lse, static_cast<bf16*>(out), lse);
+    hipLaunchKernelGGL(cascade_merge_kernel<128>, dim3(mblocks), dim3(256), 0, s, bs, Hq, kShareChunks, 1, w.header,
+                       w.prefix, w.ntiles, sh.skip, w.o, w.lse, sh.po, sh.plse, static_cast<bf16*>(out), lse);
   else
-    hipLaunchKernelGGL(decode_stream_merge_kernel<64>, dim3(mblocks), dim3(256), 0, s, bs, Hq, w.header, w.prefix,
-                       w.ntiles, w.o, w.lse, static_cast<bf16*>(out), lse);
+    hipLaunchKernelGGL(cascade_merge_kernel<64>, dim3(mblocks), dim3(256), 0, s, bs, Hq, kShareChunks, 1, w.header,
+                       w.prefix, w.ntiles, sh.skip, w.o, w.lse, sh.po, sh.plse, static_cast<bf16*>(out), lse);
   return hipGetLastError();
 }
 
@@ -1100,11 +1266,11 @@ hipError_t launch_decode_cascade(const PoolInfo& p, int32_t layer, const void* q
   if (e != hipSuccess) return e;
   const unsigned mblocks = (unsigned)(((int64_t)bs * Hq + 3) / 4);
   if (D == 128)
-    hipLaunchKernelGGL(cascade_merge_kernel<128>, dim3(mblocks), dim3(256), 0, s, bs, Hq, cp.chunks, w.stream.header,
+    hipLaunchKernelGGL(cascade_merge_kernel<128>, dim3(mblocks), dim3(256), 0, s, bs, Hq, cp.chunks, 0, w.stream.header,
                        w.stream.prefix, w.stream.ntiles, w.skip, w.stream.o, w.stream.lse, w.po, w.plse,
                        static_cast<bf16*>(out), lse);
   else
-    hipLaunchKernelGGL(cascade_merge_kernel<64>, dim3(mblocks), dim3(256), 0, s, bs, Hq, cp.chunks, w.stream.header,
+    hipLaunchKernelGGL(cascade_merge_kernel<64>, dim3(mblocks), dim3(256), 0, s, bs, Hq, cp.chunks, 0, w.stream.header,
                        w.stream.prefix, w.stream.ntiles, w.skip, w.stream.o, w.stream.lse, w.po, w.plse,
                        static_cast<bf16*>(out), lse);
   return hipGetLastError();

@@ -390,11 +390,166 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(DevMap m, const char* k_
 }
 
 // ---------------------------------------------------------------------------
+// fp32 pools: the same attention on the vector ALUs, in fp32 throughout.  One
+// wavefront per (request, query head, four query rows): lane group r = lane
+// / 16 holds row r, and lane c = lane % 16 holds elements [c E, c E + E) of
+// the row's query, of every key and value it reads and of its output (E = D
+// / 16).  The four rows read the same keys, four at a time (loads first,
+// then the dot products, reduced over the 16 lanes of a row), with an online
+// softmax per row.  Keys past a row's visible range get a zero weight;
+// every row read is a real key of the request (past the wave's last visible
+// key, reads repeat that key), so no NaN of an unused slot enters a sum.
+// ---------------------------------------------------------------------------
+template <int D, int FMT, bool SC>
+__global__ void __launch_bounds__(256) extend_f32_kernel(DevMap m, const float* k_pool, const float* v_pool,
+                                                         int64_t row_elems, const float* __restrict__ q,
+                                                         int64_t total_q, const int32_t* __restrict__ qo_indptr,
+                                                         int32_t Hq, int32_t n_req, int32_t n_qtiles, int32_t G,
+                                                         int32_t causal_all, const int32_t* __restrict__ causal_flags,
+                                                         SoftCap cap, float scale_log2, float* __restrict__ out,
+                                                         float* __restrict__ lse) {
+  constexpr int E = D / 16;
+  constexpr int UK = 4;  // keys per step
+  const int qt = (int)(blockIdx.x % n_qtiles);
+  const int rest = (int)(blockIdx.x / n_qtiles);
+  const int h = rest % Hq, i = rest / Hq;
+  if (i >= n_req) return;
+  const int causal = causal_flags ? (causal_flags[i] != 0) : causal_all;
+  const int q0 = qo_indptr[i];
+  const int n = (q0 < 0 || q0 >= total_q) ? 0 : (int)min((int64_t)(qo_indptr[i + 1] - q0), total_q - q0);
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = lane >> 4, c = lane & 15;
+  const int wrow = qt * 16 + w * 4;  // first row of this wave
+  if (wrow >= n) return;             // uniform per wave
+  int L = m.kv_lens[i];
+  if (FMT == SLOT_CONTIG && m.total_k <= 0) L = 0;
+  if (L < 0) L = 0;
+  const int row = wrow + r;
+  const bool ok = row < n;
+  const int row_end = ok ? (causal ? max(0, min(L, L - n + row + 1)) : L) : 0;
+  int wave_end = row_end;
+  for (int o = 16; o <= 32; o <<= 1) wave_end = max(wave_end, __shfl_xor(wave_end, o, 64));
+  float qv[E];
+  {
+    const float* qp = q + ((int64_t)(q0 + (ok ? row : 0)) * Hq + h) * D + c * E;
+#pragma unroll
+    for (int e = 0; e < E; e += 4) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(qp + e);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) qv[e + k] = ok ? v[k] : 0.f;
+    }
+  }
+  const SlotMap<FMT> sm = make_slotmap<FMT>(m, i);
+  const int g = h / G;
+  const float* kb = k_pool + (int64_t)g * D + c * E;
+  const float* vb = v_pool + (int64_t)g * D + c * E;
+  float m_run = -INFINITY, l_run = 0.f, o[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) o[e] = 0.f;
+  for (int t0 = 0; t0 < wave_end; t0 += UK) {
+    float kv[UK][E], vv[UK][E];
+#pragma unroll
+    for (int u = 0; u < UK; ++u) {
+      const int64_t slot = sm(min(t0 + u, wave_end - 1), true);
+#pragma unroll
+      for (int e = 0; e < E; e += 4) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(kb + slot * row_elems + e);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(vb + slot * row_elems + e);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          kv[u][e + k] = a[k];
+          vv[u][e + k] = b[k];
+        }
+      }
+    }
+    float x[UK];
+    float mx = m_run;
+#pragma unroll
+    for (int u = 0; u < UK; ++u) {
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) d = fmaf(qv[e], kv[u][e], d);
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) d += __shfl_xor(d, off, 64);
+      if constexpr (SC) d = cap(d);
+      x[u] = (t0 + u < row_end) ? d * scale_log2 : -INFINITY;
+      mx = fmaxf(mx, x[u]);
+    }
+    // a row that has seen no key yet keeps m = -inf: use 0 so every weight is 0
+    const float mu = mx == -INFINITY ? 0.f : mx;
+    const float corr = fast_exp2(m_run - mu);
+    l_run *= corr;
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] *= corr;
+#pragma unroll
+    for (int u = 0; u < UK; ++u) {
+      const float p = fast_exp2(x[u] - mu);
+      l_run += p;
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[e] = fmaf(p, vv[u][e], o[e]);
+    }
+    m_run = mx;
+  }
+  if (ok) {
+    const int64_t idx = (int64_t)(q0 + row) * Hq + h;
+    const bool any = l_run > 0.f;
+    const float inv = any ? 1.0f / l_run : 0.f;
+    float* op = out + idx * D + c * E;
+#pragma unroll
+    for (int e = 0; e < E; e += 4) {
+      f32x4 v;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[k] = o[e + k] * inv;
+      *reinterpret_cast<f32x4*>(op + e) = v;
+    }
+    if (lse && c == 0) lse[idx] = any ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 bool extend_supported(const PoolInfo& p, int32_t num_q_heads) {
-  return p.kind == 0 && p.dtype == 1 && p.head_dim_qk == p.head_dim_v &&
+  return p.kind == 0 && (p.dtype == 1 || p.dtype == 0) && p.head_dim_qk == p.head_dim_v &&
          (p.head_dim_qk == 64 || p.head_dim_qk == 128) && num_q_heads % p.num_kv_heads == 0;
+}
+
+template <int D, int FMT>
+static void launch_ext_f32(hipStream_t s, const DevMap& m, const char* kp, const char* vp, int64_t row_elems,
+                           const void* q, int64_t tq, const int32_t* qo, int32_t Hq, int32_t max_q_len, int32_t bs,
+                           int32_t G, int32_t causal, const int32_t* flags, float softcap, float sm_scale, void* out,
+                           float* lse) {
+  const int32_t qtiles = (max_q_len + 15) / 16;  // 16 rows per workgroup (four waves of four)
+  const dim3 grid((unsigned)((int64_t)bs * Hq * qtiles));
+  const float sl2 = sm_scale * kLog2e;
+  const float* k = reinterpret_cast<const float*>(kp);
+  const float* v = reinterpret_cast<const float*>(vp);
+  if (softcap > 0.0f) {
+    const SoftCap cap{2.0f * kLog2e * sm_scale / softcap, softcap / sm_scale};
+    hipLaunchKernelGGL((extend_f32_kernel<D, FMT, true>), grid, dim3(256), 0, s, m, k, v, row_elems,
+                       static_cast<const float*>(q), tq, qo, Hq, bs, qtiles, G, causal, flags, cap, sl2,
+                       static_cast<float*>(out), lse);
+  } else {
+    hipLaunchKernelGGL((extend_f32_kernel<D, FMT, false>), grid, dim3(256), 0, s, m, k, v, row_elems,
+                       static_cast<const float*>(q), tq, qo, Hq, bs, qtiles, G, causal, flags, SoftCap{0.f, 0.f}, sl2,
+                       static_cast<float*>(out), lse);
+  }
+}
+
+template <int D>
+static void launch_ext_f32_fmt(hipStream_t s, const DevMap& m, const char* kp, const char* vp, int64_t row_elems,
+                               const void* q, int64_t tq, const int32_t* qo, int32_t Hq, int32_t max_q_len, int32_t bs,
+                               int32_t G, int32_t causal, const int32_t* flags, float softcap, float sm_scale,
+                               void* out, float* lse) {
+  if (m.fmt == MAP_TOKEN_TABLE)
+    launch_ext_f32<D, SLOT_TABLE>(s, m, kp, vp, row_elems, q, tq, qo, Hq, max_q_len, bs, G, causal, flags, softcap,
+                                  sm_scale, out, lse);
+  else if (m.fmt == MAP_CONTIGUOUS)
+    launch_ext_f32<D, SLOT_CONTIG>(s, m, kp, vp, row_elems, q, tq, qo, Hq, max_q_len, bs, G, causal, flags, softcap,
+                                   sm_scale, out, lse);
+  else
+    launch_ext_f32<D, SLOT_PAGES>(s, m, kp, vp, row_elems, q, tq, qo, Hq, max_q_len, bs, G, causal, flags, softcap,
+                                  sm_scale, out, lse);
 }
 
 template <int D, int FMT>
@@ -444,6 +599,19 @@ hipError_t launch_extend(const PoolInfo& p, int32_t layer, const void* q, int64_
   const char* kp = reinterpret_cast<const char*>(m.fmt == MAP_CONTIGUOUS ? m.contig_k : p.k_layer(layer));
   const char* vp = reinterpret_cast<const char*>(m.fmt == MAP_CONTIGUOUS ? m.contig_v : p.v_layer(layer));
   const int G = Hq / p.num_kv_heads;
+  if (p.dtype == 0) {  // fp32 pool: the vector-ALU kernel
+    const int64_t row_elems = (int64_t)p.num_kv_heads * p.head_dim_qk;
+    timer_before(s);
+    if (p.head_dim_qk == 128)
+      launch_ext_f32_fmt<128>(s, m, kp, vp, row_elems, q, total_q, qo_indptr, Hq, max_q_len, bs, G, causal,
+                              causal_flags, softcap, sm_scale, out, lse);
+    else
+      launch_ext_f32_fmt<64>(s, m, kp, vp, row_elems, q, total_q, qo_indptr, Hq, max_q_len, bs, G, causal,
+                             causal_flags, softcap, sm_scale, out, lse);
+    hipError_t e = hipGetLastError();
+    timer_after(s);
+    return e;
+  }
   // (query tiles, -, requests); the launcher flattens it XCD-aware
   const int bm = p.head_dim_qk == 128 ? ExtendCfg<128>::BM : ExtendCfg<64>::BM;
   const dim3 grid(1, (unsigned)((max_q_len + bm - 1) / bm), (unsigned)bs);

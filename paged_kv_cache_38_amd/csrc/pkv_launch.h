@@ -144,11 +144,37 @@ struct StreamWs {
 };
 size_t stream_ws_layout(int32_t bs, int32_t max_tiles, int32_t runs, int32_t Hq, int32_t Dv, void* base,
                         StreamWs* w);
+// One work item of a shared-prefix pass: members [i0, i1) of one group
+// against tiles [t0, t1) of the prefix keys [0, E), read through member
+// ref's table; its partial results go to chunk slot c.  i0 < 0: no work.
+struct __attribute__((aligned(16))) PrefixItem {
+  int32_t i0, i1, ref, E, t0, t1, c, pad;
+};
+
+// Shared prefixes found by paged_decode_attn itself (share_detect_kernel):
+// per request the keys it shares with its group's reference member (s >= 0),
+// or -1 for the reference, and the group's bounds; the planner turns them
+// into each request's skip and the prefix pass's work items.
+struct ShareArgs {
+  const int32_t* s;   // [bs]: shared keys (a multiple of the tile, or the whole request), -1: reference
+  const int32_t* gs;  // [bs]: first member of the request's group
+  const int32_t* ge;  // [bs]: one past its last member
+  int32_t* skip;      // out [bs]: keys the prefix pass covers (0: none)
+  PrefixItem* items;  // out: the prefix pass's work, group after group in batch order
+  int32_t* count;     // out [1]: items listed
+  int32_t ms;         // members per slice
+  int32_t ch;         // chunks of a group's prefix
+};
+
 // skip (nullable, device int32[bs]): keys left out at the start of each
 // request, a multiple of kStreamT (cascade decode reads them elsewhere).
 // st (nullable): a KV append run by extra blocks of the same launch.
+// share (nullable): shared prefixes found by the decode itself; the planner
+// computes each request's skip from them (and writes it and the prefix
+// pass's work items).
 hipError_t launch_stream_plan(const DevMap& m, int32_t bs, int32_t max_tiles, int32_t runs, const StreamWs& w,
-                              hipStream_t s, const int32_t* skip = nullptr, const StoreArgs* st = nullptr);
+                              hipStream_t s, const int32_t* skip = nullptr, const StoreArgs* st = nullptr,
+                              const ShareArgs* share = nullptr);
 int32_t device_cu_count();
 hipError_t launch_mla_decode(const PoolInfo& p, int32_t layer, const void* q, int32_t num_q_heads, const DevMap& m,
                              int32_t bs, const DecodePlan& plan, float scale_log2, void* out, float* lse, void* ws,

@@ -43,12 +43,58 @@ __device__ __forceinline__ int32_t skip_tiles(const int32_t* skip, int32_t i, in
   return skip ? min(max(skip[i], 0) / kStreamT, T) : 0;
 }
 
+// Keys request k leaves to the prefix pass when the decode found the shared
+// prefixes itself: its own shared keys, or for its group's reference member
+// the most any other member shares (capped at the reference's length,
+// rounded up to the tile).
+__device__ __forceinline__ int32_t share_skip(const ShareArgs& a, const int32_t* kv_lens, int32_t k) {
+  const int32_t s = a.s[k];
+  if (s >= 0) return s;
+  int32_t best = 0;
+  const int32_t g1 = a.ge[k];
+  for (int32_t j = a.gs[k]; j < g1; ++j) best = max(best, a.s[j]);  // the reference's own entry is -1
+  const int32_t L = max(kv_lens[k], 0);
+  return min(best, (L + kStreamT - 1) / kStreamT * kStreamT);
+}
+
+// The prefix pass's work items for the group request k starts (0 when k
+// starts no group, or the group shares nothing): slices of ms members times
+// ch chunks.  *E_out: the prefix keys the group's reference reads.
+__device__ __forceinline__ int32_t group_items(const ShareArgs& a, const int32_t* kv_lens, int32_t k, int32_t* E_out,
+                                               int32_t* ref_out) {
+  *E_out = 0;
+  *ref_out = -1;
+  if (a.gs[k] != k) return 0;
+  const int32_t g1 = a.ge[k];
+  if (g1 - k < 2) return 0;
+  int32_t ref = -1, best = 0;
+  for (int32_t j = k; j < g1; ++j) {
+    const int32_t sj = a.s[j];
+    if (sj < 0) ref = j;
+    else best = max(best, sj);
+  }
+  if (ref < 0) return 0;
+  const int32_t L = max(kv_lens[ref], 0);
+  const int32_t E = min(L, min(best, (L + kStreamT - 1) / kStreamT * kStreamT));
+  *E_out = E;
+  *ref_out = ref;
+  return E > 0 ? (g1 - k + a.ms - 1) / a.ms * a.ch : 0;
+}
+
+// tiles left out at the start of request k (T: its tiles)
+__device__ __forceinline__ int32_t left_out(const int32_t* skip, const ShareArgs& a, const int32_t* kv_lens,
+                                            int32_t k, int32_t T) {
+  if (a.s) return min(share_skip(a, kv_lens, k) / kStreamT, T);
+  return skip_tiles(skip, k, T);
+}
+
 template <int FMT>
 __global__ void __launch_bounds__(256) stream_plan_kernel(DevMap m, int32_t bs, int32_t max_tiles, int32_t runs,
                                                        int32_t* __restrict__ header,
                                                        int32_t* __restrict__ prefix, int32_t* __restrict__ ntiles,
                                                        int32_t* __restrict__ fallback, int32_t* __restrict__ meta,
-                                                       const int32_t* __restrict__ skip, StoreArgs app) {
+                                                       const int32_t* __restrict__ skip, StoreArgs app,
+                                                       ShareArgs share) {
   __shared__ int32_t red[2][4];
   const int i = blockIdx.x, c = blockIdx.y;
   const int tid = threadIdx.x;
@@ -57,14 +103,53 @@ __global__ void __launch_bounds__(256) stream_plan_kernel(DevMap m, int32_t bs, 
     return;
   }
   const int32_t T_all = min(stream_tiles(m.kv_lens[i]), max_tiles);
-  const int32_t st = skip_tiles(skip, i, T_all);  // tiles left out at the start
+  const int32_t st = left_out(skip, share, m.kv_lens, i, T_all);  // tiles left out at the start
   const int32_t T = T_all - st;
   const bool lead = c == 0;
   if (!lead && c * kPlanTiles >= T) return;  // uniform per workgroup
+  if (lead && share.s) {
+    // this request's skip, and the prefix pass's work if a shared group
+    // starts here: slices of ms members times ch chunks of the group's
+    // prefix keys [0, E) (chunks past the prefix's tiles hold no tiles;
+    // their results are empty), listed after the work of every group that
+    // starts earlier in the batch
+    int32_t base = 0;
+    for (int k = tid; k < i; k += 256) {
+      int32_t e, r;
+      base += group_items(share, m.kv_lens, k, &e, &r);
+    }
+    for (int o = 32; o > 0; o >>= 1) base += __shfl_xor(base, o, 64);
+    if ((tid & 63) == 0) red[0][tid >> 6] = base;
+    __syncthreads();
+    base = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+    __syncthreads();  // red is reused by the tile sums below
+    int32_t E, ref;
+    const int32_t cnt = group_items(share, m.kv_lens, i, &E, &ref);
+    if (tid == 0) {
+      share.skip[i] = share_skip(share, m.kv_lens, i);
+      if (i == bs - 1) *share.count = base + cnt;
+    }
+    const int32_t tiles = (E + kStreamT - 1) / kStreamT;
+    const int32_t tpc = (tiles + share.ch - 1) / share.ch;
+    for (int t = tid; t < cnt; t += 256) {
+      const int32_t sl = t / share.ch, ck = t % share.ch;
+      const int32_t i0 = i + sl * share.ms;
+      PrefixItem it;
+      it.i0 = i0;
+      it.i1 = min(share.ge[i], i0 + share.ms);
+      it.ref = ref;
+      it.E = E;
+      it.t0 = min(ck * tpc, tiles);
+      it.t1 = min(ck * tpc + tpc, tiles);
+      it.c = ck;
+      it.pad = 0;
+      share.items[base + t] = it;
+    }
+  }
   int32_t tot = 0, pre = 0;
   for (int k = tid; k < bs; k += 256) {
     const int32_t Tk_all = min(stream_tiles(m.kv_lens[k]), max_tiles);
-    const int32_t Tk = Tk_all - skip_tiles(skip, k, Tk_all);
+    const int32_t Tk = Tk_all - left_out(skip, share, m.kv_lens, k, Tk_all);
     tot += Tk;
     if (k < i) pre += Tk;
   }
@@ -144,17 +229,19 @@ size_t stream_ws_layout(int32_t bs, int32_t max_tiles, int32_t runs, int32_t Hq,
 }
 
 hipError_t launch_stream_plan(const DevMap& m, int32_t bs, int32_t max_tiles, int32_t runs, const StreamWs& w,
-                              hipStream_t s, const int32_t* skip, const StoreArgs* st) {
+                              hipStream_t s, const int32_t* skip, const StoreArgs* st, const ShareArgs* share) {
   StoreArgs a{};
   if (st) a = *st;
+  ShareArgs sh{};
+  if (share) sh = *share;
   const int64_t store_blocks = (a.n + kStoreRowsPerBlock - 1) / kStoreRowsPerBlock;
   const dim3 grid((unsigned)(bs + store_blocks), (unsigned)std::max(1, (max_tiles + kPlanTiles - 1) / kPlanTiles));
   if (m.fmt == MAP_TOKEN_TABLE)
     hipLaunchKernelGGL(stream_plan_kernel<SLOT_TABLE>, grid, dim3(256), 0, s, m, bs, max_tiles, runs, w.header,
-                       w.prefix, w.ntiles, w.fallback, w.meta, skip, a);
+                       w.prefix, w.ntiles, w.fallback, w.meta, skip, a, sh);
   else
     hipLaunchKernelGGL(stream_plan_kernel<SLOT_PAGES>, grid, dim3(256), 0, s, m, bs, max_tiles, runs, w.header,
-                       w.prefix, w.ntiles, w.fallback, w.meta, skip, a);
+                       w.prefix, w.ntiles, w.fallback, w.meta, skip, a, sh);
   return hipGetLastError();
 }
 

@@ -80,13 +80,19 @@ def test_cascade_unaligned_prefix_partial_groups_and_empty_request():
 
 
 def test_cascade_without_groups_equals_decode_bitwise():
-    case = small(64, seed=7)
+    """With no groups the cascade is the split-K decode plus a merge: on a
+    batch where no request shares a page (so paged_decode_attn finds no
+    shared prefix either) the two give the same bits."""
+    lens = np.random.default_rng(7).integers(1, 2000, size=32)
+    case = W.shared_prefix_batch(64, [(0, [(int(L), 0)]) for L in lens], seed=7)
     vals = W.make_values(case)
     dc = DeviceCase(case, vals)
     o1, l1 = dc.decode(P.PKV_MAP_CSR)
     o2, l2 = cascade(dc, P.PKV_MAP_CSR, np.zeros(1, np.int32), np.zeros(0, np.int32), max_group=0)
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(l1, l2)
+    ref_o, _ = oracle_region(case, vals, "self")
+    assert_attn_close(o2, ref_o, "bf16", "cascade without groups")
 
 
 def test_cascade_full_size_prefix_share():

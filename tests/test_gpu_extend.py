@@ -183,3 +183,57 @@ def test_long_causal_prefill_matches_oracle(head_dim):
     ref_o, ref_l = oracle_region(case, vals, "self")
     assert_attn_close(out, ref_o, "bf16", f"long prefill d{head_dim}")
     assert_lse_close(lse, ref_l, "bf16", f"long prefill d{head_dim}")
+
+
+# ---------------------------------------------------------------------------
+# fp32 pools: the vector-ALU extend, against the oracle at the fp32 bound
+# ---------------------------------------------------------------------------
+
+def _f32(case):
+    case.geom.dtype = "f32"
+    return case
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("region", ["self", "cross"])
+def test_extend_f32_matches_oracle(region, fmt):
+    case = _f32(encdec(7))
+    print(f"f32 extend {region} fmt {fmt}", flush=True)
+    vals = W.make_values(case, canary=True)
+    dc = DeviceCase(case, vals)
+    dc.store()
+    out, lse = run_extend(dc, region, fmt)
+    ref_o, ref_l = oracle_region(case, vals, region)
+    assert_attn_close(out, ref_o, "f32", f"f32 {region} fmt {fmt}")
+    assert_lse_close(lse, ref_l, "f32", f"f32 {region} fmt {fmt}")
+
+
+@pytest.mark.parametrize("head_dim", [64, 128])
+@pytest.mark.parametrize("group", [1, 4])
+def test_extend_f32_head_dims_gqa_softcap_and_ragged(head_dim, group):
+    case = _f32(encdec(8, num_heads=4, head_dim=head_dim, bs=3, enc_len=200, new_range=(1, 130)))
+    case.geom.num_q_heads = case.geom.num_kv_heads * group
+    vals = W.make_values(case, canary=True)
+    dc = DeviceCase(case, vals)
+    dc.store()
+    for region in ("self", "cross"):
+        out, lse = run_extend(dc, region, P.PKV_MAP_CSR)
+        ref_o, ref_l = oracle_region(case, vals, region)
+        assert_attn_close(out, ref_o, "f32", f"f32 D{head_dim} G{group} {region}")
+        assert_lse_close(lse, ref_l, "f32", f"f32 D{head_dim} G{group} {region}")
+        ragged = run_extend(dc, region, P.PKV_MAP_TOKEN_TABLE, contiguous=True)
+        assert torch.equal(out.view(torch.int32), ragged[0].view(torch.int32))
+        assert torch.equal(lse, ragged[1])
+        capped, _ = run_extend(dc, region, P.PKV_MAP_CSR, softcap=5.0)
+        ref_c, _ = oracle_region(case, vals, region, softcap=5.0)
+        assert_attn_close(capped, ref_c, "f32", f"f32 D{head_dim} G{group} {region} softcap 5")
+
+
+def test_extend_f32_empty_encoder_gives_zeros():
+    case = _f32(encdec(0, enc_len=0, prefix_range=(0, 20), new_range=(1, 40)))
+    vals = W.make_values(case)
+    dc = DeviceCase(case, vals)
+    dc.store()
+    for fmt in FMTS:
+        out, lse = run_extend(dc, "cross", fmt)
+        assert (out == 0).all() and torch.isneginf(lse).all()

@@ -150,3 +150,21 @@ def test_mixed_spans_full_size(softcap):
     ref_o, ref_l = oracle_region(case, vals, "self", pk, pv, softcap=softcap)
     assert_attn_close(out, ref_o, "bf16", f"mixed spans full size, cap {softcap}")
     assert_lse_close(lse, ref_l, "bf16", f"mixed spans full size, cap {softcap}")
+
+
+def test_extend_full_size_f32():
+    """The encoder-decoder extend at full size in fp32 (the vector-ALU
+    kernel), every request against the oracle at 1e-5 + 1e-5 |o|: a dropped
+    or repeated key tile moves an fp32 output far more than that."""
+    case = W.encdec_extend(seed=0)
+    case.geom.dtype = "f32"
+    print(f"full-size encoder-decoder extend, fp32: bs {case.bs}, sum n {int(case.q_lens.sum())}", flush=True)
+    vals = W.make_values(case, device="cuda")
+    dc = DeviceCase(case, vals)
+    dc.store()
+    pk, pv = oracle_after_store(case, vals)
+    for name in ("self", "cross"):
+        out, lse = run_extend(dc, name, P.PKV_MAP_CSR)
+        ref_o, ref_l = oracle_region(case, vals, name, pk, pv)
+        assert_attn_close(out, ref_o, "f32", f"extend {name} f32")
+        assert_lse_close(lse, ref_l, "f32", f"extend {name} f32")

@@ -13,6 +13,7 @@ from .cases import (  # noqa: F401
     mla_decode,
     encdec_extend,
     mixed_spans,
+    shared_prefix_batch,
     make_values,
     to_numpy_bits,
     CONFIG_BUILDERS,

@@ -430,6 +430,66 @@ def mixed_spans(seed: int = 0, rows: int = 4, spans=((128, True), (2048, False))
     )
 
 
+def shared_prefix_batch(page_size: int, groups, seed: int = 0, num_q_heads: int = 32, num_kv_heads: int = 8,
+                        head_dim: int = 128, dtype: str = "bf16") -> Case:
+    """A decode batch with hand-placed prefix sharing, for structural tests.
+
+    ``groups`` lists consecutive runs of requests; each is ``(prefix_pages,
+    members)`` with ``members`` a list of ``(L, shared_pages)``: the member
+    has ``L`` keys, of which the first ``min(L, shared_pages * page_size)``
+    sit on the group's first ``shared_pages`` prefix pages (``shared_pages
+    <= prefix_pages``) and the rest on private pages.  A group of one member
+    with ``shared_pages = 0`` is a private request.  Pages come from a
+    seeded permutation of a pool 1.2x the pages needed; attention only (no
+    store)."""
+    rs, rp, vseed, qseed = _streams(7, seed, (page_size, len(groups)))
+    ps = page_size
+    lens, need = [], 0
+    for prefix_pages, members in groups:
+        need += prefix_pages
+        for L, sh in members:
+            assert sh <= prefix_pages
+            lens.append(int(L))
+            need += _cdiv(max(int(L) - sh * ps, 0), ps)
+    lens = np.asarray(lens, np.int32)
+    bs = len(lens)
+    num_pages = _cdiv(max(need, 1) * 12, 10)
+    geom = Geometry(dtype, ps, num_pages, num_kv_heads, head_dim, head_dim, False, num_q_heads)
+    perm = rp.permutation(num_pages)
+    width = _round32(int(lens.max(initial=1)))
+    table = _new_table(bs + 1, width, geom)
+    rpi = rs.permutation(bs).astype(np.int32)
+    pos, i, page_lists = 0, 0, []
+    for prefix_pages, members in groups:
+        shared = perm[pos:pos + prefix_pages].astype(np.int64)
+        pos += prefix_pages
+        for L, sh in members:
+            L = int(L)
+            n_sh = min(_cdiv(L, ps), sh)
+            own_n = _cdiv(max(L - sh * ps, 0), ps)
+            own = perm[pos:pos + own_n].astype(np.int64)
+            pos += own_n
+            pages = np.concatenate([shared[:n_sh], own])
+            page_lists.append(pages)
+            if L:
+                table[rpi[i], :L] = _expand(pages, ps, L)
+            i += 1
+    # unread slots: on each page, those past the last offset any request reads
+    used = {}
+    for pages, L in zip(page_lists, lens.tolist()):
+        for k, pg in enumerate(pages.tolist()):
+            used[pg] = max(used.get(pg, 0), min(ps, L - k * ps))
+    tails = [pg * ps + np.arange(u, ps, dtype=np.int64) for pg, u in used.items() if u < ps]
+    region = Region(np.zeros(bs, np.int32), lens, page_lists, causal=True)
+    return Case(
+        name=f"shared_prefix_batch_ps{ps}", geom=geom, bs=bs, req_to_token=table, req_pool_indices=rpi,
+        q_lens=np.ones(bs, np.int32), regions={"self": region}, out_loc=np.zeros(0, np.int32),
+        sm_scale=1.0 / np.sqrt(float(head_dim)), value_scale=1.0, value_seed=vseed, query_seed=qseed,
+        free_pages=perm[pos:].astype(np.int64),
+        tail_slots=np.concatenate(tails) if tails else np.zeros(0, np.int64),
+    )
+
+
 CONFIG_BUILDERS = {
     1: tiny_decode,
     2: qwen3_decode,
