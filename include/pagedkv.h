@@ -230,6 +230,22 @@ int paged_decode_attn(const pkv_pool* pool, int32_t layer, const void* q, int32_
                       const pkv_kv_map* map, float sm_scale, void* out, float* lse, void* workspace,
                       size_t ws_bytes, void* stream);
 
+/* paged_decode_attn for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation and kernels, with the workspace taken
+ * from a device array the library holds (128 MiB per device, kept until the
+ * process ends) instead of a caller's buffer.  The caller still passes q,
+ * out and lse as for paged_decode_attn.
+ *   Returns PKV_ECAPACITY, before touching the device, when this batch
+ *   shape needs more workspace than the array holds
+ *   (paged_decode_workspace_bytes() > 128 MiB); use paged_decode_attn with
+ *   a workspace then.
+ *   Every call on one device shares that device's array: calls that overlap
+ *   on one device (two streams, two threads) race and must be ordered by
+ *   the caller.  Allocates nothing and issues no memset. */
+int paged_decode_attn_noalloc(const pkv_pool* pool, int32_t layer, const void* q, int32_t num_q_heads,
+                              const pkv_kv_map* map, float sm_scale, void* out, float* lse, void* stream);
+
 /* paged_decode_attn with the step's KV append in the same call ([MINI]
  * "The KV pool: one preallocated block of memory": the attention backend
  * stores the step's new K/V by out_loc before it computes attention).  The

@@ -36,7 +36,7 @@ from ._lib import (  # noqa: F401
 __all__ = [
     "Pool", "KVMap", "kv_pool_bytes", "kv_pool_create", "kv_pool_destroy", "kv_pool_padding_page",
     "kv_pool_token_bytes", "kv_store", "build_kv_indices", "make_kv_map", "paged_decode_workspace_bytes",
-    "paged_decode_attn", "PrefixGroups", "make_prefix_groups", "paged_decode_cascade_workspace_bytes",
+    "paged_decode_attn", "paged_decode_attn_noalloc", "PrefixGroups", "make_prefix_groups", "paged_decode_cascade_workspace_bytes",
     "paged_decode_attn_cascade", "paged_decode_attn_append", "paged_verify_attn", "paged_verify_attn_append", "paged_extend_attn", "paged_extend_attn_ex", "kv_gather",
     "kv_validate",
     "pkv_set_kernel_timer", "library",
@@ -285,6 +285,17 @@ def paged_decode_attn(pool: Pool, layer: int, q: torch.Tensor, kv_map: KVMap, sm
                                        C.byref(kv_map.struct), float(sm_scale), _dev(out, "out", pool.dtype),
                                        _dev(lse, "lse", torch.float32), ws_ptr, ws_bytes, _stream(stream)),
             "paged_decode_attn")
+
+
+def paged_decode_attn_noalloc(pool: Pool, layer: int, q: torch.Tensor, kv_map: KVMap, sm_scale: float,
+                              out: torch.Tensor, lse: Optional[torch.Tensor] = None, stream=None) -> None:
+    """paged_decode_attn with its workspace in the library's own device
+    array (no allocation; calls overlapping on one device race)."""
+    _check_attn(pool, q, out, lse, (kv_map.bs,), "paged_decode_attn_noalloc")
+    L.check(L.load().paged_decode_attn_noalloc(pool.handle, layer, _dev(q, "q", pool.dtype), q.shape[1],
+                                               C.byref(kv_map.struct), float(sm_scale), _dev(out, "out", pool.dtype),
+                                               _dev(lse, "lse", torch.float32), _stream(stream)),
+            "paged_decode_attn_noalloc")
 
 
 def paged_decode_attn_append(pool: Pool, layer: int, q: torch.Tensor, kv_map: KVMap, k_new: torch.Tensor,

@@ -106,6 +106,8 @@ SIGNATURES = {
                                                C.POINTER(C.c_size_t)]),
     "paged_decode_attn": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.POINTER(KVMapStruct), C.c_float,
                                     C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "paged_decode_attn_noalloc": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.POINTER(KVMapStruct),
+                                            C.c_float, C.c_void_p, C.c_void_p, C.c_void_p]),
     "paged_decode_attn_append": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.POINTER(KVMapStruct),
                                            C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.c_float, C.c_void_p,
                                            C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),

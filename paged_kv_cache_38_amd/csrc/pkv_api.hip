@@ -5,7 +5,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <cmath>
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -172,6 +174,51 @@ int make_devmap(const pkv_pool* pool, const pkv_kv_map* m, bool allow_contiguous
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------------------
+// paged_decode_attn without a workspace argument, for callers that cannot
+// allocate device memory.  The decode workspace (split plan, tile slot
+// lists, partial results) lives in this file-scope device array, one copy
+// per device, held until the process ends.  Host code never uses the
+// array's name as an address: its device address is looked up once per
+// device with hipGetSymbolAddress and kept.  Every call on a device shares
+// that device's copy: calls that overlap on one device race.  Nothing in the
+// workspace has to start at zero (each launch's planner writes everything
+// its main kernel and merge read), so no call clears it.
+// ---------------------------------------------------------------------------
+constexpr size_t kNoAllocScratchBytes = size_t(128) << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<char*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device (looked up on the first
+// call per device, with that device current).
+int scratch_for_current_device(char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(PKV_EUNSUPPORTED, "device %d past %d", dev, kMaxDevices);
+  char* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      void* a = nullptr;
+      e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return device_status(e, "hipGetSymbolAddress(scratch)");
+      if (!a) return fail(PKV_EDEVICE, "hipGetSymbolAddress(scratch) returned a null address");
+      p = static_cast<char*>(a);
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return PKV_OK;
+}
+}  // namespace
+
 
 namespace pkv {
 void timer_before(hipStream_t s) {
@@ -367,6 +414,29 @@ int paged_decode_attn(const pkv_pool* pool, int32_t layer, const void* q, int32_
   pkv::StoreArgs none{};
   return decode_call(pool, layer, q, num_q_heads, map, sm_scale, out, lse, workspace, ws_bytes, stream, none,
                      "paged_decode_attn");
+}
+
+int paged_decode_attn_noalloc(const pkv_pool* pool, int32_t layer, const void* q, int32_t num_q_heads,
+                              const pkv_kv_map* map, float sm_scale, void* out, float* lse, void* stream) {
+  if (int st = check_pool(pool)) return st;
+  if (int st = check_layer(pool, layer)) return st;
+  if (!map) return fail(PKV_EINVAL, "null map");
+  // the size is checked before any device call, so an oversized batch is
+  // rejected the same way with or without a device
+  if (num_q_heads > 0 && map->bs >= 0 && map->max_kv_len >= 0 && pkv::decode_supported(pool->info, num_q_heads)) {
+    const pkv::DecodePlan plan = pkv::plan_decode(pool->info, map->bs, num_q_heads, map->max_kv_len);
+    const size_t need = pkv::decode_workspace_bytes(pool->info, plan, map->bs, num_q_heads);
+    if (need > kNoAllocScratchBytes)
+      return fail(PKV_ECAPACITY, "this decode needs %zu bytes of workspace; paged_decode_attn_noalloc holds %zu "
+                                 "(pass a workspace to paged_decode_attn instead)",
+                  need, kNoAllocScratchBytes);
+  }
+  char* ws = nullptr;
+  if (map->bs > 0)
+    if (int st = scratch_for_current_device(&ws)) return st;
+  pkv::StoreArgs none{};
+  return decode_call(pool, layer, q, num_q_heads, map, sm_scale, out, lse, ws, kNoAllocScratchBytes, stream, none,
+                     "paged_decode_attn_noalloc");
 }
 
 namespace {

@@ -430,3 +430,24 @@ def test_binding_rejects_short_or_misshapen_tensors():
     with pytest.raises(ValueError, match="k_new must be"):
         P.paged_verify_attn_append(lp, 0, qv, m, torch.zeros(6, 1, 512, dtype=bf), torch.zeros(6, dtype=torch.int32),
                                    0.1, torch.zeros(3, 2, 16, 512, dtype=bf))
+
+
+def test_noalloc_decode_rejects_past_its_array_before_any_device_call(lib):
+    """paged_decode_attn_noalloc refuses a batch whose workspace would not fit
+    the library's device array (128 MiB) with PKV_ECAPACITY, before it
+    touches the device (so this runs without one)."""
+    st, h = make_pool(lib, desc(num_layers=1, num_pages=1000, page_size=64, num_kv_heads=1, head_dim_qk=576,
+                                head_dim_v=512, dtype=1, kind=1), v=None)
+    assert st == 0
+    try:
+        m = L.KVMapStruct()
+        m.fmt, m.bs, m.kv_lens, m.max_kv_len = L.PKV_MAP_BLOCK_TABLE, 4096, 0x1000, 65536
+        m.block_table, m.block_stride = 0x2000, 1024
+        need = C.c_size_t()
+        assert lib.paged_decode_workspace_bytes(h, 4096, 128, 65536, C.byref(need)) == 0
+        assert need.value > (128 << 20)
+        assert lib.paged_decode_attn_noalloc(h, 0, 0x3000, 128, C.byref(m), 0.05, 0x4000, None, None) == \
+            L.PKV_ECAPACITY
+        assert b"workspace" in lib.pkv_last_error()
+    finally:
+        lib.kv_pool_destroy(h)
