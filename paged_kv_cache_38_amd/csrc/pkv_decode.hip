@@ -222,31 +222,29 @@ struct StreamSet {
   int32_t mv;  // planner word of lane l
 };
 
+// One run of the stream, by workgroup `bid` (vt: this wave's V tile in LDS).
 template <int D, int WAVES, int NS>
-__global__ void __launch_bounds__(64 * WAVES, NS <= 2 ? 8 / WAVES : 4 / WAVES) decode_stream_kernel(
-    const bf16* k_pool, const bf16* v_pool, const bf16* __restrict__ q, int32_t Hq, int32_t Hkv, int32_t G,
-    int32_t hg, const int32_t* __restrict__ header, const int32_t* __restrict__ meta, float scale_log2,
+__device__ __forceinline__ void stream_run(
+    int bid, bf16* vt, const bf16* k_pool, const bf16* v_pool, const bf16* __restrict__ q, int32_t Hq, int32_t Hkv,
+    int32_t G, int32_t hg, const int32_t* __restrict__ header, const int32_t* __restrict__ meta, float scale_log2,
     bf16* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws_o, float* __restrict__ ws_lse,
     int32_t pieces_only, const int32_t* __restrict__ prefix_skip) {
   constexpr int NK = D / 32;
   constexpr int NT = D / 16;
-  constexpr int LDS = D + 8;
-  __shared__ __attribute__((aligned(16))) bf16 vsm[WAVES][kTile * LDS];
 
   // the hg workgroups of a run sit on one XCD (dispatch goes round robin
   // over the 8 XCDs), so the halves of a slot's row meet in one L2
-  const int run = (blockIdx.x / (8 * hg)) * 8 + blockIdx.x % 8;
+  const int run = (bid / (8 * hg)) * 8 + bid % 8;
   const int Bt = header[0], total = header[1];
   const int G0 = run * Bt;
   if (G0 >= total) return;
   const int n = min(Bt, total - G0);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
-  const int g = ((blockIdx.x / 8) % hg) * WAVES + wave;
+  const int g = ((bid / 8) % hg) * WAVES + wave;
   const int64_t row_elems = (int64_t)Hkv * D;
   const bf16* kb = k_pool + (int64_t)g * D;
   const bf16* vb = v_pool + (int64_t)g * D;
-  bf16* vt = vsm[wave];
   const bool qok = col < G;
 
   auto meta_word = [&](int r) -> int32_t {
@@ -336,6 +334,17 @@ __global__ void __launch_bounds__(64 * WAVES, NS <= 2 ? 8 / WAVES : 4 / WAVES) d
       }
     }
   }
+}
+
+template <int D, int WAVES, int NS>
+__global__ void __launch_bounds__(64 * WAVES, NS <= 2 ? 8 / WAVES : 4 / WAVES) decode_stream_kernel(
+    const bf16* k_pool, const bf16* v_pool, const bf16* __restrict__ q, int32_t Hq, int32_t Hkv, int32_t G,
+    int32_t hg, const int32_t* __restrict__ header, const int32_t* __restrict__ meta, float scale_log2,
+    bf16* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws_o, float* __restrict__ ws_lse,
+    int32_t pieces_only) {
+  __shared__ __attribute__((aligned(16))) bf16 vsm[WAVES][kTile * (D + 8)];
+  stream_run<D, WAVES, NS>((int)blockIdx.x, vsm[threadIdx.x >> 6], k_pool, v_pool, q, Hq, Hkv, G, hg, header, meta,
+                           scale_log2, out, lse, ws_o, ws_lse, pieces_only, nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -463,13 +472,13 @@ __device__ __forceinline__ void cascade_prefix_work(const DevMap& m, const bf16*
                                                     int32_t Hkv, int32_t G, int i0, int i1, int rd, int S,
                                                     const int32_t* lim_arr, int E, int t_begin, int t_end, int c,
                                                     int ms, float scale_log2, float* __restrict__ ws_po,
-                                                    float* __restrict__ ws_plse, bf16* vt) {
+                                                    float* __restrict__ ws_plse, bf16* vt, int bid) {
   constexpr int NK = D / 32;
   constexpr int NT = D / 16;
   constexpr int NB = kCascadeCols / 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
-  const int h = ((blockIdx.x / 8) % (Hkv / W)) * W + wave;  // KV head
+  const int h = ((bid / 8) % (Hkv / W)) * W + wave;  // KV head
 
   // rows: column cc of block b is member i0 + cc / G, query head h G + cc % G
   bf16x8 qb[NB][NK];
@@ -576,26 +585,36 @@ __global__ void __launch_bounds__(64 * W) cascade_prefix_kernel(
   const int E = min(S, Lmax);  // prefix keys any member sees
   const int t_begin = c * tpc, t_end = min(t_begin + tpc, (E + kTile - 1) / kTile);
   cascade_prefix_work<D, W, FMT>(m, k_pool, v_pool, q, bs, Hq, Hkv, G, i0, i1, rd, S, nullptr, E, t_begin, t_end, c,
-                                 ms, scale_log2, ws_po, ws_plse, vsm[threadIdx.x >> 6]);
+                                 ms, scale_log2, ws_po, ws_plse, vsm[threadIdx.x >> 6], (int)blockIdx.x);
 }
 
-// Shared-prefix kernel for the groups paged_decode_attn finds itself: the
-// planner lists the work items (*count of them); a fixed grid strides over
-// them.
-template <int D, int W, int FMT>
-__global__ void __launch_bounds__(64 * W) share_prefix_kernel(
-    DevMap m, const bf16* k_pool, const bf16* v_pool, const bf16* __restrict__ q, int32_t bs, int32_t Hq,
-    int32_t Hkv, int32_t G, int32_t hg, const PrefixItem* __restrict__ items, const int32_t* __restrict__ count,
-    const int32_t* __restrict__ lim_arr, int32_t ms, float scale_log2, float* __restrict__ ws_po,
-    float* __restrict__ ws_plse) {
-  constexpr int LDS = D + 8;
-  __shared__ __attribute__((aligned(16))) bf16 vsm[W][kTile * LDS];
-  const int works = (int)gridDim.x / hg;  // a multiple of 8
+// The bf16 decode's main launch: workgroups [0, n_stream) stream the runs
+// of every request's own keys; the rest take the work items the planner
+// listed for the shared prefixes paged_decode_attn found (*count of them),
+// striding over them.  One launch, so the prefix work starts on each CU as
+// soon as its run is done, and a batch without shared prefixes pays no
+// second launch.
+template <int D, int WAVES, int NS, int FMT>
+__global__ void __launch_bounds__(64 * WAVES, NS <= 2 ? 8 / WAVES : 4 / WAVES) decode_share_kernel(
+    const bf16* k_pool, const bf16* v_pool, const bf16* __restrict__ q, int32_t Hq, int32_t Hkv, int32_t G,
+    int32_t hg, const int32_t* __restrict__ header, const int32_t* __restrict__ meta, float scale_log2,
+    bf16* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws_o, float* __restrict__ ws_lse,
+    int32_t n_stream, DevMap m, int32_t bs, const PrefixItem* __restrict__ items, const int32_t* __restrict__ count,
+    const int32_t* __restrict__ skip, int32_t ms, float* __restrict__ ws_po, float* __restrict__ ws_plse) {
+  __shared__ __attribute__((aligned(16))) bf16 vsm[WAVES][kTile * (D + 8)];
+  bf16* vt = vsm[threadIdx.x >> 6];
+  if ((int)blockIdx.x < n_stream) {
+    stream_run<D, WAVES, NS>((int)blockIdx.x, vt, k_pool, v_pool, q, Hq, Hkv, G, hg, header, meta, scale_log2, out,
+                             lse, ws_o, ws_lse, 0, skip);
+    return;
+  }
+  const int b = (int)blockIdx.x - n_stream;  // n_stream is a multiple of 8: b keeps the XCD of blockIdx
+  const int works = ((int)gridDim.x - n_stream) / hg;
   const int n_items = *count;
-  for (int w = (blockIdx.x / (8 * hg)) * 8 + blockIdx.x % 8; w < n_items; w += works) {
+  for (int w = (b / (8 * hg)) * 8 + b % 8; w < n_items; w += works) {
     const PrefixItem it = items[w];
-    cascade_prefix_work<D, W, FMT>(m, k_pool, v_pool, q, bs, Hq, Hkv, G, it.i0, it.i1, it.ref, 0, lim_arr, it.E,
-                                   it.t0, it.t1, it.c, ms, scale_log2, ws_po, ws_plse, vsm[threadIdx.x >> 6]);
+    cascade_prefix_work<D, WAVES, FMT>(m, k_pool, v_pool, q, bs, Hq, Hkv, G, it.i0, it.i1, it.ref, 0, skip, it.E,
+                                       it.t0, it.t1, it.c, ms, scale_log2, ws_po, ws_plse, vt, b);
   }
 }
 
@@ -1084,29 +1103,41 @@ static void launch_valu(unsigned blocks, hipStream_t s, const DevMap& m, const P
 template <int D, int W>
 static void launch_stream_main(int32_t runs, int32_t hg, hipStream_t s, const PoolInfo& p, int32_t layer,
                                const void* q, int32_t Hq, int32_t G, const StreamWs& w, float sl2, void* out,
-                               float* lse, int32_t pieces_only = 0, const int32_t* prefix_skip = nullptr) {
+                               float* lse, int32_t pieces_only = 0) {
   hipLaunchKernelGGL((decode_stream_kernel<D, W, kStreamSets>), dim3((unsigned)(runs * hg)), dim3(64 * W), 0, s,
                      reinterpret_cast<const bf16*>(p.k_layer(layer)), reinterpret_cast<const bf16*>(p.v_layer(layer)),
                      static_cast<const bf16*>(q), Hq, p.num_kv_heads, G, hg, w.header, w.meta, sl2,
-                     static_cast<bf16*>(out), lse, w.o, w.lse, pieces_only, prefix_skip);
+                     static_cast<bf16*>(out), lse, w.o, w.lse, pieces_only);
+}
+
+template <int D, int W, int FMT>
+static void launch_share_main(int32_t runs, int32_t hg, hipStream_t s, const PoolInfo& p, int32_t layer,
+                              const DevMap& m, const void* q, int32_t bs, int32_t Hq, int32_t G, const StreamWs& w,
+                              const ShareWs& sh, float sl2, void* out, float* lse) {
+  // the prefix work: at most bs * kShareChunks items, one work per CU covers the usual count
+  const int64_t works = (std::min<int64_t>((int64_t)bs * kShareChunks, device_cu_count()) + 7) / 8 * 8;
+  const int32_t n_stream = runs * hg;
+  hipLaunchKernelGGL((decode_share_kernel<D, W, kStreamSets, FMT>), dim3((unsigned)(n_stream + works * hg)),
+                     dim3(64 * W), 0, s, reinterpret_cast<const bf16*>(p.k_layer(layer)),
+                     reinterpret_cast<const bf16*>(p.v_layer(layer)), static_cast<const bf16*>(q), Hq, p.num_kv_heads,
+                     G, hg, w.header, w.meta, sl2, static_cast<bf16*>(out), lse, w.o, w.lse, n_stream, m, bs, sh.items,
+                     sh.count, sh.skip, sh.ms, sh.po, sh.plse);
 }
 
 template <int D, int W>
-static void launch_share_prefix(const PoolInfo& p, int32_t layer, const DevMap& m, const void* q, int32_t bs,
-                                int32_t Hq, int32_t G, int32_t hg, const ShareWs& sh, float sl2, hipStream_t s) {
-  // at most bs * kShareChunks items; one work per CU covers the usual count
-  const int64_t works = (std::min<int64_t>((int64_t)bs * kShareChunks, device_cu_count()) + 7) / 8 * 8;
-  auto kern = (m.fmt == MAP_TOKEN_TABLE) ? share_prefix_kernel<D, W, SLOT_TABLE> : share_prefix_kernel<D, W, SLOT_PAGES>;
-  hipLaunchKernelGGL(kern, dim3((unsigned)(works * hg)), dim3(64 * W), 0, s, m,
-                     reinterpret_cast<const bf16*>(p.k_layer(layer)), reinterpret_cast<const bf16*>(p.v_layer(layer)),
-                     static_cast<const bf16*>(q), bs, Hq, p.num_kv_heads, G, hg, sh.items, sh.count, sh.skip, sh.ms,
-                     sl2, sh.po, sh.plse);
+static void launch_share_main_fmt(int32_t runs, int32_t hg, hipStream_t s, const PoolInfo& p, int32_t layer,
+                                  const DevMap& m, const void* q, int32_t bs, int32_t Hq, int32_t G,
+                                  const StreamWs& w, const ShareWs& sh, float sl2, void* out, float* lse) {
+  if (m.fmt == MAP_TOKEN_TABLE)
+    launch_share_main<D, W, SLOT_TABLE>(runs, hg, s, p, layer, m, q, bs, Hq, G, w, sh, sl2, out, lse);
+  else
+    launch_share_main<D, W, SLOT_PAGES>(runs, hg, s, p, layer, m, q, bs, Hq, G, w, sh, sl2, out, lse);
 }
 
 // The bf16 decode: find shared prefixes (share_detect_kernel), plan the
 // stream of every request's own tiles (the append, if any, rides in the
-// planner launch), stream them, read each group's shared prefix once
-// (share_prefix_kernel), then merge pieces and prefix chunks.  Without
+// planner launch), stream them and read each group's shared prefix once
+// (decode_share_kernel), then merge pieces and prefix chunks.  Without
 // shared prefixes the prefix pass finds no work and every request one run
 // finishes is written by the stream kernel directly.
 static hipError_t launch_stream_decode(const PoolInfo& p, int32_t layer, const void* q, int32_t Hq, const DevMap& m,
@@ -1141,19 +1172,13 @@ static hipError_t launch_stream_decode(const PoolInfo& p, int32_t layer, const v
   const int D = p.head_dim_qk;
   timer_before(s);
   if (D == 128) {
-    if (W == 4) launch_stream_main<128, 4>(runs, hg, s, p, layer, q, Hq, G, w, sl2, out, lse, 0, sh.skip);
-    else if (W == 2) launch_stream_main<128, 2>(runs, hg, s, p, layer, q, Hq, G, w, sl2, out, lse, 0, sh.skip);
-    else launch_stream_main<128, 1>(runs, hg, s, p, layer, q, Hq, G, w, sl2, out, lse, 0, sh.skip);
-    if (W == 4) launch_share_prefix<128, 4>(p, layer, m, q, bs, Hq, G, hg, sh, sl2, s);
-    else if (W == 2) launch_share_prefix<128, 2>(p, layer, m, q, bs, Hq, G, hg, sh, sl2, s);
-    else launch_share_prefix<128, 1>(p, layer, m, q, bs, Hq, G, hg, sh, sl2, s);
+    if (W == 4) launch_share_main_fmt<128, 4>(runs, hg, s, p, layer, m, q, bs, Hq, G, w, sh, sl2, out, lse);
+    else if (W == 2) launch_share_main_fmt<128, 2>(runs, hg, s, p, layer, m, q, bs, Hq, G, w, sh, sl2, out, lse);
+    else launch_share_main_fmt<128, 1>(runs, hg, s, p, layer, m, q, bs, Hq, G, w, sh, sl2, out, lse);
   } else {
-    if (W == 4) launch_stream_main<64, 4>(runs, hg, s, p, layer, q, Hq, G, w, sl2, out, lse, 0, sh.skip);
-    else if (W == 2) launch_stream_main<64, 2>(runs, hg, s, p, layer, q, Hq, G, w, sl2, out, lse, 0, sh.skip);
-    else launch_stream_main<64, 1>(runs, hg, s, p, layer, q, Hq, G, w, sl2, out, lse, 0, sh.skip);
-    if (W == 4) launch_share_prefix<64, 4>(p, layer, m, q, bs, Hq, G, hg, sh, sl2, s);
-    else if (W == 2) launch_share_prefix<64, 2>(p, layer, m, q, bs, Hq, G, hg, sh, sl2, s);
-    else launch_share_prefix<64, 1>(p, layer, m, q, bs, Hq, G, hg, sh, sl2, s);
+    if (W == 4) launch_share_main_fmt<64, 4>(runs, hg, s, p, layer, m, q, bs, Hq, G, w, sh, sl2, out, lse);
+    else if (W == 2) launch_share_main_fmt<64, 2>(runs, hg, s, p, layer, m, q, bs, Hq, G, w, sh, sl2, out, lse);
+    else launch_share_main_fmt<64, 1>(runs, hg, s, p, layer, m, q, bs, Hq, G, w, sh, sl2, out, lse);
   }
   e = hipGetLastError();
   timer_after(s);
