@@ -101,12 +101,17 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(DevMap m, const char* k_
 
   // blocks are dealt to the 8 XCDs round robin (block b on XCD b % 8).  The
   // (request, head) pairs are spread over the XCDs round robin too (pair p
-  // on XCD p % 8), so every request's work is split evenly across them,
-  // and all query tiles of one pair run back to back on one XCD, sharing
-  // its L2: each key/value tile leaves HBM once.
+  // on XCD p % 8), so every request's work is split evenly across them.
+  // Non-causal calls run all query tiles of one pair back to back on one
+  // XCD, sharing its L2, so each key/value tile leaves HBM once.  Causal
+  // calls go by query tile, last tiles first: a later tile sees more keys,
+  // so the longest blocks start first and the short ones fill the tail
+  // (the tiles of one pair still share an XCD; a causal region is short).
   const int x = (int)(blockIdx.x & 7), k = (int)(blockIdx.x >> 3);
-  const int pair = x + 8 * (k / n_qtiles);
-  const int qt = k % n_qtiles;
+  const int ppx = (int)(((int64_t)n_req * Hq + 7) / 8);  // pairs per XCD
+  const bool qt_major = causal_all && !causal_flags;
+  const int pair = x + 8 * (qt_major ? k % ppx : k / n_qtiles);
+  const int qt = qt_major ? n_qtiles - 1 - k / ppx : k % n_qtiles;
   const int h = pair % Hq;
   const int i = pair / Hq;
   if (i >= n_req) return;
