@@ -741,10 +741,26 @@ __global__ void __launch_bounds__(256) cascade_merge_kernel(int32_t bs, int32_t 
     return ws_plse[row];
   };
   const int n = (b1 - b0 + 1) + nc;
-  // the sources' lse loads are independent: issue them together
+  // the first KB sources' lse and partial rows are all loaded at once (they
+  // are independent); a request with more sources takes the rest in a loop
+  constexpr int KB = 8;
+  float lb[KB], ob[KB][E];
+#pragma unroll
+  for (int k = 0; k < KB; ++k) {
+    lb[k] = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < E; ++e) ob[k][e] = 0.f;
+    if (k < n) {
+      const float* o;
+      lb[k] = piece(k, o);
+#pragma unroll
+      for (int e = 0; e < E; ++e) ob[k][e] = o[lane * E + e];
+    }
+  }
   float mx = -INFINITY;
-#pragma unroll 8
-  for (int k = 0; k < n; ++k) {
+#pragma unroll
+  for (int k = 0; k < KB; ++k) mx = fmaxf(mx, lb[k]);
+  for (int k = KB; k < n; ++k) {
     const float* o;
     mx = fmaxf(mx, piece(k, o));
   }
@@ -759,8 +775,15 @@ __global__ void __launch_bounds__(256) cascade_merge_kernel(int32_t bs, int32_t 
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
   float sum = 0.f;
-#pragma unroll 8
-  for (int k = 0; k < n; ++k) {
+  // sources without keys (lse = -inf) weigh 0 and their rows are finite
+#pragma unroll
+  for (int k = 0; k < KB; ++k) {
+    const float wgt = lb[k] == -INFINITY ? 0.f : __expf(lb[k] - mx);
+    sum += wgt;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = fmaf(wgt, ob[k][e], acc[e]);
+  }
+  for (int k = KB; k < n; ++k) {
     const float* o;
     const float l = piece(k, o);
     if (l == -INFINITY) continue;

@@ -103,10 +103,11 @@ __global__ void __launch_bounds__(256) stream_plan_kernel(DevMap m, int32_t bs, 
     return;
   }
   const int32_t T_all = min(stream_tiles(m.kv_lens[i]), max_tiles);
+  const bool lead = c == 0;
+  if (!lead && c * kPlanTiles >= T_all) return;  // past the request's tiles (uniform per workgroup)
   const int32_t st = left_out(skip, share, m.kv_lens, i, T_all);  // tiles left out at the start
   const int32_t T = T_all - st;
-  const bool lead = c == 0;
-  if (!lead && c * kPlanTiles >= T) return;  // uniform per workgroup
+  if (!lead && c * kPlanTiles >= T) return;
   if (lead && share.s) {
     // this request's skip, and the prefix pass's work if a shared group
     // starts here: slices of ms members times ch chunks of the group's

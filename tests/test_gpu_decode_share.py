@@ -158,3 +158,35 @@ def test_sharing_and_private_copies_agree_with_the_oracle_at_full_size():
     assert_lse_close(lse_s, ref_l, "bf16", "shared", rows=reqs)
     assert_lse_close(lse_p, ref_l, "bf16", "private", rows=reqs)
     P.kv_pool_destroy(pool2)
+
+
+def test_large_batch_with_groups_of_every_size():
+    """A thousand requests in groups of 1 to 70 members (groups longer than
+    the 64-request blocks split into several), random prefix and total
+    lengths, page size 16, CSR: every output against the oracle on a
+    sample, and the shared layout against itself in the block-table format
+    bit for bit."""
+    rng = np.random.default_rng(11)
+    groups, bs = [], 0
+    while bs < 1000:
+        size = int(rng.choice([1, 1, 2, 3, 8, 15, 33, 70]))
+        pp = int(rng.integers(1, 40))
+        members = []
+        for _ in range(size):
+            L = int(rng.integers(1, 1800))
+            members.append((L, int(rng.integers(0, pp + 1))))
+        groups.append((pp, members))
+        bs += size
+    case = W.shared_prefix_batch(16, groups, seed=11, num_q_heads=16, num_kv_heads=8)
+    print(f"large shared batch: bs {case.bs}, {len(groups)} groups", flush=True)
+    vals = W.make_values(case, device="cuda", canary=True)
+    dc = DeviceCase(case, vals)
+    out, lse = dc.decode(P.PKV_MAP_CSR)
+    o2, l2 = dc.decode(P.PKV_MAP_BLOCK_TABLE)
+    assert torch.equal(out.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, l2)
+    lens = case.regions["self"].kv_lens
+    live = [i for i in range(case.bs) if lens[i] > 0]
+    reqs = sorted(set(np.random.default_rng(2).choice(live, 120, replace=False).tolist()))
+    ref_o, ref_l = oracle_region(case, vals, "self", requests=reqs)
+    assert_attn_close(out, ref_o, "bf16", "large shared batch", rows=reqs)
+    assert_lse_close(lse, ref_l, "bf16", "large shared batch", rows=reqs)

@@ -40,13 +40,23 @@ def check_replays(g, outputs, refs, reset, eager):
         torch.cuda.synchronize()
 
 
+def _decode_case(name):
+    if name == "qwen3_small":
+        return W.qwen3_decode(seed=1, bs=16), P.PKV_MAP_TOKEN_TABLE
+    if name == "mla_small":
+        return W.mla_decode(seed=1, bs=8, len_range=(100, 900)), P.PKV_MAP_BLOCK_TABLE
+    # prefix sharing: the decode's own shared-prefix detection and prefix work
+    return W.gqa_prefix_share(16, seed=5, bs=24, group=8, prefix=512, median=600, clip=(64, 2000)), P.PKV_MAP_CSR
+
+
 @pytest.mark.parametrize("append", [False, True])
-@pytest.mark.parametrize("name", ["qwen3_small", "mla_small"])
+@pytest.mark.parametrize("name", ["qwen3_small", "mla_small", "prefix_share_small"])
 def test_decode_step_replays_bitwise(name, append):
-    case = W.qwen3_decode(seed=1, bs=16) if name == "qwen3_small" else W.mla_decode(seed=1, bs=8, len_range=(100, 900))
+    case, fmt = _decode_case(name)
+    if append and not case.n_new:
+        pytest.skip("the prefix-sharing workload stores nothing")
     vals = W.make_values(case)
     dc = DeviceCase(case, vals)
-    fmt = P.PKV_MAP_TOKEN_TABLE if name == "qwen3_small" else P.PKV_MAP_BLOCK_TABLE
     g_ = case.geom
     m = dc.kv_map("self", fmt)
     out = torch.empty((case.bs, g_.num_q_heads, g_.head_dim_v), dtype=dc.dtype, device="cuda")
