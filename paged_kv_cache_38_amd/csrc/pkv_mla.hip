@@ -511,8 +511,27 @@ __global__ void __launch_bounds__(256) mla_merge_kernel(int32_t bs, int32_t Hq, 
   const int Bt = header[0];
   const int b0 = P / Bt, b1 = (P + T - 1) / Bt;
   if (b0 == b1) return;
+  // the first KB pieces' lse and rows are loaded at once (they are
+  // independent); a request cut into more pieces takes the rest in a loop
+  constexpr int KB = 4;
+  float lb[KB];
+  f32x4 xb[KB][2];
+#pragma unroll
+  for (int k = 0; k < KB; ++k) {
+    lb[k] = -INFINITY;
+    xb[k][0] = xb[k][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (b0 + k <= b1) {
+      const int64_t row = ((int64_t)(b0 + k) + i) * Hq + h;
+      lb[k] = ws_lse[row];
+      const f32x4* src = reinterpret_cast<const f32x4*>(ws_o + row * kMlaV + lane * 8);
+      xb[k][0] = src[0];
+      xb[k][1] = src[1];
+    }
+  }
   float mx = -INFINITY;
-  for (int b = b0; b <= b1; ++b) mx = fmaxf(mx, ws_lse[((int64_t)b + i) * Hq + h]);
+#pragma unroll
+  for (int k = 0; k < KB; ++k) mx = fmaxf(mx, lb[k]);
+  for (int b = b0 + KB; b <= b1; ++b) mx = fmaxf(mx, ws_lse[((int64_t)b + i) * Hq + h]);
   if (mx == -INFINITY) {  // a draft that sees no key at all (kv_lens below n_draft)
 #pragma unroll
     for (int e = 0; e < 8; ++e) op[e] = (bf16)0.0f;
@@ -521,7 +540,19 @@ __global__ void __launch_bounds__(256) mla_merge_kernel(int32_t bs, int32_t Hq, 
   }
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float sum = 0.f;
-  for (int b = b0; b <= b1; ++b) {
+  // (pieces past the request, and pieces a draft sees no key of, weigh 0;
+  // their rows are finite)
+#pragma unroll
+  for (int k = 0; k < KB; ++k) {
+    const float wgt = lb[k] == -INFINITY ? 0.f : __expf(lb[k] - mx);
+    sum += wgt;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      o[e] += wgt * xb[k][0][e];
+      o[4 + e] += wgt * xb[k][1][e];
+    }
+  }
+  for (int b = b0 + KB; b <= b1; ++b) {
     const int64_t row = ((int64_t)b + i) * Hq + h;
     const float wgt = __expf(ws_lse[row] - mx);
     const f32x4* src = reinterpret_cast<const f32x4*>(ws_o + row * kMlaV + lane * 8);
