@@ -38,6 +38,7 @@ constexpr float kExtSlack = 8.0f;  // log2 headroom before a row's running max m
 template <int D>
 struct ExtendCfg {
   static constexpr int RB = D == 64 ? 3 : 2;  // 16-row blocks per wave
+  static constexpr int OCC = 2;               // workgroups per CU the registers allow
   static constexpr int WR = 16 * RB;          // query rows per wave
   static constexpr int BM = 4 * WR;           // query rows per workgroup (four waves)
   static constexpr int NK = D / 32;          // k-steps of the score product
@@ -46,7 +47,9 @@ struct ExtendCfg {
   static constexpr int TILE = kBN * D * 2;   // bytes of one K (or V) tile
   static constexpr int NI = 2 * TILE / 1024 / 4;  // K+V DMA instructions per wave per tile
   static constexpr int S = D == 64 ? 3 : 2;  // LDS stages (tiles resident)
-  static constexpr int WAIT = S == 2 ? 1 : NI + 1;
+  // memory operations a wave may leave outstanding when tile kt must have
+  // landed: the later tiles' DMAs and the newest table load
+  static constexpr int WAIT = (S - 2) * NI + 1;
 };
 
 // Byte offset of 16-byte chunk c of key row t in an LDS tile: rows are
@@ -86,7 +89,7 @@ struct SoftCap {
 };
 
 template <int D, int FMT, bool SC>
-__global__ void __launch_bounds__(256, 2) extend_kernel(DevMap m, const char* k_pool, const char* v_pool,
+__global__ void __launch_bounds__(256, ExtendCfg<D>::OCC) extend_kernel(DevMap m, const char* k_pool, const char* v_pool,
                                                      int64_t row_bytes, const bf16* __restrict__ q, int64_t total_q,
                                                      const int32_t* __restrict__ qo_indptr, int32_t Hq, int32_t n_req,
                                                      int32_t n_qtiles, int32_t G, int32_t causal_all,
@@ -185,22 +188,27 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(DevMap m, const char* k_
       dma4(sm.raw_ptr(t), lds_off(&tab_lds[w][kt % (S + 1)][0]));
     };
     // K and V rows of a tile; wave w moves chunk positions
-    // [w * NI/2 * 64, (w + 1) * NI/2 * 64) of each
+    // [w * NI/2 * 64, (w + 1) * NI/2 * 64) of each.  A lane's key row within
+    // the tile and its swizzled byte offset within the row are the same for
+    // every tile, so they are computed once.
+    int dt[NI / 2], dc[NI / 2];
+#pragma unroll
+    for (int j = 0; j < NI / 2; ++j) {
+      const unsigned pos = (unsigned)((w * (NI / 2) + j) * 64 + lane);
+      dt[j] = (int)(pos / CPK);
+      dc[j] = (int)(((pos % CPK) ^ (pos / CPK & 7)) * 16);
+    }
+    const uint32_t rbytes = (uint32_t)row_bytes;  // one token row (all heads) is far below 4 GiB
     auto kv_dma = [&](int kt) {
       const int32_t* tr = &tab_lds[w][kt % (S + 1)][0];
       const int k0 = min(kt, ntiles - 1) * kBN;
       char* kt_lds = kv_lds[kt % S][0];
       char* vt_lds = kv_lds[kt % S][1];
-      int ln = lane;
-      asm volatile("" : "+v"(ln));  // recompute per tile instead of holding NI addresses
 #pragma unroll
       for (int j = 0; j < NI / 2; ++j) {
-        const int pos = (w * (NI / 2) + j) * 64 + ln;
-        const int t = pos / CPK;
-        const int c = (pos % CPK) ^ (t & 7);
-        const int tt = min(k0 + t, kv_end - 1);
-        const int64_t slot = sm.finish(tr[t], tt, true);
-        const int64_t off = slot * row_bytes + c * 16;
+        const int tt = min(k0 + dt[j], kv_end - 1);
+        const uint32_t slot = (uint32_t)sm.finish(tr[dt[j]], tt, true);  // in [0, num_slots)
+        const uint64_t off = (uint64_t)slot * rbytes + (uint32_t)dc[j];
         dma16(kb + off, lds_off(kt_lds + (w * (NI / 2) + j) * 1024));
         dma16(vb + off, lds_off(vt_lds + (w * (NI / 2) + j) * 1024));
       }
@@ -229,15 +237,11 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(DevMap m, const char* k_
     const char* lds0 = &kv_lds[0][0][0];
     const bf16x8 ones = bf16x8{(bf16)1.f, (bf16)1.f, (bf16)1.f, (bf16)1.f, (bf16)1.f, (bf16)1.f, (bf16)1.f, (bf16)1.f};
 
-    auto tile_step = [&](int kt, auto stage_c, auto mask_c) {
+    // ---- S^T = K Q^T of tile kt (stage st): four 16-key subtiles x kRB
+    // 16-row blocks (softcapped, if asked)
+    auto qk = [&](auto stage_c, f32x4 (&sacc)[4][kRB]) {
       constexpr int st = decltype(stage_c)::value;
-      constexpr bool MASK = decltype(mask_c)::value;
       const char* ks = lds0 + (st * 2 + 0) * C::TILE;
-      const char* vs = lds0 + (st * 2 + 1) * C::TILE;
-      const int k0 = kt * kBN;
-
-      // ---- S^T = K Q^T: four 16-key subtiles x two 16-row blocks
-      f32x4 sacc[4][kRB];
 #pragma unroll
       for (int a2 = 0; a2 < 4; ++a2)
 #pragma unroll
@@ -260,6 +264,14 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(DevMap m, const char* k_
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) sacc[a2][rb][rr] = cap(sacc[a2][rb][rr]);
       }
+    };
+
+    // ---- the softmax of tile kt's scores and O^T += V^T P^T (stage st)
+    auto smpv = [&](int kt, auto stage_c, auto mask_c, f32x4 (&sacc)[4][kRB]) {
+      constexpr int st = decltype(stage_c)::value;
+      constexpr bool MASK = decltype(mask_c)::value;
+      const char* vs = lds0 + (st * 2 + 1) * C::TILE;
+      const int k0 = kt * kBN;
 
       // ---- online softmax (log2 domain); lane holds keys k0 + 16a + 4grp + rr
       // of row rb*16 + col.  The max is taken on raw scores (the scale is
@@ -352,10 +364,12 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(DevMap m, const char* k_
       // tile's keys, only helps move the tiles; keys past what every row of
       // the wave sees need the per-element mask
       if (rw < n && kt * kBN < w_end) {
+        f32x4 sacc[4][kRB];
+        qk(stage_c, sacc);
         if (kt * kBN + kBN <= w_free)
-          tile_step(kt, stage_c, std::false_type{});
+          smpv(kt, stage_c, std::false_type{}, sacc);
         else
-          tile_step(kt, stage_c, std::true_type{});
+          smpv(kt, stage_c, std::true_type{}, sacc);
       }
     };
     for (int kt = 0; kt < ntiles; kt += S) {
@@ -621,6 +635,7 @@ hipError_t launch_extend(const PoolInfo& p, int32_t layer, const void* q, int64_
   const int bm = p.head_dim_qk == 128 ? ExtendCfg<128>::BM : ExtendCfg<64>::BM;
   const dim3 grid(1, (unsigned)((max_q_len + bm - 1) / bm), (unsigned)bs);
   const int64_t row_bytes = (int64_t)p.num_kv_heads * p.head_dim_qk * 2;  // one token row, all KV heads
+  if (row_bytes > (int64_t)UINT32_MAX) return hipErrorInvalidValue;  // the kernel's row offsets are 32-bit
   timer_before(s);
   if (p.head_dim_qk == 128)
     launch_ext_fmt<128>(grid, s, m, kp, vp, row_bytes, q, total_q, qo_indptr, Hq, G, causal, causal_flags, softcap,
