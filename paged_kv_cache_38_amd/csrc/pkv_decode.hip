@@ -215,6 +215,15 @@ __device__ __forceinline__ void decode_compute(const DecodeTile<D>& T, int t0, i
 // the run is written directly; one cut by a run boundary leaves a piece
 // (id run + request) for the merge.
 // ---------------------------------------------------------------------------
+// Minimum workgroups per CU the stream kernels are compiled for.  At D =
+// 128 four waves with three tile sets need a whole SIMD's registers (VGPRs
+// and AGPRs) each, so W = 4 is one workgroup per CU.  Narrower workgroups (KV
+// head counts not divisible by 4) share a CU with their siblings, as the
+// plan's run count assumes, but are still given a whole SIMD's registers
+// per wave: asking for 4 / W workgroups would cap each wave at 256 or 128
+// registers and spill the tile sets.
+constexpr int stream_min_blocks(int waves, int ns) { return waves >= 4 ? (ns <= 2 ? 8 / waves : 4 / waves) : 1; }
+
 template <int D>
 struct StreamSet {
   DecodeTile<D> t;
@@ -337,7 +346,7 @@ __device__ __forceinline__ void stream_run(
 }
 
 template <int D, int WAVES, int NS>
-__global__ void __launch_bounds__(64 * WAVES, NS <= 2 ? 8 / WAVES : 4 / WAVES) decode_stream_kernel(
+__global__ void __launch_bounds__(64 * WAVES, stream_min_blocks(WAVES, NS)) decode_stream_kernel(
     const bf16* k_pool, const bf16* v_pool, const bf16* __restrict__ q, int32_t Hq, int32_t Hkv, int32_t G,
     int32_t hg, const int32_t* __restrict__ header, const int32_t* __restrict__ meta, float scale_log2,
     bf16* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws_o, float* __restrict__ ws_lse,
@@ -595,7 +604,7 @@ __global__ void __launch_bounds__(64 * W) cascade_prefix_kernel(
 // soon as its run is done, and a batch without shared prefixes pays no
 // second launch.
 template <int D, int WAVES, int NS, int FMT>
-__global__ void __launch_bounds__(64 * WAVES, NS <= 2 ? 8 / WAVES : 4 / WAVES) decode_share_kernel(
+__global__ void __launch_bounds__(64 * WAVES, stream_min_blocks(WAVES, NS)) decode_share_kernel(
     const bf16* k_pool, const bf16* v_pool, const bf16* __restrict__ q, int32_t Hq, int32_t Hkv, int32_t G,
     int32_t hg, const int32_t* __restrict__ header, const int32_t* __restrict__ meta, float scale_log2,
     bf16* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws_o, float* __restrict__ ws_lse,
