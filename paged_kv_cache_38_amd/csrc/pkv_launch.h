@@ -218,7 +218,7 @@ hipError_t launch_decode_cascade(const PoolInfo& p, int32_t layer, const void* q
                                  const int32_t* prefix_len, int32_t num_groups, float sm_scale, void* out, float* lse,
                                  void* ws, hipStream_t s);
 
-bool extend_supported(const PoolInfo& p, int32_t num_q_heads);bool extend_supported(const PoolInfo& p, int32_t num_q_heads);
+bool extend_supported(const PoolInfo& p, int32_t num_q_heads);
 hipError_t launch_extend(const PoolInfo& p, int32_t layer, const void* q, int64_t total_q, const int32_t* qo_indptr,
                          int32_t num_q_heads, int32_t max_q_len, const DevMap& m, int32_t bs, int32_t max_kv_len,
                          int32_t causal, const int32_t* causal_flags, float softcap, float sm_scale, void* out,
