@@ -207,14 +207,9 @@ __global__ void __launch_bounds__(64 * W, 1) mla_decode_kernel(
   bf16x8 qf[HB][NK];
   float m_ref[HB], l_part[HB];
   float s_over[HB];  // raw score above which P could overflow (kMlaHeadroom past the reference)
-  // VERIFY: each row's draft index, and the request's first key that the
-  // first draft cannot see
-  int jrow[HB];
+  // VERIFY: the request's first key that the first draft cannot see (a
+  // row's draft index is worked out in the tiles that need it)
   int k_zone = 0;
-  if constexpr (VERIFY) {
-#pragma unroll
-    for (int hb = 0; hb < HB; ++hb) jrow[hb] = (row_off + hw + hb * 16 + col) / hq_base;
-  }
 
   // Per iteration r a wave issues meta(r + 6) then tile(r + 3); tile(r) is
   // then followed in the queue by meta(r + 4), tile(r + 1), meta(r + 5),
@@ -332,7 +327,10 @@ __global__ void __launch_bounds__(64 * W, 1) mla_decode_kernel(
       if (valid < kMlaT || jt * kMlaT + kMlaT > k_zone) {
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb) {
-          const int lim = min(valid, k_zone + jrow[hb] - jt * kMlaT);
+          int c = col;
+          asm volatile("" : "+v"(c));  // recomputed here, not held across the loop (registers)
+          const int jrow = (row_off + hw + hb * 16 + c) / hq_base;  // this row's draft
+          const int lim = min(valid, k_zone + jrow - jt * kMlaT);
 #pragma unroll
           for (int a = 0; a < 2; ++a)
 #pragma unroll
