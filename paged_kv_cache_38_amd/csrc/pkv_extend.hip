@@ -215,7 +215,10 @@ __global__ void __launch_bounds__(256, ExtendCfg<D>::OCC) extend_kernel(DevMap m
     };
     // prologue: queue = [tables 0 .. S-1 landed] tile 0 .. tile S-2, table S-1 ..
     for (int k = 0; k < S; ++k) tab_dma(k);
-    wait_vm<0>();
+    // the tables and the queries have landed.  A wait the compiler sees:
+    // otherwise it adds its own before the first score product, where it
+    // would also drain the tile DMAs issued below
+    __builtin_amdgcn_s_waitcnt(0);
     for (int k = 0; k < S - 1; ++k) kv_dma(k);
 
     // per-lane parts of the LDS addresses; the tile loop is unrolled by the
