@@ -263,13 +263,14 @@ __device__ __forceinline__ void stream_run(
     S.mv = mv;
     decode_issue<D>(S.t, mv, lane, kb, vb, row_elems);
     const int i = __builtin_amdgcn_readlane(mv, 32);
+    // columns past G read the group's first query row: finite scores in
+    // columns no output row reads (a column's softmax and its P*V column
+    // use only that column).  Zeroing them instead is a select on the
+    // loaded value, which makes the compiler wait for these loads, and
+    // so for every load issued before them, at the loop's back edge.
     const bf16* qp = q + ((int64_t)i * Hq + g * G + (qok ? col : 0)) * D + grp * 8;
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      u32x4 w = *reinterpret_cast<const u32x4*>(qp + kk * 32);
-      if (!qok) w = u32x4{0u, 0u, 0u, 0u};
-      S.q[kk] = as_bf16x8(w);
-    }
+    for (int kk = 0; kk < NK; ++kk) S.q[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + kk * 32));
   };
 
   f32x4 acc[NT];
@@ -522,20 +523,38 @@ __device__ __forceinline__ void cascade_prefix_work(const DevMap& m, const bf16*
     const int64_t row_elems = (int64_t)Hkv * D;
     const bf16* kb = k_pool + (int64_t)h * D;
     const bf16* vb = v_pool + (int64_t)h * D;
-    // lane l < 32 holds the slot of key 32 t + l (keys past E read the padding slot)
-    auto slot_word = [&](int t) -> int32_t {
+    // Lane l < 32 resolves key 32 t + l (keys past E, and tiles past
+    // t_end, read the padding slot).  As in the stream kernel, three tile
+    // sets in fixed registers: while tile t is computed, tiles t + 1 and
+    // t + 2 are in flight.  A tile's table entry is loaded (raw_word, the
+    // bare load of a real entry) a tile before its rows are issued and
+    // checked (slot_of) then, so no wait for it is also a wait for rows
+    // still in flight (loads complete in order).  Every load is issued
+    // unconditionally; only the compute stops at t_end.
+    auto raw_word = [&](int t) -> int32_t { return sm.raw(min(t * kTile + (lane & 31), E - 1)); };
+    auto slot_of = [&](int t, int32_t r) -> int32_t {
       const int key = t * kTile + (lane & 31);
-      return sm(min(key, E - 1), key < E);
+      return sm.finish(r, min(key, E - 1), key < E);
     };
-    DecodeTile<D> T[2];
-    decode_issue<D>(T[0], slot_word(t_begin), lane, kb, vb, row_elems);
-    for (int t = t_begin; t < t_end; t += 2) {
-      if (t + 1 < t_end) decode_issue<D>(T[1], slot_word(t + 1), lane, kb, vb, row_elems);
-      cascade_tile<D, NB>(T[0], t * kTile, E, lim, lane, qb, scale_log2, vt, acc, m_run, l_run);
-      if (t + 1 < t_end) {
-        if (t + 2 < t_end) decode_issue<D>(T[0], slot_word(t + 2), lane, kb, vb, row_elems);
-        cascade_tile<D, NB>(T[1], (t + 1) * kTile, E, lim, lane, qb, scale_log2, vt, acc, m_run, l_run);
-      }
+    DecodeTile<D> T[3];
+    int32_t r0 = raw_word(t_begin), r1 = raw_word(t_begin + 1), r2 = raw_word(t_begin + 2);
+    decode_issue<D>(T[0], slot_of(t_begin, r0), lane, kb, vb, row_elems);
+    decode_issue<D>(T[1], slot_of(t_begin + 1, r1), lane, kb, vb, row_elems);
+    auto step = [&](int t, DecodeTile<D>& cur, DecodeTile<D>& nxt2, int32_t& r_nxt2, int32_t& r_reload) {
+      // tile t + 2's rows (its entry r_nxt2 was loaded a tile ago), then
+      // the entry of tile t + 3 into the register tile t's entry held
+      const int32_t rn = raw_word(t + 3);
+      __builtin_amdgcn_sched_barrier(0);
+      decode_issue<D>(nxt2, slot_of(t + 2, r_nxt2), lane, kb, vb, row_elems);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      r_reload = rn;
+      if (t < t_end) cascade_tile<D, NB>(cur, t * kTile, E, lim, lane, qb, scale_log2, vt, acc, m_run, l_run);
+    };
+    for (int t = t_begin; t < t_end; t += 3) {
+      step(t, T[0], T[2], r2, r0);
+      step(t + 1, T[1], T[0], r0, r1);
+      step(t + 2, T[2], T[1], r1, r2);
     }
   }
 

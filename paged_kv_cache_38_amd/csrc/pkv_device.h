@@ -154,16 +154,19 @@ struct SlotMap {
       return base[min(max(t >> shift, 0), max(limit - 1, 0))];
     }
   }
+  // (the tests use & rather than &&: every operand is cheap and side-effect
+  // free, and a short-circuit would let the compiler move a table load
+  // issued early into a branch of its own, with a wait for it there)
   __device__ __forceinline__ int32_t finish(int32_t r, int32_t t, bool valid) const {
     if constexpr (FMT == SLOT_CONTIG) {
       const int32_t s = off + t;
       return (valid && (uint32_t)s < (uint32_t)num_slots) ? s : pad;
     } else if constexpr (FMT == SLOT_TABLE) {
-      const bool ok = valid && t < limit;
+      const bool ok = valid & (t < limit);
       const int32_t s = ok ? r : pad;
       return ((uint32_t)s < (uint32_t)num_slots) ? s : pad;
     } else {
-      const bool ok = valid && (t >> shift) < limit && r >= 0;
+      const bool ok = valid & ((t >> shift) < limit) & (r >= 0);
       const int32_t s = ok ? ((r << shift) | (t & mask)) : pad;
       return ((uint32_t)s < (uint32_t)num_slots) ? s : pad;
     }
