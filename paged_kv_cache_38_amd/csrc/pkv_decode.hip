@@ -228,7 +228,9 @@ template <int D>
 struct StreamSet {
   DecodeTile<D> t;
   bf16x8 q[D / 32];
-  int32_t mv;  // planner word of lane l
+  // the planner's words for the tile: request, key tile within it, the
+  // request's tile count and first tile in the stream, valid keys
+  int i, jt, T, P, valid;
 };
 
 // One run of the stream, by workgroup `bid` (vt: this wave's V tile in LDS).
@@ -259,10 +261,16 @@ __device__ __forceinline__ void stream_run(
   auto meta_word = [&](int r) -> int32_t {
     return meta[(int64_t)(G0 + min(r, n - 1)) * kStreamMetaWords + min(lane, kStreamMetaWords - 1)];
   };
+  // (the planner words are read out of mv here, so that mv is dead once
+  // the tile is issued and its register can take the next word's load)
   auto issue = [&](StreamSet<D>& S, int32_t mv) {
-    S.mv = mv;
     decode_issue<D>(S.t, mv, lane, kb, vb, row_elems);
     const int i = __builtin_amdgcn_readlane(mv, 32);
+    S.i = i;
+    S.jt = __builtin_amdgcn_readlane(mv, 33);
+    S.T = __builtin_amdgcn_readlane(mv, 34);
+    S.P = __builtin_amdgcn_readlane(mv, 35);
+    S.valid = __builtin_amdgcn_readlane(mv, 36);
     // columns past G read the group's first query row: finite scores in
     // columns no output row reads (a column's softmax and its P*V column
     // use only that column).  Zeroing them instead is a select on the
@@ -310,40 +318,62 @@ __device__ __forceinline__ void stream_run(
     }
   };
 
+  auto step = [&](int r, StreamSet<D>& cur) {
+    const int i = cur.i, jt = cur.jt, T = cur.T, P = cur.P, valid = cur.valid;
+    if (r == 0 || jt == 0) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      m_run = -INFINITY;
+      l_run = 0.f;
+    }
+    decode_compute<D>(cur.t, 0, valid, lane, cur.q, scale_log2, vt, acc, m_run, l_run);
+    if (r == n - 1 || jt == T - 1) finish(i, P, T);
+  };
+
   StreamSet<D> S[NS];
+  if (n < NS) {  // a short run: its tiles at once
+#pragma unroll
+    for (int k = 0; k < NS - 1; ++k) issue(S[k], meta_word(k));
+#pragma unroll
+    for (int k = 0; k < NS - 1; ++k)
+      if (k < n) step(k, S[k]);
+    return;
+  }
+  // Tile r sits in set r % NS and is issued NS - 1 tiles ahead of its use.
+  // The loop runs whole rounds of NS tiles with no exit between them, and is
+  // entered only when there is a round to run: a round that could stop
+  // after any tile, or a loop that could be skipped, gives the compiler
+  // paths on which a tile's loads were never issued (or spills the sets
+  // across the skip), and the wait counts, which must hold on every path,
+  // then drain the loads in flight at every round.  The last n % NS tiles,
+  // issued by the loop, are taken afterwards.  (Issues past the end re-read
+  // the run's last tile; nothing uses them.)
+  // A tile's meta word is loaded two tiles before the tile is issued, into
+  // M[tile % NS]: loads complete in order, so waiting for a word loaded one
+  // tile earlier would also wait for the tile issued before it (the one
+  // about to be computed), and the next issue could not go out ahead of it.
 #pragma unroll
   for (int k = 0; k < NS - 1; ++k) issue(S[k], meta_word(k));
-  int32_t mv_next = meta_word(NS - 1);
-  bool done = false;
-  for (int r = 0; !done;) {
+  int32_t M[NS];
+  M[(NS - 1) % NS] = meta_word(NS - 1);
+  M[0] = meta_word(NS);
+  int r = 0;
+  do {
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
-      if (!done) {
-        const int32_t mv_new = meta_word(r + NS);
-        __builtin_amdgcn_sched_barrier(0);
-        issue(S[(j + NS - 1) % NS], mv_next);
-        mv_next = mv_new;
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-        const int32_t mv = S[j].mv;
-        const int i = __builtin_amdgcn_readlane(mv, 32);
-        const int jt = __builtin_amdgcn_readlane(mv, 33);
-        const int T = __builtin_amdgcn_readlane(mv, 34);
-        const int P = __builtin_amdgcn_readlane(mv, 35);
-        const int valid = __builtin_amdgcn_readlane(mv, 36);
-        if (r == 0 || jt == 0) {
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-          m_run = -INFINITY;
-          l_run = 0.f;
-        }
-        decode_compute<D>(S[j].t, 0, valid, lane, S[j].q, scale_log2, vt, acc, m_run, l_run);
-        if (r == n - 1 || jt == T - 1) finish(i, P, T);
-        ++r;
-        if (r >= n) done = true;
-      }
+      const int32_t mv_new = meta_word(r + j + NS + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(S[(j + NS - 1) % NS], M[(j + NS - 1) % NS]);
+      M[(j + 1) % NS] = mv_new;
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      step(r + j, S[j]);
     }
-  }
+    r += NS;
+  } while (r + NS <= n);
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+    if (r + j < n) step(r + j, S[j]);
 }
 
 template <int D, int WAVES, int NS>
