@@ -124,6 +124,22 @@ __global__ void __launch_bounds__(256) build_indices_kernel(int32_t fmt, const i
   const bool row_ok = row >= 0 && row < rows && start >= 0;
   const int32_t* rowp = table + (row_ok ? row : 0) * width;
 
+  // kBatch entries per thread are loaded before any is stored, so a long
+  // request's block waits for one load latency per 256 * kBatch pages
+  // rather than one per 256; the first batch goes out before the CSR
+  // offset sum, which only the stores need
+  constexpr int kBatch = 8;
+  int32_t v[kBatch];
+  auto load_batch = [&](int32_t k0) {
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int32_t k = k0 + u * 256 + tid;
+      const int64_t col = start + ((int64_t)k << shift);
+      v[u] = (k < cnt && row_ok && col < width) ? rowp[col] : -1;
+    }
+  };
+  load_batch(0);
+
   int64_t base = 0;
   if (fmt == MAP_CSR) {
     int32_t acc = 0;
@@ -138,14 +154,18 @@ __global__ void __launch_bounds__(256) build_indices_kernel(int32_t fmt, const i
       kv_indptr[i + 1] = (int32_t)(base + cnt);
     }
   }
-  for (int32_t k = tid; k < cnt; k += 256) {
-    const int64_t col = start + ((int64_t)k << shift);
-    const int32_t v = (row_ok && col < width) ? rowp[col] : -1;
-    const int32_t page = v >= 0 ? (v >> shift) : -1;
-    if (fmt == MAP_CSR) {
-      if (base + k < capacity) out[base + k] = page;
-    } else if (k < capacity) {
-      out[(int64_t)i * capacity + k] = page;
+  for (int32_t k0 = 0; k0 < cnt; k0 += 256 * kBatch) {
+    if (k0 > 0) load_batch(k0);
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int32_t k = k0 + u * 256 + tid;
+      if (k >= cnt) break;
+      const int32_t page = v[u] >= 0 ? (v[u] >> shift) : -1;
+      if (fmt == MAP_CSR) {
+        if (base + k < capacity) out[base + k] = page;
+      } else if (k < capacity) {
+        out[(int64_t)i * capacity + k] = page;
+      }
     }
   }
   if (fmt == MAP_BLOCK_TABLE) {

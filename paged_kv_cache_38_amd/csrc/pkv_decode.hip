@@ -734,17 +734,34 @@ __global__ void __launch_bounds__(64) share_detect_kernel(DevMap m, int32_t bs, 
       const int32_t gran = FMT == SLOT_PAGES ? (1 << m.page_shift) : 1;  // one probe per page
       const SlotMap<FMT> smi = make_slotmap<FMT>(m, i), smr = make_slotmap<FMT>(m, ref);
       const int32_t nk = (n + gran - 1) / gran;
+      // 4 x 64 probes per pass, every table load of the pass issued before
+      // the first comparison (a prefix of a few hundred pages then costs one
+      // load latency, not one per 64 pages)
+      constexpr int kProbeRounds = 4;
       int32_t c = n;
-      for (int32_t kb = 0; kb < nk; kb += 64) {
-        const int32_t k = kb + lane;
-        bool mis = false;
-        if (k < nk) {
-          const int32_t a = smi(k * gran, true), b = smr(k * gran, true);
-          mis = a != b || a == smi.pad;
+      for (int32_t kb = 0; kb < nk; kb += 64 * kProbeRounds) {
+        int32_t ra[kProbeRounds], rb[kProbeRounds];
+#pragma unroll
+        for (int u = 0; u < kProbeRounds; ++u) {
+          const int32_t t = min(kb + u * 64 + lane, nk - 1) * gran;
+          ra[u] = smi.raw(t);
+          rb[u] = smr.raw(t);
         }
-        const uint64_t mm = __builtin_amdgcn_ballot_w64(mis);
+        uint64_t mm = 0;
+        int u_hit = 0;
+#pragma unroll
+        for (int u = kProbeRounds - 1; u >= 0; --u) {
+          const int32_t k = kb + u * 64 + lane;
+          const int32_t a = smi.finish(ra[u], min(k, nk - 1) * gran, true);
+          const int32_t b = smr.finish(rb[u], min(k, nk - 1) * gran, true);
+          const uint64_t mu = __builtin_amdgcn_ballot_w64(k < nk && (a != b || a == smi.pad));
+          if (mu) {  // the lowest round with a mismatch wins
+            mm = mu;
+            u_hit = u;
+          }
+        }
         if (mm) {
-          c = min(n, (kb + (int32_t)__builtin_ctzll(mm)) * gran);
+          c = min(n, (kb + u_hit * 64 + (int32_t)__builtin_ctzll(mm)) * gran);
           break;
         }
       }

@@ -51,8 +51,19 @@ __device__ __forceinline__ int32_t share_skip(const ShareArgs& a, const int32_t*
   const int32_t s = a.s[k];
   if (s >= 0) return s;
   int32_t best = 0;
-  const int32_t g1 = a.ge[k];
-  for (int32_t j = a.gs[k]; j < g1; ++j) best = max(best, a.s[j]);  // the reference's own entry is -1
+  const int32_t g0 = a.gs[k], g1 = a.ge[k];
+  // eight members' entries are loaded at a time (a group spans at most 64
+  // requests), unconditionally at clamped indices so that no branch on a
+  // loaded value separates the loads; the reference's own entry is -1
+  for (int32_t j0 = g0; j0 < g1; j0 += 8) {
+    int32_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = a.s[min(j0 + u, g1 - 1)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = j0 + u < g1 ? v[u] : 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) best = max(best, v[u]);
+  }
   const int32_t L = max(kv_lens[k], 0);
   return min(best, (L + kStreamT - 1) / kStreamT * kStreamT);
 }
@@ -68,10 +79,19 @@ __device__ __forceinline__ int32_t group_items(const ShareArgs& a, const int32_t
   const int32_t g1 = a.ge[k];
   if (g1 - k < 2) return 0;
   int32_t ref = -1, best = 0;
-  for (int32_t j = k; j < g1; ++j) {
-    const int32_t sj = a.s[j];
-    if (sj < 0) ref = j;
-    else best = max(best, sj);
+  for (int32_t j0 = k; j0 < g1; j0 += 8) {  // eight entries loaded at a time, as in share_skip
+    int32_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = a.s[min(j0 + u, g1 - 1)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = j0 + u < g1 ? v[u] : 0;
+    // (selects, not branches: a branch on a loaded value waits for it
+    // before the next load is issued; best >= 0 absorbs the -1)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      ref = v[u] < 0 ? j0 + u : ref;
+      best = max(best, v[u]);
+    }
   }
   if (ref < 0) return 0;
   const int32_t L = max(kv_lens[ref], 0);
@@ -105,7 +125,9 @@ __global__ void __launch_bounds__(256) stream_plan_kernel(DevMap m, int32_t bs, 
   const int32_t T_all = min(stream_tiles(m.kv_lens[i]), max_tiles);
   const bool lead = c == 0;
   if (!lead && c * kPlanTiles >= T_all) return;  // past the request's tiles (uniform per workgroup)
-  const int32_t st = left_out(skip, share, m.kv_lens, i, T_all);  // tiles left out at the start
+  // keys and tiles left out at the start
+  const int32_t sk = share.s ? share_skip(share, m.kv_lens, i) : 0;
+  const int32_t st = share.s ? min(sk / kStreamT, T_all) : skip_tiles(skip, i, T_all);
   const int32_t T = T_all - st;
   if (!lead && c * kPlanTiles >= T) return;
   if (lead && share.s) {
@@ -127,7 +149,7 @@ __global__ void __launch_bounds__(256) stream_plan_kernel(DevMap m, int32_t bs, 
     int32_t E, ref;
     const int32_t cnt = group_items(share, m.kv_lens, i, &E, &ref);
     if (tid == 0) {
-      share.skip[i] = share_skip(share, m.kv_lens, i);
+      share.skip[i] = sk;
       if (i == bs - 1) *share.count = base + cnt;
     }
     const int32_t tiles = (E + kStreamT - 1) / kStreamT;
@@ -177,21 +199,37 @@ __global__ void __launch_bounds__(256) stream_plan_kernel(DevMap m, int32_t bs, 
       header[1] = tot;
     }
   }
+  // Thread tid takes key tid % 32 of tiles j0, j0 + 8, ...: every table
+  // load of the workgroup is issued before the first store, so the loads
+  // cost one latency instead of one per pass.
   const SlotMap<FMT> sm = make_slotmap<FMT>(m, i);
   const int j_end = min(T, (c + 1) * kPlanTiles);
-  for (int j = c * kPlanTiles + (tid >> 5); j < j_end; j += 256 / 32) {
-    int32_t* tile = meta + (int64_t)(pre + j) * kStreamMetaWords;
-    const int32_t jt = st + j;  // key tile
-    tile[tid & 31] = sm(min(jt * kStreamT + (tid & 31), L - 1), true);
-    const int f = tid & 31;
-    if (f < 8) {
-      int32_t v = 0;
-      if (f == 0) v = i;
-      else if (f == 1) v = j;
-      else if (f == 2) v = T;
-      else if (f == 3) v = pre;
-      else if (f == 4) v = min(kStreamT, L - jt * kStreamT);
-      tile[32 + f] = v;
+  const int j0 = c * kPlanTiles + (tid >> 5);
+  const int f = tid & 31;
+  constexpr int kPasses = kPlanTiles / (256 / 32);
+  int32_t key[kPasses], raw[kPasses];
+#pragma unroll
+  for (int u = 0; u < kPasses; ++u) {
+    const int32_t jt = st + j0 + u * (256 / 32);  // key tile
+    key[u] = min(jt * kStreamT + f, L - 1);
+    raw[u] = sm.raw(key[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < kPasses; ++u) {
+    const int j = j0 + u * (256 / 32);
+    if (j < j_end) {
+      int32_t* tile = meta + (int64_t)(pre + j) * kStreamMetaWords;
+      const int32_t jt = st + j;
+      tile[f] = sm.finish(raw[u], key[u], true);
+      if (f < 8) {
+        int32_t v = 0;
+        if (f == 0) v = i;
+        else if (f == 1) v = j;
+        else if (f == 2) v = T;
+        else if (f == 3) v = pre;
+        else if (f == 4) v = min(kStreamT, L - jt * kStreamT);
+        tile[32 + f] = v;
+      }
     }
   }
 }
