@@ -496,20 +496,21 @@ __device__ __forceinline__ void cascade_tile(const DecodeTile<D>& T, int t0, int
   __builtin_amdgcn_wave_barrier();
 }
 
+constexpr int kShareChunks = 4;  // chunks of a group's prefix in the prefix pass
 constexpr int kCascadeCols = 32;  // query rows (member x head) per wave: two MFMA column blocks
 
 // One prefix work item of the cascade: members [i0, i1) (consecutive
 // requests of one group, up to 32 / G of them so their rows fill two
 // 16-row MFMA column blocks) against tiles [t_begin, t_end) of the prefix
-// keys [0, E), read through the table of member rd (whose keys [0, E) every
-// member shares up to its own limit).  Row limits: min(kv_len, S) with one
+// keys [0, E), read through the table of the group's reference member
+// (view rv; its keys [0, E) every member shares up to its own limit).  Row limits: min(kv_len, S) with one
 // S for the group, or min(kv_len, lim_arr[member]) when lim_arr is given.
 // Every (member, head) row gets a partial result in chunk slot c, o = 0 /
 // lse = -inf where the chunk holds none of the member's prefix keys.
 template <int D, int W, int FMT>
 __device__ __forceinline__ void cascade_prefix_work(const DevMap& m, const bf16* k_pool, const bf16* v_pool,
                                                     const bf16* __restrict__ q, int32_t bs, int32_t Hq,
-                                                    int32_t Hkv, int32_t G, int i0, int i1, int rd, int S,
+                                                    int32_t Hkv, int32_t G, int i0, int i1, ReqView rv, int S,
                                                     const int32_t* lim_arr, int E, int t_begin, int t_end, int c,
                                                     int ms, float scale_log2, float* __restrict__ ws_po,
                                                     float* __restrict__ ws_plse, bf16* vt, int bid) {
@@ -520,24 +521,62 @@ __device__ __forceinline__ void cascade_prefix_work(const DevMap& m, const bf16*
   const int col = lane & 15, grp = lane >> 4;
   const int h = ((bid / 8) % (Hkv / W)) * W + wave;  // KV head
 
-  // rows: column cc of block b is member i0 + cc / G, query head h G + cc % G
+  // Lane l < 32 resolves key 32 t + l (keys past E, and tiles past t_end,
+  // read the padding slot).  As in the stream kernel, three tile sets in
+  // fixed registers: while tile t is computed, tiles t + 1 and t + 2 are in
+  // flight.  A tile's table entry is loaded (raw_word, the bare load of a
+  // real entry) a tile before its rows are issued and checked (slot_of)
+  // then, so no wait for it is also a wait for rows still in flight (loads
+  // complete in order).  Every load is issued unconditionally; only the
+  // compute stops at t_end.
+  const SlotMap<FMT> sm = slotmap_from_view<FMT>(m, rv);
+  const int64_t row_elems = (int64_t)Hkv * D;
+  const bf16* kb = k_pool + (int64_t)h * D;
+  const bf16* vb = v_pool + (int64_t)h * D;
+  auto raw_word = [&](int t) -> int32_t { return sm.raw(min(t * kTile + (lane & 31), E - 1)); };
+  auto slot_of = [&](int t, int32_t r) -> int32_t {
+    const int key = t * kTile + (lane & 31);
+    return sm.finish(r, min(key, E - 1), key < E);
+  };
+
+  // Start-up order: the first four tiles' table entries, the queries, the
+  // row limits' loads; the first two tiles' rows go out as soon as their
+  // entries are in, and only then are the limits formed (a select on a
+  // loaded value waits for it, and so for every load issued before it).
+  // Tile k's entry is held in R[(k - t_begin) % 3] from two tiles before
+  // its rows are issued (the first two tiles' in a0, a1).
+  const int32_t a0 = raw_word(t_begin), a1 = raw_word(t_begin + 1);
+  int32_t R[3];
+  R[2] = raw_word(t_begin + 2);
+  R[0] = raw_word(t_begin + 3);
+  // rows: column cc of block b is member i0 + cc / G, query head h G + cc %
+  // G.  A column past the slice's rows reads member i0's query and limit
+  // loads (finite values) and gets limit 0, so all its keys are masked and
+  // nothing of it is written.
   bf16x8 qb[NB][NK];
-  int lim[NB];
+  int l_kv[NB], l_cap[NB];
+  bool okb[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     const int cc = b * 16 + col;
     const int mm = i0 + cc / G;
-    const bool ok = cc < ms * G && mm < i1;
-    const int L = ok ? m.kv_lens[mm] : 0;
-    lim[b] = ok ? min(L, lim_arr ? lim_arr[mm] : S) : 0;
-    const bf16* qp = q + ((int64_t)(ok ? mm : i0) * Hq + h * G + cc % G) * D + grp * 8;
+    okb[b] = cc < ms * G && mm < i1;
+    const int mr = okb[b] ? mm : i0;
+    const bf16* qp = q + ((int64_t)mr * Hq + h * G + cc % G) * D + grp * 8;
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      u32x4 v = *reinterpret_cast<const u32x4*>(qp + kk * 32);
-      if (!ok) v = u32x4{0u, 0u, 0u, 0u};
-      qb[b][kk] = as_bf16x8(v);
-    }
+    for (int kk = 0; kk < NK; ++kk) qb[b][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + kk * 32));
+    l_kv[b] = m.kv_lens[mr];
+    l_cap[b] = lim_arr ? lim_arr[mr] : S;
   }
+  DecodeTile<D> T[3];
+  __builtin_amdgcn_sched_barrier(0);
+  decode_issue<D>(T[0], slot_of(t_begin, a0), lane, kb, vb, row_elems);
+  decode_issue<D>(T[1], slot_of(t_begin + 1, a1), lane, kb, vb, row_elems);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  int lim[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) lim[b] = okb[b] ? min(l_kv[b], l_cap[b]) : 0;
   f32x4 acc[NB][NT];
   float m_run[NB], l_run[NB];
 #pragma unroll
@@ -548,43 +587,23 @@ __device__ __forceinline__ void cascade_prefix_work(const DevMap& m, const bf16*
     l_run[b] = 0.f;
   }
 
-  if (t_begin < t_end) {
-    const SlotMap<FMT> sm = make_slotmap<FMT>(m, rd);
-    const int64_t row_elems = (int64_t)Hkv * D;
-    const bf16* kb = k_pool + (int64_t)h * D;
-    const bf16* vb = v_pool + (int64_t)h * D;
-    // Lane l < 32 resolves key 32 t + l (keys past E, and tiles past
-    // t_end, read the padding slot).  As in the stream kernel, three tile
-    // sets in fixed registers: while tile t is computed, tiles t + 1 and
-    // t + 2 are in flight.  A tile's table entry is loaded (raw_word, the
-    // bare load of a real entry) a tile before its rows are issued and
-    // checked (slot_of) then, so no wait for it is also a wait for rows
-    // still in flight (loads complete in order).  Every load is issued
-    // unconditionally; only the compute stops at t_end.
-    auto raw_word = [&](int t) -> int32_t { return sm.raw(min(t * kTile + (lane & 31), E - 1)); };
-    auto slot_of = [&](int t, int32_t r) -> int32_t {
-      const int key = t * kTile + (lane & 31);
-      return sm.finish(r, min(key, E - 1), key < E);
-    };
-    DecodeTile<D> T[3];
-    int32_t r0 = raw_word(t_begin), r1 = raw_word(t_begin + 1), r2 = raw_word(t_begin + 2);
-    decode_issue<D>(T[0], slot_of(t_begin, r0), lane, kb, vb, row_elems);
-    decode_issue<D>(T[1], slot_of(t_begin + 1, r1), lane, kb, vb, row_elems);
-    auto step = [&](int t, DecodeTile<D>& cur, DecodeTile<D>& nxt2, int32_t& r_nxt2, int32_t& r_reload) {
-      // tile t + 2's rows (its entry r_nxt2 was loaded a tile ago), then
-      // the entry of tile t + 3 into the register tile t's entry held
-      const int32_t rn = raw_word(t + 3);
+  {
+    // step t: tile t + 2's rows (its entry, r_use, was loaded two tiles
+    // ago: waiting for it waits for no tile not yet computed), the entry of
+    // tile t + 4 into the register tile t + 1's entry held, then tile t
+    auto step = [&](int t, DecodeTile<D>& cur, DecodeTile<D>& nxt2, int32_t r_use, int32_t& r_load) {
+      const int32_t rn = raw_word(t + 4);
       __builtin_amdgcn_sched_barrier(0);
-      decode_issue<D>(nxt2, slot_of(t + 2, r_nxt2), lane, kb, vb, row_elems);
+      decode_issue<D>(nxt2, slot_of(t + 2, r_use), lane, kb, vb, row_elems);
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
-      r_reload = rn;
+      r_load = rn;
       if (t < t_end) cascade_tile<D, NB>(cur, t * kTile, E, lim, lane, qb, scale_log2, vt, acc, m_run, l_run);
     };
     for (int t = t_begin; t < t_end; t += 3) {
-      step(t, T[0], T[2], r2, r0);
-      step(t + 1, T[1], T[0], r0, r1);
-      step(t + 2, T[2], T[1], r1, r2);
+      step(t, T[0], T[2], R[2], R[1]);
+      step(t + 1, T[1], T[0], R[0], R[2]);
+      step(t + 2, T[2], T[1], R[1], R[0]);
     }
   }
 
@@ -642,7 +661,8 @@ __global__ void __launch_bounds__(64 * W) cascade_prefix_kernel(
   }
   const int E = min(S, Lmax);  // prefix keys any member sees
   const int t_begin = c * tpc, t_end = min(t_begin + tpc, (E + kTile - 1) / kTile);
-  cascade_prefix_work<D, W, FMT>(m, k_pool, v_pool, q, bs, Hq, Hkv, G, i0, i1, rd, S, nullptr, E, t_begin, t_end, c,
+  cascade_prefix_work<D, W, FMT>(m, k_pool, v_pool, q, bs, Hq, Hkv, G, i0, i1, request_view(m, rd), S, nullptr, E,
+                                 t_begin, t_end, c,
                                  ms, scale_log2, ws_po, ws_plse, vsm[threadIdx.x >> 6], (int)blockIdx.x);
 }
 
@@ -668,11 +688,21 @@ __global__ void __launch_bounds__(64 * WAVES, stream_min_blocks(WAVES, NS)) deco
   }
   const int b = (int)blockIdx.x - n_stream;  // n_stream is a multiple of 8: b keeps the XCD of blockIdx
   const int works = ((int)gridDim.x - n_stream) / hg;
+  // the first item is loaded beside the count (at an index clamped into
+  // the list's capacity, bs * kShareChunks), not after it
+  const int cap = bs * kShareChunks;
+  int w = (b / (8 * hg)) * 8 + b % 8;
+  PrefixItem it = items[min(w, cap - 1)];
   const int n_items = *count;
-  for (int w = (b / (8 * hg)) * 8 + b % 8; w < n_items; w += works) {
-    const PrefixItem it = items[w];
-    cascade_prefix_work<D, WAVES, FMT>(m, k_pool, v_pool, q, bs, Hq, Hkv, G, it.i0, it.i1, it.ref, 0, skip, it.E,
-                                       it.t0, it.t1, it.c, ms, scale_log2, ws_po, ws_plse, vt, b);
+  // (both loads stand here, issued together: the compiler would otherwise
+  // move the item's load into the loop, after the wait for the count)
+  asm volatile("" ::"s"(n_items), "s"(it.i0), "s"(it.i1), "s"(it.E), "s"(it.t0), "s"(it.t1), "s"(it.c),
+               "s"(it.limit), "s"(it.off_lo), "s"(it.off_hi));
+  while (w < n_items) {
+    cascade_prefix_work<D, WAVES, FMT>(m, k_pool, v_pool, q, bs, Hq, Hkv, G, it.i0, it.i1, prefix_item_view(it), 0,
+                                       skip, it.E, it.t0, it.t1, it.c, ms, scale_log2, ws_po, ws_plse, vt, b);
+    w += works;
+    if (w < n_items) it = items[w];
   }
 }
 
@@ -1132,7 +1162,6 @@ size_t decode_ws_layout(const PoolInfo& p, const DecodePlan& plan, int32_t bs, i
 }
 
 // ---- shared prefixes found by the stream decode itself
-constexpr int kShareChunks = 4;  // chunks of a group's prefix in the prefix pass
 struct ShareWs {
   int32_t* s;
   int32_t* gs;

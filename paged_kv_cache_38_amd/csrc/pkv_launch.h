@@ -147,9 +147,19 @@ size_t stream_ws_layout(int32_t bs, int32_t max_tiles, int32_t runs, int32_t Hq,
 // One work item of a shared-prefix pass: members [i0, i1) of one group
 // against tiles [t0, t1) of the prefix keys [0, E), read through member
 // ref's table; its partial results go to chunk slot c.  i0 < 0: no work.
+// The planner also stores ref's table view (row offset, readable entries),
+// so a work item reaches its table entries with no lookup of its own.
 struct __attribute__((aligned(16))) PrefixItem {
-  int32_t i0, i1, ref, E, t0, t1, c, pad;
+  int32_t i0, i1, ref, E, t0, t1, c, limit;
+  int32_t off_lo, off_hi, pad0, pad1;
 };
+
+__device__ __forceinline__ ReqView prefix_item_view(const PrefixItem& it) {
+  ReqView v;
+  v.off = ((int64_t)it.off_hi << 32) | (uint32_t)it.off_lo;
+  v.limit = it.limit;
+  return v;
+}
 
 // Shared prefixes found by paged_decode_attn itself (share_detect_kernel):
 // per request the keys it shares with its group's reference member (s >= 0),

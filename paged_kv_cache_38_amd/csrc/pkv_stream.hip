@@ -154,6 +154,7 @@ __global__ void __launch_bounds__(256) stream_plan_kernel(DevMap m, int32_t bs, 
     }
     const int32_t tiles = (E + kStreamT - 1) / kStreamT;
     const int32_t tpc = (tiles + share.ch - 1) / share.ch;
+    const ReqView rv = cnt > 0 ? request_view(m, ref) : ReqView{0, 0};
     for (int t = tid; t < cnt; t += 256) {
       const int32_t sl = t / share.ch, ck = t % share.ch;
       const int32_t i0 = i + sl * share.ms;
@@ -165,7 +166,10 @@ __global__ void __launch_bounds__(256) stream_plan_kernel(DevMap m, int32_t bs, 
       it.t0 = min(ck * tpc, tiles);
       it.t1 = min(ck * tpc + tpc, tiles);
       it.c = ck;
-      it.pad = 0;
+      it.limit = rv.limit;
+      it.off_lo = (int32_t)(uint32_t)(uint64_t)rv.off;
+      it.off_hi = (int32_t)(rv.off >> 32);
+      it.pad0 = it.pad1 = 0;
       share.items[base + t] = it;
     }
   }
