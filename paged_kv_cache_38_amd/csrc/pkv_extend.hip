@@ -412,6 +412,328 @@ __global__ void __launch_bounds__(256, ExtendCfg<D>::OCC) extend_kernel(DevMap m
 }
 
 // ---------------------------------------------------------------------------
+// The same extend with the two waves of each SIMD in opposite phases.
+//
+// A wave's work per 64-key tile t splits into a matrix phase, MM(t) = the
+// P V^T of tile t - 1 and the K Q^T of tile t, and a softmax phase SM(t)
+// (masks, row maxima, exponentials: vector ALU).  Eight waves share the
+// tiles; waves w and w + 4 sit on the same SIMD.  Group A (waves 0..3) runs
+// MM(t) while group B (waves 4..7) runs SM(t - 1), and then A runs SM(t)
+// while B runs MM(t), with a workgroup barrier between the halves, so each
+// SIMD has one wave on the matrix cores while the other is on the vector
+// ALU.  The two waves of a SIMD take adjacent row ranges, so a short query
+// block still pairs its waves.
+// ---------------------------------------------------------------------------
+template <int D>
+struct PpCfg {
+  static constexpr int RB = D == 64 ? 3 : 2;  // 16-row blocks per wave
+  static constexpr int W = 8;                 // waves per workgroup
+  static constexpr int WR = 16 * RB;          // query rows per wave
+  static constexpr int BM = W * WR;           // query rows per workgroup
+  static constexpr int NK = D / 32;
+  static constexpr int NT = D / 16;
+  static constexpr int CPK = D / 8;
+  static constexpr int TILE = kBN * D * 2;
+  static constexpr int NI = 2 * TILE / 1024 / W;  // K+V DMA instructions per wave per tile
+  static constexpr int S = D == 64 ? 5 : 4;       // LDS stages
+  static constexpr int R = S + 1;                 // table ring entries per wave (the prologue loads S at once)
+  // Iteration t issues the table of tile t + S and then the rows of tile
+  // t + S - 2.  Before its first barrier it needs tile t's rows and tile
+  // t + S - 2's table; the memory operations a wave may leave outstanding
+  // then are the smaller of those issued after either.
+  static constexpr int WAIT_ROWS = (S - 3) * (NI + 1) + 1;
+  static constexpr int WAIT_TAB = 2 * NI + 2;
+  static constexpr int WAIT = WAIT_ROWS < WAIT_TAB ? WAIT_ROWS : WAIT_TAB;
+  static constexpr int WAIT0 = (S - 3) * NI + 1;  // iteration 0: the prologue issued no tables between its tiles
+};
+
+template <int D, int FMT, bool SC>
+__global__ void __launch_bounds__(512, 1) extend_pp_kernel(DevMap m, const char* k_pool, const char* v_pool,
+                                                       int64_t row_bytes, const bf16* __restrict__ q, int64_t total_q,
+                                                       const int32_t* __restrict__ qo_indptr, int32_t Hq,
+                                                       int32_t n_req, int32_t n_qtiles, int32_t G, int32_t causal_all,
+                                                       const int32_t* __restrict__ causal_flags, SoftCap cap,
+                                                       float scale_log2, bf16* __restrict__ out,
+                                                       float* __restrict__ lse) {
+  using C = PpCfg<D>;
+  constexpr int NK = C::NK, NT = C::NT, CPK = C::CPK, NI = C::NI, S = C::S, R = C::R;
+  constexpr int kRB = C::RB, kWR = C::WR, kBM = C::BM;
+  static_assert(C::WAIT0 <= C::WAIT && C::WAIT < 64, "wait counts");
+  __shared__ __attribute__((aligned(1024))) char kv_lds[S][2][C::TILE];
+  __shared__ __attribute__((aligned(256))) int32_t tab_lds[C::W][R][64];
+
+  // block -> (pair, query tile) exactly as in extend_kernel
+  const int x = (int)(blockIdx.x & 7), k = (int)(blockIdx.x >> 3);
+  const int ppx = (int)(((int64_t)n_req * Hq + 7) / 8);
+  const bool qt_major = causal_all && !causal_flags;
+  const int pair = x + 8 * (qt_major ? k % ppx : k / n_qtiles);
+  const int qt = qt_major ? n_qtiles - 1 - k / ppx : k % n_qtiles;
+  const int h = pair % Hq;
+  const int i = pair / Hq;
+  if (i >= n_req) return;
+  const int causal = causal_flags ? (causal_flags[i] != 0) : causal_all;
+  const int q0 = qo_indptr[i];
+  const int n = (q0 < 0 || q0 >= total_q) ? 0 : (int)min((int64_t)(qo_indptr[i + 1] - q0), total_q - q0);
+  if (qt * kBM >= n) return;
+  int L = m.kv_lens[i];
+  if (FMT == SLOT_CONTIG && m.total_k <= 0) L = 0;
+  if (L < 0) L = 0;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int g = h / G;
+  const int grp_w = w >> 2;  // 0: group A, 1: group B
+  const int rw = qt * kBM + (2 * (w & 3) + grp_w) * kWR;  // the SIMD's two waves take adjacent rows
+
+  int kv_end = L;
+  if (causal) kv_end = min(L, L - n + min(qt * kBM + kBM, n));
+  if (kv_end < 0) kv_end = 0;
+  const int ntiles = (kv_end + kBN - 1) / kBN;
+  const int w_end = causal ? max(0, min(L, L - n + min(rw + kWR, n))) : L;
+  const int w_free = causal ? max(0, L - n + rw + 1) : L;
+  // tiles this wave computes (0 when its rows are all past n)
+  const int Tw = rw < n ? min(ntiles, (w_end + kBN - 1) / kBN) : 0;
+
+  bf16x8 qb[kRB][NK];
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) {
+    const int row = rw + rb * 16 + col;
+    const bool ok = row < n;
+    const bf16* qp = q + ((int64_t)(q0 + (ok ? row : 0)) * Hq + h) * D + grp * 8;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      u32x4 v = *reinterpret_cast<const u32x4*>(qp + kk * 32);
+      if (!ok) v = u32x4{0u, 0u, 0u, 0u};
+      qb[rb][kk] = as_bf16x8(v);
+    }
+  }
+  int row_end[kRB];
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) {
+    const int row = rw + rb * 16 + col;
+    row_end[rb] = causal ? min(L, L - n + row + 1) : L;
+  }
+
+  f32x4 acc[kRB][NT];
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[rb][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 acc_l[kRB];
+  float m_run[kRB];
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) {
+    acc_l[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[rb] = -INFINITY;
+  }
+
+  if (ntiles > 0) {
+    const SlotMap<FMT> sm = make_slotmap<FMT>(m, i);
+    const char* kb = k_pool + (int64_t)g * D * 2;
+    const char* vb = v_pool + (int64_t)g * D * 2;
+    auto tab_dma = [&](int kt) __attribute__((always_inline)) {
+      const int t = min(min(kt, ntiles - 1) * kBN + lane, kv_end - 1);
+      dma4(sm.raw_ptr(t), lds_off(&tab_lds[w][kt % R][0]));
+    };
+    int dt[NI / 2], dc[NI / 2];
+#pragma unroll
+    for (int j = 0; j < NI / 2; ++j) {
+      const unsigned pos = (unsigned)((w * (NI / 2) + j) * 64 + lane);
+      dt[j] = (int)(pos / CPK);
+      dc[j] = (int)(((pos % CPK) ^ (pos / CPK & 7)) * 16);
+    }
+    const uint32_t rbytes = (uint32_t)row_bytes;
+    auto kv_dma = [&](int kt) __attribute__((always_inline)) {
+      const int32_t* tr = &tab_lds[w][kt % R][0];
+      const int k0 = min(kt, ntiles - 1) * kBN;
+      char* kt_lds = kv_lds[kt % S][0];
+      char* vt_lds = kv_lds[kt % S][1];
+#pragma unroll
+      for (int j = 0; j < NI / 2; ++j) {
+        const int tt = min(k0 + dt[j], kv_end - 1);
+        const uint32_t slot = (uint32_t)sm.finish(tr[dt[j]], tt, true);
+        const uint64_t off = (uint64_t)slot * rbytes + (uint32_t)dc[j];
+        dma16(kb + off, lds_off(kt_lds + (w * (NI / 2) + j) * 1024));
+        dma16(vb + off, lds_off(vt_lds + (w * (NI / 2) + j) * 1024));
+      }
+    };
+    // prologue: the tables of tiles 0 .. S - 1 and the queries land (a wait
+    // the compiler sees), then the rows of tiles 0 .. S - 3
+    for (int kk = 0; kk < S; ++kk) tab_dma(kk);
+    __builtin_amdgcn_s_waitcnt(0);
+    for (int kk = 0; kk < S - 2; ++kk) kv_dma(kk);
+
+    const int sk = col & 7;
+    const int kbase0 = (col * CPK + (grp ^ sk)) * 16;
+    const int kbase1 = (col * CPK + ((4 + grp) ^ sk)) * 16;
+    int vbase[4];
+    {
+      const int xx = lane & 15, j = lane >> 4;
+      const int t = 4 * j + (xx >> 2);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) vbase[u] = (t * CPK + ((2 * u + ((xx & 3) >> 1)) ^ (t & 7))) * 16 + (xx & 1) * 8;
+    }
+    const char* lds0 = &kv_lds[0][0][0];
+    const bf16x8 ones = bf16x8{(bf16)1.f, (bf16)1.f, (bf16)1.f, (bf16)1.f, (bf16)1.f, (bf16)1.f, (bf16)1.f, (bf16)1.f};
+
+    f32x4 sacc[4][kRB];    // scores of the tile whose softmax is next
+    bf16x8 pa[kRB][2];     // probabilities of the tile whose P V^T is next
+
+    // K Q^T of the tile in stage st
+    auto qk = [&](auto stage_c) __attribute__((always_inline)) {
+      constexpr int st = decltype(stage_c)::value;
+      const char* ks = lds0 + (st * 2 + 0) * C::TILE;
+#pragma unroll
+      for (int a2 = 0; a2 < 4; ++a2)
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) sacc[a2][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        const char* kp = ks + ((kk & 1) ? kbase1 : kbase0) + (kk >> 1) * 128;
+#pragma unroll
+        for (int a2 = 0; a2 < 4; ++a2) {
+          const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(kp + a2 * 16 * CPK * 16));
+#pragma unroll
+          for (int rb = 0; rb < kRB; ++rb) sacc[a2][rb] = mfma16x16x32(ka, qb[rb][kk], sacc[a2][rb]);
+        }
+      }
+    };
+    // O^T += V^T P^T of the tile in stage st (row sums as a row of ones)
+    auto pv = [&](auto stage_c) __attribute__((always_inline)) {
+      constexpr int st = decltype(stage_c)::value;
+      const char* vs = lds0 + (st * 2 + 1) * C::TILE;
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const char* lo = vs + vbase[nt & 3] + (nt >> 2) * 128 + b2 * 32 * CPK * 16;
+          const i16x4 va = lds_read_tr16(reinterpret_cast<const bf16*>(lo));
+          const i16x4 vc = lds_read_tr16(reinterpret_cast<const bf16*>(lo + 16 * CPK * 16));
+          const bf16x4 ba = __builtin_bit_cast(bf16x4, va), bc = __builtin_bit_cast(bf16x4, vc);
+          const bf16x8 vf = bf16x8{ba[0], ba[1], ba[2], ba[3], bc[0], bc[1], bc[2], bc[3]};
+#pragma unroll
+          for (int rb = 0; rb < kRB; ++rb) acc[rb][nt] = mfma16x16x32(vf, pa[rb][b2], acc[rb][nt]);
+        }
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) acc_l[rb] = mfma16x16x32(ones, pa[rb][b2], acc_l[rb]);
+      }
+    };
+    // softmax of tile kt's scores into pa (softcap, masks, reference moves
+    // and rescales exactly as in extend_kernel)
+    auto smx = [&](int kt, auto mask_c) __attribute__((always_inline)) {
+      constexpr bool MASK = decltype(mask_c)::value;
+      const int k0 = kt * kBN;
+      if constexpr (SC) {
+#pragma unroll
+        for (int a2 = 0; a2 < 4; ++a2)
+#pragma unroll
+          for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) sacc[a2][rb][rr] = cap(sacc[a2][rb][rr]);
+      }
+      if (MASK) {
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) {
+          const int lim = row_end[rb] - k0 - grp * 4;
+#pragma unroll
+          for (int a2 = 0; a2 < 4; ++a2)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+              if (a2 * 16 + rr >= lim) sacc[a2][rb][rr] = -INFINITY;
+        }
+      }
+      float lane_max[kRB];
+      bool lane_bump = false;
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) {
+        float mr = -INFINITY;
+#pragma unroll
+        for (int a2 = 0; a2 < 4; ++a2)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) mr = fmaxf(mr, sacc[a2][rb][rr]);
+        lane_max[rb] = mr;
+        lane_bump |= mr * scale_log2 > m_run[rb] + kExtSlack;
+      }
+      if (__builtin_amdgcn_ballot_w64(lane_bump) != 0) {
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) {
+          const float m_tile = max_xor16_32(lane_max[rb]) * scale_log2;
+          const bool bump = m_tile > m_run[rb] + kExtSlack;
+          const float alpha = bump ? fast_exp2(m_run[rb] - m_tile) : 1.0f;
+          m_run[rb] = bump ? m_tile : m_run[rb];
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) acc[rb][nt] *= alpha;
+          acc_l[rb] *= alpha;
+        }
+      }
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) {
+        const float mu = m_run[rb] == -INFINITY ? 0.f : m_run[rb];
+#pragma unroll
+        for (int a2 = 0; a2 < 4; ++a2)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            pa[rb][a2 >> 1][(a2 & 1) * 4 + rr] = (bf16)fast_exp2(fmaf(sacc[a2][rb][rr], scale_log2, -mu));
+      }
+    };
+    auto SM = [&](int kt) __attribute__((always_inline)) {
+      if (kt >= 0 && kt < Tw) {
+        if (kt * kBN + kBN <= w_free) smx(kt, std::false_type{});
+        else smx(kt, std::true_type{});
+      }
+    };
+    // MM(t): P V^T of tile t - 1 (stage SP), K Q^T of tile t (stage SK)
+    auto MM = [&](int t, auto sk_c, auto sp_c) __attribute__((always_inline)) {
+      if (t >= 1 && t - 1 < Tw) pv(sp_c);
+      if (t < Tw) qk(sk_c);
+    };
+    // iteration t (stage j = t % S): slot 2t then slot 2t + 1
+    auto iter = [&](int t, auto j_c) __attribute__((always_inline)) {
+      constexpr int j = decltype(j_c)::value;
+      tab_dma(t + S);
+      if (t == 0) wait_vm<C::WAIT0>();
+      else wait_vm<C::WAIT>();
+      __syncthreads();     // tile t in LDS; every wave past slot 2t - 1
+      kv_dma(t + S - 2);   // into the stage of tile t - 2 (last read in slot 2t - 1)
+      if (grp_w == 0) MM(t, std::integral_constant<int, j>{}, std::integral_constant<int, (j + S - 1) % S>{});
+      else SM(t - 1);
+      __syncthreads();
+      if (grp_w == 0) SM(t);
+      else MM(t, std::integral_constant<int, j>{}, std::integral_constant<int, (j + S - 1) % S>{});
+    };
+    static_assert(S == 4 || S == 5, "the iteration loop is unrolled for four or five stages");
+    for (int tb = 0; tb <= ntiles; tb += S) {
+      iter(tb, std::integral_constant<int, 0>{});
+      if (tb + 1 <= ntiles) iter(tb + 1, std::integral_constant<int, 1>{});
+      if (tb + 2 <= ntiles) iter(tb + 2, std::integral_constant<int, 2>{});
+      if (tb + 3 <= ntiles) iter(tb + 3, std::integral_constant<int, 3>{});
+      if constexpr (S > 4) {
+        if (tb + 4 <= ntiles) iter(tb + 4, std::integral_constant<int, 4 % S>{});
+      }
+    }
+    wait_vm<0>();  // no load may still target this block's LDS when it ends
+  }
+
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) {
+    const int row = rw + rb * 16 + col;
+    if (row < n) {
+      const int64_t o = ((int64_t)(q0 + row) * Hq + h);
+      const float lt = acc_l[rb][0];
+      const bool any = lt > 0.f;
+      const float inv = any ? 1.0f / lt : 0.f;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        bf16x4 v;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) v[rr] = (bf16)(acc[rb][nt][rr] * inv);
+        *reinterpret_cast<bf16x4*>(out + o * D + nt * 16 + grp * 4) = v;
+      }
+      if (lse && grp == 0) lse[o] = any ? (m_run[rb] + __log2f(lt)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 pools: the same attention on the vector ALUs, in fp32 throughout.  One
 // wavefront per (request, query head, four query rows): lane group r = lane
 // / 16 holds row r, and lane c = lane % 16 holds elements [c E, c E + E) of
@@ -577,13 +899,19 @@ static void launch_ext_f32_fmt(hipStream_t s, const DevMap& m, const char* kp, c
 template <int D, int FMT>
 static void launch_ext(dim3 grid, hipStream_t s, const DevMap& m, const char* kp, const char* vp, int64_t row_bytes,
                        const void* q, int64_t tq, const int32_t* qo, int32_t Hq, int32_t G, int32_t causal,
-                       const int32_t* flags, float softcap, float sm_scale, void* out, float* lse) {
+                       const int32_t* flags, float softcap, float sm_scale, void* out, float* lse, bool pp) {
   const int32_t qtiles = (int32_t)grid.y;
   const int32_t nreq = (int32_t)grid.z;
   const int64_t pairs = (int64_t)nreq * Hq;
   const dim3 g1((unsigned)(8 * ((pairs + 7) / 8) * qtiles));
   const float sl2 = sm_scale * kLog2e;
-  if (softcap > 0.0f) {
+  // pp: the phase-alternating kernel (see launch_extend)
+  if (pp) {
+    const SoftCap cap{2.0f * kLog2e * sm_scale / softcap, softcap / sm_scale};
+    hipLaunchKernelGGL((extend_pp_kernel<D, FMT, true>), g1, dim3(512), 0, s, m, kp, vp, row_bytes,
+                       static_cast<const bf16*>(q), tq, qo, Hq, nreq, qtiles, G, causal, flags, cap, sl2,
+                       static_cast<bf16*>(out), lse);
+  } else if (softcap > 0.0f) {
     const SoftCap cap{2.0f * kLog2e * sm_scale / softcap, softcap / sm_scale};
     hipLaunchKernelGGL((extend_kernel<D, FMT, true>), g1, dim3(256), 0, s, m, kp, vp, row_bytes,
                        static_cast<const bf16*>(q), tq, qo, Hq, nreq, qtiles, G, causal, flags, cap, sl2,
@@ -599,16 +927,16 @@ template <int D>
 static void launch_ext_fmt(dim3 grid, hipStream_t s, const DevMap& m, const char* kp, const char* vp,
                            int64_t row_bytes, const void* q, int64_t tq, const int32_t* qo, int32_t Hq, int32_t G,
                            int32_t causal, const int32_t* flags, float softcap, float sm_scale, void* out,
-                           float* lse) {
+                           float* lse, bool pp) {
   if (m.fmt == MAP_TOKEN_TABLE)
     launch_ext<D, SLOT_TABLE>(grid, s, m, kp, vp, row_bytes, q, tq, qo, Hq, G, causal, flags, softcap, sm_scale, out,
-                              lse);
+                              lse, pp);
   else if (m.fmt == MAP_CONTIGUOUS)
     launch_ext<D, SLOT_CONTIG>(grid, s, m, kp, vp, row_bytes, q, tq, qo, Hq, G, causal, flags, softcap, sm_scale, out,
-                               lse);
+                               lse, pp);
   else
     launch_ext<D, SLOT_PAGES>(grid, s, m, kp, vp, row_bytes, q, tq, qo, Hq, G, causal, flags, softcap, sm_scale, out,
-                              lse);
+                              lse, pp);
 }
 
 hipError_t launch_extend(const PoolInfo& p, int32_t layer, const void* q, int64_t total_q, const int32_t* qo_indptr,
@@ -635,17 +963,25 @@ hipError_t launch_extend(const PoolInfo& p, int32_t layer, const void* q, int64_
     return e;
   }
   // (query tiles, -, requests); the launcher flattens it XCD-aware
-  const int bm = p.head_dim_qk == 128 ? ExtendCfg<128>::BM : ExtendCfg<64>::BM;
+  // The phase-alternating kernel (extend_pp_kernel) pays where the softmax
+  // phase is heavy (a softcap adds an exp2 and a reciprocal per score) and
+  // the query blocks fill its larger workgroups (at least one on average):
+  // measured, softcapped mixed spans 0.40 -> 0.375 ms; uncapped mixed spans
+  // 0.31 -> 0.33 and the encoder-decoder extend 0.17 -> 0.32 ms (short
+  // blocks leave a CU with one mostly empty workgroup).
+  const int pp_bm = p.head_dim_qk == 128 ? PpCfg<128>::BM : PpCfg<64>::BM;
+  const bool pp = softcap > 0.0f && total_q >= (int64_t)bs * pp_bm;
+  const int bm = pp ? pp_bm : (p.head_dim_qk == 128 ? ExtendCfg<128>::BM : ExtendCfg<64>::BM);
   const dim3 grid(1, (unsigned)((max_q_len + bm - 1) / bm), (unsigned)bs);
   const int64_t row_bytes = (int64_t)p.num_kv_heads * p.head_dim_qk * 2;  // one token row, all KV heads
   if (row_bytes > (int64_t)UINT32_MAX) return hipErrorInvalidValue;  // the kernel's row offsets are 32-bit
   timer_before(s);
   if (p.head_dim_qk == 128)
     launch_ext_fmt<128>(grid, s, m, kp, vp, row_bytes, q, total_q, qo_indptr, Hq, G, causal, causal_flags, softcap,
-                        sm_scale, out, lse);
+                        sm_scale, out, lse, pp);
   else
     launch_ext_fmt<64>(grid, s, m, kp, vp, row_bytes, q, total_q, qo_indptr, Hq, G, causal, causal_flags, softcap,
-                       sm_scale, out, lse);
+                       sm_scale, out, lse, pp);
   hipError_t e = hipGetLastError();
   timer_after(s);
   return e;

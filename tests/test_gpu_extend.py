@@ -170,6 +170,29 @@ def test_softcap_matches_oracle(softcap, head_dim):
 
 
 @pytest.mark.parametrize("head_dim", [64, 128])
+@pytest.mark.parametrize("fmt", [P.PKV_MAP_CSR, P.PKV_MAP_BLOCK_TABLE])
+def test_softcap_long_blocks_match_oracle(head_dim, fmt):
+    """Softcapped segments long enough on average (600 query rows per
+    request) for the phase-alternating kernel: causal 700-row and full
+    500-row segments over a shared row of keys, GQA 4, several query tiles
+    per segment and the causal diagonal inside them; every row against the
+    oracle, and the ragged variant bit for bit."""
+    case = W.mixed_spans(seed=14, rows=2, spans=((700, True), (500, False)), num_q_heads=8, num_kv_heads=2,
+                         head_dim=head_dim)
+    print(f"softcap long blocks d{head_dim} fmt {fmt}: q rows {int(case.q_lens.sum())}", flush=True)
+    vals = W.make_values(case, canary=True)
+    vals["q"] = {k: (v.float() * 4).to(v.dtype) for k, v in vals["q"].items()}  # so the cap bites
+    dc = DeviceCase(case, vals)
+    dc.store()
+    out, lse = run_extend(dc, "self", fmt, softcap=20.0)
+    ref_o, ref_l = oracle_region(case, vals, "self", softcap=20.0)
+    assert_attn_close(out, ref_o, "bf16", f"softcap long blocks d{head_dim}")
+    assert_lse_close(lse, ref_l, "bf16", f"softcap long blocks d{head_dim}")
+    out2, _ = run_extend(dc, "self", P.PKV_MAP_TOKEN_TABLE, contiguous=True, softcap=20.0)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+@pytest.mark.parametrize("head_dim", [64, 128])
 def test_long_causal_prefill_matches_oracle(head_dim):
     """One 3000-token causal prefill (16 query tiles of the diagonal, every
     mask boundary) followed by a 1000-token full span over all 4000 keys."""
