@@ -29,14 +29,15 @@
 //  * Math.  Each wave owns 32 query heads (16 when there are fewer than 128)
 //    end to end: S^T = K Q^T with the queries in registers, the softmax, and
 //    O += P V over all 512 value columns with the accumulators in AGPRs, P
-//    going straight from the score registers into the MFMA A operand.  Every
-//    K and V fragment read from LDS feeds two MFMAs (two 16-head blocks),
-//    and one barrier per tile is the only synchronisation.  The softmax
-//    reference is the maximum of a piece's first tile and then stays fixed,
-//    so the accumulators are never rescaled (any reference gives the same
-//    normalised result); should a later score exceed it by more than 2^64 (P
-//    could overflow), the request is recomputed exactly by a fallback in the
-//    merge pass.
+//    going straight from the score registers into the MFMA A operand.  The
+//    scores come in two halves of 16 tokens with their results in VGPRs.
+//    Every K and V fragment read from LDS feeds two MFMAs (two 16-head
+//    blocks), and one barrier per tile is the only synchronisation.  The
+//    softmax reference is the maximum over the first half of a piece's first
+//    tile and then stays fixed, so the accumulators are never rescaled (any
+//    reference gives the same normalised result); should a later score
+//    exceed it by more than 2^64 (P could overflow), the request is
+//    recomputed exactly by a fallback in the merge pass.
 #include <math.h>
 
 #include <algorithm>
@@ -86,40 +87,57 @@ __device__ __forceinline__ float acc_get(float a) {
   return v;
 }
 
-// O += P V for one tile over all 32 column blocks of the wave's HB head
-// blocks.  The B operand of column block cb = 4 m + u comes from two
+// One MFMA of the score product, issued from inline assembly so that its
+// result lands in VGPRs.  Left to the compiler, every MFMA of this kernel
+// takes the AGPR-result form: the score accumulators would then claim AGPRs
+// beside the 256 P*V accumulators, and the compiler would shuttle
+// accumulators between the register files on every tile.  Opaque to the
+// compiler, the asm carries the wait states the hardware needs after a
+// half's last MFMA: the 19 that cover a VALU read of a 16-pass result.  Its
+// operands come from LDS reads and global loads, never from a VALU write
+// just before it (which would need two more wait states; a test checks the
+// built code for that).  FIRST starts the accumulator from zero.
+__device__ __forceinline__ void mfma_score(f32x4& c, const bf16x8& a, const bf16x8& b, bool first, bool tail) {
+  if (first)
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+  else if (tail)
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 2" : "+v"(c) : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+
+// V operand reads of column group m (column blocks 4 m .. 4 m + 3) for
+// O += P V.  The B operand of column block cb = 4 m + u comes from two
 // transposed reads: lane (x, j) starts at token t = 4 j + x / 4, chunk
 // 8 m + ((2 u + (x & 3) / 2) ^ (t & 7)), so four per-lane bases (u) plus
 // compile-time offsets cover every read; lane (x, j) then holds
 // V[4j + r][16 cb + x] and V[16 + 4j + r][16 cb + x] (r = 0..3), the token
-// order of the P fragment the score layout leaves in the lane.  ZERO starts
-// the accumulators from zero inside the MFMA.
+// order of the P fragment the score layout leaves in the lane.
+__device__ __forceinline__ void mla_v_group(const char* tile, int lane, int m, bf16x8 (&vf)[4]) {
+  const int x = lane & 15, jg = lane >> 4;
+  const int t = 4 * jg + (x >> 2);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const char* lo = tile + t * kMlaMainBytes + ((2 * u + ((x & 3) >> 1)) ^ (t & 7)) * 16 + (x & 1) * 8 + m * 128;
+    const i16x4 va = lds_read_tr16(reinterpret_cast<const bf16*>(lo));
+    const i16x4 vc = lds_read_tr16(reinterpret_cast<const bf16*>(lo + 16 * kMlaMainBytes));
+    const bf16x4 ba = __builtin_bit_cast(bf16x4, va), bc = __builtin_bit_cast(bf16x4, vc);
+    vf[u] = bf16x8{ba[0], ba[1], ba[2], ba[3], bc[0], bc[1], bc[2], bc[3]};
+  }
+}
+
+// O += P V for one tile over all 32 column blocks of the wave's HB head
+// blocks.  ZERO starts the accumulators from zero inside the MFMA.
 template <int HB, bool ZERO>
 __device__ __forceinline__ void mla_pv(f32x4 (&acc)[HB][kMlaV / 16], const char* tile, const bf16x8 (&pa)[HB],
                                        int lane) {
-  const int x = lane & 15, jg = lane >> 4;
-  const int t = 4 * jg + (x >> 2);
-  const char* vb[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-    vb[u] = tile + t * kMlaMainBytes + ((2 * u + ((x & 3) >> 1)) ^ (t & 7)) * 16 + (x & 1) * 8;
-  auto vload = [&](int m, bf16x8* vf) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const char* lo = vb[u] + m * 128;
-      const i16x4 va = lds_read_tr16(reinterpret_cast<const bf16*>(lo));
-      const i16x4 vc = lds_read_tr16(reinterpret_cast<const bf16*>(lo + 16 * kMlaMainBytes));
-      const bf16x4 ba = __builtin_bit_cast(bf16x4, va), bc = __builtin_bit_cast(bf16x4, vc);
-      vf[u] = bf16x8{ba[0], ba[1], ba[2], ba[3], bc[0], bc[1], bc[2], bc[3]};
-    }
-  };
   // groups of four column blocks, the next group's reads in flight while
   // this group's MFMAs run
   bf16x8 vf[2][4];
-  vload(0, vf[0]);
+  mla_v_group(tile, lane, 0, vf[0]);
 #pragma unroll
   for (int m = 0; m < kMlaV / 64; ++m) {
-    if (m + 1 < kMlaV / 64) vload(m + 1, vf[(m + 1) & 1]);
+    if (m + 1 < kMlaV / 64) mla_v_group(tile, lane, m + 1, vf[(m + 1) & 1]);
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
@@ -264,122 +282,112 @@ __global__ void __launch_bounds__(64 * W, 1) mla_decode_kernel(
       __builtin_amdgcn_s_waitcnt(0);
     }
 
-    // ---- S^T = K Q^T for this wave's heads.  Chunk 4kk + grp (kk < 16) of
-    // token t sits at 8 (kk / 2) + ((4 (kk & 1) + grp) ^ (t & 7)) of its main
-    // row: two per-lane bases (even / odd kk) plus compile-time offsets.
-    // kk = 16, 17 read the tail part, whose row of token 16a + col is
-    // ((16a + col) % W) RPW + (16a + col) / W.
-    f32x4 sacc[2][HB];
-    {
-      const int t = col;  // token 16a + col; (t & 7) is the same for a = 0, 1
-      const char* kb_even = tile + t * kMlaMainBytes + (grp ^ (t & 7)) * 16;
-      const char* kb_odd = tile + t * kMlaMainBytes + ((4 + grp) ^ (t & 7)) * 16;
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb) sacc[a][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      // K fragments stream through a window of KD k-steps (2 fragments each);
-      // a sched barrier per step keeps the compiler from hoisting all 36
-      // reads
-      constexpr int KD = 3;
-      bf16x8 kf[KD][2];
-      auto kload = [&](int kk, bf16x8* dst) {
-        if (kk < 16) {
-          const char* kb = (kk & 1) ? kb_odd : kb_even;
-#pragma unroll
-          for (int a = 0; a < 2; ++a)
-            dst[a] = as_bf16x8(*reinterpret_cast<const u32x4*>(kb + a * 16 * kMlaMainBytes + (kk >> 1) * 128));
-        } else {
-#pragma unroll
-          for (int a = 0; a < 2; ++a) {
-            const int ta = 16 * a + col;
-            const char* tb = tile + kMlaTailOff + ((ta % W) * RPW + ta / W) * 128 +
-                             ((4 * (kk & 1) + grp) ^ (ta & 7)) * 16;
-            dst[a] = as_bf16x8(*reinterpret_cast<const u32x4*>(tb));
-          }
-        }
-      };
-#pragma unroll
-      for (int kk = 0; kk < KD - 1; ++kk) kload(kk, kf[kk]);
-#pragma unroll
-      for (int kk = 0; kk < NK; ++kk) {
-        if (kk + KD - 1 < NK) kload(kk + KD - 1, kf[(kk + KD - 1) % KD]);
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-          for (int hb = 0; hb < HB; ++hb) sacc[a][hb] = mfma16x16x32(kf[kk % KD][a], qf[hb][kk], sacc[a][hb]);
-        __builtin_amdgcn_sched_barrier(0);
+    // ---- S^T = K Q^T and the softmax (log2 domain), in two halves of 16
+    // tokens (a = 0, 1), so that one half's scores take 8 VGPRs.  Chunk
+    // 4kk + grp (kk < 16) of token t sits at 8 (kk / 2) + ((4 (kk & 1) + grp)
+    // ^ (t & 7)) of its main row: two per-lane bases (even / odd kk) plus
+    // compile-time offsets.  kk = 16, 17 read the tail part, whose row of
+    // token 16a + col is ((16a + col) % W) RPW + (16a + col) / W.
+    const char* kb_even = tile + col * kMlaMainBytes + (grp ^ (col & 7)) * 16;
+    const char* kb_odd = tile + col * kMlaMainBytes + ((4 + grp) ^ (col & 7)) * 16;
+    auto kload = [&](int a, int kk) -> bf16x8 {
+      if (kk < 16) {
+        const char* kb = (kk & 1) ? kb_odd : kb_even;
+        return as_bf16x8(*reinterpret_cast<const u32x4*>(kb + a * 16 * kMlaMainBytes + (kk >> 1) * 128));
       }
-    }
-
-    tile_dma(r + 3, vs_next, std::integral_constant<int, 1>{});
-
-    // ---- softmax (log2 domain) for head hw + 16 hb + col; this lane holds
-    // tokens 16a + 4 grp + rr, which is also the token order of P as the A
-    // operand of P*V.  The reference maximum is the first tile's maximum
-    // and stays fixed for the piece, so the accumulators are never
-    // rescaled; a later score more than kMlaHeadroom above it (P could
-    // overflow) sends the request to the exact fallback in the merge pass.
-    // keys past the request's end (its last tile only) get -inf in place;
-    // VERIFY: so do keys past each draft's position, in the tiles that
-    // reach past the first draft's
-    if constexpr (VERIFY) {
-      if (valid < kMlaT || jt * kMlaT + kMlaT > k_zone) {
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb) {
-          int c = col;
-          asm volatile("" : "+v"(c));  // recomputed here, not held across the loop (registers)
-          const int jrow = (row_off + hw + hb * 16 + c) / hq_base;  // this row's draft
-          const int lim = min(valid, k_zone + jrow - jt * kMlaT);
-#pragma unroll
-          for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr)
-              if (16 * a + 4 * grp + rr >= lim) sacc[a][hb][rr] = -INFINITY;
-        }
-      }
-    } else if (valid < kMlaT) {
-#pragma unroll
-      for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr)
-            if (16 * a + 4 * grp + rr >= valid) sacc[a][hb][rr] = -INFINITY;
-    }
-    // the scale is positive (checked at the boundary): maxima and the
-    // overflow test work on raw scores, each probability is one fma + exp2
+      const int ta = 16 * a + col;
+      const char* tb = tile + kMlaTailOff + ((ta % W) * RPW + ta / W) * 128 + ((4 * (kk & 1) + grp) ^ (ta & 7)) * 16;
+      return as_bf16x8(*reinterpret_cast<const u32x4*>(tb));
+    };
+    // This lane holds tokens 16a + 4 grp + rr of head hw + 16 hb + col,
+    // which is also the token order of P as the A operand of P*V.  The
+    // reference maximum is taken over the first half of a piece's first tile
+    // and stays fixed for the piece, so the accumulators are never rescaled
+    // (any reference gives the same normalised result); a later score more
+    // than kMlaHeadroom above it (P could overflow) sends the request to the
+    // exact fallback in the merge pass.  Keys past the request's end (its
+    // last tile only) get -inf in place; VERIFY: so do keys past each draft's
+    // position, in the tiles that reach past the first draft's.  The scale
+    // is positive (checked at the boundary): maxima and the overflow test
+    // work on raw scores, each probability is one fma + exp2.
+    // One stream of 2 x 18 k-steps, the first half's then the second's, the
+    // K fragments KD - 1 steps ahead of their MFMAs across the half
+    // boundary, so the first half's softmax runs with the second half's
+    // first reads in flight.
+    constexpr int KD = 5;  // K fragments: four k-steps (eight MFMAs) ahead
+    bf16x8 kf[KD];
+    f32x4 sh[2][HB];
     bool over = false;
     bf16x8 pa[HB];
+    float ps[HB];
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
-      if (seg_begin) {
-        float mt = -INFINITY;
+    for (int g = 0; g < KD - 1; ++g) kf[g] = kload(g / NK, g % NK);
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < 2; ++a) {
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) mt = fmaxf(mt, sacc[a][hb][rr]);
-        m_ref[hb] = max_xor16_32(mt) * scale_log2;
-        // VERIFY: a draft that sees none of the piece's first tile sees none
-        // of the piece (keys only grow): any finite reference gives P = 0
-        if constexpr (VERIFY) m_ref[hb] = m_ref[hb] == -INFINITY ? 0.f : m_ref[hb];
-        s_over[hb] = (m_ref[hb] + kMlaHeadroom) / scale_log2;
+      for (int kk = 0; kk < NK; ++kk) {
+        const int g = a * NK + kk;
+        // the read of a later step goes out between this step's first and
+        // second MFMA (the wave stalls at an MFMA until the previous one has
+        // issued, so a read placed after both would leave later)
+        mfma_score(sh[a][0], kf[g % KD], qf[0][kk], kk == 0, HB == 1 && kk == NK - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (g + KD - 1 < 2 * NK) kf[(g + KD - 1) % KD] = kload((g + KD - 1) / NK, (g + KD - 1) % NK);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int hb = 1; hb < HB; ++hb)
+          mfma_score(sh[a][hb], kf[g % KD], qf[hb][kk], kk == 0, hb == HB - 1 && kk == NK - 1);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      float ps = 0.f;
+      if (a == 0) tile_dma(r + 3, vs_next, std::integral_constant<int, 1>{});
+      if constexpr (VERIFY) {
+        if (valid < kMlaT || jt * kMlaT + kMlaT > k_zone) {
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
+          for (int hb = 0; hb < HB; ++hb) {
+            int c = col;
+            asm volatile("" : "+v"(c));  // recomputed here, not held across the loop (registers)
+            const int jrow = (row_off + hw + hb * 16 + c) / hq_base;  // this row's draft
+            const int lim = min(valid, k_zone + jrow - jt * kMlaT);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+              if (16 * a + 4 * grp + rr >= lim) sh[a][hb][rr] = -INFINITY;
+          }
+        }
+      } else if (valid < kMlaT) {
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            if (16 * a + 4 * grp + rr >= valid) sh[a][hb][rr] = -INFINITY;
+      }
+      // (written out here rather than as a lambda over sh[a]: passing the
+      // array by reference kept it out of registers)
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        const float mx = fmaxf(fmaxf(sh[a][hb][0], sh[a][hb][1]), fmaxf(sh[a][hb][2], sh[a][hb][3]));
+        if (a == 0 && seg_begin) {
+          m_ref[hb] = max_xor16_32(mx) * scale_log2;
+          // VERIFY: a draft that sees none of the piece's first tile sees
+          // none of the piece (keys only grow), and one that sees none of
+          // its first half sees none of the tile: any finite reference
+          // gives P = 0
+          if constexpr (VERIFY) m_ref[hb] = m_ref[hb] == -INFINITY ? 0.f : m_ref[hb];
+          s_over[hb] = (m_ref[hb] + kMlaHeadroom) / scale_log2;
+        }
+        over |= mx > s_over[hb];
+        float sum = 0.f;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          const float sv = sacc[a][hb][rr];
-          over |= sv > s_over[hb];
-          const float p = fast_exp2(fmaf(sv, scale_log2, -m_ref[hb]));
-          ps += p;
+          const float p = fast_exp2(fmaf(sh[a][hb][rr], scale_log2, -m_ref[hb]));
+          sum += p;
           pa[hb][a * 4 + rr] = (bf16)p;
         }
-      l_part[hb] += ps;
+        ps[hb] = a == 0 ? sum : ps[hb] + sum;
+      }
     }
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) l_part[hb] += ps[hb];
     if (__builtin_amdgcn_ballot_w64(over) != 0 && lane == 0) fallback[i] = 1;
-
     tile_dma(r + 3, vs_next, std::integral_constant<int, 2>{});
 
     // ---- O += P V over all columns of this wave's heads (the first tile of
