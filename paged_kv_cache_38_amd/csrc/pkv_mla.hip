@@ -191,13 +191,28 @@ __global__ void __launch_bounds__(64 * W, 1) mla_decode_kernel(
   // chunks 0..63 into the main part, from the row's address in SGPRs (slot
   // id via v_readlane), lane l fetching chunk l ^ (row & 7); and per eight
   // rows one 64-lane DMA of their chunks 64..71 into the tail part (lane l:
-  // row l / 8 of the group, slot via ds_bpermute).  Part p of 3 issues rows
-  // [p RPW / 3, (p + 1) RPW / 3) of the wave and, with the last part, the
-  // tail DMAs: the main loop spreads a tile's DMAs over its phases.
+  // row l / 8 of the group, its slot read from the ring by tail_slots).
+  // Part p of 3 issues rows [p RPW / 3, (p + 1) RPW / 3) of the wave and,
+  // with the last part, the tail DMAs: the main loop spreads a tile's DMAs
+  // over its phases.
   const int wu = __builtin_amdgcn_readfirstlane(w);
-  auto tile_dma = [&](int r, int32_t vslot, auto part_c) {
+  struct TailSlots {
+    int32_t s[RPW / 8];
+  };
+  auto tail_slots = [&](int r) {
+    TailSlots ts;
+#pragma unroll
+    for (int g8 = 0; g8 < RPW / 8; ++g8)
+      ts.s[g8] = meta_lds[w][r & (kMlaMetaRing - 1)][(g8 * 8 + (lane >> 3)) * W + wu];
+    return ts;
+  };
+  auto tile_dma = [&](int r, int32_t vslot, TailSlots ts, auto part_c) {
     constexpr int p = decltype(part_c)::value;
     char* buf = tiles[r % kMlaBufs];
+    // pinned here: without it the slot reads and address arithmetic of every
+    // part get hoisted to the top of the tile, where they wait for the LDS
+    // read of the slots before the first score step can start
+    asm volatile("" : "+v"(vslot));
 #pragma unroll
     for (int k = p * RPW / 3; k < (p + 1) * RPW / 3; ++k) {
       const int t = k * W + wu;
@@ -207,11 +222,12 @@ __global__ void __launch_bounds__(64 * W, 1) mla_decode_kernel(
     }
     if constexpr (p == 2) {
 #pragma unroll
+      for (int g8 = 0; g8 < RPW / 8; ++g8) asm volatile("" : "+v"(ts.s[g8]));
+#pragma unroll
       for (int g8 = 0; g8 < RPW / 8; ++g8) {
         const int k = g8 * 8 + (lane >> 3);
         const int t = k * W + wu;
-        const int64_t slot = __shfl(vslot, t, 64);
-        const char* src = kpool + slot * kMlaRowBytes + (64 + ((lane & 7) ^ (t & 7))) * 16;
+        const char* src = kpool + (int64_t)ts.s[g8] * kMlaRowBytes + (64 + ((lane & 7) ^ (t & 7))) * 16;
         dma16(src, lds_off(buf + kMlaTailOff + (wu * RPW + g8 * 8) * 128));
       }
     }
@@ -242,25 +258,26 @@ __global__ void __launch_bounds__(64 * W, 1) mla_decode_kernel(
   for (int k = 0; k < 3; ++k) {
     meta_dma(k + 3);
     const int32_t vs = tile_slots(k);
-    tile_dma(k, vs, std::integral_constant<int, 0>{});
-    tile_dma(k, vs, std::integral_constant<int, 1>{});
-    tile_dma(k, vs, std::integral_constant<int, 2>{});
+    const TailSlots ts = tail_slots(k);
+    tile_dma(k, vs, ts, std::integral_constant<int, 0>{});
+    tile_dma(k, vs, ts, std::integral_constant<int, 1>{});
+    tile_dma(k, vs, ts, std::integral_constant<int, 2>{});
   }
+  // the info words of a tile (request, tile of the request, tiles of the
+  // request, first tile of the request, valid keys) are loaded into SGPRs
+  // one tile ahead, so their LDS latency never sits at the top of a tile
+  auto tile_info = [&](int r, int k) { return __builtin_amdgcn_readlane(meta_lds[w][r & (kMlaMetaRing - 1)][32 + min(lane, 4)], k); };
+  int i = tile_info(0, 0), jt = tile_info(0, 1), T = tile_info(0, 2), P = tile_info(0, 3), valid = tile_info(0, 4);
 
   for (int r = 0; r < n; ++r) {
     meta_dma(r + 6);
     wait_vm<kWait>();   // tile(r) (and every meta before it) has landed
     __syncthreads();    // tile r visible to all waves; every wave is past tile r - 1
-    // tile r + 3 goes into the buffer tile r - 1 used, in three parts
+    // tile r + 3 goes into the buffer tile r - 1 used, in three parts; its
+    // slot ids are read here and used a few score steps later
     const int32_t vs_next = tile_slots(r + 3);
-    tile_dma(r + 3, vs_next, std::integral_constant<int, 0>{});
-
-    const int32_t* info = &meta_lds[w][r & (kMlaMetaRing - 1)][32];
-    const int i = __builtin_amdgcn_readfirstlane(info[0]);
-    const int jt = __builtin_amdgcn_readfirstlane(info[1]);
-    const int T = __builtin_amdgcn_readfirstlane(info[2]);
-    const int P = __builtin_amdgcn_readfirstlane(info[3]);
-    const int valid = __builtin_amdgcn_readfirstlane(info[4]);
+    const TailSlots ts_next = tail_slots(r + 3);
+    const int32_t info_next = meta_lds[w][(r + 1) & (kMlaMetaRing - 1)][32 + min(lane, 4)];
     const bool seg_begin = (r == 0) || (jt == 0);
     const bool seg_end = (r == n - 1) || (jt == T - 1);
     const char* tile = tiles[r % kMlaBufs];
@@ -327,6 +344,7 @@ __global__ void __launch_bounds__(64 * W, 1) mla_decode_kernel(
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
         const int g = a * NK + kk;
+        if (a == 0 && kk == 4) tile_dma(r + 3, vs_next, ts_next, std::integral_constant<int, 0>{});
         // the read of a later step goes out between this step's first and
         // second MFMA (the wave stalls at an MFMA until the previous one has
         // issued, so a read placed after both would leave later)
@@ -339,7 +357,7 @@ __global__ void __launch_bounds__(64 * W, 1) mla_decode_kernel(
           mfma_score(sh[a][hb], kf[g % KD], qf[hb][kk], kk == 0, hb == HB - 1 && kk == NK - 1);
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (a == 0) tile_dma(r + 3, vs_next, std::integral_constant<int, 1>{});
+      if (a == 0) tile_dma(r + 3, vs_next, ts_next, std::integral_constant<int, 1>{});
       if constexpr (VERIFY) {
         if (valid < kMlaT || jt * kMlaT + kMlaT > k_zone) {
 #pragma unroll
@@ -388,7 +406,7 @@ __global__ void __launch_bounds__(64 * W, 1) mla_decode_kernel(
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) l_part[hb] += ps[hb];
     if (__builtin_amdgcn_ballot_w64(over) != 0 && lane == 0) fallback[i] = 1;
-    tile_dma(r + 3, vs_next, std::integral_constant<int, 2>{});
+    tile_dma(r + 3, vs_next, ts_next, std::integral_constant<int, 2>{});
 
     // ---- O += P V over all columns of this wave's heads (the first tile of
     // a piece starts the accumulators from zero inside the MFMA)
@@ -433,6 +451,11 @@ __global__ void __launch_bounds__(64 * W, 1) mla_decode_kernel(
       // no zeroing here: the next piece's first tile starts the
       // accumulators from zero inside the MFMA
     }
+    i = __builtin_amdgcn_readlane(info_next, 0);
+    jt = __builtin_amdgcn_readlane(info_next, 1);
+    T = __builtin_amdgcn_readlane(info_next, 2);
+    P = __builtin_amdgcn_readlane(info_next, 3);
+    valid = __builtin_amdgcn_readlane(info_next, 4);
   }
   wait_vm<0>();  // no load may still target this workgroup's LDS when it ends
 }
