@@ -140,8 +140,8 @@ __device__ __forceinline__ void decode_compute(const DecodeTile<D>& T, int t0, i
   constexpr int VIT = DecodeTile<D>::VIT;
   constexpr int NT = D / 16;
   constexpr int LDS = D + 8;
-  const int col = lane & 15, grp = lane >> 4;
-  // ---- S^T = K Q^T  (rows: tokens a*16 + 4*grp + rr; column: head col)
+  const int grp = lane >> 4;
+  // ---- S^T = K Q^T  (rows: tokens a*16 + 4*grp + rr; column: head lane & 15)
   f32x4 sacc[2];
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
