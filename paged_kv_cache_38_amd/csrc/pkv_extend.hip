@@ -75,6 +75,14 @@ __device__ __forceinline__ bf16x8 ext_v_operand(const char* tile, int r0, int c0
   return bf16x8{ba[0], ba[1], ba[2], ba[3], bb[0], bb[1], bb[2], bb[3]};
 }
 
+// O^T += V^T P^T over a 16-key slice with v_mfma_f32_16x16x16_bf16: A = V^T
+// (lane (x, j) holds V[4j + r][x], r = 0..3: the low half of the transposed
+// read above), B = P^T (lane (row, j) holds P[row][4j + r]: the keys the
+// score layout leaves in the lane).
+__device__ __forceinline__ f32x4 mfma16x16x16(i16x4 a, i16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
 // Softcap ([XPU] "Approach 2": the ragged call passes softcap; a score s
 // becomes cap tanh(s / cap)).  Scores stay in the kernel's raw domain (the
 // scale is applied inside exp2), so a raw score x turns into
@@ -131,7 +139,13 @@ __global__ void __launch_bounds__(256, ExtendCfg<D>::OCC) extend_kernel(DevMap m
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int g = h / G;
-  const int rw = qt * kBM + w * kWR;  // first query row (within the request) of this wave
+  // A block whose rows fit one wave runs key-split: every wave takes all of
+  // its rows and its own 16-key slice (keys 16 w .. 16 w + 15) of each tile,
+  // and the four partial softmax states are merged through LDS at the end.
+  // Otherwise a short block would leave three waves with no rows, and its
+  // tiles would wait on one wave's chain of dependent phases.
+  const bool ks = n - qt * kBM <= kWR;
+  const int rw = qt * kBM + (ks ? 0 : w * kWR);  // first query row (within the request) of this wave
 
   // keys any row of this block may see
   int kv_end = L;
@@ -358,7 +372,85 @@ __global__ void __launch_bounds__(256, ExtendCfg<D>::OCC) extend_kernel(DevMap m
       }
     };
 
-    auto step = [&](int kt, auto stage_c) {
+    // ---- key-split form of the two above: this wave's 16-key slice of
+    // the tile against all kRB row blocks.  The lane holds keys
+    // k0 + 16 w + 4 grp + rr of row rb * 16 + col, which is also the B
+    // operand of the 16-key P V^T product.
+    auto qk_ks = [&](auto stage_c, f32x4 (&sacc)[kRB]) {
+      constexpr int st = decltype(stage_c)::value;
+      const char* ks_lds = lds0 + (st * 2 + 0) * C::TILE + w * 16 * CPK * 16;
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) sacc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        const bf16x8 ka =
+            as_bf16x8(*reinterpret_cast<const u32x4*>(ks_lds + ((kk & 1) ? kbase1 : kbase0) + (kk >> 1) * 128));
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) sacc[rb] = mfma16x16x32(ka, qb[rb][kk], sacc[rb]);
+      }
+      if constexpr (SC) {
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) sacc[rb][rr] = cap(sacc[rb][rr]);
+      }
+    };
+    auto smpv_ks = [&](int kt, auto stage_c, auto mask_c, f32x4 (&sacc)[kRB]) {
+      constexpr int st = decltype(stage_c)::value;
+      constexpr bool MASK = decltype(mask_c)::value;
+      const char* vs = lds0 + (st * 2 + 1) * C::TILE + w * 16 * CPK * 16;
+      const int k0 = kt * kBN + w * 16;
+      if (MASK) {
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) {
+          const int lim = row_end[rb] - k0 - grp * 4;
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            if (rr >= lim) sacc[rb][rr] = -INFINITY;
+        }
+      }
+      float lane_max[kRB];
+      bool lane_bump = false;
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) {
+        const float mr = fmaxf(fmaxf(sacc[rb][0], sacc[rb][1]), fmaxf(sacc[rb][2], sacc[rb][3]));
+        lane_max[rb] = mr;
+        lane_bump |= mr * scale_log2 > m_run[rb] + kExtSlack;
+      }
+      if (__builtin_amdgcn_ballot_w64(lane_bump) != 0) {
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) {
+          const float m_tile = max_xor16_32(lane_max[rb]) * scale_log2;
+          const bool bump = m_tile > m_run[rb] + kExtSlack;
+          const float alpha = bump ? fast_exp2(m_run[rb] - m_tile) : 1.0f;
+          m_run[rb] = bump ? m_tile : m_run[rb];
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) acc[rb][nt] *= alpha;
+          acc_l[rb] *= alpha;
+        }
+      }
+      i16x4 pb[kRB];
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) {
+        const float mu = m_run[rb] == -INFINITY ? 0.f : m_run[rb];
+        bf16x4 p;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) p[rr] = (bf16)fast_exp2(fmaf(sacc[rb][rr], scale_log2, -mu));
+        pb[rb] = __builtin_bit_cast(i16x4, p);
+      }
+      const i16x4 ones4 = __builtin_bit_cast(i16x4, bf16x4{(bf16)1.f, (bf16)1.f, (bf16)1.f, (bf16)1.f});
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const i16x4 va = lds_read_tr16(reinterpret_cast<const bf16*>(vs + vbase[nt & 3] + (nt >> 2) * 128));
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) acc[rb][nt] = mfma16x16x16(va, pb[rb], acc[rb][nt]);
+      }
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) acc_l[rb] = mfma16x16x16(ones4, pb[rb], acc_l[rb]);
+    };
+
+    auto step = [&](int kt, auto stage_c, auto ks_c) {
+      constexpr bool KS = decltype(ks_c)::value;
       tab_dma(kt + S);
       wait_vm<C::WAIT>();  // tile kt and table kt + S - 1 have landed
       __syncthreads();     // tile kt visible to all waves; every wave is past tile kt - 1
@@ -367,26 +459,102 @@ __global__ void __launch_bounds__(256, ExtendCfg<D>::OCC) extend_kernel(DevMap m
       // tile's keys, only helps move the tiles; keys past what every row of
       // the wave sees need the per-element mask
       if (rw < n && kt * kBN < w_end) {
-        f32x4 sacc[4][kRB];
-        qk(stage_c, sacc);
-        if (kt * kBN + kBN <= w_free)
-          smpv(kt, stage_c, std::false_type{}, sacc);
-        else
-          smpv(kt, stage_c, std::true_type{}, sacc);
+        if constexpr (KS) {
+          f32x4 sacc[kRB];
+          qk_ks(stage_c, sacc);
+          if (kt * kBN + kBN <= w_free)
+            smpv_ks(kt, stage_c, std::false_type{}, sacc);
+          else
+            smpv_ks(kt, stage_c, std::true_type{}, sacc);
+        } else {
+          f32x4 sacc[4][kRB];
+          qk(stage_c, sacc);
+          if (kt * kBN + kBN <= w_free)
+            smpv(kt, stage_c, std::false_type{}, sacc);
+          else
+            smpv(kt, stage_c, std::true_type{}, sacc);
+        }
       }
     };
-    for (int kt = 0; kt < ntiles; kt += S) {
-      step(kt, std::integral_constant<int, 0>{});
-      if (kt + 1 < ntiles) step(kt + 1, std::integral_constant<int, 1>{});
-      if constexpr (S > 2) {
-        if (kt + 2 < ntiles) step(kt + 2, std::integral_constant<int, 2 % S>{});
+    auto tiles = [&](auto ks_c) {
+      for (int kt = 0; kt < ntiles; kt += S) {
+        step(kt, std::integral_constant<int, 0>{}, ks_c);
+        if (kt + 1 < ntiles) step(kt + 1, std::integral_constant<int, 1>{}, ks_c);
+        if constexpr (S > 2) {
+          if (kt + 2 < ntiles) step(kt + 2, std::integral_constant<int, 2 % S>{}, ks_c);
+        }
+        if constexpr (S > 3) {
+          if (kt + 3 < ntiles) step(kt + 3, std::integral_constant<int, 3 % S>{}, ks_c);
+        }
+        static_assert(S <= 4, "the tile loop is unrolled for at most four stages");
       }
-      if constexpr (S > 3) {
-        if (kt + 3 < ntiles) step(kt + 3, std::integral_constant<int, 3 % S>{});
-      }
-      static_assert(S <= 4, "the tile loop is unrolled for at most four stages");
-    }
+    };
+    if (ks)
+      tiles(std::true_type{});
+    else
+      tiles(std::false_type{});
     wait_vm<0>();  // no load may still target this block's LDS when it ends
+  }
+
+  if (ks) {
+    // ---- merge the four waves' partial states of the block's rows: each
+    // wave leaves its O rows (fp32), row references and row sums in the
+    // tile buffers, then wave w finishes d columns [D / 4 w, D / 4 (w + 1))
+    // of every row: O = sum_w exp2(m_w - m) O_w / sum_w exp2(m_w - m) l_w.
+    static_assert(4 * kWR * D * 4 <= S * 2 * C::TILE, "partial rows fit the tile buffers");
+    static_assert(2 * 4 * kWR * 4 <= (int)sizeof(tab_lds), "row statistics fit the table buffers");
+    float* po = reinterpret_cast<float*>(&kv_lds[0][0][0]);  // [wave][row][d]
+    float* pm = reinterpret_cast<float*>(&tab_lds[0][0][0]);  // [wave][row]
+    float* pl = pm + 4 * kWR;
+    __syncthreads();  // every wave is done with the tiles
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) {
+      const int r = rb * 16 + col;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        *reinterpret_cast<f32x4*>(po + ((w * kWR + r) * D + nt * 16 + grp * 4)) = acc[rb][nt];
+      if (grp == 0) {
+        pm[w * kWR + r] = m_run[rb];
+        pl[w * kWR + r] = acc_l[rb][0];
+      }
+    }
+    __syncthreads();
+    constexpr int DW = D / 4;  // d columns this wave finishes
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) {
+      const int r = rb * 16 + col;
+      const int row = rw + r;
+      float mw[4], m = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        mw[v] = pm[v * kWR + r];
+        m = fmaxf(m, mw[v]);
+      }
+      float wt[4], lt = 0.f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        wt[v] = mw[v] == -INFINITY ? 0.f : fast_exp2(mw[v] - m);
+        lt += wt[v] * pl[v * kWR + r];
+      }
+      const bool any = lt > 0.f;
+      const float inv = any ? 1.0f / lt : 0.f;
+#pragma unroll
+      for (int d4 = 0; d4 < DW / 16; ++d4) {
+        const int d0 = w * DW + d4 * 16 + grp * 4;
+        f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int v = 0; v < 4; ++v) o += wt[v] * *reinterpret_cast<const f32x4*>(po + ((v * kWR + r) * D + d0));
+        if (row < n) {
+          bf16x4 ov;
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) ov[rr] = (bf16)(o[rr] * inv);
+          *reinterpret_cast<bf16x4*>(out + ((int64_t)(q0 + row) * Hq + h) * D + d0) = ov;
+        }
+      }
+      if (lse && w == 0 && grp == 0 && row < n)
+        lse[(int64_t)(q0 + row) * Hq + h] = any ? (m + __log2f(lt)) * kLn2 : -INFINITY;
+    }
+    return;
   }
 
   // ---- finalise: lane (row col of block rb, group grp) holds
