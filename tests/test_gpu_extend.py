@@ -260,3 +260,32 @@ def test_extend_f32_empty_encoder_gives_zeros():
     for fmt in FMTS:
         out, lse = run_extend(dc, "cross", fmt)
         assert (out == 0).all() and torch.isneginf(lse).all()
+
+
+@pytest.mark.parametrize("head_dim", [64, 128])
+@pytest.mark.parametrize("region", ["self", "cross"])
+@pytest.mark.parametrize("fmt", [P.PKV_MAP_CSR, P.PKV_MAP_BLOCK_TABLE])
+def test_key_split_short_blocks_match_oracle(head_dim, region, fmt):
+    """Query blocks whose rows fit one wave (48 rows at D = 64, 32 at
+    D = 128) run key-split: every wave takes all of the block's rows and a
+    16-key slice of each tile, and the partial states are merged at the end.
+    Requests of 1 .. 48 (32) new tokens make every block such a block; 193 ..
+    240 (129 .. 160) new tokens give a full block followed by a short one.
+    Causal self region and full cross region; ragged equals paged bit for
+    bit."""
+    wr = 48 if head_dim == 64 else 32
+    bm = 4 * wr
+    for k, new_range in enumerate([(1, wr), (bm + 1, bm + wr)]):
+        case = W.encdec_extend(seed=21 + k, bs=6, enc_len=700, prefix_range=(0, 300), new_range=new_range,
+                               num_heads=4, head_dim=head_dim)
+        vals = W.make_values(case, canary=True)
+        dc = DeviceCase(case, vals)
+        dc.store()
+        out, lse = run_extend(dc, region, fmt)
+        ref_o, ref_l = oracle_region(case, vals, region)
+        tag = f"D {head_dim} {region} fmt {fmt} n {new_range}"
+        assert_attn_close(out, ref_o, "bf16", tag)
+        assert_lse_close(lse, ref_l, "bf16", tag)
+        ragged = run_extend(dc, region, P.PKV_MAP_TOKEN_TABLE, contiguous=True)
+        assert torch.equal(out.view(torch.int16), ragged[0].view(torch.int16)), tag
+        assert torch.equal(lse, ragged[1]), tag
