@@ -233,13 +233,14 @@ struct StreamSet {
   int i, jt, T, P, valid;
 };
 
-// One run of the stream, by workgroup `bid` (vt: this wave's V tile in LDS).
+// One run of the stream, by workgroup `bid` (vt: this wave's V tile in LDS;
+// prefix_skip: per request the keys a shared-prefix pass reads instead).
 template <int D, int WAVES, int NS>
 __device__ __forceinline__ void stream_run(
     int bid, bf16* vt, const bf16* k_pool, const bf16* v_pool, const bf16* __restrict__ q, int32_t Hq, int32_t Hkv,
     int32_t G, int32_t hg, const int32_t* __restrict__ header, const int32_t* __restrict__ meta, float scale_log2,
     bf16* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws_o, float* __restrict__ ws_lse,
-    int32_t pieces_only, const int32_t* __restrict__ prefix_skip) {
+    const int32_t* __restrict__ prefix_skip) {
   constexpr int NK = D / 32;
   constexpr int NT = D / 16;
 
@@ -288,10 +289,9 @@ __device__ __forceinline__ void stream_run(
 
   auto finish = [&](int i, int P, int T) {
     const int b0 = P / Bt, b1 = (P + T - 1) / Bt;
-    // (cascade decode merges every request afterwards: all results are
-    // pieces; with shared prefixes found by the decode, so is every request
-    // part of whose keys the prefix pass reads)
-    const bool direct = b0 == b1 && !pieces_only && (!prefix_skip || prefix_skip[i] == 0);
+    // (a request part of whose keys the prefix pass reads is merged
+    // afterwards: its result is a piece)
+    const bool direct = b0 == b1 && prefix_skip[i] == 0;
     float l_tot = l_run + shfl_xor(l_run, 16);
     l_tot += shfl_xor(l_tot, 32);
 #pragma unroll
@@ -376,17 +376,6 @@ __device__ __forceinline__ void stream_run(
     if (r + j < n) step(r + j, S[j]);
 }
 
-template <int D, int WAVES, int NS>
-__global__ void __launch_bounds__(64 * WAVES, stream_min_blocks(WAVES, NS)) decode_stream_kernel(
-    const bf16* k_pool, const bf16* v_pool, const bf16* __restrict__ q, int32_t Hq, int32_t Hkv, int32_t G,
-    int32_t hg, const int32_t* __restrict__ header, const int32_t* __restrict__ meta, float scale_log2,
-    bf16* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws_o, float* __restrict__ ws_lse,
-    int32_t pieces_only) {
-  __shared__ __attribute__((aligned(16))) bf16 vsm[WAVES][kTile * (D + 8)];
-  stream_run<D, WAVES, NS>((int)blockIdx.x, vsm[threadIdx.x >> 6], k_pool, v_pool, q, Hq, Hkv, G, hg, header, meta,
-                           scale_log2, out, lse, ws_o, ws_lse, pieces_only, nullptr);
-}
-
 // ---------------------------------------------------------------------------
 // Cascade decode over shared prefixes ([XPU] introduction and [MINI]: the
 // requests of a group reuse the same prefix pages; [BACKEND]: split-K with a
@@ -400,24 +389,106 @@ __global__ void __launch_bounds__(64 * WAVES, stream_min_blocks(WAVES, NS)) deco
 // paged_decode_attn, with every shared K/V row leaving HBM once per group.
 // ---------------------------------------------------------------------------
 
-// skip[i] = S_g for a member of group g (groups are increasing, disjoint
-// ranges of the batch), 0 for a request in no group.
-__global__ void __launch_bounds__(256) cascade_skip_kernel(const int32_t* __restrict__ group_indptr,
+// The cascade's plan.  Blocks [0, nb): skip[i] = S_g for a member of group g
+// (groups are increasing, disjoint ranges of the batch), 0 for a request in
+// no group.  Block nb + g: group g's prefix work items, listed after those
+// of every earlier group: min(ceil(members / ms), slices) slices of ms
+// members times `chunks` chunks of the prefix keys [0, E), E = min(S_g, the
+// longest member's length), read through the longest member's table (the
+// first on ties; every member's prefix keys are among its keys).  The
+// chunks split the group's own prefix tiles evenly; a chunk past them holds
+// no tiles and its results are empty.  The last group's block writes the
+// item count (block 0 does when there are no groups).
+__global__ void __launch_bounds__(256) cascade_plan_kernel(DevMap m, const int32_t* __restrict__ group_indptr,
                                                            const int32_t* __restrict__ prefix_len,
-                                                           int32_t num_groups, int32_t bs,
-                                                           int32_t* __restrict__ skip) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= bs) return;
-  int lo = 0, hi = num_groups;  // last g with group_indptr[g] <= i, in [lo, hi)
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (group_indptr[mid] <= i) lo = mid;
-    else hi = mid;
+                                                           int32_t num_groups, int32_t bs, int32_t ms,
+                                                           int32_t slices, int32_t chunks,
+                                                           int32_t* __restrict__ skip,
+                                                           PrefixItem* __restrict__ items,
+                                                           int32_t* __restrict__ count) {
+  __shared__ int32_t red[3][4];
+  const int tid = threadIdx.x;
+  const int nb = (bs + 255) / 256;
+  if ((int)blockIdx.x < nb) {
+    if (num_groups == 0 && blockIdx.x == 0 && tid == 0) *count = 0;
+    const int i = blockIdx.x * 256 + tid;
+    if (i >= bs) return;
+    int lo = 0, hi = num_groups;  // last g with group_indptr[g] <= i, in [lo, hi)
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (group_indptr[mid] <= i) lo = mid;
+      else hi = mid;
+    }
+    int32_t v = 0;
+    if (num_groups > 0 && group_indptr[lo] <= i && i < group_indptr[lo + 1])
+      v = max(prefix_len[lo], 0) & ~(kTile - 1);
+    skip[i] = v;
+    return;
   }
-  int32_t v = 0;
-  if (num_groups > 0 && group_indptr[lo] <= i && i < group_indptr[lo + 1])
-    v = max(prefix_len[lo], 0) & ~(kTile - 1);
-  skip[i] = v;
+  const int g = (int)blockIdx.x - nb;
+  auto n_slices = [&](int k) {
+    const int a = max(group_indptr[k], 0), b = min(group_indptr[k + 1], bs);
+    return b > a ? min((b - a + ms - 1) / ms, slices) : 0;
+  };
+  const int ga = max(group_indptr[g], 0), gb = min(group_indptr[g + 1], bs);
+  int base = 0;
+  for (int k = tid; k < g; k += 256) base += n_slices(k);
+  // the longest member, the first on ties: the largest (L, -k)
+  int bl = -1, bk = bs;
+  for (int k = ga + tid; k < gb; k += 256) {
+    const int L = max(m.kv_lens[k], 0);
+    if (L > bl) {
+      bl = L;
+      bk = k;
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    base += __shfl_xor(base, o, 64);
+    const int ol = __shfl_xor(bl, o, 64), ok = __shfl_xor(bk, o, 64);
+    if (ol > bl || (ol == bl && ok < bk)) {
+      bl = ol;
+      bk = ok;
+    }
+  }
+  if ((tid & 63) == 0) {
+    red[0][tid >> 6] = base;
+    red[1][tid >> 6] = bl;
+    red[2][tid >> 6] = bk;
+  }
+  __syncthreads();
+  base = (red[0][0] + red[0][1] + red[0][2] + red[0][3]) * chunks;
+  bl = red[1][0];
+  bk = red[2][0];
+  for (int w = 1; w < 4; ++w)
+    if (red[1][w] > bl || (red[1][w] == bl && red[2][w] < bk)) {
+      bl = red[1][w];
+      bk = red[2][w];
+    }
+  const int cnt = n_slices(g) * chunks;
+  if (g == num_groups - 1 && tid == 0) *count = base + cnt;
+  if (cnt == 0) return;  // no member (uniform per workgroup)
+  const int32_t S = max(prefix_len[g], 0) & ~(kTile - 1);
+  const int32_t E = min(S, bl);
+  const int32_t tiles = (E + kTile - 1) / kTile;
+  const int32_t tpc = (tiles + chunks - 1) / chunks;
+  const ReqView rv = request_view(m, bk);
+  for (int t = tid; t < cnt; t += 256) {
+    const int32_t sl = t / chunks, ck = t % chunks;
+    const int32_t i0 = ga + sl * ms;
+    PrefixItem it;
+    it.i0 = i0;
+    it.i1 = min(gb, i0 + ms);
+    it.ref = bk;
+    it.E = E;
+    it.t0 = min(ck * tpc, tiles);
+    it.t1 = min(ck * tpc + tpc, tiles);
+    it.c = ck;
+    it.limit = rv.limit;
+    it.off_lo = (int32_t)(uint32_t)(uint64_t)rv.off;
+    it.off_hi = (int32_t)(rv.off >> 32);
+    it.pad0 = it.pad1 = 0;
+    items[base + t] = it;
+  }
 }
 
 // One tile of the shared prefix against NB blocks of 16 query rows.  Like
@@ -503,14 +574,14 @@ constexpr int kCascadeCols = 32;  // query rows (member x head) per wave: two MF
 // requests of one group, up to 32 / G of them so their rows fill two
 // 16-row MFMA column blocks) against tiles [t_begin, t_end) of the prefix
 // keys [0, E), read through the table of the group's reference member
-// (view rv; its keys [0, E) every member shares up to its own limit).  Row limits: min(kv_len, S) with one
-// S for the group, or min(kv_len, lim_arr[member]) when lim_arr is given.
+// (view rv; its keys [0, E) every member shares up to its own limit).  Row
+// limits: min(kv_len, lim_arr[member]).
 // Every (member, head) row gets a partial result in chunk slot c, o = 0 /
 // lse = -inf where the chunk holds none of the member's prefix keys.
 template <int D, int W, int FMT>
 __device__ __forceinline__ void cascade_prefix_work(const DevMap& m, const bf16* k_pool, const bf16* v_pool,
                                                     const bf16* __restrict__ q, int32_t bs, int32_t Hq,
-                                                    int32_t Hkv, int32_t G, int i0, int i1, ReqView rv, int S,
+                                                    int32_t Hkv, int32_t G, int i0, int i1, ReqView rv,
                                                     const int32_t* lim_arr, int E, int t_begin, int t_end, int c,
                                                     int ms, float scale_log2, float* __restrict__ ws_po,
                                                     float* __restrict__ ws_plse, bf16* vt, int bid) {
@@ -566,7 +637,7 @@ __device__ __forceinline__ void cascade_prefix_work(const DevMap& m, const bf16*
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) qb[b][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + kk * 32));
     l_kv[b] = m.kv_lens[mr];
-    l_cap[b] = lim_arr ? lim_arr[mr] : S;
+    l_cap[b] = lim_arr[mr];
   }
   DecodeTile<D> T[3];
   __builtin_amdgcn_sched_barrier(0);
@@ -631,46 +702,12 @@ __device__ __forceinline__ void cascade_prefix_work(const DevMap& m, const bf16*
   }
 }
 
-// Shared-prefix kernel for caller-given groups: one wave per (group, member
-// slice, prefix chunk, KV head).  The prefix tiles are read through the
-// table of the group's longest member (every member's prefix keys are among
-// its keys).  The hg workgroups of one work item are 8 blocks apart (one
-// XCD), as in the stream kernel.
-template <int D, int W, int FMT>
-__global__ void __launch_bounds__(64 * W) cascade_prefix_kernel(
-    DevMap m, const bf16* k_pool, const bf16* v_pool, const bf16* __restrict__ q, int32_t bs, int32_t Hq,
-    int32_t Hkv, int32_t G, int32_t hg, const int32_t* __restrict__ group_indptr,
-    const int32_t* __restrict__ prefix_len, int32_t num_groups, int32_t slices, int32_t chunks, int32_t tpc,
-    int32_t ms, float scale_log2, float* __restrict__ ws_po, float* __restrict__ ws_plse) {
-  constexpr int LDS = D + 8;
-  __shared__ __attribute__((aligned(16))) bf16 vsm[W][kTile * LDS];
-  const int work = (blockIdx.x / (8 * hg)) * 8 + blockIdx.x % 8;
-  if (work >= num_groups * slices * chunks) return;
-  const int c = work % chunks, sl = (work / chunks) % slices, gi = work / (chunks * slices);
-  const int ga = max(group_indptr[gi], 0), gb = min(group_indptr[gi + 1], bs);
-  const int i0 = ga + sl * ms, i1 = min(gb, i0 + ms);
-  if (i0 >= i1) return;  // uniform per workgroup
-  const int S = max(prefix_len[gi], 0) & ~(kTile - 1);
-  int rd = ga, Lmax = 0;  // the longest member reads the prefix
-  for (int k = ga; k < gb; ++k) {
-    const int L = m.kv_lens[k];
-    if (L > Lmax) {
-      Lmax = L;
-      rd = k;
-    }
-  }
-  const int E = min(S, Lmax);  // prefix keys any member sees
-  const int t_begin = c * tpc, t_end = min(t_begin + tpc, (E + kTile - 1) / kTile);
-  cascade_prefix_work<D, W, FMT>(m, k_pool, v_pool, q, bs, Hq, Hkv, G, i0, i1, request_view(m, rd), S, nullptr, E,
-                                 t_begin, t_end, c,
-                                 ms, scale_log2, ws_po, ws_plse, vsm[threadIdx.x >> 6], (int)blockIdx.x);
-}
-
 // The bf16 decode's main launch: workgroups [0, n_stream) stream the runs
-// of every request's own keys; the rest take the work items the planner
-// listed for the shared prefixes paged_decode_attn found (*count of them),
-// striding over them.  One launch, so the prefix work starts on each CU as
-// soon as its run is done, and a batch without shared prefixes pays no
+// of every request's own keys; the rest take the shared-prefix work items
+// listed by the planner (*count of them, at most cap): the prefixes
+// paged_decode_attn found, or the caller's groups of the cascade decode;
+// they stride over them.  One launch, so the prefix work starts on each CU
+// as soon as its run is done, and a batch without shared prefixes pays no
 // second launch.
 template <int D, int WAVES, int NS, int FMT>
 __global__ void __launch_bounds__(64 * WAVES, stream_min_blocks(WAVES, NS)) decode_share_kernel(
@@ -678,19 +715,19 @@ __global__ void __launch_bounds__(64 * WAVES, stream_min_blocks(WAVES, NS)) deco
     int32_t hg, const int32_t* __restrict__ header, const int32_t* __restrict__ meta, float scale_log2,
     bf16* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws_o, float* __restrict__ ws_lse,
     int32_t n_stream, DevMap m, int32_t bs, const PrefixItem* __restrict__ items, const int32_t* __restrict__ count,
-    const int32_t* __restrict__ skip, int32_t ms, float* __restrict__ ws_po, float* __restrict__ ws_plse) {
+    const int32_t* __restrict__ skip, int32_t ms, int32_t cap, float* __restrict__ ws_po,
+    float* __restrict__ ws_plse) {
   __shared__ __attribute__((aligned(16))) bf16 vsm[WAVES][kTile * (D + 8)];
   bf16* vt = vsm[threadIdx.x >> 6];
   if ((int)blockIdx.x < n_stream) {
     stream_run<D, WAVES, NS>((int)blockIdx.x, vt, k_pool, v_pool, q, Hq, Hkv, G, hg, header, meta, scale_log2, out,
-                             lse, ws_o, ws_lse, 0, skip);
+                             lse, ws_o, ws_lse, skip);
     return;
   }
   const int b = (int)blockIdx.x - n_stream;  // n_stream is a multiple of 8: b keeps the XCD of blockIdx
   const int works = ((int)gridDim.x - n_stream) / hg;
   // the first item is loaded beside the count (at an index clamped into
-  // the list's capacity, bs * kShareChunks), not after it
-  const int cap = bs * kShareChunks;
+  // the list's capacity), not after it
   int w = (b / (8 * hg)) * 8 + b % 8;
   PrefixItem it = items[min(w, cap - 1)];
   const int n_items = *count;
@@ -699,8 +736,8 @@ __global__ void __launch_bounds__(64 * WAVES, stream_min_blocks(WAVES, NS)) deco
   asm volatile("" ::"s"(n_items), "s"(it.i0), "s"(it.i1), "s"(it.E), "s"(it.t0), "s"(it.t1), "s"(it.c),
                "s"(it.limit), "s"(it.off_lo), "s"(it.off_hi));
   while (w < n_items) {
-    cascade_prefix_work<D, WAVES, FMT>(m, k_pool, v_pool, q, bs, Hq, Hkv, G, it.i0, it.i1, prefix_item_view(it), 0,
-                                       skip, it.E, it.t0, it.t1, it.c, ms, scale_log2, ws_po, ws_plse, vt, b);
+    cascade_prefix_work<D, WAVES, FMT>(m, k_pool, v_pool, q, bs, Hq, Hkv, G, it.i0, it.i1, prefix_item_view(it), skip,
+                                       it.E, it.t0, it.t1, it.c, ms, scale_log2, ws_po, ws_plse, vt, b);
     w += works;
     if (w < n_items) it = items[w];
   }
@@ -805,15 +842,13 @@ __global__ void __launch_bounds__(64) share_detect_kernel(DevMap m, int32_t bs, 
   }
 }
 
-// Final merge of a cascade decode: one wavefront per (request, head) over the
-// suffix pieces (ids run + request, every one in the workspace) and, for a
-// group member, the prefix chunks.
-// With direct_written (shared prefixes found by the decode itself), a
-// request outside the prefix pass that one run finished was written by the
-// stream kernel and is skipped here.
+// Final merge of a decode with a shared-prefix pass: one wavefront per
+// (request, head) over the suffix pieces (ids run + request, every one in
+// the workspace) and, for a request whose skip is nonzero, the prefix
+// chunks.  A request outside the prefix pass that one run finished was
+// written by the stream kernel and is skipped here.
 template <int D>
 __global__ void __launch_bounds__(256) cascade_merge_kernel(int32_t bs, int32_t Hq, int32_t chunks,
-                                                            int32_t direct_written,
                                                             const int32_t* __restrict__ header,
                                                             const int32_t* __restrict__ prefix,
                                                             const int32_t* __restrict__ ntiles,
@@ -833,7 +868,7 @@ __global__ void __launch_bounds__(256) cascade_merge_kernel(int32_t bs, int32_t 
   const int P = prefix[i];
   const int b0 = P / Bt, b1 = T > 0 ? (P + T - 1) / Bt : b0 - 1;
   const int nc = skip[i] > 0 ? chunks : 0;
-  if (direct_written && nc == 0 && b0 == b1) return;
+  if (nc == 0 && b0 == b1) return;
   auto piece = [&](int k, const float*& o) -> float {  // k < pieces: suffix, else prefix chunk
     const int np = b1 - b0 + 1;
     if (k < np) {
@@ -1227,38 +1262,49 @@ static void launch_valu(unsigned blocks, hipStream_t s, const DevMap& m, const P
                      static_cast<float*>(out), lse, w.o, w.lse);
 }
 
-template <int D, int W>
-static void launch_stream_main(int32_t runs, int32_t hg, hipStream_t s, const PoolInfo& p, int32_t layer,
-                               const void* q, int32_t Hq, int32_t G, const StreamWs& w, float sl2, void* out,
-                               float* lse, int32_t pieces_only = 0) {
-  hipLaunchKernelGGL((decode_stream_kernel<D, W, kStreamSets>), dim3((unsigned)(runs * hg)), dim3(64 * W), 0, s,
-                     reinterpret_cast<const bf16*>(p.k_layer(layer)), reinterpret_cast<const bf16*>(p.v_layer(layer)),
-                     static_cast<const bf16*>(q), Hq, p.num_kv_heads, G, hg, w.header, w.meta, sl2,
-                     static_cast<bf16*>(out), lse, w.o, w.lse, pieces_only);
-}
+// The prefix pass's inputs to decode_share_kernel: its work items (at
+// most cap; cap 0 launches no prefix workgroups), each request's skip, the
+// members per slice and the partial results' slots.
+struct PrefixPass {
+  const PrefixItem* items;
+  const int32_t* count;
+  const int32_t* skip;
+  int32_t ms;
+  int32_t cap;
+  float* po;
+  float* plse;
+};
 
 template <int D, int W, int FMT>
 static void launch_share_main(int32_t runs, int32_t hg, hipStream_t s, const PoolInfo& p, int32_t layer,
                               const DevMap& m, const void* q, int32_t bs, int32_t Hq, int32_t G, const StreamWs& w,
-                              const ShareWs& sh, float sl2, void* out, float* lse) {
-  // the prefix work: at most bs * kShareChunks items, one work per CU covers the usual count
-  const int64_t works = (std::min<int64_t>((int64_t)bs * kShareChunks, device_cu_count()) + 7) / 8 * 8;
+                              const PrefixPass& pp, float sl2, void* out, float* lse) {
+  // the prefix work: one work per CU covers the usual count
+  const int64_t works = (std::min<int64_t>(pp.cap, device_cu_count()) + 7) / 8 * 8;
   const int32_t n_stream = runs * hg;
   hipLaunchKernelGGL((decode_share_kernel<D, W, kStreamSets, FMT>), dim3((unsigned)(n_stream + works * hg)),
                      dim3(64 * W), 0, s, reinterpret_cast<const bf16*>(p.k_layer(layer)),
                      reinterpret_cast<const bf16*>(p.v_layer(layer)), static_cast<const bf16*>(q), Hq, p.num_kv_heads,
-                     G, hg, w.header, w.meta, sl2, static_cast<bf16*>(out), lse, w.o, w.lse, n_stream, m, bs, sh.items,
-                     sh.count, sh.skip, sh.ms, sh.po, sh.plse);
+                     G, hg, w.header, w.meta, sl2, static_cast<bf16*>(out), lse, w.o, w.lse, n_stream, m, bs, pp.items,
+                     pp.count, pp.skip, pp.ms, pp.cap, pp.po, pp.plse);
 }
 
-template <int D, int W>
-static void launch_share_main_fmt(int32_t runs, int32_t hg, hipStream_t s, const PoolInfo& p, int32_t layer,
-                                  const DevMap& m, const void* q, int32_t bs, int32_t Hq, int32_t G,
-                                  const StreamWs& w, const ShareWs& sh, float sl2, void* out, float* lse) {
-  if (m.fmt == MAP_TOKEN_TABLE)
-    launch_share_main<D, W, SLOT_TABLE>(runs, hg, s, p, layer, m, q, bs, Hq, G, w, sh, sl2, out, lse);
-  else
-    launch_share_main<D, W, SLOT_PAGES>(runs, hg, s, p, layer, m, q, bs, Hq, G, w, sh, sl2, out, lse);
+// decode_share_kernel for the pool's head dim, the waves per workgroup W
+// (one KV head each) and the map's slot form
+static void launch_share_any(int32_t W, int32_t runs, int32_t hg, hipStream_t s, const PoolInfo& p, int32_t layer,
+                             const DevMap& m, const void* q, int32_t bs, int32_t Hq, int32_t G, const StreamWs& w,
+                             const PrefixPass& pp, float sl2, void* out, float* lse) {
+  const bool tab = m.fmt == MAP_TOKEN_TABLE;
+  auto go = [&](auto launch) { launch(runs, hg, s, p, layer, m, q, bs, Hq, G, w, pp, sl2, out, lse); };
+  if (p.head_dim_qk == 128) {
+    if (W == 4) tab ? go(launch_share_main<128, 4, SLOT_TABLE>) : go(launch_share_main<128, 4, SLOT_PAGES>);
+    else if (W == 2) tab ? go(launch_share_main<128, 2, SLOT_TABLE>) : go(launch_share_main<128, 2, SLOT_PAGES>);
+    else tab ? go(launch_share_main<128, 1, SLOT_TABLE>) : go(launch_share_main<128, 1, SLOT_PAGES>);
+  } else {
+    if (W == 4) tab ? go(launch_share_main<64, 4, SLOT_TABLE>) : go(launch_share_main<64, 4, SLOT_PAGES>);
+    else if (W == 2) tab ? go(launch_share_main<64, 2, SLOT_TABLE>) : go(launch_share_main<64, 2, SLOT_PAGES>);
+    else tab ? go(launch_share_main<64, 1, SLOT_TABLE>) : go(launch_share_main<64, 1, SLOT_PAGES>);
+  }
 }
 
 // The bf16 decode: find shared prefixes (share_detect_kernel), plan the
@@ -1297,25 +1343,18 @@ static hipError_t launch_stream_decode(const PoolInfo& p, int32_t layer, const v
   e = launch_stream_plan(m, bs, plan.chunk, runs, w, s, nullptr, st, &sa);
   if (e != hipSuccess) return e;
   const int D = p.head_dim_qk;
+  const PrefixPass pp{sh.items, sh.count, sh.skip, sh.ms, bs * kShareChunks, sh.po, sh.plse};
   timer_before(s);
-  if (D == 128) {
-    if (W == 4) launch_share_main_fmt<128, 4>(runs, hg, s, p, layer, m, q, bs, Hq, G, w, sh, sl2, out, lse);
-    else if (W == 2) launch_share_main_fmt<128, 2>(runs, hg, s, p, layer, m, q, bs, Hq, G, w, sh, sl2, out, lse);
-    else launch_share_main_fmt<128, 1>(runs, hg, s, p, layer, m, q, bs, Hq, G, w, sh, sl2, out, lse);
-  } else {
-    if (W == 4) launch_share_main_fmt<64, 4>(runs, hg, s, p, layer, m, q, bs, Hq, G, w, sh, sl2, out, lse);
-    else if (W == 2) launch_share_main_fmt<64, 2>(runs, hg, s, p, layer, m, q, bs, Hq, G, w, sh, sl2, out, lse);
-    else launch_share_main_fmt<64, 1>(runs, hg, s, p, layer, m, q, bs, Hq, G, w, sh, sl2, out, lse);
-  }
+  launch_share_any(W, runs, hg, s, p, layer, m, q, bs, Hq, G, w, pp, sl2, out, lse);
   e = hipGetLastError();
   timer_after(s);
   if (e != hipSuccess) return e;
   const unsigned mblocks = (unsigned)(((int64_t)bs * Hq + 3) / 4);
   if (D == 128)
-    hipLaunchKernelGGL(cascade_merge_kernel<128>, dim3(mblocks), dim3(256), 0, s, bs, Hq, kShareChunks, 1, w.header,
+    hipLaunchKernelGGL(cascade_merge_kernel<128>, dim3(mblocks), dim3(256), 0, s, bs, Hq, kShareChunks, w.header,
                        w.prefix, w.ntiles, sh.skip, w.o, w.lse, sh.po, sh.plse, static_cast<bf16*>(out), lse);
   else
-    hipLaunchKernelGGL(cascade_merge_kernel<64>, dim3(mblocks), dim3(256), 0, s, bs, Hq, kShareChunks, 1, w.header,
+    hipLaunchKernelGGL(cascade_merge_kernel<64>, dim3(mblocks), dim3(256), 0, s, bs, Hq, kShareChunks, w.header,
                        w.prefix, w.ntiles, sh.skip, w.o, w.lse, sh.po, sh.plse, static_cast<bf16*>(out), lse);
   return hipGetLastError();
 }
@@ -1332,13 +1371,14 @@ CascadePlan plan_cascade(const PoolInfo& p, int32_t bs, int32_t Hq, int32_t max_
   const int ptiles = std::max(1, (std::min(max_prefix_len, max_kv_len) + kTile - 1) / kTile);
   const int64_t items = std::max<int64_t>(1, (int64_t)num_groups * cp.slices * Hkv);
   // about four waves per CU over the prefix work
-  int chunks = (int)std::min<int64_t>(ptiles, std::max<int64_t>(1, (device_cu_count() * 4 + items - 1) / items));
-  cp.tpc = (ptiles + chunks - 1) / chunks;
-  cp.chunks = (ptiles + cp.tpc - 1) / cp.tpc;
+  const int chunks = (int)std::min<int64_t>(ptiles, std::max<int64_t>(1, (device_cu_count() * 4 + items - 1) / items));
+  const int tpc = (ptiles + chunks - 1) / chunks;
+  cp.chunks = (ptiles + tpc - 1) / tpc;
+  cp.cap = (int32_t)std::max<int64_t>(1, (int64_t)num_groups * cp.slices * cp.chunks);
   return cp;
 }
 
-// [stream workspace | skip[bs] | prefix o[chunks][bs][Hq][D] | prefix lse[chunks][bs][Hq]]
+// [stream workspace | skip[bs] | count | items[cap] | prefix o[chunks][bs][Hq][D] | prefix lse[chunks][bs][Hq]]
 size_t cascade_ws_layout(const PoolInfo& p, const CascadePlan& cp, int32_t bs, int32_t Hq, void* base,
                          CascadeWs* w) {
   char* b = static_cast<char*>(base);
@@ -1349,30 +1389,24 @@ size_t cascade_ws_layout(const PoolInfo& p, const CascadePlan& cp, int32_t bs, i
     return at;
   };
   char* skip = take((size_t)bs * 4);
+  char* count = take(4);
+  char* items = take((size_t)cp.cap * sizeof(PrefixItem));
   char* po = take((size_t)cp.chunks * bs * Hq * p.head_dim_v * 4);
   char* pl = take((size_t)cp.chunks * bs * Hq * 4);
   if (w) {
     w->skip = reinterpret_cast<int32_t*>(skip);
+    w->count = reinterpret_cast<int32_t*>(count);
+    w->items = reinterpret_cast<PrefixItem*>(items);
     w->po = reinterpret_cast<float*>(po);
     w->plse = reinterpret_cast<float*>(pl);
   }
   return off;
 }
 
-template <int D, int W>
-static void launch_cascade_prefix(const PoolInfo& p, int32_t layer, const DevMap& m, const void* q, int32_t bs,
-                                  int32_t Hq, int32_t G, int32_t hg, const int32_t* group_indptr,
-                                  const int32_t* prefix_len, int32_t num_groups, const CascadePlan& cp, float sl2,
-                                  const CascadeWs& w, hipStream_t s) {
-  const int64_t works = (int64_t)num_groups * cp.slices * cp.chunks;
-  const unsigned blocks = (unsigned)((works + 7) / 8 * 8 * hg);
-  auto kern = (m.fmt == MAP_TOKEN_TABLE) ? cascade_prefix_kernel<D, W, SLOT_TABLE> : cascade_prefix_kernel<D, W, SLOT_PAGES>;
-  hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * W), 0, s, m, reinterpret_cast<const bf16*>(p.k_layer(layer)),
-                     reinterpret_cast<const bf16*>(p.v_layer(layer)), static_cast<const bf16*>(q), bs, Hq,
-                     p.num_kv_heads, G, hg, group_indptr, prefix_len, num_groups, cp.slices, cp.chunks, cp.tpc, cp.ms,
-                     sl2, w.po, w.plse);
-}
-
+// The cascade: list each request's skip and the groups' prefix work
+// (cascade_plan_kernel), plan the stream of every request's own tiles,
+// stream them and read each group's prefix once (decode_share_kernel, as
+// for the prefixes paged_decode_attn finds), then merge.
 hipError_t launch_decode_cascade(const PoolInfo& p, int32_t layer, const void* q, int32_t Hq, const DevMap& m,
                                  int32_t bs, const CascadePlan& cp, const int32_t* group_indptr,
                                  const int32_t* prefix_len, int32_t num_groups, float sm_scale, void* out, float* lse,
@@ -1386,43 +1420,25 @@ hipError_t launch_decode_cascade(const PoolInfo& p, int32_t layer, const void* q
   if (cp.dp.kind != DK_STREAM || runs % 8 != 0) return hipErrorInvalidValue;
   CascadeWs w;
   cascade_ws_layout(p, cp, bs, Hq, ws, &w);
-  hipLaunchKernelGGL(cascade_skip_kernel, dim3((unsigned)((bs + 255) / 256)), dim3(256), 0, s, group_indptr,
-                     prefix_len, num_groups, bs, w.skip);
+  const int32_t nb = (bs + 255) / 256;
+  hipLaunchKernelGGL(cascade_plan_kernel, dim3((unsigned)(nb + num_groups)), dim3(256), 0, s, m, group_indptr,
+                     prefix_len, num_groups, bs, cp.ms, cp.slices, cp.chunks, w.skip, w.items, w.count);
   hipError_t e = launch_stream_plan(m, bs, cp.dp.chunk, runs, w.stream, s, w.skip);
   if (e != hipSuccess) return e;
   const float sl2 = sm_scale * kLog2e;
-  const int D = p.head_dim_qk;
+  const PrefixPass pp{w.items, w.count, w.skip, cp.ms, num_groups > 0 ? cp.cap : 0, w.po, w.plse};
   timer_before(s);
-  if (D == 128) {
-    if (W == 4) launch_stream_main<128, 4>(runs, hg, s, p, layer, q, Hq, G, w.stream, sl2, out, lse, 1);
-    else if (W == 2) launch_stream_main<128, 2>(runs, hg, s, p, layer, q, Hq, G, w.stream, sl2, out, lse, 1);
-    else launch_stream_main<128, 1>(runs, hg, s, p, layer, q, Hq, G, w.stream, sl2, out, lse, 1);
-  } else {
-    if (W == 4) launch_stream_main<64, 4>(runs, hg, s, p, layer, q, Hq, G, w.stream, sl2, out, lse, 1);
-    else if (W == 2) launch_stream_main<64, 2>(runs, hg, s, p, layer, q, Hq, G, w.stream, sl2, out, lse, 1);
-    else launch_stream_main<64, 1>(runs, hg, s, p, layer, q, Hq, G, w.stream, sl2, out, lse, 1);
-  }
-  if (num_groups > 0) {
-    if (D == 128) {
-      if (W == 4) launch_cascade_prefix<128, 4>(p, layer, m, q, bs, Hq, G, hg, group_indptr, prefix_len, num_groups, cp, sl2, w, s);
-      else if (W == 2) launch_cascade_prefix<128, 2>(p, layer, m, q, bs, Hq, G, hg, group_indptr, prefix_len, num_groups, cp, sl2, w, s);
-      else launch_cascade_prefix<128, 1>(p, layer, m, q, bs, Hq, G, hg, group_indptr, prefix_len, num_groups, cp, sl2, w, s);
-    } else {
-      if (W == 4) launch_cascade_prefix<64, 4>(p, layer, m, q, bs, Hq, G, hg, group_indptr, prefix_len, num_groups, cp, sl2, w, s);
-      else if (W == 2) launch_cascade_prefix<64, 2>(p, layer, m, q, bs, Hq, G, hg, group_indptr, prefix_len, num_groups, cp, sl2, w, s);
-      else launch_cascade_prefix<64, 1>(p, layer, m, q, bs, Hq, G, hg, group_indptr, prefix_len, num_groups, cp, sl2, w, s);
-    }
-  }
+  launch_share_any(W, runs, hg, s, p, layer, m, q, bs, Hq, G, w.stream, pp, sl2, out, lse);
   e = hipGetLastError();
   timer_after(s);
   if (e != hipSuccess) return e;
   const unsigned mblocks = (unsigned)(((int64_t)bs * Hq + 3) / 4);
-  if (D == 128)
-    hipLaunchKernelGGL(cascade_merge_kernel<128>, dim3(mblocks), dim3(256), 0, s, bs, Hq, cp.chunks, 0, w.stream.header,
+  if (p.head_dim_qk == 128)
+    hipLaunchKernelGGL(cascade_merge_kernel<128>, dim3(mblocks), dim3(256), 0, s, bs, Hq, cp.chunks, w.stream.header,
                        w.stream.prefix, w.stream.ntiles, w.skip, w.stream.o, w.stream.lse, w.po, w.plse,
                        static_cast<bf16*>(out), lse);
   else
-    hipLaunchKernelGGL(cascade_merge_kernel<64>, dim3(mblocks), dim3(256), 0, s, bs, Hq, cp.chunks, 0, w.stream.header,
+    hipLaunchKernelGGL(cascade_merge_kernel<64>, dim3(mblocks), dim3(256), 0, s, bs, Hq, cp.chunks, w.stream.header,
                        w.stream.prefix, w.stream.ntiles, w.skip, w.stream.o, w.stream.lse, w.po, w.plse,
                        static_cast<bf16*>(out), lse);
   return hipGetLastError();

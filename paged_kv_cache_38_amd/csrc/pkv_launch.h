@@ -211,13 +211,15 @@ struct CascadePlan {
   int32_t ms;      // members per slice (32 query rows per wave)
   int32_t slices;  // slices per group, at most
   int32_t chunks;  // prefix chunks per group
-  int32_t tpc;     // tiles per chunk
+  int32_t cap;     // prefix work items, at most: groups x slices x chunks (at least 1)
 };
 struct CascadeWs {
   StreamWs stream;
-  int32_t* skip;  // per request: keys read by the prefix pass
-  float* po;      // prefix partials [chunks][bs][Hq][Dv]
-  float* plse;    // [chunks][bs][Hq]
+  int32_t* skip;       // per request: keys read by the prefix pass
+  int32_t* count;      // prefix work items listed
+  PrefixItem* items;   // [cap]
+  float* po;           // prefix partials [chunks][bs][Hq][Dv]
+  float* plse;         // [chunks][bs][Hq]
 };
 CascadePlan plan_cascade(const PoolInfo& p, int32_t bs, int32_t Hq, int32_t max_kv_len, int32_t num_groups,
                          int32_t max_group_size, int32_t max_prefix_len);
