@@ -109,3 +109,23 @@ def test_cascade_full_size_prefix_share():
     rows = np.asarray(reqs)
     assert_attn_close(out, ref_o, "bf16", "cascade full size", rows=rows)
     assert_lse_close(lse, ref_l, "bf16", "cascade full size", rows=rows)
+
+
+@pytest.mark.parametrize("fmt", [P.PKV_MAP_CSR, P.PKV_MAP_BLOCK_TABLE])
+def test_cascade_empty_and_single_member_groups(fmt):
+    """Declared groups that are a sub-division of the shared ones: requests
+    before the first group and after the last, empty groups (one at the
+    start, one between others), groups of one member, a prefix_len of 0 and
+    prefix lengths below the shared length (any split at or below it is
+    exact).  Each group's work items are listed after those of the groups
+    before it, so empty groups must count for nothing."""
+    case = small(16, seed=11, bs=32, group=8, prefix=512)
+    vals = W.make_values(case, canary=True)
+    dc = DeviceCase(case, vals)
+    indptr = np.array([2, 2, 7, 8, 8, 9, 16, 24], np.int32)
+    pl = np.array([512, 512, 300, 0, 0, 200, 512], np.int32)
+    print(f"cascade groups {indptr.tolist()} prefix {pl.tolist()} fmt {fmt}", flush=True)
+    out, lse = cascade(dc, fmt, indptr, pl, max_group=12)
+    ref_o, ref_l = oracle_region(case, vals, "self")
+    assert_attn_close(out, ref_o, "bf16", "cascade empty/single groups")
+    assert_lse_close(lse, ref_l, "bf16", "cascade empty/single groups")
