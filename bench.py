@@ -291,9 +291,9 @@ class DecodeBench:
 class CascadeBench(DecodeBench):
     """Decode step with the prefix groups known: build_kv_indices (CSR) then
     paged_decode_attn_cascade (each group's shared prefix read once, the own
-    keys by the split-K kernel, one log-sum-exp merge)."""
+    keys by the split-K kernel in the same launch, one log-sum-exp merge)."""
 
-    kernel_name = "cascade decode: split-K kernel over own keys + shared-prefix kernel"
+    kernel_name = "cascade decode: split-K kernel over own keys and the groups' shared prefixes (one launch)"
 
     def __init__(self, case, dev="cuda"):
         super().__init__(case, "csr", dev)
