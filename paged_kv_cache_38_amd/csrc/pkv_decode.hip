@@ -863,11 +863,15 @@ __global__ void __launch_bounds__(256) cascade_merge_kernel(int32_t bs, int32_t 
   const int64_t idx = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (idx >= (int64_t)bs * Hq) return;
   const int i = (int)(idx / Hq), h = (int)(idx % Hq);
+  // the request's words go out together (the skip word, used after the
+  // divisions, was otherwise loaded in a second round trip)
+  const int sk = skip[i];
   const int T = ntiles[i];
   const int Bt = header[0];
   const int P = prefix[i];
+  asm volatile("" ::"v"(sk), "v"(T), "v"(P));
   const int b0 = P / Bt, b1 = T > 0 ? (P + T - 1) / Bt : b0 - 1;
-  const int nc = skip[i] > 0 ? chunks : 0;
+  const int nc = sk > 0 ? chunks : 0;
   if (nc == 0 && b0 == b1) return;
   auto piece = [&](int k, const float*& o) -> float {  // k < pieces: suffix, else prefix chunk
     const int np = b1 - b0 + 1;
@@ -883,7 +887,7 @@ __global__ void __launch_bounds__(256) cascade_merge_kernel(int32_t bs, int32_t 
   const int n = (b1 - b0 + 1) + nc;
   // the first KB sources' lse and partial rows are all loaded at once (they
   // are independent); a request with more sources takes the rest in a loop
-  constexpr int KB = 8;
+  constexpr int KB = 12;
   float lb[KB], ob[KB][E];
 #pragma unroll
   for (int k = 0; k < KB; ++k) {
