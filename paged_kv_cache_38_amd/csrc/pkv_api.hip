@@ -462,6 +462,7 @@ int paged_decode_cascade_workspace_bytes(const pkv_pool* pool, int32_t bs, int32
   if (int st = check_groups(pool, num_q_heads, groups)) return st;
   const pkv::CascadePlan cp = pkv::plan_cascade(pool->info, bs, num_q_heads, max_kv_len, groups->num_groups,
                                                 groups->max_group_size, groups->max_prefix_len);
+  if (cp.cap > INT32_MAX) return fail(PKV_EUNSUPPORTED, "too many prefix work items (%lld)", (long long)cp.cap);
   *bytes = pkv::cascade_ws_layout(pool->info, cp, bs, num_q_heads, nullptr, nullptr);
   return ok();
 }
@@ -481,6 +482,7 @@ int paged_decode_attn_cascade(const pkv_pool* pool, int32_t layer, const void* q
   if (!aligned16(q)) return fail(PKV_EALIGN, "q must be 16-byte aligned");
   const pkv::CascadePlan cp = pkv::plan_cascade(pool->info, map->bs, num_q_heads, map->max_kv_len,
                                                 groups->num_groups, groups->max_group_size, groups->max_prefix_len);
+  if (cp.cap > INT32_MAX) return fail(PKV_EUNSUPPORTED, "too many prefix work items (%lld)", (long long)cp.cap);
   const size_t need = pkv::cascade_ws_layout(pool->info, cp, map->bs, num_q_heads, nullptr, nullptr);
   if (ws_bytes < need) return fail(PKV_ECAPACITY, "workspace %zu bytes < %zu needed", ws_bytes, need);
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u))

@@ -1371,14 +1371,14 @@ CascadePlan plan_cascade(const PoolInfo& p, int32_t bs, int32_t Hq, int32_t max_
   const int Hkv = p.num_kv_heads;
   const int G = Hq / Hkv;
   cp.ms = std::max(1, kCascadeCols / G);
-  cp.slices = std::max(1, (max_group_size + cp.ms - 1) / cp.ms);
+  cp.slices = (int32_t)std::max<int64_t>(1, ((int64_t)max_group_size + cp.ms - 1) / cp.ms);
   const int ptiles = std::max(1, (std::min(max_prefix_len, max_kv_len) + kTile - 1) / kTile);
   const int64_t items = std::max<int64_t>(1, (int64_t)num_groups * cp.slices * Hkv);
   // about four waves per CU over the prefix work
   const int chunks = (int)std::min<int64_t>(ptiles, std::max<int64_t>(1, (device_cu_count() * 4 + items - 1) / items));
   const int tpc = (ptiles + chunks - 1) / chunks;
   cp.chunks = (ptiles + tpc - 1) / tpc;
-  cp.cap = (int32_t)std::max<int64_t>(1, (int64_t)num_groups * cp.slices * cp.chunks);
+  cp.cap = std::max<int64_t>(1, (int64_t)num_groups * cp.slices * cp.chunks);
   return cp;
 }
 
@@ -1430,7 +1430,8 @@ hipError_t launch_decode_cascade(const PoolInfo& p, int32_t layer, const void* q
   hipError_t e = launch_stream_plan(m, bs, cp.dp.chunk, runs, w.stream, s, w.skip);
   if (e != hipSuccess) return e;
   const float sl2 = sm_scale * kLog2e;
-  const PrefixPass pp{w.items, w.count, w.skip, cp.ms, num_groups > 0 ? cp.cap : 0, w.po, w.plse};
+  if (cp.cap > INT32_MAX) return hipErrorInvalidValue;  // the API refuses such bounds first
+  const PrefixPass pp{w.items, w.count, w.skip, cp.ms, num_groups > 0 ? (int32_t)cp.cap : 0, w.po, w.plse};
   timer_before(s);
   launch_share_any(W, runs, hg, s, p, layer, m, q, bs, Hq, G, w.stream, pp, sl2, out, lse);
   e = hipGetLastError();

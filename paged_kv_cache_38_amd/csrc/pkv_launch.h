@@ -211,7 +211,7 @@ struct CascadePlan {
   int32_t ms;      // members per slice (32 query rows per wave)
   int32_t slices;  // slices per group, at most
   int32_t chunks;  // prefix chunks per group
-  int32_t cap;     // prefix work items, at most: groups x slices x chunks (at least 1)
+  int64_t cap;     // prefix work items, at most: groups x slices x chunks (at least 1)
 };
 struct CascadeWs {
   StreamWs stream;

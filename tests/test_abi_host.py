@@ -340,6 +340,12 @@ def test_cascade_arguments_checked_before_launch(lib):
         assert lib.paged_decode_cascade_workspace_bytes(h, 4, 8, 100, C.byref(bad), C.byref(ws)) == L.PKV_EINVAL
         neg = L.PrefixGroups(-1, 2, 64, 0x4000, 0x5000)
         assert lib.paged_decode_cascade_workspace_bytes(h, 4, 8, 100, C.byref(neg), C.byref(ws)) == L.PKV_EINVAL
+        # bounds whose prefix work list would need more than 2^31 items are refused, not truncated
+        huge, ws2 = L.PrefixGroups(1 << 30, 1 << 20, 64, 0x4000, 0x5000), C.c_size_t()
+        assert lib.paged_decode_cascade_workspace_bytes(h, 4, 8, 100, C.byref(huge), C.byref(ws2)) == \
+            L.PKV_EUNSUPPORTED
+        assert lib.paged_decode_attn_cascade(h, 0, 0x6000, 8, C.byref(m), C.byref(huge), 0.1, 0x7000, None, 0x8000,
+                                             1 << 40, None) == L.PKV_EUNSUPPORTED
         call = lambda ws_ptr, n, scale=0.1: lib.paged_decode_attn_cascade(h, 0, 0x6000, 8, C.byref(m), C.byref(g),
                                                                          scale, 0x7000, None, ws_ptr, n, None)
         assert call(0x8000, ws.value - 1) == L.PKV_ECAPACITY
