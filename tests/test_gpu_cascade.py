@@ -129,3 +129,26 @@ def test_cascade_empty_and_single_member_groups(fmt):
     ref_o, ref_l = oracle_region(case, vals, "self")
     assert_attn_close(out, ref_o, "bf16", "cascade empty/single groups")
     assert_lse_close(lse, ref_l, "bf16", "cascade empty/single groups")
+
+
+@pytest.mark.parametrize("head_dim,num_kv_heads,num_q_heads", [(64, 8, 32), (64, 2, 8), (128, 1, 4), (64, 1, 16)])
+def test_cascade_head_dims_and_kv_head_counts(head_dim, num_kv_heads, num_q_heads):
+    """The cascade at head_dim 64 and with one or two KV heads (workgroups of
+    one or two waves; 16 query heads per KV head give slices of two
+    members), on hand-placed groups: members shorter than the prefix, a
+    one-request group with nothing shared, and a group whose declared prefix
+    is the shortest member's share."""
+    ps = 16
+    groups = [(20, [(700, 20), (320, 20), (900, 20), (100, 20)]), (1, [(250, 0)]),
+              (12, [(400, 12), (190, 12), (640, 8)])]
+    case = W.shared_prefix_batch(ps, groups, seed=head_dim + num_kv_heads, num_q_heads=num_q_heads,
+                                 num_kv_heads=num_kv_heads, head_dim=head_dim)
+    vals = W.make_values(case, canary=True)
+    dc = DeviceCase(case, vals)
+    indptr = np.array([0, 4, 5, 8], np.int32)
+    pl = np.array([20 * ps, 0, 8 * ps], np.int32)
+    print(f"cascade D {head_dim} Hkv {num_kv_heads} Hq {num_q_heads}", flush=True)
+    out, lse = cascade(dc, P.PKV_MAP_CSR, indptr, pl)
+    ref_o, ref_l = oracle_region(case, vals, "self")
+    assert_attn_close(out, ref_o, "bf16", f"cascade D {head_dim} Hkv {num_kv_heads}")
+    assert_lse_close(lse, ref_l, "bf16", f"cascade D {head_dim} Hkv {num_kv_heads}")
