@@ -131,13 +131,15 @@ def test_cascade_empty_and_single_member_groups(fmt):
     assert_lse_close(lse, ref_l, "bf16", "cascade empty/single groups")
 
 
-@pytest.mark.parametrize("head_dim,num_kv_heads,num_q_heads", [(64, 8, 32), (64, 2, 8), (128, 1, 4), (64, 1, 16)])
+@pytest.mark.parametrize("head_dim,num_kv_heads,num_q_heads",
+                         [(64, 8, 32), (64, 2, 8), (128, 1, 4), (64, 1, 16), (64, 2, 6), (128, 3, 15)])
 def test_cascade_head_dims_and_kv_head_counts(head_dim, num_kv_heads, num_q_heads):
-    """The cascade at head_dim 64 and with one or two KV heads (workgroups of
-    one or two waves; 16 query heads per KV head give slices of two
-    members), on hand-placed groups: members shorter than the prefix, a
-    one-request group with nothing shared, and a group whose declared prefix
-    is the shortest member's share."""
+    """The cascade at head_dim 64 and with one, two or three KV heads
+    (workgroups of one or two waves; 16 query heads per KV head give slices
+    of two members, 3 and 5 leave padding rows in the 32-row slices), on
+    hand-placed groups: members shorter than the prefix, a one-request group
+    with nothing shared, and a group whose declared prefix is the shortest
+    member's share."""
     ps = 16
     groups = [(20, [(700, 20), (320, 20), (900, 20), (100, 20)]), (1, [(250, 0)]),
               (12, [(400, 12), (190, 12), (640, 8)])]

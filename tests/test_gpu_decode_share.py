@@ -190,3 +190,26 @@ def test_large_batch_with_groups_of_every_size():
     ref_o, ref_l = oracle_region(case, vals, "self", requests=reqs)
     assert_attn_close(out, ref_o, "bf16", "large shared batch", rows=reqs)
     assert_lse_close(lse, ref_l, "bf16", "large shared batch", rows=reqs)
+
+
+SHAPES = [  # (KV heads, query heads per KV head, head_dim): every launch shape, odd query groups
+    (1, 1, 64), (1, 16, 128), (2, 3, 128), (3, 5, 128), (4, 4, 64), (8, 1, 64), (2, 7, 64),
+]
+
+
+@pytest.mark.parametrize("hkv,group,d", SHAPES)
+def test_detected_groups_head_shapes(hkv, group, d):
+    """Detected sharing through the prefix pass at every launch shape (one,
+    two and four waves per workgroup), head_dim 64 and 128, and query groups
+    that do not divide the pass's 32 rows (3, 5, 7 heads: slices of 10, 6 and
+    4 members with padding rows)."""
+    ps = 16
+    groups = [(20, [(700, 20), (320, 20), (900, 20), (100, 20), (2000, 20), (330, 20), (321, 20), (1200, 20),
+                    (640, 20), (500, 20), (800, 20), (350, 20)]),
+              (0, [(250, 0)]),
+              (12, [(400, 12), (190, 12), (640, 8), (13 * ps, 12)])]
+    case = W.shared_prefix_batch(ps, groups, seed=hkv * 100 + group, num_q_heads=hkv * group, num_kv_heads=hkv,
+                                 head_dim=d)
+    print(f"detected groups shape: {hkv} kv heads x {group}, head_dim {d}", flush=True)
+    for fmt in (P.PKV_MAP_CSR, P.PKV_MAP_TOKEN_TABLE):
+        _check(case, fmt, f"shape {hkv}x{group} d{d} fmt{fmt}")
