@@ -1,7 +1,9 @@
-"""Page sizes beyond the workloads' 1, 16 and 64: decode, cascade decode and
-extend (paged and ragged) against the oracle at page sizes 2 to 128, the
-whole range the pool accepts.  The index math (slot = page * page_size +
+"""Page sizes beyond the workloads' 1, 16 and 64: decode, cascade decode,
+MLA decode and extend (paged and ragged) against the oracle at page sizes
+1 to 128, the whole range the pool accepts.  The index math (slot = page * page_size +
 offset) and every tile that straddles a page boundary change with it."""
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -46,3 +48,21 @@ def test_extend_at_page_size(ps):
             out, lse = run_extend(dc, region, fmt, contiguous=ragged)
             assert_attn_close(out, ref_o, "bf16", f"extend {region} ps {ps} fmt {fmt} ragged {ragged}")
             assert_lse_close(lse, ref_l, "bf16", f"extend {region} ps {ps} fmt {fmt} ragged {ragged}")
+
+
+@pytest.mark.parametrize("ps", [1, 16, 128])
+def test_mla_decode_at_page_size(ps):
+    """The MLA pool (one 576-value latent row per token) at page sizes other
+    than the workload's 64, in every map format, with the step's append."""
+    # unit-variance values, so the outputs (~1e-1) are far above the tolerance's absolute part
+    case = dataclasses.replace(W.mla_decode(seed=ps, bs=6, len_range=(1, 1400), num_q_heads=32, page_size=ps),
+                               value_scale=1.0)
+    print(f"page size {ps}: mla decode", flush=True)
+    vals = W.make_values(case, canary=True)
+    dc = DeviceCase(case, vals)
+    dc.store()
+    ref_o, ref_l = oracle_region(case, vals, "self")
+    for fmt in FMTS:
+        out, lse = dc.decode(fmt)
+        assert_attn_close(out, ref_o, "bf16", f"mla ps {ps} fmt {fmt}")
+        assert_lse_close(lse, ref_l, "bf16", f"mla ps {ps} fmt {fmt}")

@@ -283,7 +283,7 @@ def gqa_prefix_share(page_size: int, seed: int = 0, bs: int = 256, group: int = 
 
 
 def mla_decode(seed: int = 0, bs: int = 128, len_range=(4096, 16384), num_q_heads: int = 128,
-               num_draft: int = 1, fixed_lens: Optional[Dict[int, int]] = None) -> Case:
+               num_draft: int = 1, fixed_lens: Optional[Dict[int, int]] = None, page_size: int = 64) -> Case:
     """MLA-shaped paged decode, bf16: page_size 64, 128 query heads over one
     latent KV row of 576 values (512 latent + 64 rope); V is the first 512;
     KV lengths uniform in [4096, 16384]; values N(0,1) x 0.1; pool =
@@ -294,9 +294,10 @@ def mla_decode(seed: int = 0, bs: int = 128, len_range=(4096, 16384), num_q_head
     target-verify branch): each request's last ``num_draft`` tokens are draft
     tokens appended this step (positions L - num_draft .. L - 1, those that
     exist), each with its own queries, attending causally (bottom-right).
-    ``fixed_lens`` sets chosen requests' lengths (edge cases in tests)."""
+    ``fixed_lens`` sets chosen requests' lengths (edge cases in tests);
+    ``page_size`` other than 64 is for tests (the streams do not depend on it)."""
     rs, rp, vseed, qseed = _streams(4, seed, (num_draft,) if num_draft > 1 else ())
-    ps = 64
+    ps = page_size
     lens = rs.integers(len_range[0], len_range[1] + 1, size=bs).astype(np.int32)
     for i, n in (fixed_lens or {}).items():
         lens[i] = n
