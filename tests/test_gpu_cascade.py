@@ -154,3 +154,20 @@ def test_cascade_head_dims_and_kv_head_counts(head_dim, num_kv_heads, num_q_head
     ref_o, ref_l = oracle_region(case, vals, "self")
     assert_attn_close(out, ref_o, "bf16", f"cascade D {head_dim} Hkv {num_kv_heads}")
     assert_lse_close(lse, ref_l, "bf16", f"cascade D {head_dim} Hkv {num_kv_heads}")
+
+
+def test_cascade_group_larger_than_its_bound_stays_in_bounds():
+    """A caller whose groups hold more members than max_group_size breaks the
+    bounds' promise: the members past the slices the bound sizes get an
+    unspecified result, but the call still ends normally with nothing read
+    or written out of range, and the members the bound covers are exact."""
+    case = small(16, seed=13, bs=32, group=16, prefix=256)  # two groups of 16; 8 members per slice
+    vals = W.make_values(case, canary=True)
+    dc = DeviceCase(case, vals)
+    indptr, pl = case.prefix_groups
+    print(f"cascade groups {indptr.tolist()} declared at most 8 members", flush=True)
+    out, lse = cascade(dc, P.PKV_MAP_CSR, indptr, pl, max_group=8)
+    ref_o, ref_l = oracle_region(case, vals, "self")
+    covered = list(range(0, 8)) + list(range(16, 24))
+    assert_attn_close(out, ref_o, "bf16", "cascade bound too small (covered members)", rows=covered)
+    assert_lse_close(lse, ref_l, "bf16", "cascade bound too small (covered members)", rows=covered)
